@@ -1,0 +1,176 @@
+/*
+ * mamba_mixer.h -- C ABI of the MI355X (gfx950) Mamba-1 mixer core.
+ *
+ * The library computes, on the GPU, the selective-SSM mixer that sits between a Mamba
+ * layer's input and output projections:
+ *
+ *   x, z   = the two halves of the post-in_proj activations xz            (input)
+ *   u      = SiLU(causal depthwise conv1d(x) + conv_b)                      (conv + SiLU)
+ *   xdbl   = W_x u  = [dt_low | B | C]                                      (x_proj)
+ *   dt_low, B, C each RMS-normalised over their own length                  (internal RMSNorm)
+ *   dt     = softplus(W_dt dt_low + dt_proj_b)                              (dt_proj)
+ *   h_t    = exp(dt A) h_{t-1} + Bbar_t u_t ,  Bbar = dt B (or ZOH)         (selective scan)
+ *   y_t    = (C_t . h_t + D u_t) * SiLU(z_t)                                (feed-through + gate)
+ *
+ * Sources: "Jamba: A Hybrid Transformer-Mamba Language Model" (analysis page of
+ * arXiv 2403.19887), section "The Mamba Layer: State-Space Mechanism, Selectivity, and
+ * Parallel Scan" -- continuous SSM equation (the D u feed-through), ZOH equation
+ * (Abar = exp(Delta A), Bbar), discrete recurrence equation, "From scalar SSM to vector
+ * processing" (one scalar SSM per channel), "The selective mechanism" (B, C, Delta from
+ * small linear layers of the token), "Parallel training via the parallel scan" (the
+ * associative operator that lets the sequence be cut into chunks), "Inference behavior"
+ * (O(1) recurrent decode); section "RMSNorm definition and placement" (RMSNorm equation)
+ * with "Stabilization: RMSNorm in Mamba layers" (RMSNorm on internal activations).
+ * The convolution, SiLU, softplus and gate are the standard Mamba-1 block that page
+ * builds on; the pages do not write them out.
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers, row-major, owned by the caller. The
+ *     library allocates no device memory in these calls and keeps no state between
+ *     calls; scratch space comes from the caller's workspace.
+ *   - io_dtype selects the element type of xz, y, conv_state, conv_w, conv_b, x_proj_w
+ *     and dt_proj_w (MM_F32: float, MM_BF16: bfloat16 bits in uint16). dt_proj_b, A,
+ *     Dskip, the three norm weights and ssm_state are always float.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null stream) and
+ *     return without synchronising the host. States are updated in place in stream order.
+ *     y must not alias xz; states must not alias anything else.
+ *   - Arguments are validated on the host before anything is launched; on any error
+ *     nothing is launched and no output is written. MM_ERR_HIP reports a failed launch;
+ *     asynchronous device faults surface at the caller's next synchronisation.
+ *   - Entry points are reentrant when given separate workspaces.
+ */
+#ifndef MAMBA_MIXER_H
+#define MAMBA_MIXER_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MM_ABI_VERSION 1
+
+#if defined(__GNUC__) || defined(__clang__)
+#define MM_API __attribute__((visibility("default")))
+#else
+#define MM_API
+#endif
+
+typedef enum {
+  MM_OK = 0,
+  MM_ERR_INVALID_ARG = -1,   /* NULL required pointer, non-positive size, misalignment */
+  MM_ERR_UNSUPPORTED = -2,   /* a size outside this build's limits (see mm_shape)     */
+  MM_ERR_WORKSPACE = -3,     /* workspace NULL or smaller than the *_workspace_bytes() */
+  MM_ERR_HIP = -4            /* a HIP launch failed                                    */
+} mm_status;
+
+typedef enum { MM_F32 = 0, MM_BF16 = 1 } mm_dtype;
+
+/* flags */
+enum {
+  /* Use the ZOH input matrix of the page's ZOH equation, Bbar = expm1(dt A) / A * B,
+     instead of the first-order Bbar = dt * B (the default). */
+  MM_FLAG_ZOH_B = 1u << 0
+};
+
+/*
+ * Problem size. Limits of this build (else MM_ERR_UNSUPPORTED): d_state == 16;
+ * 2 <= d_conv <= 4; d_inner % 64 == 0; with MM_BF16, dt_rank % 64 == 0 and
+ * d_inner % 128 == 0; with MM_F32, 1 <= dt_rank <= 1024. seqlen >= 1 (prefill),
+ * seqlen == 1 (decode). rms_eps > 0 is the RMSNorm epsilon.
+ */
+typedef struct {
+  int32_t batch, seqlen, d_inner, d_state, d_conv, dt_rank;
+  mm_dtype io_dtype;
+  float rms_eps;
+  uint32_t flags;
+} mm_shape;
+
+/* Parameters (device pointers, caller-owned, 16-byte aligned). */
+typedef struct {
+  const void *conv_w;      /* [d_inner, d_conv] io_dtype; tap d_conv-1 multiplies the current token */
+  const void *conv_b;      /* [d_inner] io_dtype, or NULL for no bias */
+  const void *x_proj_w;    /* [dt_rank + 2*d_state, d_inner] io_dtype; rows = [dt_low | B | C] */
+  const void *dt_proj_w;   /* [d_inner, dt_rank] io_dtype */
+  const float *dt_proj_b;  /* [d_inner] */
+  const float *A;          /* [d_inner, d_state], the (negative real) diagonal state matrix */
+  const float *Dskip;      /* [d_inner], the feed-through D */
+  const float *dt_norm_w;  /* [dt_rank]  RMSNorm weight of dt_low */
+  const float *B_norm_w;   /* [d_state]  RMSNorm weight of B */
+  const float *C_norm_w;   /* [d_state]  RMSNorm weight of C */
+} mm_params;
+
+/* Bytes of device workspace mamba_mixer_prefill needs for this shape (0 on a bad shape). */
+MM_API size_t mm_prefill_workspace_bytes(const mm_shape *s);
+
+/*
+ * Chunked long-sequence prefill over `batch` sequences of `seqlen` tokens.
+ *   xz          [batch, seqlen, 2*d_inner] io_dtype; x = first d_inner, z = last d_inner
+ *   y           [batch, seqlen, d_inner]   io_dtype (before out_proj)
+ *   conv_state  [batch, d_inner, d_conv-1] io_dtype, inputs before token 0, oldest first;
+ *               on return the last d_conv-1 inputs. NULL: zeros in, nothing out.
+ *   ssm_state   [batch, d_inner, d_state] float; on return h after the last token.
+ *               NULL: zeros in, nothing out.
+ *   states_valid  1: read conv_state / ssm_state as the carried states;
+ *                 0: start from zeros (the state buffers, if given, are only written).
+ *   workspace   >= mm_prefill_workspace_bytes(s) bytes, 256-byte aligned.
+ * Prefill over L1 tokens then over L2 more with the returned states equals one prefill
+ * over L1 + L2 tokens (the scan operator is associative).
+ */
+MM_API mm_status mamba_mixer_prefill(const mm_shape *s, const mm_params *p, const void *xz, void *y,
+                              void *conv_state, float *ssm_state, int states_valid,
+                              void *workspace, size_t workspace_bytes, void *stream);
+
+/* Bytes of device workspace mamba_mixer_decode_step needs (s->seqlen must be 1). */
+MM_API size_t mm_decode_workspace_bytes(const mm_shape *s);
+
+/*
+ * One recurrent token for each of `batch` sequences (the page's O(1) inference step).
+ *   xz [batch, 2*d_inner], y [batch, d_inner] io_dtype; conv_state [batch, d_inner, d_conv-1]
+ *   and ssm_state [batch, d_inner, d_state] are required and updated in place.
+ * N calls equal one prefill over the same N tokens from the same states.
+ */
+MM_API mm_status mamba_mixer_decode_step(const mm_shape *s, const mm_params *p, const void *xz, void *y,
+                                  void *conv_state, float *ssm_state, void *workspace,
+                                  size_t workspace_bytes, void *stream);
+
+/*
+ * Per-stage timing (a measurement aid). A timer records a pair of HIP events around
+ * each kernel stage of every *_timed call on that call's stream; mm_stage_timer_read
+ * synchronises on the recorded events and returns the summed milliseconds and the
+ * number of timed launches per stage. Stages are listed by mm_stage_name(i),
+ * 0 <= i < MM_STAGE_COUNT. A timer is not thread-safe; create one per thread.
+ */
+enum {
+  MM_STAGE_CONV = 0,       /* conv1d + SiLU feeding x_proj */
+  MM_STAGE_XPROJ = 1,      /* x_proj contraction */
+  MM_STAGE_NORM = 2,       /* RMSNorm of dt_low, B, C */
+  MM_STAGE_DTPROJ = 3,     /* dt_proj + bias + softplus */
+  MM_STAGE_SCAN = 4,       /* selective scan + D feed-through + SiLU(z) gate + final state */
+  MM_STAGE_CONV_STATE = 5, /* conv-state update (only when a conv state is given) */
+  MM_STAGE_COUNT = 6
+};
+typedef struct mm_stage_timer mm_stage_timer;
+MM_API mm_stage_timer *mm_stage_timer_create(void);
+MM_API void mm_stage_timer_destroy(mm_stage_timer *t);
+MM_API void mm_stage_timer_reset(mm_stage_timer *t);
+MM_API mm_status mm_stage_timer_read(mm_stage_timer *t, double *ms_sum, int64_t *launches);
+MM_API const char *mm_stage_name(int stage);
+
+MM_API mm_status mamba_mixer_prefill_timed(const mm_shape *s, const mm_params *p, const void *xz, void *y,
+                                    void *conv_state, float *ssm_state, int states_valid,
+                                    void *workspace, size_t workspace_bytes, void *stream,
+                                    mm_stage_timer *timer);
+MM_API mm_status mamba_mixer_decode_step_timed(const mm_shape *s, const mm_params *p, const void *xz,
+                                        void *y, void *conv_state, float *ssm_state,
+                                        void *workspace, size_t workspace_bytes, void *stream,
+                                        mm_stage_timer *timer);
+
+MM_API const char *mm_status_string(mm_status st);
+MM_API int mm_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MAMBA_MIXER_H */

@@ -1,0 +1,210 @@
+"""Python binding of the gfx950 Mamba-1 mixer-core library (libmamba_mixer.so).
+
+Argument marshalling only: every step of the mixer runs in the library's HIP kernels.
+torch supplies device memory (outputs and workspace are allocated with torch when the
+caller does not pass them) and the current HIP stream. There is no CPU fallback: when
+the library is missing, importing the entry points raises.
+
+    from mamba_selective_scan_02_amd import prefill, decode_step
+    y, conv_state, ssm_state = prefill(xz, params, return_states=True)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmamba_mixer.so")
+
+MM_OK, MM_ERR_INVALID_ARG, MM_ERR_UNSUPPORTED, MM_ERR_WORKSPACE, MM_ERR_HIP = 0, -1, -2, -3, -4
+MM_F32, MM_BF16 = 0, 1
+MM_FLAG_ZOH_B = 1
+STAGES = ("conv_silu", "x_proj", "rmsnorm", "dt_proj_softplus", "selective_scan", "conv_state")
+
+
+class MixerError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {_status_string(status)} ({status})")
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("seqlen", ctypes.c_int32),
+                ("d_inner", ctypes.c_int32), ("d_state", ctypes.c_int32),
+                ("d_conv", ctypes.c_int32), ("dt_rank", ctypes.c_int32),
+                ("io_dtype", ctypes.c_int), ("rms_eps", ctypes.c_float),
+                ("flags", ctypes.c_uint32)]
+
+
+class Params(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("conv_w", "conv_b", "x_proj_w", "dt_proj_w", "dt_proj_b", "A", "Dskip",
+                 "dt_norm_w", "B_norm_w", "C_norm_w")]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it has not been built (python -m ...build)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m mamba_selective_scan_02_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P, S, I, V, Z = ctypes.POINTER, Shape, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t
+        for name, args, res in [
+            ("mm_prefill_workspace_bytes", [P(S)], Z),
+            ("mm_decode_workspace_bytes", [P(S)], Z),
+            ("mamba_mixer_prefill", [P(S), P(Params), V, V, V, V, I, V, Z, V], I),
+            ("mamba_mixer_prefill_timed", [P(S), P(Params), V, V, V, V, I, V, Z, V, V], I),
+            ("mamba_mixer_decode_step", [P(S), P(Params), V, V, V, V, V, Z, V], I),
+            ("mamba_mixer_decode_step_timed", [P(S), P(Params), V, V, V, V, V, Z, V, V], I),
+            ("mm_stage_timer_create", [], V),
+            ("mm_stage_timer_destroy", [V], None),
+            ("mm_stage_timer_reset", [V], None),
+            ("mm_stage_timer_read", [V, P(ctypes.c_double), P(ctypes.c_int64)], I),
+            ("mm_stage_name", [I], ctypes.c_char_p),
+            ("mm_status_string", [I], ctypes.c_char_p),
+            ("mm_abi_version", [], I),
+        ]:
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = L
+    return _lib
+
+
+def _status_string(st: int) -> str:
+    try:
+        return lib().mm_status_string(st).decode()
+    except ImportError:
+        return "unknown"
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _io_code(dtype: torch.dtype) -> int:
+    if dtype == torch.bfloat16:
+        return MM_BF16
+    if dtype == torch.float32:
+        return MM_F32
+    raise TypeError(f"unsupported I/O dtype {dtype} (bfloat16 or float32)")
+
+
+def make_shape(batch, seqlen, d_inner, d_state, d_conv, dt_rank, dtype, eps=1e-6, flags=0) -> Shape:
+    return Shape(batch, seqlen, d_inner, d_state, d_conv, dt_rank, _io_code(dtype), eps, flags)
+
+
+def shape_of(xz: torch.Tensor, params: dict, *, decode=False, eps=1e-6, zoh=False) -> Shape:
+    if decode:
+        B, D2 = xz.shape
+        L = 1
+    else:
+        B, L, D2 = xz.shape
+    D = D2 // 2
+    N = params["A"].shape[1]
+    K = params["conv_w"].shape[1]
+    R = params["dt_proj_w"].shape[1]
+    return make_shape(B, L, D, N, K, R, xz.dtype, eps, MM_FLAG_ZOH_B if zoh else 0)
+
+
+def params_struct(params: dict) -> Params:
+    return Params(*[_ptr(params.get(n)) for n in
+                    ("conv_w", "conv_b", "x_proj_w", "dt_proj_w", "dt_proj_b", "A", "Dskip",
+                     "dt_norm_w", "B_norm_w", "C_norm_w")])
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def prefill_workspace_bytes(shape: Shape) -> int:
+    return int(lib().mm_prefill_workspace_bytes(ctypes.byref(shape)))
+
+
+def decode_workspace_bytes(shape: Shape) -> int:
+    return int(lib().mm_decode_workspace_bytes(ctypes.byref(shape)))
+
+
+def alloc_workspace(nbytes: int, device) -> torch.Tensor:
+    # torch's caching allocator returns 512-byte aligned blocks
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+
+
+class StageTimer:
+    """Per-stage HIP-event timer of the *_timed entry points (see mm_stage_timer_*)."""
+
+    def __init__(self):
+        self.h = lib().mm_stage_timer_create()
+
+    def reset(self):
+        lib().mm_stage_timer_reset(self.h)
+
+    def read(self) -> dict:
+        ms = (ctypes.c_double * len(STAGES))()
+        n = (ctypes.c_int64 * len(STAGES))()
+        st = lib().mm_stage_timer_read(self.h, ms, n)
+        if st != MM_OK:
+            raise MixerError(st, "mm_stage_timer_read")
+        return {STAGES[i]: (ms[i], n[i]) for i in range(len(STAGES))}
+
+    def __del__(self):
+        try:
+            if getattr(self, "h", None):
+                lib().mm_stage_timer_destroy(self.h)
+                self.h = None
+        except Exception:
+            pass
+
+
+def prefill(xz, params, *, conv_state=None, ssm_state=None, states_valid=False, y=None,
+            workspace=None, eps=1e-6, zoh=False, stream=None, timer: StageTimer | None = None):
+    """Run mamba_mixer_prefill. xz [B, L, 2D] (bf16 or fp32, on the GPU); conv_state
+    [B, D, K-1] and ssm_state [B, D, N] are updated in place when given. Returns y."""
+    shape = shape_of(xz, params, eps=eps, zoh=zoh)
+    if y is None:
+        y = torch.empty(xz.shape[:-1] + (shape.d_inner,), dtype=xz.dtype, device=xz.device)
+    need = prefill_workspace_bytes(shape)
+    if workspace is None:
+        workspace = alloc_workspace(need, xz.device)
+    p = params_struct(params)
+    args = (ctypes.byref(shape), ctypes.byref(p), _ptr(xz), _ptr(y), _ptr(conv_state),
+            _ptr(ssm_state), 1 if states_valid else 0, _ptr(workspace),
+            workspace.numel() * workspace.element_size(), _stream(stream))
+    if timer is None:
+        st = lib().mamba_mixer_prefill(*args)
+    else:
+        st = lib().mamba_mixer_prefill_timed(*args, timer.h)
+    if st != MM_OK:
+        raise MixerError(st, "mamba_mixer_prefill")
+    return y
+
+
+def decode_step(xz, params, conv_state, ssm_state, *, y=None, workspace=None, eps=1e-6,
+                zoh=False, stream=None, timer: StageTimer | None = None):
+    """Run mamba_mixer_decode_step on xz [B, 2D]; states are updated in place. Returns y [B, D]."""
+    shape = shape_of(xz, params, decode=True, eps=eps, zoh=zoh)
+    if y is None:
+        y = torch.empty((xz.shape[0], shape.d_inner), dtype=xz.dtype, device=xz.device)
+    need = decode_workspace_bytes(shape)
+    if workspace is None:
+        workspace = alloc_workspace(need, xz.device)
+    p = params_struct(params)
+    args = (ctypes.byref(shape), ctypes.byref(p), _ptr(xz), _ptr(y), _ptr(conv_state),
+            _ptr(ssm_state), _ptr(workspace), workspace.numel() * workspace.element_size(),
+            _stream(stream))
+    if timer is None:
+        st = lib().mamba_mixer_decode_step(*args)
+    else:
+        st = lib().mamba_mixer_decode_step_timed(*args, timer.h)
+    if st != MM_OK:
+        raise MixerError(st, "mamba_mixer_decode_step")
+    return y

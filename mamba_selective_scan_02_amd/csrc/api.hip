@@ -1,0 +1,299 @@
+// C ABI of the mixer library: argument validation, workspace layout, stage sequencing and
+// the per-stage timer. Declarations and contracts: include/mamba_mixer.h.
+#include <vector>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace {
+
+using namespace mm;
+
+constexpr size_t kAlign = 256;
+inline size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+inline size_t esz(mm_dtype d) { return d == MM_BF16 ? 2 : 4; }
+
+struct Workspace {
+  size_t u, u_lo, xdbl, dtlow, dtlow_lo, bc, dt, total;
+};
+
+// Byte offsets of the prefill intermediates for T = batch * seqlen tokens.
+//   fp32 mode: u [T,D] f32 | xdbl [T,R+2N] f32 | dt_low [T,R] f32 | B,C [T,2N] f32 | dt [T,D] f32
+//   bf16 mode: u_hi, u_lo [T,D] bf16 | xdbl f32 | dt_low hi, lo [T,R] bf16 | B,C f32 | dt [T,D] f16
+Workspace layout(const mm_shape &s) {
+  const size_t T = (size_t)s.batch * s.seqlen;
+  const bool bf = s.io_dtype == MM_BF16;
+  const size_t e = esz(s.io_dtype);
+  Workspace w;
+  size_t o = 0;
+  w.u = o; o += up(T * s.d_inner * e);
+  w.u_lo = o; if (bf) o += up(T * s.d_inner * 2);
+  w.xdbl = o; o += up(T * (s.dt_rank + 2 * s.d_state) * 4);
+  w.dtlow = o; o += up(T * s.dt_rank * e);
+  w.dtlow_lo = o; if (bf) o += up(T * s.dt_rank * 2);
+  w.bc = o; o += up(T * 2 * s.d_state * 4);
+  w.dt = o; o += up(T * s.d_inner * (bf ? 2 : 4));
+  w.total = o;
+  return w;
+}
+
+bool aligned(const void *p) { return ((uintptr_t)p & 15) == 0; }
+
+mm_status check_shape(const mm_shape *s, bool decode) {
+  if (!s) return MM_ERR_INVALID_ARG;
+  if (s->batch <= 0 || s->seqlen <= 0 || s->d_inner <= 0 || s->d_state <= 0 || s->d_conv <= 0 ||
+      s->dt_rank <= 0 || !(s->rms_eps > 0.0f))
+    return MM_ERR_INVALID_ARG;
+  if (s->io_dtype != MM_F32 && s->io_dtype != MM_BF16) return MM_ERR_INVALID_ARG;
+  if (s->flags & ~(uint32_t)MM_FLAG_ZOH_B) return MM_ERR_INVALID_ARG;
+  if (decode && s->seqlen != 1) return MM_ERR_INVALID_ARG;
+  if (s->d_state != 16 || s->d_conv < 2 || s->d_conv > 4 || s->d_inner % 64 != 0)
+    return MM_ERR_UNSUPPORTED;
+  if (s->io_dtype == MM_BF16 && (s->dt_rank % 64 != 0 || s->d_inner % 128 != 0))
+    return MM_ERR_UNSUPPORTED;
+  if (s->io_dtype == MM_F32 && s->dt_rank > 1024) return MM_ERR_UNSUPPORTED;
+  // index arithmetic inside kernels uses 64-bit offsets, grid sizes 32-bit counts
+  const double T = (double)s->batch * s->seqlen;
+  if (T * s->d_inner / 8 > 2e9) return MM_ERR_UNSUPPORTED;
+  return MM_OK;
+}
+
+mm_status check_params(const mm_params *p) {
+  if (!p) return MM_ERR_INVALID_ARG;
+  const void *req[] = {p->conv_w, p->x_proj_w, p->dt_proj_w, p->dt_proj_b, p->A,
+                       p->Dskip,  p->dt_norm_w, p->B_norm_w, p->C_norm_w};
+  for (const void *q : req)
+    if (!q || !aligned(q)) return MM_ERR_INVALID_ARG;
+  if (p->conv_b && !aligned(p->conv_b)) return MM_ERR_INVALID_ARG;
+  return MM_OK;
+}
+
+}  // namespace
+
+struct mm_stage_timer {
+  struct Rec {
+    int stage;
+    hipEvent_t a, b;
+  };
+  std::vector<hipEvent_t> pool;
+  std::vector<Rec> recs;
+  hipEvent_t get() {
+    if (!pool.empty()) {
+      hipEvent_t e = pool.back();
+      pool.pop_back();
+      return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+  }
+};
+
+namespace {
+
+// Brackets one stage with a pair of events when a timer is given.
+struct StageScope {
+  mm_stage_timer *t;
+  hipStream_t s;
+  mm_stage_timer::Rec rec{};
+  StageScope(mm_stage_timer *t_, hipStream_t s_, int stage) : t(t_), s(s_) {
+    if (!t) return;
+    rec.stage = stage;
+    rec.a = t->get();
+    rec.b = t->get();
+    if (rec.a) hipEventRecord(rec.a, s);
+  }
+  ~StageScope() {
+    if (!t || !rec.a || !rec.b) return;
+    hipEventRecord(rec.b, s);
+    t->recs.push_back(rec);
+  }
+};
+
+#define MM_TRY(expr)                                   \
+  do {                                                 \
+    if ((expr) != hipSuccess) return MM_ERR_HIP;       \
+  } while (0)
+
+mm_status run_mixer(const mm_shape *s, const mm_params *p, const void *xz, void *y,
+                    void *conv_state, float *ssm_state, int states_valid, void *workspace,
+                    size_t workspace_bytes, hipStream_t st, mm_stage_timer *timer) {
+  const Workspace w = layout(*s);
+  char *ws = (char *)workspace;
+  const int B = s->batch, L = s->seqlen, D = s->d_inner, N = s->d_state, K = s->d_conv;
+  const int R = s->dt_rank, T = B * L;
+  const mm_dtype dt = s->io_dtype;
+  void *u = ws + w.u;
+  void *u_lo = ws + w.u_lo;
+  float *xdbl = (float *)(ws + w.xdbl);
+  void *dtlow = ws + w.dtlow;
+  void *dtlow_lo = ws + w.dtlow_lo;
+  float *bc = (float *)(ws + w.bc);
+  void *delta = ws + w.dt;
+  (void)workspace_bytes;
+  const int conv_valid = states_valid && conv_state != nullptr;
+
+  ConvArgs ca{xz, u, u_lo, p->conv_w, p->conv_b, conv_state, conv_valid, B, L, D, K};
+  {
+    StageScope sc(timer, st, MM_STAGE_CONV);
+    MM_TRY(launch_conv_silu(dt, ca, st));
+  }
+  {
+    StageScope sc(timer, st, MM_STAGE_XPROJ);
+    MM_TRY(launch_xproj(dt, u, u_lo, p->x_proj_w, xdbl, T, D, R + 2 * N, st));
+  }
+  {
+    StageScope sc(timer, st, MM_STAGE_NORM);
+    MM_TRY(launch_norm(dt, xdbl, dtlow, dtlow_lo, bc, p->dt_norm_w, p->B_norm_w, p->C_norm_w, T,
+                       R, N, s->rms_eps, st));
+  }
+  {
+    StageScope sc(timer, st, MM_STAGE_DTPROJ);
+    MM_TRY(launch_dtproj(dt, dtlow, dtlow_lo, p->dt_proj_w, p->dt_proj_b, delta, T, D, R, st));
+  }
+  {
+    StageScope sc(timer, st, MM_STAGE_SCAN);
+    ScanArgs sa{xz, p->conv_w, p->conv_b, conv_state, conv_valid, K, delta, bc, p->A, p->Dskip,
+                y, ssm_state, states_valid && ssm_state != nullptr,
+                (s->flags & MM_FLAG_ZOH_B) ? 1 : 0, B, L, D, N};
+    MM_TRY(launch_scan(dt, sa, st));
+  }
+  if (conv_state) {
+    // last: the conv and scan kernels above read the carried conv state
+    StageScope sc(timer, st, MM_STAGE_CONV_STATE);
+    MM_TRY(launch_conv_state_update(dt, ca, conv_state, st));
+  }
+  return MM_OK;
+}
+
+mm_status prefill_impl(const mm_shape *s, const mm_params *p, const void *xz, void *y,
+                       void *conv_state, float *ssm_state, int states_valid, void *workspace,
+                       size_t workspace_bytes, void *stream, mm_stage_timer *timer) {
+  mm_status r = check_shape(s, false);
+  if (r != MM_OK) return r;
+  if ((r = check_params(p)) != MM_OK) return r;
+  if (!xz || !y || !aligned(xz) || !aligned(y) || xz == y) return MM_ERR_INVALID_ARG;
+  if ((conv_state && !aligned(conv_state)) || (ssm_state && !aligned(ssm_state)))
+    return MM_ERR_INVALID_ARG;
+  if (states_valid != 0 && states_valid != 1) return MM_ERR_INVALID_ARG;
+  if (!workspace || ((uintptr_t)workspace & (kAlign - 1)) ||
+      workspace_bytes < layout(*s).total)
+    return MM_ERR_WORKSPACE;
+  return run_mixer(s, p, xz, y, conv_state, ssm_state, states_valid, workspace, workspace_bytes,
+                   (hipStream_t)stream, timer);
+}
+
+mm_status decode_impl(const mm_shape *s, const mm_params *p, const void *xz, void *y,
+                      void *conv_state, float *ssm_state, void *workspace, size_t workspace_bytes,
+                      void *stream, mm_stage_timer *timer) {
+  mm_status r = check_shape(s, true);
+  if (r != MM_OK) return r;
+  if ((r = check_params(p)) != MM_OK) return r;
+  if (!xz || !y || !conv_state || !ssm_state || xz == y) return MM_ERR_INVALID_ARG;
+  if (!aligned(xz) || !aligned(y) || !aligned(conv_state) || !aligned(ssm_state))
+    return MM_ERR_INVALID_ARG;
+  if (!workspace || ((uintptr_t)workspace & (kAlign - 1)) ||
+      workspace_bytes < layout(*s).total)
+    return MM_ERR_WORKSPACE;
+  return run_mixer(s, p, xz, y, conv_state, ssm_state, 1, workspace, workspace_bytes,
+                   (hipStream_t)stream, timer);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t mm_prefill_workspace_bytes(const mm_shape *s) {
+  if (check_shape(s, false) != MM_OK) return 0;
+  return layout(*s).total;
+}
+
+size_t mm_decode_workspace_bytes(const mm_shape *s) {
+  if (check_shape(s, true) != MM_OK) return 0;
+  return layout(*s).total;
+}
+
+mm_status mamba_mixer_prefill(const mm_shape *s, const mm_params *p, const void *xz, void *y,
+                              void *conv_state, float *ssm_state, int states_valid,
+                              void *workspace, size_t workspace_bytes, void *stream) {
+  return prefill_impl(s, p, xz, y, conv_state, ssm_state, states_valid, workspace,
+                      workspace_bytes, stream, nullptr);
+}
+
+mm_status mamba_mixer_prefill_timed(const mm_shape *s, const mm_params *p, const void *xz, void *y,
+                                    void *conv_state, float *ssm_state, int states_valid,
+                                    void *workspace, size_t workspace_bytes, void *stream,
+                                    mm_stage_timer *timer) {
+  return prefill_impl(s, p, xz, y, conv_state, ssm_state, states_valid, workspace,
+                      workspace_bytes, stream, timer);
+}
+
+mm_status mamba_mixer_decode_step(const mm_shape *s, const mm_params *p, const void *xz, void *y,
+                                  void *conv_state, float *ssm_state, void *workspace,
+                                  size_t workspace_bytes, void *stream) {
+  return decode_impl(s, p, xz, y, conv_state, ssm_state, workspace, workspace_bytes, stream,
+                     nullptr);
+}
+
+mm_status mamba_mixer_decode_step_timed(const mm_shape *s, const mm_params *p, const void *xz,
+                                        void *y, void *conv_state, float *ssm_state,
+                                        void *workspace, size_t workspace_bytes, void *stream,
+                                        mm_stage_timer *timer) {
+  return decode_impl(s, p, xz, y, conv_state, ssm_state, workspace, workspace_bytes, stream,
+                     timer);
+}
+
+mm_stage_timer *mm_stage_timer_create(void) { return new mm_stage_timer(); }
+
+void mm_stage_timer_reset(mm_stage_timer *t) {
+  if (!t) return;
+  for (auto &r : t->recs) {
+    t->pool.push_back(r.a);
+    t->pool.push_back(r.b);
+  }
+  t->recs.clear();
+}
+
+void mm_stage_timer_destroy(mm_stage_timer *t) {
+  if (!t) return;
+  mm_stage_timer_reset(t);
+  for (hipEvent_t e : t->pool) hipEventDestroy(e);
+  delete t;
+}
+
+mm_status mm_stage_timer_read(mm_stage_timer *t, double *ms_sum, int64_t *launches) {
+  if (!t || !ms_sum || !launches) return MM_ERR_INVALID_ARG;
+  for (int i = 0; i < MM_STAGE_COUNT; ++i) {
+    ms_sum[i] = 0.0;
+    launches[i] = 0;
+  }
+  for (auto &r : t->recs) {
+    if (hipEventSynchronize(r.b) != hipSuccess) return MM_ERR_HIP;
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess) return MM_ERR_HIP;
+    ms_sum[r.stage] += ms;
+    launches[r.stage] += 1;
+  }
+  return MM_OK;
+}
+
+const char *mm_stage_name(int stage) {
+  static const char *names[MM_STAGE_COUNT] = {"conv_silu", "x_proj", "rmsnorm", "dt_proj_softplus",
+                                              "selective_scan", "conv_state"};
+  return (stage >= 0 && stage < MM_STAGE_COUNT) ? names[stage] : "unknown";
+}
+
+const char *mm_status_string(mm_status st) {
+  switch (st) {
+    case MM_OK: return "ok";
+    case MM_ERR_INVALID_ARG: return "invalid argument";
+    case MM_ERR_UNSUPPORTED: return "unsupported size";
+    case MM_ERR_WORKSPACE: return "workspace missing or too small";
+    case MM_ERR_HIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+int mm_abi_version(void) { return MM_ABI_VERSION; }
+
+}  // extern "C"

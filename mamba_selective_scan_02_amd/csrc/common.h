@@ -1,0 +1,66 @@
+// Shared device/host helpers of the gfx950 mixer library (internal; not part of the ABI).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mm {
+
+typedef uint16_t bf16_t;  // bfloat16 bits
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// ---------------------------------------------------------------- element conversion
+__device__ __forceinline__ float bf2f(bf16_t v) { return __uint_as_float(((uint32_t)v) << 16); }
+// round-to-nearest-even (lowers to v_cvt_pk_bf16_f32 on gfx950)
+__device__ __forceinline__ bf16_t f2bf(float f) {
+  __bf16 h = (__bf16)f;
+  return __builtin_bit_cast(bf16_t, h);
+}
+__device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
+  return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+}
+__device__ __forceinline__ float lo_bf(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi_bf(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+template <typename T> struct io;
+template <> struct io<float> {
+  static __device__ __forceinline__ float ld(const float *p) { return *p; }
+  static __device__ __forceinline__ void st(float *p, float v) { *p = v; }
+  static __device__ __forceinline__ float cvt(float v) { return v; }
+};
+template <> struct io<bf16_t> {
+  static __device__ __forceinline__ float ld(const bf16_t *p) { return bf2f(*p); }
+  static __device__ __forceinline__ void st(bf16_t *p, float v) { *p = f2bf(v); }
+  static __device__ __forceinline__ float cvt(bf16_t v) { return bf2f(v); }
+};
+
+// ---------------------------------------------------------------- math
+// exp via the hardware base-2 exponential (v_exp_f32)
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+// SiLU(v) = v / (1 + e^-v); e^-v overflowing to +inf gives v * 0 = -0 for very negative v.
+__device__ __forceinline__ float silu_f(float v) {
+  return v * __builtin_amdgcn_rcpf(1.0f + exp2_hw(-v * kLog2e));
+}
+// softplus(v) = log(1 + e^v); above 20 it equals v to within 2e-9 relative.
+__device__ __forceinline__ float softplus_f(float v) {
+  return v > 20.0f ? v : log1pf(expf(v));
+}
+
+// ---------------------------------------------------------------- launch geometry
+// Workgroup i runs on XCD (i mod 8). Map hardware ids so that logical ids
+// [k*per, (k+1)*per) all run on XCD k in dispatch order: neighbouring tiles that
+// share operands then share one L2.
+__device__ __forceinline__ int xcd_remap(int i, int G) {
+  const int per = G >> 3;
+  const int full = per << 3;
+  if (i >= full) return i;
+  return (i & 7) * per + (i >> 3);
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+}  // namespace mm

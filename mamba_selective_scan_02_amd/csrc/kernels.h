@@ -1,0 +1,59 @@
+// Host-side launchers of the mixer's kernels (internal; the ABI is include/mamba_mixer.h).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/mamba_mixer.h"
+
+namespace mm {
+
+struct ConvArgs {
+  const void *xz;       // [B, L, 2D]; x = first D columns
+  void *u;              // [B, L, D]: fp32 u (fp32 mode) or its bf16 high part (bf16 mode)
+  void *u_lo;           // [B, L, D]: bf16 mode only, bf16(u - high part)
+  const void *w;        // [D, K]
+  const void *bias;     // [D] or null
+  const void *state;    // [B, D, K-1] or null
+  int state_valid;
+  int B, L, D, K;
+};
+hipError_t launch_conv_silu(mm_dtype dt, const ConvArgs &a, hipStream_t s);
+// Rewrites state[b, i, :] with the last K-1 inputs; runs after every kernel that reads it.
+hipError_t launch_conv_state_update(mm_dtype dt, const ConvArgs &a, void *state_out, hipStream_t s);
+
+// xdbl[T, Nx] (fp32) = u[T, D] . W[Nx, D]^T. bf16 mode: u = u_hi + u_lo, two MFMA passes.
+hipError_t launch_xproj(mm_dtype dt, const void *u, const void *u_lo, const void *w, float *xdbl,
+                        int T, int D, int Nx, hipStream_t s);
+
+// Per token: dt_low = RMSNorm(xdbl[:, :R]) -> dtlow [T, R] (fp32 mode: fp32; bf16 mode: bf16
+// high part in dtlow, bf16 low part in dtlow_lo); B, C = RMSNorm of the next two N-slices ->
+// bc [T, 2N] (fp32).
+hipError_t launch_norm(mm_dtype dt, const float *xdbl, void *dtlow, void *dtlow_lo, float *bc,
+                       const float *g_dt, const float *g_B, const float *g_C, int T, int R, int N,
+                       float eps, hipStream_t s);
+
+// dt[T, D] = softplus(dtlow[T, R] . Wdt[D, R]^T + bias); fp32 out (fp32 mode) or fp16 out
+// (bf16 mode, where dtlow = hi + lo takes two MFMA passes).
+hipError_t launch_dtproj(mm_dtype dt, const void *dtlow, const void *dtlow_lo, const void *w,
+                         const float *bias, void *dtout, int T, int D, int R, hipStream_t s);
+
+struct ScanArgs {
+  const void *xz;       // [B, L, 2D]; x = first D columns (conv input), z = last D (gate)
+  const void *conv_w;   // [D, K] io dtype
+  const void *conv_b;   // [D] io dtype or null
+  const void *conv_state;  // [B, D, K-1] io dtype or null (read before it is updated)
+  int conv_valid;
+  int K;
+  const void *delta;    // [B, L, D]: fp32 (fp32 mode) or fp16 (bf16 mode)
+  const float *bc;      // [B*L, 2N]: B then C per token
+  const float *A;       // [D, N]
+  const float *Dskip;   // [D]
+  void *y;              // [B, L, D]
+  float *state;         // [B, D, N] or null
+  int state_valid;
+  int zoh;
+  int B, L, D, N;
+};
+hipError_t launch_scan(mm_dtype dt, const ScanArgs &a, hipStream_t s);
+
+}  // namespace mm

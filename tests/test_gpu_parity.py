@@ -1,0 +1,145 @@
+"""GPU parity: the HIP library (through its C ABI) against the fp64 oracle, element by
+element, on the same seeded inputs. Sizes here finish in seconds on the oracle while
+spanning several tiles of every kernel and a ragged tail; the full workload sizes are in
+test_gpu_fullsize.py."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from tests.parity import check, to64
+
+pytestmark = pytest.mark.gpu
+
+mm = pytest.importorskip("mamba_selective_scan_02_amd")
+
+
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _case(cfg, seed, *, states=False, conv_bias=False, gamma_random=False, zoh=False,
+          channels=None, check_y=True):
+    _need_gpu()
+    print(f"[case] {cfg.name} B={cfg.batch} L={cfg.seqlen} D={cfg.d_inner} R={cfg.dt_rank} "
+          f"io={cfg.io_dtype} seed={seed} states={states} bias={conv_bias} zoh={zoh}", flush=True)
+    dev = "cuda"
+    p = synth.make_params(cfg, seed, dev, conv_bias=conv_bias, gamma_random=gamma_random)
+    xz = synth.make_xz(cfg, seed, dev)
+    if states:
+        cs, ss = synth.make_states(cfg, seed, dev)
+    else:
+        cs = torch.zeros(cfg.batch, cfg.d_inner, cfg.d_conv - 1, dtype=cfg.torch_dtype, device=dev)
+        ss = torch.zeros(cfg.batch, cfg.d_inner, cfg.d_state, dtype=torch.float32, device=dev)
+    cs_in, ss_in = cs.clone(), ss.clone()
+    y = mm.prefill(xz, p, conv_state=cs, ssm_state=ss, states_valid=states, eps=cfg.rms_eps,
+                   zoh=zoh)
+    torch.cuda.synchronize()
+    yr, csr, ssr = oracle.mixer_prefill(
+        to64(xz), oracle.as_f64_params(p), to64(cs_in) if states else None,
+        to64(ss_in) if states else None, eps=cfg.rms_eps, zoh=zoh, channels=channels)
+    sel = slice(None) if channels is None else channels
+    errs = {}
+    if check_y:
+        errs["y"] = check(y[:, :, sel], yr, cfg.io_dtype, "y")
+    errs["ssm_state"] = check(ss[:, sel], ssr, cfg.io_dtype, "ssm_state")
+    np.testing.assert_array_equal(to64(cs), csr)
+    print(f"[case] errors {errs}", flush=True)
+    return y, cs, ss
+
+
+TINY = synth.CONFIGS["tiny_f32"]
+
+
+def test_tiny_f32_zero_states():
+    _case(TINY, synth.seed_for("tiny_f32"))
+
+
+def test_tiny_f32_carried_states_bias_gamma():
+    _case(TINY, 7, states=True, conv_bias=True, gamma_random=True)
+
+
+def test_tiny_f32_zoh():
+    _case(TINY, 8, states=True, zoh=True)
+
+
+@pytest.mark.parametrize("L", [1, 2, 3, 77])
+def test_f32_ragged_and_short_sequences(L):
+    _case(TINY.with_(batch=3, seqlen=L, name=f"f32_L{L}"), 20 + L, states=True, conv_bias=True)
+
+
+def test_f32_d_conv_variants():
+    for K in (2, 3):
+        _case(TINY.with_(d_conv=K, seqlen=50, name=f"f32_K{K}"), 30 + K, states=True)
+
+
+BF16_SMALL = synth.MixerConfig("bf16_small", 2, 300, 256, 16, 4, 64, "bf16")
+
+
+def test_bf16_small_ragged_tiles():
+    _case(BF16_SMALL, 41, states=True, conv_bias=True, gamma_random=True)
+
+
+def test_bf16_small_zero_states_zoh():
+    _case(BF16_SMALL, 42, zoh=True)
+
+
+@pytest.mark.parametrize("L", [1, 2, 129])
+def test_bf16_short_sequences(L):
+    _case(BF16_SMALL.with_(seqlen=L, name=f"bf16_L{L}"), 50 + L, states=True)
+
+
+def test_bf16_mini_prefill_4k_full():
+    cfg = synth.CONFIGS["mini_prefill_4k"]
+    _case(cfg, synth.seed_for("mini_prefill_4k"))
+
+
+def test_chunked_prefill_equals_whole_on_gpu_and_oracle():
+    """Prefill over L1 tokens, then L2 more from the returned states, equals one prefill
+    (associativity of the page's scan operator); checked against the oracle."""
+    _need_gpu()
+    cfg = BF16_SMALL.with_(seqlen=257, name="bf16_chunked")
+    dev = "cuda"
+    p = synth.make_params(cfg, 61, dev, conv_bias=True)
+    xz = synth.make_xz(cfg, 61, dev)
+    cs0, ss0 = synth.make_states(cfg, 61, dev)
+    cs, ss = cs0.clone(), ss0.clone()
+    y1 = mm.prefill(xz[:, :100].contiguous(), p, conv_state=cs, ssm_state=ss, states_valid=True)
+    y2 = mm.prefill(xz[:, 100:].contiguous(), p, conv_state=cs, ssm_state=ss, states_valid=True)
+    torch.cuda.synchronize()
+    yr, csr, ssr = oracle.mixer_prefill(to64(xz), oracle.as_f64_params(p), to64(cs0), to64(ss0))
+    check(torch.cat([y1, y2], dim=1), yr, "bf16", "y (chunked)")
+    check(ss, ssr, "bf16", "ssm_state (chunked)")
+    np.testing.assert_array_equal(to64(cs), csr)
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_decode_steps_match_oracle(io):
+    _need_gpu()
+    cfg = (TINY if io == "f32" else BF16_SMALL).with_(batch=4, seqlen=1, name=f"decode_{io}")
+    dev = "cuda"
+    p = synth.make_params(cfg, 71, dev, conv_bias=True)
+    cs, ss = synth.make_states(cfg, 71, dev)
+    csr, ssr = to64(cs), to64(ss)
+    p64 = oracle.as_f64_params(p)
+    for step in range(6):
+        xt = synth.make_xz(cfg, 71, dev, seqlen=1, tensor="decode_xz", step=step)[:, 0]
+        y = mm.decode_step(xt, p, cs, ss)
+        torch.cuda.synchronize()
+        yr, csr, ssr = oracle.mixer_decode_step(to64(xt), p64, csr, ssr)
+        check(y, yr, io, f"y step {step}")
+        check(ss, ssr, io, f"ssm_state step {step}")
+        np.testing.assert_array_equal(to64(cs), csr)
+
+
+def test_outputs_are_deterministic():
+    _need_gpu()
+    cfg = BF16_SMALL
+    p = synth.make_params(cfg, 81, "cuda")
+    xz = synth.make_xz(cfg, 81, "cuda")
+    y1 = mm.prefill(xz, p)
+    y2 = mm.prefill(xz, p)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
