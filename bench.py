@@ -1,0 +1,198 @@
+"""Benchmark of the gfx950 Mamba-1 mixer core on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-decode]
+
+One step = one mamba_mixer_prefill over the long-context workload (B=1, L=131072,
+d_inner=8192, d_state=16, d_conv=4, dt_rank=256, bf16 I/O, fp32 state): conv1d+SiLU,
+x_proj, RMSNorm, dt_proj+softplus, selective scan with D feed-through and SiLU(z) gate,
+final conv/SSM states. Inputs are synthetic, seeded, resident in HBM before timing.
+The decode leg times 512 batched decode steps (B=256, d_inner=8192) after a 1024-token
+prefill seeds the states. Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+
+PREFILL_WORKLOAD = "long_prefill_128k"
+DECODE_WORKLOAD = "decode_b256"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor peak
+CU, CLOCK_HZ, LANES = 256, 2.4e9, 64
+
+
+def scan_alu_peak_updates_per_s() -> float:
+    """ALU roofline of the selective scan in state updates (token, channel, state) per second.
+    Each update needs 4 full-rate fp32 VALU issue slots (dt*A, (dt*u)*B, the h FMA, the y FMA)
+    plus one v_exp_f32, which issues at half rate on gfx950 (2 slots): 6 slots per update;
+    the chip issues 64 lanes x 256 CUs x 2.4 GHz slots per second."""
+    return LANES * CU * CLOCK_HZ / 6.0
+
+
+def scan_algorithmic_bytes(cfg) -> int:
+    """Bytes the scan kernel must move per launch: read x and z (the two halves of xz, bf16),
+    dt (fp16), B and C (fp32, 2N per token); write y (bf16); plus the SSM state in/out."""
+    T, D, N = cfg.batch * cfg.seqlen, cfg.d_inner, cfg.d_state
+    return T * D * (2 + 2 + 2 + 2) + T * 2 * N * 4 + 2 * cfg.batch * D * N * 4
+
+
+def prefill_leg(args, mm):
+    cfg = synth.CONFIGS[PREFILL_WORKLOAD]
+    seed = synth.seed_for(PREFILL_WORKLOAD)
+    dev = "cuda"
+    p = synth.make_params(cfg, seed, dev)
+    xz = synth.make_xz(cfg, seed, dev)
+    y = torch.empty(cfg.batch, cfg.seqlen, cfg.d_inner, dtype=cfg.torch_dtype, device=dev)
+    cs = torch.zeros(cfg.batch, cfg.d_inner, cfg.d_conv - 1, dtype=cfg.torch_dtype, device=dev)
+    ss = torch.zeros(cfg.batch, cfg.d_inner, cfg.d_state, dtype=torch.float32, device=dev)
+    shape = mm.shape_of(xz, p, eps=cfg.rms_eps)
+    ws = mm.alloc_workspace(mm.prefill_workspace_bytes(shape), dev)
+    timer = mm.StageTimer()
+
+    def step(t=None):
+        mm.prefill(xz, p, conv_state=cs, ssm_state=ss, states_valid=False, y=y, workspace=ws,
+                   eps=cfg.rms_eps, timer=t)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    timer.reset()
+    print(f"[bench] prefill {PREFILL_WORKLOAD}: {args.warmup} warmup done, timing {args.steps}",
+          file=sys.stderr, flush=True)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(timer)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    stages = timer.read()
+    ms_per_step = wall * 1e3 / args.steps
+    tokens = cfg.batch * cfg.seqlen
+    scan_ms, scan_n = stages["selective_scan"]
+    scan_avg_s = scan_ms / max(scan_n, 1) * 1e-3
+    updates = tokens * cfg.d_inner * cfg.d_state
+    peak = scan_alu_peak_updates_per_s()
+    achieved = updates / scan_avg_s
+    sbytes = scan_algorithmic_bytes(cfg)
+    out = {
+        "value": tokens / (ms_per_step * 1e-3),
+        "ms_per_step": ms_per_step,
+        "config": {"workload": PREFILL_WORKLOAD, "batch": cfg.batch, "seq_len": cfg.seqlen,
+                   "d_inner": cfg.d_inner, "d_state": cfg.d_state, "d_conv": cfg.d_conv,
+                   "dt_rank": cfg.dt_rank, "io_dtype": "bf16", "state_dtype": "f32"},
+        "roofline": {"bound": "alu", "kernel": "selective_scan", "achieved": achieved,
+                     "peak": peak, "unit": "state-updates/s", "frac": achieved / peak,
+                     "traffic": None,
+                     "hbm_view": {"algorithmic_bytes": sbytes,
+                                  "achieved_GBs": sbytes / scan_avg_s / 1e9,
+                                  "peak_GBs": HBM_PEAK_GBS,
+                                  "frac": sbytes / scan_avg_s / 1e9 / HBM_PEAK_GBS}},
+        "stages_ms_per_step": {k: v[0] / max(v[1], 1) for k, v in stages.items() if v[1]},
+    }
+    return out, (xz, p, cfg)
+
+
+def decode_leg(args, mm):
+    cfg = synth.CONFIGS[DECODE_WORKLOAD]
+    seed = synth.seed_for(DECODE_WORKLOAD)
+    dev = "cuda"
+    p = synth.make_params(cfg, seed, dev)
+    cs = torch.zeros(cfg.batch, cfg.d_inner, cfg.d_conv - 1, dtype=cfg.torch_dtype, device=dev)
+    ss = torch.zeros(cfg.batch, cfg.d_inner, cfg.d_state, dtype=torch.float32, device=dev)
+    # seeded random prefill of 1024 tokens per sequence gives the carried states
+    pre = synth.make_xz(cfg, seed, dev, seqlen=cfg.decode_prefix)
+    mm.prefill(pre, p, conv_state=cs, ssm_state=ss, states_valid=False, eps=cfg.rms_eps)
+    del pre
+    steps = cfg.decode_steps
+    xs = synth.make_xz(cfg, seed, dev, seqlen=steps, tensor="decode_xz")  # [B, steps, 2D]
+    xs = xs.transpose(0, 1).contiguous()                                   # [steps, B, 2D]
+    y = torch.empty(cfg.batch, cfg.d_inner, dtype=cfg.torch_dtype, device=dev)
+    shape = mm.shape_of(xs[0], p, decode=True, eps=cfg.rms_eps)
+    ws = mm.alloc_workspace(mm.decode_workspace_bytes(shape), dev)
+    timer = mm.StageTimer()
+    for i in range(min(8, steps)):
+        mm.decode_step(xs[i], p, cs, ss, y=y, workspace=ws, eps=cfg.rms_eps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        mm.decode_step(xs[i], p, cs, ss, y=y, workspace=ws, eps=cfg.rms_eps, timer=timer)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    stages = timer.read()
+    # state read + write (fp32), conv state read + write, xz in, y out, weights once per step
+    D, N, K, R, B = cfg.d_inner, cfg.d_state, cfg.d_conv, cfg.dt_rank, cfg.batch
+    step_bytes = (B * D * N * 4 * 2 + B * D * (K - 1) * 2 * 2 + B * 2 * D * 2 + B * D * 2
+                  + (R + 2 * N) * D * 2 + D * R * 2)
+    return {"metric": "decode steps/sec", "value": steps / wall, "unit": "steps/s",
+            "tokens_per_s": steps * B / wall, "ms_per_step": wall * 1e3 / steps,
+            "workload": DECODE_WORKLOAD, "batch": B, "d_inner": D, "steps": steps,
+            "hbm_frac_of_step": step_bytes / (wall / steps) / 1e9 / HBM_PEAK_GBS,
+            "algorithmic_bytes_per_step": step_bytes,
+            "stages_ms_per_step": {k: v[0] / max(v[1], 1) for k, v in stages.items() if v[1]}}
+
+
+def cpu_baseline(xz, p, cfg, tokens: int):
+    """The fp64 oracle, as it stands, on the first `tokens` tokens of the same workload."""
+    import numpy as np
+    import threadpoolctl
+    import oracle
+    x = xz[:, :tokens].float().cpu().double().numpy()
+    p64 = oracle.as_f64_params(p)
+    info = threadpoolctl.threadpool_info()
+    blas_threads = max([i.get("num_threads", 1) for i in info] or [1])
+    t0 = time.perf_counter()
+    oracle.mixer_prefill(x, p64, eps=cfg.rms_eps)
+    dt = time.perf_counter() - t0
+    del np
+    return {"value": tokens * cfg.batch / dt, "unit": "tokens/s", "cores": blas_threads,
+            "kind": "oracle",
+            "sample": (f"first {tokens} tokens of the {PREFILL_WORKLOAD} input, all "
+                       f"{cfg.d_inner} channels, fp64 numpy ({dt:.1f} s; matmuls on "
+                       f"{blas_threads} BLAS threads, elementwise steps on 1 thread)")}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--cpu-tokens", type=int, default=4096)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    import mamba_selective_scan_02_amd as mm
+    mm.lib()  # fails loudly when the HIP library is missing
+    pre, (xz, p, cfg) = prefill_leg(args, mm)
+    line = {"metric": "mixer prefill tokens/sec at L=128K (+ decode steps/sec; % HBM peak)",
+            "value": pre["value"], "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": pre["ms_per_step"], "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+            "data": "synthetic (seeded; Jamba-Mini-shaped widths, random weights)",
+            "config": pre["config"], "roofline": pre["roofline"],
+            "stages_ms_per_step": pre["stages_ms_per_step"]}
+    if not args.no_decode:
+        print("[bench] decode leg", file=sys.stderr, flush=True)
+        line["decode"] = decode_leg(args, mm)
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(xz, p, cfg, args.cpu_tokens)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
