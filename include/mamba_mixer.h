@@ -71,7 +71,12 @@ typedef enum { MM_F32 = 0, MM_BF16 = 1 } mm_dtype;
 enum {
   /* Use the ZOH input matrix of the page's ZOH equation, Bbar = expm1(dt A) / A * B,
      instead of the first-order Bbar = dt * B (the default). */
-  MM_FLAG_ZOH_B = 1u << 0
+  MM_FLAG_ZOH_B = 1u << 0,
+  /* Scan kernel selection (results agree to fp32 rounding; at most one may be set).
+     Default: the time-parallel kernel when batch * d_inner / 64 < 2048 and seqlen > 128,
+     else the sequential one. */
+  MM_FLAG_SCAN_SEQUENTIAL = 1u << 1,  /* one lane per (sequence, channel), all 16 states */
+  MM_FLAG_SCAN_CHUNKED = 1u << 2      /* 128-token blocks, 8 segments composed in LDS */
 };
 
 /*

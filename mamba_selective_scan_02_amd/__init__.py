@@ -21,6 +21,8 @@ LIB_PATH = os.path.join(_PKG, "libmamba_mixer.so")
 MM_OK, MM_ERR_INVALID_ARG, MM_ERR_UNSUPPORTED, MM_ERR_WORKSPACE, MM_ERR_HIP = 0, -1, -2, -3, -4
 MM_F32, MM_BF16 = 0, 1
 MM_FLAG_ZOH_B = 1
+MM_FLAG_SCAN_SEQUENTIAL = 2
+MM_FLAG_SCAN_CHUNKED = 4
 STAGES = ("conv_silu", "x_proj", "rmsnorm", "dt_proj_softplus", "selective_scan", "conv_state")
 
 
@@ -101,7 +103,8 @@ def make_shape(batch, seqlen, d_inner, d_state, d_conv, dt_rank, dtype, eps=1e-6
     return Shape(batch, seqlen, d_inner, d_state, d_conv, dt_rank, _io_code(dtype), eps, flags)
 
 
-def shape_of(xz: torch.Tensor, params: dict, *, decode=False, eps=1e-6, zoh=False) -> Shape:
+def shape_of(xz: torch.Tensor, params: dict, *, decode=False, eps=1e-6, zoh=False,
+             scan: str | None = None) -> Shape:
     if decode:
         B, D2 = xz.shape
         L = 1
@@ -111,7 +114,10 @@ def shape_of(xz: torch.Tensor, params: dict, *, decode=False, eps=1e-6, zoh=Fals
     N = params["A"].shape[1]
     K = params["conv_w"].shape[1]
     R = params["dt_proj_w"].shape[1]
-    return make_shape(B, L, D, N, K, R, xz.dtype, eps, MM_FLAG_ZOH_B if zoh else 0)
+    flags = MM_FLAG_ZOH_B if zoh else 0
+    if scan is not None:
+        flags |= {"sequential": MM_FLAG_SCAN_SEQUENTIAL, "chunked": MM_FLAG_SCAN_CHUNKED}[scan]
+    return make_shape(B, L, D, N, K, R, xz.dtype, eps, flags)
 
 
 def params_struct(params: dict) -> Params:
@@ -166,10 +172,12 @@ class StageTimer:
 
 
 def prefill(xz, params, *, conv_state=None, ssm_state=None, states_valid=False, y=None,
-            workspace=None, eps=1e-6, zoh=False, stream=None, timer: StageTimer | None = None):
+            workspace=None, eps=1e-6, zoh=False, stream=None, timer: StageTimer | None = None,
+            scan: str | None = None):
     """Run mamba_mixer_prefill. xz [B, L, 2D] (bf16 or fp32, on the GPU); conv_state
-    [B, D, K-1] and ssm_state [B, D, N] are updated in place when given. Returns y."""
-    shape = shape_of(xz, params, eps=eps, zoh=zoh)
+    [B, D, K-1] and ssm_state [B, D, N] are updated in place when given. scan = None picks
+    the scan kernel by size; "sequential" / "chunked" force one. Returns y."""
+    shape = shape_of(xz, params, eps=eps, zoh=zoh, scan=scan)
     if y is None:
         y = torch.empty(xz.shape[:-1] + (shape.d_inner,), dtype=xz.dtype, device=xz.device)
     need = prefill_workspace_bytes(shape)

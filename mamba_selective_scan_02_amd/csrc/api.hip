@@ -45,7 +45,10 @@ mm_status check_shape(const mm_shape *s, bool decode) {
       s->dt_rank <= 0 || !(s->rms_eps > 0.0f))
     return MM_ERR_INVALID_ARG;
   if (s->io_dtype != MM_F32 && s->io_dtype != MM_BF16) return MM_ERR_INVALID_ARG;
-  if (s->flags & ~(uint32_t)MM_FLAG_ZOH_B) return MM_ERR_INVALID_ARG;
+  if (s->flags & ~(uint32_t)(MM_FLAG_ZOH_B | MM_FLAG_SCAN_SEQUENTIAL | MM_FLAG_SCAN_CHUNKED))
+    return MM_ERR_INVALID_ARG;
+  if ((s->flags & MM_FLAG_SCAN_SEQUENTIAL) && (s->flags & MM_FLAG_SCAN_CHUNKED))
+    return MM_ERR_INVALID_ARG;
   if (decode && s->seqlen != 1) return MM_ERR_INVALID_ARG;
   if (s->d_state != 16 || s->d_conv < 2 || s->d_conv > 4 || s->d_inner % 64 != 0)
     return MM_ERR_UNSUPPORTED;
@@ -155,7 +158,9 @@ mm_status run_mixer(const mm_shape *s, const mm_params *p, const void *xz, void 
     StageScope sc(timer, st, MM_STAGE_SCAN);
     ScanArgs sa{xz, p->conv_w, p->conv_b, conv_state, conv_valid, K, delta, bc, p->A, p->Dskip,
                 y, ssm_state, states_valid && ssm_state != nullptr,
-                (s->flags & MM_FLAG_ZOH_B) ? 1 : 0, B, L, D, N};
+                (s->flags & MM_FLAG_ZOH_B) ? 1 : 0,
+                (s->flags & MM_FLAG_SCAN_SEQUENTIAL) ? 1 : (s->flags & MM_FLAG_SCAN_CHUNKED) ? 2 : 0,
+                B, L, D, N};
     MM_TRY(launch_scan(dt, sa, st));
   }
   if (conv_state) {

@@ -41,6 +41,20 @@ __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2
 __device__ __forceinline__ float silu_f(float v) {
   return v * __builtin_amdgcn_rcpf(1.0f + exp2_hw(-v * kLog2e));
 }
+// expm1(x) = e^x - 1 without cancellation: e^x - 1 from the hardware exp when |x| > 0.5
+// (relative error ~2 ulp there), else the Taylor series to x^8 in Horner form (truncation
+// below |x|^9 / 9! < 6e-9 relative for |x| <= 0.5).
+__device__ __forceinline__ float expm1_f(float x) {
+  if (fabsf(x) > 0.5f) return exp2_hw(x * kLog2e) - 1.0f;
+  float r = __builtin_fmaf(x, 1.0f / 8.0f, 1.0f);
+  r = __builtin_fmaf(x * (1.0f / 7.0f), r, 1.0f);
+  r = __builtin_fmaf(x * (1.0f / 6.0f), r, 1.0f);
+  r = __builtin_fmaf(x * (1.0f / 5.0f), r, 1.0f);
+  r = __builtin_fmaf(x * (1.0f / 4.0f), r, 1.0f);
+  r = __builtin_fmaf(x * (1.0f / 3.0f), r, 1.0f);
+  r = __builtin_fmaf(x * 0.5f, r, 1.0f);
+  return x * r;
+}
 // softplus(v) = log(1 + e^v); above 20 it equals v to within 2e-9 relative.
 __device__ __forceinline__ float softplus_f(float v) {
   return v > 20.0f ? v : log1pf(expf(v));

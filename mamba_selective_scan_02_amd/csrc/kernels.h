@@ -52,6 +52,7 @@ struct ScanArgs {
   float *state;         // [B, D, N] or null
   int state_valid;
   int zoh;
+  int force;            // 0: pick by size; 1: sequential kernel; 2: time-parallel kernel
   int B, L, D, N;
 };
 hipError_t launch_scan(mm_dtype dt, const ScanArgs &a, hipStream_t s);

@@ -21,10 +21,11 @@ def _need_gpu():
 
 
 def _case(cfg, seed, *, states=False, conv_bias=False, gamma_random=False, zoh=False,
-          channels=None, check_y=True):
+          channels=None, check_y=True, scan=None):
     _need_gpu()
     print(f"[case] {cfg.name} B={cfg.batch} L={cfg.seqlen} D={cfg.d_inner} R={cfg.dt_rank} "
-          f"io={cfg.io_dtype} seed={seed} states={states} bias={conv_bias} zoh={zoh}", flush=True)
+          f"io={cfg.io_dtype} seed={seed} states={states} bias={conv_bias} zoh={zoh} scan={scan}",
+          flush=True)
     dev = "cuda"
     p = synth.make_params(cfg, seed, dev, conv_bias=conv_bias, gamma_random=gamma_random)
     xz = synth.make_xz(cfg, seed, dev)
@@ -35,7 +36,7 @@ def _case(cfg, seed, *, states=False, conv_bias=False, gamma_random=False, zoh=F
         ss = torch.zeros(cfg.batch, cfg.d_inner, cfg.d_state, dtype=torch.float32, device=dev)
     cs_in, ss_in = cs.clone(), ss.clone()
     y = mm.prefill(xz, p, conv_state=cs, ssm_state=ss, states_valid=states, eps=cfg.rms_eps,
-                   zoh=zoh)
+                   zoh=zoh, scan=scan)
     torch.cuda.synchronize()
     yr, csr, ssr = oracle.mixer_prefill(
         to64(xz), oracle.as_f64_params(p), to64(cs_in) if states else None,
@@ -94,6 +95,21 @@ def test_bf16_short_sequences(L):
 def test_bf16_mini_prefill_4k_full():
     cfg = synth.CONFIGS["mini_prefill_4k"]
     _case(cfg, synth.seed_for("mini_prefill_4k"))
+
+
+@pytest.mark.parametrize("scan", ["sequential", "chunked"])
+@pytest.mark.parametrize("zoh", [False, True])
+def test_both_scan_kernels_f32(scan, zoh):
+    # L = 300: two full 128-token blocks and a ragged tail of 44 for the time-parallel kernel
+    _case(TINY.with_(batch=2, seqlen=300, name="f32_L300"), 90, states=True, conv_bias=True,
+          gamma_random=True, zoh=zoh, scan=scan)
+
+
+@pytest.mark.parametrize("scan", ["sequential", "chunked"])
+@pytest.mark.parametrize("L", [5, 128, 129, 300])
+def test_both_scan_kernels_bf16(scan, L):
+    _case(BF16_SMALL.with_(seqlen=L, name=f"bf16_L{L}"), 91 + L, states=True, conv_bias=True,
+          scan=scan)
 
 
 def test_chunked_prefill_equals_whole_on_gpu_and_oracle():
