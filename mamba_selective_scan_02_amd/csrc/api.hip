@@ -14,21 +14,28 @@ inline size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 inline size_t esz(mm_dtype d) { return d == MM_BF16 ? 2 : 4; }
 
 struct Workspace {
+  bool fused_xproj;  // bf16: conv + x_proj + RMSNorm in one kernel (no u / xdbl buffers)
+  bool tiled_dtproj; // bf16: token-stationary dt_proj kernel
   size_t u, u_lo, xdbl, dtlow, dtlow_lo, bc, dt, total;
 };
 
 // Byte offsets of the prefill intermediates for T = batch * seqlen tokens.
 //   fp32 mode: u [T,D] f32 | xdbl [T,R+2N] f32 | dt_low [T,R] f32 | B,C [T,2N] f32 | dt [T,D] f32
-//   bf16 mode: u_hi, u_lo [T,D] bf16 | xdbl f32 | dt_low hi, lo [T,R] bf16 | B,C f32 | dt [T,D] f16
+//   bf16 mode: (u_hi, u_lo [T,D] bf16 | xdbl f32, unless fused) | dt_low hi, lo [T,R] bf16 |
+//              B,C [T,2N] f32 | dt [T,D] f16
 Workspace layout(const mm_shape &s) {
   const size_t T = (size_t)s.batch * s.seqlen;
   const bool bf = s.io_dtype == MM_BF16;
   const size_t e = esz(s.io_dtype);
   Workspace w;
+  // one workgroup per 128 tokens: worth it once there are enough tokens to fill the chip
+  w.fused_xproj = bf && T >= 32768 &&
+                  xproj_fused_supported(s.dt_rank, s.d_state, s.d_inner, s.d_conv);
+  w.tiled_dtproj = bf && dtproj_supported(s.dt_rank, s.d_inner);
   size_t o = 0;
-  w.u = o; o += up(T * s.d_inner * e);
-  w.u_lo = o; if (bf) o += up(T * s.d_inner * 2);
-  w.xdbl = o; o += up(T * (s.dt_rank + 2 * s.d_state) * 4);
+  w.u = o; if (!w.fused_xproj) o += up(T * s.d_inner * e);
+  w.u_lo = o; if (bf && !w.fused_xproj) o += up(T * s.d_inner * 2);
+  w.xdbl = o; if (!w.fused_xproj) o += up(T * (s.dt_rank + 2 * s.d_state) * 4);
   w.dtlow = o; o += up(T * s.dt_rank * e);
   w.dtlow_lo = o; if (bf) o += up(T * s.dt_rank * 2);
   w.bc = o; o += up(T * 2 * s.d_state * 4);
@@ -137,22 +144,37 @@ mm_status run_mixer(const mm_shape *s, const mm_params *p, const void *xz, void 
   const int conv_valid = states_valid && conv_state != nullptr;
 
   ConvArgs ca{xz, u, u_lo, p->conv_w, p->conv_b, conv_state, conv_valid, B, L, D, K};
-  {
-    StageScope sc(timer, st, MM_STAGE_CONV);
-    MM_TRY(launch_conv_silu(dt, ca, st));
-  }
-  {
+  if (w.fused_xproj) {
     StageScope sc(timer, st, MM_STAGE_XPROJ);
-    MM_TRY(launch_xproj(dt, u, u_lo, p->x_proj_w, xdbl, T, D, R + 2 * N, st));
-  }
-  {
-    StageScope sc(timer, st, MM_STAGE_NORM);
-    MM_TRY(launch_norm(dt, xdbl, dtlow, dtlow_lo, bc, p->dt_norm_w, p->B_norm_w, p->C_norm_w, T,
-                       R, N, s->rms_eps, st));
+    XprojFusedArgs xa{(const uint16_t *)xz, (const uint16_t *)p->conv_w, (const uint16_t *)p->conv_b,
+                      (const uint16_t *)conv_state, conv_valid, (const uint16_t *)p->x_proj_w,
+                      (uint16_t *)dtlow, (uint16_t *)dtlow_lo, bc, p->dt_norm_w, p->B_norm_w,
+                      p->C_norm_w, s->rms_eps, B, L, D, R, K};
+    MM_TRY(launch_xproj_fused(xa, st));
+  } else {
+    {
+      StageScope sc(timer, st, MM_STAGE_CONV);
+      MM_TRY(launch_conv_silu(dt, ca, st));
+    }
+    {
+      StageScope sc(timer, st, MM_STAGE_XPROJ);
+      MM_TRY(launch_xproj(dt, u, u_lo, p->x_proj_w, xdbl, T, D, R + 2 * N, st));
+    }
+    {
+      StageScope sc(timer, st, MM_STAGE_NORM);
+      MM_TRY(launch_norm(dt, xdbl, dtlow, dtlow_lo, bc, p->dt_norm_w, p->B_norm_w, p->C_norm_w, T,
+                         R, N, s->rms_eps, st));
+    }
   }
   {
     StageScope sc(timer, st, MM_STAGE_DTPROJ);
-    MM_TRY(launch_dtproj(dt, dtlow, dtlow_lo, p->dt_proj_w, p->dt_proj_b, delta, T, D, R, st));
+    if (w.tiled_dtproj) {
+      DtprojArgs da{(const uint16_t *)dtlow, (const uint16_t *)dtlow_lo,
+                    (const uint16_t *)p->dt_proj_w, p->dt_proj_b, (_Float16 *)delta, T, D, R};
+      MM_TRY(launch_dtproj_tiled(da, st));
+    } else {
+      MM_TRY(launch_dtproj(dt, dtlow, dtlow_lo, p->dt_proj_w, p->dt_proj_b, delta, T, D, R, st));
+    }
   }
   {
     StageScope sc(timer, st, MM_STAGE_SCAN);

@@ -55,9 +55,15 @@ __device__ __forceinline__ float expm1_f(float x) {
   r = __builtin_fmaf(x * 0.5f, r, 1.0f);
   return x * r;
 }
-// softplus(v) = log(1 + e^v); above 20 it equals v to within 2e-9 relative.
+// softplus(v) = log(1 + e^v) from the hardware exp2 / log2: above 20 it equals v to within
+// 2e-9 relative; otherwise e = e^v, w = 1 + e (rounded) and log(1 + e) = log(w) * e / (w - 1),
+// which cancels the rounding of w to first order (and is e itself when w rounds to 1).
 __device__ __forceinline__ float softplus_f(float v) {
-  return v > 20.0f ? v : log1pf(expf(v));
+  if (v > 20.0f) return v;
+  const float e = exp2_hw(v * kLog2e);
+  const float w = 1.0f + e;
+  if (w == 1.0f) return e;
+  return __builtin_amdgcn_logf(w) * 0.69314718055994531f * (e * __builtin_amdgcn_rcpf(w - 1.0f));
 }
 
 // ---------------------------------------------------------------- launch geometry

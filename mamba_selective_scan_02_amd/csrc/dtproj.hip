@@ -1,0 +1,154 @@
+// dt_proj + bias + softplus for bf16 I/O on split-precision bf16 MFMA.
+//
+//   dt[t, i] = softplus(W_dt[i, :] . dt_low[t, :] + b_i)        (stored as fp16)
+//
+// Jamba analysis page, "The selective mechanism": Delta is a function of the token through a
+// small learned linear layer ("From scalar SSM to vector processing": one Delta per channel).
+// Softplus maps it to a positive step (Mamba-1 block).
+//
+// The contraction is short (dt_rank = 256) and the output wide (d_inner per token), so the
+// kernel keeps the token side stationary: a workgroup of 8 waves owns 128 tokens; each wave
+// loads the MFMA B-operand fragments of its 16 tokens' dt_low (bf16 high and low parts, whole
+// dt_rank) into VGPRs once, then streams the workgroup's channel range through LDS in chunks
+// of 64 W_dt rows (direct-to-LDS loads, double-buffered, 16-byte slots XOR-swizzled so the
+// 16-row fragment reads are bank-conflict free). Per chunk a wave issues
+// (64/16) x (dt_rank/32) x 2 MFMAs and writes 16 tokens x 64 channels of fp16 dt.
+#include "common.h"
+#include "kernels.h"
+
+namespace mm {
+namespace {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+
+constexpr int kTokD = 128;   // tokens per workgroup
+constexpr int kChD = 64;     // channels per chunk
+
+__device__ __forceinline__ void load_lds16(const void *src, void *lds) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)lds, 16, 0, 0);
+}
+
+// 16-byte slot swizzle for rows of S slots: 16 consecutive rows read at one logical slot land
+// in 16 distinct bank groups (64 banks x 4 B).
+template <int S>
+__device__ __forceinline__ int swz(int r, int c) {
+  if (S == 8) return c ^ ((r >> 1) & 7);
+  return c ^ (r & 15);
+}
+
+// softplus for fp16 storage: log(1 + e) from the hardware log2 when e = exp(v) is not tiny,
+// else e - e^2/2 (the rounding of 1 + e would dominate there); v itself above 15.
+__device__ __forceinline__ float softplus_h(float v) {
+  const float e = exp2_hw(v * kLog2e);
+  const float l = __builtin_amdgcn_logf(1.0f + e) * 0.69314718055994531f;
+  const float r = e < 9.765625e-4f ? __builtin_fmaf(-0.5f * e, e, e) : l;
+  return v > 15.0f ? v : r;
+}
+
+__device__ __forceinline__ uint32_t pack_h2(float a, float b) {
+  const _Float16 ha = (_Float16)fminf(a, 65504.0f), hb = (_Float16)fminf(b, 65504.0f);
+  return (uint32_t)__builtin_bit_cast(uint16_t, ha) | ((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16);
+}
+
+template <int R>
+__global__ __launch_bounds__(512) void dtproj_kernel(DtprojArgs a, int ch_per_wg) {
+  constexpr int S = R / 8;             // 16-byte slots per W_dt row
+  constexpr int KS = R / 32;           // k-steps
+  constexpr int RPW = 64 / S > 0 ? 64 / S : 1;  // rows per 1 KB wave-load (S <= 64)
+  __shared__ __attribute__((aligned(16))) bf16_t w_s[2][kChD][R];
+
+  const int ntok = (a.T + kTokD - 1) / kTokD;
+  const int gid = xcd_remap(blockIdx.x, gridDim.x);
+  const int tt = gid % ntok, cg = gid / ntok;      // token tile, channel group
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int tl = lane & 15, g = lane >> 4;
+  const int tok = tt * kTokD + wv * 16 + tl;
+  const int tokc = min(tok, a.T - 1);
+  const int cbeg = cg * ch_per_wg;
+  const int nck = ch_per_wg / kChD;
+
+  // this lane's B-operand fragments: token tok, dt_rank slice [32 ks + 8 g, +8)
+  uint4 fh[KS], fl[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    fh[ks] = *(const uint4 *)(a.dtlow + (int64_t)tokc * R + ks * 32 + g * 8);
+    fl[ks] = *(const uint4 *)(a.dtlow_lo + (int64_t)tokc * R + ks * 32 + g * 8);
+  }
+
+  auto stage = [&](int ck, int buf) {
+    const int c0 = cbeg + ck * kChD;
+    constexpr int loads = kChD * S / 64;           // 1 KB wave-loads per chunk
+    for (int ld = wv; ld < loads; ld += 8) {
+      const int e = ld * 64 + lane;                // 16-byte slot index within the chunk
+      const int r = e / S, ps = e % S;
+      load_lds16(a.w + (int64_t)(c0 + r) * R + swz<S>(r, ps) * 8, &w_s[buf][0][0] + ld * 512);
+    }
+  };
+
+  stage(0, 0);
+  for (int ck = 0; ck < nck; ++ck) {
+    const int buf = ck & 1;
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (ck + 1 < nck) stage(ck + 1, buf ^ 1);
+    f32x4 acc[4];
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const bf16x8 bh = __builtin_bit_cast(bf16x8, fh[ks]);
+      const bf16x8 bl = __builtin_bit_cast(bf16x8, fl[ks]);
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
+        const int r = nb * 16 + tl;
+        const bf16x8 fw = __builtin_bit_cast(
+            bf16x8, *(const uint4 *)&w_s[buf][r][swz<S>(r, ks * 4 + g) * 8]);
+        acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fw, bl, acc[nb], 0, 0, 0);
+        acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fw, bh, acc[nb], 0, 0, 0);
+      }
+    }
+    // acc[nb][j] = pre-activation of (token tok, channel c0 + 16 nb + 4 g + j)
+    if (tok < a.T) {
+      const int c0 = cbeg + ck * kChD;
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
+        const int c = c0 + nb * 16 + 4 * g;
+        const float4 bv = *(const float4 *)(a.bias + c);
+        uint2 o;
+        o.x = pack_h2(softplus_h(acc[nb][0] + bv.x), softplus_h(acc[nb][1] + bv.y));
+        o.y = pack_h2(softplus_h(acc[nb][2] + bv.z), softplus_h(acc[nb][3] + bv.w));
+        *(uint2 *)(a.dt + (int64_t)tok * a.D + c) = o;
+      }
+    }
+  }
+}
+
+template <int R>
+hipError_t launch_r(const DtprojArgs &a, hipStream_t s) {
+  const int ntok = (a.T + kTokD - 1) / kTokD;
+  // split the channels so that there are >= 2 workgroups per CU when tokens are few
+  int split = 1;
+  while (ntok * split < 512 && a.D / (split * 2) >= kChD && (a.D / (split * 2)) % kChD == 0) split *= 2;
+  hipLaunchKernelGGL((dtproj_kernel<R>), dim3((unsigned)(ntok * split)), dim3(512), 0, s, a,
+                     a.D / split);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool dtproj_supported(int R, int D) {
+  return D % kChD == 0 && (R == 64 || R == 128 || R == 256 || R == 512);
+}
+
+hipError_t launch_dtproj_tiled(const DtprojArgs &a, hipStream_t s) {
+  switch (a.R) {
+    case 64: return launch_r<64>(a, s);
+    case 128: return launch_r<128>(a, s);
+    case 256: return launch_r<256>(a, s);
+    case 512: return launch_r<512>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace mm

@@ -37,6 +37,34 @@ hipError_t launch_norm(mm_dtype dt, const float *xdbl, void *dtlow, void *dtlow_
 hipError_t launch_dtproj(mm_dtype dt, const void *dtlow, const void *dtlow_lo, const void *w,
                          const float *bias, void *dtout, int T, int D, int R, hipStream_t s);
 
+// bf16 I/O fused path: conv1d + SiLU -> x_proj -> RMSNorm of dt_low / B / C in one kernel.
+struct XprojFusedArgs {
+  const uint16_t *xz;          // [B, L, 2D] bf16
+  const uint16_t *conv_w;      // [D, K] bf16
+  const uint16_t *conv_b;      // [D] bf16 or null
+  const uint16_t *conv_state;  // [B, D, K-1] bf16 or null
+  int conv_valid;
+  const uint16_t *w;           // x_proj weight [R + 2N, D] bf16
+  uint16_t *dtlow, *dtlow_lo;  // [T, R] bf16 high and low parts of RMSNorm(dt_low)
+  float *bc;                   // [T, 2N] RMSNorm(B) | RMSNorm(C)
+  const float *g_dt, *g_B, *g_C;
+  float eps;
+  int B, L, D, R, K;
+};
+bool xproj_fused_supported(int R, int N, int D, int K);
+hipError_t launch_xproj_fused(const XprojFusedArgs &a, hipStream_t s);
+
+// bf16 I/O dt_proj: dt[T, D] (fp16) = softplus((dtlow + dtlow_lo)[T, R] . Wdt[D, R]^T + bias)
+struct DtprojArgs {
+  const uint16_t *dtlow, *dtlow_lo;  // [T, R] bf16
+  const uint16_t *w;                 // [D, R] bf16
+  const float *bias;                 // [D]
+  _Float16 *dt;                      // [T, D]
+  int T, D, R;
+};
+bool dtproj_supported(int R, int D);
+hipError_t launch_dtproj_tiled(const DtprojArgs &a, hipStream_t s);
+
 struct ScanArgs {
   const void *xz;       // [B, L, 2D]; x = first D columns (conv input), z = last D (gate)
   const void *conv_w;   // [D, K] io dtype

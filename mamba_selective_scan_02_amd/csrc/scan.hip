@@ -106,34 +106,51 @@ __global__ __launch_bounds__(64) void scan_seq_kernel(ScanArgs a) {
 // Time-parallel scan for long sequences (few sequences x channels to fill 256 CUs).
 //
 // A workgroup owns kCh = 32 channels of one sequence and walks the sequence in blocks of
-// kW * kS = 128 tokens. Each of its kW = 8 waves takes one kS = 16-token segment of a block.
-// Lane l works on channel l/2 and on the 8 states 8*(l%2) .. 8*(l%2)+7 of it.
-//  1. Local pass: the segment is scanned from h = 0, keeping exp(dt*A) of every
+// kW * kS = 128 tokens. Per block:
+//  0. The block's x (with the 3 conv-window rows before it), z, dt and B|C rows were loaded
+//     into LDS with direct-to-LDS 16-byte loads while the previous block was computed.
+//  1. Prep (all 512 threads, one (channel, 8 tokens) run each): u = SiLU(conv1d(x) + b),
+//     dt, dt*u, D*u and SiLU(z), once per (token, channel), into LDS.
+//  2. Local pass: wave w takes tokens 16w .. 16w+15; lane l works on channel l/2 and states
+//     8*(l%2) .. +7. The segment is scanned from h = 0, keeping exp(dt*A) of every
 //     (token, state) in VGPRs (one exp per element, as in the sequential recurrence).
-//  2. The segment's transfer (P, S) -- h_out = P * h_in + S with P = exp(A * sum dt) and S the
-//     local end state -- goes to LDS; each wave composes the transfers of the segments before
-//     it onto the block's carry-in, with the page's associative scan operator
-//     ("Parallel training via the parallel scan": (a, b) then (c, d) gives (ac, ad + b) for
-//     the map h -> a h + b), and every wave also composes all 8 to get the next carry-in.
-//  3. Replay: the segment is run again from its true h_in with the stored exp(dt*A), and
-//     y_t = C_t . h_t is formed; the two half-sums of a channel meet by a DPP lane swap.
-// x, z, dt of the block are staged through LDS with 16-byte loads; so are B, C (shared by all
-// channels of a token). The conv window needs 3 tokens before the block (carried state or 0
-// before token 0).
+//  3. Compose: the segment's transfer h -> P h + S (P = exp(A * sum dt), S = the local end
+//     state) goes to LDS; each wave folds the transfers before it onto the block's carry-in
+//     with the page's associative operator ("Parallel training via the parallel scan":
+//     (a, b) then (c, d) gives (ac, ad + b) for h -> a h + b), and all 8 for the next carry.
+//  4. Replay from the true h_in with the stored exp(dt*A); y_t = C_t . h_t; the two half-sums
+//     of a channel meet by a DPP lane swap; y = (y_ssm + D u) * SiLU(z) goes out as bf16/f32.
 constexpr int kCh = 32, kW = 8, kS = 16, kG = 8, kBlk = kW * kS;
+constexpr int kHalo = 3;                  // x rows before the block (conv window, K - 1 <= 3)
+constexpr int kXRows = kBlk + 16;         // staged x rows: halo + block, padded to 16-row loads
+
+// One direct-to-LDS 16-byte load per lane: lane i of the wave fills bytes [16 i, 16 i + 16)
+// of the 1 KB LDS window at `lds` (wave-uniform).
+__device__ __forceinline__ void load_lds16(const void *src, void *lds) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)lds, 16, 0, 0);
+}
 
 template <typename T, bool ZOH, int K>
 __global__ __launch_bounds__(kW * 64) void scan_chunked_kernel(ScanArgs a) {
   typedef typename Delta<T>::type DT;
-  constexpr int kHalo = 3;  // rows before the block kept for the conv window (K - 1 <= 3)
-  __shared__ __attribute__((aligned(16))) float bc_s[kBlk][2 * kN];
-  __shared__ __attribute__((aligned(16))) float agg_s[kW][64][2 * kG];
-  __shared__ __attribute__((aligned(16))) T x_s[kBlk + kHalo][kCh];
-  __shared__ __attribute__((aligned(16))) T z_s[kBlk][kCh];
-  __shared__ __attribute__((aligned(16))) DT d_s[kBlk][kCh];
-  // per-token u and dt*u (ZOH: u) of this block, written and read by the same wave
-  __shared__ float u_s[kBlk][kCh];
-  __shared__ float du_s[kBlk][kCh];
+  constexpr int xper = 16 / sizeof(T);                 // x/z elements per 16-byte chunk
+  constexpr int xrow_chunks = kCh * sizeof(T) / 16;    // 16-byte chunks per staged x/z row
+  constexpr int drow_chunks = kCh * sizeof(DT) / 16;
+  // bf16 I/O stages x, z and dt through LDS too; fp32 I/O (small problems) reads them from
+  // global memory in the prep phase, which keeps its LDS within 160 KB.
+  constexpr bool kStageXZD = sizeof(T) == 2;
+  constexpr int kXR = kStageXZD ? kXRows : 1, kZR = kStageXZD ? kBlk : 1;
+  // staging (written by async loads)
+  __shared__ __attribute__((aligned(16))) float bc_s[2][kBlk][2 * kN];
+  __shared__ __attribute__((aligned(16))) T x_s[kXR][kCh];
+  __shared__ __attribute__((aligned(16))) T z_s[kZR][kCh];
+  __shared__ __attribute__((aligned(16))) DT d_s[kZR][kCh];
+  // prep outputs: (dt, dt*u) and (D*u, SiLU(z)) per (token, channel); rows padded by one
+  // element so that rows 1 and 8 apart fall in different LDS banks
+  __shared__ __attribute__((aligned(16))) float2 pd_s[kBlk][kCh + 1];
+  __shared__ __attribute__((aligned(16))) float2 eg_s[kBlk][kCh + 1];
+  // segment transfers, lane-contiguous 16-byte slots: [wave][P0..3, P4..7, S0..3, S4..7][lane]
+  __shared__ __attribute__((aligned(16))) float4 agg_s[kW][4][64];
 
   const int groups = a.D / kCh;
   const int gid = xcd_remap(blockIdx.x, gridDim.x);
@@ -152,11 +169,14 @@ __global__ __launch_bounds__(kW * 64) void scan_chunked_kernel(ScanArgs a) {
     iA[j] = 1.0f / Av[j];
     carry[j] = (a.state_valid && a.state) ? a.state[((int64_t)b * a.D + ch) * kN + kG * p + j] : 0.f;
   }
+  // prep thread: channel pc, tokens 8*pt .. 8*pt+7 of the block
+  const int pc = tid & (kCh - 1), pt = tid >> 5;
+  const int pch = ch0 + pc;
   float wc[K];
 #pragma unroll
-  for (int k = 0; k < K; ++k) wc[k] = io<T>::cvt(((const T *)a.conv_w)[(int64_t)ch * K + k]);
-  const float cb = a.conv_b ? io<T>::cvt(((const T *)a.conv_b)[ch]) : 0.0f;
-  const float Dv = a.Dskip[ch];
+  for (int k = 0; k < K; ++k) wc[k] = io<T>::cvt(((const T *)a.conv_w)[(int64_t)pch * K + k]);
+  const float cb = a.conv_b ? io<T>::cvt(((const T *)a.conv_b)[pch]) : 0.0f;
+  const float Dp = a.Dskip[pch];
 
   const int64_t row = 2LL * a.D;
   const T *xzb = (const T *)a.xz + (int64_t)b * a.L * row;
@@ -164,66 +184,104 @@ __global__ __launch_bounds__(kW * 64) void scan_chunked_kernel(ScanArgs a) {
   const float *bcb = a.bc + (int64_t)b * a.L * 2 * kN;
   T *yb = (T *)a.y + (int64_t)b * a.L * a.D;
   const int nblocks = (a.L + kBlk - 1) / kBlk;
+  const int Lm1 = a.L - 1;
 
+  // Issue the direct-to-LDS loads of block `blk` (rows past the end read row L-1 so every
+  // address is valid; prep and the scan ignore those rows).
+  auto stage = [&](int blk) {
+    const int T0 = blk * kBlk;
+    // B|C: 128 rows x 128 B = 16 KB = 16 wave-loads; wave wv does loads wv and wv + 8
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int ld = wv + i * kW;                 // 1 KB window index
+      const int r = ld * 8 + (lane >> 3);         // 8 lanes per 128-byte row
+      const int t = min(T0 + r, Lm1);
+      load_lds16(bcb + (int64_t)t * 2 * kN + (lane & 7) * 4, &bc_s[blk & 1][ld * 8][0]);
+    }
+    if (!kStageXZD) return;
+    // x: kXRows rows x 64 B (bf16) = 9 wave-loads of 16 rows; rows T0-3 .. ; row r <-> token T0-3+r
+    constexpr int xrpl = 64 / xrow_chunks;        // rows per wave-load
+    for (int ld = wv; ld < kXRows / xrpl; ld += kW) {
+      const int r = ld * xrpl + lane / xrow_chunks;
+      const int t = min(max(T0 - kHalo + r, 0), Lm1);
+      load_lds16(xzb + (int64_t)t * row + ch0 + (lane % xrow_chunks) * xper, &x_s[ld * xrpl][0]);
+    }
+    for (int ld = wv; ld < kBlk / xrpl; ld += kW) {
+      const int r = ld * xrpl + lane / xrow_chunks;
+      const int t = min(T0 + r, Lm1);
+      load_lds16(xzb + (int64_t)t * row + a.D + ch0 + (lane % xrow_chunks) * xper, &z_s[ld * xrpl][0]);
+    }
+    constexpr int drpl = 64 / drow_chunks;
+    constexpr int dper = 16 / sizeof(DT);
+    for (int ld = wv; ld < kBlk / drpl; ld += kW) {
+      const int r = ld * drpl + lane / drow_chunks;
+      const int t = min(T0 + r, Lm1);
+      load_lds16(db + (int64_t)t * a.D + ch0 + (lane % drow_chunks) * dper, &d_s[ld * drpl][0]);
+    }
+  };
+
+  stage(0);
   for (int blk = 0; blk < nblocks; ++blk) {
     const int T0 = blk * kBlk;
-    __syncthreads();  // previous block's readers are done with the LDS tiles
-    // ---- stage B|C rows (128 B each), 4 threads per token
+    const int cur = blk & 1;
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's direct-to-LDS loads have landed
+    __syncthreads();                // ... and every wave's; previous block fully consumed
+
+    // ---- 1. prep: conv + SiLU, dt, dt*u, D*u, SiLU(z) for (pc, tokens 8pt..8pt+7)
     {
-      const int tk = tid >> 2, q = tid & 3;
-      float4 v0 = make_float4(0.f, 0.f, 0.f, 0.f), v1 = v0;
-      if (T0 + tk < a.L) {
-        const float4 *src = (const float4 *)(bcb + (int64_t)(T0 + tk) * 2 * kN + 8 * q);
-        v0 = src[0];
-        v1 = src[1];
-      }
-      *(float4 *)&bc_s[tk][8 * q] = v0;
-      *(float4 *)&bc_s[tk][8 * q + 4] = v1;
-    }
-    // ---- stage x (with halo), z and dt rows: 32 channels = 64 B per row = 4 x 16 B
-    constexpr int xper = 16 / sizeof(T);   // elements per 16-byte chunk
-    constexpr int xcpr = kCh / xper;       // chunks per 32-channel row
-    for (int e = tid; e < (kBlk + kHalo) * xcpr; e += kW * 64) {
-      const int r = e / xcpr, q = e % xcpr;
-      const int t = T0 - kHalo + r;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (t >= 0 && t < a.L) {
-        v = *(const uint4 *)(xzb + (int64_t)t * row + ch0 + q * xper);
-      } else if (t < 0 && a.conv_valid && a.conv_state && t >= -(K - 1)) {
-        // carried conv state, oldest first: row t = -(K-1)+j holds conv_state[b, ch, j]
-        T tmp[xper];
+      // block-relative token tb (tb >= -3, T0 + tb < L where it matters)
+      auto getx = [&](int tb) -> float {
+        if (kStageXZD) return io<T>::cvt(x_s[(kStageXZD ? tb + kHalo : 0)][pc]);
+        return io<T>::cvt(xzb[(int64_t)min(T0 + tb, Lm1) * row + pch]);
+      };
+      auto getz = [&](int tb) -> float {
+        if (kStageXZD) return io<T>::cvt(z_s[(kStageXZD ? tb : 0)][pc]);
+        return io<T>::cvt(xzb[(int64_t)min(T0 + tb, Lm1) * row + a.D + pch]);
+      };
+      auto getd = [&](int tb) -> float {
+        if (kStageXZD) return (float)d_s[(kStageXZD ? tb : 0)][pc];
+        return (float)db[(int64_t)min(T0 + tb, Lm1) * a.D + pch];
+      };
+      float win[K - 1];
 #pragma unroll
-        for (int e2 = 0; e2 < xper; ++e2) {
-          const int chh = ch0 + q * xper + e2;
-          tmp[e2] = ((const T *)a.conv_state)[((int64_t)b * a.D + chh) * (K - 1) + (K - 1) + t];
+      for (int j = 0; j < K - 1; ++j) {
+        const int tb = pt * 8 - (K - 1) + j;      // block-relative token of this window row
+        const int t = T0 + tb;
+        float v = 0.f;
+        if (t >= 0) {
+          v = getx(tb);
+        } else if (a.conv_valid && a.conv_state) {
+          v = io<T>::cvt(((const T *)a.conv_state)[((int64_t)b * a.D + pch) * (K - 1) + (K - 1) + t]);
         }
-        v = *(const uint4 *)tmp;
+        win[j] = v;
       }
-      *(uint4 *)&x_s[r][q * xper] = v;
-    }
-    for (int e = tid; e < kBlk * xcpr; e += kW * 64) {
-      const int r = e / xcpr, q = e % xcpr;
-      const int t = T0 + r;
-      uint4 vz = make_uint4(0, 0, 0, 0);
-      if (t < a.L) vz = *(const uint4 *)(xzb + (int64_t)t * row + a.D + ch0 + q * xper);
-      *(uint4 *)&z_s[r][q * xper] = vz;
-    }
-    for (int e = tid; e < kBlk * (kCh * (int)sizeof(DT) / 16); e += kW * 64) {
-      constexpr int per = 16 / sizeof(DT);           // elements per 16-byte chunk
-      constexpr int cpr = kCh / per;                 // chunks per row
-      const int r = e / cpr, q = e % cpr;
-      const int t = T0 + r;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (t < a.L) v = *(const uint4 *)(db + (int64_t)t * a.D + ch0 + q * per);
-      *(uint4 *)&d_s[r][q * per] = v;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int tb = pt * 8 + e;
+        const bool valid = T0 + tb < a.L;
+        const float x = getx(tb);
+        float acc = cb;
+#pragma unroll
+        for (int j = 0; j < K - 1; ++j) acc = __builtin_fmaf(wc[j], win[j], acc);
+        acc = __builtin_fmaf(wc[K - 1], x, acc);
+#pragma unroll
+        for (int j = 0; j + 1 < K - 1; ++j) win[j] = win[j + 1];
+        win[K - 2] = x;
+        const float u = silu_f(acc);
+        const float dt = valid ? getd(tb) : 0.f;
+        const float z = getz(tb);
+        // ZOH replays Bbar u = expm1(dt A)/A * B * u, so it keeps u where Euler keeps dt*u
+        pd_s[tb][pc] = make_float2(dt, valid ? (ZOH ? u : dt * u) : 0.f);
+        eg_s[tb][pc] = make_float2(valid ? Dp * u : 0.f, valid ? silu_f(z) : 0.f);
+      }
     }
     __syncthreads();
+    // next block's staging overlaps this block's scan (x, z, dt tiles are free after prep;
+    // B|C is double-buffered)
+    if (blk + 1 < nblocks) stage(blk + 1);
 
-    // ---- 1. local pass over this wave's segment
+    // ---- 2. local pass over this wave's segment
     const int tb0 = wv * kS;
-    float win[K - 1];
-#pragma unroll
-    for (int j = 0; j < K - 1; ++j) win[j] = io<T>::cvt(x_s[tb0 + kHalo - (K - 1) + j][c]);
     float dA[kS][kG];
     float hl[kG];
 #pragma unroll
@@ -232,63 +290,50 @@ __global__ __launch_bounds__(kW * 64) void scan_chunked_kernel(ScanArgs a) {
 #pragma unroll
     for (int t = 0; t < kS; ++t) {
       const int tb = tb0 + t;
-      const float x = io<T>::cvt(x_s[tb + kHalo][c]);
-      float acc = cb;
-#pragma unroll
-      for (int j = 0; j < K - 1; ++j) acc = __builtin_fmaf(wc[j], win[j], acc);
-      acc = __builtin_fmaf(wc[K - 1], x, acc);
-#pragma unroll
-      for (int j = 0; j + 1 < K - 1; ++j) win[j] = win[j + 1];
-      win[K - 2] = x;
-      const float u = silu_f(acc);
-      const float dt = (float)d_s[tb][c];
+      const float2 pd = pd_s[tb][c];
+      const float dt = pd.x, du = pd.y;
       sumdt += dt;
-      u_s[tb][c] = u;
-      const float4 B0 = *(const float4 *)&bc_s[tb][kG * p];
-      const float4 B1 = *(const float4 *)&bc_s[tb][kG * p + 4];
+      const float4 B0 = *(const float4 *)&bc_s[cur][tb][kG * p];
+      const float4 B1 = *(const float4 *)&bc_s[cur][tb][kG * p + 4];
       const float Bv[kG] = {B0.x, B0.y, B0.z, B0.w, B1.x, B1.y, B1.z, B1.w};
-      if (ZOH) {
-        du_s[tb][c] = u;
 #pragma unroll
-        for (int j = 0; j < kG; ++j) {
+      for (int j = 0; j < kG; ++j) {
+        if (ZOH) {
           const float em1 = expm1_f(dt * Av[j]);
           dA[t][j] = em1;  // ZOH keeps expm1(dt A); exp(dt A) = 1 + it
-          hl[j] = __builtin_fmaf(em1 + 1.0f, hl[j], em1 * iA[j] * Bv[j] * u);
-        }
-      } else {
-        const float du = dt * u;
-        du_s[tb][c] = du;
-#pragma unroll
-        for (int j = 0; j < kG; ++j) {
+          hl[j] = __builtin_fmaf(em1 + 1.0f, hl[j], em1 * iA[j] * Bv[j] * du);
+        } else {
           dA[t][j] = exp2_hw(dt * A2[j]);
           hl[j] = __builtin_fmaf(dA[t][j], hl[j], du * Bv[j]);
         }
       }
     }
-    // ---- 2. publish this segment's transfer h -> P h + S
+    // ---- 3. publish this segment's transfer, then compose
+    {
+      float P[kG];
 #pragma unroll
-    for (int j = 0; j < kG; ++j) {
-      agg_s[wv][lane][j] = exp2_hw(A2[j] * sumdt);
-      agg_s[wv][lane][kG + j] = hl[j];
+      for (int j = 0; j < kG; ++j) P[j] = exp2_hw(A2[j] * sumdt);
+      agg_s[wv][0][lane] = make_float4(P[0], P[1], P[2], P[3]);
+      agg_s[wv][1][lane] = make_float4(P[4], P[5], P[6], P[7]);
+      agg_s[wv][2][lane] = make_float4(hl[0], hl[1], hl[2], hl[3]);
+      agg_s[wv][3][lane] = make_float4(hl[4], hl[5], hl[6], hl[7]);
     }
     __syncthreads();
-    // ---- compose: h_in of this segment, and the carry into the next block
-    float hin[kG];
-#pragma unroll
-    for (int j = 0; j < kG; ++j) hin[j] = carry[j];
-    for (int w2 = 0; w2 < kW; ++w2) {
-      if (w2 == wv) {
-#pragma unroll
-        for (int j = 0; j < kG; ++j) hin[j] = carry[j];
-      }
-      const float4 *ag = (const float4 *)&agg_s[w2][lane][0];
-      const float4 P0 = ag[0], P1 = ag[1], S0 = ag[2], S1 = ag[3];
+    // carry <- transfers of waves 0 .. wv-1 (this segment's h_in), then of the rest
+    auto fold = [&](int w2) {
+      const float4 P0 = agg_s[w2][0][lane], P1 = agg_s[w2][1][lane];
+      const float4 S0 = agg_s[w2][2][lane], S1 = agg_s[w2][3][lane];
       const float Pv[kG] = {P0.x, P0.y, P0.z, P0.w, P1.x, P1.y, P1.z, P1.w};
       const float Sv[kG] = {S0.x, S0.y, S0.z, S0.w, S1.x, S1.y, S1.z, S1.w};
 #pragma unroll
       for (int j = 0; j < kG; ++j) carry[j] = __builtin_fmaf(Pv[j], carry[j], Sv[j]);
-    }
-    // ---- 3. replay from the true h_in; y from the two half-sums of the channel
+    };
+    for (int w2 = 0; w2 < wv; ++w2) fold(w2);
+    float hin[kG];
+#pragma unroll
+    for (int j = 0; j < kG; ++j) hin[j] = carry[j];
+    for (int w2 = wv; w2 < kW; ++w2) fold(w2);
+    // ---- 4. replay from the true h_in; y from the two half-sums of the channel
     float h[kG];
 #pragma unroll
     for (int j = 0; j < kG; ++j) h[j] = hin[j];
@@ -298,13 +343,13 @@ __global__ __launch_bounds__(kW * 64) void scan_chunked_kernel(ScanArgs a) {
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
         const int tb = tb0 + t + e;
-        const float4 B0 = *(const float4 *)&bc_s[tb][kG * p];
-        const float4 B1 = *(const float4 *)&bc_s[tb][kG * p + 4];
-        const float4 C0 = *(const float4 *)&bc_s[tb][kN + kG * p];
-        const float4 C1 = *(const float4 *)&bc_s[tb][kN + kG * p + 4];
+        const float4 B0 = *(const float4 *)&bc_s[cur][tb][kG * p];
+        const float4 B1 = *(const float4 *)&bc_s[cur][tb][kG * p + 4];
+        const float4 C0 = *(const float4 *)&bc_s[cur][tb][kN + kG * p];
+        const float4 C1 = *(const float4 *)&bc_s[cur][tb][kN + kG * p + 4];
         const float Bv[kG] = {B0.x, B0.y, B0.z, B0.w, B1.x, B1.y, B1.z, B1.w};
         const float Cv[kG] = {C0.x, C0.y, C0.z, C0.w, C1.x, C1.y, C1.z, C1.w};
-        const float du = du_s[tb][c];
+        const float du = pd_s[tb][c].y;
         float yy = 0.f;
 #pragma unroll
         for (int j = 0; j < kG; ++j) {
@@ -324,9 +369,8 @@ __global__ __launch_bounds__(kW * 64) void scan_chunked_kernel(ScanArgs a) {
       const float other = __builtin_bit_cast(
           float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, send), 0xB1, 0xF, 0xF, false));
       const int tb = tb0 + t + p;
-      const float u = u_s[tb][c];
-      const float z = io<T>::cvt(z_s[tb][c]);
-      const float yv = __builtin_fmaf(Dv, u, keep + other) * silu_f(z);
+      const float2 eg = eg_s[tb][c];
+      const float yv = (keep + other + eg.x) * eg.y;
       if (T0 + tb < a.L) io<T>::st(yb + (int64_t)(T0 + tb) * a.D + ch, yv);
     }
   }

@@ -45,12 +45,17 @@ def _shape(**kw):
 
 def test_workspace_size_formula():
     import torch
+    up = lambda v: (v + 255) // 256 * 256  # noqa: E731
     s = _shape()
     T, D, R, N = 4096, 8192, 256, 16
-    up = lambda v: (v + 255) // 256 * 256  # noqa: E731
-    # u hi+lo, xdbl, dt_low hi+lo, B|C, dt (fp16)
+    # T < 32768: conv -> u hi+lo, xdbl, dt_low hi+lo, B|C, dt (fp16)
     expect = (2 * up(T * D * 2) + up(T * (R + 2 * N) * 4) + 2 * up(T * R * 2) + up(T * 2 * N * 4)
               + up(T * D * 2))
+    assert mm.prefill_workspace_bytes(s) == expect
+    s = _shape(seqlen=131072)
+    T = 131072
+    # fused conv/x_proj/RMSNorm path: dt_low hi+lo, B|C, dt (fp16)
+    expect = 2 * up(T * R * 2) + up(T * 2 * N * 4) + up(T * D * 2)
     assert mm.prefill_workspace_bytes(s) == expect
     s32 = _shape(dtype=torch.float32, d_inner=64, dt_rank=8, seqlen=256)
     T, D, R = 256, 64, 8
