@@ -66,6 +66,37 @@ __device__ __forceinline__ float softplus_f(float v) {
   return __builtin_amdgcn_logf(w) * 0.69314718055994531f * (e * __builtin_amdgcn_rcpf(w - 1.0f));
 }
 
+// Wait until every vector-memory operation of this wave has completed, without waiting on the
+// LDS/scalar or export counters. (Stores and direct-to-LDS loads need not retire in issue order,
+// so a partial vmcnt wait cannot prove a staged tile has landed.)
+__device__ __forceinline__ void wait_vmem_all() {
+  __builtin_amdgcn_s_waitcnt(0 | (0x7 << 4) | (0xF << 8));
+}
+
+// Workgroup barrier that orders LDS only: this wave's LDS reads and writes complete, then all
+// waves meet. Global stores and direct-to-LDS prefetches issued before it stay in flight (a
+// __syncthreads() would drain them); a prefetch that other waves read after a barrier must be
+// waited for explicitly (wait_vmem_le) before it. The memory clobber keeps the compiler from
+// moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Direct-to-LDS 16-byte load issued opaquely: lane i of the wave writes bytes
+// [lds_base + 16 i, +16) of LDS from its own global address. The compiler does not see the LDS
+// write, so it inserts no waits for it; the caller synchronises (wait_vmem_le + barrier) before
+// any wave reads that LDS. lds_base must be wave-uniform. No VGPR is written by the load.
+__device__ __forceinline__ void dma16_opaque(const void *gptr, uint32_t lds_base) {
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_base);
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(gptr), "s"(m0v)
+               : "memory", "m0");
+}
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
+}
+
 // ---------------------------------------------------------------- launch geometry
 // Workgroup i runs on XCD (i mod 8). Map hardware ids so that logical ids
 // [k*per, (k+1)*per) all run on XCD k in dispatch order: neighbouring tiles that

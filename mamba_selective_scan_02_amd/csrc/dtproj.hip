@@ -56,7 +56,8 @@ __global__ __launch_bounds__(512) void dtproj_kernel(DtprojArgs a, int ch_per_wg
   constexpr int S = R / 8;             // 16-byte slots per W_dt row
   constexpr int KS = R / 32;           // k-steps
   constexpr int RPW = 64 / S > 0 ? 64 / S : 1;  // rows per 1 KB wave-load (S <= 64)
-  __shared__ __attribute__((aligned(16))) bf16_t w_s[2][kChD][R];
+  __shared__ __attribute__((aligned(16))) bf16_t w_s0[kChD][R];
+  __shared__ __attribute__((aligned(16))) bf16_t w_s1[kChD][R];
 
   const int ntok = (a.T + kTokD - 1) / kTokD;
   const int gid = xcd_remap(blockIdx.x, gridDim.x);
@@ -76,22 +77,32 @@ __global__ __launch_bounds__(512) void dtproj_kernel(DtprojArgs a, int ch_per_wg
     fl[ks] = *(const uint4 *)(a.dtlow_lo + (int64_t)tokc * R + ks * 32 + g * 8);
   }
 
-  auto stage = [&](int ck, int buf) {
+  auto stage = [&](int ck, bf16_t (*wdst)[R]) {
     const int c0 = cbeg + ck * kChD;
     constexpr int loads = kChD * S / 64;           // 1 KB wave-loads per chunk
     for (int ld = wv; ld < loads; ld += 8) {
       const int e = ld * 64 + lane;                // 16-byte slot index within the chunk
       const int r = e / S, ps = e % S;
-      load_lds16(a.w + (int64_t)(c0 + r) * R + swz<S>(r, ps) * 8, &w_s[buf][0][0] + ld * 512);
+      load_lds16(a.w + (int64_t)(c0 + r) * R + swz<S>(r, ps) * 8, &wdst[0][0] + ld * 512);
     }
   };
 
-  stage(0, 0);
-  for (int ck = 0; ck < nck; ++ck) {
-    const int buf = ck & 1;
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (ck + 1 < nck) stage(ck + 1, buf ^ 1);
+  // Outputs of chunk ck are stored at the start of chunk ck+1, after that chunk's wait, so
+  // the wait for the staged W_dt rows never has to cover freshly issued stores.
+  uint2 pend[4];
+  int pend_c = -1;
+  auto flush = [&]() {
+    if (pend_c >= 0 && tok < a.T) {
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+        *(uint2 *)(a.dt + (int64_t)tok * a.D + pend_c + nb * 16 + 4 * g) = pend[nb];
+    }
+  };
+  auto chunk = [&](int ck, bf16_t (*wcur)[R], bf16_t (*wnxt)[R]) {
+    wait_vmem_all();   // this chunk's W_dt rows (and older stores) have landed
+    lds_barrier();     // ... for every wave; the other buffer is free
+    if (ck + 1 < nck) stage(ck + 1, wnxt);
+    flush();
     f32x4 acc[4];
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -103,25 +114,28 @@ __global__ __launch_bounds__(512) void dtproj_kernel(DtprojArgs a, int ch_per_wg
       for (int nb = 0; nb < 4; ++nb) {
         const int r = nb * 16 + tl;
         const bf16x8 fw = __builtin_bit_cast(
-            bf16x8, *(const uint4 *)&w_s[buf][r][swz<S>(r, ks * 4 + g) * 8]);
+            bf16x8, *(const uint4 *)&wcur[r][swz<S>(r, ks * 4 + g) * 8]);
         acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fw, bl, acc[nb], 0, 0, 0);
         acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fw, bh, acc[nb], 0, 0, 0);
       }
     }
     // acc[nb][j] = pre-activation of (token tok, channel c0 + 16 nb + 4 g + j)
-    if (tok < a.T) {
-      const int c0 = cbeg + ck * kChD;
+    const int c0 = cbeg + ck * kChD;
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
-        const int c = c0 + nb * 16 + 4 * g;
-        const float4 bv = *(const float4 *)(a.bias + c);
-        uint2 o;
-        o.x = pack_h2(softplus_h(acc[nb][0] + bv.x), softplus_h(acc[nb][1] + bv.y));
-        o.y = pack_h2(softplus_h(acc[nb][2] + bv.z), softplus_h(acc[nb][3] + bv.w));
-        *(uint2 *)(a.dt + (int64_t)tok * a.D + c) = o;
-      }
+    for (int nb = 0; nb < 4; ++nb) {
+      const float4 bv = *(const float4 *)(a.bias + c0 + nb * 16 + 4 * g);
+      pend[nb].x = pack_h2(softplus_h(acc[nb][0] + bv.x), softplus_h(acc[nb][1] + bv.y));
+      pend[nb].y = pack_h2(softplus_h(acc[nb][2] + bv.z), softplus_h(acc[nb][3] + bv.w));
     }
+    pend_c = c0;
+  };
+
+  stage(0, w_s0);
+  for (int ck = 0; ck < nck; ++ck) {
+    const bool odd = ck & 1;
+    chunk(ck, odd ? w_s1 : w_s0, odd ? w_s0 : w_s1);
   }
+  flush();
 }
 
 template <int R>

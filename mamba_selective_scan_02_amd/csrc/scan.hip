@@ -125,9 +125,10 @@ constexpr int kHalo = 3;                  // x rows before the block (conv windo
 constexpr int kXRows = kBlk + 16;         // staged x rows: halo + block, padded to 16-row loads
 
 // One direct-to-LDS 16-byte load per lane: lane i of the wave fills bytes [16 i, 16 i + 16)
-// of the 1 KB LDS window at `lds` (wave-uniform).
+// of the 1 KB LDS window at `lds` (wave-uniform). Issued opaquely (see dma16_opaque): the block
+// loop waits for it explicitly.
 __device__ __forceinline__ void load_lds16(const void *src, void *lds) {
-  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)lds, 16, 0, 0);
+  dma16_opaque(src, lds_addr(lds));
 }
 
 template <typename T, bool ZOH, int K>
@@ -140,8 +141,10 @@ __global__ __launch_bounds__(kW * 64) void scan_chunked_kernel(ScanArgs a) {
   // global memory in the prep phase, which keeps its LDS within 160 KB.
   constexpr bool kStageXZD = sizeof(T) == 2;
   constexpr int kXR = kStageXZD ? kXRows : 1, kZR = kStageXZD ? kBlk : 1;
-  // staging (written by async loads)
-  __shared__ __attribute__((aligned(16))) float bc_s[2][kBlk][2 * kN];
+  // staging (written by async loads); B|C double-buffered in two arrays so that the compiler
+  // can tell the prefetch target from the tile being read
+  __shared__ __attribute__((aligned(16))) float bc_s0[kBlk][2 * kN];
+  __shared__ __attribute__((aligned(16))) float bc_s1[kBlk][2 * kN];
   __shared__ __attribute__((aligned(16))) T x_s[kXR][kCh];
   __shared__ __attribute__((aligned(16))) T z_s[kZR][kCh];
   __shared__ __attribute__((aligned(16))) DT d_s[kZR][kCh];
@@ -172,11 +175,6 @@ __global__ __launch_bounds__(kW * 64) void scan_chunked_kernel(ScanArgs a) {
   // prep thread: channel pc, tokens 8*pt .. 8*pt+7 of the block
   const int pc = tid & (kCh - 1), pt = tid >> 5;
   const int pch = ch0 + pc;
-  float wc[K];
-#pragma unroll
-  for (int k = 0; k < K; ++k) wc[k] = io<T>::cvt(((const T *)a.conv_w)[(int64_t)pch * K + k]);
-  const float cb = a.conv_b ? io<T>::cvt(((const T *)a.conv_b)[pch]) : 0.0f;
-  const float Dp = a.Dskip[pch];
 
   const int64_t row = 2LL * a.D;
   const T *xzb = (const T *)a.xz + (int64_t)b * a.L * row;
@@ -188,47 +186,70 @@ __global__ __launch_bounds__(kW * 64) void scan_chunked_kernel(ScanArgs a) {
 
   // Issue the direct-to-LDS loads of block `blk` (rows past the end read row L-1 so every
   // address is valid; prep and the scan ignore those rows).
-  auto stage = [&](int blk) {
+  auto stage = [&](int blk, float (*bcdst)[2 * kN]) {
     const int T0 = blk * kBlk;
+    // Rows past the end read row L-1 (valid addresses; prep and the scan ignore them). Addresses
+    // are a wave-uniform per-block base plus 32-bit lane offsets.
+    const int rmax = Lm1 - T0;                    // last valid block-relative row
     // B|C: 128 rows x 128 B = 16 KB = 16 wave-loads; wave wv does loads wv and wv + 8
+    const float *bcbase = bcb + (int64_t)T0 * 2 * kN;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int ld = wv + i * kW;                 // 1 KB window index
-      const int r = ld * 8 + (lane >> 3);         // 8 lanes per 128-byte row
-      const int t = min(T0 + r, Lm1);
-      load_lds16(bcb + (int64_t)t * 2 * kN + (lane & 7) * 4, &bc_s[blk & 1][ld * 8][0]);
+      const int r = min(ld * 8 + (lane >> 3), rmax);   // 8 lanes per 128-byte row
+      load_lds16(bcbase + (uint32_t)(r * 2 * kN + (lane & 7) * 4), &bcdst[ld * 8][0]);
     }
     if (!kStageXZD) return;
-    // x: kXRows rows x 64 B (bf16) = 9 wave-loads of 16 rows; rows T0-3 .. ; row r <-> token T0-3+r
+    // x: kXRows rows x 64 B (bf16) = 9 wave-loads of 16 rows; row r <-> token T0 - 3 + r
     constexpr int xrpl = 64 / xrow_chunks;        // rows per wave-load
+    const T *xbase = xzb + (int64_t)T0 * row + ch0;
+    const uint32_t rowe = (uint32_t)row;
     for (int ld = wv; ld < kXRows / xrpl; ld += kW) {
-      const int r = ld * xrpl + lane / xrow_chunks;
-      const int t = min(max(T0 - kHalo + r, 0), Lm1);
-      load_lds16(xzb + (int64_t)t * row + ch0 + (lane % xrow_chunks) * xper, &x_s[ld * xrpl][0]);
+      const int r = min(max(ld * xrpl + lane / xrow_chunks - kHalo, -T0), rmax);
+      load_lds16(xbase + (int)(r * (int)rowe) + (lane % xrow_chunks) * xper, &x_s[ld * xrpl][0]);
     }
     for (int ld = wv; ld < kBlk / xrpl; ld += kW) {
-      const int r = ld * xrpl + lane / xrow_chunks;
-      const int t = min(T0 + r, Lm1);
-      load_lds16(xzb + (int64_t)t * row + a.D + ch0 + (lane % xrow_chunks) * xper, &z_s[ld * xrpl][0]);
+      const int r = min(ld * xrpl + lane / xrow_chunks, rmax);
+      load_lds16(xbase + a.D + (uint32_t)(r * rowe) + (lane % xrow_chunks) * xper,
+                 &z_s[ld * xrpl][0]);
     }
     constexpr int drpl = 64 / drow_chunks;
     constexpr int dper = 16 / sizeof(DT);
+    const DT *dbase = db + (int64_t)T0 * a.D + ch0;
     for (int ld = wv; ld < kBlk / drpl; ld += kW) {
-      const int r = ld * drpl + lane / drow_chunks;
-      const int t = min(T0 + r, Lm1);
-      load_lds16(db + (int64_t)t * a.D + ch0 + (lane % drow_chunks) * dper, &d_s[ld * drpl][0]);
+      const int r = min(ld * drpl + lane / drow_chunks, rmax);
+      load_lds16(dbase + (uint32_t)(r * a.D) + (lane % drow_chunks) * dper, &d_s[ld * drpl][0]);
     }
   };
 
-  stage(0);
-  for (int blk = 0; blk < nblocks; ++blk) {
+  // y of block b is stored at the start of block b+1, after that block's wait, so the wait
+  // for the staged tiles never has to cover freshly issued stores. Lane (c, p) owns tokens
+  // tb0 + 2i + p of its wave's segment.
+  float ypend[kS / 2];
+  int ypend_t0 = -1;
+  auto flush = [&]() {
+    if (ypend_t0 < 0) return;
+#pragma unroll
+    for (int i = 0; i < kS / 2; ++i) {
+      const int t = ypend_t0 + wv * kS + 2 * i + p;
+      if (t < a.L) io<T>::st(yb + (int64_t)t * a.D + ch, ypend[i]);
+    }
+  };
+  auto block = [&](int blk, float (*bc_cur)[2 * kN], float (*bc_nxt)[2 * kN]) {
     const int T0 = blk * kBlk;
-    const int cur = blk & 1;
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's direct-to-LDS loads have landed
-    __syncthreads();                // ... and every wave's; previous block fully consumed
+    wait_vmem_all();   // this wave's staged tiles (and its older stores) have landed
+    lds_barrier();     // ... and every wave's; the previous block is fully consumed
+    flush();
 
     // ---- 1. prep: conv + SiLU, dt, dt*u, D*u, SiLU(z) for (pc, tokens 8pt..8pt+7)
     {
+      // per-channel constants, reloaded each block (cache hits) to keep them out of the
+      // registers that live across the scan
+      float wc[K];
+#pragma unroll
+      for (int k = 0; k < K; ++k) wc[k] = io<T>::cvt(((const T *)a.conv_w)[(int64_t)pch * K + k]);
+      const float cb = a.conv_b ? io<T>::cvt(((const T *)a.conv_b)[pch]) : 0.0f;
+      const float Dp = a.Dskip[pch];
       // block-relative token tb (tb >= -3, T0 + tb < L where it matters)
       auto getx = [&](int tb) -> float {
         if (kStageXZD) return io<T>::cvt(x_s[(kStageXZD ? tb + kHalo : 0)][pc]);
@@ -275,10 +296,10 @@ __global__ __launch_bounds__(kW * 64) void scan_chunked_kernel(ScanArgs a) {
         eg_s[tb][pc] = make_float2(valid ? Dp * u : 0.f, valid ? silu_f(z) : 0.f);
       }
     }
-    __syncthreads();
+    lds_barrier();
     // next block's staging overlaps this block's scan (x, z, dt tiles are free after prep;
     // B|C is double-buffered)
-    if (blk + 1 < nblocks) stage(blk + 1);
+    if (blk + 1 < nblocks) stage(blk + 1, bc_nxt);
 
     // ---- 2. local pass over this wave's segment
     const int tb0 = wv * kS;
@@ -293,8 +314,8 @@ __global__ __launch_bounds__(kW * 64) void scan_chunked_kernel(ScanArgs a) {
       const float2 pd = pd_s[tb][c];
       const float dt = pd.x, du = pd.y;
       sumdt += dt;
-      const float4 B0 = *(const float4 *)&bc_s[cur][tb][kG * p];
-      const float4 B1 = *(const float4 *)&bc_s[cur][tb][kG * p + 4];
+      const float4 B0 = *(const float4 *)&bc_cur[tb][kG * p];
+      const float4 B1 = *(const float4 *)&bc_cur[tb][kG * p + 4];
       const float Bv[kG] = {B0.x, B0.y, B0.z, B0.w, B1.x, B1.y, B1.z, B1.w};
 #pragma unroll
       for (int j = 0; j < kG; ++j) {
@@ -318,7 +339,7 @@ __global__ __launch_bounds__(kW * 64) void scan_chunked_kernel(ScanArgs a) {
       agg_s[wv][2][lane] = make_float4(hl[0], hl[1], hl[2], hl[3]);
       agg_s[wv][3][lane] = make_float4(hl[4], hl[5], hl[6], hl[7]);
     }
-    __syncthreads();
+    lds_barrier();
     // carry <- transfers of waves 0 .. wv-1 (this segment's h_in), then of the rest
     auto fold = [&](int w2) {
       const float4 P0 = agg_s[w2][0][lane], P1 = agg_s[w2][1][lane];
@@ -343,10 +364,10 @@ __global__ __launch_bounds__(kW * 64) void scan_chunked_kernel(ScanArgs a) {
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
         const int tb = tb0 + t + e;
-        const float4 B0 = *(const float4 *)&bc_s[cur][tb][kG * p];
-        const float4 B1 = *(const float4 *)&bc_s[cur][tb][kG * p + 4];
-        const float4 C0 = *(const float4 *)&bc_s[cur][tb][kN + kG * p];
-        const float4 C1 = *(const float4 *)&bc_s[cur][tb][kN + kG * p + 4];
+        const float4 B0 = *(const float4 *)&bc_cur[tb][kG * p];
+        const float4 B1 = *(const float4 *)&bc_cur[tb][kG * p + 4];
+        const float4 C0 = *(const float4 *)&bc_cur[tb][kN + kG * p];
+        const float4 C1 = *(const float4 *)&bc_cur[tb][kN + kG * p + 4];
         const float Bv[kG] = {B0.x, B0.y, B0.z, B0.w, B1.x, B1.y, B1.z, B1.w};
         const float Cv[kG] = {C0.x, C0.y, C0.z, C0.w, C1.x, C1.y, C1.z, C1.w};
         const float du = pd_s[tb][c].y;
@@ -370,10 +391,17 @@ __global__ __launch_bounds__(kW * 64) void scan_chunked_kernel(ScanArgs a) {
           float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, send), 0xB1, 0xF, 0xF, false));
       const int tb = tb0 + t + p;
       const float2 eg = eg_s[tb][c];
-      const float yv = (keep + other + eg.x) * eg.y;
-      if (T0 + tb < a.L) io<T>::st(yb + (int64_t)(T0 + tb) * a.D + ch, yv);
+      ypend[t / 2] = (keep + other + eg.x) * eg.y;
     }
+    ypend_t0 = T0;
+  };
+
+  stage(0, bc_s0);
+  for (int blk = 0; blk < nblocks; ++blk) {
+    const bool odd = blk & 1;
+    block(blk, odd ? bc_s1 : bc_s0, odd ? bc_s0 : bc_s1);
   }
+  flush();
   if (a.state && wv == 0) {
 #pragma unroll
     for (int j = 0; j < kG; ++j) a.state[((int64_t)b * a.D + ch) * kN + kG * p + j] = carry[j];

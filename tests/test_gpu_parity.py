@@ -112,6 +112,14 @@ def test_both_scan_kernels_bf16(scan, L):
           scan=scan)
 
 
+@pytest.mark.parametrize("B,L,R", [(1, 32768 + 77, 64), (2, 16448, 128)])
+def test_bf16_fused_projection_path(B, L, R):
+    # >= 32768 tokens selects the fused conv + x_proj + RMSNorm kernel (128-token tiles, ragged
+    # last tile) and the token-stationary dt_proj kernel
+    cfg = synth.MixerConfig(f"bf16_fused_R{R}", B, L, 256, 16, 4, R, "bf16")
+    _case(cfg, 111 + R, states=True, conv_bias=True, gamma_random=True)
+
+
 def test_chunked_prefill_equals_whole_on_gpu_and_oracle():
     """Prefill over L1 tokens, then L2 more from the returned states, equals one prefill
     (associativity of the page's scan operator); checked against the oracle."""
