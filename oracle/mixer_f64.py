@@ -127,7 +127,7 @@ def as_f64_params(p: dict) -> dict:
 
 
 def mixer_prefill(xz, p, conv_state0=None, ssm_state0=None, eps=1e-6, zoh=False,
-                  channels=None, token_block=None):
+                  channels=None, token_block=None, workers=1):
     """The whole mixer core over a batch of sequences.
 
     xz: [B, L, 2D] (x = first half, z = second half); p: dict of float64 arrays
@@ -137,8 +137,10 @@ def mixer_prefill(xz, p, conv_state0=None, ssm_state0=None, eps=1e-6, zoh=False,
 
     channels: optional index array; when given, y and the SSM state are computed
     only for those channels (the convolution and x_proj still cover every channel,
-    since B, C and dt_low depend on all of them). token_block bounds the memory of
-    the convolution / x_proj pass for long sequences; it does not change any result.
+    since B, C and dt_low depend on all of them). token_block / workers split the
+    convolution + x_proj + RMSNorm pass into independent token blocks (each takes its
+    K-1 preceding inputs from x, or from the carried state before token 0) evaluated
+    on a thread pool; neither changes any result. The scan itself is sequential.
 
     Returns (y [B, L, Dsel], conv_state [B, D, K-1], ssm_state [B, Dsel, N]).
     """
@@ -151,26 +153,51 @@ def mixer_prefill(xz, p, conv_state0=None, ssm_state0=None, eps=1e-6, zoh=False,
     tb = L if token_block is None else token_block
     ys, css, sss = [], [], []
     for b in range(B_):
-        # Pass over tokens: conv + SiLU for all channels, x_proj, RMSNorm of each slice.
-        state = None if conv_state0 is None else np.asarray(conv_state0[b], np.float64)
+        state0 = None if conv_state0 is None else np.asarray(conv_state0[b], np.float64)
         u_sel = np.empty((L, len(sel)))
         dtlow = np.empty((L, R))
         Bm = np.empty((L, N))
         Cm = np.empty((L, N))
-        for t0 in range(0, L, tb):
+
+        def run_block(t0, b=b, state0=state0):
+            # conv + SiLU for all channels, x_proj, RMSNorm of each slice, for tokens [t0, t1)
             t1 = min(L, t0 + tb)
-            xblk = _f64(xz[b, t0:t1, :D])
-            u, state = causal_conv1d_silu(xblk, p["conv_w"], p.get("conv_b"), state)
+            if t0 == 0:
+                pre = state0
+            else:
+                lo = max(0, t0 - (K - 1))
+                rows = _f64(xz[b, lo:t0, :D])
+                if rows.shape[0] < K - 1:  # the window reaches back before token 0
+                    head = (np.zeros((K - 1, D)) if state0 is None else state0.T)
+                    rows = np.concatenate([head[rows.shape[0]:], rows], axis=0)
+                pre = rows.T
+            u, _ = causal_conv1d_silu(_f64(xz[b, t0:t1, :D]), p["conv_w"], p.get("conv_b"), pre)
             xd = x_proj(u, p["x_proj_w"])
             a, bb, c = split_xdbl(xd, R, N)
             dtlow[t0:t1] = rmsnorm(a, p["dt_norm_w"], eps)
             Bm[t0:t1] = rmsnorm(bb, p["B_norm_w"], eps)
             Cm[t0:t1] = rmsnorm(c, p["C_norm_w"], eps)
             u_sel[t0:t1] = u[:, sel]
-        if state is None:
-            state = np.zeros((D, K - 1))
+
+        starts = list(range(0, L, tb))
+        if workers > 1 and len(starts) > 1:
+            import concurrent.futures
+            import threadpoolctl
+            # one BLAS thread per block: the pool supplies the parallelism
+            with threadpoolctl.threadpool_limits(1), \
+                    concurrent.futures.ThreadPoolExecutor(max_workers=workers) as ex:
+                list(ex.map(run_block, starts))
+        else:
+            for t0 in starts:
+                run_block(t0)
+        # final conv state: the last K-1 inputs of concat(state0, x), oldest first
+        tail = _f64(xz[b, max(0, L - (K - 1)):L, :D])
+        if tail.shape[0] < K - 1:
+            head = np.zeros((K - 1, D)) if state0 is None else state0.T
+            tail = np.concatenate([head[tail.shape[0]:], tail], axis=0)
+        state = tail.T.copy()
         dt = dt_proj_softplus(dtlow, p["dt_proj_w"][sel], p["dt_proj_b"][sel])
-        z = _f64(xz[b, :, D:])[:, sel]
+        z = _f64(xz[b][:, D + sel])
         h0 = None if ssm_state0 is None else np.asarray(ssm_state0[b], np.float64)[sel]
         y, h = selective_scan(u_sel, dt, p["A"][sel], Bm, Cm, p["Dskip"][sel], z, h0, zoh)
         ys.append(y)

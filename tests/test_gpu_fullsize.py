@@ -1,0 +1,118 @@
+"""GPU parity at the full workload sizes, in the launch configuration bench.py times.
+
+The GPU runs the whole workload; the fp64 oracle recomputes a seeded sample of outputs one by
+one: y and the final SSM state for a sample of channels over every token, and the final conv
+state (a copy of inputs) bit for bit for every channel. The oracle's convolution / x_proj /
+RMSNorm pass still covers every channel and token, since B, C and dt_low of each token mix all
+channels; it runs in token blocks on a thread pool (same results as one block).
+
+Workloads: 128K-token prefill (B=1, L=131072, d_inner 8192), 256K-token prefill with batch 2,
+and 512 batched decode steps (B=256) after a 1024-token prefill, for d_inner 8192 / dt_rank 256
+and the wide d_inner 16384 / dt_rank 512 variant.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from tests.parity import check, to64
+
+pytestmark = pytest.mark.gpu
+
+mm = pytest.importorskip("mamba_selective_scan_02_amd")
+
+WORKERS = min(16, os.cpu_count() or 1)
+
+
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _channels(D, n, seed):
+    rng = np.random.default_rng(seed)
+    picks = rng.choice(np.arange(1, D - 1), size=n - 2, replace=False)
+    return np.sort(np.concatenate([[0, D - 1], picks]))
+
+
+def _host(t):
+    """bf16 device tensor -> host float64 numpy, in pieces to bound peak host memory."""
+    return t.detach().cpu()
+
+
+@pytest.mark.parametrize("name", ["long_prefill_128k", "prefill_256k_b2"])
+def test_fullsize_prefill_sampled_channels(name):
+    _need_gpu()
+    cfg = synth.CONFIGS[name]
+    seed = synth.seed_for(name)
+    print(f"[fullsize] {name} B={cfg.batch} L={cfg.seqlen} D={cfg.d_inner}", flush=True)
+    dev = "cuda"
+    p = synth.make_params(cfg, seed, dev)
+    xz = synth.make_xz(cfg, seed, dev)
+    cs = torch.zeros(cfg.batch, cfg.d_inner, cfg.d_conv - 1, dtype=cfg.torch_dtype, device=dev)
+    ss = torch.zeros(cfg.batch, cfg.d_inner, cfg.d_state, dtype=torch.float32, device=dev)
+    y = mm.prefill(xz, p, conv_state=cs, ssm_state=ss, states_valid=False, eps=cfg.rms_eps)
+    torch.cuda.synchronize()
+    sel = _channels(cfg.d_inner, 32, seed)
+    y_sel = to64(y[:, :, torch.as_tensor(sel, device=dev)])
+    ss_sel, cs_gpu = to64(ss[:, torch.as_tensor(sel, device=dev)]), to64(cs)
+    del y
+    xz_h = _host(xz)
+    del xz
+    torch.cuda.empty_cache()
+    print("[fullsize] oracle ...", flush=True)
+    yr, csr, ssr = oracle.mixer_prefill(xz_h, oracle.as_f64_params(p), eps=cfg.rms_eps,
+                                        channels=sel, token_block=4096, workers=WORKERS)
+    e_y = check(y_sel, yr, "bf16", f"{name} y (sampled channels)")
+    e_s = check(ss_sel, ssr, "bf16", f"{name} ssm_state (sampled channels)")
+    np.testing.assert_array_equal(cs_gpu, csr)
+    print(f"[fullsize] {name}: y err {e_y:.3e}, state err {e_s:.3e}", flush=True)
+
+
+@pytest.mark.parametrize("name", ["decode_b256", "decode_b256_wide"])
+def test_fullsize_decode_sampled_sequences(name):
+    _need_gpu()
+    cfg = synth.CONFIGS[name]
+    seed = synth.seed_for(name)
+    print(f"[fullsize] {name} B={cfg.batch} D={cfg.d_inner} R={cfg.dt_rank} "
+          f"steps={cfg.decode_steps} prefix={cfg.decode_prefix}", flush=True)
+    dev = "cuda"
+    p = synth.make_params(cfg, seed, dev)
+    cs = torch.zeros(cfg.batch, cfg.d_inner, cfg.d_conv - 1, dtype=cfg.torch_dtype, device=dev)
+    ss = torch.zeros(cfg.batch, cfg.d_inner, cfg.d_state, dtype=torch.float32, device=dev)
+    pre = synth.make_xz(cfg, seed, dev, seqlen=cfg.decode_prefix)
+    mm.prefill(pre, p, conv_state=cs, ssm_state=ss, states_valid=False, eps=cfg.rms_eps)
+    seqs = np.array([0, 77, 200, cfg.batch - 1])
+    sq = torch.as_tensor(seqs, device=dev)
+    cs_pre, ss_pre = to64(cs[sq]), to64(ss[sq])
+    pre_h = _host(pre[sq])
+    del pre
+    xs = synth.make_xz(cfg, seed, dev, seqlen=cfg.decode_steps, tensor="decode_xz")
+    xs = xs.transpose(0, 1).contiguous()                          # [steps, B, 2D]
+    check_steps = {0, 1, 2, 63, 255, cfg.decode_steps - 1}
+    ys = {}
+    for step in range(cfg.decode_steps):
+        y = mm.decode_step(xs[step], p, cs, ss, eps=cfg.rms_eps)
+        if step in check_steps:
+            ys[step] = to64(y[sq])
+    torch.cuda.synchronize()
+    cs_end, ss_end = to64(cs[sq]), to64(ss[sq])
+    xs_h = _host(xs[:, sq])
+    del xs
+    print("[fullsize] oracle ...", flush=True)
+    p64 = oracle.as_f64_params(p)
+    _, csr, ssr = oracle.mixer_prefill(pre_h, p64, eps=cfg.rms_eps, token_block=256,
+                                      workers=WORKERS)
+    np.testing.assert_array_equal(cs_pre, csr)
+    check(ss_pre, ssr, "bf16", f"{name} prefill ssm_state")
+    worst = 0.0
+    for step in range(cfg.decode_steps):
+        yr, csr, ssr = oracle.mixer_decode_step(xs_h[step], p64, csr, ssr, eps=cfg.rms_eps)
+        if step in check_steps:
+            worst = max(worst, check(ys[step], yr, "bf16", f"{name} y step {step}"))
+    np.testing.assert_array_equal(cs_end, csr)
+    e_s = check(ss_end, ssr, "bf16", f"{name} final ssm_state")
+    print(f"[fullsize] {name}: worst y err {worst:.3e}, final state err {e_s:.3e}", flush=True)

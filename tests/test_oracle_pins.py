@@ -302,6 +302,14 @@ def test_batch_independence_channel_subset_and_token_blocks():
     np.testing.assert_allclose(ysel, y[:, :, sel], rtol=1e-12, atol=1e-14)
     np.testing.assert_allclose(ssel, s[:, sel], rtol=1e-12, atol=1e-14)
     np.testing.assert_array_equal(csel, c)
+    # independent token blocks on a thread pool, including blocks shorter than K-1
+    for tb in (1, 2, 5):
+        for st in ((cs, ss), (None, None)):
+            r0 = oracle.mixer_prefill(xz, p, *st)
+            r1 = oracle.mixer_prefill(xz, p, *st, token_block=tb, workers=4)
+            np.testing.assert_allclose(r1[0], r0[0], rtol=1e-12, atol=1e-14)
+            np.testing.assert_array_equal(r1[1], r0[1])
+            np.testing.assert_allclose(r1[2], r0[2], rtol=1e-12, atol=1e-14)
 
 
 @pytest.mark.parametrize("mode", ["euler", "zoh"])
