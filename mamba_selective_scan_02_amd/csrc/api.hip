@@ -1,5 +1,6 @@
 // C ABI of the mixer library: argument validation, workspace layout, stage sequencing and
 // the per-stage timer. Declarations and contracts: include/mamba_mixer.h.
+#include <algorithm>
 #include <vector>
 
 #include "common.h"
@@ -16,26 +17,42 @@ inline size_t esz(mm_dtype d) { return d == MM_BF16 ? 2 : 4; }
 struct Workspace {
   bool fused_xproj;  // bf16: conv + x_proj + RMSNorm in one kernel (no u / xdbl buffers)
   bool tiled_dtproj; // bf16: token-stationary dt_proj kernel
-  size_t u, u_lo, xdbl, dtlow, dtlow_lo, bc, dt, total;
+  bool fast_decode;  // bf16 decode step: range-split x_proj, fused update (no u / xdbl buffers)
+  int dec_ranges, dec_range_ch;
+  size_t u, u_lo, xdbl, part, dtlow, dtlow_lo, bc, dt, total;
 };
 
 // Byte offsets of the prefill intermediates for T = batch * seqlen tokens.
 //   fp32 mode: u [T,D] f32 | xdbl [T,R+2N] f32 | dt_low [T,R] f32 | B,C [T,2N] f32 | dt [T,D] f32
 //   bf16 mode: (u_hi, u_lo [T,D] bf16 | xdbl f32, unless fused) | dt_low hi, lo [T,R] bf16 |
 //              B,C [T,2N] f32 | dt [T,D] f16
-Workspace layout(const mm_shape &s) {
+//   bf16 decode step: partial x_proj sums [ranges, B, R+2N] f32 replace u and xdbl.
+Workspace layout(const mm_shape &s, bool decode) {
   const size_t T = (size_t)s.batch * s.seqlen;
   const bool bf = s.io_dtype == MM_BF16;
   const size_t e = esz(s.io_dtype);
   Workspace w;
   // one workgroup per 128 tokens: worth it once there are enough tokens to fill the chip
-  w.fused_xproj = bf && T >= 32768 &&
+  w.fused_xproj = !decode && bf && T >= 32768 &&
                   xproj_fused_supported(s.dt_rank, s.d_state, s.d_inner, s.d_conv);
   w.tiled_dtproj = bf && dtproj_supported(s.dt_rank, s.d_inner);
+  w.fast_decode = decode && bf && decode_fast_supported(s.dt_rank, s.d_state, s.d_inner, s.d_conv);
+  w.dec_ranges = 0;
+  w.dec_range_ch = 0;
+  if (w.fast_decode) {
+    // enough (sequence tile, channel range) workgroups to fill the chip
+    const int seq_tiles = (s.batch + 63) / 64;
+    const int chunks = s.d_inner / 64;
+    const int want = std::min(chunks, std::max(1, (256 + seq_tiles - 1) / seq_tiles));
+    w.dec_range_ch = (chunks + want - 1) / want * 64;
+    w.dec_ranges = (s.d_inner + w.dec_range_ch - 1) / w.dec_range_ch;
+  }
+  const bool no_u = w.fused_xproj || w.fast_decode;
   size_t o = 0;
-  w.u = o; if (!w.fused_xproj) o += up(T * s.d_inner * e);
-  w.u_lo = o; if (bf && !w.fused_xproj) o += up(T * s.d_inner * 2);
-  w.xdbl = o; if (!w.fused_xproj) o += up(T * (s.dt_rank + 2 * s.d_state) * 4);
+  w.u = o; if (!no_u) o += up(T * s.d_inner * e);
+  w.u_lo = o; if (bf && !no_u) o += up(T * s.d_inner * 2);
+  w.xdbl = o; if (!no_u) o += up(T * (s.dt_rank + 2 * s.d_state) * 4);
+  w.part = o; if (w.fast_decode) o += up((size_t)w.dec_ranges * T * (s.dt_rank + 2 * s.d_state) * 4);
   w.dtlow = o; o += up(T * s.dt_rank * e);
   w.dtlow_lo = o; if (bf) o += up(T * s.dt_rank * 2);
   w.bc = o; o += up(T * 2 * s.d_state * 4);
@@ -125,10 +142,54 @@ struct StageScope {
     if ((expr) != hipSuccess) return MM_ERR_HIP;       \
   } while (0)
 
+// bf16 decode step with d_conv 4: range-split x_proj (conv recomputed per fragment) -> partial
+// reduction + RMSNorm -> dt_proj -> one kernel for conv, state update, gate and conv state.
+mm_status run_decode_fast(const mm_shape *s, const mm_params *p, const Workspace &w,
+                          const void *xz, void *y, void *conv_state, float *ssm_state, char *ws,
+                          hipStream_t st, mm_stage_timer *timer) {
+  const int B = s->batch, D = s->d_inner, R = s->dt_rank;
+  float *part = (float *)(ws + w.part);
+  uint16_t *dtlow = (uint16_t *)(ws + w.dtlow), *dtlow_lo = (uint16_t *)(ws + w.dtlow_lo);
+  float *bc = (float *)(ws + w.bc);
+  _Float16 *delta = (_Float16 *)(ws + w.dt);
+  const uint16_t *cw = (const uint16_t *)p->conv_w, *cb = (const uint16_t *)p->conv_b;
+  {
+    StageScope sc(timer, st, MM_STAGE_XPROJ);
+    DecodeXprojArgs xa{(const uint16_t *)xz, cw, cb, (const uint16_t *)conv_state,
+                       (const uint16_t *)p->x_proj_w, part, B, D, R, w.dec_range_ch};
+    MM_TRY(launch_decode_xproj(xa, st));
+  }
+  {
+    StageScope sc(timer, st, MM_STAGE_NORM);
+    DecodeNormArgs na{part, w.dec_ranges, dtlow, dtlow_lo, bc, p->dt_norm_w, p->B_norm_w,
+                      p->C_norm_w, s->rms_eps, B, R};
+    MM_TRY(launch_decode_norm(na, st));
+  }
+  {
+    StageScope sc(timer, st, MM_STAGE_DTPROJ);
+    if (w.tiled_dtproj) {
+      DtprojArgs da{dtlow, dtlow_lo, (const uint16_t *)p->dt_proj_w, p->dt_proj_b, delta, B, D, R};
+      MM_TRY(launch_dtproj_tiled(da, st));
+    } else {
+      MM_TRY(launch_dtproj(MM_BF16, dtlow, dtlow_lo, p->dt_proj_w, p->dt_proj_b, delta, B, D, R,
+                           st));
+    }
+  }
+  {
+    StageScope sc(timer, st, MM_STAGE_SCAN);
+    DecodeUpdateArgs ua{(const uint16_t *)xz, cw, cb, (uint16_t *)conv_state, delta, bc, p->A,
+                        p->Dskip, ssm_state, (uint16_t *)y, B, D};
+    MM_TRY(launch_decode_update(ua, (s->flags & MM_FLAG_ZOH_B) != 0, st));
+  }
+  return MM_OK;
+}
+
 mm_status run_mixer(const mm_shape *s, const mm_params *p, const void *xz, void *y,
                     void *conv_state, float *ssm_state, int states_valid, void *workspace,
-                    size_t workspace_bytes, hipStream_t st, mm_stage_timer *timer) {
-  const Workspace w = layout(*s);
+                    size_t workspace_bytes, hipStream_t st, mm_stage_timer *timer, bool decode) {
+  const Workspace w = layout(*s, decode);
+  if (w.fast_decode)
+    return run_decode_fast(s, p, w, xz, y, conv_state, ssm_state, (char *)workspace, st, timer);
   char *ws = (char *)workspace;
   const int B = s->batch, L = s->seqlen, D = s->d_inner, N = s->d_state, K = s->d_conv;
   const int R = s->dt_rank, T = B * L;
@@ -204,10 +265,10 @@ mm_status prefill_impl(const mm_shape *s, const mm_params *p, const void *xz, vo
     return MM_ERR_INVALID_ARG;
   if (states_valid != 0 && states_valid != 1) return MM_ERR_INVALID_ARG;
   if (!workspace || ((uintptr_t)workspace & (kAlign - 1)) ||
-      workspace_bytes < layout(*s).total)
+      workspace_bytes < layout(*s, false).total)
     return MM_ERR_WORKSPACE;
   return run_mixer(s, p, xz, y, conv_state, ssm_state, states_valid, workspace, workspace_bytes,
-                   (hipStream_t)stream, timer);
+                   (hipStream_t)stream, timer, false);
 }
 
 mm_status decode_impl(const mm_shape *s, const mm_params *p, const void *xz, void *y,
@@ -220,10 +281,10 @@ mm_status decode_impl(const mm_shape *s, const mm_params *p, const void *xz, voi
   if (!aligned(xz) || !aligned(y) || !aligned(conv_state) || !aligned(ssm_state))
     return MM_ERR_INVALID_ARG;
   if (!workspace || ((uintptr_t)workspace & (kAlign - 1)) ||
-      workspace_bytes < layout(*s).total)
+      workspace_bytes < layout(*s, true).total)
     return MM_ERR_WORKSPACE;
   return run_mixer(s, p, xz, y, conv_state, ssm_state, 1, workspace, workspace_bytes,
-                   (hipStream_t)stream, timer);
+                   (hipStream_t)stream, timer, true);
 }
 
 }  // namespace
@@ -232,12 +293,12 @@ extern "C" {
 
 size_t mm_prefill_workspace_bytes(const mm_shape *s) {
   if (check_shape(s, false) != MM_OK) return 0;
-  return layout(*s).total;
+  return layout(*s, false).total;
 }
 
 size_t mm_decode_workspace_bytes(const mm_shape *s) {
   if (check_shape(s, true) != MM_OK) return 0;
-  return layout(*s).total;
+  return layout(*s, true).total;
 }
 
 mm_status mamba_mixer_prefill(const mm_shape *s, const mm_params *p, const void *xz, void *y,

@@ -1,0 +1,263 @@
+// Batched single-token decode step (bf16 I/O, fp32 state).
+//
+// Jamba analysis page, "Inference behavior (generation)": at inference Mamba advances one token
+// at a time in O(1): the fixed-size state is updated from the new token with no re-scan. Per
+// sequence b and channel i: u = SiLU(conv(conv_state, x_t)), the x_proj / RMSNorm / dt_proj
+// chain of the prefill, then h = exp(dt A) h + Bbar u and y = (C . h + D u) SiLU(z)
+// ("The Mamba Layer": ZOH and recurrence equations; RMSNorm equation).
+//
+// Kernels:
+//   decode_xproj_kernel  64 sequences x a 1024-channel range of d_inner per workgroup: u in fp32
+//                        from the carried conv state and x_t (each lane forms exactly its MFMA
+//                        fragment), split hi + lo, two bf16 MFMA passes against W_x chunks that
+//                        stream through XOR-swizzled LDS (direct-to-LDS loads, double-buffered).
+//                        Writes the range's fp32 partial sums of xdbl.
+//   decode_norm_kernel   sums the ranges' partials in a fixed order (deterministic) and applies
+//                        the three RMSNorms: dt_low (bf16 hi + lo, for dt_proj) and B | C (fp32).
+//   decode_update_kernel the state update: 4 lanes per channel, 4 states each as one float4, so
+//                        a wave reads / writes 1 KB of state per instruction (the step is
+//                        bound by this read-modify-write); conv recomputed; y reduced over the
+//                        4 lanes by DPP; the new conv state written in the same pass.
+#include "common.h"
+#include "kernels.h"
+
+namespace mm {
+namespace {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+
+constexpr int kSeqW = 64;     // sequences per workgroup (4 waves x 16)
+constexpr int kKC = 64;       // channels per chunk
+
+__device__ __forceinline__ int swz(int r, int c) { return c ^ ((r >> 1) & 7); }
+
+template <int NX>
+__global__ __launch_bounds__(256) void decode_xproj_kernel(DecodeXprojArgs a) {
+  constexpr int NB = NX / 16;
+  __shared__ __attribute__((aligned(16))) bf16_t w_s0[NX][kKC];
+  __shared__ __attribute__((aligned(16))) bf16_t w_s1[NX][kKC];
+
+  const int nseqt = (a.B + kSeqW - 1) / kSeqW;
+  const int gid = blockIdx.x;
+  const int st = gid % nseqt, kr = gid / nseqt;   // sequence tile, channel range
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int tl = lane & 15, g = lane >> 4;
+  const int bs = st * kSeqW + wv * 16 + tl;       // this lane's sequence
+  const int bsc = min(bs, a.B - 1);
+  const int cbeg = kr * a.range_ch;
+  const int nck = min(a.range_ch, a.D - cbeg) / kKC;
+
+  auto stage = [&](int ck, bf16_t (*wdst)[kKC]) {
+    const int c0 = cbeg + ck * kKC;
+    for (int ld = wv; ld < NX / 8; ld += 4) {
+      const int r = ld * 8 + (lane >> 3), ps = lane & 7;
+      __builtin_amdgcn_global_load_lds(a.w + (int64_t)r * a.D + c0 + swz(r, ps) * 8,
+                                       (__attribute__((address_space(3))) void *)&wdst[ld * 8][0],
+                                       16, 0, 0);
+    }
+  };
+
+  f32x4 acc[NB];
+#pragma unroll
+  for (int i = 0; i < NB; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto chunk = [&](int ck, bf16_t (*wcur)[kKC], bf16_t (*wnxt)[kKC]) {
+    wait_vmem_all();
+    lds_barrier();
+    if (ck + 1 < nck) stage(ck + 1, wnxt);
+    const int c0 = cbeg + ck * kKC;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int lc = ks * 4 + g;                       // 8 channels: c0 + 8 lc .. +7
+      const int ch = c0 + lc * 8;
+      // conv window: carried state (3 per channel, oldest first) then x_t
+      const bf16_t *csp = a.conv_state + ((int64_t)bsc * a.D + ch) * 3;
+      const uint4 s0 = *(const uint4 *)csp, s1 = *(const uint4 *)(csp + 8),
+                  s2 = *(const uint4 *)(csp + 16);
+      const uint32_t sw[12] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w,
+                               s2.x, s2.y, s2.z, s2.w};
+      const uint4 xv = *(const uint4 *)(a.xz + (int64_t)bsc * 2 * a.D + ch);
+      const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+      float u[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint2 wr = *(const uint2 *)(a.conv_w + (int64_t)(ch + e) * 4);
+        float acc0 = a.conv_b ? bf2f(a.conv_b[ch + e]) : 0.f;
+        const int s = e * 3;  // bf16 index of channel e's first state value
+        const float c0v = (s & 1) ? hi_bf(sw[s >> 1]) : lo_bf(sw[s >> 1]);
+        const float c1v = ((s + 1) & 1) ? hi_bf(sw[(s + 1) >> 1]) : lo_bf(sw[(s + 1) >> 1]);
+        const float c2v = ((s + 2) & 1) ? hi_bf(sw[(s + 2) >> 1]) : lo_bf(sw[(s + 2) >> 1]);
+        const float x = (e & 1) ? hi_bf(xw[e >> 1]) : lo_bf(xw[e >> 1]);
+        acc0 = __builtin_fmaf(lo_bf(wr.x), c0v, acc0);
+        acc0 = __builtin_fmaf(hi_bf(wr.x), c1v, acc0);
+        acc0 = __builtin_fmaf(lo_bf(wr.y), c2v, acc0);
+        acc0 = __builtin_fmaf(hi_bf(wr.y), x, acc0);
+        u[e] = silu_f(acc0);
+      }
+      uint4 hi, lo;
+      {
+        float l8[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) l8[e] = u[e] - bf2f(f2bf(u[e]));
+        hi.x = pack_bf2(u[0], u[1]); hi.y = pack_bf2(u[2], u[3]);
+        hi.z = pack_bf2(u[4], u[5]); hi.w = pack_bf2(u[6], u[7]);
+        lo.x = pack_bf2(l8[0], l8[1]); lo.y = pack_bf2(l8[2], l8[3]);
+        lo.z = pack_bf2(l8[4], l8[5]); lo.w = pack_bf2(l8[6], l8[7]);
+      }
+      const bf16x8 fh = __builtin_bit_cast(bf16x8, hi), fl = __builtin_bit_cast(bf16x8, lo);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const int r = nb * 16 + tl;
+        const bf16x8 fw = __builtin_bit_cast(bf16x8, *(const uint4 *)&wcur[r][swz(r, lc) * 8]);
+        acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fw, fl, acc[nb], 0, 0, 0);
+        acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fw, fh, acc[nb], 0, 0, 0);
+      }
+    }
+  };
+
+  stage(0, w_s0);
+  for (int ck = 0; ck < nck; ++ck) {
+    const bool odd = ck & 1;
+    chunk(ck, odd ? w_s1 : w_s0, odd ? w_s0 : w_s1);
+  }
+  // partial sums of this channel range: part[kr][b][n]
+  if (bs < a.B) {
+    float *pp = a.part + ((int64_t)kr * a.B + bs) * NX;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+      *(float4 *)(pp + nb * 16 + 4 * g) = make_float4(acc[nb][0], acc[nb][1], acc[nb][2], acc[nb][3]);
+  }
+}
+
+// One wave per sequence: sum the ranges' partials (fixed order) and normalise.
+__global__ __launch_bounds__(256) void decode_norm_kernel(DecodeNormArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int b = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (b >= a.B) return;
+  const int NX = a.R + 32;
+  float v[10];   // NX <= 640 values per sequence, 64 lanes
+  float ssd = 0.f, ssb = 0.f, ssc = 0.f;
+#pragma unroll
+  for (int k = 0; k < 10; ++k) {
+    const int n = lane + 64 * k;
+    float s = 0.f;
+    if (n < NX) {
+      const float *pp = a.part + (int64_t)b * NX + n;
+      const int64_t rs = (int64_t)a.B * NX;
+#pragma unroll 8
+      for (int r = 0; r < a.nranges; ++r) s += pp[r * rs];
+    }
+    v[k] = s;
+    if (n < a.R) ssd = __builtin_fmaf(s, s, ssd);
+    else if (n < a.R + 16) ssb = __builtin_fmaf(s, s, ssb);
+    else if (n < NX) ssc = __builtin_fmaf(s, s, ssc);
+  }
+  ssd = wave_sum(ssd);
+  ssb = wave_sum(ssb);
+  ssc = wave_sum(ssc);
+  const float id = 1.0f / sqrtf(ssd / (float)a.R + a.eps);
+  const float ib = 1.0f / sqrtf(ssb / 16.0f + a.eps);
+  const float ic = 1.0f / sqrtf(ssc / 16.0f + a.eps);
+#pragma unroll
+  for (int k = 0; k < 10; ++k) {
+    const int n = lane + 64 * k;
+    if (n < a.R) {
+      const float x = v[k] * id * a.g_dt[n];
+      a.dtlow[(int64_t)b * a.R + n] = f2bf(x);
+      a.dtlow_lo[(int64_t)b * a.R + n] = f2bf(x - bf2f(f2bf(x)));
+    } else if (n < a.R + 16) {
+      a.bc[(int64_t)b * 32 + (n - a.R)] = v[k] * ib * a.g_B[n - a.R];
+    } else if (n < NX) {
+      a.bc[(int64_t)b * 32 + (n - a.R)] = v[k] * ic * a.g_C[n - a.R - 16];
+    }
+  }
+}
+
+// State update: lane l of a wave -> channel ch0 + l/4, states 4 (l%4) .. +3.
+template <bool ZOH>
+__global__ __launch_bounds__(256) void decode_update_kernel(DecodeUpdateArgs a) {
+  const int64_t gch = (int64_t)blockIdx.x * 64 + (threadIdx.x >> 2);   // b * D + i
+  const int q = threadIdx.x & 3;
+  const int i = (int)(gch % a.D);
+  const int b = (int)(gch / a.D);
+  const float4 Av = *(const float4 *)(a.A + (int64_t)i * 16 + 4 * q);
+  float4 h = *(const float4 *)(a.state + gch * 16 + 4 * q);
+  const float4 Bv = *(const float4 *)(a.bc + (int64_t)b * 32 + 4 * q);
+  const float4 Cv = *(const float4 *)(a.bc + (int64_t)b * 32 + 16 + 4 * q);
+  // conv window and u (every lane of the channel forms it)
+  bf16_t *csp = a.conv_state + gch * 3;
+  const float c0 = bf2f(csp[0]), c1 = bf2f(csp[1]), c2 = bf2f(csp[2]);
+  const bf16_t *xrow = a.xz + (int64_t)b * 2 * a.D;
+  const float x = bf2f(xrow[i]);
+  const float z = bf2f(xrow[a.D + i]);
+  const uint2 wr = *(const uint2 *)(a.conv_w + (int64_t)i * 4);
+  float acc = a.conv_b ? bf2f(a.conv_b[i]) : 0.f;
+  acc = __builtin_fmaf(lo_bf(wr.x), c0, acc);
+  acc = __builtin_fmaf(hi_bf(wr.x), c1, acc);
+  acc = __builtin_fmaf(lo_bf(wr.y), c2, acc);
+  acc = __builtin_fmaf(hi_bf(wr.y), x, acc);
+  const float u = silu_f(acc);
+  const float dt = (float)a.dt[gch];
+  const float av[4] = {Av.x, Av.y, Av.z, Av.w};
+  const float bv[4] = {Bv.x, Bv.y, Bv.z, Bv.w};
+  const float cv[4] = {Cv.x, Cv.y, Cv.z, Cv.w};
+  float hv[4] = {h.x, h.y, h.z, h.w};
+  float yp = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if (ZOH) {
+      const float em1 = expm1_f(dt * av[j]);
+      hv[j] = __builtin_fmaf(em1 + 1.0f, hv[j], em1 / av[j] * bv[j] * u);
+    } else {
+      hv[j] = __builtin_fmaf(exp2_hw(dt * av[j] * kLog2e), hv[j], dt * u * bv[j]);
+    }
+    yp = __builtin_fmaf(cv[j], hv[j], yp);
+  }
+  *(float4 *)(a.state + gch * 16 + 4 * q) = make_float4(hv[0], hv[1], hv[2], hv[3]);
+  // sum the 4 lanes of the channel: quad_perm [1,0,3,2] then [2,3,0,1]
+  yp += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, yp), 0xB1, 0xF, 0xF, false));
+  yp += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, yp), 0x4E, 0xF, 0xF, false));
+  if (q == 0) a.y[gch] = f2bf(__builtin_fmaf(a.Dskip[i], u, yp) * silu_f(z));
+  if (q < 3) csp[q] = f2bf(q == 0 ? c1 : q == 1 ? c2 : x);   // shift in x_t
+}
+
+template <int NX>
+hipError_t launch_xp(const DecodeXprojArgs &a, hipStream_t s) {
+  const int nseqt = (a.B + kSeqW - 1) / kSeqW;
+  const int nr = (a.D + a.range_ch - 1) / a.range_ch;
+  hipLaunchKernelGGL((decode_xproj_kernel<NX>), dim3((unsigned)(nseqt * nr)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool decode_fast_supported(int R, int N, int D, int K) {
+  return N == 16 && K == 4 && D % kKC == 0 && (R == 64 || R == 128 || R == 256 || R == 512);
+}
+
+hipError_t launch_decode_xproj(const DecodeXprojArgs &a, hipStream_t s) {
+  switch (a.R) {
+    case 64: return launch_xp<96>(a, s);
+    case 128: return launch_xp<160>(a, s);
+    case 256: return launch_xp<288>(a, s);
+    case 512: return launch_xp<544>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode_norm(const DecodeNormArgs &a, hipStream_t s) {
+  hipLaunchKernelGGL(decode_norm_kernel, dim3((unsigned)((a.B + 3) / 4)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_update(const DecodeUpdateArgs &a, bool zoh, hipStream_t s) {
+  const unsigned grid = (unsigned)((int64_t)a.B * a.D / 64);
+  if (zoh)
+    hipLaunchKernelGGL((decode_update_kernel<true>), dim3(grid), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((decode_update_kernel<false>), dim3(grid), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace mm

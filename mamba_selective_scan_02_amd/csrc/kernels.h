@@ -65,6 +65,43 @@ struct DtprojArgs {
 bool dtproj_supported(int R, int D);
 hipError_t launch_dtproj_tiled(const DtprojArgs &a, hipStream_t s);
 
+// bf16 decode step (L = 1 per sequence): partial x_proj over channel ranges, reduction +
+// RMSNorm, and the fused conv / state-update / gate / conv-state kernel.
+struct DecodeXprojArgs {
+  const uint16_t *xz;          // [B, 2D]
+  const uint16_t *conv_w;      // [D, 4]
+  const uint16_t *conv_b;      // [D] or null
+  const uint16_t *conv_state;  // [B, D, 3] (read; updated later by the update kernel)
+  const uint16_t *w;           // [R + 32, D]
+  float *part;                 // [ranges, B, R + 32]
+  int B, D, R;
+  int range_ch;                // channels per range (multiple of 64)
+};
+struct DecodeNormArgs {
+  const float *part;
+  int nranges;
+  uint16_t *dtlow, *dtlow_lo;  // [B, R]
+  float *bc;                   // [B, 32]
+  const float *g_dt, *g_B, *g_C;
+  float eps;
+  int B, R;
+};
+struct DecodeUpdateArgs {
+  const uint16_t *xz;          // [B, 2D]
+  const uint16_t *conv_w, *conv_b;
+  uint16_t *conv_state;        // [B, D, 3] in/out
+  const _Float16 *dt;          // [B, D]
+  const float *bc;             // [B, 32]
+  const float *A, *Dskip;
+  float *state;                // [B, D, 16] in/out
+  uint16_t *y;                 // [B, D]
+  int B, D;
+};
+bool decode_fast_supported(int R, int N, int D, int K);
+hipError_t launch_decode_xproj(const DecodeXprojArgs &a, hipStream_t s);
+hipError_t launch_decode_norm(const DecodeNormArgs &a, hipStream_t s);
+hipError_t launch_decode_update(const DecodeUpdateArgs &a, bool zoh, hipStream_t s);
+
 struct ScanArgs {
   const void *xz;       // [B, L, 2D]; x = first D columns (conv input), z = last D (gate)
   const void *conv_w;   // [D, K] io dtype

@@ -61,7 +61,15 @@ def test_workspace_size_formula():
     T, D, R = 256, 64, 8
     expect = up(T * D * 4) + up(T * (R + 2 * N) * 4) + up(T * R * 4) + up(T * 2 * N * 4) + up(T * D * 4)
     assert mm.prefill_workspace_bytes(s32) == expect
-    assert mm.decode_workspace_bytes(_shape(seqlen=1, batch=256)) > 0
+    # bf16 decode step, d_conv 4: x_proj partial sums over 64 ranges of 128 channels replace
+    # u and xdbl; then dt_low hi+lo, B|C, dt (fp16)
+    T, D, R = 256, 8192, 256
+    expect = up(64 * T * (R + 2 * N) * 4) + 2 * up(T * R * 2) + up(T * 2 * N * 4) + up(T * D * 2)
+    assert mm.decode_workspace_bytes(_shape(seqlen=1, batch=256)) == expect
+    # d_conv 3 takes the general path: u hi+lo and xdbl as for a prefill of B tokens
+    expect = (2 * up(T * D * 2) + up(T * (R + 2 * N) * 4) + 2 * up(T * R * 2) + up(T * 2 * N * 4)
+              + up(T * D * 2))
+    assert mm.decode_workspace_bytes(_shape(seqlen=1, batch=256, d_conv=3)) == expect
     assert mm.decode_workspace_bytes(_shape(seqlen=2)) == 0      # decode needs seqlen == 1
 
 

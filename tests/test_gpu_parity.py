@@ -158,6 +158,65 @@ def test_decode_steps_match_oracle(io):
         np.testing.assert_array_equal(to64(cs), csr)
 
 
+# bf16 decode with d_conv 4 runs the decode kernels (x_proj split over channel ranges, fused
+# state update); d_conv 3 the general path. Batches span several 64-sequence tiles with a
+# ragged one; d_inner spans several channel ranges; each supported dt_rank instantiation.
+DECODE_CASES = [
+    # name, batch, d_inner, dt_rank, d_conv, conv_bias, zoh, gamma_random
+    ("dec_b1_r64", 1, 256, 64, 4, True, False, False),
+    ("dec_b130_r128", 130, 1024, 128, 4, False, False, True),
+    ("dec_b65_r256_zoh", 65, 2048, 256, 4, True, True, True),
+    ("dec_b200_r512", 200, 512, 512, 4, True, False, False),
+    ("dec_b70_k3", 70, 512, 64, 3, True, False, False),
+]
+
+
+@pytest.mark.parametrize("case", DECODE_CASES, ids=[c[0] for c in DECODE_CASES])
+def test_decode_kernels_match_oracle(case):
+    _need_gpu()
+    name, B, D, R, K, bias, zoh, gam = case
+    cfg = synth.MixerConfig(name, B, 1, D, 16, K, R, "bf16")
+    seed = 90 + DECODE_CASES.index(case)
+    print(f"[case] {name} B={B} D={D} R={R} K={K} bias={bias} zoh={zoh} seed={seed}", flush=True)
+    dev = "cuda"
+    p = synth.make_params(cfg, seed, dev, conv_bias=bias, gamma_random=gam)
+    cs, ss = synth.make_states(cfg, seed, dev)
+    csr, ssr = to64(cs), to64(ss)
+    p64 = oracle.as_f64_params(p)
+    for step in range(4):
+        xt = synth.make_xz(cfg, seed, dev, seqlen=1, tensor="decode_xz", step=step)[:, 0]
+        y = mm.decode_step(xt, p, cs, ss, zoh=zoh)
+        torch.cuda.synchronize()
+        yr, csr, ssr = oracle.mixer_decode_step(to64(xt), p64, csr, ssr, zoh=zoh)
+        check(y, yr, "bf16", f"y step {step}")
+        check(ss, ssr, "bf16", f"ssm_state step {step}")
+        np.testing.assert_array_equal(to64(cs), csr)
+
+
+def test_prefill_then_decode_equals_longer_prefill():
+    """Decoding the last tokens one at a time continues a prefill exactly as a prefill over
+    all tokens would (to rounding): the carried states are the whole history."""
+    _need_gpu()
+    cfg = synth.MixerConfig("dec_continue", 96, 40, 1024, 16, 4, 128, "bf16")
+    seed = 97
+    dev = "cuda"
+    p = synth.make_params(cfg, seed, dev, conv_bias=True)
+    xz = synth.make_xz(cfg, seed, dev)
+    y_full = mm.prefill(xz, p)
+    cs = torch.zeros(cfg.batch, cfg.d_inner, 3, dtype=cfg.torch_dtype, device=dev)
+    ss = torch.zeros(cfg.batch, cfg.d_inner, 16, dtype=torch.float32, device=dev)
+    n0 = 32
+    y_pre = mm.prefill(xz[:, :n0].contiguous(), p, conv_state=cs, ssm_state=ss)
+    ys = [y_pre]
+    for t in range(n0, cfg.seqlen):
+        ys.append(mm.decode_step(xz[:, t].contiguous(), p, cs, ss)[:, None])
+    torch.cuda.synchronize()
+    yr, _, ssr = oracle.mixer_prefill(to64(xz), oracle.as_f64_params(p))
+    check(torch.cat(ys, dim=1), yr, "bf16", "y (prefill + decode)")
+    check(y_full, yr, "bf16", "y (prefill)")
+    check(ss, ssr, "bf16", "ssm_state (prefill + decode)")
+
+
 def test_outputs_are_deterministic():
     _need_gpu()
     cfg = BF16_SMALL
