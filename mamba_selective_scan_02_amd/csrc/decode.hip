@@ -130,24 +130,40 @@ __global__ __launch_bounds__(256) void decode_xproj_kernel(DecodeXprojArgs a) {
   }
 }
 
-// One wave per sequence: sum the ranges' partials (fixed order) and normalise.
-__global__ __launch_bounds__(256) void decode_norm_kernel(DecodeNormArgs a) {
-  const int lane = threadIdx.x & 63;
-  const int b = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (b >= a.B) return;
+// One workgroup (16 waves) per sequence: wave w sums ranges w, w + 16, ...; the waves' sums are
+// added in a fixed order (deterministic), then wave 0 normalises.
+constexpr int kNormWaves = 16;
+__global__ __launch_bounds__(64 * kNormWaves) void decode_norm_kernel(DecodeNormArgs a) {
+  constexpr int kV = 10;   // NX <= 640 values per sequence over 64 lanes
+  __shared__ float red_s[kNormWaves][kV * 64];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int b = blockIdx.x;
   const int NX = a.R + 32;
-  float v[10];   // NX <= 640 values per sequence, 64 lanes
+  const int64_t rs = (int64_t)a.B * NX;
+  const float *pp = a.part + (int64_t)b * NX;
+  float v[kV];
+#pragma unroll
+  for (int k = 0; k < kV; ++k) v[k] = 0.f;
+#pragma unroll 4
+  for (int r = wv; r < a.nranges; r += kNormWaves) {
+    const float *q = pp + r * rs;
+#pragma unroll
+    for (int k = 0; k < kV; ++k) {
+      const int n = lane + 64 * k;
+      if (n < NX) v[k] += q[n];
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < kV; ++k) red_s[wv][lane + 64 * k] = v[k];
+  __syncthreads();
+  if (wv != 0) return;
   float ssd = 0.f, ssb = 0.f, ssc = 0.f;
 #pragma unroll
-  for (int k = 0; k < 10; ++k) {
+  for (int k = 0; k < kV; ++k) {
     const int n = lane + 64 * k;
-    float s = 0.f;
-    if (n < NX) {
-      const float *pp = a.part + (int64_t)b * NX + n;
-      const int64_t rs = (int64_t)a.B * NX;
-#pragma unroll 8
-      for (int r = 0; r < a.nranges; ++r) s += pp[r * rs];
-    }
+    float s = red_s[0][n];
+#pragma unroll
+    for (int w = 1; w < kNormWaves; ++w) s += red_s[w][n];
     v[k] = s;
     if (n < a.R) ssd = __builtin_fmaf(s, s, ssd);
     else if (n < a.R + 16) ssb = __builtin_fmaf(s, s, ssb);
@@ -160,7 +176,7 @@ __global__ __launch_bounds__(256) void decode_norm_kernel(DecodeNormArgs a) {
   const float ib = 1.0f / sqrtf(ssb / 16.0f + a.eps);
   const float ic = 1.0f / sqrtf(ssc / 16.0f + a.eps);
 #pragma unroll
-  for (int k = 0; k < 10; ++k) {
+  for (int k = 0; k < kV; ++k) {
     const int n = lane + 64 * k;
     if (n < a.R) {
       const float x = v[k] * id * a.g_dt[n];
@@ -174,52 +190,89 @@ __global__ __launch_bounds__(256) void decode_norm_kernel(DecodeNormArgs a) {
   }
 }
 
-// State update: lane l of a wave -> channel ch0 + l/4, states 4 (l%4) .. +3.
-template <bool ZOH>
+// State update. A workgroup covers U x 64 consecutive (b, i) channels; in unit j, lane l of a
+// wave takes channel 64 j + l / 4 of its 16-channel slice, states 4 (l % 4) .. +3, so each
+// state load / store of a wave is 1 KB contiguous. The loads of all U units are issued before
+// any arithmetic; per-channel scalars are fetched once per channel (one lane each) and shared
+// within the channel's 4 lanes by DPP, the sequence's B | C row once per wave and shared by
+// bpermute. U = 2 keeps the kernel under 64 VGPRs (the most waves per SIMD) with two units of
+// state in flight per lane.
+template <bool ZOH, int U>
 __global__ __launch_bounds__(256) void decode_update_kernel(DecodeUpdateArgs a) {
-  const int64_t gch = (int64_t)blockIdx.x * 64 + (threadIdx.x >> 2);   // b * D + i
   const int q = threadIdx.x & 3;
-  const int i = (int)(gch % a.D);
-  const int b = (int)(gch / a.D);
-  const float4 Av = *(const float4 *)(a.A + (int64_t)i * 16 + 4 * q);
-  float4 h = *(const float4 *)(a.state + gch * 16 + 4 * q);
-  const float4 Bv = *(const float4 *)(a.bc + (int64_t)b * 32 + 4 * q);
-  const float4 Cv = *(const float4 *)(a.bc + (int64_t)b * 32 + 16 + 4 * q);
-  // conv window and u (every lane of the channel forms it)
-  bf16_t *csp = a.conv_state + gch * 3;
-  const float c0 = bf2f(csp[0]), c1 = bf2f(csp[1]), c2 = bf2f(csp[2]);
-  const bf16_t *xrow = a.xz + (int64_t)b * 2 * a.D;
-  const float x = bf2f(xrow[i]);
-  const float z = bf2f(xrow[a.D + i]);
-  const uint2 wr = *(const uint2 *)(a.conv_w + (int64_t)i * 4);
-  float acc = a.conv_b ? bf2f(a.conv_b[i]) : 0.f;
-  acc = __builtin_fmaf(lo_bf(wr.x), c0, acc);
-  acc = __builtin_fmaf(hi_bf(wr.x), c1, acc);
-  acc = __builtin_fmaf(lo_bf(wr.y), c2, acc);
-  acc = __builtin_fmaf(hi_bf(wr.y), x, acc);
-  const float u = silu_f(acc);
-  const float dt = (float)a.dt[gch];
-  const float av[4] = {Av.x, Av.y, Av.z, Av.w};
-  const float bv[4] = {Bv.x, Bv.y, Bv.z, Bv.w};
-  const float cv[4] = {Cv.x, Cv.y, Cv.z, Cv.w};
-  float hv[4] = {h.x, h.y, h.z, h.w};
-  float yp = 0.f;
+  const int64_t g0 = (int64_t)blockIdx.x * (64 * U) + (threadIdx.x >> 2);   // b * D + i
+  const int64_t w0 = (int64_t)blockIdx.x * (64 * U) + (threadIdx.x >> 6) * 16;
+  float4 h[U], Av[U];
+  float Bq[U][4], Cq[U][4];
+  uint32_t cs16[U], p16[U];
+  float Dv[U];
+  uint2 wr[U];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    if (ZOH) {
-      const float em1 = expm1_f(dt * av[j]);
-      hv[j] = __builtin_fmaf(em1 + 1.0f, hv[j], em1 / av[j] * bv[j] * u);
-    } else {
-      hv[j] = __builtin_fmaf(exp2_hw(dt * av[j] * kLog2e), hv[j], dt * u * bv[j]);
+  for (int j = 0; j < U; ++j) {
+    const int64_t gch = g0 + 64 * j;
+    const int i = (int)(gch % a.D);
+    const int b = (int)(gch / a.D);
+    // the wave's 16 channels of unit j lie in one sequence (d_inner % 16 == 0)
+    const int bw = __builtin_amdgcn_readfirstlane((int)((w0 + 64 * j) / a.D));
+    h[j] = *(const float4 *)(a.state + gch * 16 + 4 * q);
+    Av[j] = *(const float4 *)(a.A + (int64_t)i * 16 + 4 * q);
+    // lane l holds value l % 32 of the sequence's B | C row; lanes fetch theirs by bpermute
+    const float bcl = a.bc[(int64_t)bw * 32 + (threadIdx.x & 31)];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      Bq[j][s] = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((4 * q + s) * 4, __builtin_bit_cast(int, bcl)));
+      Cq[j][s] = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((16 + 4 * q + s) * 4, __builtin_bit_cast(int, bcl)));
     }
-    yp = __builtin_fmaf(cv[j], hv[j], yp);
+    // lane q of the channel loads conv state element min(q, 2); then x | z | dt | bias by q
+    cs16[j] = a.conv_state[gch * 3 + (q < 3 ? q : 2)];
+    const bf16_t *xrow = a.xz + (int64_t)b * 2 * a.D;
+    const uint16_t *src = q == 0 ? xrow + i
+                        : q == 1 ? xrow + a.D + i
+                        : q == 2 ? (const uint16_t *)a.dt + gch
+                        : (a.conv_b ? a.conv_b + i : xrow + i);
+    p16[j] = *src;
+    if (q == 3 && !a.conv_b) p16[j] = 0;
+    wr[j] = *(const uint2 *)(a.conv_w + (int64_t)i * 4);
+    Dv[j] = a.Dskip[i];
   }
-  *(float4 *)(a.state + gch * 16 + 4 * q) = make_float4(hv[0], hv[1], hv[2], hv[3]);
-  // sum the 4 lanes of the channel: quad_perm [1,0,3,2] then [2,3,0,1]
-  yp += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, yp), 0xB1, 0xF, 0xF, false));
-  yp += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, yp), 0x4E, 0xF, 0xF, false));
-  if (q == 0) a.y[gch] = f2bf(__builtin_fmaf(a.Dskip[i], u, yp) * silu_f(z));
-  if (q < 3) csp[q] = f2bf(q == 0 ? c1 : q == 1 ? c2 : x);   // shift in x_t
+#pragma unroll
+  for (int j = 0; j < U; ++j) {
+    const int64_t gch = g0 + 64 * j;
+    const int cs = (int)cs16[j], pv = (int)p16[j];
+    const float c0 = bf2f((bf16_t)__builtin_amdgcn_mov_dpp(cs, 0x00, 0xF, 0xF, false));
+    const float c1 = bf2f((bf16_t)__builtin_amdgcn_mov_dpp(cs, 0x55, 0xF, 0xF, false));
+    const float c2 = bf2f((bf16_t)__builtin_amdgcn_mov_dpp(cs, 0xAA, 0xF, 0xF, false));
+    const float xv = bf2f((bf16_t)__builtin_amdgcn_mov_dpp(pv, 0x00, 0xF, 0xF, false));
+    const float zv = bf2f((bf16_t)__builtin_amdgcn_mov_dpp(pv, 0x55, 0xF, 0xF, false));
+    const uint16_t dth = (uint16_t)__builtin_amdgcn_mov_dpp(pv, 0xAA, 0xF, 0xF, false);
+    const float bias = bf2f((bf16_t)__builtin_amdgcn_mov_dpp(pv, 0xFF, 0xF, 0xF, false));
+    const float dt = (float)__builtin_bit_cast(_Float16, dth);
+    float acc = bias;
+    acc = __builtin_fmaf(lo_bf(wr[j].x), c0, acc);
+    acc = __builtin_fmaf(hi_bf(wr[j].x), c1, acc);
+    acc = __builtin_fmaf(lo_bf(wr[j].y), c2, acc);
+    acc = __builtin_fmaf(hi_bf(wr[j].y), xv, acc);
+    const float u = silu_f(acc);
+    const float av[4] = {Av[j].x, Av[j].y, Av[j].z, Av[j].w};
+    float hv[4] = {h[j].x, h[j].y, h[j].z, h[j].w};
+    float yp = 0.f;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      if (ZOH) {
+        const float em1 = expm1_f(dt * av[s]);
+        hv[s] = __builtin_fmaf(em1 + 1.0f, hv[s], em1 / av[s] * Bq[j][s] * u);
+      } else {
+        hv[s] = __builtin_fmaf(exp2_hw(dt * av[s] * kLog2e), hv[s], dt * u * Bq[j][s]);
+      }
+      yp = __builtin_fmaf(Cq[j][s], hv[s], yp);
+    }
+    *(float4 *)(a.state + gch * 16 + 4 * q) = make_float4(hv[0], hv[1], hv[2], hv[3]);
+    // sum the channel's 4 lanes: quad_perm [1,0,3,2] then [2,3,0,1]
+    yp += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, yp), 0xB1, 0xF, 0xF, false));
+    yp += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, yp), 0x4E, 0xF, 0xF, false));
+    if (q == 0) a.y[gch] = f2bf(__builtin_fmaf(Dv[j], u, yp) * silu_f(zv));
+    if (q < 3) a.conv_state[gch * 3 + q] = f2bf(q == 0 ? c1 : q == 1 ? c2 : xv);   // shift in x_t
+  }
 }
 
 template <int NX>
@@ -247,17 +300,22 @@ hipError_t launch_decode_xproj(const DecodeXprojArgs &a, hipStream_t s) {
 }
 
 hipError_t launch_decode_norm(const DecodeNormArgs &a, hipStream_t s) {
-  hipLaunchKernelGGL(decode_norm_kernel, dim3((unsigned)((a.B + 3) / 4)), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(decode_norm_kernel, dim3((unsigned)a.B), dim3(64 * kNormWaves), 0, s, a);
+  return hipGetLastError();
+}
+
+template <bool ZOH>
+hipError_t launch_upd(const DecodeUpdateArgs &a, hipStream_t s) {
+  const int64_t n = (int64_t)a.B * a.D;   // a multiple of 64
+  if (n % 128 == 0)
+    hipLaunchKernelGGL((decode_update_kernel<ZOH, 2>), dim3((unsigned)(n / 128)), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((decode_update_kernel<ZOH, 1>), dim3((unsigned)(n / 64)), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_decode_update(const DecodeUpdateArgs &a, bool zoh, hipStream_t s) {
-  const unsigned grid = (unsigned)((int64_t)a.B * a.D / 64);
-  if (zoh)
-    hipLaunchKernelGGL((decode_update_kernel<true>), dim3(grid), dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL((decode_update_kernel<false>), dim3(grid), dim3(256), 0, s, a);
-  return hipGetLastError();
+  return zoh ? launch_upd<true>(a, s) : launch_upd<false>(a, s);
 }
 
 }  // namespace mm

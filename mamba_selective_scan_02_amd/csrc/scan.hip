@@ -115,9 +115,11 @@ __global__ __launch_bounds__(64) void scan_seq_kernel(ScanArgs a) {
 //     8*(l%2) .. +7. The segment is scanned from h = 0, keeping exp(dt*A) of every
 //     (token, state) in VGPRs (one exp per element, as in the sequential recurrence).
 //  3. Compose: the segment's transfer h -> P h + S (P = exp(A * sum dt), S = the local end
-//     state) goes to LDS; each wave folds the transfers before it onto the block's carry-in
-//     with the page's associative operator ("Parallel training via the parallel scan":
-//     (a, b) then (c, d) gives (ac, ad + b) for h -> a h + b), and all 8 for the next carry.
+//     state) goes to LDS. Thread i then owns one (channel, state) chain: it applies the 8
+//     transfers in order to the block's carry-in with the page's associative operator
+//     ("Parallel training via the parallel scan": (a, b) then (c, d) gives (ac, ad + b) for
+//     h -> a h + b), writing each segment's h_in over that segment's P, and keeps the result
+//     as the next block's carry-in.
 //  4. Replay from the true h_in with the stored exp(dt*A); y_t = C_t . h_t; the two half-sums
 //     of a channel meet by a DPP lane swap; y = (y_ssm + D u) * SiLU(z) goes out as bf16/f32.
 constexpr int kCh = 32, kW = 8, kS = 16, kG = 8, kBlk = kW * kS;
@@ -164,14 +166,19 @@ __global__ __launch_bounds__(kW * 64) void scan_chunked_kernel(ScanArgs a) {
   const int c = lane >> 1, p = lane & 1;
   const int ch = ch0 + c;
 
-  float A2[kG], Av[kG], iA[kG], carry[kG];
+  float A2[kG], Av[kG], iA[kG];
 #pragma unroll
   for (int j = 0; j < kG; ++j) {
     Av[j] = a.A[(int64_t)ch * kN + kG * p + j];
     A2[j] = Av[j] * kLog2e;
     iA[j] = 1.0f / Av[j];
-    carry[j] = (a.state_valid && a.state) ? a.state[((int64_t)b * a.D + ch) * kN + kG * p + j] : 0.f;
   }
+  // chain thread tid <-> publishing lane ql = (tid >> 2) & 63 (channel ql/2, state half ql&1),
+  // state j = 4 (tid >> 8) + (tid & 3) of that half: its P of segment w is float w*1024 + tid
+  // of agg_s, its S float w*1024 + 512 + tid (conflict-free, lane-contiguous)
+  const int ql = (tid >> 2) & 63, qj = 4 * (tid >> 8) + (tid & 3);
+  const int64_t qidx = ((int64_t)b * a.D + ch0 + (ql >> 1)) * kN + kG * (ql & 1) + qj;
+  float carry = (a.state_valid && a.state) ? a.state[qidx] : 0.f;
   // prep thread: channel pc, tokens 8*pt .. 8*pt+7 of the block
   const int pc = tid & (kCh - 1), pt = tid >> 5;
   const int pch = ch0 + pc;
@@ -229,10 +236,18 @@ __global__ __launch_bounds__(kW * 64) void scan_chunked_kernel(ScanArgs a) {
   int ypend_t0 = -1;
   auto flush = [&]() {
     if (ypend_t0 < 0) return;
+    // wave-uniform block base, 32-bit lane offsets (a block spans < 2^31 / sizeof(T) elements)
+    T *ybase = yb + (int64_t)ypend_t0 * a.D;
+    const int tl0 = wv * kS + p;
+    if (ypend_t0 + kBlk <= a.L) {
 #pragma unroll
-    for (int i = 0; i < kS / 2; ++i) {
-      const int t = ypend_t0 + wv * kS + 2 * i + p;
-      if (t < a.L) io<T>::st(yb + (int64_t)t * a.D + ch, ypend[i]);
+      for (int i = 0; i < kS / 2; ++i)
+        io<T>::st(ybase + (uint32_t)((tl0 + 2 * i) * a.D + ch), ypend[i]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < kS / 2; ++i)
+        if (ypend_t0 + tl0 + 2 * i < a.L)
+          io<T>::st(ybase + (uint32_t)((tl0 + 2 * i) * a.D + ch), ypend[i]);
     }
   };
   auto block = [&](int blk, float (*bc_cur)[2 * kN], float (*bc_nxt)[2 * kN]) {
@@ -340,20 +355,28 @@ __global__ __launch_bounds__(kW * 64) void scan_chunked_kernel(ScanArgs a) {
       agg_s[wv][3][lane] = make_float4(hl[4], hl[5], hl[6], hl[7]);
     }
     lds_barrier();
-    // carry <- transfers of waves 0 .. wv-1 (this segment's h_in), then of the rest
-    auto fold = [&](int w2) {
-      const float4 P0 = agg_s[w2][0][lane], P1 = agg_s[w2][1][lane];
-      const float4 S0 = agg_s[w2][2][lane], S1 = agg_s[w2][3][lane];
-      const float Pv[kG] = {P0.x, P0.y, P0.z, P0.w, P1.x, P1.y, P1.z, P1.w};
-      const float Sv[kG] = {S0.x, S0.y, S0.z, S0.w, S1.x, S1.y, S1.z, S1.w};
+    // chain pass: P of segment w becomes that segment's h_in
+    {
+      float *agg = &agg_s[0][0][0].x;
+      float Pw[kW], Sw[kW];
 #pragma unroll
-      for (int j = 0; j < kG; ++j) carry[j] = __builtin_fmaf(Pv[j], carry[j], Sv[j]);
-    };
-    for (int w2 = 0; w2 < wv; ++w2) fold(w2);
+      for (int w2 = 0; w2 < kW; ++w2) {
+        Pw[w2] = agg[w2 * 1024 + tid];
+        Sw[w2] = agg[w2 * 1024 + 512 + tid];
+      }
+#pragma unroll
+      for (int w2 = 0; w2 < kW; ++w2) {
+        agg[w2 * 1024 + tid] = carry;
+        carry = __builtin_fmaf(Pw[w2], carry, Sw[w2]);
+      }
+    }
+    lds_barrier();
     float hin[kG];
-#pragma unroll
-    for (int j = 0; j < kG; ++j) hin[j] = carry[j];
-    for (int w2 = wv; w2 < kW; ++w2) fold(w2);
+    {
+      const float4 H0 = agg_s[wv][0][lane], H1 = agg_s[wv][1][lane];
+      hin[0] = H0.x; hin[1] = H0.y; hin[2] = H0.z; hin[3] = H0.w;
+      hin[4] = H1.x; hin[5] = H1.y; hin[6] = H1.z; hin[7] = H1.w;
+    }
     // ---- 4. replay from the true h_in; y from the two half-sums of the channel
     float h[kG];
 #pragma unroll
@@ -402,10 +425,7 @@ __global__ __launch_bounds__(kW * 64) void scan_chunked_kernel(ScanArgs a) {
     block(blk, odd ? bc_s1 : bc_s0, odd ? bc_s0 : bc_s1);
   }
   flush();
-  if (a.state && wv == 0) {
-#pragma unroll
-    for (int j = 0; j < kG; ++j) a.state[((int64_t)b * a.D + ch) * kN + kG * p + j] = carry[j];
-  }
+  if (a.state) a.state[qidx] = carry;
 }
 
 template <typename T, int K>
