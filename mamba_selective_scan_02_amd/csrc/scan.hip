@@ -106,29 +106,31 @@ __global__ __launch_bounds__(64) void scan_seq_kernel(ScanArgs a) {
 // Time-parallel scan for long sequences (few sequences x channels to fill 256 CUs).
 //
 // A workgroup owns kCh = 32 channels of one sequence and walks the sequence in blocks of
-// kW * kS = 128 tokens. Per block:
-//  0. The block's x (with the 3 conv-window rows before it), z, dt and B|C rows were loaded
-//     into LDS with direct-to-LDS 16-byte loads while the previous block was computed.
-//  1. Prep (all 512 threads, one (channel, 8 tokens) run each): u = SiLU(conv1d(x) + b),
-//     dt, dt*u, D*u and SiLU(z), once per (token, channel), into LDS.
-//  2. Local pass: wave w takes tokens 16w .. 16w+15; lane l works on channel l/2 and states
-//     8*(l%2) .. +7. The segment is scanned from h = 0, keeping exp(dt*A) of every
-//     (token, state) in VGPRs (one exp per element, as in the sequential recurrence).
+// kW * kS = 128 tokens; wave w owns the 16-token segment w of every block, and everything but
+// the carry composition stays inside the wave (its own LDS rows, no workgroup barrier):
+//  0. The segment's B|C rows, its x rows (with the 3 conv-window rows before it), z and dt
+//     rows were loaded into the wave's LDS rows with direct-to-LDS 16-byte loads while the
+//     previous block was computed.
+//  1. Prep: lane l takes channel l/2 and tokens 8*(l%2) .. +7 of the segment: u = SiLU(conv1d(x)
+//     + b), dt, dt*u, D*u and SiLU(z), once per (token, channel), into the wave's LDS rows.
+//  2. Local pass: lane l works on channel l/2 and states 8*(l%2) .. +7. The segment is scanned
+//     from h = 0, keeping exp(dt*A) of every (token, state) in VGPRs (one exp per element, as
+//     in the sequential recurrence).
 //  3. Compose: the segment's transfer h -> P h + S (P = exp(A * sum dt), S = the local end
 //     state) goes to LDS. Thread i then owns one (channel, state) chain: it applies the 8
 //     transfers in order to the block's carry-in with the page's associative operator
 //     ("Parallel training via the parallel scan": (a, b) then (c, d) gives (ac, ad + b) for
 //     h -> a h + b), writing each segment's h_in over that segment's P, and keeps the result
-//     as the next block's carry-in.
+//     as the next block's carry-in. These are the block's only two workgroup barriers.
 //  4. Replay from the true h_in with the stored exp(dt*A); y_t = C_t . h_t; the two half-sums
 //     of a channel meet by a DPP lane swap; y = (y_ssm + D u) * SiLU(z) goes out as bf16/f32.
 constexpr int kCh = 32, kW = 8, kS = 16, kG = 8, kBlk = kW * kS;
-constexpr int kHalo = 3;                  // x rows before the block (conv window, K - 1 <= 3)
-constexpr int kXRows = kBlk + 16;         // staged x rows: halo + block, padded to 16-row loads
+constexpr int kHalo = 3;                  // x rows before the segment (conv window, K - 1 <= 3)
+constexpr int kXSeg = kS + 4;             // staged x rows per segment: halo + segment, padded
 
 // One direct-to-LDS 16-byte load per lane: lane i of the wave fills bytes [16 i, 16 i + 16)
-// of the 1 KB LDS window at `lds` (wave-uniform). Issued opaquely (see dma16_opaque): the block
-// loop waits for it explicitly.
+// of the window at `lds` (wave-uniform). Issued opaquely (see dma16_opaque): the block loop
+// waits for it explicitly.
 __device__ __forceinline__ void load_lds16(const void *src, void *lds) {
   dma16_opaque(src, lds_addr(lds));
 }
@@ -142,18 +144,18 @@ __global__ __launch_bounds__(kW * 64) void scan_chunked_kernel(ScanArgs a) {
   // bf16 I/O stages x, z and dt through LDS too; fp32 I/O (small problems) reads them from
   // global memory in the prep phase, which keeps its LDS within 160 KB.
   constexpr bool kStageXZD = sizeof(T) == 2;
-  constexpr int kXR = kStageXZD ? kXRows : 1, kZR = kStageXZD ? kBlk : 1;
-  // staging (written by async loads); B|C double-buffered in two arrays so that the compiler
-  // can tell the prefetch target from the tile being read
-  __shared__ __attribute__((aligned(16))) float bc_s0[kBlk][2 * kN];
-  __shared__ __attribute__((aligned(16))) float bc_s1[kBlk][2 * kN];
-  __shared__ __attribute__((aligned(16))) T x_s[kXR][kCh];
-  __shared__ __attribute__((aligned(16))) T z_s[kZR][kCh];
-  __shared__ __attribute__((aligned(16))) DT d_s[kZR][kCh];
-  // prep outputs: (dt, dt*u) and (D*u, SiLU(z)) per (token, channel); rows padded by one
-  // element so that rows 1 and 8 apart fall in different LDS banks
-  __shared__ __attribute__((aligned(16))) float2 pd_s[kBlk][kCh + 1];
-  __shared__ __attribute__((aligned(16))) float2 eg_s[kBlk][kCh + 1];
+  constexpr int kXR = kStageXZD ? kXSeg : 1, kZR = kStageXZD ? kS : 1;
+  // per-wave staging (written by async loads); B|C double-buffered in two arrays so that the
+  // compiler can tell the prefetch target from the tile being read
+  __shared__ __attribute__((aligned(16))) float bc_s0[kW][kS][2 * kN];
+  __shared__ __attribute__((aligned(16))) float bc_s1[kW][kS][2 * kN];
+  __shared__ __attribute__((aligned(16))) T x_s[kW][kXR][kCh];
+  __shared__ __attribute__((aligned(16))) T z_s[kW][kZR][kCh];
+  __shared__ __attribute__((aligned(16))) DT d_s[kW][kZR][kCh];
+  // prep outputs: (dt, dt*u) and (D*u, SiLU(z)) per (token, channel) of each wave's segment;
+  // rows padded by one element so that rows 8 apart fall in different LDS banks
+  __shared__ __attribute__((aligned(16))) float2 pd_s[kW][kS][kCh + 1];
+  __shared__ __attribute__((aligned(16))) float2 eg_s[kW][kS][kCh + 1];
   // segment transfers, lane-contiguous 16-byte slots: [wave][P0..3, P4..7, S0..3, S4..7][lane]
   __shared__ __attribute__((aligned(16))) float4 agg_s[kW][4][64];
 
@@ -179,9 +181,6 @@ __global__ __launch_bounds__(kW * 64) void scan_chunked_kernel(ScanArgs a) {
   const int ql = (tid >> 2) & 63, qj = 4 * (tid >> 8) + (tid & 3);
   const int64_t qidx = ((int64_t)b * a.D + ch0 + (ql >> 1)) * kN + kG * (ql & 1) + qj;
   float carry = (a.state_valid && a.state) ? a.state[qidx] : 0.f;
-  // prep thread: channel pc, tokens 8*pt .. 8*pt+7 of the block
-  const int pc = tid & (kCh - 1), pt = tid >> 5;
-  const int pch = ch0 + pc;
 
   const int64_t row = 2LL * a.D;
   const T *xzb = (const T *)a.xz + (int64_t)b * a.L * row;
@@ -191,111 +190,112 @@ __global__ __launch_bounds__(kW * 64) void scan_chunked_kernel(ScanArgs a) {
   const int nblocks = (a.L + kBlk - 1) / kBlk;
   const int Lm1 = a.L - 1;
 
-  // Issue the direct-to-LDS loads of block `blk` (rows past the end read row L-1 so every
-  // address is valid; prep and the scan ignore those rows).
+  // Issue the direct-to-LDS loads of this wave's segment of block `blk`. Rows outside
+  // [0, L) read the nearest valid row (every address is valid; prep and the scan ignore
+  // those rows). Addresses are a wave-uniform base plus signed 32-bit lane offsets (a
+  // segment past the end has rmax < 0).
   auto stage = [&](int blk, float (*bcdst)[2 * kN]) {
-    const int T0 = blk * kBlk;
-    // Rows past the end read row L-1 (valid addresses; prep and the scan ignore them). Addresses
-    // are a wave-uniform per-block base plus 32-bit lane offsets.
-    const int rmax = Lm1 - T0;                    // last valid block-relative row
-    // B|C: 128 rows x 128 B = 16 KB = 16 wave-loads; wave wv does loads wv and wv + 8
-    const float *bcbase = bcb + (int64_t)T0 * 2 * kN;
+    const int T0w = blk * kBlk + wv * kS;
+    const int rmax = Lm1 - T0w;                   // last valid segment-relative row
+    // B|C: 16 rows x 128 B = 2 wave-loads, 8 lanes per row
+    const float *bcbase = bcb + (int64_t)T0w * 2 * kN;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const int ld = wv + i * kW;                 // 1 KB window index
-      const int r = min(ld * 8 + (lane >> 3), rmax);   // 8 lanes per 128-byte row
-      load_lds16(bcbase + (uint32_t)(r * 2 * kN + (lane & 7) * 4), &bcdst[ld * 8][0]);
+      const int r = min(i * 8 + (lane >> 3), rmax);
+      load_lds16(bcbase + (r * 2 * kN + (lane & 7) * 4), &bcdst[i * 8][0]);
     }
     if (!kStageXZD) return;
-    // x: kXRows rows x 64 B (bf16) = 9 wave-loads of 16 rows; row r <-> token T0 - 3 + r
-    constexpr int xrpl = 64 / xrow_chunks;        // rows per wave-load
-    const T *xbase = xzb + (int64_t)T0 * row + ch0;
-    const uint32_t rowe = (uint32_t)row;
-    for (int ld = wv; ld < kXRows / xrpl; ld += kW) {
-      const int r = min(max(ld * xrpl + lane / xrow_chunks - kHalo, -T0), rmax);
-      load_lds16(xbase + (int)(r * (int)rowe) + (lane % xrow_chunks) * xper, &x_s[ld * xrpl][0]);
+    // x: row r <-> token T0w - 3 + r, r < kXSeg; xrpl rows per wave-load
+    constexpr int xrpl = 64 / xrow_chunks;
+    const T *xbase = xzb + (int64_t)T0w * row + ch0;
+    const int irow = (int)row;
+#pragma unroll
+    for (int ld = 0; ld * xrpl < kXSeg; ++ld) {
+      const int rr = ld * xrpl + lane / xrow_chunks;
+      if (rr < kXSeg) {
+        const int r = min(max(rr - kHalo, -T0w), rmax);
+        load_lds16(xbase + r * irow + (lane % xrow_chunks) * xper, &x_s[wv][ld * xrpl][0]);
+      }
     }
-    for (int ld = wv; ld < kBlk / xrpl; ld += kW) {
-      const int r = min(ld * xrpl + lane / xrow_chunks, rmax);
-      load_lds16(xbase + a.D + (uint32_t)(r * rowe) + (lane % xrow_chunks) * xper,
-                 &z_s[ld * xrpl][0]);
+    {
+      const int r = min(lane / xrow_chunks, rmax);
+      load_lds16(xbase + a.D + r * irow + (lane % xrow_chunks) * xper, &z_s[wv][0][0]);
     }
-    constexpr int drpl = 64 / drow_chunks;
     constexpr int dper = 16 / sizeof(DT);
-    const DT *dbase = db + (int64_t)T0 * a.D + ch0;
-    for (int ld = wv; ld < kBlk / drpl; ld += kW) {
-      const int r = min(ld * drpl + lane / drow_chunks, rmax);
-      load_lds16(dbase + (uint32_t)(r * a.D) + (lane % drow_chunks) * dper, &d_s[ld * drpl][0]);
+    const DT *dbase = db + (int64_t)T0w * a.D + ch0;
+    {
+      const int r = min(lane / drow_chunks, rmax);
+      load_lds16(dbase + r * a.D + (lane % drow_chunks) * dper, &d_s[wv][0][0]);
     }
   };
 
   // y of block b is stored at the start of block b+1, after that block's wait, so the wait
   // for the staged tiles never has to cover freshly issued stores. Lane (c, p) owns tokens
-  // tb0 + 2i + p of its wave's segment.
+  // 2i + p of its wave's segment.
   float ypend[kS / 2];
   int ypend_t0 = -1;
   auto flush = [&]() {
     if (ypend_t0 < 0) return;
-    // wave-uniform block base, 32-bit lane offsets (a block spans < 2^31 / sizeof(T) elements)
-    T *ybase = yb + (int64_t)ypend_t0 * a.D;
-    const int tl0 = wv * kS + p;
+    // wave-uniform segment base, 32-bit lane offsets
+    T *ybase = yb + (int64_t)(ypend_t0 + wv * kS) * a.D;
     if (ypend_t0 + kBlk <= a.L) {
 #pragma unroll
       for (int i = 0; i < kS / 2; ++i)
-        io<T>::st(ybase + (uint32_t)((tl0 + 2 * i) * a.D + ch), ypend[i]);
+        io<T>::st(ybase + (uint32_t)((2 * i + p) * a.D + ch), ypend[i]);
     } else {
 #pragma unroll
       for (int i = 0; i < kS / 2; ++i)
-        if (ypend_t0 + tl0 + 2 * i < a.L)
-          io<T>::st(ybase + (uint32_t)((tl0 + 2 * i) * a.D + ch), ypend[i]);
+        if (ypend_t0 + wv * kS + 2 * i + p < a.L)
+          io<T>::st(ybase + (uint32_t)((2 * i + p) * a.D + ch), ypend[i]);
     }
   };
-  auto block = [&](int blk, float (*bc_cur)[2 * kN], float (*bc_nxt)[2 * kN]) {
+  auto block = [&](int blk, float (*bc_cur)[kS][2 * kN], float (*bc_nxt)[kS][2 * kN]) {
     const int T0 = blk * kBlk;
-    wait_vmem_all();   // this wave's staged tiles (and its older stores) have landed
-    lds_barrier();     // ... and every wave's; the previous block is fully consumed
+    const int T0w = T0 + wv * kS;
+    wait_vmem_all();   // this wave's staged rows (and its older stores) have landed
     flush();
 
-    // ---- 1. prep: conv + SiLU, dt, dt*u, D*u, SiLU(z) for (pc, tokens 8pt..8pt+7)
+    // ---- 1. prep: conv + SiLU, dt, dt*u, D*u, SiLU(z) for (c, segment tokens 8p..8p+7)
     {
       // per-channel constants, reloaded each block (cache hits) to keep them out of the
       // registers that live across the scan
       float wc[K];
 #pragma unroll
-      for (int k = 0; k < K; ++k) wc[k] = io<T>::cvt(((const T *)a.conv_w)[(int64_t)pch * K + k]);
-      const float cb = a.conv_b ? io<T>::cvt(((const T *)a.conv_b)[pch]) : 0.0f;
-      const float Dp = a.Dskip[pch];
-      // block-relative token tb (tb >= -3, T0 + tb < L where it matters)
-      auto getx = [&](int tb) -> float {
-        if (kStageXZD) return io<T>::cvt(x_s[(kStageXZD ? tb + kHalo : 0)][pc]);
-        return io<T>::cvt(xzb[(int64_t)min(T0 + tb, Lm1) * row + pch]);
+      for (int k = 0; k < K; ++k) wc[k] = io<T>::cvt(((const T *)a.conv_w)[(int64_t)ch * K + k]);
+      const float cb = a.conv_b ? io<T>::cvt(((const T *)a.conv_b)[ch]) : 0.0f;
+      const float Dp = a.Dskip[ch];
+      // segment-relative token ts (ts >= -3)
+      auto getx = [&](int ts) -> float {
+        if (kStageXZD) return io<T>::cvt(x_s[wv][kStageXZD ? ts + kHalo : 0][c]);
+        return io<T>::cvt(xzb[(int64_t)min(T0w + ts, Lm1) * row + ch]);
       };
-      auto getz = [&](int tb) -> float {
-        if (kStageXZD) return io<T>::cvt(z_s[(kStageXZD ? tb : 0)][pc]);
-        return io<T>::cvt(xzb[(int64_t)min(T0 + tb, Lm1) * row + a.D + pch]);
+      auto getz = [&](int ts) -> float {
+        if (kStageXZD) return io<T>::cvt(z_s[wv][kStageXZD ? ts : 0][c]);
+        return io<T>::cvt(xzb[(int64_t)min(T0w + ts, Lm1) * row + a.D + ch]);
       };
-      auto getd = [&](int tb) -> float {
-        if (kStageXZD) return (float)d_s[(kStageXZD ? tb : 0)][pc];
-        return (float)db[(int64_t)min(T0 + tb, Lm1) * a.D + pch];
+      auto getd = [&](int ts) -> float {
+        if (kStageXZD) return (float)d_s[wv][kStageXZD ? ts : 0][c];
+        return (float)db[(int64_t)min(T0w + ts, Lm1) * a.D + ch];
       };
+      const int ts0 = 8 * p;
       float win[K - 1];
 #pragma unroll
       for (int j = 0; j < K - 1; ++j) {
-        const int tb = pt * 8 - (K - 1) + j;      // block-relative token of this window row
-        const int t = T0 + tb;
+        const int ts = ts0 - (K - 1) + j;         // segment-relative token of this window row
+        const int t = T0w + ts;
         float v = 0.f;
         if (t >= 0) {
-          v = getx(tb);
+          v = getx(ts);
         } else if (a.conv_valid && a.conv_state) {
-          v = io<T>::cvt(((const T *)a.conv_state)[((int64_t)b * a.D + pch) * (K - 1) + (K - 1) + t]);
+          v = io<T>::cvt(((const T *)a.conv_state)[((int64_t)b * a.D + ch) * (K - 1) + (K - 1) + t]);
         }
         win[j] = v;
       }
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const int tb = pt * 8 + e;
-        const bool valid = T0 + tb < a.L;
-        const float x = getx(tb);
+        const int ts = ts0 + e;
+        const bool valid = T0w + ts < a.L;
+        const float x = getx(ts);
         float acc = cb;
 #pragma unroll
         for (int j = 0; j < K - 1; ++j) acc = __builtin_fmaf(wc[j], win[j], acc);
@@ -304,20 +304,19 @@ __global__ __launch_bounds__(kW * 64) void scan_chunked_kernel(ScanArgs a) {
         for (int j = 0; j + 1 < K - 1; ++j) win[j] = win[j + 1];
         win[K - 2] = x;
         const float u = silu_f(acc);
-        const float dt = valid ? getd(tb) : 0.f;
-        const float z = getz(tb);
+        const float dt = valid ? getd(ts) : 0.f;
+        const float z = getz(ts);
         // ZOH replays Bbar u = expm1(dt A)/A * B * u, so it keeps u where Euler keeps dt*u
-        pd_s[tb][pc] = make_float2(dt, valid ? (ZOH ? u : dt * u) : 0.f);
-        eg_s[tb][pc] = make_float2(valid ? Dp * u : 0.f, valid ? silu_f(z) : 0.f);
+        pd_s[wv][ts][c] = make_float2(dt, valid ? (ZOH ? u : dt * u) : 0.f);
+        eg_s[wv][ts][c] = make_float2(valid ? Dp * u : 0.f, valid ? silu_f(z) : 0.f);
       }
     }
-    lds_barrier();
-    // next block's staging overlaps this block's scan (x, z, dt tiles are free after prep;
-    // B|C is double-buffered)
-    if (blk + 1 < nblocks) stage(blk + 1, bc_nxt);
+    // the staged x, z, dt rows are consumed once this wave's LDS reads have returned; then the
+    // next block's rows may land (B|C is double-buffered)
+    __builtin_amdgcn_s_waitcnt(0xC07F);           // lgkmcnt(0), vmcnt / expcnt unconstrained
+    if (blk + 1 < nblocks) stage(blk + 1, bc_nxt[wv]);
 
     // ---- 2. local pass over this wave's segment
-    const int tb0 = wv * kS;
     float dA[kS][kG];
     float hl[kG];
 #pragma unroll
@@ -325,12 +324,11 @@ __global__ __launch_bounds__(kW * 64) void scan_chunked_kernel(ScanArgs a) {
     float sumdt = 0.f;
 #pragma unroll
     for (int t = 0; t < kS; ++t) {
-      const int tb = tb0 + t;
-      const float2 pd = pd_s[tb][c];
+      const float2 pd = pd_s[wv][t][c];
       const float dt = pd.x, du = pd.y;
       sumdt += dt;
-      const float4 B0 = *(const float4 *)&bc_cur[tb][kG * p];
-      const float4 B1 = *(const float4 *)&bc_cur[tb][kG * p + 4];
+      const float4 B0 = *(const float4 *)&bc_cur[wv][t][kG * p];
+      const float4 B1 = *(const float4 *)&bc_cur[wv][t][kG * p + 4];
       const float Bv[kG] = {B0.x, B0.y, B0.z, B0.w, B1.x, B1.y, B1.z, B1.w};
 #pragma unroll
       for (int j = 0; j < kG; ++j) {
@@ -371,37 +369,34 @@ __global__ __launch_bounds__(kW * 64) void scan_chunked_kernel(ScanArgs a) {
       }
     }
     lds_barrier();
-    float hin[kG];
+    float h[kG];
     {
       const float4 H0 = agg_s[wv][0][lane], H1 = agg_s[wv][1][lane];
-      hin[0] = H0.x; hin[1] = H0.y; hin[2] = H0.z; hin[3] = H0.w;
-      hin[4] = H1.x; hin[5] = H1.y; hin[6] = H1.z; hin[7] = H1.w;
+      h[0] = H0.x; h[1] = H0.y; h[2] = H0.z; h[3] = H0.w;
+      h[4] = H1.x; h[5] = H1.y; h[6] = H1.z; h[7] = H1.w;
     }
     // ---- 4. replay from the true h_in; y from the two half-sums of the channel
-    float h[kG];
-#pragma unroll
-    for (int j = 0; j < kG; ++j) h[j] = hin[j];
 #pragma unroll
     for (int t = 0; t < kS; t += 2) {
       float ys[2];
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
-        const int tb = tb0 + t + e;
-        const float4 B0 = *(const float4 *)&bc_cur[tb][kG * p];
-        const float4 B1 = *(const float4 *)&bc_cur[tb][kG * p + 4];
-        const float4 C0 = *(const float4 *)&bc_cur[tb][kN + kG * p];
-        const float4 C1 = *(const float4 *)&bc_cur[tb][kN + kG * p + 4];
+        const int ts = t + e;
+        const float4 B0 = *(const float4 *)&bc_cur[wv][ts][kG * p];
+        const float4 B1 = *(const float4 *)&bc_cur[wv][ts][kG * p + 4];
+        const float4 C0 = *(const float4 *)&bc_cur[wv][ts][kN + kG * p];
+        const float4 C1 = *(const float4 *)&bc_cur[wv][ts][kN + kG * p + 4];
         const float Bv[kG] = {B0.x, B0.y, B0.z, B0.w, B1.x, B1.y, B1.z, B1.w};
         const float Cv[kG] = {C0.x, C0.y, C0.z, C0.w, C1.x, C1.y, C1.z, C1.w};
-        const float du = pd_s[tb][c].y;
+        const float du = pd_s[wv][ts][c].y;
         float yy = 0.f;
 #pragma unroll
         for (int j = 0; j < kG; ++j) {
           if (ZOH) {
-            const float em1 = dA[t + e][j];
+            const float em1 = dA[ts][j];
             h[j] = __builtin_fmaf(em1 + 1.0f, h[j], em1 * iA[j] * Bv[j] * du);
           } else {
-            h[j] = __builtin_fmaf(dA[t + e][j], h[j], du * Bv[j]);
+            h[j] = __builtin_fmaf(dA[ts][j], h[j], du * Bv[j]);
           }
           yy = __builtin_fmaf(Cv[j], h[j], yy);
         }
@@ -412,14 +407,13 @@ __global__ __launch_bounds__(kW * 64) void scan_chunked_kernel(ScanArgs a) {
       const float send = p ? ys[0] : ys[1];
       const float other = __builtin_bit_cast(
           float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, send), 0xB1, 0xF, 0xF, false));
-      const int tb = tb0 + t + p;
-      const float2 eg = eg_s[tb][c];
+      const float2 eg = eg_s[wv][t + p][c];
       ypend[t / 2] = (keep + other + eg.x) * eg.y;
     }
     ypend_t0 = T0;
   };
 
-  stage(0, bc_s0);
+  stage(0, bc_s0[wv]);
   for (int blk = 0; blk < nblocks; ++blk) {
     const bool odd = blk & 1;
     block(blk, odd ? bc_s1 : bc_s0, odd ? bc_s0 : bc_s1);
