@@ -16,7 +16,8 @@
 //     which makes the 16-row fragment reads of the MFMA loop bank-conflict free.
 //   * Lane l of wave w owns token 16w + l%16 and channels 8*(l/16) .. +7 of each 32-channel
 //     k-step: exactly the MFMA B-operand fragment of v_mfma_f32_16x16x32_bf16. It computes
-//     u = SiLU(conv) for those 8 channels in fp32 from the staged x rows, splits
+//     u = SiLU(conv) for those 8 channels in fp32 from the staged x rows (the 4-tap conv as
+//     two packed bf16 dot products per channel), splits
 //     u = hi + lo (both bf16) and issues two MFMAs per W fragment, so the product carries u to
 //     ~2^-17 relative.
 //   * Epilogue: lane (token, 4 consecutive outputs per 16-wide block) squares and sums its
@@ -29,6 +30,7 @@ namespace mm {
 namespace {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 
 constexpr int kTok = 128;          // tokens per workgroup
@@ -99,14 +101,14 @@ __global__ __launch_bounds__(512) void xproj_fused_kernel(XprojFusedArgs a) {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       const int lc = ks * 4 + g;                  // logical 16-byte chunk = 8 channels
-      // x rows tw .. tw+3 of this lane's 8 channels (row tw+3 is the current token)
-      float xv[4][8];
+      // x rows tw .. tw+3 of this lane's 8 channels (row tw+3 is the current token), as
+      // packed bf16 pairs (dword k holds channels 2k, 2k+1)
+      uint32_t xr[4][4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int r = tw + j;
         const uint4 v = *(const uint4 *)&x_s[buf][r][swz(r, lc) * 8];
-        xv[j][0] = lo_bf(v.x); xv[j][1] = hi_bf(v.x); xv[j][2] = lo_bf(v.y); xv[j][3] = hi_bf(v.y);
-        xv[j][4] = lo_bf(v.z); xv[j][5] = hi_bf(v.z); xv[j][6] = lo_bf(v.w); xv[j][7] = hi_bf(v.w);
+        xr[j][0] = v.x; xr[j][1] = v.y; xr[j][2] = v.z; xr[j][3] = v.w;
       }
       if (first_tile && tw < 3) {
         // rows before token 0: carried conv state (oldest first) or zeros
@@ -115,25 +117,33 @@ __global__ __launch_bounds__(512) void xproj_fused_kernel(XprojFusedArgs a) {
           const int t = tw + j - 3;
           if (t < 0) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const int ch = c0 + lc * 8 + e;
-              xv[j][e] = (a.conv_valid && a.conv_state)
-                             ? bf2f(a.conv_state[((int64_t)b * a.D + ch) * (K - 1) + (K - 1) + t])
-                             : 0.f;
+            for (int k = 0; k < 4; ++k) {
+              uint32_t w = 0;
+              if (a.conv_valid && a.conv_state) {
+                const int64_t s0 = ((int64_t)b * a.D + c0 + lc * 8 + 2 * k) * (K - 1) + (K - 1) + t;
+                w = (uint32_t)a.conv_state[s0] | ((uint32_t)a.conv_state[s0 + (K - 1)] << 16);
+              }
+              xr[j][k] = w;
             }
           }
         }
       }
-      // conv taps for these 8 channels: cw_s[ch*4 + k]
+      // conv = (x_{t-3}, x_{t-2}) . (w0, w1) + (x_{t-1}, x_t) . (w2, w3) + b: each pair of
+      // window rows of one channel is gathered into one bf16x2 (v_perm) and multiplied with the
+      // channel's packed taps (v_dot2, fp32 accumulate)
       float u[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int cl = lc * 8 + e;
-        const uint2 wr = *(const uint2 *)&cw_s[buf][cl * 4];   // 4 taps (K <= 4)
-        const float wk[4] = {lo_bf(wr.x), hi_bf(wr.x), lo_bf(wr.y), hi_bf(wr.y)};
+        const uint2 wr = *(const uint2 *)&cw_s[buf][cl * 4];   // (w0 | w1), (w2 | w3)
+        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+        const uint32_t p01 = __builtin_amdgcn_perm(xr[1][e >> 1], xr[0][e >> 1], sel);
+        const uint32_t p23 = __builtin_amdgcn_perm(xr[3][e >> 1], xr[2][e >> 1], sel);
         float accv = a.conv_b ? bf2f(cb_s[buf][cl]) : 0.f;
-#pragma unroll
-        for (int k = 0; k < K; ++k) accv = __builtin_fmaf(wk[k], xv[4 - K + k][e], accv);
+        accv = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, p01),
+                                              __builtin_bit_cast(bf16x2, wr.x), accv, false);
+        accv = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, p23),
+                                              __builtin_bit_cast(bf16x2, wr.y), accv, false);
         u[e] = silu_f(accv);
       }
       uint4 hi, lo;
