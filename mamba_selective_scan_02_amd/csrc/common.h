@@ -72,11 +72,19 @@ __device__ __forceinline__ float softplus_f(float v) {
 __device__ __forceinline__ void wait_vmem_all() {
   __builtin_amdgcn_s_waitcnt(0 | (0x7 << 4) | (0xF << 8));
 }
+// At most N of this wave's vector-memory loads still in flight (the oldest ones complete
+// first). Only for waves whose outstanding vector-memory operations are all loads: stores
+// and loads do not retire in a common order.
+template <int N>
+__device__ __forceinline__ void wait_vmem_le() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
 
 // Workgroup barrier that orders LDS only: this wave's LDS reads and writes complete, then all
 // waves meet. Global stores and direct-to-LDS prefetches issued before it stay in flight (a
 // __syncthreads() would drain them); a prefetch that other waves read after a barrier must be
-// waited for explicitly (wait_vmem_le) before it. The memory clobber keeps the compiler from
+// waited for explicitly (wait_vmem_all / wait_vmem_le) before it. The memory clobber keeps the compiler from
 // moving memory accesses across it.
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -84,7 +92,7 @@ __device__ __forceinline__ void lds_barrier() {
 
 // Direct-to-LDS 16-byte load issued opaquely: lane i of the wave writes bytes
 // [lds_base + 16 i, +16) of LDS from its own global address. The compiler does not see the LDS
-// write, so it inserts no waits for it; the caller synchronises (wait_vmem_le + barrier) before
+// write, so it inserts no waits for it; the caller synchronises (a vmcnt wait + barrier) before
 // any wave reads that LDS. lds_base must be wave-uniform. No VGPR is written by the load.
 __device__ __forceinline__ void dma16_opaque(const void *gptr, uint32_t lds_base) {
   const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_base);
