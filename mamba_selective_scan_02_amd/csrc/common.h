@@ -101,6 +101,22 @@ __device__ __forceinline__ void dma16_opaque(const void *gptr, uint32_t lds_base
                : "v"(gptr), "s"(m0v)
                : "memory", "m0");
 }
+// As dma16_opaque, addressing global memory as a wave-uniform base plus this lane's unsigned
+// 32-bit byte offset (the base lives in SGPRs, one VGPR per lane for the offset).
+__device__ __forceinline__ void dma16_opaque_so(const void *sbase, uint32_t voff,
+                                                uint32_t lds_base) {
+  // readfirstlane works on int: each half goes back to uint32_t before widening, so the low
+  // half is zero-extended (sign-extending it would corrupt the high half of the address)
+  const uint64_t bp = (uint64_t)(uintptr_t)sbase;
+  const uint32_t bhi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(bp >> 32));
+  const uint32_t blo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)bp);
+  const uint64_t sb = ((uint64_t)bhi << 32) | (uint64_t)blo;
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_base);
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(sb), "s"(m0v)
+               : "memory", "m0");
+}
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
 }

@@ -11,16 +11,18 @@
 //     run in the epilogue (xdbl never goes to memory).
 //   * The contraction over d_inner advances in chunks of 32 channels (one MFMA k-step) through
 //     a producer / consumer pipeline with one workgroup barrier per chunk:
-//       - producer waves 0..3 form u = SiLU(conv1d(x) + b) of chunk i in fp32 (the 4-tap conv
-//         as two packed bf16 dot products per channel), split it as u = hi + lo (both bf16)
-//         and write both into LDS; they also issue the direct-to-LDS loads of the x rows,
-//         conv taps and W_x rows of chunk i + 2;
-//       - consumer waves 4..7 (one per SIMD) multiply chunk i - 1: wave 4 + c owns tokens
-//         32c .. 32c+31 and every output row, two MFMAs (u_lo, u_hi) per W fragment, so the
-//         product carries u to ~2^-17 relative.
+//       - producer waves 0..7 (lane = one token x 8 channels) form u = SiLU(conv1d(x) + b) of
+//         chunk i in fp32 (the 4-tap conv as two packed bf16 dot products per channel), split
+//         it as u = hi + lo (both bf16) and write both into LDS; they also issue the
+//         direct-to-LDS loads of the x rows, conv taps and W_x rows of chunk i + 2;
+//       - consumer waves 8..15 multiply chunk i - 1: wave 8 + c owns tokens 16c .. 16c+15 and
+//         every output row, two MFMAs (u_lo, u_hi) per W fragment, so the product carries u
+//         to ~2^-17 relative.
+//     Each SIMD runs two producer and two consumer waves (<= 128 VGPRs each), so the VALU
+//     work of one role overlaps the MFMAs of the other.
 //     W_x chunks are 4-deep buffered, x rows 3-deep, u 2-deep. LDS rows are 64 B; 16-byte
-//     slot s of row r holds logical slot s ^ ((r >> 2) & 3), which keeps the 16-row fragment
-//     reads and writes bank-conflict free.
+//     slots are XOR-swizzled by row so the 16-row fragment reads and writes are
+//     bank-conflict free.
 //   * Epilogue (consumers): lane (token, 4 consecutive outputs per 16-wide block) squares and
 //     sums its dt_low / B / C values, the 4 lanes of a token reduce by lane shuffles, and the
 //     normalised dt_low (as bf16 hi + lo for dt_proj) and B|C (fp32) are written.
@@ -38,19 +40,23 @@ constexpr int kTok = 128;          // tokens per workgroup
 constexpr int kKC = 32;            // channels per chunk (one MFMA k-step)
 constexpr int kXR = 144;           // staged x rows: 3 before the tile + 128, padded to 16-row loads
 
-// physical 16-byte slot of logical slot c (0..3) in 64-byte row r
-__device__ __forceinline__ int swz(int r, int c) { return c ^ ((r >> 2) & 3); }
+// physical 16-byte slot of logical slot c (0..3) in 64-byte row r: any 16 consecutive rows
+// read at one logical slot fall in distinct 16-byte bank groups both per 128 B (8 rows) and
+// per 256 B (16 rows)
+__device__ __forceinline__ int swz(int r, int c) { return c ^ ((r >> 1) & 3) ^ ((r >> 3) & 1); }
 
 template <int RB, int K>
-__global__ __launch_bounds__(512) void xproj_fused_kernel(XprojFusedArgs a) {
+__global__ __launch_bounds__(1024) void xproj_fused_kernel(XprojFusedArgs a) {
   static_assert(K == 4, "the staged conv taps are laid out as [channel][4]");
   constexpr int R = RB * 16;
   constexpr int NX = R + 32;           // outputs: dt_low | B | C
   constexpr int NB = NX / 16;          // 16-row MFMA blocks
   constexpr int LW = NX / 16;          // 1 KB wave-loads per chunk: W_x rows
   constexpr int LX = kXR / 16;         //                             x rows
-  constexpr int NLOAD = LW + LX + 2;   //                             + taps + bias
-  constexpr int PER = (NLOAD + 3) / 4; // loads per producer wave per chunk (padded)
+  constexpr int PW = (LW + 7) / 8;     // W_x loads per producer wave (padded)
+  constexpr int PX = 2;                // loads per producer wave from the list x rows | taps | bias
+  static_assert(LX + 2 <= 8 * PX, "x-row list");
+  constexpr int PER = PW + PX;         // loads per producer wave per chunk
   __shared__ __attribute__((aligned(16))) bf16_t w_s[4][NX][kKC];
   __shared__ __attribute__((aligned(16))) bf16_t x_s[3][kXR][kKC];
   __shared__ __attribute__((aligned(16))) bf16_t u_s[2][2][kTok][kKC];   // [buf][hi, lo]
@@ -62,50 +68,58 @@ __global__ __launch_bounds__(512) void xproj_fused_kernel(XprojFusedArgs a) {
   const int b = gid / tiles_per_seq;
   const int t0 = (gid % tiles_per_seq) * kTok;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const bool producer = wv < 4;
+  const bool producer = wv < 8;
   const int64_t row = 2LL * a.D;
   const bf16_t *xzb = a.xz + (int64_t)b * a.L * row;
   const int Lm1 = a.L - 1;
   const int nck = a.D / kKC;
 
-  // Producer wave wv issues loads wv, wv + 4, ... of chunk ck's list (indices past the list
-  // repeat load 0, which rewrites the same bytes), so every producer wave issues PER loads.
+  // Producer wave wv issues W_x loads wv, wv + 8, ... and loads wv, wv + 8 of the list
+  // [x row loads | taps | bias]; indices past a list repeat its load 0, which rewrites the
+  // same bytes, so every producer wave issues PER loads per chunk. Addresses are wave-uniform
+  // bases plus unsigned 32-bit lane offsets.
+  const int xrow0 = max(t0 - 3, 0);                 // x rows are read relative to this token
+  const bf16_t *xbase = xzb + (int64_t)xrow0 * row;
+  const bf16_t *bsrc = a.conv_b ? a.conv_b : a.conv_w;  // without a bias: the taps, unused
   auto issue = [&](int ck) {
     const int c0 = ck * kKC;
     const int b3 = ck % 3, b4 = ck & 3;
+    const int ps = lane & 3;
 #pragma unroll
-    for (int q = 0; q < PER; ++q) {
-      int ld = wv + 4 * q;
-      if (ld >= NLOAD) ld = 0;
-      if (ld < LW) {
-        const int r = ld * 16 + (lane >> 2), ps = lane & 3;
-        dma16_opaque(a.w + (int64_t)r * a.D + c0 + swz(r, ps) * 8, lds_addr(&w_s[b4][ld * 16][0]));
-      } else if (ld < LW + LX) {
-        const int lx = ld - LW;
-        const int r = lx * 16 + (lane >> 2), ps = lane & 3;
-        const int tt = min(max(t0 - 3 + r, 0), Lm1);   // row r <-> token t0 - 3 + r
-        dma16_opaque(xzb + (int64_t)tt * row + c0 + swz(r, ps) * 8, lds_addr(&x_s[b3][lx * 16][0]));
-      } else if (ld == LW + LX) {
-        if (lane < 16) dma16_opaque(a.conv_w + (int64_t)c0 * K + lane * 8, lds_addr(&cw_s[b3][0]));
+    for (int q = 0; q < PW; ++q) {
+      int ld = wv + 8 * q;
+      if (ld >= LW) ld = 0;
+      const int r = ld * 16 + (lane >> 2);
+      dma16_opaque_so(a.w, (uint32_t)(r * a.D + c0 + swz(r, ps) * 8) * 2u,
+                      lds_addr(&w_s[b4][ld * 16][0]));
+    }
+#pragma unroll
+    for (int q = 0; q < PX; ++q) {
+      int li = wv + 8 * q;
+      if (li >= LX + 2) li = 0;
+      if (li < LX) {
+        const int r = li * 16 + (lane >> 2);
+        const int tt = min(max(t0 - 3 + r, 0), Lm1) - xrow0;   // row r <-> token t0 - 3 + r
+        dma16_opaque_so(xbase, (uint32_t)(tt * (int)row + c0 + swz(r, ps) * 8) * 2u,
+                        lds_addr(&x_s[b3][li * 16][0]));
+      } else if (li == LX) {
+        if (lane < 16)
+          dma16_opaque_so(a.conv_w, (uint32_t)(c0 * K + lane * 8) * 2u, lds_addr(&cw_s[b3][0]));
       } else {
-        // bias (or, without one, the taps again: the bias slot is then unused)
-        if (lane < 4) {
-          const bf16_t *src = a.conv_b ? a.conv_b + c0 + lane * 8 : a.conv_w + (int64_t)c0 * K + lane * 8;
-          dma16_opaque(src, lds_addr(&cb_s[b3][0]));
-        }
+        if (lane < 4)
+          dma16_opaque_so(bsrc, (uint32_t)(c0 + lane * 8) * 2u, lds_addr(&cb_s[b3][0]));
       }
     }
   };
 
-  // ---- producer: u of chunk ck for token ptok and channel groups pg, pg + 2 (8 channels each)
-  const int pidx = wv * 64 + lane;              // producers: 0 .. 255
-  const int ptok = pidx & (kTok - 1), pg0 = (pidx >> 7) & 1;
+  // ---- producer: u of chunk ck for token ptok and channel group pgrp (8 channels)
+  const int pidx = wv * 64 + lane;              // producers: 0 .. 511
+  const int ptok = pidx & (kTok - 1), pgrp = (pidx >> 7) & 3;
   auto produce = [&](int ck) {
     const int c0 = ck * kKC;
     const int b3 = ck % 3;
-#pragma unroll
-    for (int gi = 0; gi < 2; ++gi) {
-      const int grp = pg0 + 2 * gi;
+    {
+      const int grp = pgrp;
       uint32_t xr[4][4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -165,20 +179,21 @@ __global__ __launch_bounds__(512) void xproj_fused_kernel(XprojFusedArgs a) {
     }
   };
 
-  // ---- consumer: wave 4 + cw, tokens 32 cw .. +31 (two 16-token MFMA column blocks)
-  const int cw = wv - 4;
+  // ---- consumer: wave 8 + cw, tokens 16 cw .. +15 (one MFMA column block)
+  constexpr int TB = 1;
+  const int cw = wv - 8;
   const int tl = lane & 15, g = lane >> 4;
-  f32x4 acc[2][NB];
+  f32x4 acc[TB][NB];
 #pragma unroll
-  for (int tb = 0; tb < 2; ++tb)
+  for (int tb = 0; tb < TB; ++tb)
 #pragma unroll
     for (int i = 0; i < NB; ++i) acc[tb][i] = f32x4{0.f, 0.f, 0.f, 0.f};
   auto consume = [&](int ck) {
     const int ub = ck & 1, b4 = ck & 3;
-    bf16x8 fh[2], fl[2];
+    bf16x8 fh[TB], fl[TB];
 #pragma unroll
-    for (int tb = 0; tb < 2; ++tb) {
-      const int tk = cw * 32 + tb * 16 + tl;
+    for (int tb = 0; tb < TB; ++tb) {
+      const int tk = (cw * TB + tb) * 16 + tl;
       const int sl = swz(tk, g) * 8;
       fh[tb] = __builtin_bit_cast(bf16x8, *(const uint4 *)&u_s[ub][0][tk][sl]);
       fl[tb] = __builtin_bit_cast(bf16x8, *(const uint4 *)&u_s[ub][1][tk][sl]);
@@ -188,36 +203,36 @@ __global__ __launch_bounds__(512) void xproj_fused_kernel(XprojFusedArgs a) {
       const int r = nb * 16 + tl;
       const bf16x8 fw = __builtin_bit_cast(bf16x8, *(const uint4 *)&w_s[b4][r][swz(r, g) * 8]);
 #pragma unroll
-      for (int tb = 0; tb < 2; ++tb) {
+      for (int tb = 0; tb < TB; ++tb) {
         acc[tb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fw, fl[tb], acc[tb][nb], 0, 0, 0);
         acc[tb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fw, fh[tb], acc[tb][nb], 0, 0, 0);
       }
     }
   };
 
+  // The two roles run separate loops with the same barrier count (nck + 1), so the consumers'
+  // accumulators are not live in the producers' code.
   if (producer) {
     issue(0);
     if (nck > 1) issue(1);
-  }
-  for (int it = 0; it <= nck; ++it) {
-    if (producer) {
+    for (int it = 0; it <= nck; ++it) {
       // chunk it's loads (issued two iterations ago) have landed; chunk it+1's may be in flight
       if (it + 1 < nck) wait_vmem_le<PER>();
       else wait_vmem_all();
-    }
-    lds_barrier();
-    if (producer) {
+      lds_barrier();
       if (it + 2 < nck) issue(it + 2);
       if (it < nck) produce(it);
-    } else if (it > 0) {
-      consume(it - 1);
     }
+    return;
   }
-  if (producer) return;
+  for (int it = 0; it <= nck; ++it) {
+    lds_barrier();
+    if (it > 0) consume(it - 1);
+  }
 
-  // ---- epilogue: acc[tb][nb][j] = xdbl[token cw*32 + tb*16 + tl][nb*16 + 4g + j]
+  // ---- epilogue: acc[tb][nb][j] = xdbl[token (cw*TB + tb)*16 + tl][nb*16 + 4g + j]
 #pragma unroll
-  for (int tb = 0; tb < 2; ++tb) {
+  for (int tb = 0; tb < TB; ++tb) {
     float ssd = 0.f, ssb = 0.f, ssc = 0.f;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
@@ -235,7 +250,7 @@ __global__ __launch_bounds__(512) void xproj_fused_kernel(XprojFusedArgs a) {
     const float id = 1.0f / sqrtf(ssd / (float)R + a.eps);
     const float ib = 1.0f / sqrtf(ssb / 16.0f + a.eps);
     const float ic = 1.0f / sqrtf(ssc / 16.0f + a.eps);
-    const int t = t0 + cw * 32 + tb * 16 + tl;
+    const int t = t0 + (cw * TB + tb) * 16 + tl;
     if (t < a.L) {
       const int64_t tok = (int64_t)b * a.L + t;
 #pragma unroll
@@ -267,7 +282,7 @@ template <int RB>
 hipError_t launch_rb(const XprojFusedArgs &a, hipStream_t s) {
   const unsigned grid = (unsigned)(a.B * ((a.L + kTok - 1) / kTok));
   if (a.K != 4) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((xproj_fused_kernel<RB, 4>), dim3(grid), dim3(512), 0, s, a);
+  hipLaunchKernelGGL((xproj_fused_kernel<RB, 4>), dim3(grid), dim3(1024), 0, s, a);
   return hipGetLastError();
 }
 
