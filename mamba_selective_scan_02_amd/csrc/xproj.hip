@@ -20,9 +20,10 @@
 //         to ~2^-17 relative.
 //     Each SIMD runs two producer and two consumer waves (<= 128 VGPRs each), so the VALU
 //     work of one role overlaps the MFMAs of the other.
-//     W_x chunks are 4-deep buffered, x rows 3-deep, u 2-deep. LDS rows are 64 B; 16-byte
-//     slots are XOR-swizzled by row so the 16-row fragment reads and writes are
-//     bank-conflict free.
+//     W_x chunks are 4-deep buffered, x rows 3-deep, u 2-deep. W_x and u are stored in MFMA
+//     fragment order (each 16 x 32 operand block is 1 KB with lane i's 16 bytes at 16 i), so
+//     every fragment read is one contiguous, bank-conflict-free 1 KB access; x rows are 64 B
+//     with 16-byte slots XOR-swizzled by row.
 //   * Epilogue (consumers): lane (token, 4 consecutive outputs per 16-wide block) squares and
 //     sums its dt_low / B / C values, the 4 lanes of a token reduce by lane shuffles, and the
 //     normalised dt_low (as bf16 hi + lo for dt_proj) and B|C (fp32) are written.
@@ -57,9 +58,9 @@ __global__ __launch_bounds__(1024) void xproj_fused_kernel(XprojFusedArgs a) {
   constexpr int PX = 2;                // loads per producer wave from the list x rows | taps | bias
   static_assert(LX + 2 <= 8 * PX, "x-row list");
   constexpr int PER = PW + PX;         // loads per producer wave per chunk
-  __shared__ __attribute__((aligned(16))) bf16_t w_s[4][NX][kKC];
+  __shared__ __attribute__((aligned(16))) bf16_t w_s[4][NB][64 * 8];   // fragment order
   __shared__ __attribute__((aligned(16))) bf16_t x_s[3][kXR][kKC];
-  __shared__ __attribute__((aligned(16))) bf16_t u_s[2][2][kTok][kKC];   // [buf][hi, lo]
+  __shared__ __attribute__((aligned(16))) bf16_t u_s[2][2][kTok / 16][64 * 8];  // [buf][hi, lo]
   __shared__ __attribute__((aligned(16))) bf16_t cw_s[3][kKC * 4];       // conv taps [ch][4]
   __shared__ __attribute__((aligned(16))) bf16_t cb_s[3][kKC];           // conv bias
 
@@ -87,11 +88,12 @@ __global__ __launch_bounds__(1024) void xproj_fused_kernel(XprojFusedArgs a) {
     const int ps = lane & 3;
 #pragma unroll
     for (int q = 0; q < PW; ++q) {
-      int ld = wv + 8 * q;
+      int ld = wv + 8 * q;                          // = 16-row block nb of W_x
       if (ld >= LW) ld = 0;
-      const int r = ld * 16 + (lane >> 2);
-      dma16_opaque_so(a.w, (uint32_t)(r * a.D + c0 + swz(r, ps) * 8) * 2u,
-                      lds_addr(&w_s[b4][ld * 16][0]));
+      // fragment lane l: row 16 nb + l % 16, channels c0 + 8 (l / 16) .. +7
+      const int r = ld * 16 + (lane & 15);
+      dma16_opaque_so(a.w, (uint32_t)(r * a.D + c0 + (lane >> 4) * 8) * 2u,
+                      lds_addr(&w_s[b4][ld][0]));
     }
 #pragma unroll
     for (int q = 0; q < PX; ++q) {
@@ -173,9 +175,10 @@ __global__ __launch_bounds__(1024) void xproj_fused_kernel(XprojFusedArgs a) {
         lo.x = pack_bf2(l8[0], l8[1]); lo.y = pack_bf2(l8[2], l8[3]);
         lo.z = pack_bf2(l8[4], l8[5]); lo.w = pack_bf2(l8[6], l8[7]);
       }
-      const int sl = swz(ptok, grp) * 8;
-      *(uint4 *)&u_s[ck & 1][0][ptok][sl] = hi;
-      *(uint4 *)&u_s[ck & 1][1][ptok][sl] = lo;
+      // fragment lane (token % 16) + 16 * grp of column block token / 16
+      const int fo = (grp * 16 + (ptok & 15)) * 8;
+      *(uint4 *)&u_s[ck & 1][0][ptok >> 4][fo] = hi;
+      *(uint4 *)&u_s[ck & 1][1][ptok >> 4][fo] = lo;
     }
   };
 
@@ -193,15 +196,13 @@ __global__ __launch_bounds__(1024) void xproj_fused_kernel(XprojFusedArgs a) {
     bf16x8 fh[TB], fl[TB];
 #pragma unroll
     for (int tb = 0; tb < TB; ++tb) {
-      const int tk = (cw * TB + tb) * 16 + tl;
-      const int sl = swz(tk, g) * 8;
-      fh[tb] = __builtin_bit_cast(bf16x8, *(const uint4 *)&u_s[ub][0][tk][sl]);
-      fl[tb] = __builtin_bit_cast(bf16x8, *(const uint4 *)&u_s[ub][1][tk][sl]);
+      const int cb = cw * TB + tb;
+      fh[tb] = __builtin_bit_cast(bf16x8, *(const uint4 *)&u_s[ub][0][cb][lane * 8]);
+      fl[tb] = __builtin_bit_cast(bf16x8, *(const uint4 *)&u_s[ub][1][cb][lane * 8]);
     }
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      const int r = nb * 16 + tl;
-      const bf16x8 fw = __builtin_bit_cast(bf16x8, *(const uint4 *)&w_s[b4][r][swz(r, g) * 8]);
+      const bf16x8 fw = __builtin_bit_cast(bf16x8, *(const uint4 *)&w_s[b4][nb][lane * 8]);
 #pragma unroll
       for (int tb = 0; tb < TB; ++tb) {
         acc[tb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fw, fl[tb], acc[tb][nb], 0, 0, 0);
