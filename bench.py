@@ -118,7 +118,7 @@ def prefill_leg(args, mm):
     return out, (xz, p, cfg)
 
 
-def decode_leg(args, mm):
+def decode_leg(args, mm, steps=None):
     cfg = synth.CONFIGS[DECODE_WORKLOAD]
     seed = synth.seed_for(DECODE_WORKLOAD)
     dev = "cuda"
@@ -129,7 +129,7 @@ def decode_leg(args, mm):
     pre = synth.make_xz(cfg, seed, dev, seqlen=cfg.decode_prefix)
     mm.prefill(pre, p, conv_state=cs, ssm_state=ss, states_valid=False, eps=cfg.rms_eps)
     del pre
-    steps = cfg.decode_steps
+    steps = cfg.decode_steps if steps is None else steps
     xs = synth.make_xz(cfg, seed, dev, seqlen=steps, tensor="decode_xz")  # [B, steps, 2D]
     xs = xs.transpose(0, 1).contiguous()                                   # [steps, B, 2D]
     y = torch.empty(cfg.batch, cfg.d_inner, dtype=cfg.torch_dtype, device=dev)
@@ -189,7 +189,10 @@ def profile_run(args, mm):
     args.steps, args.warmup = max(1, min(args.steps, 3)), 1
     prefill_leg(args, mm)
     torch.cuda.synchronize()
-    print("[profile] done", file=sys.stderr, flush=True)
+    print("[profile] prefill done", file=sys.stderr, flush=True)
+    decode_leg(args, mm, steps=32)
+    torch.cuda.synchronize()
+    print("[profile] decode done", file=sys.stderr, flush=True)
 
 
 def main():
@@ -197,7 +200,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--cpu-tokens", type=int, default=4096)
+    ap.add_argument("--cpu-tokens", type=int, default=8192)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--profile", action="store_true",
