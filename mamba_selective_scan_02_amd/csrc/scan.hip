@@ -304,11 +304,14 @@ __global__ __launch_bounds__(kW * 64) void scan_chunked_kernel(ScanArgs a) {
         for (int j = 0; j + 1 < K - 1; ++j) win[j] = win[j + 1];
         win[K - 2] = x;
         const float u = silu_f(acc);
+        // Past the end only dt is zeroed: the step is then the identity (exp(0 A) = 1, no
+        // input), and those tokens' outputs are never stored. Staged rows there hold copies of
+        // row L-1, so u and z stay finite.
         const float dt = valid ? getd(ts) : 0.f;
         const float z = getz(ts);
         // ZOH replays Bbar u = expm1(dt A)/A * B * u, so it keeps u where Euler keeps dt*u
-        pd_s[wv][ts][c] = make_float2(dt, valid ? (ZOH ? u : dt * u) : 0.f);
-        eg_s[wv][ts][c] = make_float2(valid ? Dp * u : 0.f, valid ? silu_f(z) : 0.f);
+        pd_s[wv][ts][c] = make_float2(dt, ZOH ? u : dt * u);
+        eg_s[wv][ts][c] = make_float2(Dp * u, silu_f(z));
       }
     }
     // the staged x, z, dt rows are consumed once this wave's LDS reads have returned; then the

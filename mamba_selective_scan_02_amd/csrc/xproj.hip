@@ -20,10 +20,10 @@
 //         to ~2^-17 relative.
 //     Each SIMD runs two producer and two consumer waves (<= 128 VGPRs each), so the VALU
 //     work of one role overlaps the MFMAs of the other.
-//     W_x chunks are 4-deep buffered, x rows 3-deep, u 2-deep. W_x and u are stored in MFMA
-//     fragment order (each 16 x 32 operand block is 1 KB with lane i's 16 bytes at 16 i), so
-//     every fragment read is one contiguous, bank-conflict-free 1 KB access; x rows are 64 B
-//     with 16-byte slots XOR-swizzled by row.
+//     W_x chunks are 4-deep buffered, x rows (128 B = two chunks per stage) 2-deep, u
+//     2-deep. W_x and u are stored in MFMA fragment order (each 16 x 32 operand block is 1 KB
+//     with lane i's 16 bytes at 16 i), so every fragment read is one contiguous,
+//     bank-conflict-free 1 KB access; x rows have their 16-byte slots XOR-swizzled by row.
 //   * Epilogue (consumers): lane (token, 4 consecutive outputs per 16-wide block) squares and
 //     sums its dt_low / B / C values, the 4 lanes of a token reduce by lane shuffles, and the
 //     normalised dt_low (as bf16 hi + lo for dt_proj) and B|C (fp32) are written.
@@ -41,10 +41,9 @@ constexpr int kTok = 128;          // tokens per workgroup
 constexpr int kKC = 32;            // channels per chunk (one MFMA k-step)
 constexpr int kXR = 144;           // staged x rows: 3 before the tile + 128, padded to 16-row loads
 
-// physical 16-byte slot of logical slot c (0..3) in 64-byte row r: any 16 consecutive rows
-// read at one logical slot fall in distinct 16-byte bank groups both per 128 B (8 rows) and
-// per 256 B (16 rows)
-__device__ __forceinline__ int swz(int r, int c) { return c ^ ((r >> 1) & 3) ^ ((r >> 3) & 1); }
+// physical 16-byte slot of logical slot c (0..7) in a 128-byte x row r (conflict-free reads of
+// one logical slot of consecutive rows)
+__device__ __forceinline__ int swz8(int r, int c) { return c ^ ((r >> 1) & 7); }
 
 template <int RB, int K>
 __global__ __launch_bounds__(1024) void xproj_fused_kernel(XprojFusedArgs a) {
@@ -53,13 +52,17 @@ __global__ __launch_bounds__(1024) void xproj_fused_kernel(XprojFusedArgs a) {
   constexpr int NX = R + 32;           // outputs: dt_low | B | C
   constexpr int NB = NX / 16;          // 16-row MFMA blocks
   constexpr int LW = NX / 16;          // 1 KB wave-loads per chunk: W_x rows
-  constexpr int LX = kXR / 16;         //                             x rows
   constexpr int PW = (LW + 7) / 8;     // W_x loads per producer wave (padded)
-  constexpr int PX = 2;                // loads per producer wave from the list x rows | taps | bias
-  static_assert(LX + 2 <= 8 * PX, "x-row list");
-  constexpr int PER = PW + PX;         // loads per producer wave per chunk
+  // x rows are staged 128 B wide (two chunks, 64 channels): every row is one whole 128-byte
+  // line (rows are 2 d_inner apart in memory, so half lines would be evicted before the
+  // second half is read). One x stage = kXR rows = kXR / 8 wave-loads, issued with the loads
+  // of every even chunk.
+  constexpr int LX = kXR / 8;
+  constexpr int PXS = (LX + 7) / 8;    // x loads per producer wave per x stage (padded)
+  constexpr int PODD = PW + 1;         // loads per producer wave issued for an odd chunk
+  constexpr int PEVEN = PW + 1 + PXS;  //                                   an even chunk
   __shared__ __attribute__((aligned(16))) bf16_t w_s[4][NB][64 * 8];   // fragment order
-  __shared__ __attribute__((aligned(16))) bf16_t x_s[3][kXR][kKC];
+  __shared__ __attribute__((aligned(16))) bf16_t x_s[2][kXR][2 * kKC];   // x stages
   __shared__ __attribute__((aligned(16))) bf16_t u_s[2][2][kTok / 16][64 * 8];  // [buf][hi, lo]
   __shared__ __attribute__((aligned(16))) bf16_t cw_s[3][kKC * 4];       // conv taps [ch][4]
   __shared__ __attribute__((aligned(16))) bf16_t cb_s[3][kKC];           // conv bias
@@ -75,17 +78,17 @@ __global__ __launch_bounds__(1024) void xproj_fused_kernel(XprojFusedArgs a) {
   const int Lm1 = a.L - 1;
   const int nck = a.D / kKC;
 
-  // Producer wave wv issues W_x loads wv, wv + 8, ... and loads wv, wv + 8 of the list
-  // [x row loads | taps | bias]; indices past a list repeat its load 0, which rewrites the
-  // same bytes, so every producer wave issues PER loads per chunk. Addresses are wave-uniform
-  // bases plus unsigned 32-bit lane offsets.
+  // Producer wave wv issues W_x loads wv, wv + 8, ... of chunk ck, load wv of the list
+  // [taps | bias] (the other waves repeat the taps load, which rewrites the same bytes) and,
+  // for an even chunk, x loads wv, wv + 8, ... of x stage ck / 2; indices past a list repeat
+  // its load 0. So every producer wave issues PEVEN loads for an even chunk and PODD for an
+  // odd one. Addresses are wave-uniform bases plus unsigned 32-bit lane offsets.
   const int xrow0 = max(t0 - 3, 0);                 // x rows are read relative to this token
   const bf16_t *xbase = xzb + (int64_t)xrow0 * row;
   const bf16_t *bsrc = a.conv_b ? a.conv_b : a.conv_w;  // without a bias: the taps, unused
   auto issue = [&](int ck) {
     const int c0 = ck * kKC;
     const int b3 = ck % 3, b4 = ck & 3;
-    const int ps = lane & 3;
 #pragma unroll
     for (int q = 0; q < PW; ++q) {
       int ld = wv + 8 * q;                          // = 16-row block nb of W_x
@@ -95,21 +98,23 @@ __global__ __launch_bounds__(1024) void xproj_fused_kernel(XprojFusedArgs a) {
       dma16_opaque_so(a.w, (uint32_t)(r * a.D + c0 + (lane >> 4) * 8) * 2u,
                       lds_addr(&w_s[b4][ld][0]));
     }
+    if (wv == 1) {
+      if (lane < 4)
+        dma16_opaque_so(bsrc, (uint32_t)(c0 + lane * 8) * 2u, lds_addr(&cb_s[b3][0]));
+    } else {
+      if (lane < 16)
+        dma16_opaque_so(a.conv_w, (uint32_t)(c0 * K + lane * 8) * 2u, lds_addr(&cw_s[b3][0]));
+    }
+    if ((ck & 1) == 0) {
+      const int xb = (ck >> 1) & 1;
 #pragma unroll
-    for (int q = 0; q < PX; ++q) {
-      int li = wv + 8 * q;
-      if (li >= LX + 2) li = 0;
-      if (li < LX) {
-        const int r = li * 16 + (lane >> 2);
+      for (int q = 0; q < PXS; ++q) {
+        int li = wv + 8 * q;
+        if (li >= LX) li = 0;
+        const int r = li * 8 + (lane >> 3), ps = lane & 7;
         const int tt = min(max(t0 - 3 + r, 0), Lm1) - xrow0;   // row r <-> token t0 - 3 + r
-        dma16_opaque_so(xbase, (uint32_t)(tt * (int)row + c0 + swz(r, ps) * 8) * 2u,
-                        lds_addr(&x_s[b3][li * 16][0]));
-      } else if (li == LX) {
-        if (lane < 16)
-          dma16_opaque_so(a.conv_w, (uint32_t)(c0 * K + lane * 8) * 2u, lds_addr(&cw_s[b3][0]));
-      } else {
-        if (lane < 4)
-          dma16_opaque_so(bsrc, (uint32_t)(c0 + lane * 8) * 2u, lds_addr(&cb_s[b3][0]));
+        dma16_opaque_so(xbase, (uint32_t)(tt * (int)row + c0 + swz8(r, ps) * 8) * 2u,
+                        lds_addr(&x_s[xb][li * 8][0]));
       }
     }
   };
@@ -120,13 +125,14 @@ __global__ __launch_bounds__(1024) void xproj_fused_kernel(XprojFusedArgs a) {
   auto produce = [&](int ck) {
     const int c0 = ck * kKC;
     const int b3 = ck % 3;
+    const int xb = (ck >> 1) & 1, xs0 = (ck & 1) * 4;   // x stage buffer, logical slot base
     {
       const int grp = pgrp;
       uint32_t xr[4][4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int r = ptok + j;                  // rows ptok .. ptok+3: tokens t-3 .. t
-        const uint4 v = *(const uint4 *)&x_s[b3][r][swz(r, grp) * 8];
+        const uint4 v = *(const uint4 *)&x_s[xb][r][swz8(r, xs0 + grp) * 8];
         xr[j][0] = v.x; xr[j][1] = v.y; xr[j][2] = v.z; xr[j][3] = v.w;
       }
       if (t0 == 0 && ptok < 3) {
@@ -218,8 +224,12 @@ __global__ __launch_bounds__(1024) void xproj_fused_kernel(XprojFusedArgs a) {
     if (nck > 1) issue(1);
     for (int it = 0; it <= nck; ++it) {
       // chunk it's loads (issued two iterations ago) have landed; chunk it+1's may be in flight
-      if (it + 1 < nck) wait_vmem_le<PER>();
-      else wait_vmem_all();
+      if (it + 1 < nck) {
+        if ((it + 1) & 1) wait_vmem_le<PODD>();
+        else wait_vmem_le<PEVEN>();
+      } else {
+        wait_vmem_all();
+      }
       lds_barrier();
       if (it + 2 < nck) issue(it + 2);
       if (it < nck) produce(it);
@@ -290,7 +300,7 @@ hipError_t launch_rb(const XprojFusedArgs &a, hipStream_t s) {
 }  // namespace
 
 bool xproj_fused_supported(int R, int N, int D, int K) {
-  return N == 16 && K == 4 && D % kKC == 0 && (R == 64 || R == 128 || R == 256);
+  return N == 16 && K == 4 && D % (2 * kKC) == 0 && (R == 64 || R == 128 || R == 256);
 }
 
 hipError_t launch_xproj_fused(const XprojFusedArgs &a, hipStream_t s) {
