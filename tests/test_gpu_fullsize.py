@@ -1,8 +1,9 @@
 """GPU parity at the full workload sizes, in the launch configuration bench.py times.
 
 The GPU runs the whole workload; the fp64 oracle recomputes a seeded sample of outputs one by
-one: y and the final SSM state for a sample of channels over every token, and the final conv
-state (a copy of inputs) bit for bit for every channel. The oracle's convolution / x_proj /
+one: y and the final SSM state for 64 sampled channels over every token (prefill) or for 16
+sampled sequences over every step (decode), and the final conv state (a copy of inputs) bit for
+bit. The oracle's convolution / x_proj /
 RMSNorm pass still covers every channel and token, since B, C and dt_low of each token mix all
 channels; it runs in token blocks on a thread pool (same results as one block).
 
@@ -56,7 +57,7 @@ def test_fullsize_prefill_sampled_channels(name):
     ss = torch.zeros(cfg.batch, cfg.d_inner, cfg.d_state, dtype=torch.float32, device=dev)
     y = mm.prefill(xz, p, conv_state=cs, ssm_state=ss, states_valid=False, eps=cfg.rms_eps)
     torch.cuda.synchronize()
-    sel = _channels(cfg.d_inner, 32, seed)
+    sel = _channels(cfg.d_inner, 64, seed)
     y_sel = to64(y[:, :, torch.as_tensor(sel, device=dev)])
     ss_sel, cs_gpu = to64(ss[:, torch.as_tensor(sel, device=dev)]), to64(cs)
     del y
@@ -85,7 +86,10 @@ def test_fullsize_decode_sampled_sequences(name):
     ss = torch.zeros(cfg.batch, cfg.d_inner, cfg.d_state, dtype=torch.float32, device=dev)
     pre = synth.make_xz(cfg, seed, dev, seqlen=cfg.decode_prefix)
     mm.prefill(pre, p, conv_state=cs, ssm_state=ss, states_valid=False, eps=cfg.rms_eps)
-    seqs = np.array([0, 77, 200, cfg.batch - 1])
+    # 16 seeded sequences, always including the first and the last
+    rng = np.random.default_rng(seed)
+    seqs = np.sort(np.concatenate([[0, cfg.batch - 1],
+                                   rng.choice(np.arange(1, cfg.batch - 1), 14, replace=False)]))
     sq = torch.as_tensor(seqs, device=dev)
     cs_pre, ss_pre = to64(cs[sq]), to64(ss[sq])
     pre_h = _host(pre[sq])
@@ -102,7 +106,7 @@ def test_fullsize_decode_sampled_sequences(name):
     cs_end, ss_end = to64(cs[sq]), to64(ss[sq])
     xs_h = _host(xs[:, sq])
     del xs
-    print("[fullsize] oracle ...", flush=True)
+    print("[fullsize] oracle prefix prefill ...", flush=True)
     p64 = oracle.as_f64_params(p)
     _, csr, ssr = oracle.mixer_prefill(pre_h, p64, eps=cfg.rms_eps, token_block=256,
                                       workers=WORKERS)
@@ -113,6 +117,8 @@ def test_fullsize_decode_sampled_sequences(name):
         yr, csr, ssr = oracle.mixer_decode_step(xs_h[step], p64, csr, ssr, eps=cfg.rms_eps)
         if step in check_steps:
             worst = max(worst, check(ys[step], yr, "bf16", f"{name} y step {step}"))
+        if step % 128 == 127:
+            print(f"[fullsize] oracle decode step {step + 1}/{cfg.decode_steps}", flush=True)
     np.testing.assert_array_equal(cs_end, csr)
     e_s = check(ss_end, ssr, "bf16", f"{name} final ssm_state")
     print(f"[fullsize] {name}: worst y err {worst:.3e}, final state err {e_s:.3e}", flush=True)
