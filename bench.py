@@ -63,6 +63,44 @@ def measured_scan_traffic():
     return rec["read_bytes"] + rec["write_bytes"]
 
 
+MFMA_BF16_PEAK_FLOPS = 2.5e15  # MI355X dense bf16 MFMA, vendor peak
+
+
+def copy_ceiling_gbs() -> float:
+    """Measured device-copy bandwidth (read + write) on this GPU: the practical HBM ceiling
+    against which the bandwidth-bound stages are also reported."""
+    a = torch.empty(1 << 29, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    gbs = 5 * 2 * a.numel() / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del a, b
+    torch.cuda.empty_cache()
+    return gbs
+
+
+def stage_view(ms, nbytes=None, flops=None, copy_gbs=None):
+    """One stage's time with its algorithmic bytes (GB/s, fraction of the HBM peak and of the
+    measured copy ceiling) and, for the projections, algorithmic flops (MFMA utilisation)."""
+    out = {"ms": ms}
+    if nbytes is not None:
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        out.update({"algorithmic_bytes": nbytes, "GBs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS})
+        if copy_gbs:
+            out["copy_frac"] = gbs / copy_gbs
+    if flops is not None:
+        out.update({"algorithmic_flops": flops,
+                    "mfma_util": flops / (ms * 1e-3) / MFMA_BF16_PEAK_FLOPS})
+    return out
+
+
 def prefill_leg(args, mm):
     cfg = synth.CONFIGS[PREFILL_WORKLOAD]
     seed = synth.seed_for(PREFILL_WORKLOAD)
@@ -115,6 +153,23 @@ def prefill_leg(args, mm):
                                   "frac": sbytes / scan_avg_s / 1e9 / HBM_PEAK_GBS}},
         "stages_ms_per_step": {k: v[0] / max(v[1], 1) for k, v in stages.items() if v[1]},
     }
+    # per-stage rooflines: the fused conv + x_proj + RMSNorm reads x and writes dt_low (hi, lo)
+    # and B|C; dt_proj reads dt_low and writes dt (fp16); weights are counted once
+    T, D, R, N = tokens, cfg.d_inner, cfg.dt_rank, cfg.d_state
+    sm = out["stages_ms_per_step"]
+    copy_gbs = args.copy_gbs
+    xproj_bytes = T * D * 2 + T * R * 4 + T * 2 * N * 4 + (R + 2 * N) * D * 2 + D * cfg.d_conv * 2
+    dtproj_bytes = T * R * 4 + T * D * 2 + D * R * 2
+    out["stages"] = {
+        "x_proj": stage_view(sm["x_proj"], xproj_bytes, 2 * T * D * (R + 2 * N), copy_gbs),
+        "dt_proj_softplus": stage_view(sm["dt_proj_softplus"], dtproj_bytes, 2 * T * D * R, copy_gbs),
+        "selective_scan": stage_view(sm["selective_scan"], sbytes, None, copy_gbs),
+    }
+    mixer_min = T * D * (4 + 2)            # xz in, y out: the mixer's own I/O
+    unfused = scan_algorithmic_bytes(cfg) + T * D * 4 + xproj_bytes + dtproj_bytes
+    out["mixer"] = {"min_bytes": mixer_min, "unfused_design_bytes": unfused,
+                    "min_bytes_hbm_frac": mixer_min / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                    "copy_ceiling_GBs": copy_gbs}
     return out, (xz, p, cfg)
 
 
@@ -154,7 +209,12 @@ def decode_leg(args, mm, steps=None):
             "workload": DECODE_WORKLOAD, "batch": B, "d_inner": D, "steps": steps,
             "hbm_frac_of_step": step_bytes / (wall / steps) / 1e9 / HBM_PEAK_GBS,
             "algorithmic_bytes_per_step": step_bytes,
-            "stages_ms_per_step": {k: v[0] / max(v[1], 1) for k, v in stages.items() if v[1]}}
+            "stages_ms_per_step": {k: v[0] / max(v[1], 1) for k, v in stages.items() if v[1]},
+            # the state update (conv, scan step, gate, conv-state shift): state read + write,
+            # conv state read + write, xz, dt (fp16) and y
+            "update_stage": stage_view(stages["selective_scan"][0] / max(stages["selective_scan"][1], 1),
+                                       B * D * (N * 4 * 2 + (K - 1) * 2 * 2 + 2 * 2 + 2 + 2),
+                                       None, args.copy_gbs)}
 
 
 def cpu_baseline(xz, p, cfg, tokens: int):
@@ -217,8 +277,10 @@ def main():
     import mamba_selective_scan_02_amd as mm
     mm.lib()  # fails loudly when the HIP library is missing
     if args.profile:
+        args.copy_gbs = None
         profile_run(args, mm)
         return
+    args.copy_gbs = copy_ceiling_gbs()
     pre, (xz, p, cfg) = prefill_leg(args, mm)
     line = {"metric": "mixer prefill tokens/sec at L=128K (+ decode steps/sec; % HBM peak)",
             "value": pre["value"], "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
@@ -226,7 +288,8 @@ def main():
             "scaling": "weak", "vs_baseline": None, "dtype": "f32",
             "data": "synthetic (seeded; Jamba-Mini-shaped widths, random weights)",
             "config": pre["config"], "roofline": pre["roofline"],
-            "stages_ms_per_step": pre["stages_ms_per_step"]}
+            "stages_ms_per_step": pre["stages_ms_per_step"], "stages": pre["stages"],
+            "mixer": pre["mixer"]}
     if not args.no_decode:
         print("[bench] decode leg", file=sys.stderr, flush=True)
         line["decode"] = decode_leg(args, mm)
