@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define MM_ABI_VERSION 1
+#define MM_ABI_VERSION 2
 
 #if defined(__GNUC__) || defined(__clang__)
 #define MM_API __attribute__((visibility("default")))
@@ -154,7 +154,10 @@ enum {
   MM_STAGE_DTPROJ = 3,     /* dt_proj + bias + softplus */
   MM_STAGE_SCAN = 4,       /* selective scan + D feed-through + SiLU(z) gate + final state */
   MM_STAGE_CONV_STATE = 5, /* conv-state update (only when a conv state is given) */
-  MM_STAGE_COUNT = 6
+  MM_STAGE_LAYER_NORM = 6, /* mamba_layer_prefill: RMSNorm of the layer input */
+  MM_STAGE_IN_PROJ = 7,    /* mamba_layer_prefill: in_proj */
+  MM_STAGE_OUT_PROJ = 8,   /* mamba_layer_prefill: out_proj + residual */
+  MM_STAGE_COUNT = 9
 };
 typedef struct mm_stage_timer mm_stage_timer;
 MM_API mm_stage_timer *mm_stage_timer_create(void);
@@ -171,6 +174,50 @@ MM_API mm_status mamba_mixer_decode_step_timed(const mm_shape *s, const mm_param
                                         void *y, void *conv_state, float *ssm_state,
                                         void *workspace, size_t workspace_bytes, void *stream,
                                         mm_stage_timer *timer);
+
+/*
+ * Mamba layer around the mixer (bf16 I/O only):
+ *     out = x + W_out . mixer(W_in . RMSNorm(x))
+ * Jamba analysis page: "RMSNorm definition and placement" (RMSNorm at the input of every Mamba
+ * module, RMSNorm equation) and "From scalar SSM to vector processing" (the hidden state is
+ * projected to d_inner scalar SSMs whose outputs are projected back). The residual add is the
+ * pre-norm block the architecture description implies.
+ *   norm_w      [d_model] float, RMSNorm gain of the layer input; norm_eps its epsilon
+ *   in_proj_w   [2*d_inner, d_model] bf16; rows 0 .. d_inner-1 give x, the rest z
+ *   out_proj_w  [d_model, d_inner] bf16
+ *   mixer       the mixer parameters, as for mamba_mixer_prefill
+ * Limits (MM_ERR_UNSUPPORTED otherwise): io_dtype MM_BF16, d_model % 128 == 0, and the
+ * mixer's own limits.
+ */
+typedef struct {
+  const float *norm_w;
+  const void *in_proj_w;
+  const void *out_proj_w;
+  float norm_eps;
+  mm_params mixer;
+} mm_layer_params;
+
+/* Bytes of device workspace mamba_layer_prefill needs (0 on a bad shape). */
+MM_API size_t mm_layer_workspace_bytes(const mm_shape *s, int32_t d_model);
+
+/*
+ * Layer prefill over `batch` sequences of `seqlen` tokens.
+ *   x    [batch, seqlen, d_model] bf16 (caller-owned, not modified)
+ *   out  [batch, seqlen, d_model] bf16; must not alias x
+ *   conv_state, ssm_state, states_valid: as for mamba_mixer_prefill (the mixer's states)
+ *   workspace >= mm_layer_workspace_bytes(s, d_model) bytes, 256-byte aligned; it holds the
+ *   normalised input, xz and the mixer output besides the mixer's own workspace.
+ * Asynchronous on `stream`; on a validation error nothing is launched and nothing written.
+ */
+MM_API mm_status mamba_layer_prefill(const mm_shape *s, int32_t d_model, const mm_layer_params *p,
+                                     const void *x, void *out, void *conv_state, float *ssm_state,
+                                     int states_valid, void *workspace, size_t workspace_bytes,
+                                     void *stream);
+MM_API mm_status mamba_layer_prefill_timed(const mm_shape *s, int32_t d_model,
+                                           const mm_layer_params *p, const void *x, void *out,
+                                           void *conv_state, float *ssm_state, int states_valid,
+                                           void *workspace, size_t workspace_bytes, void *stream,
+                                           mm_stage_timer *timer);
 
 MM_API const char *mm_status_string(mm_status st);
 MM_API int mm_abi_version(void);

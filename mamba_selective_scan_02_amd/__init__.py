@@ -23,7 +23,8 @@ MM_F32, MM_BF16 = 0, 1
 MM_FLAG_ZOH_B = 1
 MM_FLAG_SCAN_SEQUENTIAL = 2
 MM_FLAG_SCAN_CHUNKED = 4
-STAGES = ("conv_silu", "x_proj", "rmsnorm", "dt_proj_softplus", "selective_scan", "conv_state")
+STAGES = ("conv_silu", "x_proj", "rmsnorm", "dt_proj_softplus", "selective_scan", "conv_state",
+          "layer_rmsnorm", "in_proj", "out_proj")
 
 
 class MixerError(RuntimeError):
@@ -44,6 +45,12 @@ class Params(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in
                 ("conv_w", "conv_b", "x_proj_w", "dt_proj_w", "dt_proj_b", "A", "Dskip",
                  "dt_norm_w", "B_norm_w", "C_norm_w")]
+
+
+class LayerParams(ctypes.Structure):
+    _fields_ = [("norm_w", ctypes.c_void_p), ("in_proj_w", ctypes.c_void_p),
+                ("out_proj_w", ctypes.c_void_p), ("norm_eps", ctypes.c_float),
+                ("mixer", Params)]
 
 
 _lib = None
@@ -72,6 +79,9 @@ def lib() -> ctypes.CDLL:
             ("mm_stage_name", [I], ctypes.c_char_p),
             ("mm_status_string", [I], ctypes.c_char_p),
             ("mm_abi_version", [], I),
+            ("mm_layer_workspace_bytes", [P(S), I], Z),
+            ("mamba_layer_prefill", [P(S), I, P(LayerParams), V, V, V, V, I, V, Z, V], I),
+            ("mamba_layer_prefill_timed", [P(S), I, P(LayerParams), V, V, V, V, I, V, Z, V, V], I),
         ]:
             fn = getattr(L, name)
             fn.argtypes = args
@@ -216,3 +226,36 @@ def decode_step(xz, params, conv_state, ssm_state, *, y=None, workspace=None, ep
     if st != MM_OK:
         raise MixerError(st, "mamba_mixer_decode_step")
     return y
+
+
+def layer_workspace_bytes(shape: Shape, d_model: int) -> int:
+    return int(lib().mm_layer_workspace_bytes(ctypes.byref(shape), d_model))
+
+
+def layer_prefill(x, params, layer, *, conv_state=None, ssm_state=None, states_valid=False,
+                  out=None, workspace=None, eps=1e-6, norm_eps=1e-6, zoh=False, stream=None,
+                  timer: StageTimer | None = None):
+    """Run mamba_layer_prefill: out = x + W_out . mixer(W_in . RMSNorm(x)). x [B, L, d_model]
+    bf16; params: the mixer's parameters; layer: {"norm_w", "in_proj_w", "out_proj_w"}."""
+    B, L, Dm = x.shape
+    D = params["Dskip"].shape[0]
+    N = params["A"].shape[1]
+    K = params["conv_w"].shape[1]
+    R = params["dt_proj_w"].shape[1]
+    shape = make_shape(B, L, D, N, K, R, x.dtype, eps, MM_FLAG_ZOH_B if zoh else 0)
+    if out is None:
+        out = torch.empty_like(x)
+    if workspace is None:
+        workspace = alloc_workspace(layer_workspace_bytes(shape, Dm), x.device)
+    lp = LayerParams(_ptr(layer["norm_w"]), _ptr(layer["in_proj_w"]), _ptr(layer["out_proj_w"]),
+                     norm_eps, params_struct(params))
+    args = (ctypes.byref(shape), Dm, ctypes.byref(lp), _ptr(x), _ptr(out), _ptr(conv_state),
+            _ptr(ssm_state), 1 if states_valid else 0, _ptr(workspace),
+            workspace.numel() * workspace.element_size(), _stream(stream))
+    if timer is None:
+        st = lib().mamba_layer_prefill(*args)
+    else:
+        st = lib().mamba_layer_prefill_timed(*args, timer.h)
+    if st != MM_OK:
+        raise MixerError(st, "mamba_layer_prefill")
+    return out

@@ -287,9 +287,99 @@ mm_status decode_impl(const mm_shape *s, const mm_params *p, const void *xz, voi
                    (hipStream_t)stream, timer, true);
 }
 
+// Layer workspace: x_norm [T, d_model] bf16 | xz [T, 2D] bf16 | y [T, D] bf16 | mixer workspace
+struct LayerWs {
+  size_t xn, xz, y, mixer, total;
+};
+LayerWs layer_layout(const mm_shape &s, int d_model) {
+  const size_t T = (size_t)s.batch * s.seqlen;
+  LayerWs w;
+  size_t o = 0;
+  w.xn = o; o += up(T * d_model * 2);
+  w.xz = o; o += up(T * 2 * s.d_inner * 2);
+  w.y = o; o += up(T * s.d_inner * 2);
+  w.mixer = o; o += layout(s, false).total;
+  w.total = o;
+  return w;
+}
+
+mm_status check_layer(const mm_shape *s, int d_model, const mm_layer_params *p) {
+  mm_status r = check_shape(s, false);
+  if (r != MM_OK) return r;
+  if (d_model <= 0) return MM_ERR_INVALID_ARG;
+  if (s->io_dtype != MM_BF16 || d_model % 128 != 0) return MM_ERR_UNSUPPORTED;
+  const int T = s->batch * s->seqlen;
+  if (!gemm_nt_supported(T, 2 * s->d_inner, d_model) || !gemm_nt_supported(T, d_model, s->d_inner))
+    return MM_ERR_UNSUPPORTED;
+  if (!p) return MM_ERR_INVALID_ARG;
+  if (!p->norm_w || !p->in_proj_w || !p->out_proj_w || !aligned(p->norm_w) ||
+      !aligned(p->in_proj_w) || !aligned(p->out_proj_w) || !(p->norm_eps > 0.0f))
+    return MM_ERR_INVALID_ARG;
+  return check_params(&p->mixer);
+}
+
+mm_status layer_impl(const mm_shape *s, int d_model, const mm_layer_params *p, const void *x,
+                     void *out, void *conv_state, float *ssm_state, int states_valid,
+                     void *workspace, size_t workspace_bytes, void *stream, mm_stage_timer *timer) {
+  mm_status r = check_layer(s, d_model, p);
+  if (r != MM_OK) return r;
+  if (!x || !out || !aligned(x) || !aligned(out) || x == out) return MM_ERR_INVALID_ARG;
+  if ((conv_state && !aligned(conv_state)) || (ssm_state && !aligned(ssm_state)))
+    return MM_ERR_INVALID_ARG;
+  if (states_valid != 0 && states_valid != 1) return MM_ERR_INVALID_ARG;
+  const LayerWs w = layer_layout(*s, d_model);
+  if (!workspace || ((uintptr_t)workspace & (kAlign - 1)) || workspace_bytes < w.total)
+    return MM_ERR_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  char *ws = (char *)workspace;
+  const int T = s->batch * s->seqlen, D = s->d_inner;
+  uint16_t *xn = (uint16_t *)(ws + w.xn), *xz = (uint16_t *)(ws + w.xz), *y = (uint16_t *)(ws + w.y);
+  {
+    StageScope sc(timer, st, MM_STAGE_LAYER_NORM);
+    MM_TRY(launch_rmsnorm_rows((const uint16_t *)x, p->norm_w, xn, T, d_model, p->norm_eps, st));
+  }
+  {
+    StageScope sc(timer, st, MM_STAGE_IN_PROJ);
+    GemmArgs g{xn, (const uint16_t *)p->in_proj_w, nullptr, xz, T, 2 * D, d_model, 2 * D, 0};
+    MM_TRY(launch_gemm_nt(g, st));
+  }
+  r = run_mixer(s, &p->mixer, xz, y, conv_state, ssm_state, states_valid, ws + w.mixer,
+                workspace_bytes - w.mixer, st, timer, false);
+  if (r != MM_OK) return r;
+  {
+    StageScope sc(timer, st, MM_STAGE_OUT_PROJ);
+    GemmArgs g{y, (const uint16_t *)p->out_proj_w, (const uint16_t *)x, (uint16_t *)out, T,
+               d_model, D, d_model, d_model};
+    MM_TRY(launch_gemm_nt(g, st));
+  }
+  return MM_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t mm_layer_workspace_bytes(const mm_shape *s, int32_t d_model) {
+  if (!s || check_shape(s, false) != MM_OK || d_model <= 0) return 0;
+  return layer_layout(*s, d_model).total;
+}
+
+mm_status mamba_layer_prefill(const mm_shape *s, int32_t d_model, const mm_layer_params *p,
+                              const void *x, void *out, void *conv_state, float *ssm_state,
+                              int states_valid, void *workspace, size_t workspace_bytes,
+                              void *stream) {
+  return layer_impl(s, d_model, p, x, out, conv_state, ssm_state, states_valid, workspace,
+                    workspace_bytes, stream, nullptr);
+}
+
+mm_status mamba_layer_prefill_timed(const mm_shape *s, int32_t d_model, const mm_layer_params *p,
+                                    const void *x, void *out, void *conv_state, float *ssm_state,
+                                    int states_valid, void *workspace, size_t workspace_bytes,
+                                    void *stream, mm_stage_timer *timer) {
+  return layer_impl(s, d_model, p, x, out, conv_state, ssm_state, states_valid, workspace,
+                    workspace_bytes, stream, timer);
+}
+
 
 size_t mm_prefill_workspace_bytes(const mm_shape *s) {
   if (check_shape(s, false) != MM_OK) return 0;
@@ -367,7 +457,8 @@ mm_status mm_stage_timer_read(mm_stage_timer *t, double *ms_sum, int64_t *launch
 
 const char *mm_stage_name(int stage) {
   static const char *names[MM_STAGE_COUNT] = {"conv_silu", "x_proj", "rmsnorm", "dt_proj_softplus",
-                                              "selective_scan", "conv_state"};
+                                              "selective_scan", "conv_state", "layer_rmsnorm",
+                                              "in_proj", "out_proj"};
   return (stage >= 0 && stage < MM_STAGE_COUNT) ? names[stage] : "unknown";
 }
 

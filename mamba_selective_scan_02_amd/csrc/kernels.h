@@ -102,6 +102,20 @@ hipError_t launch_decode_xproj(const DecodeXprojArgs &a, hipStream_t s);
 hipError_t launch_decode_norm(const DecodeNormArgs &a, hipStream_t s);
 hipError_t launch_decode_update(const DecodeUpdateArgs &a, bool zoh, hipStream_t s);
 
+// C[M, N] = A[M, K] . B[N, K]^T (+ R), bf16, fp32 accumulate (row-major, lda = ldb = K)
+struct GemmArgs {
+  const uint16_t *A, *B;
+  const uint16_t *R;           // residual [M, ldr] added to C, or null
+  uint16_t *C;
+  int M, N, K, ldc, ldr;
+};
+bool gemm_nt_supported(int M, int N, int K);
+// tile: 256 or 128 (the workgroup tile); 0 picks 256 when N % 256 == 0 and the 256 x 256 tiles
+// number at least 256, else 128.
+hipError_t launch_gemm_nt(const GemmArgs &g, hipStream_t s, int tile = 0);
+hipError_t launch_rmsnorm_rows(const uint16_t *x, const float *gamma, uint16_t *y, int T, int Dm,
+                               float eps, hipStream_t s);
+
 struct ScanArgs {
   const void *xz;       // [B, L, 2D]; x = first D columns (conv input), z = last D (gate)
   const void *conv_w;   // [D, K] io dtype

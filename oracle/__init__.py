@@ -25,7 +25,10 @@ SSM; an unrolled O(L^2) cumulative-dt formula evaluated in mpmath for the scan;
 scipy ODE integration of the continuous SSM for the ZOH input matrix; the closed
 form h_L = exp(L*dt*A)*h_0 for zero input; chunked == sequential and
 prefill == repeated decode invariants; a tiny whole-mixer fixture computed in
-mpmath by a separate script (tests/golden/).
+mpmath by a separate script (tests/golden/). The layer around the mixer (layer_f64):
+residual identity with W_out = 0, linearity in W_out, and an mpmath evaluation of a tiny
+layer whose mixer reduces to its D feed-through; its bf16 activation rounding (round_bf16)
+against hand-worked ties and torch's float32 -> bfloat16 conversion.
 """
 from .mixer_f64 import (  # noqa: F401
     silu,
@@ -40,3 +43,4 @@ from .mixer_f64 import (  # noqa: F401
     mixer_decode_step,
     as_f64_params,
 )
+from .layer_f64 import layer_prefill, round_bf16  # noqa: F401,E402

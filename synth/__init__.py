@@ -49,6 +49,7 @@ class MixerConfig:
     rms_eps: float = 1e-6
     decode_steps: int = 0           # > 0 marks a decode workload
     decode_prefix: int = 0          # length of the prefill that seeds decode states
+    d_model: int = 4096             # hidden size around the mixer (layer entry point only)
 
     @property
     def torch_dtype(self) -> torch.dtype:
@@ -75,7 +76,8 @@ CONFIGS = {
 
 # Tensor ids keep the streams of different tensors apart for one seed.
 _TID = {"xz": 1, "conv_w": 2, "conv_b": 3, "x_proj_w": 4, "dt_proj_w": 5, "dt0": 6,
-        "gamma": 7, "conv_state": 8, "ssm_state": 9, "decode_xz": 10, "misc": 11}
+        "gamma": 7, "conv_state": 8, "ssm_state": 9, "decode_xz": 10, "misc": 11,
+        "layer_x": 12, "in_proj_w": 13, "out_proj_w": 14, "norm_w": 15}
 
 
 def generator(seed: int, tensor: str, device, step: int = 0) -> torch.Generator:
@@ -161,3 +163,33 @@ def make_states(cfg: MixerConfig, seed: int, device="cpu", *, batch=None,
 def seed_for(cfg_name: str) -> int:
     """Fixed seed per workload: 1000 + its position in CONFIGS."""
     return 1000 + list(CONFIGS).index(cfg_name)
+
+
+def make_layer(cfg: MixerConfig, seed: int, device="cpu", *, gamma_random: bool = False) -> dict:
+    """Weights of the layer around the mixer: in_proj [2 d_inner, d_model] ~ N(0, 1/d_model) and
+    out_proj [d_model, d_inner] ~ N(0, 1/d_inner) in the I/O dtype; the input RMSNorm gain
+    (fp32) is 1, or U(0.5, 1.5)."""
+    D, Dm, dt = cfg.d_inner, cfg.d_model, cfg.torch_dtype
+    lay = {"in_proj_w": _normal((2 * D, Dm), 1.0 / math.sqrt(Dm),
+                                generator(seed, "in_proj_w", device), device, dt),
+           "out_proj_w": _normal((Dm, D), 1.0 / math.sqrt(D),
+                                 generator(seed, "out_proj_w", device), device, dt)}
+    lay["norm_w"] = (_uniform((Dm,), 0.5, 1.5, generator(seed, "norm_w", device), device)
+                     if gamma_random else torch.ones(Dm, dtype=torch.float32, device=device))
+    return lay
+
+
+def make_layer_x(cfg: MixerConfig, seed: int, device="cpu", *, batch=None, seqlen=None,
+                 chunk_tokens: int = 1 << 14) -> torch.Tensor:
+    """Layer input x ~ N(0, 1), [B, L, d_model] in the I/O dtype, drawn in token chunks."""
+    B = cfg.batch if batch is None else batch
+    L = cfg.seqlen if seqlen is None else seqlen
+    out = torch.empty((B, L, cfg.d_model), dtype=cfg.torch_dtype, device=device)
+    g = generator(seed, "layer_x", device)
+    for b in range(B):
+        for t0 in range(0, L, chunk_tokens):
+            t1 = min(L, t0 + chunk_tokens)
+            tmp = torch.empty((t1 - t0, cfg.d_model), dtype=torch.float32, device=device)
+            tmp.normal_(0.0, 1.0, generator=g)
+            out[b, t0:t1] = tmp.to(cfg.torch_dtype)
+    return out

@@ -32,7 +32,7 @@ def test_library_exports_every_declared_symbol():
     L = mm.lib()
     for name in _declared_functions():
         assert hasattr(L, name), name
-    assert L.mm_abi_version() == 1
+    assert L.mm_abi_version() == 2
 
 
 def _shape(**kw):
