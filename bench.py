@@ -7,7 +7,9 @@ d_inner=8192, d_state=16, d_conv=4, dt_rank=256, bf16 I/O, fp32 state): conv1d+S
 x_proj, RMSNorm, dt_proj+softplus, selective scan with D feed-through and SiLU(z) gate,
 final conv/SSM states. Inputs are synthetic, seeded, resident in HBM before timing.
 The decode leg times 512 batched decode steps (B=256, d_inner=8192) after a 1024-token
-prefill seeds the states. Prints one JSON line.
+prefill seeds the states. The layer leg times mamba_layer_prefill (pre-RMSNorm, in_proj
+4096 -> 16384, the mixer, out_proj 8192 -> 4096 with the residual) on the same 128K tokens.
+Prints one JSON line.
 """
 from __future__ import annotations
 
@@ -217,6 +219,48 @@ def decode_leg(args, mm, steps=None):
                                        None, args.copy_gbs)}
 
 
+def layer_leg(args, mm, steps=None):
+    """mamba_layer_prefill over the 128K workload at d_model 4096 (x ~ N(0, 1), random weights)."""
+    cfg = synth.CONFIGS[PREFILL_WORKLOAD]
+    seed = synth.seed_for(PREFILL_WORKLOAD)
+    dev = "cuda"
+    p = synth.make_params(cfg, seed, dev)
+    lay = synth.make_layer(cfg, seed, dev)
+    x = synth.make_layer_x(cfg, seed, dev)
+    out = torch.empty_like(x)
+    shape = mm.make_shape(cfg.batch, cfg.seqlen, cfg.d_inner, cfg.d_state, cfg.d_conv,
+                          cfg.dt_rank, x.dtype, cfg.rms_eps, 0)
+    ws = mm.alloc_workspace(mm.layer_workspace_bytes(shape, cfg.d_model), dev)
+    timer = mm.StageTimer()
+    steps = args.steps if steps is None else steps
+
+    def step(t=None):
+        mm.layer_prefill(x, p, lay, out=out, workspace=ws, eps=cfg.rms_eps, timer=t)
+
+    for _ in range(max(1, args.warmup)):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step(timer)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    st = {k: v[0] / max(v[1], 1) for k, v in timer.read().items() if v[1]}
+    T, D, Dm = cfg.batch * cfg.seqlen, cfg.d_inner, cfg.d_model
+    ms = wall * 1e3 / steps
+    return {"metric": "Mamba layer prefill tokens/sec at L=128K", "value": T / (ms * 1e-3),
+            "unit": "tokens/s", "ms_per_step": ms, "steps": steps,
+            "config": {"workload": PREFILL_WORKLOAD, "d_model": Dm, "d_inner": D,
+                       "dt_rank": cfg.dt_rank, "d_state": cfg.d_state, "io_dtype": "bf16"},
+            "stages_ms_per_step": st,
+            "stages": {
+                # x read, xn written, gain once
+                "layer_rmsnorm": stage_view(st["layer_rmsnorm"], T * Dm * 2 * 2 + Dm * 4, None,
+                                            args.copy_gbs),
+                "in_proj": stage_view(st["in_proj"], None, 2 * T * Dm * 2 * D),
+                "out_proj": stage_view(st["out_proj"], None, 2 * T * D * Dm)}}
+
+
 def cpu_baseline(xz, p, cfg, tokens: int):
     """The fp64 oracle, as it stands, on the first `tokens` tokens of the same workload."""
     import numpy as np
@@ -253,6 +297,10 @@ def profile_run(args, mm):
     decode_leg(args, mm, steps=32)
     torch.cuda.synchronize()
     print("[profile] decode done", file=sys.stderr, flush=True)
+    if not args.no_layer:
+        layer_leg(args, mm, steps=2)
+        torch.cuda.synchronize()
+        print("[profile] layer done", file=sys.stderr, flush=True)
 
 
 def main():
@@ -263,6 +311,7 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=8192)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-layer", action="store_true")
     ap.add_argument("--profile", action="store_true",
                     help="short run for rocprofv3: a few prefill and decode steps plus one plain "
                          "1 GiB device copy (the reference kernel for counter calibration)")
@@ -293,6 +342,9 @@ def main():
     if not args.no_decode:
         print("[bench] decode leg", file=sys.stderr, flush=True)
         line["decode"] = decode_leg(args, mm)
+    if not args.no_layer:
+        print("[bench] layer leg", file=sys.stderr, flush=True)
+        line["layer"] = layer_leg(args, mm)
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(xz, p, cfg, args.cpu_tokens)
