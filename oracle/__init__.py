@@ -28,7 +28,10 @@ prefill == repeated decode invariants; a tiny whole-mixer fixture computed in
 mpmath by a separate script (tests/golden/). The layer around the mixer (layer_f64):
 residual identity with W_out = 0, linearity in W_out, and an mpmath evaluation of a tiny
 layer whose mixer reduces to its D feed-through; its bf16 activation rounding (round_bf16)
-against hand-worked ties and torch's float32 -> bfloat16 conversion.
+against hand-worked ties and torch's float32 -> bfloat16 conversion. The gradients
+(mixer_bwd_f64, the backward of the prefill): central finite differences of mixer_prefill for
+every parameter, xz and both carried states (first-order and ZOH Bbar), chunk-length
+independence of its state checkpoints, linearity in dy.
 """
 from .mixer_f64 import (  # noqa: F401
     silu,
@@ -44,3 +47,4 @@ from .mixer_f64 import (  # noqa: F401
     as_f64_params,
 )
 from .layer_f64 import layer_prefill, round_bf16  # noqa: F401,E402
+from .mixer_bwd_f64 import mixer_prefill_backward  # noqa: F401,E402
