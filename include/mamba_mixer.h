@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define MM_ABI_VERSION 2
+#define MM_ABI_VERSION 3
 
 #if defined(__GNUC__) || defined(__clang__)
 #define MM_API __attribute__((visibility("default")))
@@ -157,7 +157,11 @@ enum {
   MM_STAGE_LAYER_NORM = 6, /* mamba_layer_prefill: RMSNorm of the layer input */
   MM_STAGE_IN_PROJ = 7,    /* mamba_layer_prefill: in_proj */
   MM_STAGE_OUT_PROJ = 8,   /* mamba_layer_prefill: out_proj + residual */
-  MM_STAGE_COUNT = 9
+  MM_STAGE_BWD_RECOMPUTE = 9,  /* backward: u, x_proj, the norms, dt, SiLU(z) dy recomputed */
+  MM_STAGE_BWD_SCAN = 10,      /* backward: range transfers, carries, the reverse scan, dB / dC */
+  MM_STAGE_BWD_PROJ = 11,      /* backward: dt_proj, RMSNorm and x_proj gradients */
+  MM_STAGE_BWD_CONV = 12,      /* backward: conv1d + SiLU gradients */
+  MM_STAGE_COUNT = 13
 };
 typedef struct mm_stage_timer mm_stage_timer;
 MM_API mm_stage_timer *mm_stage_timer_create(void);
@@ -218,6 +222,59 @@ MM_API mm_status mamba_layer_prefill_timed(const mm_shape *s, int32_t d_model,
                                            void *conv_state, float *ssm_state, int states_valid,
                                            void *workspace, size_t workspace_bytes, void *stream,
                                            mm_stage_timer *timer);
+
+/*
+ * Backward of the prefill, for training through the parallel scan (Jamba analysis page,
+ * "Parallel training via the parallel scan"; the forward is the one of mamba_mixer_prefill,
+ * above, with the same shape, flags and parameters). Given the gradient dy of a loss with
+ * respect to y, writes the gradients of that loss with respect to xz, every parameter and the
+ * two carried states, i.e. the gradients of sum(dy * y):
+ *   h_t = Abar_t h_{t-1} + Bbar_t u_t runs backward as dh_t = C_t dys_t + Abar_{t+1} dh_{t+1}
+ *   (dys = dy * SiLU(z)); the states h are recomputed from the inputs, never stored by the
+ *   forward. Arithmetic is fp32 throughout (bf16 I/O only rounds dxz on output).
+ *   xz, conv_state, ssm_state, states_valid: the forward's inputs (states as they were BEFORE
+ *               the forward call; NULL / states_valid 0 = zeros)
+ *   dy          [batch, seqlen, d_inner] io_dtype
+ *   g           output pointers (all caller-owned device memory, overwritten, not accumulated):
+ *               dxz required; the parameter gradients required, except conv_b (required iff
+ *               p->conv_b is given); conv_state / ssm_state gradients optional (NULL = skip)
+ *   workspace   >= mm_backward_workspace_bytes(s) bytes, 256-byte aligned
+ * Limits: those of mamba_mixer_prefill (d_state == 16, 2 <= d_conv <= 4, d_inner % 64 == 0)
+ * with 1 <= dt_rank <= 1024 for either io_dtype. The result is deterministic (fixed-order
+ * reductions, no atomics).
+ */
+typedef struct {
+  void *dxz;           /* [batch, seqlen, 2*d_inner] io_dtype: d/dx, then d/dz */
+  float *conv_w;       /* [d_inner, d_conv] */
+  float *conv_b;       /* [d_inner] (NULL when the forward has no conv bias) */
+  float *x_proj_w;     /* [dt_rank + 2*d_state, d_inner] */
+  float *dt_proj_w;    /* [d_inner, dt_rank] */
+  float *dt_proj_b;    /* [d_inner] */
+  float *A;            /* [d_inner, d_state] */
+  float *Dskip;        /* [d_inner] */
+  float *dt_norm_w;    /* [dt_rank] */
+  float *B_norm_w;     /* [d_state] */
+  float *C_norm_w;     /* [d_state] */
+  float *conv_state;   /* [batch, d_inner, d_conv-1] fp32, or NULL */
+  float *ssm_state;    /* [batch, d_inner, d_state], or NULL */
+} mm_grads;
+
+/* Bytes of device workspace mamba_mixer_prefill_backward needs (0 on a bad shape). */
+MM_API size_t mm_backward_workspace_bytes(const mm_shape *s);
+
+MM_API mm_status mamba_mixer_prefill_backward(const mm_shape *s, const mm_params *p,
+                                              const void *xz, const void *dy,
+                                              const void *conv_state, const float *ssm_state,
+                                              int states_valid, const mm_grads *g,
+                                              void *workspace, size_t workspace_bytes,
+                                              void *stream);
+MM_API mm_status mamba_mixer_prefill_backward_timed(const mm_shape *s, const mm_params *p,
+                                                    const void *xz, const void *dy,
+                                                    const void *conv_state,
+                                                    const float *ssm_state, int states_valid,
+                                                    const mm_grads *g, void *workspace,
+                                                    size_t workspace_bytes, void *stream,
+                                                    mm_stage_timer *timer);
 
 MM_API const char *mm_status_string(mm_status st);
 MM_API int mm_abi_version(void);

@@ -24,7 +24,10 @@ MM_FLAG_ZOH_B = 1
 MM_FLAG_SCAN_SEQUENTIAL = 2
 MM_FLAG_SCAN_CHUNKED = 4
 STAGES = ("conv_silu", "x_proj", "rmsnorm", "dt_proj_softplus", "selective_scan", "conv_state",
-          "layer_rmsnorm", "in_proj", "out_proj")
+          "layer_rmsnorm", "in_proj", "out_proj", "bwd_recompute", "bwd_scan", "bwd_proj",
+          "bwd_conv")
+GRAD_NAMES = ("dxz", "conv_w", "conv_b", "x_proj_w", "dt_proj_w", "dt_proj_b", "A", "Dskip",
+              "dt_norm_w", "B_norm_w", "C_norm_w", "conv_state", "ssm_state")
 
 
 class MixerError(RuntimeError):
@@ -51,6 +54,10 @@ class LayerParams(ctypes.Structure):
     _fields_ = [("norm_w", ctypes.c_void_p), ("in_proj_w", ctypes.c_void_p),
                 ("out_proj_w", ctypes.c_void_p), ("norm_eps", ctypes.c_float),
                 ("mixer", Params)]
+
+
+class Grads(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in GRAD_NAMES]
 
 
 _lib = None
@@ -82,6 +89,10 @@ def lib() -> ctypes.CDLL:
             ("mm_layer_workspace_bytes", [P(S), I], Z),
             ("mamba_layer_prefill", [P(S), I, P(LayerParams), V, V, V, V, I, V, Z, V], I),
             ("mamba_layer_prefill_timed", [P(S), I, P(LayerParams), V, V, V, V, I, V, Z, V, V], I),
+            ("mm_backward_workspace_bytes", [P(S)], Z),
+            ("mamba_mixer_prefill_backward", [P(S), P(Params), V, V, V, V, I, P(Grads), V, Z, V], I),
+            ("mamba_mixer_prefill_backward_timed",
+             [P(S), P(Params), V, V, V, V, I, P(Grads), V, Z, V, V], I),
         ]:
             fn = getattr(L, name)
             fn.argtypes = args
@@ -259,3 +270,46 @@ def layer_prefill(x, params, layer, *, conv_state=None, ssm_state=None, states_v
     if st != MM_OK:
         raise MixerError(st, "mamba_layer_prefill")
     return out
+
+
+def backward_workspace_bytes(shape: Shape) -> int:
+    n = lib().mm_backward_workspace_bytes(ctypes.byref(shape))
+    if n == 0:
+        raise MixerError(MM_ERR_UNSUPPORTED, "mm_backward_workspace_bytes")
+    return n
+
+
+def prefill_backward(xz, params, dy, *, conv_state=None, ssm_state=None, states_valid=False,
+                     grads: dict | None = None, state_grads=True, workspace=None, eps=1e-6,
+                     zoh=False, stream=None, timer: StageTimer | None = None) -> dict:
+    """Run mamba_mixer_prefill_backward: gradients of sum(dy * y) for y = prefill(xz, params,
+    conv_state, ssm_state) (states as they were before the forward). Returns a dict with the
+    keys of GRAD_NAMES (dxz in the I/O dtype, the rest float32; conv_b None without a conv
+    bias; the state gradients None when state_grads is False)."""
+    shape = shape_of(xz, params, eps=eps, zoh=zoh)
+    B, L, D2 = xz.shape
+    D, K, R = D2 // 2, params["conv_w"].shape[1], params["dt_proj_w"].shape[1]
+    N = params["A"].shape[1]
+    f32 = dict(dtype=torch.float32, device=xz.device)
+    if grads is None:
+        grads = {"dxz": torch.empty_like(xz), "conv_w": torch.empty(D, K, **f32),
+                 "conv_b": (torch.empty(D, **f32) if params.get("conv_b") is not None else None),
+                 "x_proj_w": torch.empty(R + 2 * N, D, **f32), "dt_proj_w": torch.empty(D, R, **f32),
+                 "dt_proj_b": torch.empty(D, **f32), "A": torch.empty(D, N, **f32),
+                 "Dskip": torch.empty(D, **f32), "dt_norm_w": torch.empty(R, **f32),
+                 "B_norm_w": torch.empty(N, **f32), "C_norm_w": torch.empty(N, **f32),
+                 "conv_state": torch.empty(B, D, K - 1, **f32) if state_grads else None,
+                 "ssm_state": torch.empty(B, D, N, **f32) if state_grads else None}
+    if workspace is None:
+        workspace = alloc_workspace(backward_workspace_bytes(shape), xz.device)
+    g = Grads(*[_ptr(grads.get(n)) for n in GRAD_NAMES])
+    args = (ctypes.byref(shape), ctypes.byref(params_struct(params)), _ptr(xz), _ptr(dy),
+            _ptr(conv_state), _ptr(ssm_state), 1 if states_valid else 0, ctypes.byref(g),
+            _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+    if timer is None:
+        st = lib().mamba_mixer_prefill_backward(*args)
+    else:
+        st = lib().mamba_mixer_prefill_backward_timed(*args, timer.h)
+    if st != MM_OK:
+        raise MixerError(st, "mamba_mixer_prefill_backward")
+    return grads

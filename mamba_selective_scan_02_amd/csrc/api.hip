@@ -355,6 +355,145 @@ mm_status layer_impl(const mm_shape *s, int d_model, const mm_layer_params *p, c
   return MM_OK;
 }
 
+// Backward workspace (fp32 arrays; T = batch * seqlen, W = dt_rank + 32, nr = ranges).
+struct BwWs {
+  size_t wx32, wdt32, u, xd, dtn, bc, dt, sig, dys, du, rP, rS, rR, dA_part, dD_part, bc_part,
+      dbc, ddtn, dxd, gc, cs_part, gsum, conv_part, total;
+};
+BwWs bw_layout(const mm_shape &s) {
+  const size_t T = (size_t)s.batch * s.seqlen, D = s.d_inner, R = s.dt_rank, W = R + 32;
+  const size_t nr = (size_t)bw_ranges(s.seqlen), SR = (size_t)s.batch * nr * D * 16;
+  const size_t nbT = (size_t)bw_colsum_blocks((int64_t)T);
+  const size_t nbR = (size_t)bw_colsum_blocks((int64_t)s.batch * nr);
+  const size_t nbc = ((size_t)s.seqlen + 1023) / 1024;
+  BwWs w;
+  size_t o = 0;
+  auto take = [&](size_t &f, size_t floats) { f = o; o += up(floats * 4); };
+  take(w.wx32, W * D);
+  take(w.wdt32, D * R);
+  take(w.u, T * D);
+  take(w.xd, T * W);
+  take(w.dtn, T * R);
+  take(w.bc, T * 32);
+  take(w.dt, T * D);
+  take(w.sig, T * D);
+  take(w.dys, T * D);
+  take(w.du, T * D);
+  take(w.rP, SR);
+  take(w.rS, SR);
+  take(w.rR, SR);
+  take(w.dA_part, SR);
+  take(w.dD_part, (size_t)s.batch * nr * D);
+  take(w.bc_part, T * (D / 64) * 32);
+  take(w.dbc, T * 32);
+  take(w.ddtn, T * R);
+  take(w.dxd, T * W);
+  take(w.gc, T * W);
+  take(w.cs_part, std::max(nbT * std::max(D, W), nbR * D * 16));
+  take(w.gsum, W);
+  take(w.conv_part, (size_t)s.batch * nbc * D * 5);
+  w.total = o;
+  return w;
+}
+
+mm_status check_backward(const mm_shape *s, const mm_params *p, const void *xz, const void *dy,
+                         const void *conv_state, const float *ssm_state, int states_valid,
+                         const mm_grads *g) {
+  mm_status r = check_shape(s, false);
+  if (r != MM_OK) return r;
+  if (s->dt_rank > 1024) return MM_ERR_UNSUPPORTED;
+  r = check_params(p);
+  if (r != MM_OK) return r;
+  if (!xz || !dy || !g || !aligned(xz) || !aligned(dy)) return MM_ERR_INVALID_ARG;
+  if (states_valid != 0 && states_valid != 1) return MM_ERR_INVALID_ARG;
+  if ((conv_state && !aligned(conv_state)) || (ssm_state && !aligned(ssm_state)))
+    return MM_ERR_INVALID_ARG;
+  const void *req[] = {g->dxz, g->conv_w, g->x_proj_w, g->dt_proj_w, g->dt_proj_b, g->A,
+                       g->Dskip, g->dt_norm_w, g->B_norm_w, g->C_norm_w};
+  for (const void *q : req)
+    if (!q || !aligned(q)) return MM_ERR_INVALID_ARG;
+  if ((p->conv_b != nullptr) != (g->conv_b != nullptr)) return MM_ERR_INVALID_ARG;
+  if (g->conv_b && !aligned(g->conv_b)) return MM_ERR_INVALID_ARG;
+  if ((g->conv_state && !aligned(g->conv_state)) || (g->ssm_state && !aligned(g->ssm_state)))
+    return MM_ERR_INVALID_ARG;
+  if (g->dxz == xz || g->dxz == dy) return MM_ERR_INVALID_ARG;
+  return MM_OK;
+}
+
+mm_status backward_impl(const mm_shape *s, const mm_params *p, const void *xz, const void *dy,
+                        const void *conv_state, const float *ssm_state, int states_valid,
+                        const mm_grads *g, void *workspace, size_t workspace_bytes, void *stream,
+                        mm_stage_timer *timer) {
+  mm_status r = check_backward(s, p, xz, dy, conv_state, ssm_state, states_valid, g);
+  if (r != MM_OK) return r;
+  const BwWs w = bw_layout(*s);
+  if (!workspace || ((uintptr_t)workspace & (kAlign - 1)) || workspace_bytes < w.total)
+    return MM_ERR_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  char *ws = (char *)workspace;
+  auto F = [&](size_t off) { return (float *)(ws + off); };
+  const int B = s->batch, L = s->seqlen, D = s->d_inner, R = s->dt_rank, W = R + 32;
+  const int64_t T = (int64_t)B * L;
+  const bool bf = s->io_dtype == MM_BF16;
+
+  BwArgs a{};
+  a.xz = xz; a.dy = dy; a.conv_w = p->conv_w; a.conv_b = p->conv_b;
+  a.conv_state = conv_state; a.cs_valid = states_valid && conv_state;
+  a.ssm_state = ssm_state; a.ss_valid = states_valid && ssm_state;
+  a.x_proj_w = p->x_proj_w; a.dt_proj_w = p->dt_proj_w;
+  a.dt_b = p->dt_proj_b; a.A = p->A; a.Dskip = p->Dskip;
+  a.g_dt = p->dt_norm_w; a.g_B = p->B_norm_w; a.g_C = p->C_norm_w;
+  a.eps = s->rms_eps; a.zoh = (s->flags & MM_FLAG_ZOH_B) ? 1 : 0;
+  a.B = B; a.L = L; a.D = D; a.K = s->d_conv; a.R = R; a.nr = bw_ranges(L); a.T = T;
+  a.wx32 = F(w.wx32); a.wdt32 = F(w.wdt32); a.u = F(w.u); a.xd = F(w.xd); a.dtn = F(w.dtn);
+  a.bc = F(w.bc); a.dt = F(w.dt); a.sig = F(w.sig); a.dys = F(w.dys); a.du = F(w.du);
+  a.rP = F(w.rP); a.rS = F(w.rS); a.rR = F(w.rR); a.dA_part = F(w.dA_part);
+  a.dD_part = F(w.dD_part); a.bc_part = F(w.bc_part); a.dbc = F(w.dbc); a.ddtn = F(w.ddtn);
+  a.dxd = F(w.dxd); a.gc = F(w.gc); a.conv_part = F(w.conv_part);
+  a.dxz = g->dxz; a.d_conv_w = g->conv_w; a.d_conv_b = g->conv_b;
+  a.d_ssm_state = g->ssm_state; a.d_conv_state = g->conv_state;
+  const float *wx = bf ? a.wx32 : (const float *)p->x_proj_w;
+  const float *wdt = bf ? a.wdt32 : (const float *)p->dt_proj_w;
+  float *cs = F(w.cs_part);
+
+  {
+    StageScope sc(timer, st, MM_STAGE_BWD_RECOMPUTE);
+    if (bf) MM_TRY(launch_backward_stage(s->io_dtype, a, 6, st));
+    MM_TRY(launch_backward_stage(s->io_dtype, a, 0, st));                    // u
+    MM_TRY(launch_gemm_f32({a.u, wx, a.xd, (int)T, W, D, D, 1, 1, D, W, 0}, st));   // xdbl
+    MM_TRY(launch_norm(MM_F32, a.xd, a.dtn, nullptr, a.bc, a.g_dt, a.g_B, a.g_C, (int)T, R, 16,
+                       a.eps, st));
+    MM_TRY(launch_gemm_f32({a.dtn, wdt, a.dt, (int)T, D, R, R, 1, 1, R, D, 0}, st));  // W_dt dt_low
+    MM_TRY(launch_backward_stage(s->io_dtype, a, 1, st));                    // dt, sigmoid, dys
+  }
+  {
+    StageScope sc(timer, st, MM_STAGE_BWD_SCAN);
+    MM_TRY(launch_backward_stage(s->io_dtype, a, 2, st));
+    MM_TRY(launch_colsum(a.dA_part, (int64_t)B * a.nr, (int64_t)D * 16, cs, g->A, st));
+    MM_TRY(launch_colsum(a.dD_part, (int64_t)B * a.nr, D, cs, g->Dskip, st));
+  }
+  {
+    StageScope sc(timer, st, MM_STAGE_BWD_PROJ);
+    float *dp = a.sig;   // d / d (dt_proj pre-activation), [T, D]
+    MM_TRY(launch_colsum(dp, T, D, cs, g->dt_proj_b, st));
+    MM_TRY(launch_gemm_f32({dp, a.dtn, g->dt_proj_w, D, R, (int)T, 1, D, R, 1, R, 0}, st));
+    MM_TRY(launch_gemm_f32({dp, wdt, a.ddtn, (int)T, R, D, D, 1, R, 1, R, 0}, st));
+    MM_TRY(launch_backward_stage(s->io_dtype, a, 3, st));                    // RMSNorm backward
+    MM_TRY(launch_colsum(a.gc, T, W, cs, F(w.gsum), st));
+    MM_TRY(hipMemcpyAsync(g->dt_norm_w, F(w.gsum), (size_t)R * 4, hipMemcpyDeviceToDevice, st));
+    MM_TRY(hipMemcpyAsync(g->B_norm_w, F(w.gsum) + R, 64, hipMemcpyDeviceToDevice, st));
+    MM_TRY(hipMemcpyAsync(g->C_norm_w, F(w.gsum) + R + 16, 64, hipMemcpyDeviceToDevice, st));
+    MM_TRY(launch_gemm_f32({a.dxd, a.u, g->x_proj_w, W, D, (int)T, 1, W, D, 1, D, 0}, st));
+    MM_TRY(launch_gemm_f32({a.dxd, wx, a.du, (int)T, D, W, W, 1, D, 1, D, 1}, st));
+  }
+  {
+    StageScope sc(timer, st, MM_STAGE_BWD_CONV);
+    MM_TRY(launch_backward_stage(s->io_dtype, a, 4, st));
+    MM_TRY(launch_backward_stage(s->io_dtype, a, 5, st));
+  }
+  return MM_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -396,6 +535,29 @@ mm_status mamba_mixer_prefill(const mm_shape *s, const mm_params *p, const void 
                               void *workspace, size_t workspace_bytes, void *stream) {
   return prefill_impl(s, p, xz, y, conv_state, ssm_state, states_valid, workspace,
                       workspace_bytes, stream, nullptr);
+}
+
+size_t mm_backward_workspace_bytes(const mm_shape *s) {
+  if (check_shape(s, false) != MM_OK || s->dt_rank > 1024) return 0;
+  return bw_layout(*s).total;
+}
+
+mm_status mamba_mixer_prefill_backward(const mm_shape *s, const mm_params *p, const void *xz,
+                                       const void *dy, const void *conv_state,
+                                       const float *ssm_state, int states_valid, const mm_grads *g,
+                                       void *workspace, size_t workspace_bytes, void *stream) {
+  return backward_impl(s, p, xz, dy, conv_state, ssm_state, states_valid, g, workspace,
+                       workspace_bytes, stream, nullptr);
+}
+
+mm_status mamba_mixer_prefill_backward_timed(const mm_shape *s, const mm_params *p,
+                                             const void *xz, const void *dy,
+                                             const void *conv_state, const float *ssm_state,
+                                             int states_valid, const mm_grads *g, void *workspace,
+                                             size_t workspace_bytes, void *stream,
+                                             mm_stage_timer *timer) {
+  return backward_impl(s, p, xz, dy, conv_state, ssm_state, states_valid, g, workspace,
+                       workspace_bytes, stream, timer);
 }
 
 mm_status mamba_mixer_prefill_timed(const mm_shape *s, const mm_params *p, const void *xz, void *y,
@@ -458,7 +620,8 @@ mm_status mm_stage_timer_read(mm_stage_timer *t, double *ms_sum, int64_t *launch
 const char *mm_stage_name(int stage) {
   static const char *names[MM_STAGE_COUNT] = {"conv_silu", "x_proj", "rmsnorm", "dt_proj_softplus",
                                               "selective_scan", "conv_state", "layer_rmsnorm",
-                                              "in_proj", "out_proj"};
+                                              "in_proj", "out_proj", "bwd_recompute",
+                                              "bwd_scan", "bwd_proj", "bwd_conv"};
   return (stage >= 0 && stage < MM_STAGE_COUNT) ? names[stage] : "unknown";
 }
 

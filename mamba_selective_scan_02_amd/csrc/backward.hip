@@ -1,0 +1,575 @@
+// Backward of the mixer prefill: gradients of sum(dy * y) with respect to xz, the parameters
+// and the carried states (training through the parallel scan, Jamba analysis page, "Parallel
+// training via the parallel scan"). Arithmetic is fp32; xz, dy and dxz are in the I/O dtype.
+//
+// The forward (continuous SSM / ZOH / recurrence equations of "The Mamba Layer", the RMSNorm
+// equation, and the Mamba-1 conv, softplus and gate) is differentiated step by step in reverse:
+//   gate      y = ys SiLU(z), ys = C.h + D u  ->  dys = dy SiLU(z), dz = dy ys SiLU'(z)
+//   scan      h_t = a_t h_{t-1} + bb_t u_t, a = exp(dt A), bb = dt B (or expm1(dt A) / A B)
+//             dh_t = C_t dys_t + a_{t+1} dh_{t+1}, and from dh_t, h_{t-1}: d dt, dA, dB, du
+//   softplus  dt = softplus(p)  ->  dp = d dt sigmoid(p)
+//   RMSNorm   o = v / r g  ->  dv = g do / r - v sum(g do v) / (n r^3),  dg = sum_t do v / r
+//   x_proj / dt_proj: products with the weights (and their transposes); conv + SiLU last.
+//
+// Kernels, in launch order:
+//   bw_conv_u_kernel          u = SiLU(conv1d(x) + b) in fp32                  [T, D]
+//   gemm_f32_kernel           the six products (x_proj, dt_proj, their input and weight
+//                             gradients): fp32 16x16x4 MFMA, 64 x 64 tiles, any strides
+//   (norm_kernel)             the forward's RMSNorm of dt_low, B, C (fp32 mode)
+//   bw_pointwise_kernel       dt = softplus(p), sigmoid(p), dys = dy SiLU(z)
+//   bw_range_transfer_kernel  per range of kRT tokens and (channel, state): the forward
+//                             transfer (prod a, local end state) and the reverse one (local
+//                             a_t0 dh_t0 from zero)
+//   bw_range_carry_kernel     sequential over ranges: each range's true start state and the
+//                             dh carry entering it from later ranges; the last carry is the
+//                             gradient of the carried SSM state
+//   bw_scan_kernel            per range, 64 channels x 16 states per workgroup: a forward pass
+//                             (gate gradient dz, checkpoints every kSB tokens in LDS), then
+//                             sub-blocks in reverse, each recomputed into registers and walked
+//                             backward. Sums over the 16 states by DPP within a 16-lane row;
+//                             dB and dC (shared by all channels) sum over the wave's 4 channels
+//                             by lane swaps, over the 16 waves in LDS, into per-workgroup rows
+//   bw_rowsum_kernel          dB | dC from those per-workgroup rows
+//   bw_norm_bwd_kernel        the three RMSNorm backwards per token (+ gain terms)
+//   bw_colsum_kernels         fixed-order column sums (bias, gains, D, A, conv partials)
+//   bw_dq_kernel / bw_conv_bwd_kernel   SiLU' and the transposed depthwise convolution
+#include "common.h"
+#include "kernels.h"
+
+namespace mm {
+namespace {
+
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+
+constexpr int kRT = 512;          // tokens per range (carry granularity)
+constexpr int kSB = 32;           // tokens per recomputed sub-block
+constexpr int kNSB = kRT / kSB;   // sub-blocks per range
+constexpr int kCG = 64;           // channels per scan workgroup
+constexpr int kColRows = 1024;    // rows per partial of a column sum
+
+__device__ __forceinline__ float sigmoid_f(float v) {
+  return __builtin_amdgcn_rcpf(1.0f + exp2_hw(-v * kLog2e));
+}
+__device__ __forceinline__ float dsilu_f(float v) {
+  const float s = sigmoid_f(v);
+  return s * __builtin_fmaf(v, 1.0f - s, 1.0f);
+}
+// sum over the 16 lanes of a DPP row; every lane of the row receives the sum
+__device__ __forceinline__ float row_sum16(float v) {
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x124, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x128, 0xF, 0xF, false));
+  return v;
+}
+
+// ---------------------------------------------------------------- weights to fp32
+template <typename T>
+__global__ __launch_bounds__(256) void to_f32_kernel(const T *src, float *dst, int64_t n) {
+  for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+    dst[i] = io<T>::ld(src + i);
+}
+
+// ---------------------------------------------------------------- u = SiLU(conv1d(x) + b)
+// x at position s < 0 is the carried conv state (index K-1+s, oldest first) or zero.
+template <typename T>
+__device__ __forceinline__ float conv_in(const BwArgs &a, int b, int s, int i) {
+  if (s >= 0) return io<T>::ld((const T *)a.xz + ((int64_t)b * a.L + s) * 2 * a.D + i);
+  if (!a.cs_valid) return 0.f;
+  return io<T>::ld((const T *)a.conv_state + ((int64_t)b * a.D + i) * (a.K - 1) + (a.K - 1 + s));
+}
+template <typename T>
+__device__ __forceinline__ float conv_pre(const BwArgs &a, int b, int t, int i) {
+  float q = a.conv_b ? io<T>::ld((const T *)a.conv_b + i) : 0.f;
+  for (int k = 0; k < a.K; ++k)
+    q = __builtin_fmaf(io<T>::ld((const T *)a.conv_w + i * a.K + k), conv_in<T>(a, b, t - (a.K - 1) + k, i), q);
+  return q;
+}
+template <typename T>
+__global__ __launch_bounds__(256) void bw_conv_u_kernel(BwArgs a) {
+  const int64_t n = (int64_t)a.B * a.L * a.D;
+  for (int64_t e = blockIdx.x * 256ll + threadIdx.x; e < n; e += (int64_t)gridDim.x * 256) {
+    const int i = (int)(e % a.D);
+    const int64_t tok = e / a.D;
+    const int t = (int)(tok % a.L), b = (int)(tok / a.L);
+    a.u[e] = silu_f(conv_pre<T>(a, b, t, i));
+  }
+}
+
+// ---------------------------------------------------------------- dt, sigmoid(p), dys
+template <typename T>
+__global__ __launch_bounds__(256) void bw_pointwise_kernel(BwArgs a) {
+  const int64_t n = (int64_t)a.B * a.L * a.D;
+  for (int64_t e = blockIdx.x * 256ll + threadIdx.x; e < n; e += (int64_t)gridDim.x * 256) {
+    const int i = (int)(e % a.D);
+    const int64_t tok = e / a.D;
+    const float p = a.dt[e] + a.dt_b[i];        // dt holds dt_proj's product on entry
+    a.dt[e] = softplus_f(p);
+    a.sig[e] = sigmoid_f(p);
+    const float z = io<T>::ld((const T *)a.xz + tok * 2 * a.D + a.D + i);
+    a.dys[e] = io<T>::ld((const T *)a.dy + e) * silu_f(z);
+  }
+}
+
+// ---------------------------------------------------------------- per-range transfers
+// lanes: 16 channels x 16 states per workgroup; one range of one sequence
+__global__ __launch_bounds__(256) void bw_range_transfer_kernel(BwArgs a) {
+  const int ncg = a.D / 16;
+  const int cg = blockIdx.x % ncg;
+  const int r = (blockIdx.x / ncg) % a.nr;
+  const int b = blockIdx.x / (ncg * a.nr);
+  const int n = threadIdx.x & 15, i = cg * 16 + (threadIdx.x >> 4);
+  const int t0 = r * kRT, t1 = min(a.L, t0 + kRT);
+  const float An = a.A[i * 16 + n];
+  float P = 1.f, S = 0.f;
+  for (int t = t0; t < t1; ++t) {
+    const int64_t tok = (int64_t)b * a.L + t;
+    const float dtv = a.dt[tok * a.D + i];
+    const float av = exp2_hw(dtv * An * kLog2e);
+    const float bb = (a.zoh ? expm1_f(dtv * An) / An : dtv) * a.bc[tok * 32 + n];
+    S = __builtin_fmaf(av, S, bb * a.u[tok * a.D + i]);
+    P *= av;
+  }
+  float g = 0.f;
+  for (int t = t1 - 1; t >= t0; --t) {
+    const int64_t tok = (int64_t)b * a.L + t;
+    const float dtv = a.dt[tok * a.D + i];
+    const float av = exp2_hw(dtv * An * kLog2e);
+    g = av * __builtin_fmaf(a.bc[tok * 32 + 16 + n], a.dys[tok * a.D + i], g);
+  }
+  const int64_t o = (((int64_t)b * a.nr + r) * a.D + i) * 16 + n;
+  a.rP[o] = P;
+  a.rS[o] = S;
+  a.rR[o] = g;
+}
+
+// sequential over the ranges of one (sequence, channel, state): rS becomes the start state
+// of each range, rR the carry a_{t1} dh_{t1} entering it from the ranges after it
+__global__ __launch_bounds__(256) void bw_range_carry_kernel(BwArgs a) {
+  const int64_t e = blockIdx.x * 256ll + threadIdx.x;
+  if (e >= (int64_t)a.B * a.D * 16) return;
+  const int64_t b = e / ((int64_t)a.D * 16), in = e % ((int64_t)a.D * 16);
+  float h = (a.ss_valid && a.ssm_state) ? a.ssm_state[e] : 0.f;
+  for (int r = 0; r < a.nr; ++r) {
+    const int64_t o = (b * a.nr + r) * a.D * 16 + in;
+    const float s = a.rS[o];
+    a.rS[o] = h;
+    h = __builtin_fmaf(a.rP[o], h, s);
+  }
+  float g = 0.f;
+  for (int r = a.nr - 1; r >= 0; --r) {
+    const int64_t o = (b * a.nr + r) * a.D * 16 + in;
+    const float rr = a.rR[o];
+    a.rR[o] = g;
+    g = __builtin_fmaf(a.rP[o], g, rr);
+  }
+  if (a.d_ssm_state) a.d_ssm_state[e] = g;
+}
+
+// ---------------------------------------------------------------- the reverse scan
+template <typename T, bool ZOH>
+__global__ __launch_bounds__(1024) void bw_scan_kernel(BwArgs a) {
+  __shared__ float ck_s[kNSB][1024];        // state checkpoints, one column per thread
+  __shared__ float red_s[kSB][16][32];      // per token, per wave: dB (16) | dC (16)
+
+  const int ncg = a.D / kCG;
+  const int cg = blockIdx.x % ncg;
+  const int r = (blockIdx.x / ncg) % a.nr;
+  const int b = blockIdx.x / (ncg * a.nr);
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int n = lane & 15, cl = lane >> 4;
+  const int i = cg * kCG + wv * 4 + cl;
+  const int t0 = r * kRT, t1 = min(a.L, t0 + kRT);
+  const int nsb = (t1 - t0 + kSB - 1) / kSB;
+  const float An = a.A[i * 16 + n];
+  const float Dv = a.Dskip[i];
+  const int64_t so = (((int64_t)b * a.nr + r) * a.D + i) * 16 + n;
+  const int64_t tb = (int64_t)b * a.L;
+
+  // pass 1: true states from the range's start state; checkpoints; the gate gradient dz
+  float h = a.rS[so];
+  float dD = 0.f;
+  for (int j = 0; j < nsb; ++j) {
+    ck_s[j][tid] = h;
+    const int te = min(t1, t0 + (j + 1) * kSB);
+    for (int t = t0 + j * kSB; t < te; ++t) {
+      const int64_t tok = tb + t;
+      const float dtv = a.dt[tok * a.D + i], uv = a.u[tok * a.D + i];
+      const float av = exp2_hw(dtv * An * kLog2e);
+      const float bb = (ZOH ? expm1_f(dtv * An) / An : dtv) * a.bc[tok * 32 + n];
+      h = __builtin_fmaf(av, h, bb * uv);
+      const float ys = row_sum16(a.bc[tok * 32 + 16 + n] * h);
+      if (n == 0) {
+        const float zv = io<T>::ld((const T *)a.xz + tok * 2 * a.D + a.D + i);
+        const float dyv = io<T>::ld((const T *)a.dy + tok * a.D + i);
+        io<T>::st((T *)a.dxz + tok * 2 * a.D + a.D + i, dyv * __builtin_fmaf(Dv, uv, ys) * dsilu_f(zv));
+        dD = __builtin_fmaf(a.dys[tok * a.D + i], uv, dD);
+      }
+    }
+  }
+
+  // pass 2: sub-blocks in reverse; carry = a_{t+1} dh_{t+1}
+  float carry = a.rR[so];
+  float dA = 0.f;
+  for (int j = nsb - 1; j >= 0; --j) {
+    const int tj = t0 + j * kSB;
+    float hist[kSB + 1], ah[kSB];
+    hist[0] = ck_s[j][tid];
+#pragma unroll
+    for (int k = 0; k < kSB; ++k) {
+      const int t = tj + k;
+      if (t < t1) {
+        const int64_t tok = tb + t;
+        const float dtv = a.dt[tok * a.D + i];
+        const float av = exp2_hw(dtv * An * kLog2e);
+        const float bb = (ZOH ? expm1_f(dtv * An) / An : dtv) * a.bc[tok * 32 + n];
+        ah[k] = av;
+        hist[k + 1] = __builtin_fmaf(av, hist[k], bb * a.u[tok * a.D + i]);
+      } else {
+        ah[k] = 0.f;
+        hist[k + 1] = 0.f;
+      }
+    }
+#pragma unroll
+    for (int k = kSB - 1; k >= 0; --k) {
+      const int t = tj + k;
+      float pB = 0.f, pC = 0.f;
+      if (t < t1) {
+        const int64_t tok = tb + t;
+        const float dtv = a.dt[tok * a.D + i], uv = a.u[tok * a.D + i];
+        const float Bn = a.bc[tok * 32 + n], Cn = a.bc[tok * 32 + 16 + n];
+        const float dysv = a.dys[tok * a.D + i];
+        const float av = ah[k];
+        const float dh = __builtin_fmaf(Cn, dysv, carry);
+        const float dAb = dh * hist[k];           // d / d a_t
+        const float dBb = dh * uv;                // d / d bb_t
+        float gdt, gdu;
+        if (ZOH) {
+          const float x = dtv * An;
+          const float E = expm1_f(x);
+          gdt = dAb * av * An + dBb * av * Bn;
+          dA += dAb * av * dtv + dBb * Bn * (x * av - E) / (An * An);
+          pB = dBb * E / An;
+          gdu = dh * (E / An) * Bn;
+        } else {
+          gdt = __builtin_fmaf(dAb * av, An, dBb * Bn);
+          dA = __builtin_fmaf(dAb * av, dtv, dA);
+          pB = dBb * dtv;
+          gdu = dh * dtv * Bn;
+        }
+        pC = dysv * hist[k + 1];
+        carry = av * dh;
+        const float sdt = row_sum16(gdt), sdu = row_sum16(gdu);
+        if (n == 0) {
+          const int64_t e = tok * a.D + i;
+          a.sig[e] = sdt * a.sig[e];                   // d / d (dt_proj pre-activation)
+          a.du[e] = __builtin_fmaf(Dv, dysv, sdu);     // d / du from the scan and D u
+        }
+      }
+      // the wave's 4 channels, then (lanes 0..15) one row per wave in LDS
+      pB += __shfl_xor(pB, 16, 64);
+      pB += __shfl_xor(pB, 32, 64);
+      pC += __shfl_xor(pC, 16, 64);
+      pC += __shfl_xor(pC, 32, 64);
+      if (cl == 0) {
+        red_s[k][wv][n] = pB;
+        red_s[k][wv][16 + n] = pC;
+      }
+    }
+    __syncthreads();
+    {
+      const int k = tid >> 5, c = tid & 31;
+      const int t = tj + k;
+      if (t < t1) {
+        float s = 0.f;
+#pragma unroll
+        for (int w = 0; w < 16; ++w) s += red_s[k][w][c];
+        a.bc_part[((tb + t) * ncg + cg) * 32 + c] = s;
+      }
+    }
+    __syncthreads();
+  }
+  a.dA_part[so] = dA;
+  if (n == 0) a.dD_part[((int64_t)b * a.nr + r) * a.D + i] = dD;
+}
+
+// dB | dC [T, 32] = sum over the channel groups of the scan's per-workgroup rows
+__global__ __launch_bounds__(256) void bw_rowsum_kernel(const float *part, float *out, int64_t T,
+                                                        int ncg) {
+  const int64_t e = blockIdx.x * 256ll + threadIdx.x;
+  if (e >= T * 32) return;
+  const int64_t tok = e >> 5;
+  const int c = (int)(e & 31);
+  float s = 0.f;
+  for (int g = 0; g < ncg; ++g) s += part[(tok * ncg + g) * 32 + c];
+  out[e] = s;
+}
+
+// ---------------------------------------------------------------- column sums
+// part[blk][c] = sum of rows [blk * kColRows, +kColRows) of column c; then out[c] = sum_blk
+__global__ __launch_bounds__(256) void bw_colsum_part_kernel(const float *in, int64_t rows,
+                                                             int64_t cols, float *part) {
+  const int64_t c = blockIdx.x * 256ll + threadIdx.x;
+  const int64_t blk = blockIdx.y;
+  if (c >= cols) return;
+  const int64_t r0 = blk * kColRows, r1 = min(rows, r0 + kColRows);
+  float s = 0.f;
+  for (int64_t rr = r0; rr < r1; ++rr) s += in[rr * cols + c];
+  part[blk * cols + c] = s;
+}
+__global__ __launch_bounds__(256) void bw_colsum_final_kernel(const float *part, int64_t nblk,
+                                                              int64_t cols, float *out) {
+  const int64_t c = blockIdx.x * 256ll + threadIdx.x;
+  if (c >= cols) return;
+  float s = 0.f;
+  for (int64_t k = 0; k < nblk; ++k) s += part[k * cols + c];
+  out[c] = s;
+}
+
+// ---------------------------------------------------------------- RMSNorm backward
+// one wave per token; slices [0, R) dt_low, [R, R+16) B, [R+16, R+32) C of xdbl
+__global__ __launch_bounds__(256) void bw_norm_bwd_kernel(BwArgs a) {
+  const int64_t tok = blockIdx.x * 4ll + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (tok >= a.T) return;
+  const int W = a.R + 32;
+  const float *v = a.xd + tok * W;
+  float *dv = a.dxd + tok * W, *gc = a.gc + tok * W;
+  auto slice = [&](int off, int len, const float *gamma, const float *dout) {
+    float ss = 0.f, sg = 0.f;
+    for (int j = lane; j < len; j += 64) {
+      const float x = v[off + j];
+      ss = __builtin_fmaf(x, x, ss);
+      sg = __builtin_fmaf(gamma[j] * dout[j], x, sg);
+    }
+    ss = wave_sum(ss);
+    sg = wave_sum(sg);
+    const float rinv = 1.0f / sqrtf(ss / (float)len + a.eps);
+    const float c = sg * rinv * rinv * rinv / (float)len;
+    for (int j = lane; j < len; j += 64) {
+      const float x = v[off + j];
+      dv[off + j] = gamma[j] * dout[j] * rinv - x * c;
+      gc[off + j] = dout[j] * x * rinv;
+    }
+  };
+  slice(0, a.R, a.g_dt, a.ddtn + tok * a.R);
+  slice(a.R, 16, a.g_B, a.dbc + tok * 32);
+  slice(a.R + 16, 16, a.g_C, a.dbc + tok * 32 + 16);
+}
+
+// ---------------------------------------------------------------- conv + SiLU backward
+// dq = du SiLU'(q), in place
+template <typename T>
+__global__ __launch_bounds__(256) void bw_dq_kernel(BwArgs a) {
+  const int64_t n = (int64_t)a.B * a.L * a.D;
+  for (int64_t e = blockIdx.x * 256ll + threadIdx.x; e < n; e += (int64_t)gridDim.x * 256) {
+    const int i = (int)(e % a.D);
+    const int64_t tok = e / a.D;
+    const int t = (int)(tok % a.L), b = (int)(tok / a.L);
+    a.du[e] *= dsilu_f(conv_pre<T>(a, b, t, i));
+  }
+}
+// dx[t] = sum_k w_k dq[t + K-1-k]; the carried state's gradient likewise for s < 0; per block
+// of kColRows tokens, partial sums of dq x(t - (K-1) + k) (d conv_w) and of dq (d conv_b)
+template <typename T>
+__global__ __launch_bounds__(256) void bw_conv_bwd_kernel(BwArgs a) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  const int blk = blockIdx.y, b = blockIdx.z;
+  if (i >= a.D) return;
+  const int nb = (a.L + kColRows - 1) / kColRows;
+  const int s0 = blk * kColRows, s1 = min(a.L, s0 + kColRows);
+  float w[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int k = 0; k < a.K; ++k) w[k] = io<T>::ld((const T *)a.conv_w + i * a.K + k);
+  const int64_t tb = (int64_t)b * a.L;
+  float pw[4] = {0.f, 0.f, 0.f, 0.f}, pb = 0.f;
+  for (int t = s0; t < s1; ++t) {
+    float dx = 0.f;
+    for (int k = 0; k < a.K; ++k) {
+      const int q = t + a.K - 1 - k;
+      if (q < a.L) dx = __builtin_fmaf(w[k], a.du[(tb + q) * a.D + i], dx);
+    }
+    io<T>::st((T *)a.dxz + (tb + t) * 2 * a.D + i, dx);
+    const float dq = a.du[(tb + t) * a.D + i];
+    pb += dq;
+    for (int k = 0; k < a.K; ++k) pw[k] = __builtin_fmaf(dq, conv_in<T>(a, b, t - (a.K - 1) + k, i), pw[k]);
+  }
+  float *cp = a.conv_part + (((int64_t)b * nb + blk) * a.D + i) * 5;
+  for (int k = 0; k < 4; ++k) cp[k] = pw[k];
+  cp[4] = pb;
+  if (blk == 0 && a.d_conv_state) {
+    // positions s = -(K-1) .. -1 of the input (state index K-1+s)
+    for (int s = -(a.K - 1); s < 0; ++s) {
+      float d = 0.f;
+      for (int k = 0; k < a.K; ++k) {
+        const int q = s + a.K - 1 - k;
+        if (q >= 0 && q < a.L) d = __builtin_fmaf(w[k], a.du[(tb + q) * a.D + i], d);
+      }
+      a.d_conv_state[((int64_t)b * a.D + i) * (a.K - 1) + (a.K - 1 + s)] = d;
+    }
+  }
+}
+// conv_part [B * nb][D][5] -> d conv_w [D, K], d conv_b [D]
+__global__ __launch_bounds__(256) void bw_conv_final_kernel(BwArgs a, int nparts) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= a.D) return;
+  float s[5] = {0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int p = 0; p < nparts; ++p)
+    for (int k = 0; k < 5; ++k) s[k] += a.conv_part[((int64_t)p * a.D + i) * 5 + k];
+  for (int k = 0; k < a.K; ++k) a.d_conv_w[i * a.K + k] = s[k];
+  if (a.d_conv_b) a.d_conv_b[i] = s[4];
+}
+
+// ---------------------------------------------------------------- fp32 GEMM
+// C[m, n] (+)= sum_k A(m, k) B(k, n), A(m, k) = A[m sam + k sak], B(k, n) = B[k sbk + n sbn].
+// 64 x 64 tiles, 4 waves of 32 x 32 (2 x 2 blocks of v_mfma_f32_16x16x4_f32), K in chunks of 16
+// through LDS (rows padded to 65 floats: the 4 k-rows a fragment read touches fall in distinct
+// banks); the next chunk's elements are loaded into registers during the current chunk.
+__global__ __launch_bounds__(256) void gemm_f32_kernel(GemmF32Args g) {
+  __shared__ float as[16][65], bs[16][65];
+  const int m0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int wm = wv >> 1, wn = wv & 1;
+  const int l16 = lane & 15, lk = lane >> 4;
+  float ra[4], rb[4];
+  auto load = [&](int k0) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = tid + 256 * j;
+      int mm, kk, nn, kb;
+      if (g.sak == 1) { kk = e & 15; mm = e >> 4; } else { mm = e & 63; kk = e >> 6; }
+      if (g.sbn == 1) { nn = e & 63; kb = e >> 6; } else { kb = e & 15; nn = e >> 4; }
+      const int m = m0 + mm, ka = k0 + kk, n = n0 + nn, k2 = k0 + kb;
+      ra[j] = (m < g.M && ka < g.K) ? g.A[(int64_t)m * g.sam + (int64_t)ka * g.sak] : 0.f;
+      rb[j] = (n < g.N && k2 < g.K) ? g.B[(int64_t)k2 * g.sbk + (int64_t)n * g.sbn] : 0.f;
+    }
+  };
+  auto stash = [&]() {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = tid + 256 * j;
+      if (g.sak == 1) as[e & 15][e >> 4] = ra[j]; else as[e >> 6][e & 63] = ra[j];
+      if (g.sbn == 1) bs[e >> 6][e & 63] = rb[j]; else bs[e & 15][e >> 4] = rb[j];
+    }
+  };
+  f32x4 acc[2][2];
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int y = 0; y < 2; ++y) acc[x][y] = f32x4{0.f, 0.f, 0.f, 0.f};
+  load(0);
+  for (int k0 = 0; k0 < g.K; k0 += 16) {
+    stash();
+    __syncthreads();
+    if (k0 + 16 < g.K) load(k0 + 16);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int kr = ks * 4 + lk;
+      float fa[2], fb[2];
+#pragma unroll
+      for (int x = 0; x < 2; ++x) fa[x] = as[kr][wm * 32 + x * 16 + l16];
+#pragma unroll
+      for (int y = 0; y < 2; ++y) fb[y] = bs[kr][wn * 32 + y * 16 + l16];
+      // lane (l16, lk) of block (x, y) ends with C[m = 16 x + 4 lk + q][n = 16 y + l16]
+#pragma unroll
+      for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int y = 0; y < 2; ++y)
+          acc[x][y] = __builtin_amdgcn_mfma_f32_16x16x4f32(fa[x], fb[y], acc[x][y], 0, 0, 0);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int y = 0; y < 2; ++y)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int m = m0 + wm * 32 + x * 16 + lk * 4 + q;
+        const int n = n0 + wn * 32 + y * 16 + l16;
+        if (m < g.M && n < g.N) {
+          float *c = g.C + (int64_t)m * g.ldc + n;
+          *c = g.accumulate ? *c + acc[x][y][q] : acc[x][y][q];
+        }
+      }
+}
+
+inline unsigned grid_for(int64_t n) {
+  const int64_t b = (n + 255) / 256;
+  return (unsigned)(b < 65536 ? b : 65536);
+}
+
+}  // namespace
+
+hipError_t launch_gemm_f32(const GemmF32Args &g, hipStream_t s) {
+  if (g.M <= 0 || g.N <= 0) return hipSuccess;
+  hipLaunchKernelGGL(gemm_f32_kernel, dim3((unsigned)((g.N + 63) / 64), (unsigned)((g.M + 63) / 64)),
+                     dim3(256), 0, s, g);
+  return hipGetLastError();
+}
+
+hipError_t launch_colsum(const float *in, int64_t rows, int64_t cols, float *part, float *out,
+                         hipStream_t s) {
+  const int64_t nblk = (rows + kColRows - 1) / kColRows;
+  hipLaunchKernelGGL(bw_colsum_part_kernel, dim3((unsigned)((cols + 255) / 256), (unsigned)nblk),
+                     dim3(256), 0, s, in, rows, cols, part);
+  hipLaunchKernelGGL(bw_colsum_final_kernel, dim3((unsigned)((cols + 255) / 256)), dim3(256), 0, s,
+                     part, nblk, cols, out);
+  return hipGetLastError();
+}
+
+int bw_ranges(int L) { return (L + kRT - 1) / kRT; }
+int64_t bw_colsum_blocks(int64_t rows) { return (rows + kColRows - 1) / kColRows; }
+
+template <typename T>
+hipError_t bw_dispatch(const BwArgs &a, int stage, hipStream_t s) {
+  const int64_t TD = (int64_t)a.B * a.L * a.D;
+  switch (stage) {
+    case 0:
+      hipLaunchKernelGGL(bw_conv_u_kernel<T>, dim3(grid_for(TD)), dim3(256), 0, s, a);
+      break;
+    case 1:
+      hipLaunchKernelGGL(bw_pointwise_kernel<T>, dim3(grid_for(TD)), dim3(256), 0, s, a);
+      break;
+    case 2: {
+      hipLaunchKernelGGL(bw_range_transfer_kernel, dim3((unsigned)(a.B * a.nr * (a.D / 16))),
+                         dim3(256), 0, s, a);
+      const int64_t nc = (int64_t)a.B * a.D * 16;
+      hipLaunchKernelGGL(bw_range_carry_kernel, dim3((unsigned)((nc + 255) / 256)), dim3(256), 0, s, a);
+      const unsigned grid = (unsigned)(a.B * a.nr * (a.D / kCG));
+      if (a.zoh) hipLaunchKernelGGL((bw_scan_kernel<T, true>), dim3(grid), dim3(1024), 0, s, a);
+      else hipLaunchKernelGGL((bw_scan_kernel<T, false>), dim3(grid), dim3(1024), 0, s, a);
+      hipLaunchKernelGGL(bw_rowsum_kernel, dim3((unsigned)((a.T * 32 + 255) / 256)), dim3(256), 0, s,
+                         a.bc_part, a.dbc, a.T, a.D / kCG);
+      break;
+    }
+    case 3:
+      hipLaunchKernelGGL(bw_norm_bwd_kernel, dim3((unsigned)((a.T + 3) / 4)), dim3(256), 0, s, a);
+      break;
+    case 4:
+      hipLaunchKernelGGL(bw_dq_kernel<T>, dim3(grid_for(TD)), dim3(256), 0, s, a);
+      break;
+    case 5: {
+      const int nb = (a.L + kColRows - 1) / kColRows;
+      hipLaunchKernelGGL(bw_conv_bwd_kernel<T>, dim3((unsigned)((a.D + 255) / 256), (unsigned)nb, (unsigned)a.B),
+                         dim3(256), 0, s, a);
+      hipLaunchKernelGGL(bw_conv_final_kernel, dim3((unsigned)((a.D + 255) / 256)), dim3(256), 0, s,
+                         a, a.B * nb);
+      break;
+    }
+    case 6: {  // weights to fp32 (bf16 I/O)
+      const int W = a.R + 32;
+      hipLaunchKernelGGL(to_f32_kernel<T>, dim3(grid_for((int64_t)W * a.D)), dim3(256), 0, s,
+                         (const T *)a.x_proj_w, a.wx32, (int64_t)W * a.D);
+      hipLaunchKernelGGL(to_f32_kernel<T>, dim3(grid_for((int64_t)a.D * a.R)), dim3(256), 0, s,
+                         (const T *)a.dt_proj_w, a.wdt32, (int64_t)a.D * a.R);
+      break;
+    }
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_backward_stage(mm_dtype dt, const BwArgs &a, int stage, hipStream_t s) {
+  return dt == MM_F32 ? bw_dispatch<float>(a, stage, s) : bw_dispatch<bf16_t>(a, stage, s);
+}
+
+}  // namespace mm

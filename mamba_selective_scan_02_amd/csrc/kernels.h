@@ -116,6 +116,52 @@ hipError_t launch_gemm_nt(const GemmArgs &g, hipStream_t s, int tile = 0);
 hipError_t launch_rmsnorm_rows(const uint16_t *x, const float *gamma, uint16_t *y, int T, int Dm,
                                float eps, hipStream_t s);
 
+
+// ---- backward of the prefill (backward.hip). fp32 workspace arrays; T = batch * seqlen.
+struct BwArgs {
+  // forward inputs (io dtype unless noted) and dy
+  const void *xz, *dy, *conv_w, *conv_b, *conv_state;
+  int cs_valid;
+  const float *ssm_state;
+  int ss_valid;
+  const void *x_proj_w, *dt_proj_w;
+  const float *dt_b, *A, *Dskip, *g_dt, *g_B, *g_C;
+  float eps;
+  int zoh;
+  int B, L, D, K, R, nr;   // nr = ranges per sequence
+  int64_t T;
+  // workspace
+  float *wx32, *wdt32;     // weights in fp32 (bf16 I/O)
+  float *u, *xd, *dtn, *bc;                 // [T, D], [T, R+32], [T, R], [T, 32]
+  float *dt, *sig, *dys, *du;               // [T, D]; sig becomes d/d(dt_proj pre-activation)
+  float *rP, *rS, *rR, *dA_part;            // [B, nr, D, 16]
+  float *dD_part;                           // [B, nr, D]
+  float *bc_part, *dbc;                     // [T, D/64, 32], [T, 32]
+  float *ddtn, *dxd, *gc;                   // [T, R], [T, R+32], [T, R+32]
+  float *conv_part;                         // [B, ceil(L/1024), D, 5]
+  // outputs
+  void *dxz;
+  float *d_conv_w, *d_conv_b, *d_ssm_state, *d_conv_state;
+};
+// stage: 0 u; 1 dt / sigmoid / dys; 2 range transfers + carries + reverse scan + dB|dC;
+// 3 RMSNorm backward; 4 SiLU'; 5 conv backward + conv weight sums; 6 weights to fp32
+hipError_t launch_backward_stage(mm_dtype dt, const BwArgs &a, int stage, hipStream_t s);
+int bw_ranges(int L);
+int64_t bw_colsum_blocks(int64_t rows);
+
+// C[m, n] (+)= sum_k A[m sam + k sak] B[k sbk + n sbn], fp32 (16x16x4 fp32 MFMA)
+struct GemmF32Args {
+  const float *A, *B;
+  float *C;
+  int M, N, K;
+  int64_t sam, sak, sbk, sbn, ldc;
+  int accumulate;
+};
+hipError_t launch_gemm_f32(const GemmF32Args &g, hipStream_t s);
+// out[c] = sum over rows of in[rows, cols] (fixed order); part >= bw_colsum_blocks(rows) * cols
+hipError_t launch_colsum(const float *in, int64_t rows, int64_t cols, float *part, float *out,
+                         hipStream_t s);
+
 struct ScanArgs {
   const void *xz;       // [B, L, 2D]; x = first D columns (conv input), z = last D (gate)
   const void *conv_w;   // [D, K] io dtype

@@ -32,7 +32,7 @@ def test_library_exports_every_declared_symbol():
     L = mm.lib()
     for name in _declared_functions():
         assert hasattr(L, name), name
-    assert L.mm_abi_version() == 2
+    assert L.mm_abi_version() == 3
 
 
 def _shape(**kw):
@@ -134,3 +134,33 @@ def test_status_strings_and_stage_names():
     assert L.mm_status_string(mm.MM_OK) == b"ok"
     assert L.mm_status_string(mm.MM_ERR_WORKSPACE).startswith(b"workspace")
     assert [L.mm_stage_name(i).decode() for i in range(len(mm.STAGES))] == list(mm.STAGES)
+
+
+def test_backward_validation_before_launch():
+    L = mm.lib()
+    s = _shape(seqlen=1000, d_inner=256, dt_rank=64)
+    need = mm.backward_workspace_bytes(s)
+    assert need > 0
+    fake = 0x100000
+    p = mm.Params(*([fake] * 10))
+    g = mm.Grads(*([3 * fake] * len(mm.GRAD_NAMES)))
+    g.dxz = 4 * fake
+
+    def call(p=p, g=g, xz=fake, dy=2 * fake, ws=fake, nbytes=need, s=s):
+        return L.mamba_mixer_prefill_backward(ctypes.byref(s), ctypes.byref(p), xz, dy, None,
+                                              None, 0, ctypes.byref(g), ws, nbytes, None)
+    assert call(nbytes=need - 1) == mm.MM_ERR_WORKSPACE
+    assert call(ws=fake + 16) == mm.MM_ERR_WORKSPACE
+    assert call(xz=None) == mm.MM_ERR_INVALID_ARG
+    assert call(dy=fake + 4) == mm.MM_ERR_INVALID_ARG
+    g2 = mm.Grads(*([3 * fake] * len(mm.GRAD_NAMES)))
+    g2.dxz = fake                                   # dxz aliases xz
+    assert call(g=g2) == mm.MM_ERR_INVALID_ARG
+    g3 = mm.Grads(*([3 * fake] * len(mm.GRAD_NAMES)))
+    g3.dxz, g3.A = 4 * fake, None                   # a required parameter gradient missing
+    assert call(g=g3) == mm.MM_ERR_INVALID_ARG
+    p2 = mm.Params(*([fake] * 10))
+    p2.conv_b = None                                # conv_b gradient given without a conv bias
+    assert call(p=p2) == mm.MM_ERR_INVALID_ARG
+    assert call(s=_shape(seqlen=1000, d_inner=256, dt_rank=64, d_state=8)) == mm.MM_ERR_UNSUPPORTED
+    assert mm.lib().mm_backward_workspace_bytes(ctypes.byref(_shape(d_state=8))) == 0
