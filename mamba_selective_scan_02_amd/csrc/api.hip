@@ -357,7 +357,7 @@ mm_status layer_impl(const mm_shape *s, int d_model, const mm_layer_params *p, c
 
 // Backward workspace (fp32 arrays; T = batch * seqlen, W = dt_rank + 32, nr = ranges).
 struct BwWs {
-  size_t wx32, wdt32, u, xd, dtn, bc, dt, sig, dys, du, rP, rS, rR, dA_part, dD_part, bc_part,
+  size_t wx32, wdt32, u, xd, dtn, bc, dt, sig, dys, du, ys, rP, rS, rR, dA_part, dD_part, bc_part,
       dbc, ddtn, dxd, gc, cs_part, gsum, conv_part, total;
 };
 BwWs bw_layout(const mm_shape &s) {
@@ -379,6 +379,7 @@ BwWs bw_layout(const mm_shape &s) {
   take(w.sig, T * D);
   take(w.dys, T * D);
   take(w.du, T * D);
+  take(w.ys, T * D);
   take(w.rP, SR);
   take(w.rS, SR);
   take(w.rR, SR);
@@ -447,6 +448,7 @@ mm_status backward_impl(const mm_shape *s, const mm_params *p, const void *xz, c
   a.B = B; a.L = L; a.D = D; a.K = s->d_conv; a.R = R; a.nr = bw_ranges(L); a.T = T;
   a.wx32 = F(w.wx32); a.wdt32 = F(w.wdt32); a.u = F(w.u); a.xd = F(w.xd); a.dtn = F(w.dtn);
   a.bc = F(w.bc); a.dt = F(w.dt); a.sig = F(w.sig); a.dys = F(w.dys); a.du = F(w.du);
+  a.ys = F(w.ys);
   a.rP = F(w.rP); a.rS = F(w.rS); a.rR = F(w.rR); a.dA_part = F(w.dA_part);
   a.dD_part = F(w.dD_part); a.bc_part = F(w.bc_part); a.dbc = F(w.dbc); a.ddtn = F(w.ddtn);
   a.dxd = F(w.dxd); a.gc = F(w.gc); a.conv_part = F(w.conv_part);

@@ -24,11 +24,15 @@
 //                             dh carry entering it from later ranges; the last carry is the
 //                             gradient of the carried SSM state
 //   bw_scan_kernel            per range, 64 channels x 16 states per workgroup: a forward pass
-//                             (gate gradient dz, checkpoints every kSB tokens in LDS), then
-//                             sub-blocks in reverse, each recomputed into registers and walked
-//                             backward. Sums over the 16 states by DPP within a 16-lane row;
-//                             dB and dC (shared by all channels) sum over the wave's 4 channels
-//                             by lane swaps, over the 16 waves in LDS, into per-workgroup rows
+//                             (ys = C.h + D u for the gate, checkpoints every kSB tokens in
+//                             LDS), then sub-blocks in reverse, each recomputed into registers
+//                             and walked backward. Each sub-block's inputs are staged in LDS by
+//                             coalesced loads issued one sub-block ahead (the recurrence never
+//                             waits on global memory). Sums over the 16 states by DPP within a
+//                             16-lane row; dB and dC (shared by all channels) sum over the
+//                             wave's 4 channels by lane swaps, over the 16 waves in LDS, into
+//                             per-workgroup rows
+//   bw_post_scan_kernel       d(dt_proj pre-activation) = d dt sigmoid(p); dz = dy ys SiLU'(z)
 //   bw_rowsum_kernel          dB | dC from those per-workgroup rows
 //   bw_norm_bwd_kernel        the three RMSNorm backwards per token (+ gain terms)
 //   bw_colsum_kernels         fixed-order column sums (bias, gains, D, A, conv partials)
@@ -112,30 +116,83 @@ __global__ __launch_bounds__(256) void bw_pointwise_kernel(BwArgs a) {
 }
 
 // ---------------------------------------------------------------- per-range transfers
-// lanes: 16 channels x 16 states per workgroup; one range of one sequence
+// lanes: 16 channels x 16 states per workgroup; one range of one sequence. The inputs of each
+// kSB-token sub-block (dt, u, dys of the 16 channels, B|C) are staged in LDS by coalesced
+// loads, the next sub-block's fetched into registers while the current one is processed.
+constexpr int kRTF = kSB * 16;                   // floats per staged [kSB][16] array
+constexpr int kRTStage = 3 * kRTF + kSB * 32;    // dt | u | dys | B|C
 __global__ __launch_bounds__(256) void bw_range_transfer_kernel(BwArgs a) {
+  __shared__ float st_s[kRTStage];
   const int ncg = a.D / 16;
   const int cg = blockIdx.x % ncg;
   const int r = (blockIdx.x / ncg) % a.nr;
   const int b = blockIdx.x / (ncg * a.nr);
-  const int n = threadIdx.x & 15, i = cg * 16 + (threadIdx.x >> 4);
+  const int tid = threadIdx.x;
+  const int n = tid & 15, c = tid >> 4, i = cg * 16 + c;
   const int t0 = r * kRT, t1 = min(a.L, t0 + kRT);
+  const int nsb = (t1 - t0 + kSB - 1) / kSB;
+  const int64_t tb = (int64_t)b * a.L;
   const float An = a.A[i * 16 + n];
+  constexpr int NQ = kRTStage / 256;
+  float pf[NQ];
+  auto fetch = [&](int j) {
+    const int tj = t0 + j * kSB;
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      const int e = tid + 256 * q;
+      float v = 0.f;
+      if (e < 3 * kRTF) {
+        const int off = e % kRTF, k = off >> 4, ch = off & 15;
+        const float *src = e < kRTF ? a.dt : (e < 2 * kRTF ? a.u : a.dys);
+        if (tj + k < t1) v = src[(tb + tj + k) * a.D + cg * 16 + ch];
+      } else {
+        const int off = e - 3 * kRTF, k = off >> 5, ch = off & 31;
+        if (tj + k < t1) v = a.bc[(tb + tj + k) * 32 + ch];
+      }
+      pf[q] = v;
+    }
+  };
+  auto stash = [&]() {
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) st_s[tid + 256 * q] = pf[q];
+  };
+  const float *s_dt = st_s, *s_u = st_s + kRTF, *s_dys = st_s + 2 * kRTF, *s_bc = st_s + 3 * kRTF;
+
   float P = 1.f, S = 0.f;
-  for (int t = t0; t < t1; ++t) {
-    const int64_t tok = (int64_t)b * a.L + t;
-    const float dtv = a.dt[tok * a.D + i];
-    const float av = exp2_hw(dtv * An * kLog2e);
-    const float bb = (a.zoh ? expm1_f(dtv * An) / An : dtv) * a.bc[tok * 32 + n];
-    S = __builtin_fmaf(av, S, bb * a.u[tok * a.D + i]);
-    P *= av;
+  fetch(0);
+  for (int j = 0; j < nsb; ++j) {
+    __syncthreads();
+    stash();
+    __syncthreads();
+    if (j + 1 < nsb) fetch(j + 1);
+    const int tj = t0 + j * kSB;
+#pragma unroll
+    for (int k = 0; k < kSB; ++k) {
+      if (tj + k < t1) {
+        const float dtv = s_dt[k * 16 + c];
+        const float av = exp2_hw(dtv * An * kLog2e);
+        const float bb = (a.zoh ? expm1_f(dtv * An) / An : dtv) * s_bc[k * 32 + n];
+        S = __builtin_fmaf(av, S, bb * s_u[k * 16 + c]);
+        P *= av;
+      }
+    }
   }
   float g = 0.f;
-  for (int t = t1 - 1; t >= t0; --t) {
-    const int64_t tok = (int64_t)b * a.L + t;
-    const float dtv = a.dt[tok * a.D + i];
-    const float av = exp2_hw(dtv * An * kLog2e);
-    g = av * __builtin_fmaf(a.bc[tok * 32 + 16 + n], a.dys[tok * a.D + i], g);
+  fetch(nsb - 1);
+  for (int j = nsb - 1; j >= 0; --j) {
+    __syncthreads();
+    stash();
+    __syncthreads();
+    if (j > 0) fetch(j - 1);
+    const int tj = t0 + j * kSB;
+#pragma unroll
+    for (int k = kSB - 1; k >= 0; --k) {
+      if (tj + k < t1) {
+        const float dtv = s_dt[k * 16 + c];
+        const float av = exp2_hw(dtv * An * kLog2e);
+        g = av * __builtin_fmaf(s_bc[k * 32 + 16 + n], s_dys[k * 16 + c], g);
+      }
+    }
   }
   const int64_t o = (((int64_t)b * a.nr + r) * a.D + i) * 16 + n;
   a.rP[o] = P;
@@ -167,10 +224,15 @@ __global__ __launch_bounds__(256) void bw_range_carry_kernel(BwArgs a) {
 }
 
 // ---------------------------------------------------------------- the reverse scan
+// Staged inputs of one kSB-token sub-block for the workgroup's 64 channels: dt | u | dys
+// ([kSB][64] each) and B|C ([kSB][32]); thread tid stages elements tid + 1024 q.
+constexpr int kSF = kSB * kCG;
+constexpr int kSStage = 3 * kSF + kSB * 32;
 template <typename T, bool ZOH>
 __global__ __launch_bounds__(1024) void bw_scan_kernel(BwArgs a) {
   __shared__ float ck_s[kNSB][1024];        // state checkpoints, one column per thread
   __shared__ float red_s[kSB][16][32];      // per token, per wave: dB (16) | dC (16)
+  __shared__ float st_s[kSStage];           // the current sub-block's inputs
 
   const int ncg = a.D / kCG;
   const int cg = blockIdx.x % ncg;
@@ -178,32 +240,62 @@ __global__ __launch_bounds__(1024) void bw_scan_kernel(BwArgs a) {
   const int b = blockIdx.x / (ncg * a.nr);
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int n = lane & 15, cl = lane >> 4;
-  const int i = cg * kCG + wv * 4 + cl;
+  const int c = wv * 4 + cl;                // channel within the group
+  const int i = cg * kCG + c;
   const int t0 = r * kRT, t1 = min(a.L, t0 + kRT);
   const int nsb = (t1 - t0 + kSB - 1) / kSB;
   const float An = a.A[i * 16 + n];
   const float Dv = a.Dskip[i];
   const int64_t so = (((int64_t)b * a.nr + r) * a.D + i) * 16 + n;
   const int64_t tb = (int64_t)b * a.L;
+  constexpr int NQ = kSStage / 1024;
+  float pf[NQ];
+  auto fetch = [&](int j) {
+    const int tj = t0 + j * kSB;
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      const int e = tid + 1024 * q;
+      float v = 0.f;
+      if (e < 3 * kSF) {
+        const int off = e % kSF, k = off >> 6, ch = off & 63;
+        const float *src = e < kSF ? a.dt : (e < 2 * kSF ? a.u : a.dys);
+        if (tj + k < t1) v = src[(tb + tj + k) * a.D + cg * kCG + ch];
+      } else {
+        const int off = e - 3 * kSF, k = off >> 5, ch = off & 31;
+        if (tj + k < t1) v = a.bc[(tb + tj + k) * 32 + ch];
+      }
+      pf[q] = v;
+    }
+  };
+  auto stash = [&]() {
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) st_s[tid + 1024 * q] = pf[q];
+  };
+  const float *s_dt = st_s, *s_u = st_s + kSF, *s_dys = st_s + 2 * kSF, *s_bc = st_s + 3 * kSF;
 
-  // pass 1: true states from the range's start state; checkpoints; the gate gradient dz
+  // pass 1: true states from the range's start state; checkpoints; ys = C.h + D u for the gate
   float h = a.rS[so];
   float dD = 0.f;
+  fetch(0);
   for (int j = 0; j < nsb; ++j) {
+    __syncthreads();
+    stash();
+    __syncthreads();
+    if (j + 1 < nsb) fetch(j + 1);
     ck_s[j][tid] = h;
-    const int te = min(t1, t0 + (j + 1) * kSB);
-    for (int t = t0 + j * kSB; t < te; ++t) {
-      const int64_t tok = tb + t;
-      const float dtv = a.dt[tok * a.D + i], uv = a.u[tok * a.D + i];
-      const float av = exp2_hw(dtv * An * kLog2e);
-      const float bb = (ZOH ? expm1_f(dtv * An) / An : dtv) * a.bc[tok * 32 + n];
-      h = __builtin_fmaf(av, h, bb * uv);
-      const float ys = row_sum16(a.bc[tok * 32 + 16 + n] * h);
-      if (n == 0) {
-        const float zv = io<T>::ld((const T *)a.xz + tok * 2 * a.D + a.D + i);
-        const float dyv = io<T>::ld((const T *)a.dy + tok * a.D + i);
-        io<T>::st((T *)a.dxz + tok * 2 * a.D + a.D + i, dyv * __builtin_fmaf(Dv, uv, ys) * dsilu_f(zv));
-        dD = __builtin_fmaf(a.dys[tok * a.D + i], uv, dD);
+    const int tj = t0 + j * kSB;
+#pragma unroll
+    for (int k = 0; k < kSB; ++k) {
+      if (tj + k < t1) {
+        const float dtv = s_dt[k * kCG + c], uv = s_u[k * kCG + c];
+        const float av = exp2_hw(dtv * An * kLog2e);
+        const float bb = (ZOH ? expm1_f(dtv * An) / An : dtv) * s_bc[k * 32 + n];
+        h = __builtin_fmaf(av, h, bb * uv);
+        const float ys = row_sum16(s_bc[k * 32 + 16 + n] * h);
+        if (n == 0) {
+          a.ys[(tb + tj + k) * a.D + i] = __builtin_fmaf(Dv, uv, ys);
+          dD = __builtin_fmaf(s_dys[k * kCG + c], uv, dD);
+        }
       }
     }
   }
@@ -211,20 +303,23 @@ __global__ __launch_bounds__(1024) void bw_scan_kernel(BwArgs a) {
   // pass 2: sub-blocks in reverse; carry = a_{t+1} dh_{t+1}
   float carry = a.rR[so];
   float dA = 0.f;
+  fetch(nsb - 1);
   for (int j = nsb - 1; j >= 0; --j) {
+    __syncthreads();     // the stage and red_s are free (previous sub-block fully consumed)
+    stash();
+    __syncthreads();
+    if (j > 0) fetch(j - 1);
     const int tj = t0 + j * kSB;
     float hist[kSB + 1], ah[kSB];
     hist[0] = ck_s[j][tid];
 #pragma unroll
     for (int k = 0; k < kSB; ++k) {
-      const int t = tj + k;
-      if (t < t1) {
-        const int64_t tok = tb + t;
-        const float dtv = a.dt[tok * a.D + i];
+      if (tj + k < t1) {
+        const float dtv = s_dt[k * kCG + c];
         const float av = exp2_hw(dtv * An * kLog2e);
-        const float bb = (ZOH ? expm1_f(dtv * An) / An : dtv) * a.bc[tok * 32 + n];
+        const float bb = (ZOH ? expm1_f(dtv * An) / An : dtv) * s_bc[k * 32 + n];
         ah[k] = av;
-        hist[k + 1] = __builtin_fmaf(av, hist[k], bb * a.u[tok * a.D + i]);
+        hist[k + 1] = __builtin_fmaf(av, hist[k], bb * s_u[k * kCG + c]);
       } else {
         ah[k] = 0.f;
         hist[k + 1] = 0.f;
@@ -235,10 +330,9 @@ __global__ __launch_bounds__(1024) void bw_scan_kernel(BwArgs a) {
       const int t = tj + k;
       float pB = 0.f, pC = 0.f;
       if (t < t1) {
-        const int64_t tok = tb + t;
-        const float dtv = a.dt[tok * a.D + i], uv = a.u[tok * a.D + i];
-        const float Bn = a.bc[tok * 32 + n], Cn = a.bc[tok * 32 + 16 + n];
-        const float dysv = a.dys[tok * a.D + i];
+        const float dtv = s_dt[k * kCG + c], uv = s_u[k * kCG + c];
+        const float Bn = s_bc[k * 32 + n], Cn = s_bc[k * 32 + 16 + n];
+        const float dysv = s_dys[k * kCG + c];
         const float av = ah[k];
         const float dh = __builtin_fmaf(Cn, dysv, carry);
         const float dAb = dh * hist[k];           // d / d a_t
@@ -261,8 +355,8 @@ __global__ __launch_bounds__(1024) void bw_scan_kernel(BwArgs a) {
         carry = av * dh;
         const float sdt = row_sum16(gdt), sdu = row_sum16(gdu);
         if (n == 0) {
-          const int64_t e = tok * a.D + i;
-          a.sig[e] = sdt * a.sig[e];                   // d / d (dt_proj pre-activation)
+          const int64_t e = (tb + t) * a.D + i;
+          a.dt[e] = sdt;                               // d / d dt (dt is not read again)
           a.du[e] = __builtin_fmaf(Dv, dysv, sdu);     // d / du from the scan and D u
         }
       }
@@ -278,19 +372,33 @@ __global__ __launch_bounds__(1024) void bw_scan_kernel(BwArgs a) {
     }
     __syncthreads();
     {
-      const int k = tid >> 5, c = tid & 31;
+      const int k = tid >> 5, cc = tid & 31;
       const int t = tj + k;
       if (t < t1) {
-        float s = 0.f;
+        float sum = 0.f;
 #pragma unroll
-        for (int w = 0; w < 16; ++w) s += red_s[k][w][c];
-        a.bc_part[((tb + t) * ncg + cg) * 32 + c] = s;
+        for (int w = 0; w < 16; ++w) sum += red_s[k][w][cc];
+        a.bc_part[((tb + t) * ncg + cg) * 32 + cc] = sum;
       }
     }
-    __syncthreads();
   }
   a.dA_part[so] = dA;
   if (n == 0) a.dD_part[((int64_t)b * a.nr + r) * a.D + i] = dD;
+}
+
+// after the scan: d(dt_proj pre-activation) = d dt * sigmoid(p) (into sig) and the gate's
+// dz = dy ys SiLU'(z) (into dxz)
+template <typename T>
+__global__ __launch_bounds__(256) void bw_post_scan_kernel(BwArgs a) {
+  const int64_t n = (int64_t)a.B * a.L * a.D;
+  for (int64_t e = blockIdx.x * 256ll + threadIdx.x; e < n; e += (int64_t)gridDim.x * 256) {
+    const int i = (int)(e % a.D);
+    const int64_t tok = e / a.D;
+    a.sig[e] *= a.dt[e];
+    const float z = io<T>::ld((const T *)a.xz + tok * 2 * a.D + a.D + i);
+    io<T>::st((T *)a.dxz + tok * 2 * a.D + a.D + i,
+              io<T>::ld((const T *)a.dy + e) * a.ys[e] * dsilu_f(z));
+  }
 }
 
 // dB | dC [T, 32] = sum over the channel groups of the scan's per-workgroup rows
@@ -540,6 +648,7 @@ hipError_t bw_dispatch(const BwArgs &a, int stage, hipStream_t s) {
       else hipLaunchKernelGGL((bw_scan_kernel<T, false>), dim3(grid), dim3(1024), 0, s, a);
       hipLaunchKernelGGL(bw_rowsum_kernel, dim3((unsigned)((a.T * 32 + 255) / 256)), dim3(256), 0, s,
                          a.bc_part, a.dbc, a.T, a.D / kCG);
+      hipLaunchKernelGGL(bw_post_scan_kernel<T>, dim3(grid_for(TD)), dim3(256), 0, s, a);
       break;
     }
     case 3:

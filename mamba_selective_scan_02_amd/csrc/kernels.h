@@ -133,7 +133,8 @@ struct BwArgs {
   // workspace
   float *wx32, *wdt32;     // weights in fp32 (bf16 I/O)
   float *u, *xd, *dtn, *bc;                 // [T, D], [T, R+32], [T, R], [T, 32]
-  float *dt, *sig, *dys, *du;               // [T, D]; sig becomes d/d(dt_proj pre-activation)
+  float *dt, *sig, *dys, *du, *ys;          // [T, D]; the scan turns dt into d/d dt and the
+                                            // post-scan pass sig into d/d(dt_proj pre-act.)
   float *rP, *rS, *rR, *dA_part;            // [B, nr, D, 16]
   float *dD_part;                           // [B, nr, D]
   float *bc_part, *dbc;                     // [T, D/64, 32], [T, 32]
