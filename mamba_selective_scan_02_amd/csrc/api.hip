@@ -358,14 +358,15 @@ mm_status layer_impl(const mm_shape *s, int d_model, const mm_layer_params *p, c
 // Backward workspace (fp32 arrays; T = batch * seqlen, W = dt_rank + 32, nr = ranges).
 struct BwWs {
   size_t wx32, wdt32, u, xd, dtn, bc, dt, sig, dys, du, ys, rP, rS, rR, dA_part, dD_part, bc_part,
-      dbc, ddtn, dxd, gc, cs_part, gsum, conv_part, total;
+      dbc, ddtn, dxd, gc, cs_part, gsum, conv_part, conv_sum, gemm_part, total;
 };
 BwWs bw_layout(const mm_shape &s) {
   const size_t T = (size_t)s.batch * s.seqlen, D = s.d_inner, R = s.dt_rank, W = R + 32;
   const size_t nr = (size_t)bw_ranges(s.seqlen), SR = (size_t)s.batch * nr * D * 16;
   const size_t nbT = (size_t)bw_colsum_blocks((int64_t)T);
   const size_t nbR = (size_t)bw_colsum_blocks((int64_t)s.batch * nr);
-  const size_t nbc = ((size_t)s.seqlen + 1023) / 1024;
+  const size_t nstrip = (size_t)s.batch * bw_conv_strips(s.seqlen);
+  const size_t nbS = (size_t)bw_colsum_blocks((int64_t)nstrip);
   BwWs w;
   size_t o = 0;
   auto take = [&](size_t &f, size_t floats) { f = o; o += up(floats * 4); };
@@ -390,9 +391,11 @@ BwWs bw_layout(const mm_shape &s) {
   take(w.ddtn, T * R);
   take(w.dxd, T * W);
   take(w.gc, T * W);
-  take(w.cs_part, std::max(nbT * std::max(D, W), nbR * D * 16));
+  take(w.cs_part, std::max(std::max(nbT * std::max(D, W), nbR * D * 16), nbS * D * 5));
   take(w.gsum, W);
-  take(w.conv_part, (size_t)s.batch * nbc * D * 5);
+  take(w.conv_part, nstrip * D * 5);
+  take(w.conv_sum, D * 5);
+  take(w.gemm_part, (size_t)kMaxSplit * D * std::max(W, R));
   w.total = o;
   return w;
 }
@@ -452,6 +455,7 @@ mm_status backward_impl(const mm_shape *s, const mm_params *p, const void *xz, c
   a.rP = F(w.rP); a.rS = F(w.rS); a.rR = F(w.rR); a.dA_part = F(w.dA_part);
   a.dD_part = F(w.dD_part); a.bc_part = F(w.bc_part); a.dbc = F(w.dbc); a.ddtn = F(w.ddtn);
   a.dxd = F(w.dxd); a.gc = F(w.gc); a.conv_part = F(w.conv_part);
+  a.conv_sum = F(w.conv_sum);
   a.dxz = g->dxz; a.d_conv_w = g->conv_w; a.d_conv_b = g->conv_b;
   a.d_ssm_state = g->ssm_state; a.d_conv_state = g->conv_state;
   const float *wx = bf ? a.wx32 : (const float *)p->x_proj_w;
@@ -462,10 +466,10 @@ mm_status backward_impl(const mm_shape *s, const mm_params *p, const void *xz, c
     StageScope sc(timer, st, MM_STAGE_BWD_RECOMPUTE);
     if (bf) MM_TRY(launch_backward_stage(s->io_dtype, a, 6, st));
     MM_TRY(launch_backward_stage(s->io_dtype, a, 0, st));                    // u
-    MM_TRY(launch_gemm_f32({a.u, wx, a.xd, (int)T, W, D, D, 1, 1, D, W, 0}, st));   // xdbl
+    MM_TRY(launch_gemm_f32({a.u, wx, a.xd, (int)T, W, D, D, 1, 1, D, W, 1, 0}, st));   // xdbl
     MM_TRY(launch_norm(MM_F32, a.xd, a.dtn, nullptr, a.bc, a.g_dt, a.g_B, a.g_C, (int)T, R, 16,
                        a.eps, st));
-    MM_TRY(launch_gemm_f32({a.dtn, wdt, a.dt, (int)T, D, R, R, 1, 1, R, D, 0}, st));  // W_dt dt_low
+    MM_TRY(launch_gemm_f32({a.dtn, wdt, a.dt, (int)T, D, R, R, 1, 1, R, D, 1, 0}, st));  // W_dt dt_low
     MM_TRY(launch_backward_stage(s->io_dtype, a, 1, st));                    // dt, sigmoid, dys
   }
   {
@@ -478,20 +482,24 @@ mm_status backward_impl(const mm_shape *s, const mm_params *p, const void *xz, c
     StageScope sc(timer, st, MM_STAGE_BWD_PROJ);
     float *dp = a.sig;   // d / d (dt_proj pre-activation), [T, D]
     MM_TRY(launch_colsum(dp, T, D, cs, g->dt_proj_b, st));
-    MM_TRY(launch_gemm_f32({dp, a.dtn, g->dt_proj_w, D, R, (int)T, 1, D, R, 1, R, 0}, st));
-    MM_TRY(launch_gemm_f32({dp, wdt, a.ddtn, (int)T, R, D, D, 1, R, 1, R, 0}, st));
+    float *gp = F(w.gemm_part);
+    MM_TRY(launch_gemm_f32({dp, a.dtn, g->dt_proj_w, D, R, (int)T, 1, D, R, 1, R, 1, 0, gp}, st));
+    MM_TRY(launch_gemm_f32({dp, wdt, a.ddtn, (int)T, R, D, D, 1, R, 1, R, 1, 0}, st));
     MM_TRY(launch_backward_stage(s->io_dtype, a, 3, st));                    // RMSNorm backward
     MM_TRY(launch_colsum(a.gc, T, W, cs, F(w.gsum), st));
     MM_TRY(hipMemcpyAsync(g->dt_norm_w, F(w.gsum), (size_t)R * 4, hipMemcpyDeviceToDevice, st));
     MM_TRY(hipMemcpyAsync(g->B_norm_w, F(w.gsum) + R, 64, hipMemcpyDeviceToDevice, st));
     MM_TRY(hipMemcpyAsync(g->C_norm_w, F(w.gsum) + R + 16, 64, hipMemcpyDeviceToDevice, st));
-    MM_TRY(launch_gemm_f32({a.dxd, a.u, g->x_proj_w, W, D, (int)T, 1, W, D, 1, D, 0}, st));
-    MM_TRY(launch_gemm_f32({a.dxd, wx, a.du, (int)T, D, W, W, 1, D, 1, D, 1}, st));
+    // d x_proj_w [W, D] computed transposed (M = D, N = W) so the long side is M
+    MM_TRY(launch_gemm_f32({a.u, a.dxd, g->x_proj_w, D, W, (int)T, 1, D, W, 1, 1, D, 0, gp}, st));
+    MM_TRY(launch_gemm_f32({a.dxd, wx, a.du, (int)T, D, W, W, 1, D, 1, D, 1, 1}, st));
   }
   {
     StageScope sc(timer, st, MM_STAGE_BWD_CONV);
-    MM_TRY(launch_backward_stage(s->io_dtype, a, 4, st));
     MM_TRY(launch_backward_stage(s->io_dtype, a, 5, st));
+    MM_TRY(launch_colsum(a.conv_part, (int64_t)B * bw_conv_strips(L), (int64_t)D * 5, cs,
+                         a.conv_sum, st));
+    MM_TRY(launch_backward_stage(s->io_dtype, a, 7, st));
   }
   return MM_OK;
 }

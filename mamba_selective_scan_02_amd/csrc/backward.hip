@@ -14,7 +14,8 @@
 // Kernels, in launch order:
 //   bw_conv_u_kernel          u = SiLU(conv1d(x) + b) in fp32                  [T, D]
 //   gemm_f32_kernel           the six products (x_proj, dt_proj, their input and weight
-//                             gradients): fp32 16x16x4 MFMA, 64 x 64 tiles, any strides
+//                             gradients): fp32 16x16x4 MFMA, 128 x 128 (128 x 64 for
+//                             N <= 512) tiles, any strides
 //   (norm_kernel)             the forward's RMSNorm of dt_low, B, C (fp32 mode)
 //   bw_pointwise_kernel       dt = softplus(p), sigmoid(p), dys = dy SiLU(z)
 //   bw_range_transfer_kernel  per range of kRT tokens and (channel, state): the forward
@@ -36,7 +37,9 @@
 //   bw_rowsum_kernel          dB | dC from those per-workgroup rows
 //   bw_norm_bwd_kernel        the three RMSNorm backwards per token (+ gain terms)
 //   bw_colsum_kernels         fixed-order column sums (bias, gains, D, A, conv partials)
-//   bw_dq_kernel / bw_conv_bwd_kernel   SiLU' and the transposed depthwise convolution
+//   bw_conv_bwd_kernel        SiLU' and the transposed depthwise convolution in one pass
+//                             (sliding windows of x and dq per 64-token strip), conv weight
+//                             partials; bw_conv_scatter_kernel places their column sums
 #include "common.h"
 #include "kernels.h"
 
@@ -89,14 +92,64 @@ __device__ __forceinline__ float conv_pre(const BwArgs &a, int b, int t, int i) 
     q = __builtin_fmaf(io<T>::ld((const T *)a.conv_w + i * a.K + k), conv_in<T>(a, b, t - (a.K - 1) + k, i), q);
   return q;
 }
+// 4 consecutive channels of a row (8-byte bf16 / 16-byte fp32 accesses)
+template <typename T> struct v4io;
+template <> struct v4io<float> {
+  static __device__ __forceinline__ void ld(const float *p, float v[4]) {
+    const float4 x = *(const float4 *)p;
+    v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+  }
+  static __device__ __forceinline__ void st(float *p, const float v[4]) {
+    *(float4 *)p = make_float4(v[0], v[1], v[2], v[3]);
+  }
+};
+template <> struct v4io<bf16_t> {
+  static __device__ __forceinline__ void ld(const bf16_t *p, float v[4]) {
+    const uint2 x = *(const uint2 *)p;
+    v[0] = lo_bf(x.x); v[1] = hi_bf(x.x); v[2] = lo_bf(x.y); v[3] = hi_bf(x.y);
+  }
+  static __device__ __forceinline__ void st(bf16_t *p, const float v[4]) {
+    uint2 x;
+    x.x = pack_bf2(v[0], v[1]);
+    x.y = pack_bf2(v[2], v[3]);
+    *(uint2 *)p = x;
+  }
+};
+// x of channels i0 .. i0+3 at position s of sequence b (s < 0: the carried state or zero)
 template <typename T>
+__device__ __forceinline__ void conv_in4(const BwArgs &a, int b, int s, int i0, float v[4]) {
+  if (s >= 0) {
+    v4io<T>::ld((const T *)a.xz + ((int64_t)b * a.L + s) * 2 * a.D + i0, v);
+    return;
+  }
+#pragma unroll
+  for (int c = 0; c < 4; ++c) v[c] = conv_in<T>(a, b, s, i0 + c);
+}
+template <typename T, int K>
 __global__ __launch_bounds__(256) void bw_conv_u_kernel(BwArgs a) {
-  const int64_t n = (int64_t)a.B * a.L * a.D;
+  const int nq = a.D / 4;
+  const int64_t n = (int64_t)a.B * a.L * nq;
   for (int64_t e = blockIdx.x * 256ll + threadIdx.x; e < n; e += (int64_t)gridDim.x * 256) {
-    const int i = (int)(e % a.D);
-    const int64_t tok = e / a.D;
+    const int i0 = (int)(e % nq) * 4;
+    const int64_t tok = e / nq;
     const int t = (int)(tok % a.L), b = (int)(tok / a.L);
-    a.u[e] = silu_f(conv_pre<T>(a, b, t, i));
+    float q[4], xv[4], w[4][K];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      q[c] = a.conv_b ? io<T>::ld((const T *)a.conv_b + i0 + c) : 0.f;
+#pragma unroll
+      for (int k = 0; k < K; ++k) w[c][k] = io<T>::ld((const T *)a.conv_w + (i0 + c) * K + k);
+    }
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      conv_in4<T>(a, b, t - (K - 1) + k, i0, xv);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) q[c] = __builtin_fmaf(w[c][k], xv[c], q[c]);
+    }
+    float u[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) u[c] = silu_f(q[c]);
+    v4io<float>::st(a.u + tok * a.D + i0, u);
   }
 }
 
@@ -466,139 +519,233 @@ __global__ __launch_bounds__(256) void bw_norm_bwd_kernel(BwArgs a) {
 }
 
 // ---------------------------------------------------------------- conv + SiLU backward
-// dq = du SiLU'(q), in place
-template <typename T>
-__global__ __launch_bounds__(256) void bw_dq_kernel(BwArgs a) {
-  const int64_t n = (int64_t)a.B * a.L * a.D;
-  for (int64_t e = blockIdx.x * 256ll + threadIdx.x; e < n; e += (int64_t)gridDim.x * 256) {
-    const int i = (int)(e % a.D);
-    const int64_t tok = e / a.D;
-    const int t = (int)(tok % a.L), b = (int)(tok / a.L);
-    a.du[e] *= dsilu_f(conv_pre<T>(a, b, t, i));
-  }
-}
-// dx[t] = sum_k w_k dq[t + K-1-k]; the carried state's gradient likewise for s < 0; per block
-// of kColRows tokens, partial sums of dq x(t - (K-1) + k) (d conv_w) and of dq (d conv_b)
-template <typename T>
+// One thread per (sequence, strip of kStrip tokens, 4 channels). Walking t' over the strip
+// (and K-1 tokens past it), it recomputes q(t') from a sliding window of x, forms
+// dq = du SiLU'(q), and keeps the last K values of dq: dx[t] = sum_k w_k dq[t + K-1-k] is
+// complete once t' = t + K-1. Partial sums of dq x(t - (K-1) + k) (d conv_w) and of dq
+// (d conv_b) per strip go to conv_part [strips][D][5]; the strip at t = 0 also forms the
+// carried conv state's gradient.
+constexpr int kStrip = 64;
+template <typename T, int K>
 __global__ __launch_bounds__(256) void bw_conv_bwd_kernel(BwArgs a) {
-  const int i = blockIdx.x * 256 + threadIdx.x;
-  const int blk = blockIdx.y, b = blockIdx.z;
-  if (i >= a.D) return;
-  const int nb = (a.L + kColRows - 1) / kColRows;
-  const int s0 = blk * kColRows, s1 = min(a.L, s0 + kColRows);
-  float w[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int k = 0; k < a.K; ++k) w[k] = io<T>::ld((const T *)a.conv_w + i * a.K + k);
+  const int nq = a.D / 4;
+  const int nstrip = (a.L + kStrip - 1) / kStrip;
+  const int64_t e = blockIdx.x * 256ll + threadIdx.x;
+  if (e >= (int64_t)a.B * nstrip * nq) return;
+  const int i0 = (int)(e % nq) * 4;
+  const int strip = (int)((e / nq) % nstrip), b = (int)(e / ((int64_t)nq * nstrip));
+  const int t0 = strip * kStrip, t1 = min(a.L, t0 + kStrip);
   const int64_t tb = (int64_t)b * a.L;
-  float pw[4] = {0.f, 0.f, 0.f, 0.f}, pb = 0.f;
-  for (int t = s0; t < s1; ++t) {
-    float dx = 0.f;
-    for (int k = 0; k < a.K; ++k) {
-      const int q = t + a.K - 1 - k;
-      if (q < a.L) dx = __builtin_fmaf(w[k], a.du[(tb + q) * a.D + i], dx);
-    }
-    io<T>::st((T *)a.dxz + (tb + t) * 2 * a.D + i, dx);
-    const float dq = a.du[(tb + t) * a.D + i];
-    pb += dq;
-    for (int k = 0; k < a.K; ++k) pw[k] = __builtin_fmaf(dq, conv_in<T>(a, b, t - (a.K - 1) + k, i), pw[k]);
+  float w[4][K], bias[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    bias[c] = a.conv_b ? io<T>::ld((const T *)a.conv_b + i0 + c) : 0.f;
+#pragma unroll
+    for (int k = 0; k < K; ++k) w[c][k] = io<T>::ld((const T *)a.conv_w + (i0 + c) * K + k);
   }
-  float *cp = a.conv_part + (((int64_t)b * nb + blk) * a.D + i) * 5;
-  for (int k = 0; k < 4; ++k) cp[k] = pw[k];
-  cp[4] = pb;
-  if (blk == 0 && a.d_conv_state) {
-    // positions s = -(K-1) .. -1 of the input (state index K-1+s)
-    for (int s = -(a.K - 1); s < 0; ++s) {
-      float d = 0.f;
-      for (int k = 0; k < a.K; ++k) {
-        const int q = s + a.K - 1 - k;
-        if (q >= 0 && q < a.L) d = __builtin_fmaf(w[k], a.du[(tb + q) * a.D + i], d);
+  float xw[K][4];                 // xw[k] = x(t' - (K-1) + k)
+#pragma unroll
+  for (int k = 0; k < K - 1; ++k) conv_in4<T>(a, b, t0 - (K - 1) + k, i0, xw[k]);
+  float dqr[K][4];                // dqr[K-1-j] = dq(t' - j)
+  float first[K][4];              // dq(0 .. K-2) of the strip at t = 0
+  float pw[K][4], pb[4];
+#pragma unroll
+  for (int k = 0; k < K; ++k)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) dqr[k][c] = pw[k][c] = first[k][c] = 0.f;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) pb[c] = 0.f;
+  for (int tp = t0; tp < t1 + K - 1; ++tp) {
+    float dq[4] = {0.f, 0.f, 0.f, 0.f};
+    if (tp < a.L) {
+      conv_in4<T>(a, b, tp, i0, xw[K - 1]);
+      float du[4];
+      v4io<float>::ld(a.du + (tb + tp) * a.D + i0, du);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        float q = bias[c];
+#pragma unroll
+        for (int k = 0; k < K; ++k) q = __builtin_fmaf(w[c][k], xw[k][c], q);
+        dq[c] = du[c] * dsilu_f(q);
       }
-      a.d_conv_state[((int64_t)b * a.D + i) * (a.K - 1) + (a.K - 1 + s)] = d;
+      if (tp < t1) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          pb[c] += dq[c];
+#pragma unroll
+          for (int k = 0; k < K; ++k) pw[k][c] = __builtin_fmaf(dq[c], xw[k][c], pw[k][c]);
+        }
+      }
+      if (tp < K - 1) {
+#pragma unroll
+        for (int k = 0; k < K - 1; ++k)
+          if (tp == k)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) first[k][c] = dq[c];
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < K - 1; ++k)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        dqr[k][c] = dqr[k + 1][c];
+        xw[k][c] = xw[k + 1][c];
+      }
+#pragma unroll
+    for (int c = 0; c < 4; ++c) dqr[K - 1][c] = dq[c];
+    const int t = tp - (K - 1);
+    if (t >= t0) {
+      float dx[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        float v = 0.f;
+#pragma unroll
+        for (int k = 0; k < K; ++k) v = __builtin_fmaf(w[c][k], dqr[K - 1 - k][c], v);
+        dx[c] = v;
+      }
+      v4io<T>::st((T *)a.dxz + (tb + t) * 2 * a.D + i0, dx);
+    }
+  }
+  float *cp = a.conv_part + (((int64_t)b * nstrip + strip) * a.D + i0) * 5;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+#pragma unroll
+    for (int k = 0; k < K; ++k) cp[c * 5 + k] = pw[k][c];
+#pragma unroll
+    for (int k = K; k < 4; ++k) cp[c * 5 + k] = 0.f;
+    cp[c * 5 + 4] = pb[c];
+  }
+  if (strip == 0 && a.d_conv_state) {
+    // position s in [-(K-1), 0): sum over k of w_k dq(s + K-1-k), dq known for 0 <= . < L
+#pragma unroll
+    for (int sidx = 0; sidx < K - 1; ++sidx) {
+      const int sp = sidx - (K - 1);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        float d = 0.f;
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+          const int q = sp + K - 1 - k;
+          if (q >= 0 && q < K - 1 && q < a.L) d = __builtin_fmaf(w[c][k], first[q][c], d);
+        }
+        a.d_conv_state[((int64_t)b * a.D + i0 + c) * (K - 1) + sidx] = d;
+      }
     }
   }
 }
-// conv_part [B * nb][D][5] -> d conv_w [D, K], d conv_b [D]
-__global__ __launch_bounds__(256) void bw_conv_final_kernel(BwArgs a, int nparts) {
+// column sums of conv_part, [D][5] in conv_sum -> d conv_w [D, K], d conv_b [D]
+__global__ __launch_bounds__(256) void bw_conv_scatter_kernel(BwArgs a) {
   const int i = blockIdx.x * 256 + threadIdx.x;
   if (i >= a.D) return;
-  float s[5] = {0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int p = 0; p < nparts; ++p)
-    for (int k = 0; k < 5; ++k) s[k] += a.conv_part[((int64_t)p * a.D + i) * 5 + k];
-  for (int k = 0; k < a.K; ++k) a.d_conv_w[i * a.K + k] = s[k];
-  if (a.d_conv_b) a.d_conv_b[i] = s[4];
+  for (int k = 0; k < a.K; ++k) a.d_conv_w[i * a.K + k] = a.conv_sum[i * 5 + k];
+  if (a.d_conv_b) a.d_conv_b[i] = a.conv_sum[i * 5 + 4];
 }
 
 // ---------------------------------------------------------------- fp32 GEMM
-// C[m, n] (+)= sum_k A(m, k) B(k, n), A(m, k) = A[m sam + k sak], B(k, n) = B[k sbk + n sbn].
-// 64 x 64 tiles, 4 waves of 32 x 32 (2 x 2 blocks of v_mfma_f32_16x16x4_f32), K in chunks of 16
-// through LDS (rows padded to 65 floats: the 4 k-rows a fragment read touches fall in distinct
-// banks); the next chunk's elements are loaded into registers during the current chunk.
+// C[m scm + n scn] (+)= sum_k A(m, k) B(k, n), A(m, k) = A[m sam + k sak],
+// B(k, n) = B[k sbk + n sbn]. BM x BN tiles, 4 waves of (BM/2) x (BN/2) (blocks of
+// v_mfma_f32_16x16x4_f32), K in chunks of 16 through LDS; rows padded to a stride of 16 mod 64
+// floats so that the 4 k-rows of a fragment read fall in distinct bank groups. The next chunk's
+// elements are loaded into registers while the current chunk is multiplied.
+template <int BM, int BN>
 __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmF32Args g) {
-  __shared__ float as[16][65], bs[16][65];
-  const int m0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
+  constexpr int PA = BM + 16, PB = BN + 16;
+  constexpr int NA = BM * 16 / 256, NB = BN * 16 / 256;   // elements per thread per chunk
+  constexpr int XB = BM / 32, YB = BN / 32;               // 16 x 16 blocks per wave
+  __shared__ float as[16 * PA], bs[16 * PB];
+  const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int wm = wv >> 1, wn = wv & 1;
   const int l16 = lane & 15, lk = lane >> 4;
-  float ra[4], rb[4];
+  // split-K: this workgroup's K range (chunks of 16 per split)
+  const int kc = ((g.K + g.split - 1) / g.split + 15) / 16 * 16;
+  const int kbeg = blockIdx.z * kc, kend = min(g.K, kbeg + kc);
+  float ra[NA], rb[NB];
   auto load = [&](int k0) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < NA; ++j) {
       const int e = tid + 256 * j;
-      int mm, kk, nn, kb;
-      if (g.sak == 1) { kk = e & 15; mm = e >> 4; } else { mm = e & 63; kk = e >> 6; }
-      if (g.sbn == 1) { nn = e & 63; kb = e >> 6; } else { kb = e & 15; nn = e >> 4; }
-      const int m = m0 + mm, ka = k0 + kk, n = n0 + nn, k2 = k0 + kb;
-      ra[j] = (m < g.M && ka < g.K) ? g.A[(int64_t)m * g.sam + (int64_t)ka * g.sak] : 0.f;
-      rb[j] = (n < g.N && k2 < g.K) ? g.B[(int64_t)k2 * g.sbk + (int64_t)n * g.sbn] : 0.f;
+      const int mm = g.sak == 1 ? e >> 4 : e % BM, kk = g.sak == 1 ? e & 15 : e / BM;
+      const int m = m0 + mm, k = k0 + kk;
+      ra[j] = (m < g.M && k < kend) ? g.A[(int64_t)m * g.sam + (int64_t)k * g.sak] : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const int e = tid + 256 * j;
+      const int nn = g.sbn == 1 ? e % BN : e >> 4, kk = g.sbn == 1 ? e / BN : e & 15;
+      const int n = n0 + nn, k = k0 + kk;
+      rb[j] = (n < g.N && k < kend) ? g.B[(int64_t)k * g.sbk + (int64_t)n * g.sbn] : 0.f;
     }
   };
   auto stash = [&]() {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < NA; ++j) {
       const int e = tid + 256 * j;
-      if (g.sak == 1) as[e & 15][e >> 4] = ra[j]; else as[e >> 6][e & 63] = ra[j];
-      if (g.sbn == 1) bs[e >> 6][e & 63] = rb[j]; else bs[e & 15][e >> 4] = rb[j];
+      if (g.sak == 1) as[(e & 15) * PA + (e >> 4)] = ra[j];
+      else as[(e / BM) * PA + e % BM] = ra[j];
+    }
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const int e = tid + 256 * j;
+      if (g.sbn == 1) bs[(e / BN) * PB + e % BN] = rb[j];
+      else bs[(e & 15) * PB + (e >> 4)] = rb[j];
     }
   };
-  f32x4 acc[2][2];
+  f32x4 acc[XB][YB];
 #pragma unroll
-  for (int x = 0; x < 2; ++x)
+  for (int x = 0; x < XB; ++x)
 #pragma unroll
-    for (int y = 0; y < 2; ++y) acc[x][y] = f32x4{0.f, 0.f, 0.f, 0.f};
-  load(0);
-  for (int k0 = 0; k0 < g.K; k0 += 16) {
+    for (int y = 0; y < YB; ++y) acc[x][y] = f32x4{0.f, 0.f, 0.f, 0.f};
+  load(kbeg);
+  for (int k0 = kbeg; k0 < kend; k0 += 16) {
     stash();
     __syncthreads();
-    if (k0 + 16 < g.K) load(k0 + 16);
+    if (k0 + 16 < kend) load(k0 + 16);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const int kr = ks * 4 + lk;
-      float fa[2], fb[2];
+      float fa[XB], fb[YB];
 #pragma unroll
-      for (int x = 0; x < 2; ++x) fa[x] = as[kr][wm * 32 + x * 16 + l16];
+      for (int x = 0; x < XB; ++x) fa[x] = as[kr * PA + wm * (BM / 2) + x * 16 + l16];
 #pragma unroll
-      for (int y = 0; y < 2; ++y) fb[y] = bs[kr][wn * 32 + y * 16 + l16];
+      for (int y = 0; y < YB; ++y) fb[y] = bs[kr * PB + wn * (BN / 2) + y * 16 + l16];
       // lane (l16, lk) of block (x, y) ends with C[m = 16 x + 4 lk + q][n = 16 y + l16]
 #pragma unroll
-      for (int x = 0; x < 2; ++x)
+      for (int x = 0; x < XB; ++x)
 #pragma unroll
-        for (int y = 0; y < 2; ++y)
+        for (int y = 0; y < YB; ++y)
           acc[x][y] = __builtin_amdgcn_mfma_f32_16x16x4f32(fa[x], fb[y], acc[x][y], 0, 0, 0);
     }
     __syncthreads();
   }
 #pragma unroll
-  for (int x = 0; x < 2; ++x)
+  for (int x = 0; x < XB; ++x)
 #pragma unroll
-    for (int y = 0; y < 2; ++y)
+    for (int y = 0; y < YB; ++y)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int m = m0 + wm * 32 + x * 16 + lk * 4 + q;
-        const int n = n0 + wn * 32 + y * 16 + l16;
+        const int m = m0 + wm * (BM / 2) + x * 16 + lk * 4 + q;
+        const int n = n0 + wn * (BN / 2) + y * 16 + l16;
         if (m < g.M && n < g.N) {
-          float *c = g.C + (int64_t)m * g.ldc + n;
-          *c = g.accumulate ? *c + acc[x][y][q] : acc[x][y][q];
+          if (g.split > 1) {
+            g.part[((int64_t)blockIdx.z * g.M + m) * g.N + n] = acc[x][y][q];
+          } else {
+            float *c = g.C + (int64_t)m * g.scm + (int64_t)n * g.scn;
+            *c = g.accumulate ? *c + acc[x][y][q] : acc[x][y][q];
+          }
         }
       }
+}
+
+// split-K: C[m scm + n scn] (+)= sum over splits of part[split][m][n], in split order
+__global__ __launch_bounds__(256) void gemm_f32_splitk_sum_kernel(GemmF32Args g) {
+  const int64_t e = blockIdx.x * 256ll + threadIdx.x;
+  if (e >= (int64_t)g.M * g.N) return;
+  const int64_t m = e / g.N, n = e % g.N;
+  float v = 0.f;
+  for (int z = 0; z < g.split; ++z) v += g.part[(int64_t)z * g.M * g.N + e];
+  float *c = g.C + m * g.scm + n * g.scn;
+  *c = g.accumulate ? *c + v : v;
 }
 
 inline unsigned grid_for(int64_t n) {
@@ -608,10 +755,28 @@ inline unsigned grid_for(int64_t n) {
 
 }  // namespace
 
-hipError_t launch_gemm_f32(const GemmF32Args &g, hipStream_t s) {
-  if (g.M <= 0 || g.N <= 0) return hipSuccess;
-  hipLaunchKernelGGL(gemm_f32_kernel, dim3((unsigned)((g.N + 63) / 64), (unsigned)((g.M + 63) / 64)),
-                     dim3(256), 0, s, g);
+int gemm_f32_split(int M, int N, int K) {
+  const int64_t tiles = (int64_t)((M + 127) / 128) * (N <= 512 ? (N + 63) / 64 : (N + 127) / 128);
+  int split = 1;
+  while (split < kMaxSplit && tiles * split < 1024 && K / (split * 2) >= 2048) split *= 2;
+  return split;
+}
+
+hipError_t launch_gemm_f32(const GemmF32Args &g0, hipStream_t s) {
+  if (g0.M <= 0 || g0.N <= 0) return hipSuccess;
+  GemmF32Args g = g0;
+  g.split = g.part ? gemm_f32_split(g.M, g.N, g.K) : 1;
+  if (g.N <= 512)
+    hipLaunchKernelGGL((gemm_f32_kernel<128, 64>),
+                       dim3((unsigned)((g.N + 63) / 64), (unsigned)((g.M + 127) / 128), (unsigned)g.split),
+                       dim3(256), 0, s, g);
+  else
+    hipLaunchKernelGGL((gemm_f32_kernel<128, 128>),
+                       dim3((unsigned)((g.N + 127) / 128), (unsigned)((g.M + 127) / 128), (unsigned)g.split),
+                       dim3(256), 0, s, g);
+  if (g.split > 1)
+    hipLaunchKernelGGL(gemm_f32_splitk_sum_kernel, dim3((unsigned)(((int64_t)g.M * g.N + 255) / 256)),
+                       dim3(256), 0, s, g);
   return hipGetLastError();
 }
 
@@ -626,6 +791,7 @@ hipError_t launch_colsum(const float *in, int64_t rows, int64_t cols, float *par
 }
 
 int bw_ranges(int L) { return (L + kRT - 1) / kRT; }
+int bw_conv_strips(int L) { return (L + kStrip - 1) / kStrip; }
 int64_t bw_colsum_blocks(int64_t rows) { return (rows + kColRows - 1) / kColRows; }
 
 template <typename T>
@@ -633,7 +799,9 @@ hipError_t bw_dispatch(const BwArgs &a, int stage, hipStream_t s) {
   const int64_t TD = (int64_t)a.B * a.L * a.D;
   switch (stage) {
     case 0:
-      hipLaunchKernelGGL(bw_conv_u_kernel<T>, dim3(grid_for(TD)), dim3(256), 0, s, a);
+      if (a.K == 2) hipLaunchKernelGGL((bw_conv_u_kernel<T, 2>), dim3(grid_for(TD / 4)), dim3(256), 0, s, a);
+      else if (a.K == 3) hipLaunchKernelGGL((bw_conv_u_kernel<T, 3>), dim3(grid_for(TD / 4)), dim3(256), 0, s, a);
+      else hipLaunchKernelGGL((bw_conv_u_kernel<T, 4>), dim3(grid_for(TD / 4)), dim3(256), 0, s, a);
       break;
     case 1:
       hipLaunchKernelGGL(bw_pointwise_kernel<T>, dim3(grid_for(TD)), dim3(256), 0, s, a);
@@ -654,17 +822,17 @@ hipError_t bw_dispatch(const BwArgs &a, int stage, hipStream_t s) {
     case 3:
       hipLaunchKernelGGL(bw_norm_bwd_kernel, dim3((unsigned)((a.T + 3) / 4)), dim3(256), 0, s, a);
       break;
-    case 4:
-      hipLaunchKernelGGL(bw_dq_kernel<T>, dim3(grid_for(TD)), dim3(256), 0, s, a);
-      break;
     case 5: {
-      const int nb = (a.L + kColRows - 1) / kColRows;
-      hipLaunchKernelGGL(bw_conv_bwd_kernel<T>, dim3((unsigned)((a.D + 255) / 256), (unsigned)nb, (unsigned)a.B),
-                         dim3(256), 0, s, a);
-      hipLaunchKernelGGL(bw_conv_final_kernel, dim3((unsigned)((a.D + 255) / 256)), dim3(256), 0, s,
-                         a, a.B * nb);
+      const int64_t nth = (int64_t)a.B * ((a.L + kStrip - 1) / kStrip) * (a.D / 4);
+      const dim3 grid((unsigned)((nth + 255) / 256));
+      if (a.K == 2) hipLaunchKernelGGL((bw_conv_bwd_kernel<T, 2>), grid, dim3(256), 0, s, a);
+      else if (a.K == 3) hipLaunchKernelGGL((bw_conv_bwd_kernel<T, 3>), grid, dim3(256), 0, s, a);
+      else hipLaunchKernelGGL((bw_conv_bwd_kernel<T, 4>), grid, dim3(256), 0, s, a);
       break;
     }
+    case 7:
+      hipLaunchKernelGGL(bw_conv_scatter_kernel, dim3((unsigned)((a.D + 255) / 256)), dim3(256), 0, s, a);
+      break;
     case 6: {  // weights to fp32 (bf16 I/O)
       const int W = a.R + 32;
       hipLaunchKernelGGL(to_f32_kernel<T>, dim3(grid_for((int64_t)W * a.D)), dim3(256), 0, s,

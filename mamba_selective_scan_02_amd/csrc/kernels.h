@@ -139,24 +139,33 @@ struct BwArgs {
   float *dD_part;                           // [B, nr, D]
   float *bc_part, *dbc;                     // [T, D/64, 32], [T, 32]
   float *ddtn, *dxd, *gc;                   // [T, R], [T, R+32], [T, R+32]
-  float *conv_part;                         // [B, ceil(L/1024), D, 5]
+  float *conv_part;                         // [B, conv strips, D, 5]
+  float *conv_sum;                          // [D, 5]
   // outputs
   void *dxz;
   float *d_conv_w, *d_conv_b, *d_ssm_state, *d_conv_state;
 };
-// stage: 0 u; 1 dt / sigmoid / dys; 2 range transfers + carries + reverse scan + dB|dC;
-// 3 RMSNorm backward; 4 SiLU'; 5 conv backward + conv weight sums; 6 weights to fp32
+// stage: 0 u; 1 dt / sigmoid / dys; 2 range transfers + carries + reverse scan + dB|dC + dz;
+// 3 RMSNorm backward; 5 conv + SiLU backward (dx, partials); 6 weights to fp32; 7 conv
+// weight gradients from the column sums of the partials
 hipError_t launch_backward_stage(mm_dtype dt, const BwArgs &a, int stage, hipStream_t s);
 int bw_ranges(int L);
+int bw_conv_strips(int L);
 int64_t bw_colsum_blocks(int64_t rows);
 
-// C[m, n] (+)= sum_k A[m sam + k sak] B[k sbk + n sbn], fp32 (16x16x4 fp32 MFMA)
+// C[m scm + n scn] (+)= sum_k A[m sam + k sak] B[k sbk + n sbn], fp32 (16x16x4 fp32 MFMA)
+// With part != null the K range may be split over up to kMaxSplit workgroups per tile (for
+// short-and-wide products whose K is long); part then holds kMaxSplit * M * N floats and the
+// splits are summed in a fixed order.
+constexpr int kMaxSplit = 8;
 struct GemmF32Args {
   const float *A, *B;
   float *C;
   int M, N, K;
-  int64_t sam, sak, sbk, sbn, ldc;
+  int64_t sam, sak, sbk, sbn, scm, scn;
   int accumulate;
+  float *part = nullptr;
+  int split = 1;
 };
 hipError_t launch_gemm_f32(const GemmF32Args &g, hipStream_t s);
 // out[c] = sum over rows of in[rows, cols] (fixed order); part >= bw_colsum_blocks(rows) * cols

@@ -110,3 +110,8 @@ def test_backward_is_deterministic():
     for k in g1:
         if g1[k] is not None:
             assert torch.equal(g1[k], g2[k]), k
+
+
+def test_bf16_long_sequence_split_k():
+    # 8192 tokens: 16 ranges; the weight gradients' products (K = tokens) are split 4 ways
+    _case(synth.MixerConfig("bwd_bf16_8k", 1, 8192, 256, 16, 4, 64, "bf16"), 323)
