@@ -8,7 +8,8 @@ x_proj, RMSNorm, dt_proj+softplus, selective scan with D feed-through and SiLU(z
 final conv/SSM states. Inputs are synthetic, seeded, resident in HBM before timing.
 The decode leg times 512 batched decode steps (B=256, d_inner=8192) after a 1024-token
 prefill seeds the states. The layer leg times mamba_layer_prefill (pre-RMSNorm, in_proj
-4096 -> 16384, the mixer, out_proj 8192 -> 4096 with the residual) on the same 128K tokens.
+4096 -> 16384, the mixer, out_proj 8192 -> 4096 with the residual) on the same 128K tokens;
+the backward leg times mamba_mixer_prefill_backward (gradients of the prefill) on them.
 Prints one JSON line.
 """
 from __future__ import annotations
@@ -261,6 +262,44 @@ def layer_leg(args, mm, steps=None):
                 "out_proj": stage_view(st["out_proj"], None, 2 * T * D * Dm)}}
 
 
+def backward_leg(args, mm, steps=None):
+    """mamba_mixer_prefill_backward over the 128K workload (dy ~ N(0, 1), seeded)."""
+    cfg = synth.CONFIGS[PREFILL_WORKLOAD]
+    seed = synth.seed_for(PREFILL_WORKLOAD)
+    dev = "cuda"
+    p = synth.make_params(cfg, seed, dev)
+    xz = synth.make_xz(cfg, seed, dev)
+    dy = synth.make_xz(cfg, seed + 1, dev)[:, :, :cfg.d_inner].contiguous()
+    shape = mm.shape_of(xz, p, eps=cfg.rms_eps)
+    ws = mm.alloc_workspace(mm.backward_workspace_bytes(shape), dev)
+    timer = mm.StageTimer()
+    steps = max(1, min(args.steps, 5)) if steps is None else steps
+    grads = mm.prefill_backward(xz, p, dy, workspace=ws, eps=cfg.rms_eps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        mm.prefill_backward(xz, p, dy, grads=grads, workspace=ws, eps=cfg.rms_eps, timer=timer)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    st = {k: v[0] / max(v[1], 1) for k, v in timer.read().items() if v[1]}
+    T, D, N, R = cfg.batch * cfg.seqlen, cfg.d_inner, cfg.d_state, cfg.dt_rank
+    ms = wall * 1e3 / steps
+    W = R + 2 * N
+    # six products: x_proj, its input and weight gradients (inner size W), and the same three
+    # for dt_proj (R)
+    gemm_flops = 2 * T * D * (3 * W + 3 * R)
+    return {"metric": "mixer prefill backward tokens/sec at L=128K", "value": T / (ms * 1e-3),
+            "unit": "tokens/s", "ms_per_step": ms, "steps": steps,
+            "config": {"workload": PREFILL_WORKLOAD, "d_inner": D, "dt_rank": R, "d_state": N,
+                       "io_dtype": "bf16", "arithmetic": "f32"},
+            "stages_ms_per_step": st,
+            # the reverse scan stage: state updates per second (each (token, channel, state)
+            # is recomputed twice forward and walked once backward)
+            "scan_state_updates_per_s": T * D * N / (st["bwd_scan"] * 1e-3),
+            "gemm_algorithmic_flops": gemm_flops,
+            "gemm_TFLOPs_in_recompute_and_proj": gemm_flops / ((st["bwd_recompute"] + st["bwd_proj"]) * 1e-3) / 1e12}
+
+
 def cpu_baseline(xz, p, cfg, tokens: int):
     """The fp64 oracle, as it stands, on the first `tokens` tokens of the same workload."""
     import numpy as np
@@ -301,6 +340,10 @@ def profile_run(args, mm):
         layer_leg(args, mm, steps=2)
         torch.cuda.synchronize()
         print("[profile] layer done", file=sys.stderr, flush=True)
+    if not args.no_backward:
+        backward_leg(args, mm, steps=1)
+        torch.cuda.synchronize()
+        print("[profile] backward done", file=sys.stderr, flush=True)
 
 
 def main():
@@ -312,6 +355,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-layer", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--profile", action="store_true",
                     help="short run for rocprofv3: a few prefill and decode steps plus one plain "
                          "1 GiB device copy (the reference kernel for counter calibration)")
@@ -345,6 +389,9 @@ def main():
     if not args.no_layer:
         print("[bench] layer leg", file=sys.stderr, flush=True)
         line["layer"] = layer_leg(args, mm)
+    if not args.no_backward:
+        print("[bench] backward leg", file=sys.stderr, flush=True)
+        line["backward"] = backward_leg(args, mm)
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(xz, p, cfg, args.cpu_tokens)
