@@ -9,8 +9,8 @@ final conv/SSM states. Inputs are synthetic, seeded, resident in HBM before timi
 The decode leg times 512 batched decode steps (B=256, d_inner=8192) after a 1024-token
 prefill seeds the states. The layer leg times mamba_layer_prefill (pre-RMSNorm, in_proj
 4096 -> 16384, the mixer, out_proj 8192 -> 4096 with the residual) on the same 128K tokens;
-the backward leg times mamba_mixer_prefill_backward (gradients of the prefill) on them.
-Prints one JSON line.
+the backward leg times mamba_mixer_prefill_backward (gradients of the prefill) on them; the
+sweep leg repeats the prefill at d_state 8, 16, 32 and 64. Prints one JSON line.
 """
 from __future__ import annotations
 
@@ -262,6 +262,38 @@ def layer_leg(args, mm, steps=None):
                 "out_proj": stage_view(st["out_proj"], None, 2 * T * D * Dm)}}
 
 
+def state_sweep_leg(args, mm, sizes=(8, 16, 32, 64)):
+    """The 128K prefill at d_state 8, 16, 32, 64 (same widths; A[i, n] = -(n + 1))."""
+    base = synth.CONFIGS[PREFILL_WORKLOAD]
+    seed = synth.seed_for(PREFILL_WORKLOAD)
+    out = {}
+    steps = max(1, min(args.steps, 3))
+    for N in sizes:
+        cfg = base.with_(d_state=N, name=f"{PREFILL_WORKLOAD}_N{N}")
+        p = synth.make_params(cfg, seed, "cuda")
+        xz = synth.make_xz(cfg, seed, "cuda")
+        y = torch.empty(cfg.batch, cfg.seqlen, cfg.d_inner, dtype=cfg.torch_dtype, device="cuda")
+        shape = mm.shape_of(xz, p, eps=cfg.rms_eps)
+        ws = mm.alloc_workspace(mm.prefill_workspace_bytes(shape), "cuda")
+        timer = mm.StageTimer()
+        mm.prefill(xz, p, y=y, workspace=ws, eps=cfg.rms_eps)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            mm.prefill(xz, p, y=y, workspace=ws, eps=cfg.rms_eps, timer=timer)
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / steps
+        st = {k: v[0] / max(v[1], 1) for k, v in timer.read().items() if v[1]}
+        T = cfg.batch * cfg.seqlen
+        out[str(N)] = {"tokens_per_s": T / (ms * 1e-3), "ms_per_step": ms,
+                       "scan_ms": st["selective_scan"],
+                       "scan_state_updates_per_s": T * cfg.d_inner * N / (st["selective_scan"] * 1e-3),
+                       "stages_ms_per_step": st}
+        del p, xz, y, ws
+        torch.cuda.empty_cache()
+    return {"workload": PREFILL_WORKLOAD, "steps": steps, "by_d_state": out}
+
+
 def backward_leg(args, mm, steps=None):
     """mamba_mixer_prefill_backward over the 128K workload (dy ~ N(0, 1), seeded)."""
     cfg = synth.CONFIGS[PREFILL_WORKLOAD]
@@ -356,6 +388,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-layer", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--profile", action="store_true",
                     help="short run for rocprofv3: a few prefill and decode steps plus one plain "
                          "1 GiB device copy (the reference kernel for counter calibration)")
@@ -392,6 +425,9 @@ def main():
     if not args.no_backward:
         print("[bench] backward leg", file=sys.stderr, flush=True)
         line["backward"] = backward_leg(args, mm)
+    if not args.no_sweep:
+        print("[bench] d_state sweep", file=sys.stderr, flush=True)
+        line["d_state_sweep"] = state_sweep_leg(args, mm)
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(xz, p, cfg, args.cpu_tokens)

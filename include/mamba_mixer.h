@@ -80,7 +80,9 @@ enum {
 };
 
 /*
- * Problem size. Limits of this build (else MM_ERR_UNSUPPORTED): d_state == 16;
+ * Problem size. Limits of this build (else MM_ERR_UNSUPPORTED): d_state in {8, 16, 32, 64}
+ * (16, the Jamba configuration, runs the tuned kernels; the other sizes a general
+ * time-parallel scan, and the scan-selection flags apply to 16 only; the backward takes 16);
  * 2 <= d_conv <= 4; d_inner % 64 == 0; with MM_BF16, dt_rank % 64 == 0 and
  * d_inner % 128 == 0; with MM_F32, 1 <= dt_rank <= 1024. seqlen >= 1 (prefill),
  * seqlen == 1 (decode). rms_eps > 0 is the RMSNorm epsilon.

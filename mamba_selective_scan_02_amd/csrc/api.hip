@@ -19,7 +19,7 @@ struct Workspace {
   bool tiled_dtproj; // bf16: token-stationary dt_proj kernel
   bool fast_decode;  // bf16 decode step: range-split x_proj, fused update (no u / xdbl buffers)
   int dec_ranges, dec_range_ch;
-  size_t u, u_lo, xdbl, part, dtlow, dtlow_lo, bc, dt, total;
+  size_t u, u_lo, xdbl, part, dtlow, dtlow_lo, bc, dt, gP, gS, total;
 };
 
 // Byte offsets of the prefill intermediates for T = batch * seqlen tokens.
@@ -57,6 +57,11 @@ Workspace layout(const mm_shape &s, bool decode) {
   w.dtlow_lo = o; if (bf) o += up(T * s.dt_rank * 2);
   w.bc = o; o += up(T * 2 * s.d_state * 4);
   w.dt = o; o += up(T * s.d_inner * (bf ? 2 : 4));
+  // d_state != 16: per-range transfers of the general scan
+  const size_t gsz = s.d_state != 16
+                         ? (size_t)s.batch * scan_n_ranges(s.seqlen) * s.d_inner * s.d_state * 4 : 0;
+  w.gP = o; o += up(gsz);
+  w.gS = o; o += up(gsz);
   w.total = o;
   return w;
 }
@@ -74,7 +79,8 @@ mm_status check_shape(const mm_shape *s, bool decode) {
   if ((s->flags & MM_FLAG_SCAN_SEQUENTIAL) && (s->flags & MM_FLAG_SCAN_CHUNKED))
     return MM_ERR_INVALID_ARG;
   if (decode && s->seqlen != 1) return MM_ERR_INVALID_ARG;
-  if (s->d_state != 16 || s->d_conv < 2 || s->d_conv > 4 || s->d_inner % 64 != 0)
+  if ((s->d_state != 16 && !scan_n_supported(s->d_state)) || s->d_conv < 2 || s->d_conv > 4 ||
+      s->d_inner % 64 != 0)
     return MM_ERR_UNSUPPORTED;
   if (s->io_dtype == MM_BF16 && (s->dt_rank % 64 != 0 || s->d_inner % 128 != 0))
     return MM_ERR_UNSUPPORTED;
@@ -244,7 +250,15 @@ mm_status run_mixer(const mm_shape *s, const mm_params *p, const void *xz, void 
                 (s->flags & MM_FLAG_ZOH_B) ? 1 : 0,
                 (s->flags & MM_FLAG_SCAN_SEQUENTIAL) ? 1 : (s->flags & MM_FLAG_SCAN_CHUNKED) ? 2 : 0,
                 B, L, D, N};
-    MM_TRY(launch_scan(dt, sa, st));
+    if (N == 16) {
+      MM_TRY(launch_scan(dt, sa, st));
+    } else {
+      sa.u = u;
+      sa.u_lo = u_lo;
+      sa.gP = (float *)(ws + w.gP);
+      sa.gS = (float *)(ws + w.gS);
+      MM_TRY(launch_scan_n(dt, sa, st));
+    }
   }
   if (conv_state) {
     // last: the conv and scan kernels above read the carried conv state
@@ -405,7 +419,8 @@ mm_status check_backward(const mm_shape *s, const mm_params *p, const void *xz, 
                          const mm_grads *g) {
   mm_status r = check_shape(s, false);
   if (r != MM_OK) return r;
-  if (s->dt_rank > 1024) return MM_ERR_UNSUPPORTED;
+  // the backward's lanes are (channel, 16 states)
+  if (s->dt_rank > 1024 || s->d_state != 16) return MM_ERR_UNSUPPORTED;
   r = check_params(p);
   if (r != MM_OK) return r;
   if (!xz || !dy || !g || !aligned(xz) || !aligned(dy)) return MM_ERR_INVALID_ARG;
@@ -548,7 +563,7 @@ mm_status mamba_mixer_prefill(const mm_shape *s, const mm_params *p, const void 
 }
 
 size_t mm_backward_workspace_bytes(const mm_shape *s) {
-  if (check_shape(s, false) != MM_OK || s->dt_rank > 1024) return 0;
+  if (check_shape(s, false) != MM_OK || s->dt_rank > 1024 || s->d_state != 16) return 0;
   return bw_layout(*s).total;
 }
 

@@ -189,7 +189,14 @@ struct ScanArgs {
   int zoh;
   int force;            // 0: pick by size; 1: sequential kernel; 2: time-parallel kernel
   int B, L, D, N;
+  // d_state != 16 (scan_n.hip): u from the conv kernel (fp32, or bf16 high + low parts) and
+  // the per-range transfers [B, ranges, D, N] (P, and S / the range start states)
+  const void *u = nullptr, *u_lo = nullptr;
+  float *gP = nullptr, *gS = nullptr;
 };
 hipError_t launch_scan(mm_dtype dt, const ScanArgs &a, hipStream_t s);
+bool scan_n_supported(int N);
+int scan_n_ranges(int L);
+hipError_t launch_scan_n(mm_dtype dt, const ScanArgs &a, hipStream_t s);
 
 }  // namespace mm

@@ -37,13 +37,20 @@ __global__ __launch_bounds__(256) void norm_kernel(const float *__restrict__ xdb
     // bf16 mode: the low part carries v - bf16(v) for dt_proj's second MFMA pass
     if (sizeof(T) == 2) io<T>::st(dtlow_lo + t * R + r, v - bf2f(f2bf(v)));
   }
-  // lanes [0, N): B ; lanes [N, 2N): C  (N <= 32)
-  const bool isB = lane < N, isC = lane >= N && lane < 2 * N;
-  const float v = (isB || isC) ? row[R + lane] : 0.f;
-  const float sb = wave_sum(isB ? v * v : 0.f);
-  const float sc = wave_sum(isC ? v * v : 0.f);
-  if (isB) bc[t * 2 * N + lane] = v * (1.0f / sqrtf(sb / (float)N + eps)) * g_B[lane];
-  if (isC) bc[t * 2 * N + lane] = v * (1.0f / sqrtf(sc / (float)N + eps)) * g_C[lane - N];
+  // B = row[R, R+N), C = row[R+N, R+2N); lane j takes elements j, j + 64, ... (N <= 64)
+  float sb = 0.f, sc = 0.f;
+  for (int j = lane; j < N; j += 64) {
+    const float vb = row[R + j], vc = row[R + N + j];
+    sb = __builtin_fmaf(vb, vb, sb);
+    sc = __builtin_fmaf(vc, vc, sc);
+  }
+  sb = wave_sum(sb);
+  sc = wave_sum(sc);
+  const float ib = 1.0f / sqrtf(sb / (float)N + eps), ic = 1.0f / sqrtf(sc / (float)N + eps);
+  for (int j = lane; j < N; j += 64) {
+    bc[t * 2 * N + j] = row[R + j] * ib * g_B[j];
+    bc[t * 2 * N + N + j] = row[R + N + j] * ic * g_C[j];
+  }
 }
 
 }  // namespace

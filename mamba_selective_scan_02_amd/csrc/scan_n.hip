@@ -1,0 +1,231 @@
+// Selective scan + D feed-through + SiLU(z) gate for state sizes other than 16 (d_state 8, 32,
+// 64: the state-size sweep around the N = 16 of the Jamba configuration).
+//
+// Same recurrence as scan.hip (Jamba analysis page, "The Mamba Layer": ZOH equation, discrete
+// recurrence, the D u feed-through of the continuous SSM; Mamba-1 gate), cut into ranges of
+// kGR tokens and composed with the page's associative operator ("Parallel training via the
+// parallel scan": h -> a h + b composes as (a, b) then (c, d) = (ac, ad + b)):
+//   scanN_transfer_kernel  per (range, channel, state): the range's transfer h -> P h + S from
+//                          zero (P = prod exp(dt A), S = the local end state)
+//   scanN_carry_kernel     per (sequence, channel, state), sequential over ranges: each range's
+//                          true start state (written over S) and the final state
+//   scanN_replay_kernel    per range: the recurrence from the true start state, y_t = C_t . h_t
+//                          summed over the N state lanes (DPP mirrors within 8 / 16 lanes, lane
+//                          swaps across 16-lane rows), y = (y + D u) SiLU(z)
+// Lanes are (channel, state): a 256-thread workgroup covers 256 / N channels. Each kGS-token
+// sub-block's inputs are staged in LDS by coalesced loads issued one sub-block ahead. u comes
+// from the conv kernel's output (fp32, or bf16 high + low parts: ~2^-17 relative).
+#include "common.h"
+#include "kernels.h"
+
+namespace mm {
+namespace {
+
+constexpr int kGR = 512;   // tokens per range
+constexpr int kGS = 32;    // tokens per staged sub-block
+
+template <typename T> struct DeltaG;
+template <> struct DeltaG<float> {
+  static __device__ __forceinline__ float ld(const void *p, int64_t e) { return ((const float *)p)[e]; }
+};
+template <> struct DeltaG<bf16_t> {
+  static __device__ __forceinline__ float ld(const void *p, int64_t e) {
+    return (float)((const _Float16 *)p)[e];
+  }
+};
+template <typename T> __device__ __forceinline__ float ld_u(const ScanArgs &a, int64_t e);
+template <> __device__ __forceinline__ float ld_u<float>(const ScanArgs &a, int64_t e) {
+  return ((const float *)a.u)[e];
+}
+template <> __device__ __forceinline__ float ld_u<bf16_t>(const ScanArgs &a, int64_t e) {
+  return bf2f(((const bf16_t *)a.u)[e]) + bf2f(((const bf16_t *)a.u_lo)[e]);
+}
+
+// sum over the N lanes of a state group (groups are aligned to N lanes); every lane gets it
+template <int N>
+__device__ __forceinline__ float sum_states(float v) {
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));   // ^1
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));   // ^2
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false));  // 7-i
+  if (N >= 16)
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, false));  // 15-i
+  if (N >= 32) v += __shfl_xor(v, 16, 64);
+  if (N >= 64) v += __shfl_xor(v, 32, 64);
+  return v;
+}
+
+template <typename T, int N, bool ZOH>
+__global__ __launch_bounds__(256) void scanN_transfer_kernel(ScanArgs a, int nr) {
+  constexpr int CPW = 256 / N;             // channels per workgroup
+  constexpr int F = kGS * CPW;             // floats of a staged [kGS][CPW] array
+  constexpr int ST = 2 * F + kGS * N;      // dt | u | B
+  constexpr int NQ = (ST + 255) / 256;
+  __shared__ float st_s[NQ * 256];
+  const int ncg = a.D / CPW;
+  const int cg = blockIdx.x % ncg;
+  const int r = (blockIdx.x / ncg) % nr;
+  const int b = blockIdx.x / (ncg * nr);
+  const int tid = threadIdx.x, n = tid % N, c = tid / N, i = cg * CPW + c;
+  const int t0 = r * kGR, t1 = min(a.L, t0 + kGR);
+  const int nsb = (t1 - t0 + kGS - 1) / kGS;
+  const int64_t tb = (int64_t)b * a.L;
+  const float An = a.A[(int64_t)i * N + n];
+  const float A2 = An * kLog2e, iA = 1.0f / An;
+  float pf[NQ];
+  auto fetch = [&](int j) {
+    const int tj = t0 + j * kGS;
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      const int e = tid + 256 * q;
+      float v = 0.f;
+      if (e < 2 * F) {
+        const int off = e % F, k = off / CPW, ch = off % CPW;
+        const int64_t x = (tb + tj + k) * a.D + cg * CPW + ch;
+        if (tj + k < t1) v = e < F ? DeltaG<T>::ld(a.delta, x) : ld_u<T>(a, x);
+      } else if (e < ST) {
+        const int off = e - 2 * F, k = off / N, nn = off % N;
+        if (tj + k < t1) v = a.bc[(tb + tj + k) * 2 * N + nn];
+      }
+      pf[q] = v;
+    }
+  };
+  const float *s_dt = st_s, *s_u = st_s + F, *s_b = st_s + 2 * F;
+  float P = 1.f, S = 0.f;
+  fetch(0);
+  for (int j = 0; j < nsb; ++j) {
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) st_s[tid + 256 * q] = pf[q];
+    __syncthreads();
+    if (j + 1 < nsb) fetch(j + 1);
+    const int tj = t0 + j * kGS;
+#pragma unroll
+    for (int k = 0; k < kGS; ++k) {
+      if (tj + k < t1) {
+        const float dtv = s_dt[k * CPW + c];
+        const float av = exp2_hw(dtv * A2);
+        const float bb = (ZOH ? expm1_f(dtv * An) * iA : dtv) * s_b[k * N + n];
+        S = __builtin_fmaf(av, S, bb * s_u[k * CPW + c]);
+        P *= av;
+      }
+    }
+  }
+  const int64_t o = (((int64_t)b * nr + r) * a.D + i) * N + n;
+  a.gP[o] = P;
+  a.gS[o] = S;
+}
+
+template <int N>
+__global__ __launch_bounds__(256) void scanN_carry_kernel(ScanArgs a, int nr) {
+  const int64_t e = blockIdx.x * 256ll + threadIdx.x;
+  if (e >= (int64_t)a.B * a.D * N) return;
+  const int64_t b = e / ((int64_t)a.D * N), in = e % ((int64_t)a.D * N);
+  float h = (a.state_valid && a.state) ? a.state[e] : 0.f;
+  for (int r = 0; r < nr; ++r) {
+    const int64_t o = (b * nr + r) * a.D * N + in;
+    const float s = a.gS[o];
+    a.gS[o] = h;
+    h = __builtin_fmaf(a.gP[o], h, s);
+  }
+  if (a.state) a.state[e] = h;
+}
+
+template <typename T, int N, bool ZOH>
+__global__ __launch_bounds__(256) void scanN_replay_kernel(ScanArgs a, int nr) {
+  constexpr int CPW = 256 / N;
+  constexpr int F = kGS * CPW;
+  constexpr int ST = 3 * F + kGS * 2 * N;  // dt | u | z | B|C
+  constexpr int NQ = (ST + 255) / 256;
+  __shared__ float st_s[NQ * 256];
+  const int ncg = a.D / CPW;
+  const int cg = blockIdx.x % ncg;
+  const int r = (blockIdx.x / ncg) % nr;
+  const int b = blockIdx.x / (ncg * nr);
+  const int tid = threadIdx.x, n = tid % N, c = tid / N, i = cg * CPW + c;
+  const int t0 = r * kGR, t1 = min(a.L, t0 + kGR);
+  const int nsb = (t1 - t0 + kGS - 1) / kGS;
+  const int64_t tb = (int64_t)b * a.L;
+  const float An = a.A[(int64_t)i * N + n];
+  const float A2 = An * kLog2e, iA = 1.0f / An;
+  const float Dv = a.Dskip[i];
+  float pf[NQ];
+  auto fetch = [&](int j) {
+    const int tj = t0 + j * kGS;
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      const int e = tid + 256 * q;
+      float v = 0.f;
+      if (e < 3 * F) {
+        const int off = e % F, k = off / CPW, ch = off % CPW;
+        const int64_t tok = tb + tj + k;
+        const int ic = cg * CPW + ch;
+        if (tj + k < t1) {
+          if (e < F) v = DeltaG<T>::ld(a.delta, tok * a.D + ic);
+          else if (e < 2 * F) v = ld_u<T>(a, tok * a.D + ic);
+          else v = io<T>::ld((const T *)a.xz + tok * 2 * a.D + a.D + ic);
+        }
+      } else if (e < ST) {
+        const int off = e - 3 * F, k = off / (2 * N), nn = off % (2 * N);
+        if (tj + k < t1) v = a.bc[(tb + tj + k) * 2 * N + nn];
+      }
+      pf[q] = v;
+    }
+  };
+  const float *s_dt = st_s, *s_u = st_s + F, *s_z = st_s + 2 * F, *s_bc = st_s + 3 * F;
+  float h = a.gS[(((int64_t)b * nr + r) * a.D + i) * N + n];
+  fetch(0);
+  for (int j = 0; j < nsb; ++j) {
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) st_s[tid + 256 * q] = pf[q];
+    __syncthreads();
+    if (j + 1 < nsb) fetch(j + 1);
+    const int tj = t0 + j * kGS;
+#pragma unroll
+    for (int k = 0; k < kGS; ++k) {
+      if (tj + k < t1) {
+        const float dtv = s_dt[k * CPW + c], uv = s_u[k * CPW + c];
+        const float av = exp2_hw(dtv * A2);
+        const float bb = (ZOH ? expm1_f(dtv * An) * iA : dtv) * s_bc[k * 2 * N + n];
+        h = __builtin_fmaf(av, h, bb * uv);
+        const float ys = sum_states<N>(s_bc[k * 2 * N + N + n] * h);
+        if (n == 0)
+          io<T>::st((T *)a.y + (tb + tj + k) * a.D + i,
+                    __builtin_fmaf(Dv, uv, ys) * silu_f(s_z[k * CPW + c]));
+      }
+    }
+  }
+}
+
+template <typename T, int N, bool ZOH>
+hipError_t launch_n(const ScanArgs &a, hipStream_t s) {
+  const int nr = (a.L + kGR - 1) / kGR;
+  const unsigned grid = (unsigned)((int64_t)a.B * nr * (a.D / (256 / N)));
+  hipLaunchKernelGGL((scanN_transfer_kernel<T, N, ZOH>), dim3(grid), dim3(256), 0, s, a, nr);
+  const int64_t nc = (int64_t)a.B * a.D * N;
+  hipLaunchKernelGGL((scanN_carry_kernel<N>), dim3((unsigned)((nc + 255) / 256)), dim3(256), 0, s, a, nr);
+  hipLaunchKernelGGL((scanN_replay_kernel<T, N, ZOH>), dim3(grid), dim3(256), 0, s, a, nr);
+  return hipGetLastError();
+}
+
+template <typename T, bool ZOH>
+hipError_t dispatch_n(const ScanArgs &a, hipStream_t s) {
+  switch (a.N) {
+    case 8: return launch_n<T, 8, ZOH>(a, s);
+    case 32: return launch_n<T, 32, ZOH>(a, s);
+    case 64: return launch_n<T, 64, ZOH>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+bool scan_n_supported(int N) { return N == 8 || N == 32 || N == 64; }
+int scan_n_ranges(int L) { return (L + kGR - 1) / kGR; }
+
+hipError_t launch_scan_n(mm_dtype dt, const ScanArgs &a, hipStream_t s) {
+  if (dt == MM_BF16) return a.zoh ? dispatch_n<bf16_t, true>(a, s) : dispatch_n<bf16_t, false>(a, s);
+  return a.zoh ? dispatch_n<float, true>(a, s) : dispatch_n<float, false>(a, s);
+}
+
+}  // namespace mm

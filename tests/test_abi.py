@@ -74,7 +74,7 @@ def test_workspace_size_formula():
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(d_state=8), mm.MM_ERR_UNSUPPORTED),
+    (dict(d_state=12), mm.MM_ERR_UNSUPPORTED),
     (dict(d_conv=5), mm.MM_ERR_UNSUPPORTED),
     (dict(d_inner=96), mm.MM_ERR_UNSUPPORTED),
     (dict(dt_rank=100), mm.MM_ERR_UNSUPPORTED),

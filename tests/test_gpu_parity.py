@@ -226,3 +226,45 @@ def test_outputs_are_deterministic():
     y2 = mm.prefill(xz, p)
     torch.cuda.synchronize()
     assert torch.equal(y1, y2)
+
+
+# d_state other than 16: the general path (conv, x_proj, RMSNorm, dt_proj kernels) and the
+# general time-parallel scan (512-token ranges, their transfers composed in order)
+@pytest.mark.parametrize("N", [8, 32, 64])
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_state_size_sweep_prefill(N, io):
+    if io == "f32":
+        cfg = TINY.with_(batch=2, seqlen=77, d_state=N, name=f"f32_N{N}")
+    else:
+        # 1100 tokens: two full ranges and a ragged third
+        cfg = BF16_SMALL.with_(batch=1, seqlen=1100, d_state=N, name=f"bf16_N{N}")
+    _case(cfg, 400 + N, states=True, conv_bias=True, gamma_random=True)
+
+
+@pytest.mark.parametrize("N", [8, 64])
+def test_state_size_sweep_zoh(N):
+    _case(BF16_SMALL.with_(seqlen=600, d_state=N, name=f"bf16_zoh_N{N}"), 450 + N, states=True,
+          zoh=True)
+
+
+@pytest.mark.parametrize("N", [8, 32, 64])
+def test_state_size_sweep_decode_continues_prefill(N):
+    """Prefill, then decode steps one token at a time, at d_state N: equals the oracle's
+    prefill over all tokens."""
+    _need_gpu()
+    cfg = synth.MixerConfig(f"dec_N{N}", 8, 40, 256, N, 4, 64, "bf16")
+    seed = 460 + N
+    dev = "cuda"
+    p = synth.make_params(cfg, seed, dev, conv_bias=True)
+    xz = synth.make_xz(cfg, seed, dev)
+    cs = torch.zeros(cfg.batch, cfg.d_inner, 3, dtype=cfg.torch_dtype, device=dev)
+    ss = torch.zeros(cfg.batch, cfg.d_inner, N, dtype=torch.float32, device=dev)
+    n0 = 30
+    ys = [mm.prefill(xz[:, :n0].contiguous(), p, conv_state=cs, ssm_state=ss)]
+    for t in range(n0, cfg.seqlen):
+        ys.append(mm.decode_step(xz[:, t].contiguous(), p, cs, ss)[:, None])
+    torch.cuda.synchronize()
+    yr, csr, ssr = oracle.mixer_prefill(to64(xz), oracle.as_f64_params(p))
+    check(torch.cat(ys, dim=1), yr, "bf16", f"y (N={N}, prefill + decode)")
+    check(ss, ssr, "bf16", f"ssm_state (N={N})")
+    np.testing.assert_array_equal(to64(cs), csr)
