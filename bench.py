@@ -203,6 +203,21 @@ def decode_leg(args, mm, steps=None):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     stages = timer.read()
+    # the same steps captured once in a HIP graph and replayed (no per-step host launches)
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            for i in range(steps):
+                mm.decode_step(xs[i], p, cs, ss, y=y, workspace=ws, eps=cfg.rms_eps)
+    torch.cuda.current_stream().wait_stream(side)
+    graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    graph.replay()
+    torch.cuda.synchronize()
+    gwall = time.perf_counter() - t0
     # state read + write (fp32), conv state read + write, xz in, y out, weights once per step
     D, N, K, R, B = cfg.d_inner, cfg.d_state, cfg.d_conv, cfg.dt_rank, cfg.batch
     step_bytes = (B * D * N * 4 * 2 + B * D * (K - 1) * 2 * 2 + B * 2 * D * 2 + B * D * 2
@@ -215,6 +230,9 @@ def decode_leg(args, mm, steps=None):
             "stages_ms_per_step": {k: v[0] / max(v[1], 1) for k, v in stages.items() if v[1]},
             # the state update (conv, scan step, gate, conv-state shift): state read + write,
             # conv state read + write, xz, dt (fp16) and y
+            "graph_replay": {"steps_per_s": steps / gwall, "tokens_per_s": steps * B / gwall,
+                             "ms_per_step": gwall * 1e3 / steps,
+                             "hbm_frac_of_step": step_bytes / (gwall / steps) / 1e9 / HBM_PEAK_GBS},
             "update_stage": stage_view(stages["selective_scan"][0] / max(stages["selective_scan"][1], 1),
                                        B * D * (N * 4 * 2 + (K - 1) * 2 * 2 + 2 * 2 + 2 + 2),
                                        None, args.copy_gbs)}
