@@ -48,6 +48,22 @@ def scan_algorithmic_bytes(cfg) -> int:
     return T * D * (2 + 2 + 2 + 2) + T * 2 * N * 4 + 2 * cfg.batch * D * N * 4
 
 
+def scan_source_sha256() -> str:
+    """Hash of the scan kernel's source: scan.hip, common.h and the ScanArgs definition in
+    kernels.h (the rest of kernels.h declares other kernels)."""
+    import hashlib
+    import re
+    csrc = os.path.join(ROOT, "mamba_selective_scan_02_amd", "csrc")
+    h = hashlib.sha256()
+    for f in ("scan.hip", "common.h"):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    hdr = open(os.path.join(csrc, "kernels.h")).read()
+    m = re.search(r"struct ScanArgs \{.*?\n\};", hdr, re.S)
+    h.update(m.group(0).encode() if m else b"")
+    return h.hexdigest()
+
+
 def measured_scan_traffic():
     """HBM bytes per launch of the scan kernel from the committed rocprofv3 FETCH_SIZE /
     WRITE_SIZE passes (profiles/selective_scan_traffic.json), or None when the scan kernel's
@@ -57,11 +73,7 @@ def measured_scan_traffic():
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))["selective_scan"]
-    h = hashlib.sha256()
-    for f in ("scan.hip", "common.h", "kernels.h"):
-        with open(os.path.join(ROOT, "mamba_selective_scan_02_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
-    if h.hexdigest() != rec["source_sha256"] or rec["workload"] != PREFILL_WORKLOAD:
+    if scan_source_sha256() != rec["source_sha256"] or rec["workload"] != PREFILL_WORKLOAD:
         return None
     return rec["read_bytes"] + rec["write_bytes"]
 

@@ -13,7 +13,8 @@
 //                        stream through XOR-swizzled LDS (direct-to-LDS loads, double-buffered).
 //                        Writes the range's fp32 partial sums of xdbl.
 //   decode_norm_kernel   sums the ranges' partials in a fixed order (deterministic) and applies
-//                        the three RMSNorms: dt_low (bf16 hi + lo, for dt_proj) and B | C (fp32).
+//                        the three RMSNorms: dt_low (bf16 hi + lo, for dt_proj) and B | C (fp32);
+//                        one thread per value of the sequence for the combine and the norm.
 //   decode_update_kernel the state update: 4 lanes per channel, 4 states each as one float4, so
 //                        a wave reads / writes 1 KB of state per instruction (the step is
 //                        bound by this read-modify-write); conv recomputed; y reduced over the
@@ -156,37 +157,47 @@ __global__ __launch_bounds__(64 * kNormWaves) void decode_norm_kernel(DecodeNorm
 #pragma unroll
   for (int k = 0; k < kV; ++k) red_s[wv][lane + 64 * k] = v[k];
   __syncthreads();
-  if (wv != 0) return;
+  // thread n combines value n over the waves (fixed order), then the three sums of squares
+  // (dt_low over [0, R), B over [R, R+16), C over [R+16, R+32)) are wave sums followed by a
+  // fixed-order sum over the waves, and thread n normalises its value
+  __shared__ float ss_s[kNormWaves][3];
+  const int n = threadIdx.x;
+  float s = 0.f;
+  if (n < NX) {
+#pragma unroll
+    for (int w = 0; w < kNormWaves; ++w) s += red_s[w][n];
+  }
+  const float sq = s * s;
+  float pd = n < a.R ? sq : 0.f;
+  float pb = (n >= a.R && n < a.R + 16) ? sq : 0.f;
+  float pc = (n >= a.R + 16 && n < NX) ? sq : 0.f;
+  pd = wave_sum(pd);
+  pb = wave_sum(pb);
+  pc = wave_sum(pc);
+  if (lane == 0) {
+    ss_s[wv][0] = pd;
+    ss_s[wv][1] = pb;
+    ss_s[wv][2] = pc;
+  }
+  __syncthreads();
   float ssd = 0.f, ssb = 0.f, ssc = 0.f;
 #pragma unroll
-  for (int k = 0; k < kV; ++k) {
-    const int n = lane + 64 * k;
-    float s = red_s[0][n];
-#pragma unroll
-    for (int w = 1; w < kNormWaves; ++w) s += red_s[w][n];
-    v[k] = s;
-    if (n < a.R) ssd = __builtin_fmaf(s, s, ssd);
-    else if (n < a.R + 16) ssb = __builtin_fmaf(s, s, ssb);
-    else if (n < NX) ssc = __builtin_fmaf(s, s, ssc);
+  for (int w = 0; w < kNormWaves; ++w) {
+    ssd += ss_s[w][0];
+    ssb += ss_s[w][1];
+    ssc += ss_s[w][2];
   }
-  ssd = wave_sum(ssd);
-  ssb = wave_sum(ssb);
-  ssc = wave_sum(ssc);
   const float id = 1.0f / sqrtf(ssd / (float)a.R + a.eps);
   const float ib = 1.0f / sqrtf(ssb / 16.0f + a.eps);
   const float ic = 1.0f / sqrtf(ssc / 16.0f + a.eps);
-#pragma unroll
-  for (int k = 0; k < kV; ++k) {
-    const int n = lane + 64 * k;
-    if (n < a.R) {
-      const float x = v[k] * id * a.g_dt[n];
-      a.dtlow[(int64_t)b * a.R + n] = f2bf(x);
-      a.dtlow_lo[(int64_t)b * a.R + n] = f2bf(x - bf2f(f2bf(x)));
-    } else if (n < a.R + 16) {
-      a.bc[(int64_t)b * 32 + (n - a.R)] = v[k] * ib * a.g_B[n - a.R];
-    } else if (n < NX) {
-      a.bc[(int64_t)b * 32 + (n - a.R)] = v[k] * ic * a.g_C[n - a.R - 16];
-    }
+  if (n < a.R) {
+    const float x = s * id * a.g_dt[n];
+    a.dtlow[(int64_t)b * a.R + n] = f2bf(x);
+    a.dtlow_lo[(int64_t)b * a.R + n] = f2bf(x - bf2f(f2bf(x)));
+  } else if (n < a.R + 16) {
+    a.bc[(int64_t)b * 32 + (n - a.R)] = s * ib * a.g_B[n - a.R];
+  } else if (n < NX) {
+    a.bc[(int64_t)b * 32 + (n - a.R)] = s * ic * a.g_C[n - a.R - 16];
   }
 }
 
