@@ -12,9 +12,13 @@
 //   scanN_replay_kernel    per range: the recurrence from the true start state, y_t = C_t . h_t
 //                          summed over the N state lanes (DPP mirrors within 8 / 16 lanes, lane
 //                          swaps across 16-lane rows), y = (y + D u) SiLU(z)
-// Lanes are (channel, state): a 256-thread workgroup covers 256 / N channels. Each kGS-token
-// sub-block's inputs are staged in LDS by coalesced loads issued one sub-block ahead. u comes
-// from the conv kernel's output (fp32, or bf16 high + low parts: ~2^-17 relative).
+// Lanes are (channel, group of S consecutive states; S = 1 for N = 8, N / 16 otherwise): N / S
+// lanes per channel (8 for N = 8, 16 otherwise), so a workgroup of 256 threads covers 256 S / N
+// channels and the sum over states is one 8- or 16-lane DPP reduction per token, shared by S
+// states. (Two states per lane for N = 8 measured slower: 64 channels per workgroup raise the
+// staged prefetch to 26 registers per thread.) Each
+// kGS-token sub-block's inputs are staged in LDS by coalesced loads issued one sub-block ahead.
+// u comes from the conv kernel's output (fp32, or bf16 high + low parts: ~2^-17 relative).
 #include "common.h"
 #include "kernels.h"
 
@@ -41,39 +45,63 @@ template <> __device__ __forceinline__ float ld_u<bf16_t>(const ScanArgs &a, int
   return bf2f(((const bf16_t *)a.u)[e]) + bf2f(((const bf16_t *)a.u_lo)[e]);
 }
 
-// sum over the N lanes of a state group (groups are aligned to N lanes); every lane gets it
-template <int N>
-__device__ __forceinline__ float sum_states(float v) {
+// sum over the G lanes of a channel (G = 4, 8 or 16, groups aligned to G lanes); every lane
+// of the group receives it
+template <int G>
+__device__ __forceinline__ float sum_group(float v) {
   v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));   // ^1
   v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));   // ^2
-  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false));  // 7-i
-  if (N >= 16)
+  if (G >= 8)
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false));  // 7-i
+  if (G >= 16)
     v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, false));  // 15-i
-  if (N >= 32) v += __shfl_xor(v, 16, 64);
-  if (N >= 64) v += __shfl_xor(v, 32, 64);
   return v;
+}
+template <int N> constexpr int states_per_lane() { return N >= 16 ? N / 16 : 1; }
+
+// S consecutive floats of a staged row (8- or 16-byte LDS reads for S = 2, 4)
+template <int S>
+__device__ __forceinline__ void lds_vec(const float *p, float v[S]) {
+  if (S == 4) {
+    const float4 x = *(const float4 *)p;
+    v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+  } else if (S == 2) {
+    const float2 x = *(const float2 *)p;
+    v[0] = x.x; v[1] = x.y;
+  } else {
+    v[0] = p[0];
+  }
 }
 
 template <typename T, int N, bool ZOH>
 __global__ __launch_bounds__(256) void scanN_transfer_kernel(ScanArgs a, int nr) {
-  constexpr int CPW = 256 / N;             // channels per workgroup
+  constexpr int S = states_per_lane<N>(), G = N / S;
+  constexpr int CPW = 256 / G;             // channels per workgroup
   constexpr int F = kGS * CPW;             // floats of a staged [kGS][CPW] array
   constexpr int ST = 2 * F + kGS * N;      // dt | u | B
   constexpr int NQ = (ST + 255) / 256;
-  __shared__ float st_s[NQ * 256];
+  __shared__ __attribute__((aligned(16))) float st_s[NQ * 256];
   const int ncg = a.D / CPW;
   const int cg = blockIdx.x % ncg;
   const int r = (blockIdx.x / ncg) % nr;
   const int b = blockIdx.x / (ncg * nr);
-  const int tid = threadIdx.x, n = tid % N, c = tid / N, i = cg * CPW + c;
+  const int tid = threadIdx.x, j = tid % G, c = tid / G, i = cg * CPW + c;
+  const int n0 = j * S;                    // this lane's states n0 .. n0 + S - 1
   const int t0 = r * kGR, t1 = min(a.L, t0 + kGR);
   const int nsb = (t1 - t0 + kGS - 1) / kGS;
   const int64_t tb = (int64_t)b * a.L;
-  const float An = a.A[(int64_t)i * N + n];
-  const float A2 = An * kLog2e, iA = 1.0f / An;
+  float An[S], A2[S], iA[S], P[S], Sv[S];
+#pragma unroll
+  for (int q = 0; q < S; ++q) {
+    An[q] = a.A[(int64_t)i * N + n0 + q];
+    A2[q] = An[q] * kLog2e;
+    iA[q] = 1.0f / An[q];
+    P[q] = 1.f;
+    Sv[q] = 0.f;
+  }
   float pf[NQ];
-  auto fetch = [&](int j) {
-    const int tj = t0 + j * kGS;
+  auto fetch = [&](int jb) {
+    const int tj = t0 + jb * kGS;
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
       const int e = tid + 256 * q;
@@ -90,29 +118,36 @@ __global__ __launch_bounds__(256) void scanN_transfer_kernel(ScanArgs a, int nr)
     }
   };
   const float *s_dt = st_s, *s_u = st_s + F, *s_b = st_s + 2 * F;
-  float P = 1.f, S = 0.f;
   fetch(0);
-  for (int j = 0; j < nsb; ++j) {
+  for (int jb = 0; jb < nsb; ++jb) {
     __syncthreads();
 #pragma unroll
     for (int q = 0; q < NQ; ++q) st_s[tid + 256 * q] = pf[q];
     __syncthreads();
-    if (j + 1 < nsb) fetch(j + 1);
-    const int tj = t0 + j * kGS;
-#pragma unroll
+    if (jb + 1 < nsb) fetch(jb + 1);
+    const int tj = t0 + jb * kGS;
+#pragma unroll 4
     for (int k = 0; k < kGS; ++k) {
       if (tj + k < t1) {
-        const float dtv = s_dt[k * CPW + c];
-        const float av = exp2_hw(dtv * A2);
-        const float bb = (ZOH ? expm1_f(dtv * An) * iA : dtv) * s_b[k * N + n];
-        S = __builtin_fmaf(av, S, bb * s_u[k * CPW + c]);
-        P *= av;
+        const float dtv = s_dt[k * CPW + c], uv = s_u[k * CPW + c];
+        float Bv[S];
+        lds_vec<S>(s_b + k * N + n0, Bv);
+#pragma unroll
+        for (int q = 0; q < S; ++q) {
+          const float av = exp2_hw(dtv * A2[q]);
+          const float bb = (ZOH ? expm1_f(dtv * An[q]) * iA[q] : dtv) * Bv[q];
+          Sv[q] = __builtin_fmaf(av, Sv[q], bb * uv);
+          P[q] *= av;
+        }
       }
     }
   }
-  const int64_t o = (((int64_t)b * nr + r) * a.D + i) * N + n;
-  a.gP[o] = P;
-  a.gS[o] = S;
+  const int64_t o = (((int64_t)b * nr + r) * a.D + i) * N + n0;
+#pragma unroll
+  for (int q = 0; q < S; ++q) {
+    a.gP[o + q] = P[q];
+    a.gS[o + q] = Sv[q];
+  }
 }
 
 template <int N>
@@ -132,25 +167,34 @@ __global__ __launch_bounds__(256) void scanN_carry_kernel(ScanArgs a, int nr) {
 
 template <typename T, int N, bool ZOH>
 __global__ __launch_bounds__(256) void scanN_replay_kernel(ScanArgs a, int nr) {
-  constexpr int CPW = 256 / N;
+  constexpr int S = states_per_lane<N>(), G = N / S;
+  constexpr int CPW = 256 / G;
   constexpr int F = kGS * CPW;
   constexpr int ST = 3 * F + kGS * 2 * N;  // dt | u | z | B|C
   constexpr int NQ = (ST + 255) / 256;
-  __shared__ float st_s[NQ * 256];
+  __shared__ __attribute__((aligned(16))) float st_s[NQ * 256];
   const int ncg = a.D / CPW;
   const int cg = blockIdx.x % ncg;
   const int r = (blockIdx.x / ncg) % nr;
   const int b = blockIdx.x / (ncg * nr);
-  const int tid = threadIdx.x, n = tid % N, c = tid / N, i = cg * CPW + c;
+  const int tid = threadIdx.x, j = tid % G, c = tid / G, i = cg * CPW + c;
+  const int n0 = j * S;
   const int t0 = r * kGR, t1 = min(a.L, t0 + kGR);
   const int nsb = (t1 - t0 + kGS - 1) / kGS;
   const int64_t tb = (int64_t)b * a.L;
-  const float An = a.A[(int64_t)i * N + n];
-  const float A2 = An * kLog2e, iA = 1.0f / An;
+  float An[S], A2[S], iA[S], h[S];
+  const int64_t so = (((int64_t)b * nr + r) * a.D + i) * N + n0;
+#pragma unroll
+  for (int q = 0; q < S; ++q) {
+    An[q] = a.A[(int64_t)i * N + n0 + q];
+    A2[q] = An[q] * kLog2e;
+    iA[q] = 1.0f / An[q];
+    h[q] = a.gS[so + q];
+  }
   const float Dv = a.Dskip[i];
   float pf[NQ];
-  auto fetch = [&](int j) {
-    const int tj = t0 + j * kGS;
+  auto fetch = [&](int jb) {
+    const int tj = t0 + jb * kGS;
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
       const int e = tid + 256 * q;
@@ -172,24 +216,31 @@ __global__ __launch_bounds__(256) void scanN_replay_kernel(ScanArgs a, int nr) {
     }
   };
   const float *s_dt = st_s, *s_u = st_s + F, *s_z = st_s + 2 * F, *s_bc = st_s + 3 * F;
-  float h = a.gS[(((int64_t)b * nr + r) * a.D + i) * N + n];
   fetch(0);
-  for (int j = 0; j < nsb; ++j) {
+  for (int jb = 0; jb < nsb; ++jb) {
     __syncthreads();
 #pragma unroll
     for (int q = 0; q < NQ; ++q) st_s[tid + 256 * q] = pf[q];
     __syncthreads();
-    if (j + 1 < nsb) fetch(j + 1);
-    const int tj = t0 + j * kGS;
-#pragma unroll
+    if (jb + 1 < nsb) fetch(jb + 1);
+    const int tj = t0 + jb * kGS;
+#pragma unroll 4
     for (int k = 0; k < kGS; ++k) {
       if (tj + k < t1) {
         const float dtv = s_dt[k * CPW + c], uv = s_u[k * CPW + c];
-        const float av = exp2_hw(dtv * A2);
-        const float bb = (ZOH ? expm1_f(dtv * An) * iA : dtv) * s_bc[k * 2 * N + n];
-        h = __builtin_fmaf(av, h, bb * uv);
-        const float ys = sum_states<N>(s_bc[k * 2 * N + N + n] * h);
-        if (n == 0)
+        float Bv[S], Cv[S];
+        lds_vec<S>(s_bc + k * 2 * N + n0, Bv);
+        lds_vec<S>(s_bc + k * 2 * N + N + n0, Cv);
+        float yp = 0.f;
+#pragma unroll
+        for (int q = 0; q < S; ++q) {
+          const float av = exp2_hw(dtv * A2[q]);
+          const float bb = (ZOH ? expm1_f(dtv * An[q]) * iA[q] : dtv) * Bv[q];
+          h[q] = __builtin_fmaf(av, h[q], bb * uv);
+          yp = __builtin_fmaf(Cv[q], h[q], yp);
+        }
+        const float ys = sum_group<G>(yp);
+        if (j == 0)
           io<T>::st((T *)a.y + (tb + tj + k) * a.D + i,
                     __builtin_fmaf(Dv, uv, ys) * silu_f(s_z[k * CPW + c]));
       }
@@ -200,7 +251,8 @@ __global__ __launch_bounds__(256) void scanN_replay_kernel(ScanArgs a, int nr) {
 template <typename T, int N, bool ZOH>
 hipError_t launch_n(const ScanArgs &a, hipStream_t s) {
   const int nr = (a.L + kGR - 1) / kGR;
-  const unsigned grid = (unsigned)((int64_t)a.B * nr * (a.D / (256 / N)));
+  constexpr int G = N / states_per_lane<N>();
+  const unsigned grid = (unsigned)((int64_t)a.B * nr * (a.D / (256 / G)));
   hipLaunchKernelGGL((scanN_transfer_kernel<T, N, ZOH>), dim3(grid), dim3(256), 0, s, a, nr);
   const int64_t nc = (int64_t)a.B * a.D * N;
   hipLaunchKernelGGL((scanN_carry_kernel<N>), dim3((unsigned)((nc + 255) / 256)), dim3(256), 0, s, a, nr);
