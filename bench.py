@@ -324,6 +324,15 @@ def state_sweep_leg(args, mm, sizes=(8, 16, 32, 64)):
     return {"workload": PREFILL_WORKLOAD, "steps": steps, "by_d_state": out}
 
 
+def backward_scan_alu_peak_updates_per_s() -> float:
+    """ALU roofline of the backward's scan in state updates per second. Per (token, channel,
+    state) the backward needs the forward state (dt*A, the v_exp_f32 at half rate = 2 slots,
+    (dt*u)*B, the h FMA: 5 slots) and the reverse step (dh = C*dys + carry, dh*h_prev,
+    dh*u, d dt = (dh*h_prev*a)*A + (dh*u)*B: 3, dA += (dh*h_prev*a)*dt, dB term dh*u*dt,
+    dC term dys*h, du term dh*dt*B: 2, carry = a*dh: 12 slots): 17 issue slots."""
+    return LANES * CU * CLOCK_HZ / 17.0
+
+
 def backward_leg(args, mm, steps=None):
     """mamba_mixer_prefill_backward over the 128K workload (dy ~ N(0, 1), seeded)."""
     cfg = synth.CONFIGS[PREFILL_WORKLOAD]
@@ -358,6 +367,10 @@ def backward_leg(args, mm, steps=None):
             # the reverse scan stage: state updates per second (each (token, channel, state)
             # is recomputed twice forward and walked once backward)
             "scan_state_updates_per_s": T * D * N / (st["bwd_scan"] * 1e-3),
+            "roofline": {"bound": "alu", "kernel": "bwd_scan stage (transfers, carries, reverse scan)",
+                         "achieved": T * D * N / (st["bwd_scan"] * 1e-3),
+                         "peak": backward_scan_alu_peak_updates_per_s(), "unit": "state-updates/s",
+                         "frac": T * D * N / (st["bwd_scan"] * 1e-3) / backward_scan_alu_peak_updates_per_s()},
             "gemm_algorithmic_flops": gemm_flops,
             "gemm_TFLOPs_in_recompute_and_proj": gemm_flops / ((st["bwd_recompute"] + st["bwd_proj"]) * 1e-3) / 1e12}
 

@@ -18,7 +18,8 @@
 //                             N <= 512) tiles, any strides
 //   (norm_kernel)             the forward's RMSNorm of dt_low, B, C (fp32 mode)
 //   bw_pointwise_kernel       dt = softplus(p), sigmoid(p), dys = dy SiLU(z)
-//   bw_range_transfer_kernel  per range of kRT tokens and (channel, state): the forward
+//   bw_range_transfer_kernel  per range of kRT tokens and (channel, state), 64 channels per
+//                             workgroup with staged inputs: the forward
 //                             transfer (prod a, local end state) and the reverse one (local
 //                             a_t0 dh_t0 from zero)
 //   bw_range_carry_kernel     sequential over ranges: each range's true start state and the
@@ -169,35 +170,36 @@ __global__ __launch_bounds__(256) void bw_pointwise_kernel(BwArgs a) {
 }
 
 // ---------------------------------------------------------------- per-range transfers
-// lanes: 16 channels x 16 states per workgroup; one range of one sequence. The inputs of each
-// kSB-token sub-block (dt, u, dys of the 16 channels, B|C) are staged in LDS by coalesced
-// loads, the next sub-block's fetched into registers while the current one is processed.
-constexpr int kRTF = kSB * 16;                   // floats per staged [kSB][16] array
+// lanes: 64 channels x 16 states per workgroup (1024 threads); one range of one sequence. The
+// inputs of each kSB-token sub-block (dt, u, dys of the 64 channels: whole 256-byte rows; B|C)
+// are staged in LDS by coalesced loads, the next sub-block's fetched into registers while the
+// current one is processed.
+constexpr int kRTF = kSB * kCG;                  // floats per staged [kSB][64] array
 constexpr int kRTStage = 3 * kRTF + kSB * 32;    // dt | u | dys | B|C
-__global__ __launch_bounds__(256) void bw_range_transfer_kernel(BwArgs a) {
+__global__ __launch_bounds__(1024) void bw_range_transfer_kernel(BwArgs a) {
   __shared__ float st_s[kRTStage];
-  const int ncg = a.D / 16;
+  const int ncg = a.D / kCG;
   const int cg = blockIdx.x % ncg;
   const int r = (blockIdx.x / ncg) % a.nr;
   const int b = blockIdx.x / (ncg * a.nr);
   const int tid = threadIdx.x;
-  const int n = tid & 15, c = tid >> 4, i = cg * 16 + c;
+  const int n = tid & 15, c = tid >> 4, i = cg * kCG + c;
   const int t0 = r * kRT, t1 = min(a.L, t0 + kRT);
   const int nsb = (t1 - t0 + kSB - 1) / kSB;
   const int64_t tb = (int64_t)b * a.L;
   const float An = a.A[i * 16 + n];
-  constexpr int NQ = kRTStage / 256;
+  constexpr int NQ = kRTStage / 1024;
   float pf[NQ];
   auto fetch = [&](int j) {
     const int tj = t0 + j * kSB;
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
-      const int e = tid + 256 * q;
+      const int e = tid + 1024 * q;
       float v = 0.f;
       if (e < 3 * kRTF) {
-        const int off = e % kRTF, k = off >> 4, ch = off & 15;
+        const int off = e % kRTF, k = off >> 6, ch = off & 63;
         const float *src = e < kRTF ? a.dt : (e < 2 * kRTF ? a.u : a.dys);
-        if (tj + k < t1) v = src[(tb + tj + k) * a.D + cg * 16 + ch];
+        if (tj + k < t1) v = src[(tb + tj + k) * a.D + cg * kCG + ch];
       } else {
         const int off = e - 3 * kRTF, k = off >> 5, ch = off & 31;
         if (tj + k < t1) v = a.bc[(tb + tj + k) * 32 + ch];
@@ -207,7 +209,7 @@ __global__ __launch_bounds__(256) void bw_range_transfer_kernel(BwArgs a) {
   };
   auto stash = [&]() {
 #pragma unroll
-    for (int q = 0; q < NQ; ++q) st_s[tid + 256 * q] = pf[q];
+    for (int q = 0; q < NQ; ++q) st_s[tid + 1024 * q] = pf[q];
   };
   const float *s_dt = st_s, *s_u = st_s + kRTF, *s_dys = st_s + 2 * kRTF, *s_bc = st_s + 3 * kRTF;
 
@@ -222,10 +224,10 @@ __global__ __launch_bounds__(256) void bw_range_transfer_kernel(BwArgs a) {
 #pragma unroll
     for (int k = 0; k < kSB; ++k) {
       if (tj + k < t1) {
-        const float dtv = s_dt[k * 16 + c];
+        const float dtv = s_dt[k * kCG + c];
         const float av = exp2_hw(dtv * An * kLog2e);
         const float bb = (a.zoh ? expm1_f(dtv * An) / An : dtv) * s_bc[k * 32 + n];
-        S = __builtin_fmaf(av, S, bb * s_u[k * 16 + c]);
+        S = __builtin_fmaf(av, S, bb * s_u[k * kCG + c]);
         P *= av;
       }
     }
@@ -241,9 +243,9 @@ __global__ __launch_bounds__(256) void bw_range_transfer_kernel(BwArgs a) {
 #pragma unroll
     for (int k = kSB - 1; k >= 0; --k) {
       if (tj + k < t1) {
-        const float dtv = s_dt[k * 16 + c];
+        const float dtv = s_dt[k * kCG + c];
         const float av = exp2_hw(dtv * An * kLog2e);
-        g = av * __builtin_fmaf(s_bc[k * 32 + 16 + n], s_dys[k * 16 + c], g);
+        g = av * __builtin_fmaf(s_bc[k * 32 + 16 + n], s_dys[k * kCG + c], g);
       }
     }
   }
@@ -807,8 +809,8 @@ hipError_t bw_dispatch(const BwArgs &a, int stage, hipStream_t s) {
       hipLaunchKernelGGL(bw_pointwise_kernel<T>, dim3(grid_for(TD)), dim3(256), 0, s, a);
       break;
     case 2: {
-      hipLaunchKernelGGL(bw_range_transfer_kernel, dim3((unsigned)(a.B * a.nr * (a.D / 16))),
-                         dim3(256), 0, s, a);
+      hipLaunchKernelGGL(bw_range_transfer_kernel, dim3((unsigned)(a.B * a.nr * (a.D / kCG))),
+                         dim3(1024), 0, s, a);
       const int64_t nc = (int64_t)a.B * a.D * 16;
       hipLaunchKernelGGL(bw_range_carry_kernel, dim3((unsigned)((nc + 255) / 256)), dim3(256), 0, s, a);
       const unsigned grid = (unsigned)(a.B * a.nr * (a.D / kCG));
