@@ -369,13 +369,26 @@ mm_status layer_impl(const mm_shape *s, int d_model, const mm_layer_params *p, c
   return MM_OK;
 }
 
-// Backward workspace (fp32 arrays; T = batch * seqlen, W = dt_rank + 32, nr = ranges).
+// Backward workspace (fp32 arrays; T = batch * seqlen, W = dt_rank + 32, nr = ranges). With
+// bf16 I/O the products run on split bf16 planes (bwgemm.hip): u, d(dt_proj pre-activation)
+// and their transposes occupy arrays that are dead by then (du, dys, ys, dt; ys and dt hold
+// [D, Tp] planes, Tp = T rounded up to 64); the narrow planes and weight copies get their own.
 struct BwWs {
   size_t wx32, wdt32, u, xd, dtn, bc, dt, sig, dys, du, ys, rP, rS, rR, dA_part, dD_part, bc_part,
-      dbc, ddtn, dxd, gc, cs_part, gsum, conv_part, conv_sum, gemm_part, total;
+      dbc, ddtn, dxd, gc, cs_part, gsum, conv_part, conv_sum, gemm_part;
+  size_t wdtp, wdtT, wxT, dtn_s, dtnT, dxd_s, dxdT;   // bf16 planes (split products only)
+  size_t total;
 };
+inline int64_t pad64(int64_t v) { return (v + 63) / 64 * 64; }
+// the split-bf16 products serve bf16 I/O up to 4M tokens (32-bit lane offsets in a tile)
+inline bool bw_split_products(const mm_shape &s) {
+  return s.io_dtype == MM_BF16 && pad64((int64_t)s.batch * s.seqlen) <= (1 << 22);
+}
 BwWs bw_layout(const mm_shape &s) {
   const size_t T = (size_t)s.batch * s.seqlen, D = s.d_inner, R = s.dt_rank, W = R + 32;
+  const size_t Tp = (size_t)pad64((int64_t)T), Rp = (size_t)pad64((int64_t)R),
+               Wp = (size_t)pad64((int64_t)W);
+  const bool sp = bw_split_products(s);
   const size_t nr = (size_t)bw_ranges(s.seqlen), SR = (size_t)s.batch * nr * D * 16;
   const size_t nbT = (size_t)bw_colsum_blocks((int64_t)T);
   const size_t nbR = (size_t)bw_colsum_blocks((int64_t)s.batch * nr);
@@ -390,11 +403,11 @@ BwWs bw_layout(const mm_shape &s) {
   take(w.xd, T * W);
   take(w.dtn, T * R);
   take(w.bc, T * 32);
-  take(w.dt, T * D);
+  take(w.dt, (sp ? Tp : T) * D);
   take(w.sig, T * D);
   take(w.dys, T * D);
   take(w.du, T * D);
-  take(w.ys, T * D);
+  take(w.ys, (sp ? Tp : T) * D);
   take(w.rP, SR);
   take(w.rS, SR);
   take(w.rR, SR);
@@ -409,7 +422,16 @@ BwWs bw_layout(const mm_shape &s) {
   take(w.gsum, W);
   take(w.conv_part, nstrip * D * 5);
   take(w.conv_sum, D * 5);
-  take(w.gemm_part, (size_t)kMaxSplit * D * std::max(W, R));
+  take(w.gemm_part, (size_t)(sp ? kSpMaxSplit : kMaxSplit) * D * std::max(W, R));
+  // bf16 planes: two bf16 per float of take()
+  auto planes = [&](size_t &f, size_t elems) { take(f, sp ? (elems + 1) / 2 : 0); };
+  planes(w.wdtp, D * Rp);
+  planes(w.wdtT, R * D);
+  planes(w.wxT, D * Wp);
+  planes(w.dtn_s, 2 * T * Rp);
+  planes(w.dtnT, 2 * R * Tp);
+  planes(w.dxd_s, 2 * T * Wp);
+  planes(w.dxdT, 2 * W * Tp);
   w.total = o;
   return w;
 }
@@ -476,15 +498,44 @@ mm_status backward_impl(const mm_shape *s, const mm_params *p, const void *xz, c
   const float *wx = bf ? a.wx32 : (const float *)p->x_proj_w;
   const float *wdt = bf ? a.wdt32 : (const float *)p->dt_proj_w;
   float *cs = F(w.cs_part);
+  // split-bf16 planes (bf16 I/O)
+  const bool sp = bw_split_products(*s);
+  const int Tp = (int)pad64(T), Rp = (int)pad64(R), Wp = (int)pad64(W);
+  auto H = [&](size_t off) { return (uint16_t *)(ws + off); };
+  uint16_t *wdtp = H(w.wdtp), *wdtT = H(w.wdtT), *wxT = H(w.wxT);
+  uint16_t *u_hi = H(w.du), *u_lo = u_hi + T * D;
+  uint16_t *dtn_hi = H(w.dtn_s), *dtn_lo = dtn_hi + T * Rp;
+  uint16_t *dtnT_hi = H(w.dtnT), *dtnT_lo = dtnT_hi + (int64_t)R * Tp;
+  uint16_t *dp_hi = H(w.dys), *dp_lo = dp_hi + T * D;
+  uint16_t *dpT_hi = H(w.ys), *dpT_lo = dpT_hi + (int64_t)D * Tp;
+  uint16_t *dxd_hi = H(w.dxd_s), *dxd_lo = dxd_hi + T * Wp;
+  uint16_t *dxdT_hi = H(w.dxdT), *dxdT_lo = dxdT_hi + (int64_t)W * Tp;
+  uint16_t *uT_hi = H(w.dt), *uT_lo = uT_hi + (int64_t)D * Tp;
 
   {
     StageScope sc(timer, st, MM_STAGE_BWD_RECOMPUTE);
     if (bf) MM_TRY(launch_backward_stage(s->io_dtype, a, 6, st));
+    if (sp) {   // exactly-bf16 weight copies: W_dt [D, Rp], W_dt^T [R, D], W_x^T [D, Wp]
+      MM_TRY(launch_split_bf16(a.wdt32, D, R, R, wdtp, nullptr, Rp, st));
+      MM_TRY(launch_tsplit_bf16(a.wdt32, D, R, R, wdtT, nullptr, D, st));
+      MM_TRY(launch_tsplit_bf16(a.wx32, W, D, D, wxT, nullptr, Wp, st));
+    }
     MM_TRY(launch_backward_stage(s->io_dtype, a, 0, st));                    // u
-    MM_TRY(launch_gemm_f32({a.u, wx, a.xd, (int)T, W, D, D, 1, 1, D, W, 1, 0}, st));   // xdbl
+    if (sp) {   // xdbl = u W_x^T on the planes of u (in du, which the scan writes later)
+      MM_TRY(launch_split_bf16(a.u, T, D, D, u_hi, u_lo, D, st));
+      MM_TRY(launch_xproj(MM_BF16, u_hi, u_lo, p->x_proj_w, a.xd, (int)T, D, W, st));
+    } else {
+      MM_TRY(launch_gemm_f32({a.u, wx, a.xd, (int)T, W, D, D, 1, 1, D, W, 1, 0}, st));   // xdbl
+    }
     MM_TRY(launch_norm(MM_F32, a.xd, a.dtn, nullptr, a.bc, a.g_dt, a.g_B, a.g_C, (int)T, R, 16,
                        a.eps, st));
-    MM_TRY(launch_gemm_f32({a.dtn, wdt, a.dt, (int)T, D, R, R, 1, 1, R, D, 1, 0}, st));  // W_dt dt_low
+    if (sp) {   // dt_proj's product on the planes of dt_low
+      MM_TRY(launch_split_bf16(a.dtn, T, R, R, dtn_hi, dtn_lo, Rp, st));
+      MM_TRY(launch_gemm_sp({{dtn_hi, dtn_lo, nullptr}, {wdtp, wdtp, nullptr}, 2, a.dt, (int)T, D,
+                             Rp, Rp, Rp, D, 0, nullptr, 1}, st));
+    } else {
+      MM_TRY(launch_gemm_f32({a.dtn, wdt, a.dt, (int)T, D, R, R, 1, 1, R, D, 1, 0}, st));
+    }
     MM_TRY(launch_backward_stage(s->io_dtype, a, 1, st));                    // dt, sigmoid, dys
   }
   {
@@ -498,16 +549,40 @@ mm_status backward_impl(const mm_shape *s, const mm_params *p, const void *xz, c
     float *dp = a.sig;   // d / d (dt_proj pre-activation), [T, D]
     MM_TRY(launch_colsum(dp, T, D, cs, g->dt_proj_b, st));
     float *gp = F(w.gemm_part);
-    MM_TRY(launch_gemm_f32({dp, a.dtn, g->dt_proj_w, D, R, (int)T, 1, D, R, 1, R, 1, 0, gp}, st));
-    MM_TRY(launch_gemm_f32({dp, wdt, a.ddtn, (int)T, R, D, D, 1, R, 1, R, 1, 0}, st));
+    if (sp) {
+      // planes of dp (in dys) and of dp^T, dt_low^T ([D | R, Tp]; dp^T in ys)
+      MM_TRY(launch_split_bf16(dp, T, D, D, dp_hi, dp_lo, D, st));
+      MM_TRY(launch_tsplit_bf16(dp, (int)T, D, D, dpT_hi, dpT_lo, Tp, st));
+      MM_TRY(launch_tsplit_bf16(a.dtn, (int)T, R, R, dtnT_hi, dtnT_lo, Tp, st));
+      // d W_dt [D, R] = dp^T dt_low (over tokens); d dt_low [T, R] = dp W_dt
+      MM_TRY(launch_gemm_sp({{dpT_hi, dpT_hi, dpT_lo}, {dtnT_hi, dtnT_lo, dtnT_hi}, 3,
+                             g->dt_proj_w, D, R, Tp, Tp, Tp, R, 0, gp, 1}, st));
+      MM_TRY(launch_gemm_sp({{dp_hi, dp_lo, nullptr}, {wdtT, wdtT, nullptr}, 2, a.ddtn, (int)T, R,
+                             D, D, D, R, 0, nullptr, 1}, st));
+    } else {
+      MM_TRY(launch_gemm_f32({dp, a.dtn, g->dt_proj_w, D, R, (int)T, 1, D, R, 1, R, 1, 0, gp}, st));
+      MM_TRY(launch_gemm_f32({dp, wdt, a.ddtn, (int)T, R, D, D, 1, R, 1, R, 1, 0}, st));
+    }
     MM_TRY(launch_backward_stage(s->io_dtype, a, 3, st));                    // RMSNorm backward
     MM_TRY(launch_colsum(a.gc, T, W, cs, F(w.gsum), st));
     MM_TRY(hipMemcpyAsync(g->dt_norm_w, F(w.gsum), (size_t)R * 4, hipMemcpyDeviceToDevice, st));
     MM_TRY(hipMemcpyAsync(g->B_norm_w, F(w.gsum) + R, 64, hipMemcpyDeviceToDevice, st));
     MM_TRY(hipMemcpyAsync(g->C_norm_w, F(w.gsum) + R + 16, 64, hipMemcpyDeviceToDevice, st));
-    // d x_proj_w [W, D] computed transposed (M = D, N = W) so the long side is M
-    MM_TRY(launch_gemm_f32({a.u, a.dxd, g->x_proj_w, D, W, (int)T, 1, D, W, 1, 1, D, 0, gp}, st));
-    MM_TRY(launch_gemm_f32({a.dxd, wx, a.du, (int)T, D, W, W, 1, D, 1, D, 1, 1}, st));
+    if (sp) {
+      // planes of dxdbl [T, Wp] and dxdbl^T [W, Tp], u^T [D, Tp] (in dt)
+      MM_TRY(launch_split_bf16(a.dxd, T, W, W, dxd_hi, dxd_lo, Wp, st));
+      MM_TRY(launch_tsplit_bf16(a.dxd, (int)T, W, W, dxdT_hi, dxdT_lo, Tp, st));
+      MM_TRY(launch_tsplit_bf16(a.u, (int)T, D, D, uT_hi, uT_lo, Tp, st));
+      // d W_x [W, D] = dxdbl^T u (over tokens); du += dxdbl W_x
+      MM_TRY(launch_gemm_sp({{dxdT_hi, dxdT_hi, dxdT_lo}, {uT_hi, uT_lo, uT_hi}, 3, g->x_proj_w,
+                             W, D, Tp, Tp, Tp, D, 0, gp, 1}, st));
+      MM_TRY(launch_gemm_sp({{dxd_hi, dxd_lo, nullptr}, {wxT, wxT, nullptr}, 2, a.du, (int)T, D,
+                             Wp, Wp, Wp, D, 1, nullptr, 1}, st));
+    } else {
+      // d x_proj_w [W, D] computed transposed (M = D, N = W) so the long side is M
+      MM_TRY(launch_gemm_f32({a.u, a.dxd, g->x_proj_w, D, W, (int)T, 1, D, W, 1, 1, D, 0, gp}, st));
+      MM_TRY(launch_gemm_f32({a.dxd, wx, a.du, (int)T, D, W, W, 1, D, 1, D, 1, 1}, st));
+    }
   }
   {
     StageScope sc(timer, st, MM_STAGE_BWD_CONV);

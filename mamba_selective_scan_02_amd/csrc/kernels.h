@@ -172,6 +172,34 @@ hipError_t launch_gemm_f32(const GemmF32Args &g, hipStream_t s);
 hipError_t launch_colsum(const float *in, int64_t rows, int64_t cols, float *part, float *out,
                          hipStream_t s);
 
+// ---- split-precision bf16 products of the backward (bwgemm.hip)
+// C[M, N] (+)= sum over segments s < nseg of A[s][M, K] . B[s][N, K]^T: bf16 planes whose rows
+// are contiguous along K (row strides lda, ldb), fp32 out (row stride ldc). K % 64 == 0,
+// N % 4 == 0; M and N otherwise arbitrary. With part != null a long K is split over up to
+// kSpMaxSplit workgroups per tile; part then holds kSpMaxSplit * M * N floats and the splits
+// are added in a fixed order.
+constexpr int kSpMaxSplit = 32;
+struct SpGemmArgs {
+  const uint16_t *A[3], *B[3];
+  int nseg;
+  float *C;
+  int M, N, K;
+  int lda, ldb, ldc;
+  int accumulate;
+  float *part;
+  int split;
+};
+hipError_t launch_gemm_sp(const SpGemmArgs &g, hipStream_t s);
+int gemm_sp_split(int M, int N, int K);
+// fp32 src[rows, cols] (row stride lds) -> bf16 hi = bf16(v), lo = bf16(v - hi) planes
+// [rows, ldd], zero past cols; lo may be null (exactly-bf16 sources)
+hipError_t launch_split_bf16(const float *src, int64_t rows, int cols, int64_t lds, uint16_t *hi,
+                             uint16_t *lo, int ldd, hipStream_t s);
+// the same split, transposed: planes [cols, ldd] with element [c][r] = src[r][c], zero for
+// r >= rows; ldd % 64 == 0
+hipError_t launch_tsplit_bf16(const float *src, int rows, int cols, int64_t lds, uint16_t *hi,
+                              uint16_t *lo, int64_t ldd, hipStream_t s);
+
 struct ScanArgs {
   const void *xz;       // [B, L, 2D]; x = first D columns (conv input), z = last D (gate)
   const void *conv_w;   // [D, K] io dtype
