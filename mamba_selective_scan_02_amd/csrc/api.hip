@@ -511,6 +511,10 @@ mm_status backward_impl(const mm_shape *s, const mm_params *p, const void *xz, c
   uint16_t *dxd_hi = H(w.dxd_s), *dxd_lo = dxd_hi + T * Wp;
   uint16_t *dxdT_hi = H(w.dxdT), *dxdT_lo = dxdT_hi + (int64_t)W * Tp;
   uint16_t *uT_hi = H(w.dt), *uT_lo = uT_hi + (int64_t)D * Tp;
+  if (sp) {   // the u and dp planes come from the kernels that form u and dp
+    a.u_hi = u_hi; a.u_lo = u_lo;
+    a.dp_hi = dp_hi; a.dp_lo = dp_lo;
+  }
 
   {
     StageScope sc(timer, st, MM_STAGE_BWD_RECOMPUTE);
@@ -522,7 +526,6 @@ mm_status backward_impl(const mm_shape *s, const mm_params *p, const void *xz, c
     }
     MM_TRY(launch_backward_stage(s->io_dtype, a, 0, st));                    // u
     if (sp) {   // xdbl = u W_x^T on the planes of u (in du, which the scan writes later)
-      MM_TRY(launch_split_bf16(a.u, T, D, D, u_hi, u_lo, D, st));
       MM_TRY(launch_xproj(MM_BF16, u_hi, u_lo, p->x_proj_w, a.xd, (int)T, D, W, st));
     } else {
       MM_TRY(launch_gemm_f32({a.u, wx, a.xd, (int)T, W, D, D, 1, 1, D, W, 1, 0}, st));   // xdbl
@@ -550,8 +553,8 @@ mm_status backward_impl(const mm_shape *s, const mm_params *p, const void *xz, c
     MM_TRY(launch_colsum(dp, T, D, cs, g->dt_proj_b, st));
     float *gp = F(w.gemm_part);
     if (sp) {
-      // planes of dp (in dys) and of dp^T, dt_low^T ([D | R, Tp]; dp^T in ys)
-      MM_TRY(launch_split_bf16(dp, T, D, D, dp_hi, dp_lo, D, st));
+      // planes of dp^T and dt_low^T ([D | R, Tp]; dp^T in ys); those of dp (in dys) are the
+      // post-scan kernel's
       MM_TRY(launch_tsplit_bf16(dp, (int)T, D, D, dpT_hi, dpT_lo, Tp, st));
       MM_TRY(launch_tsplit_bf16(a.dtn, (int)T, R, R, dtnT_hi, dtnT_lo, Tp, st));
       // d W_dt [D, R] = dp^T dt_low (over tokens); d dt_low [T, R] = dp W_dt

@@ -19,7 +19,7 @@
 //   (norm_kernel)             the forward's RMSNorm of dt_low, B, C (fp32 mode)
 //   bw_pointwise_kernel       dt = softplus(p), sigmoid(p), dys = dy SiLU(z)
 //   bw_range_transfer_kernel  per range of kRT tokens and (channel, state), 64 channels per
-//                             workgroup with staged inputs: the forward
+//                             workgroup with staged inputs, one forward pass: the forward
 //                             transfer (prod a, local end state) and the reverse one (local
 //                             a_t0 dh_t0 from zero)
 //   bw_range_carry_kernel     sequential over ranges: each range's true start state and the
@@ -62,12 +62,14 @@ __device__ __forceinline__ float dsilu_f(float v) {
   const float s = sigmoid_f(v);
   return s * __builtin_fmaf(v, 1.0f - s, 1.0f);
 }
-// sum over the 16 lanes of a DPP row; every lane of the row receives the sum
+// sum over the 16 lanes of a DPP row; every lane of the row receives the sum. Every source lane
+// lies inside the row, so bound_ctrl changes no value; it lets the compiler fold each move into
+// its add (one v_add_f32_dpp per step).
 __device__ __forceinline__ float row_sum16(float v) {
-  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
-  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));
-  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x124, 0xF, 0xF, false));
-  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x128, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true));
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x124, 0xF, 0xF, true));
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x128, 0xF, 0xF, true));
   return v;
 }
 
@@ -126,56 +128,101 @@ __device__ __forceinline__ void conv_in4(const BwArgs &a, int b, int s, int i0, 
 #pragma unroll
   for (int c = 0; c < 4; ++c) v[c] = conv_in<T>(a, b, s, i0 + c);
 }
+// bf16 hi = bf16(v), lo = bf16(v - hi) of 4 values, packed for two 8-byte stores
+__device__ __forceinline__ void split4(const float v[4], uint2 &hi, uint2 &lo) {
+  bf16_t h[4], l[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    h[c] = f2bf(v[c]);
+    l[c] = f2bf(v[c] - bf2f(h[c]));
+  }
+  hi = make_uint2((uint32_t)h[0] | ((uint32_t)h[1] << 16), (uint32_t)h[2] | ((uint32_t)h[3] << 16));
+  lo = make_uint2((uint32_t)l[0] | ((uint32_t)l[1] << 16), (uint32_t)l[2] | ((uint32_t)l[3] << 16));
+}
+
+// One thread per 4 channels of a kUStrip-token strip (blockIdx.x: strips, blockIdx.y: blocks
+// of 1024 channels): the K-tap window slides along the strip, so each x row is read once.
+// With u_hi set, u is also written as bf16 hi / lo planes (the split products' operand).
+constexpr int kUStrip = 64;
 template <typename T, int K>
 __global__ __launch_bounds__(256) void bw_conv_u_kernel(BwArgs a) {
-  const int nq = a.D / 4;
-  const int64_t n = (int64_t)a.B * a.L * nq;
-  for (int64_t e = blockIdx.x * 256ll + threadIdx.x; e < n; e += (int64_t)gridDim.x * 256) {
-    const int i0 = (int)(e % nq) * 4;
-    const int64_t tok = e / nq;
-    const int t = (int)(tok % a.L), b = (int)(tok / a.L);
-    float q[4], xv[4], w[4][K];
+  const int i0 = (blockIdx.y * 256 + threadIdx.x) * 4;
+  if (i0 >= a.D) return;
+  const int ns = (a.L + kUStrip - 1) / kUStrip;
+  const int b = blockIdx.x / ns, s0 = (blockIdx.x % ns) * kUStrip;
+  const int s1 = min(a.L, s0 + kUStrip);
+  float w[4][K], bias[4], xw[K][4];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      q[c] = a.conv_b ? io<T>::ld((const T *)a.conv_b + i0 + c) : 0.f;
+  for (int c = 0; c < 4; ++c) {
+    bias[c] = a.conv_b ? io<T>::ld((const T *)a.conv_b + i0 + c) : 0.f;
 #pragma unroll
-      for (int k = 0; k < K; ++k) w[c][k] = io<T>::ld((const T *)a.conv_w + (i0 + c) * K + k);
-    }
+    for (int k = 0; k < K; ++k) w[c][k] = io<T>::ld((const T *)a.conv_w + (i0 + c) * K + k);
+  }
 #pragma unroll
-    for (int k = 0; k < K; ++k) {
-      conv_in4<T>(a, b, t - (K - 1) + k, i0, xv);
-#pragma unroll
-      for (int c = 0; c < 4; ++c) q[c] = __builtin_fmaf(w[c][k], xv[c], q[c]);
-    }
+  for (int k = 0; k < K - 1; ++k) conv_in4<T>(a, b, s0 - (K - 1) + k, i0, xw[k]);
+  for (int t = s0; t < s1; ++t) {
+    v4io<T>::ld((const T *)a.xz + ((int64_t)b * a.L + t) * 2 * a.D + i0, xw[K - 1]);
     float u[4];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) u[c] = silu_f(q[c]);
-    v4io<float>::st(a.u + tok * a.D + i0, u);
+    for (int c = 0; c < 4; ++c) {
+      float q = bias[c];
+#pragma unroll
+      for (int k = 0; k < K; ++k) q = __builtin_fmaf(w[c][k], xw[k][c], q);
+      u[c] = silu_f(q);
+    }
+    const int64_t e = ((int64_t)b * a.L + t) * a.D + i0;
+    v4io<float>::st(a.u + e, u);
+    if (a.u_hi) {
+      uint2 hi, lo;
+      split4(u, hi, lo);
+      *(uint2 *)(a.u_hi + e) = hi;
+      *(uint2 *)(a.u_lo + e) = lo;
+    }
+#pragma unroll
+    for (int k = 0; k < K - 1; ++k)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) xw[k][c] = xw[k + 1][c];
   }
 }
 
 // ---------------------------------------------------------------- dt, sigmoid(p), dys
+// one token per blockIdx.x, 4 channels per thread (blockIdx.y: blocks of 1024 channels)
 template <typename T>
 __global__ __launch_bounds__(256) void bw_pointwise_kernel(BwArgs a) {
-  const int64_t n = (int64_t)a.B * a.L * a.D;
-  for (int64_t e = blockIdx.x * 256ll + threadIdx.x; e < n; e += (int64_t)gridDim.x * 256) {
-    const int i = (int)(e % a.D);
-    const int64_t tok = e / a.D;
-    const float p = a.dt[e] + a.dt_b[i];        // dt holds dt_proj's product on entry
-    a.dt[e] = softplus_f(p);
-    a.sig[e] = sigmoid_f(p);
-    const float z = io<T>::ld((const T *)a.xz + tok * 2 * a.D + a.D + i);
-    a.dys[e] = io<T>::ld((const T *)a.dy + e) * silu_f(z);
+  const int i0 = (blockIdx.y * 256 + threadIdx.x) * 4;
+  if (i0 >= a.D) return;
+  const int64_t tok = blockIdx.x, e = tok * a.D + i0;
+  const float4 pre = *(const float4 *)(a.dt + e);   // dt holds dt_proj's product on entry
+  const float4 bias = *(const float4 *)(a.dt_b + i0);
+  const float p[4] = {pre.x + bias.x, pre.y + bias.y, pre.z + bias.z, pre.w + bias.w};
+  float z[4], dy[4], dt[4], sg[4], dys[4];
+  v4io<T>::ld((const T *)a.xz + tok * 2 * a.D + a.D + i0, z);
+  v4io<T>::ld((const T *)a.dy + e, dy);
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    dt[c] = softplus_f(p[c]);
+    sg[c] = sigmoid_f(p[c]);
+    dys[c] = dy[c] * silu_f(z[c]);
   }
+  v4io<float>::st(a.dt + e, dt);
+  v4io<float>::st(a.sig + e, sg);
+  v4io<float>::st(a.dys + e, dys);
 }
 
 // ---------------------------------------------------------------- per-range transfers
 // lanes: 64 channels x 16 states per workgroup (1024 threads); one range of one sequence. The
 // inputs of each kSB-token sub-block (dt, u, dys of the 64 channels: whole 256-byte rows; B|C)
 // are staged in LDS by coalesced loads, the next sub-block's fetched into registers while the
-// current one is processed.
+// current one is processed. Without ZOH the u slot is staged as dt u.
+//
+// One forward pass gives all three transfers of the range [t0, t1): P = prod a_t, the local
+// end state S (from zero), and the reverse carry R = sum_t (a_t0 ... a_t) C_t dys_t, which is
+// the reverse recursion g <- a_t (C_t dys_t + g) from zero at t1 unrolled (the running product
+// is P's own). Tokens past t1 are staged as zeros: a = 1 and zero inputs leave all three as
+// they are.
 constexpr int kRTF = kSB * kCG;                  // floats per staged [kSB][64] array
 constexpr int kRTStage = 3 * kRTF + kSB * 32;    // dt | u | dys | B|C
+template <bool ZOH>
 __global__ __launch_bounds__(1024) void bw_range_transfer_kernel(BwArgs a) {
   __shared__ float st_s[kRTStage];
   const int ncg = a.D / kCG;
@@ -187,8 +234,9 @@ __global__ __launch_bounds__(1024) void bw_range_transfer_kernel(BwArgs a) {
   const int t0 = r * kRT, t1 = min(a.L, t0 + kRT);
   const int nsb = (t1 - t0 + kSB - 1) / kSB;
   const int64_t tb = (int64_t)b * a.L;
-  const float An = a.A[i * 16 + n];
-  constexpr int NQ = kRTStage / 1024;
+  const float An = a.A[i * 16 + n], An2 = An * kLog2e;
+  constexpr int NQ = kRTStage / 1024;   // q 0-1: dt, 2-3: u (same elements as q - 2), 4-5: dys, 6: B|C
+  static_assert(NQ == 7 && 2 * kRTF == 4096, "staging slots");
   float pf[NQ];
   auto fetch = [&](int j) {
     const int tj = t0 + j * kSB;
@@ -209,44 +257,27 @@ __global__ __launch_bounds__(1024) void bw_range_transfer_kernel(BwArgs a) {
   };
   auto stash = [&]() {
 #pragma unroll
-    for (int q = 0; q < NQ; ++q) st_s[tid + 1024 * q] = pf[q];
+    for (int q = 0; q < NQ; ++q)
+      st_s[tid + 1024 * q] = (!ZOH && (q == 2 || q == 3)) ? pf[q] * pf[q - 2] : pf[q];
   };
   const float *s_dt = st_s, *s_u = st_s + kRTF, *s_dys = st_s + 2 * kRTF, *s_bc = st_s + 3 * kRTF;
 
-  float P = 1.f, S = 0.f;
+  float P = 1.f, S = 0.f, g = 0.f;
   fetch(0);
   for (int j = 0; j < nsb; ++j) {
     __syncthreads();
     stash();
     __syncthreads();
     if (j + 1 < nsb) fetch(j + 1);
-    const int tj = t0 + j * kSB;
 #pragma unroll
     for (int k = 0; k < kSB; ++k) {
-      if (tj + k < t1) {
-        const float dtv = s_dt[k * kCG + c];
-        const float av = exp2_hw(dtv * An * kLog2e);
-        const float bb = (a.zoh ? expm1_f(dtv * An) / An : dtv) * s_bc[k * 32 + n];
-        S = __builtin_fmaf(av, S, bb * s_u[k * kCG + c]);
-        P *= av;
-      }
-    }
-  }
-  float g = 0.f;
-  fetch(nsb - 1);
-  for (int j = nsb - 1; j >= 0; --j) {
-    __syncthreads();
-    stash();
-    __syncthreads();
-    if (j > 0) fetch(j - 1);
-    const int tj = t0 + j * kSB;
-#pragma unroll
-    for (int k = kSB - 1; k >= 0; --k) {
-      if (tj + k < t1) {
-        const float dtv = s_dt[k * kCG + c];
-        const float av = exp2_hw(dtv * An * kLog2e);
-        g = av * __builtin_fmaf(s_bc[k * 32 + 16 + n], s_dys[k * kCG + c], g);
-      }
+      const float dtv = s_dt[k * kCG + c];
+      const float av = exp2_hw(dtv * An2);
+      const float bu = ZOH ? expm1_f(dtv * An) / An * s_bc[k * 32 + n] * s_u[k * kCG + c]
+                           : s_u[k * kCG + c] * s_bc[k * 32 + n];
+      S = __builtin_fmaf(av, S, bu);
+      P *= av;
+      g = __builtin_fmaf(P, s_bc[k * 32 + 16 + n] * s_dys[k * kCG + c], g);
     }
   }
   const int64_t o = (((int64_t)b * a.nr + r) * a.D + i) * 16 + n;
@@ -441,19 +472,33 @@ __global__ __launch_bounds__(1024) void bw_scan_kernel(BwArgs a) {
   if (n == 0) a.dD_part[((int64_t)b * a.nr + r) * a.D + i] = dD;
 }
 
-// after the scan: d(dt_proj pre-activation) = d dt * sigmoid(p) (into sig) and the gate's
-// dz = dy ys SiLU'(z) (into dxz)
+// after the scan: d(dt_proj pre-activation) = d dt * sigmoid(p) (into sig; with dp_hi set also
+// as bf16 hi / lo planes) and the gate's dz = dy ys SiLU'(z) (into dxz). Grid as the pointwise
+// kernel's.
 template <typename T>
 __global__ __launch_bounds__(256) void bw_post_scan_kernel(BwArgs a) {
-  const int64_t n = (int64_t)a.B * a.L * a.D;
-  for (int64_t e = blockIdx.x * 256ll + threadIdx.x; e < n; e += (int64_t)gridDim.x * 256) {
-    const int i = (int)(e % a.D);
-    const int64_t tok = e / a.D;
-    a.sig[e] *= a.dt[e];
-    const float z = io<T>::ld((const T *)a.xz + tok * 2 * a.D + a.D + i);
-    io<T>::st((T *)a.dxz + tok * 2 * a.D + a.D + i,
-              io<T>::ld((const T *)a.dy + e) * a.ys[e] * dsilu_f(z));
+  const int i0 = (blockIdx.y * 256 + threadIdx.x) * 4;
+  if (i0 >= a.D) return;
+  const int64_t tok = blockIdx.x, e = tok * a.D + i0;
+  float sg[4], ddt[4], ys[4], z[4], dy[4], dz[4];
+  v4io<float>::ld(a.sig + e, sg);
+  v4io<float>::ld(a.dt + e, ddt);
+  v4io<float>::ld(a.ys + e, ys);
+  v4io<T>::ld((const T *)a.xz + tok * 2 * a.D + a.D + i0, z);
+  v4io<T>::ld((const T *)a.dy + e, dy);
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    sg[c] *= ddt[c];
+    dz[c] = dy[c] * ys[c] * dsilu_f(z[c]);
   }
+  v4io<float>::st(a.sig + e, sg);
+  if (a.dp_hi) {
+    uint2 hi, lo;
+    split4(sg, hi, lo);
+    *(uint2 *)(a.dp_hi + e) = hi;
+    *(uint2 *)(a.dp_lo + e) = lo;
+  }
+  v4io<T>::st((T *)a.dxz + tok * 2 * a.D + a.D + i0, dz);
 }
 
 // dB | dC [T, 32] = sum over the channel groups of the scan's per-workgroup rows
@@ -798,19 +843,23 @@ int64_t bw_colsum_blocks(int64_t rows) { return (rows + kColRows - 1) / kColRows
 
 template <typename T>
 hipError_t bw_dispatch(const BwArgs &a, int stage, hipStream_t s) {
-  const int64_t TD = (int64_t)a.B * a.L * a.D;
+  // one token per blockIdx.x, 1024 channels per blockIdx.y
+  const dim3 tok_grid((unsigned)a.T, (unsigned)((a.D + 1023) / 1024));
   switch (stage) {
-    case 0:
-      if (a.K == 2) hipLaunchKernelGGL((bw_conv_u_kernel<T, 2>), dim3(grid_for(TD / 4)), dim3(256), 0, s, a);
-      else if (a.K == 3) hipLaunchKernelGGL((bw_conv_u_kernel<T, 3>), dim3(grid_for(TD / 4)), dim3(256), 0, s, a);
-      else hipLaunchKernelGGL((bw_conv_u_kernel<T, 4>), dim3(grid_for(TD / 4)), dim3(256), 0, s, a);
+    case 0: {
+      const dim3 grid((unsigned)(a.B * ((a.L + kUStrip - 1) / kUStrip)), (unsigned)((a.D + 1023) / 1024));
+      if (a.K == 2) hipLaunchKernelGGL((bw_conv_u_kernel<T, 2>), grid, dim3(256), 0, s, a);
+      else if (a.K == 3) hipLaunchKernelGGL((bw_conv_u_kernel<T, 3>), grid, dim3(256), 0, s, a);
+      else hipLaunchKernelGGL((bw_conv_u_kernel<T, 4>), grid, dim3(256), 0, s, a);
       break;
+    }
     case 1:
-      hipLaunchKernelGGL(bw_pointwise_kernel<T>, dim3(grid_for(TD)), dim3(256), 0, s, a);
+      hipLaunchKernelGGL(bw_pointwise_kernel<T>, tok_grid, dim3(256), 0, s, a);
       break;
     case 2: {
-      hipLaunchKernelGGL(bw_range_transfer_kernel, dim3((unsigned)(a.B * a.nr * (a.D / kCG))),
-                         dim3(1024), 0, s, a);
+      const dim3 rgrid((unsigned)(a.B * a.nr * (a.D / kCG)));
+      if (a.zoh) hipLaunchKernelGGL(bw_range_transfer_kernel<true>, rgrid, dim3(1024), 0, s, a);
+      else hipLaunchKernelGGL(bw_range_transfer_kernel<false>, rgrid, dim3(1024), 0, s, a);
       const int64_t nc = (int64_t)a.B * a.D * 16;
       hipLaunchKernelGGL(bw_range_carry_kernel, dim3((unsigned)((nc + 255) / 256)), dim3(256), 0, s, a);
       const unsigned grid = (unsigned)(a.B * a.nr * (a.D / kCG));
@@ -818,7 +867,7 @@ hipError_t bw_dispatch(const BwArgs &a, int stage, hipStream_t s) {
       else hipLaunchKernelGGL((bw_scan_kernel<T, false>), dim3(grid), dim3(1024), 0, s, a);
       hipLaunchKernelGGL(bw_rowsum_kernel, dim3((unsigned)((a.T * 32 + 255) / 256)), dim3(256), 0, s,
                          a.bc_part, a.dbc, a.T, a.D / kCG);
-      hipLaunchKernelGGL(bw_post_scan_kernel<T>, dim3(grid_for(TD)), dim3(256), 0, s, a);
+      hipLaunchKernelGGL(bw_post_scan_kernel<T>, tok_grid, dim3(256), 0, s, a);
       break;
     }
     case 3:

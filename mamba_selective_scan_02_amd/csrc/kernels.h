@@ -141,6 +141,8 @@ struct BwArgs {
   float *ddtn, *dxd, *gc;                   // [T, R], [T, R+32], [T, R+32]
   float *conv_part;                         // [B, conv strips, D, 5]
   float *conv_sum;                          // [D, 5]
+  uint16_t *u_hi, *u_lo, *dp_hi, *dp_lo;    // optional bf16 hi / lo planes [T, D] of u and of
+                                            // d(dt_proj pre-activation) (split products)
   // outputs
   void *dxz;
   float *d_conv_w, *d_conv_b, *d_ssm_state, *d_conv_state;

@@ -46,15 +46,16 @@ template <> __device__ __forceinline__ float ld_u<bf16_t>(const ScanArgs &a, int
 }
 
 // sum over the G lanes of a channel (G = 4, 8 or 16, groups aligned to G lanes); every lane
-// of the group receives it
+// of the group receives it. All source lanes lie inside the row (bound_ctrl changes no value
+// and lets each move fold into its add).
 template <int G>
 __device__ __forceinline__ float sum_group(float v) {
-  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));   // ^1
-  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));   // ^2
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));   // ^1
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true));   // ^2
   if (G >= 8)
-    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false));  // 7-i
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, true));  // 7-i
   if (G >= 16)
-    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, false));  // 15-i
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, true));  // 15-i
   return v;
 }
 template <int N> constexpr int states_per_lane() { return N >= 16 ? N / 16 : 1; }
