@@ -26,14 +26,14 @@
 //                             dh carry entering it from later ranges; the last carry is the
 //                             gradient of the carried SSM state
 //   bw_scan_kernel            per range, 64 channels x 16 states per workgroup: a forward pass
-//                             (ys = C.h + D u for the gate, checkpoints every kSB tokens in
+//                             (ys = C.h + D u for the gate, checkpoints every kSB2 tokens in
 //                             LDS), then sub-blocks in reverse, each recomputed into registers
 //                             and walked backward. Each sub-block's inputs are staged in LDS by
 //                             coalesced loads issued one sub-block ahead (the recurrence never
-//                             waits on global memory). Sums over the 16 states by DPP within a
-//                             16-lane row; dB and dC (shared by all channels) sum over the
-//                             wave's 4 channels by lane swaps, over the 16 waves in LDS, into
-//                             per-workgroup rows
+//                             waits on global memory). Sums over the 16 states: transposed DPP
+//                             reductions within a 16-lane row; dB and dC (shared by all
+//                             channels) sum over the wave's 4 channels on fp32 MFMA, over the
+//                             16 waves in LDS, into per-workgroup rows
 //   bw_post_scan_kernel       d(dt_proj pre-activation) = d dt sigmoid(p); dz = dy ys SiLU'(z)
 //   bw_rowsum_kernel          dB | dC from those per-workgroup rows
 //   bw_norm_bwd_kernel        the three RMSNorm backwards per token (+ gain terms)
@@ -49,9 +49,8 @@ namespace {
 
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 
-constexpr int kRT = 512;          // tokens per range (carry granularity)
-constexpr int kSB = 32;           // tokens per recomputed sub-block
-constexpr int kNSB = kRT / kSB;   // sub-blocks per range
+constexpr int kRT = 256;          // tokens per range (carry granularity)
+constexpr int kSB = 32;           // tokens per staged sub-block of the range transfers
 constexpr int kCG = 64;           // channels per scan workgroup
 constexpr int kColRows = 1024;    // rows per partial of a column sum
 
@@ -62,17 +61,6 @@ __device__ __forceinline__ float dsilu_f(float v) {
   const float s = sigmoid_f(v);
   return s * __builtin_fmaf(v, 1.0f - s, 1.0f);
 }
-// sum over the 16 lanes of a DPP row; every lane of the row receives the sum. Every source lane
-// lies inside the row, so bound_ctrl changes no value; it lets the compiler fold each move into
-// its add (one v_add_f32_dpp per step).
-__device__ __forceinline__ float row_sum16(float v) {
-  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));
-  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true));
-  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x124, 0xF, 0xF, true));
-  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x128, 0xF, 0xF, true));
-  return v;
-}
-
 // ---------------------------------------------------------------- weights to fp32
 template <typename T>
 __global__ __launch_bounds__(256) void to_f32_kernel(const T *src, float *dst, int64_t n) {
@@ -310,15 +298,67 @@ __global__ __launch_bounds__(256) void bw_range_carry_kernel(BwArgs a) {
 }
 
 // ---------------------------------------------------------------- the reverse scan
-// Staged inputs of one kSB-token sub-block for the workgroup's 64 channels: dt | u | dys
-// ([kSB][64] each) and B|C ([kSB][32]); thread tid stages elements tid + 1024 q.
-constexpr int kSF = kSB * kCG;
-constexpr int kSStage = 3 * kSF + kSB * 32;
+// Lanes: 64 channels x 16 states per workgroup (1024 threads; lane n = state, the wave's four
+// 16-lane rows = four channels); one range of one sequence, in sub-blocks of kSB2 tokens whose
+// inputs are staged in LDS by coalesced loads one sub-block ahead: dt | u | dt u | dys
+// ([kSB2][64] each) and B|C ([kSB2][32]); thread tid stages elements tid + 1024 q. Tokens past
+// the range end are staged as zeros (a = 1, no input: the states and the carry pass through
+// them unchanged, and nothing of theirs is stored).
+//
+// Sums over the 16 states of a channel (ys, and the d dt, du contributions) are transposed
+// reductions: each lane holds 8 partial values (8 tokens, or 4 tokens x 2 quantities), and
+// four DPP exchange-and-add steps inside the row leave lanes 2j and 2j + 1 with the row's sum of
+// value j, 22 VALU operations for 8 sums. Sums over channels (dB, dC: per token and state) run
+// on the matrix cores: with B[k][n] = this lane's term (k = the wave's channel) and A[m][k] = 1
+// for the token's row m only, a 16x16x4 fp32 MFMA adds the four channels' terms into row m of a
+// [token, state] accumulator; each wave's 16 x 16 result goes to LDS once per sub-block and
+// the 16 waves are added in a fixed order.
+constexpr int kSB2 = 16;                        // tokens per recomputed sub-block
+constexpr int kNSB2 = kRT / kSB2;               // sub-blocks per range
+constexpr int kSF2 = kSB2 * kCG;                // floats per staged [kSB2][64] array
+constexpr int kS2Stage = 4 * kSF2 + kSB2 * 32;  // dt | u | dt u | dys | B|C
+constexpr int kS2NQ = (kS2Stage + 1023) / 1024;
+static_assert(kSF2 == 1024, "one staged array per 1024 threads");
+
+// expm1 as expm1_f computes it (hardware exp above |x| = 0.5, Taylor series to x^8 below),
+// with both branches evaluated and one selected, so that an unrolled loop needs no divergent
+// control flow
+__device__ __forceinline__ float expm1_sel(float x) {
+  const float big = exp2_hw(x * kLog2e) - 1.0f;
+  float r = __builtin_fmaf(x, 1.0f / 8.0f, 1.0f);
+  r = __builtin_fmaf(x * (1.0f / 7.0f), r, 1.0f);
+  r = __builtin_fmaf(x * (1.0f / 6.0f), r, 1.0f);
+  r = __builtin_fmaf(x * (1.0f / 5.0f), r, 1.0f);
+  r = __builtin_fmaf(x * (1.0f / 4.0f), r, 1.0f);
+  r = __builtin_fmaf(x * (1.0f / 3.0f), r, 1.0f);
+  r = __builtin_fmaf(x * 0.5f, r, 1.0f);
+  return fabsf(x) > 0.5f ? big : x * r;
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+// v[0..7] in every lane of a 16-lane row -> lane n returns the row's sum of v[n >> 1]. Steps 1-3
+// pair lanes that differ in bit 3, 2, 1 of n (row_ror:8, half-row mirror, quad xor 2): each lane
+// keeps the half of the remaining values its bit selects and adds the partner's copy of them;
+// the last step adds the two copies of the one value left (quad xor 1). 22 VALU operations.
+__device__ __forceinline__ float tsum8(const float (&v)[8], int n) {
+  const bool b3 = n & 8, b2 = n & 4, b1 = n & 2;
+  float w[4], x[2];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) w[j] = (b3 ? v[j + 4] : v[j]) + dpp_f<0x128>(b3 ? v[j] : v[j + 4]);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) x[j] = (b2 ? w[j + 2] : w[j]) + dpp_f<0x141>(b2 ? w[j] : w[j + 2]);
+  const float y = (b1 ? x[1] : x[0]) + dpp_f<0x4E>(b1 ? x[0] : x[1]);
+  return y + dpp_f<0xB1>(y);
+}
+
 template <typename T, bool ZOH>
 __global__ __launch_bounds__(1024) void bw_scan_kernel(BwArgs a) {
-  __shared__ float ck_s[kNSB][1024];        // state checkpoints, one column per thread
-  __shared__ float red_s[kSB][16][32];      // per token, per wave: dB (16) | dC (16)
-  __shared__ float st_s[kSStage];           // the current sub-block's inputs
+  __shared__ float ck_s[kNSB2][1024];       // state checkpoints, one column per thread
+  __shared__ f32x4 red_s[16][2][64];        // per wave: MFMA [token, state] sums of dB | dC
+  __shared__ float st_s[kS2NQ * 1024];      // the current sub-block's inputs
 
   const int ncg = a.D / kCG;
   const int cg = blockIdx.x % ncg;
@@ -329,25 +369,25 @@ __global__ __launch_bounds__(1024) void bw_scan_kernel(BwArgs a) {
   const int c = wv * 4 + cl;                // channel within the group
   const int i = cg * kCG + c;
   const int t0 = r * kRT, t1 = min(a.L, t0 + kRT);
-  const int nsb = (t1 - t0 + kSB - 1) / kSB;
-  const float An = a.A[i * 16 + n];
+  const int nsb = (t1 - t0 + kSB2 - 1) / kSB2;
+  const float An = a.A[i * 16 + n], An2 = An * kLog2e;
+  const float rA = ZOH ? 1.0f / An : 0.f;   // ZOH: (e^(dt A) - 1) / A as expm1 times 1 / A
   const float Dv = a.Dskip[i];
   const int64_t so = (((int64_t)b * a.nr + r) * a.D + i) * 16 + n;
   const int64_t tb = (int64_t)b * a.L;
-  constexpr int NQ = kSStage / 1024;
-  float pf[NQ];
+  float pf[kS2NQ];   // q 0: dt, 1: u, 2: (dt u, formed at the stash), 3: dys, 4: B|C
   auto fetch = [&](int j) {
-    const int tj = t0 + j * kSB;
+    const int tj = t0 + j * kSB2;
 #pragma unroll
-    for (int q = 0; q < NQ; ++q) {
+    for (int q = 0; q < kS2NQ; ++q) {
       const int e = tid + 1024 * q;
       float v = 0.f;
-      if (e < 3 * kSF) {
-        const int off = e % kSF, k = off >> 6, ch = off & 63;
-        const float *src = e < kSF ? a.dt : (e < 2 * kSF ? a.u : a.dys);
-        if (tj + k < t1) v = src[(tb + tj + k) * a.D + cg * kCG + ch];
-      } else {
-        const int off = e - 3 * kSF, k = off >> 5, ch = off & 31;
+      if (q < 4) {
+        const int k = tid >> 6, ch = tid & 63;
+        const float *src = q == 0 ? a.dt : (q == 1 ? a.u : a.dys);
+        if (q != 2 && tj + k < t1) v = src[(tb + tj + k) * a.D + cg * kCG + ch];
+      } else if (e < kS2Stage) {
+        const int off = e - 4 * kSF2, k = off >> 5, ch = off & 31;
         if (tj + k < t1) v = a.bc[(tb + tj + k) * 32 + ch];
       }
       pf[q] = v;
@@ -355,13 +395,20 @@ __global__ __launch_bounds__(1024) void bw_scan_kernel(BwArgs a) {
   };
   auto stash = [&]() {
 #pragma unroll
-    for (int q = 0; q < NQ; ++q) st_s[tid + 1024 * q] = pf[q];
+    for (int q = 0; q < kS2NQ; ++q)
+      if (q < 4 || tid + 1024 * q < kS2Stage)
+        st_s[tid + 1024 * q] = q == 2 ? pf[0] * pf[1] : pf[q];
   };
-  const float *s_dt = st_s, *s_u = st_s + kSF, *s_dys = st_s + 2 * kSF, *s_bc = st_s + 3 * kSF;
+  const float *s_dt = st_s, *s_u = st_s + kSF2, *s_dtu = st_s + 2 * kSF2,
+              *s_dys = st_s + 3 * kSF2, *s_bc = st_s + 4 * kSF2;
+  // input contribution of token k to the state: bb_t u_t
+  auto bu_of = [&](int k, float dtv) {
+    if (ZOH) return expm1_sel(dtv * An) * rA * s_bc[k * 32 + n] * s_u[k * kCG + c];
+    return s_dtu[k * kCG + c] * s_bc[k * 32 + n];
+  };
 
   // pass 1: true states from the range's start state; checkpoints; ys = C.h + D u for the gate
   float h = a.rS[so];
-  float dD = 0.f;
   fetch(0);
   for (int j = 0; j < nsb; ++j) {
     __syncthreads();
@@ -369,102 +416,101 @@ __global__ __launch_bounds__(1024) void bw_scan_kernel(BwArgs a) {
     __syncthreads();
     if (j + 1 < nsb) fetch(j + 1);
     ck_s[j][tid] = h;
-    const int tj = t0 + j * kSB;
+    float yp[8];
 #pragma unroll
-    for (int k = 0; k < kSB; ++k) {
-      if (tj + k < t1) {
-        const float dtv = s_dt[k * kCG + c], uv = s_u[k * kCG + c];
-        const float av = exp2_hw(dtv * An * kLog2e);
-        const float bb = (ZOH ? expm1_f(dtv * An) / An : dtv) * s_bc[k * 32 + n];
-        h = __builtin_fmaf(av, h, bb * uv);
-        const float ys = row_sum16(s_bc[k * 32 + 16 + n] * h);
-        if (n == 0) {
-          a.ys[(tb + tj + k) * a.D + i] = __builtin_fmaf(Dv, uv, ys);
-          dD = __builtin_fmaf(s_dys[k * kCG + c], uv, dD);
-        }
+    for (int k = 0; k < kSB2; ++k) {
+      const float dtv = s_dt[k * kCG + c];
+      h = __builtin_fmaf(exp2_hw(dtv * An2), h, bu_of(k, dtv));
+      yp[k & 7] = s_bc[k * 32 + 16 + n] * h;
+      if ((k & 7) == 7) {
+        const float ys = tsum8(yp, n);       // token k - 7 + n / 2 (both lanes of a pair)
+        const int kt = k - 7 + (n >> 1), t = t0 + j * kSB2 + kt;
+        if (!(n & 1) && t < t1)
+          a.ys[(tb + t) * a.D + i] = __builtin_fmaf(Dv, s_u[kt * kCG + c], ys);
       }
     }
   }
 
   // pass 2: sub-blocks in reverse; carry = a_{t+1} dh_{t+1}
   float carry = a.rR[so];
-  float dA = 0.f;
+  float dA = 0.f, dD = 0.f;
   fetch(nsb - 1);
   for (int j = nsb - 1; j >= 0; --j) {
     __syncthreads();     // the stage and red_s are free (previous sub-block fully consumed)
     stash();
     __syncthreads();
     if (j > 0) fetch(j - 1);
-    const int tj = t0 + j * kSB;
-    float hist[kSB + 1], ah[kSB];
+    const int tj = t0 + j * kSB2;
+    f32x4 accB = {0.f, 0.f, 0.f, 0.f}, accC = {0.f, 0.f, 0.f, 0.f};
+    float gv[8];                             // window of 4 tokens: d dt terms | du terms
+    // A = e_k for token k: 1 in lane n == k of each row, moved down one lane per token
+    float oh = n == kSB2 - 1 ? 1.f : 0.f;
+    float hist[kSB2 + 1], ah[kSB2];
     hist[0] = ck_s[j][tid];
 #pragma unroll
-    for (int k = 0; k < kSB; ++k) {
-      if (tj + k < t1) {
-        const float dtv = s_dt[k * kCG + c];
-        const float av = exp2_hw(dtv * An * kLog2e);
-        const float bb = (ZOH ? expm1_f(dtv * An) / An : dtv) * s_bc[k * 32 + n];
-        ah[k] = av;
-        hist[k + 1] = __builtin_fmaf(av, hist[k], bb * s_u[k * kCG + c]);
-      } else {
-        ah[k] = 0.f;
-        hist[k + 1] = 0.f;
-      }
+    for (int k = 0; k < kSB2; ++k) {
+      const float dtv = s_dt[k * kCG + c];
+      ah[k] = exp2_hw(dtv * An2);
+      hist[k + 1] = __builtin_fmaf(ah[k], hist[k], bu_of(k, dtv));
     }
+    // reverse walk
 #pragma unroll
-    for (int k = kSB - 1; k >= 0; --k) {
-      const int t = tj + k;
-      float pB = 0.f, pC = 0.f;
-      if (t < t1) {
-        const float dtv = s_dt[k * kCG + c], uv = s_u[k * kCG + c];
-        const float Bn = s_bc[k * 32 + n], Cn = s_bc[k * 32 + 16 + n];
-        const float dysv = s_dys[k * kCG + c];
-        const float av = ah[k];
-        const float dh = __builtin_fmaf(Cn, dysv, carry);
-        const float dAb = dh * hist[k];           // d / d a_t
-        const float dBb = dh * uv;                // d / d bb_t
-        float gdt, gdu;
-        if (ZOH) {
-          const float x = dtv * An;
-          const float E = expm1_f(x);
-          gdt = dAb * av * An + dBb * av * Bn;
-          dA += dAb * av * dtv + dBb * Bn * (x * av - E) / (An * An);
-          pB = dBb * E / An;
-          gdu = dh * (E / An) * Bn;
-        } else {
-          gdt = __builtin_fmaf(dAb * av, An, dBb * Bn);
-          dA = __builtin_fmaf(dAb * av, dtv, dA);
-          pB = dBb * dtv;
-          gdu = dh * dtv * Bn;
-        }
-        pC = dysv * hist[k + 1];
-        carry = av * dh;
-        const float sdt = row_sum16(gdt), sdu = row_sum16(gdu);
-        if (n == 0) {
-          const int64_t e = (tb + t) * a.D + i;
-          a.dt[e] = sdt;                               // d / d dt (dt is not read again)
-          a.du[e] = __builtin_fmaf(Dv, dysv, sdu);     // d / du from the scan and D u
-        }
+    for (int k = kSB2 - 1; k >= 0; --k) {
+      const float dtv = s_dt[k * kCG + c], uv = s_u[k * kCG + c];
+      const float Bn = s_bc[k * 32 + n], Cn = s_bc[k * 32 + 16 + n];
+      const float dysv = s_dys[k * kCG + c];
+      const float av = ah[k];
+      const float dh = __builtin_fmaf(Cn, dysv, carry);
+      const float ra = dh * hist[k] * av;      // d / d a_t, times a_t
+      float pB, gdt, gdu;
+      if (ZOH) {
+        const float x = dtv * An;
+        const float E = expm1_sel(x), q = E * rA;
+        const float dBb = dh * uv;
+        gdt = ra * An + dBb * av * Bn;
+        dA += ra * dtv + dBb * Bn * (x * av - E) * rA * rA;
+        pB = dBb * q;
+        gdu = dh * q * Bn;
+      } else {
+        const float gB = dh * Bn;
+        gdt = __builtin_fmaf(ra, An, gB * uv);
+        dA = __builtin_fmaf(ra, dtv, dA);
+        pB = dh * s_dtu[k * kCG + c];
+        gdu = gB * dtv;
       }
-      // the wave's 4 channels, then (lanes 0..15) one row per wave in LDS
-      pB += __shfl_xor(pB, 16, 64);
-      pB += __shfl_xor(pB, 32, 64);
-      pC += __shfl_xor(pC, 16, 64);
-      pC += __shfl_xor(pC, 32, 64);
-      if (cl == 0) {
-        red_s[k][wv][n] = pB;
-        red_s[k][wv][16 + n] = pC;
+      const float pC = dysv * hist[k + 1];
+      carry = av * dh;
+      dD = __builtin_fmaf(dysv, uv, dD);
+      accB = __builtin_amdgcn_mfma_f32_16x16x4f32(oh, pB, accB, 0, 0, 0);   // row k += terms
+      accC = __builtin_amdgcn_mfma_f32_16x16x4f32(oh, pC, accC, 0, 0, 0);
+      oh = dpp_f<0x12F>(oh);                   // row_ror:15: lane n takes lane n + 1's
+      gv[k & 3] = gdt;
+      gv[4 + (k & 3)] = gdu;
+      if ((k & 3) == 0) {
+        // lane n: d dt (n < 8) or du (n >= 8) of token k + (n / 2) % 4 (both lanes of a pair)
+        const float sv = tsum8(gv, n);
+        const int kt = k + ((n >> 1) & 3), t = tj + kt;
+        if (!(n & 1) && t < t1) {
+          const int64_t e = (tb + t) * a.D + i;
+          if (n < 8) a.dt[e] = sv;             // d / d dt (dt is not read again)
+          else a.du[e] = __builtin_fmaf(Dv, s_dys[kt * kCG + c], sv);   // with D u's term
+        }
       }
     }
+    // lane (n, cl): accB[q] = sum over the wave's channels of dB terms of token 4 cl + q, state n
+    red_s[wv][0][lane] = accB;
+    red_s[wv][1][lane] = accC;
     __syncthreads();
-    {
-      const int k = tid >> 5, cc = tid & 31;
-      const int t = tj + k;
+    if (tid < kSB2 * 32) {
+      const int m = tid >> 5, v = tid & 31, qn = v >> 4, sn = v & 15;
+      const int t = tj + m;
       if (t < t1) {
+        const float *rs = (const float *)red_s;
+        const int off = (qn * 64 + 16 * (m >> 2) + sn) * 4 + (m & 3);
         float sum = 0.f;
 #pragma unroll
-        for (int w = 0; w < 16; ++w) sum += red_s[k][w][cc];
-        a.bc_part[((tb + t) * ncg + cg) * 32 + cc] = sum;
+        for (int w = 0; w < 16; ++w) sum += rs[w * 512 + off];
+        a.bc_part[((tb + t) * ncg + cg) * 32 + v] = sum;
       }
     }
   }
