@@ -413,7 +413,7 @@ BwWs bw_layout(const mm_shape &s) {
   take(w.rR, SR);
   take(w.dA_part, SR);
   take(w.dD_part, (size_t)s.batch * nr * D);
-  take(w.bc_part, T * (D / 64) * 32);
+  take(w.bc_part, T * (D / 32) * 32);   // per token, per 32-channel group of the reverse scan
   take(w.dbc, T * 32);
   take(w.ddtn, T * R);
   take(w.dxd, T * W);

@@ -315,10 +315,12 @@ __global__ __launch_bounds__(256) void bw_range_carry_kernel(BwArgs a) {
 // the 16 waves are added in a fixed order.
 constexpr int kSB2 = 16;                        // tokens per recomputed sub-block
 constexpr int kNSB2 = kRT / kSB2;               // sub-blocks per range
-constexpr int kSF2 = kSB2 * kCG;                // floats per staged [kSB2][64] array
-constexpr int kS2Stage = 4 * kSF2 + kSB2 * 32;  // dt | u | dt u | dys | B|C
-constexpr int kS2NQ = (kS2Stage + 1023) / 1024;
-static_assert(kSF2 == 1024, "one staged array per 1024 threads");
+constexpr int kCG2 = 32;                        // channels per reverse-scan workgroup
+constexpr int kST2 = kCG2 * 16;                 // threads: (channel, state)
+constexpr int kW2 = kST2 / 64;                  // waves
+constexpr int kSF2 = kSB2 * kCG2;               // floats per staged [kSB2][32] array
+constexpr int kS2NQ = 5;                        // dt | u | dt u | dys | B|C, one element each
+static_assert(kSF2 == kST2 && kSB2 * 32 == kST2, "one staged element per thread and array");
 
 // expm1 as expm1_f computes it (hardware exp above |x| = 0.5, Taylor series to x^8 below),
 // with both branches evaluated and one selected, so that an unrolled loop needs no divergent
@@ -355,19 +357,19 @@ __device__ __forceinline__ float tsum8(const float (&v)[8], int n) {
 }
 
 template <typename T, bool ZOH>
-__global__ __launch_bounds__(1024) void bw_scan_kernel(BwArgs a) {
-  __shared__ float ck_s[kNSB2][1024];       // state checkpoints, one column per thread
-  __shared__ f32x4 red_s[16][2][64];        // per wave: MFMA [token, state] sums of dB | dC
-  __shared__ float st_s[kS2NQ * 1024];      // the current sub-block's inputs
+__global__ __launch_bounds__(kST2, 4) void bw_scan_kernel(BwArgs a) {
+  __shared__ float ck_s[kNSB2][kST2];       // state checkpoints, one column per thread
+  __shared__ f32x4 red_s[kW2][2][64];       // per wave: MFMA [token, state] sums of dB | dC
+  __shared__ float st_s[kS2NQ * kST2];      // the current sub-block's inputs
 
-  const int ncg = a.D / kCG;
+  const int ncg = a.D / kCG2;
   const int cg = blockIdx.x % ncg;
   const int r = (blockIdx.x / ncg) % a.nr;
   const int b = blockIdx.x / (ncg * a.nr);
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int n = lane & 15, cl = lane >> 4;
   const int c = wv * 4 + cl;                // channel within the group
-  const int i = cg * kCG + c;
+  const int i = cg * kCG2 + c;
   const int t0 = r * kRT, t1 = min(a.L, t0 + kRT);
   const int nsb = (t1 - t0 + kSB2 - 1) / kSB2;
   const float An = a.A[i * 16 + n], An2 = An * kLog2e;
@@ -380,31 +382,29 @@ __global__ __launch_bounds__(1024) void bw_scan_kernel(BwArgs a) {
     const int tj = t0 + j * kSB2;
 #pragma unroll
     for (int q = 0; q < kS2NQ; ++q) {
-      const int e = tid + 1024 * q;
+      const int k = tid >> 5, ch = tid & 31;   // [kSB2][32] element of every array
       float v = 0.f;
-      if (q < 4) {
-        const int k = tid >> 6, ch = tid & 63;
-        const float *src = q == 0 ? a.dt : (q == 1 ? a.u : a.dys);
-        if (q != 2 && tj + k < t1) v = src[(tb + tj + k) * a.D + cg * kCG + ch];
-      } else if (e < kS2Stage) {
-        const int off = e - 4 * kSF2, k = off >> 5, ch = off & 31;
-        if (tj + k < t1) v = a.bc[(tb + tj + k) * 32 + ch];
+      if (q != 2 && tj + k < t1) {
+        if (q < 4) {
+          const float *src = q == 0 ? a.dt : (q == 1 ? a.u : a.dys);
+          v = src[(tb + tj + k) * a.D + cg * kCG2 + ch];
+        } else {
+          v = a.bc[(tb + tj + k) * 32 + ch];
+        }
       }
       pf[q] = v;
     }
   };
   auto stash = [&]() {
 #pragma unroll
-    for (int q = 0; q < kS2NQ; ++q)
-      if (q < 4 || tid + 1024 * q < kS2Stage)
-        st_s[tid + 1024 * q] = q == 2 ? pf[0] * pf[1] : pf[q];
+    for (int q = 0; q < kS2NQ; ++q) st_s[tid + kST2 * q] = q == 2 ? pf[0] * pf[1] : pf[q];
   };
   const float *s_dt = st_s, *s_u = st_s + kSF2, *s_dtu = st_s + 2 * kSF2,
               *s_dys = st_s + 3 * kSF2, *s_bc = st_s + 4 * kSF2;
   // input contribution of token k to the state: bb_t u_t
   auto bu_of = [&](int k, float dtv) {
-    if (ZOH) return expm1_sel(dtv * An) * rA * s_bc[k * 32 + n] * s_u[k * kCG + c];
-    return s_dtu[k * kCG + c] * s_bc[k * 32 + n];
+    if (ZOH) return expm1_sel(dtv * An) * rA * s_bc[k * 32 + n] * s_u[k * kCG2 + c];
+    return s_dtu[k * kCG2 + c] * s_bc[k * 32 + n];
   };
 
   // pass 1: true states from the range's start state; checkpoints; ys = C.h + D u for the gate
@@ -419,14 +419,14 @@ __global__ __launch_bounds__(1024) void bw_scan_kernel(BwArgs a) {
     float yp[8];
 #pragma unroll
     for (int k = 0; k < kSB2; ++k) {
-      const float dtv = s_dt[k * kCG + c];
+      const float dtv = s_dt[k * kCG2 + c];
       h = __builtin_fmaf(exp2_hw(dtv * An2), h, bu_of(k, dtv));
       yp[k & 7] = s_bc[k * 32 + 16 + n] * h;
       if ((k & 7) == 7) {
         const float ys = tsum8(yp, n);       // token k - 7 + n / 2 (both lanes of a pair)
         const int kt = k - 7 + (n >> 1), t = t0 + j * kSB2 + kt;
         if (!(n & 1) && t < t1)
-          a.ys[(tb + t) * a.D + i] = __builtin_fmaf(Dv, s_u[kt * kCG + c], ys);
+          a.ys[(tb + t) * a.D + i] = __builtin_fmaf(Dv, s_u[kt * kCG2 + c], ys);
       }
     }
   }
@@ -449,16 +449,16 @@ __global__ __launch_bounds__(1024) void bw_scan_kernel(BwArgs a) {
     hist[0] = ck_s[j][tid];
 #pragma unroll
     for (int k = 0; k < kSB2; ++k) {
-      const float dtv = s_dt[k * kCG + c];
+      const float dtv = s_dt[k * kCG2 + c];
       ah[k] = exp2_hw(dtv * An2);
       hist[k + 1] = __builtin_fmaf(ah[k], hist[k], bu_of(k, dtv));
     }
     // reverse walk
 #pragma unroll
     for (int k = kSB2 - 1; k >= 0; --k) {
-      const float dtv = s_dt[k * kCG + c], uv = s_u[k * kCG + c];
+      const float dtv = s_dt[k * kCG2 + c], uv = s_u[k * kCG2 + c];
       const float Bn = s_bc[k * 32 + n], Cn = s_bc[k * 32 + 16 + n];
-      const float dysv = s_dys[k * kCG + c];
+      const float dysv = s_dys[k * kCG2 + c];
       const float av = ah[k];
       const float dh = __builtin_fmaf(Cn, dysv, carry);
       const float ra = dh * hist[k] * av;      // d / d a_t, times a_t
@@ -475,7 +475,7 @@ __global__ __launch_bounds__(1024) void bw_scan_kernel(BwArgs a) {
         const float gB = dh * Bn;
         gdt = __builtin_fmaf(ra, An, gB * uv);
         dA = __builtin_fmaf(ra, dtv, dA);
-        pB = dh * s_dtu[k * kCG + c];
+        pB = dh * s_dtu[k * kCG2 + c];
         gdu = gB * dtv;
       }
       const float pC = dysv * hist[k + 1];
@@ -493,7 +493,7 @@ __global__ __launch_bounds__(1024) void bw_scan_kernel(BwArgs a) {
         if (!(n & 1) && t < t1) {
           const int64_t e = (tb + t) * a.D + i;
           if (n < 8) a.dt[e] = sv;             // d / d dt (dt is not read again)
-          else a.du[e] = __builtin_fmaf(Dv, s_dys[kt * kCG + c], sv);   // with D u's term
+          else a.du[e] = __builtin_fmaf(Dv, s_dys[kt * kCG2 + c], sv);   // with D u's term
         }
       }
     }
@@ -501,7 +501,7 @@ __global__ __launch_bounds__(1024) void bw_scan_kernel(BwArgs a) {
     red_s[wv][0][lane] = accB;
     red_s[wv][1][lane] = accC;
     __syncthreads();
-    if (tid < kSB2 * 32) {
+    {   // one output per thread: token m, value v (dB states 0-15 | dC states 0-15)
       const int m = tid >> 5, v = tid & 31, qn = v >> 4, sn = v & 15;
       const int t = tj + m;
       if (t < t1) {
@@ -509,7 +509,7 @@ __global__ __launch_bounds__(1024) void bw_scan_kernel(BwArgs a) {
         const int off = (qn * 64 + 16 * (m >> 2) + sn) * 4 + (m & 3);
         float sum = 0.f;
 #pragma unroll
-        for (int w = 0; w < 16; ++w) sum += rs[w * 512 + off];
+        for (int w = 0; w < kW2; ++w) sum += rs[w * 512 + off];
         a.bc_part[((tb + t) * ncg + cg) * 32 + v] = sum;
       }
     }
@@ -908,11 +908,11 @@ hipError_t bw_dispatch(const BwArgs &a, int stage, hipStream_t s) {
       else hipLaunchKernelGGL(bw_range_transfer_kernel<false>, rgrid, dim3(1024), 0, s, a);
       const int64_t nc = (int64_t)a.B * a.D * 16;
       hipLaunchKernelGGL(bw_range_carry_kernel, dim3((unsigned)((nc + 255) / 256)), dim3(256), 0, s, a);
-      const unsigned grid = (unsigned)(a.B * a.nr * (a.D / kCG));
-      if (a.zoh) hipLaunchKernelGGL((bw_scan_kernel<T, true>), dim3(grid), dim3(1024), 0, s, a);
-      else hipLaunchKernelGGL((bw_scan_kernel<T, false>), dim3(grid), dim3(1024), 0, s, a);
+      const unsigned grid = (unsigned)(a.B * a.nr * (a.D / kCG2));
+      if (a.zoh) hipLaunchKernelGGL((bw_scan_kernel<T, true>), dim3(grid), dim3(kST2), 0, s, a);
+      else hipLaunchKernelGGL((bw_scan_kernel<T, false>), dim3(grid), dim3(kST2), 0, s, a);
       hipLaunchKernelGGL(bw_rowsum_kernel, dim3((unsigned)((a.T * 32 + 255) / 256)), dim3(256), 0, s,
-                         a.bc_part, a.dbc, a.T, a.D / kCG);
+                         a.bc_part, a.dbc, a.T, a.D / kCG2);
       hipLaunchKernelGGL(bw_post_scan_kernel<T>, tok_grid, dim3(256), 0, s, a);
       break;
     }
