@@ -407,7 +407,7 @@ BwWs bw_layout(const mm_shape &s) {
   take(w.sig, T * D);
   take(w.dys, T * D);
   take(w.du, T * D);
-  take(w.ys, (sp ? Tp : T) * D);
+  take(w.ys, sp ? Tp * D : 0);   // holds the dp^T planes
   take(w.rP, SR);
   take(w.rS, SR);
   take(w.rR, SR);
@@ -539,7 +539,6 @@ mm_status backward_impl(const mm_shape *s, const mm_params *p, const void *xz, c
     } else {
       MM_TRY(launch_gemm_f32({a.dtn, wdt, a.dt, (int)T, D, R, R, 1, 1, R, D, 1, 0}, st));
     }
-    MM_TRY(launch_backward_stage(s->io_dtype, a, 1, st));                    // dt, sigmoid, dys
   }
   {
     StageScope sc(timer, st, MM_STAGE_BWD_SCAN);

@@ -17,24 +17,26 @@
 //                             gradients): fp32 16x16x4 MFMA, 128 x 128 (128 x 64 for
 //                             N <= 512) tiles, any strides
 //   (norm_kernel)             the forward's RMSNorm of dt_low, B, C (fp32 mode)
-//   bw_pointwise_kernel       dt = softplus(p), sigmoid(p), dys = dy SiLU(z)
 //   bw_range_transfer_kernel  per range of kRT tokens and (channel, state), 64 channels per
 //                             workgroup with staged inputs, one forward pass: the forward
 //                             transfer (prod a, local end state) and the reverse one (local
-//                             a_t0 dh_t0 from zero)
+//                             a_t0 dh_t0 from zero). The staging forms dt = softplus(p) and
+//                             dys = dy SiLU(z) from dt_proj's product, dy and z, once per
+//                             (token, channel); neither goes to memory
 //   bw_range_carry_kernel     sequential over ranges: each range's true start state and the
 //                             dh carry entering it from later ranges; the last carry is the
 //                             gradient of the carried SSM state
-//   bw_scan_kernel            per range, 64 channels x 16 states per workgroup: a forward pass
-//                             (ys = C.h + D u for the gate, checkpoints every kSB2 tokens in
-//                             LDS), then sub-blocks in reverse, each recomputed into registers
-//                             and walked backward. Each sub-block's inputs are staged in LDS by
-//                             coalesced loads issued one sub-block ahead (the recurrence never
-//                             waits on global memory). Sums over the 16 states: transposed DPP
-//                             reductions within a 16-lane row; dB and dC (shared by all
-//                             channels) sum over the wave's 4 channels on fp32 MFMA, over the
-//                             16 waves in LDS, into per-workgroup rows
-//   bw_post_scan_kernel       d(dt_proj pre-activation) = d dt sigmoid(p); dz = dy ys SiLU'(z)
+//   bw_scan_kernel            per range, 32 channels x 16 states per workgroup: a forward pass
+//                             (ys = C.h + D u, and the gate's dz = dy ys SiLU'(z) straight to
+//                             dxz; checkpoints every kSB2 tokens in LDS), then sub-blocks in
+//                             reverse, each recomputed into registers and walked backward,
+//                             writing d(dt_proj pre-activation) = d dt sigmoid(p) and du. Each
+//                             sub-block's inputs are staged in LDS by coalesced loads issued one
+//                             sub-block ahead (the recurrence never waits on global memory).
+//                             Sums over the 16 states: transposed DPP reductions within a
+//                             16-lane row; dB and dC (shared by all channels) sum over the
+//                             wave's 4 channels on fp32 MFMA, over the 8 waves in LDS, into
+//                             per-workgroup rows
 //   bw_rowsum_kernel          dB | dC from those per-workgroup rows
 //   bw_norm_bwd_kernel        the three RMSNorm backwards per token (+ gain terms)
 //   bw_colsum_kernels         fixed-order column sums (bias, gains, D, A, conv partials)
@@ -173,28 +175,19 @@ __global__ __launch_bounds__(256) void bw_conv_u_kernel(BwArgs a) {
   }
 }
 
-// ---------------------------------------------------------------- dt, sigmoid(p), dys
-// one token per blockIdx.x, 4 channels per thread (blockIdx.y: blocks of 1024 channels)
-template <typename T>
-__global__ __launch_bounds__(256) void bw_pointwise_kernel(BwArgs a) {
-  const int i0 = (blockIdx.y * 256 + threadIdx.x) * 4;
-  if (i0 >= a.D) return;
-  const int64_t tok = blockIdx.x, e = tok * a.D + i0;
-  const float4 pre = *(const float4 *)(a.dt + e);   // dt holds dt_proj's product on entry
-  const float4 bias = *(const float4 *)(a.dt_b + i0);
-  const float p[4] = {pre.x + bias.x, pre.y + bias.y, pre.z + bias.z, pre.w + bias.w};
-  float z[4], dy[4], dt[4], sg[4], dys[4];
-  v4io<T>::ld((const T *)a.xz + tok * 2 * a.D + a.D + i0, z);
-  v4io<T>::ld((const T *)a.dy + e, dy);
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    dt[c] = softplus_f(p[c]);
-    sg[c] = sigmoid_f(p[c]);
-    dys[c] = dy[c] * silu_f(z[c]);
-  }
-  v4io<float>::st(a.dt + e, dt);
-  v4io<float>::st(a.sig + e, sg);
-  v4io<float>::st(a.dys + e, dys);
+// expm1 as expm1_f computes it (hardware exp above |x| = 0.5, Taylor series to x^8 below),
+// with both branches evaluated and one selected, so that an unrolled loop needs no divergent
+// control flow
+__device__ __forceinline__ float expm1_sel(float x) {
+  const float big = exp2_hw(x * kLog2e) - 1.0f;
+  float r = __builtin_fmaf(x, 1.0f / 8.0f, 1.0f);
+  r = __builtin_fmaf(x * (1.0f / 7.0f), r, 1.0f);
+  r = __builtin_fmaf(x * (1.0f / 6.0f), r, 1.0f);
+  r = __builtin_fmaf(x * (1.0f / 5.0f), r, 1.0f);
+  r = __builtin_fmaf(x * (1.0f / 4.0f), r, 1.0f);
+  r = __builtin_fmaf(x * (1.0f / 3.0f), r, 1.0f);
+  r = __builtin_fmaf(x * 0.5f, r, 1.0f);
+  return fabsf(x) > 0.5f ? big : x * r;
 }
 
 // ---------------------------------------------------------------- per-range transfers
@@ -210,7 +203,7 @@ __global__ __launch_bounds__(256) void bw_pointwise_kernel(BwArgs a) {
 // they are.
 constexpr int kRTF = kSB * kCG;                  // floats per staged [kSB][64] array
 constexpr int kRTStage = 3 * kRTF + kSB * 32;    // dt | u | dys | B|C
-template <bool ZOH>
+template <typename T, bool ZOH>
 __global__ __launch_bounds__(1024) void bw_range_transfer_kernel(BwArgs a) {
   __shared__ float st_s[kRTStage];
   const int ncg = a.D / kCG;
@@ -223,30 +216,43 @@ __global__ __launch_bounds__(1024) void bw_range_transfer_kernel(BwArgs a) {
   const int nsb = (t1 - t0 + kSB - 1) / kSB;
   const int64_t tb = (int64_t)b * a.L;
   const float An = a.A[i * 16 + n], An2 = An * kLog2e;
-  constexpr int NQ = kRTStage / 1024;   // q 0-1: dt, 2-3: u (same elements as q - 2), 4-5: dys, 6: B|C
-  static_assert(NQ == 7 && 2 * kRTF == 4096, "staging slots");
-  float pf[NQ];
+  const float rA = ZOH ? 1.0f / An : 0.f;   // ZOH: (e^(dt A) - 1) / A as expm1 times 1 / A
+  // this thread stages elements tid and tid + 1024 of each [kSB][64] array: channel tid & 63
+  const int sch = tid & 63;
+  const float sbias = a.dt_b[cg * kCG + sch];
+  static_assert(kRTF == 2 * 1024 && kSB * 32 == 1024, "two staged elements per thread, one of B|C");
+  // per element: dt_proj's product (pre-bias), u, dy, z; then B|C
+  float pp[2], pu[2], pdy[2], pz[2], pbc;
+  bool pl[2];   // the element's token lies inside the range
   auto fetch = [&](int j) {
     const int tj = t0 + j * kSB;
 #pragma unroll
-    for (int q = 0; q < NQ; ++q) {
-      const int e = tid + 1024 * q;
-      float v = 0.f;
-      if (e < 3 * kRTF) {
-        const int off = e % kRTF, k = off >> 6, ch = off & 63;
-        const float *src = e < kRTF ? a.dt : (e < 2 * kRTF ? a.u : a.dys);
-        if (tj + k < t1) v = src[(tb + tj + k) * a.D + cg * kCG + ch];
-      } else {
-        const int off = e - 3 * kRTF, k = off >> 5, ch = off & 31;
-        if (tj + k < t1) v = a.bc[(tb + tj + k) * 32 + ch];
+    for (int h = 0; h < 2; ++h) {
+      const int k = (tid >> 6) + 16 * h;
+      pp[h] = pu[h] = pdy[h] = pz[h] = 0.f;
+      pl[h] = tj + k < t1;
+      if (pl[h]) {
+        const int64_t tok = tb + tj + k, e = tok * a.D + cg * kCG + sch;
+        pp[h] = a.dt[e];
+        pu[h] = a.u[e];
+        pdy[h] = io<T>::ld((const T *)a.dy + e);
+        pz[h] = io<T>::ld((const T *)a.xz + tok * 2 * a.D + a.D + cg * kCG + sch);
       }
-      pf[q] = v;
     }
+    const int k = tid >> 5;
+    pbc = tj + k < t1 ? a.bc[(tb + tj + k) * 32 + (tid & 31)] : 0.f;
   };
+  // dt = softplus(p), p = product + bias; dys = dy SiLU(z); without ZOH the u slot holds dt u.
+  // A zero-staged token has dt = 0 (not softplus(bias)), so it stays an identity step.
   auto stash = [&]() {
 #pragma unroll
-    for (int q = 0; q < NQ; ++q)
-      st_s[tid + 1024 * q] = (!ZOH && (q == 2 || q == 3)) ? pf[q] * pf[q - 2] : pf[q];
+    for (int h = 0; h < 2; ++h) {
+      const float dt = pl[h] ? softplus_f(pp[h] + sbias) : 0.f;
+      st_s[tid + 1024 * h] = dt;
+      st_s[kRTF + tid + 1024 * h] = ZOH ? pu[h] : dt * pu[h];
+      st_s[2 * kRTF + tid + 1024 * h] = pdy[h] * silu_f(pz[h]);
+    }
+    st_s[3 * kRTF + tid] = pbc;
   };
   const float *s_dt = st_s, *s_u = st_s + kRTF, *s_dys = st_s + 2 * kRTF, *s_bc = st_s + 3 * kRTF;
 
@@ -261,7 +267,7 @@ __global__ __launch_bounds__(1024) void bw_range_transfer_kernel(BwArgs a) {
     for (int k = 0; k < kSB; ++k) {
       const float dtv = s_dt[k * kCG + c];
       const float av = exp2_hw(dtv * An2);
-      const float bu = ZOH ? expm1_f(dtv * An) / An * s_bc[k * 32 + n] * s_u[k * kCG + c]
+      const float bu = ZOH ? expm1_sel(dtv * An) * rA * s_bc[k * 32 + n] * s_u[k * kCG + c]
                            : s_u[k * kCG + c] * s_bc[k * 32 + n];
       S = __builtin_fmaf(av, S, bu);
       P *= av;
@@ -319,23 +325,9 @@ constexpr int kCG2 = 32;                        // channels per reverse-scan wor
 constexpr int kST2 = kCG2 * 16;                 // threads: (channel, state)
 constexpr int kW2 = kST2 / 64;                  // waves
 constexpr int kSF2 = kSB2 * kCG2;               // floats per staged [kSB2][32] array
-constexpr int kS2NQ = 5;                        // dt | u | dt u | dys | B|C, one element each
+// staged arrays: dt | u | dt u | dys | sigmoid(p) | dy SiLU'(z) | B|C, one element each
+constexpr int kS2NA = 7;
 static_assert(kSF2 == kST2 && kSB2 * 32 == kST2, "one staged element per thread and array");
-
-// expm1 as expm1_f computes it (hardware exp above |x| = 0.5, Taylor series to x^8 below),
-// with both branches evaluated and one selected, so that an unrolled loop needs no divergent
-// control flow
-__device__ __forceinline__ float expm1_sel(float x) {
-  const float big = exp2_hw(x * kLog2e) - 1.0f;
-  float r = __builtin_fmaf(x, 1.0f / 8.0f, 1.0f);
-  r = __builtin_fmaf(x * (1.0f / 7.0f), r, 1.0f);
-  r = __builtin_fmaf(x * (1.0f / 6.0f), r, 1.0f);
-  r = __builtin_fmaf(x * (1.0f / 5.0f), r, 1.0f);
-  r = __builtin_fmaf(x * (1.0f / 4.0f), r, 1.0f);
-  r = __builtin_fmaf(x * (1.0f / 3.0f), r, 1.0f);
-  r = __builtin_fmaf(x * 0.5f, r, 1.0f);
-  return fabsf(x) > 0.5f ? big : x * r;
-}
 
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float v) {
@@ -360,7 +352,8 @@ template <typename T, bool ZOH>
 __global__ __launch_bounds__(kST2, 4) void bw_scan_kernel(BwArgs a) {
   __shared__ float ck_s[kNSB2][kST2];       // state checkpoints, one column per thread
   __shared__ f32x4 red_s[kW2][2][64];       // per wave: MFMA [token, state] sums of dB | dC
-  __shared__ float st_s[kS2NQ * kST2];      // the current sub-block's inputs
+  __shared__ float st_s[kS2NA * kST2];      // the current sub-block's inputs
+  __shared__ float o_s[2][kSB2][kCG2];      // the current sub-block's per-(token, channel) outputs
 
   const int ncg = a.D / kCG2;
   const int cg = blockIdx.x % ncg;
@@ -377,30 +370,64 @@ __global__ __launch_bounds__(kST2, 4) void bw_scan_kernel(BwArgs a) {
   const float Dv = a.Dskip[i];
   const int64_t so = (((int64_t)b * a.nr + r) * a.D + i) * 16 + n;
   const int64_t tb = (int64_t)b * a.L;
-  float pf[kS2NQ];   // q 0: dt, 1: u, 2: (dt u, formed at the stash), 3: dys, 4: B|C
+  // this thread stages element tid of each array: token tid / 32, channel tid % 32
+  const int sk = tid >> 5, sch = tid & 31;
+  const float sbias = a.dt_b[cg * kCG2 + sch];
+  float pp, pu, pdy, pz, pbc;   // dt_proj's product (pre-bias), u, dy, z; B|C
+  bool pl;                      // the element's token lies inside the range
   auto fetch = [&](int j) {
-    const int tj = t0 + j * kSB2;
-#pragma unroll
-    for (int q = 0; q < kS2NQ; ++q) {
-      const int k = tid >> 5, ch = tid & 31;   // [kSB2][32] element of every array
-      float v = 0.f;
-      if (q != 2 && tj + k < t1) {
-        if (q < 4) {
-          const float *src = q == 0 ? a.dt : (q == 1 ? a.u : a.dys);
-          v = src[(tb + tj + k) * a.D + cg * kCG2 + ch];
-        } else {
-          v = a.bc[(tb + tj + k) * 32 + ch];
-        }
-      }
-      pf[q] = v;
+    const int64_t tok = tb + t0 + j * kSB2 + sk, e = tok * a.D + cg * kCG2 + sch;
+    pl = t0 + j * kSB2 + sk < t1;
+    pp = pu = pdy = pz = pbc = 0.f;
+    if (pl) {
+      pp = a.dt[e];
+      pu = a.u[e];
+      pdy = io<T>::ld((const T *)a.dy + e);
+      pz = io<T>::ld((const T *)a.xz + tok * 2 * a.D + a.D + cg * kCG2 + sch);
+      pbc = a.bc[tok * 32 + sch];
     }
   };
-  auto stash = [&]() {
-#pragma unroll
-    for (int q = 0; q < kS2NQ; ++q) st_s[tid + kST2 * q] = q == 2 ? pf[0] * pf[1] : pf[q];
+  // dt = softplus(p) and sigmoid(p), p = product + bias; dys = dy SiLU(z); dy SiLU'(z) for the
+  // gate's dz. A token past the range end gets dt = 0 and no inputs: an identity step.
+  // (the forward pass needs dy SiLU'(z), the reverse pass dys and sigmoid(p))
+  auto stash = [&](bool rev) {
+    const float p = pp + sbias;
+    const float dt = pl ? softplus_f(p) : 0.f;
+    st_s[tid] = dt;
+    st_s[kST2 + tid] = pu;
+    st_s[2 * kST2 + tid] = dt * pu;
+    if (rev) {
+      st_s[3 * kST2 + tid] = pdy * silu_f(pz);
+      st_s[4 * kST2 + tid] = sigmoid_f(p);
+    } else {
+      st_s[5 * kST2 + tid] = pdy * dsilu_f(pz);
+    }
+    st_s[6 * kST2 + tid] = pbc;
   };
-  const float *s_dt = st_s, *s_u = st_s + kSF2, *s_dtu = st_s + 2 * kSF2,
-              *s_dys = st_s + 3 * kSF2, *s_bc = st_s + 4 * kSF2;
+  // per-sub-block output tiles [kSB2][32], written by the lanes that own the sums and stored
+  // by one thread per element (whole rows of the 32 channels)
+  auto flush_dz = [&](int jp) {   // the forward pass's dz of sub-block jp
+    const int t = t0 + jp * kSB2 + sk;
+    if (t < t1)
+      io<T>::st((T *)a.dxz + (tb + t) * 2 * a.D + a.D + cg * kCG2 + sch, o_s[0][sk][sch]);
+  };
+  auto flush_dp_du = [&](int jp) {   // the reverse pass's d(dt_proj pre-activation) and du
+    const int t = t0 + jp * kSB2 + sk;
+    if (t < t1) {
+      const int64_t e = (tb + t) * a.D + cg * kCG2 + sch;
+      const float dp = o_s[0][sk][sch];
+      a.sig[e] = dp;
+      if (a.dp_hi) {
+        const bf16_t hi = f2bf(dp);
+        a.dp_hi[e] = hi;
+        a.dp_lo[e] = f2bf(dp - bf2f(hi));
+      }
+      a.du[e] = o_s[1][sk][sch];
+    }
+  };
+  const float *s_dt = st_s, *s_u = st_s + kST2, *s_dtu = st_s + 2 * kST2,
+              *s_dys = st_s + 3 * kST2, *s_sg = st_s + 4 * kST2, *s_gz = st_s + 5 * kST2,
+              *s_bc = st_s + 6 * kST2;
   // input contribution of token k to the state: bb_t u_t
   auto bu_of = [&](int k, float dtv) {
     if (ZOH) return expm1_sel(dtv * An) * rA * s_bc[k * 32 + n] * s_u[k * kCG2 + c];
@@ -412,7 +439,8 @@ __global__ __launch_bounds__(kST2, 4) void bw_scan_kernel(BwArgs a) {
   fetch(0);
   for (int j = 0; j < nsb; ++j) {
     __syncthreads();
-    stash();
+    stash(false);
+    if (j > 0) flush_dz(j - 1);
     __syncthreads();
     if (j + 1 < nsb) fetch(j + 1);
     ck_s[j][tid] = h;
@@ -425,8 +453,10 @@ __global__ __launch_bounds__(kST2, 4) void bw_scan_kernel(BwArgs a) {
       if ((k & 7) == 7) {
         const float ys = tsum8(yp, n);       // token k - 7 + n / 2 (both lanes of a pair)
         const int kt = k - 7 + (n >> 1), t = t0 + j * kSB2 + kt;
-        if (!(n & 1) && t < t1)
-          a.ys[(tb + t) * a.D + i] = __builtin_fmaf(Dv, s_u[kt * kCG2 + c], ys);
+        if (!(n & 1)) {   // the gate: dz = dy ys SiLU'(z), ys = C.h + D u
+          const float yv = __builtin_fmaf(Dv, s_u[kt * kCG2 + c], ys);
+          o_s[0][kt][c] = s_gz[kt * kCG2 + c] * yv;
+        }
       }
     }
   }
@@ -436,8 +466,9 @@ __global__ __launch_bounds__(kST2, 4) void bw_scan_kernel(BwArgs a) {
   float dA = 0.f, dD = 0.f;
   fetch(nsb - 1);
   for (int j = nsb - 1; j >= 0; --j) {
-    __syncthreads();     // the stage and red_s are free (previous sub-block fully consumed)
-    stash();
+    __syncthreads();     // the stage, red_s and o_s are free (previous sub-block consumed)
+    if (j == nsb - 1) flush_dz(j);   // the forward pass's last tile
+    stash(true);
     __syncthreads();
     if (j > 0) fetch(j - 1);
     const int tj = t0 + j * kSB2;
@@ -489,11 +520,10 @@ __global__ __launch_bounds__(kST2, 4) void bw_scan_kernel(BwArgs a) {
       if ((k & 3) == 0) {
         // lane n: d dt (n < 8) or du (n >= 8) of token k + (n / 2) % 4 (both lanes of a pair)
         const float sv = tsum8(gv, n);
-        const int kt = k + ((n >> 1) & 3), t = tj + kt;
-        if (!(n & 1) && t < t1) {
-          const int64_t e = (tb + t) * a.D + i;
-          if (n < 8) a.dt[e] = sv;             // d / d dt (dt is not read again)
-          else a.du[e] = __builtin_fmaf(Dv, s_dys[kt * kCG2 + c], sv);   // with D u's term
+        const int kt = k + ((n >> 1) & 3);
+        if (!(n & 1)) {
+          if (n < 8) o_s[0][kt][c] = sv * s_sg[kt * kCG2 + c];   // d dt sigmoid(p)
+          else o_s[1][kt][c] = __builtin_fmaf(Dv, s_dys[kt * kCG2 + c], sv);   // with D u's term
         }
       }
     }
@@ -513,38 +543,10 @@ __global__ __launch_bounds__(kST2, 4) void bw_scan_kernel(BwArgs a) {
         a.bc_part[((tb + t) * ncg + cg) * 32 + v] = sum;
       }
     }
+    flush_dp_du(j);
   }
   a.dA_part[so] = dA;
   if (n == 0) a.dD_part[((int64_t)b * a.nr + r) * a.D + i] = dD;
-}
-
-// after the scan: d(dt_proj pre-activation) = d dt * sigmoid(p) (into sig; with dp_hi set also
-// as bf16 hi / lo planes) and the gate's dz = dy ys SiLU'(z) (into dxz). Grid as the pointwise
-// kernel's.
-template <typename T>
-__global__ __launch_bounds__(256) void bw_post_scan_kernel(BwArgs a) {
-  const int i0 = (blockIdx.y * 256 + threadIdx.x) * 4;
-  if (i0 >= a.D) return;
-  const int64_t tok = blockIdx.x, e = tok * a.D + i0;
-  float sg[4], ddt[4], ys[4], z[4], dy[4], dz[4];
-  v4io<float>::ld(a.sig + e, sg);
-  v4io<float>::ld(a.dt + e, ddt);
-  v4io<float>::ld(a.ys + e, ys);
-  v4io<T>::ld((const T *)a.xz + tok * 2 * a.D + a.D + i0, z);
-  v4io<T>::ld((const T *)a.dy + e, dy);
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    sg[c] *= ddt[c];
-    dz[c] = dy[c] * ys[c] * dsilu_f(z[c]);
-  }
-  v4io<float>::st(a.sig + e, sg);
-  if (a.dp_hi) {
-    uint2 hi, lo;
-    split4(sg, hi, lo);
-    *(uint2 *)(a.dp_hi + e) = hi;
-    *(uint2 *)(a.dp_lo + e) = lo;
-  }
-  v4io<T>::st((T *)a.dxz + tok * 2 * a.D + a.D + i0, dz);
 }
 
 // dB | dC [T, 32] = sum over the channel groups of the scan's per-workgroup rows
@@ -889,8 +891,6 @@ int64_t bw_colsum_blocks(int64_t rows) { return (rows + kColRows - 1) / kColRows
 
 template <typename T>
 hipError_t bw_dispatch(const BwArgs &a, int stage, hipStream_t s) {
-  // one token per blockIdx.x, 1024 channels per blockIdx.y
-  const dim3 tok_grid((unsigned)a.T, (unsigned)((a.D + 1023) / 1024));
   switch (stage) {
     case 0: {
       const dim3 grid((unsigned)(a.B * ((a.L + kUStrip - 1) / kUStrip)), (unsigned)((a.D + 1023) / 1024));
@@ -899,13 +899,10 @@ hipError_t bw_dispatch(const BwArgs &a, int stage, hipStream_t s) {
       else hipLaunchKernelGGL((bw_conv_u_kernel<T, 4>), grid, dim3(256), 0, s, a);
       break;
     }
-    case 1:
-      hipLaunchKernelGGL(bw_pointwise_kernel<T>, tok_grid, dim3(256), 0, s, a);
-      break;
     case 2: {
       const dim3 rgrid((unsigned)(a.B * a.nr * (a.D / kCG)));
-      if (a.zoh) hipLaunchKernelGGL(bw_range_transfer_kernel<true>, rgrid, dim3(1024), 0, s, a);
-      else hipLaunchKernelGGL(bw_range_transfer_kernel<false>, rgrid, dim3(1024), 0, s, a);
+      if (a.zoh) hipLaunchKernelGGL((bw_range_transfer_kernel<T, true>), rgrid, dim3(1024), 0, s, a);
+      else hipLaunchKernelGGL((bw_range_transfer_kernel<T, false>), rgrid, dim3(1024), 0, s, a);
       const int64_t nc = (int64_t)a.B * a.D * 16;
       hipLaunchKernelGGL(bw_range_carry_kernel, dim3((unsigned)((nc + 255) / 256)), dim3(256), 0, s, a);
       const unsigned grid = (unsigned)(a.B * a.nr * (a.D / kCG2));
@@ -913,7 +910,6 @@ hipError_t bw_dispatch(const BwArgs &a, int stage, hipStream_t s) {
       else hipLaunchKernelGGL((bw_scan_kernel<T, false>), dim3(grid), dim3(kST2), 0, s, a);
       hipLaunchKernelGGL(bw_rowsum_kernel, dim3((unsigned)((a.T * 32 + 255) / 256)), dim3(256), 0, s,
                          a.bc_part, a.dbc, a.T, a.D / kCG2);
-      hipLaunchKernelGGL(bw_post_scan_kernel<T>, tok_grid, dim3(256), 0, s, a);
       break;
     }
     case 3:

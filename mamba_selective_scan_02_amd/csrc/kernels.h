@@ -133,8 +133,10 @@ struct BwArgs {
   // workspace
   float *wx32, *wdt32;     // weights in fp32 (bf16 I/O)
   float *u, *xd, *dtn, *bc;                 // [T, D], [T, R+32], [T, R], [T, 32]
-  float *dt, *sig, *dys, *du, *ys;          // [T, D]; the scan turns dt into d/d dt and the
-                                            // post-scan pass sig into d/d(dt_proj pre-act.)
+  float *dt, *sig, *dys, *du, *ys;          // [T, D]: dt holds dt_proj's product (before the
+                                            // bias); the reverse scan writes d(dt_proj
+                                            // pre-activation) into sig and du; dys and ys
+                                            // hold bf16 planes for the split products
   float *rP, *rS, *rR, *dA_part;            // [B, nr, D, 16]
   float *dD_part;                           // [B, nr, D]
   float *bc_part, *dbc;                     // [T, D/64, 32], [T, 32]
@@ -147,7 +149,7 @@ struct BwArgs {
   void *dxz;
   float *d_conv_w, *d_conv_b, *d_ssm_state, *d_conv_state;
 };
-// stage: 0 u; 1 dt / sigmoid / dys; 2 range transfers + carries + reverse scan + dB|dC + dz;
+// stage: 0 u; 2 range transfers + carries + reverse scan + dB|dC + dz + d(dt_proj pre-act.);
 // 3 RMSNorm backward; 5 conv + SiLU backward (dx, partials); 6 weights to fp32; 7 conv
 // weight gradients from the column sums of the partials
 hipError_t launch_backward_stage(mm_dtype dt, const BwArgs &a, int stage, hipStream_t s);
