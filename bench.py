@@ -367,7 +367,8 @@ def backward_leg(args, mm, steps=None):
             # the reverse scan stage: state updates per second (each (token, channel, state)
             # is recomputed twice forward and walked once backward)
             "scan_state_updates_per_s": T * D * N / (st["bwd_scan"] * 1e-3),
-            "roofline": {"bound": "alu", "kernel": "bwd_scan stage (transfers, carries, reverse scan)",
+            "roofline": {"bound": "alu", "kernel": "bwd_scan stage (transfers, carries, reverse scan "
+                                                   "with the softplus and gate derivatives)",
                          "achieved": T * D * N / (st["bwd_scan"] * 1e-3),
                          "peak": backward_scan_alu_peak_updates_per_s(), "unit": "state-updates/s",
                          "frac": T * D * N / (st["bwd_scan"] * 1e-3) / backward_scan_alu_peak_updates_per_s()},
