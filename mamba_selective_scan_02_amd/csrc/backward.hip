@@ -17,7 +17,7 @@
 //                             gradients): fp32 16x16x4 MFMA, 128 x 128 (128 x 64 for
 //                             N <= 512) tiles, any strides
 //   (norm_kernel)             the forward's RMSNorm of dt_low, B, C (fp32 mode)
-//   bw_range_transfer_kernel  per range of kRT tokens and (channel, state), 64 channels per
+//   bw_range_transfer_kernel  per range of kRT tokens and (channel, 4 states), 64 channels per
 //                             workgroup with staged inputs, one forward pass: the forward
 //                             transfer (prod a, local end state) and the reverse one (local
 //                             a_t0 dh_t0 from zero). The staging forms dt = softplus(p) and
@@ -52,7 +52,6 @@ namespace {
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 
 constexpr int kRT = 256;          // tokens per range (carry granularity)
-constexpr int kSB = 32;           // tokens per staged sub-block of the range transfers
 constexpr int kCG = 64;           // channels per scan workgroup
 constexpr int kColRows = 1024;    // rows per partial of a column sum
 
@@ -191,8 +190,8 @@ __device__ __forceinline__ float expm1_sel(float x) {
 }
 
 // ---------------------------------------------------------------- per-range transfers
-// lanes: 64 channels x 16 states per workgroup (1024 threads); one range of one sequence. The
-// inputs of each kSB-token sub-block (dt, u, dys of the 64 channels: whole 256-byte rows; B|C)
+// One workgroup per range of one sequence and 64 channels. The
+// inputs of each kRS-token sub-block (dt, u, dys of the 64 channels: whole 256-byte rows; B|C)
 // are staged in LDS by coalesced loads, the next sub-block's fetched into registers while the
 // current one is processed. Without ZOH the u slot is staged as dt u.
 //
@@ -201,34 +200,42 @@ __device__ __forceinline__ float expm1_sel(float x) {
 // the reverse recursion g <- a_t (C_t dys_t + g) from zero at t1 unrolled (the running product
 // is P's own). Tokens past t1 are staged as zeros: a = 1 and zero inputs leave all three as
 // they are.
-constexpr int kRTF = kSB * kCG;                  // floats per staged [kSB][64] array
-constexpr int kRTStage = 3 * kRTF + kSB * 32;    // dt | u | dys | B|C
+// Lanes: 64 channels x 4 groups of 4 states per workgroup (256 threads): the per-(token,
+// channel) values are read once per 4 states, and B, C as 16-byte vectors.
+constexpr int kRS = 16;                          // tokens per staged sub-block
+constexpr int kRA = kRS * kCG;                   // floats per staged [kRS][64] array
+static_assert(kRA == 4 * 256 && kRS * 32 == 2 * 256, "four staged elements per thread, two of B|C");
 template <typename T, bool ZOH>
-__global__ __launch_bounds__(1024) void bw_range_transfer_kernel(BwArgs a) {
-  __shared__ float st_s[kRTStage];
+__global__ __launch_bounds__(256) void bw_range_transfer_kernel(BwArgs a) {
+  __shared__ __attribute__((aligned(16))) float st_s[3 * kRA + kRS * 32];   // dt | dt u (or u) | dys | B|C
   const int ncg = a.D / kCG;
   const int cg = blockIdx.x % ncg;
   const int r = (blockIdx.x / ncg) % a.nr;
   const int b = blockIdx.x / (ncg * a.nr);
   const int tid = threadIdx.x;
-  const int n = tid & 15, c = tid >> 4, i = cg * kCG + c;
+  const int sg = tid & 3, c = tid >> 2, i = cg * kCG + c;
   const int t0 = r * kRT, t1 = min(a.L, t0 + kRT);
-  const int nsb = (t1 - t0 + kSB - 1) / kSB;
+  const int nsb = (t1 - t0 + kRS - 1) / kRS;
   const int64_t tb = (int64_t)b * a.L;
-  const float An = a.A[i * 16 + n], An2 = An * kLog2e;
-  const float rA = ZOH ? 1.0f / An : 0.f;   // ZOH: (e^(dt A) - 1) / A as expm1 times 1 / A
-  // this thread stages elements tid and tid + 1024 of each [kSB][64] array: channel tid & 63
+  const float4 A4 = *(const float4 *)(a.A + i * 16 + 4 * sg);
+  const float An[4] = {A4.x, A4.y, A4.z, A4.w};
+  float An2[4], rA[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    An2[j] = An[j] * kLog2e;
+    rA[j] = ZOH ? 1.0f / An[j] : 0.f;   // ZOH: (e^(dt A) - 1) / A as expm1 times 1 / A
+  }
+  // this thread stages elements tid + 256 h (token (tid >> 6) + 4 h, channel tid & 63) of the
+  // [kRS][64] arrays, h < 4, and of the [kRS][32] B|C array, h < 2
   const int sch = tid & 63;
   const float sbias = a.dt_b[cg * kCG + sch];
-  static_assert(kRTF == 2 * 1024 && kSB * 32 == 1024, "two staged elements per thread, one of B|C");
-  // per element: dt_proj's product (pre-bias), u, dy, z; then B|C
-  float pp[2], pu[2], pdy[2], pz[2], pbc;
-  bool pl[2];   // the element's token lies inside the range
+  float pp[4], pu[4], pdy[4], pz[4], pbc[2];
+  bool pl[4];   // the element's token lies inside the range
   auto fetch = [&](int j) {
-    const int tj = t0 + j * kSB;
+    const int tj = t0 + j * kRS;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int k = (tid >> 6) + 16 * h;
+    for (int h = 0; h < 4; ++h) {
+      const int k = (tid >> 6) + 4 * h;
       pp[h] = pu[h] = pdy[h] = pz[h] = 0.f;
       pl[h] = tj + k < t1;
       if (pl[h]) {
@@ -239,24 +246,28 @@ __global__ __launch_bounds__(1024) void bw_range_transfer_kernel(BwArgs a) {
         pz[h] = io<T>::ld((const T *)a.xz + tok * 2 * a.D + a.D + cg * kCG + sch);
       }
     }
-    const int k = tid >> 5;
-    pbc = tj + k < t1 ? a.bc[(tb + tj + k) * 32 + (tid & 31)] : 0.f;
-  };
-  // dt = softplus(p), p = product + bias; dys = dy SiLU(z); without ZOH the u slot holds dt u.
-  // A zero-staged token has dt = 0 (not softplus(bias)), so it stays an identity step.
-  auto stash = [&]() {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const float dt = pl[h] ? softplus_f(pp[h] + sbias) : 0.f;
-      st_s[tid + 1024 * h] = dt;
-      st_s[kRTF + tid + 1024 * h] = ZOH ? pu[h] : dt * pu[h];
-      st_s[2 * kRTF + tid + 1024 * h] = pdy[h] * silu_f(pz[h]);
+      const int e = tid + 256 * h, k = e >> 5;
+      pbc[h] = tj + k < t1 ? a.bc[(tb + tj + k) * 32 + (e & 31)] : 0.f;
     }
-    st_s[3 * kRTF + tid] = pbc;
   };
-  const float *s_dt = st_s, *s_u = st_s + kRTF, *s_dys = st_s + 2 * kRTF, *s_bc = st_s + 3 * kRTF;
+  // dt = softplus(p), p = product + bias; dys = dy SiLU(z); without ZOH the u slot holds dt u.
+  // A token past the range end gets dt = 0: an identity step.
+  auto stash = [&]() {
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const float dt = pl[h] ? softplus_f(pp[h] + sbias) : 0.f;
+      st_s[tid + 256 * h] = dt;
+      st_s[kRA + tid + 256 * h] = ZOH ? pu[h] : dt * pu[h];
+      st_s[2 * kRA + tid + 256 * h] = pdy[h] * silu_f(pz[h]);
+    }
+    st_s[3 * kRA + tid] = pbc[0];
+    st_s[3 * kRA + 256 + tid] = pbc[1];
+  };
+  const float *s_dt = st_s, *s_u = st_s + kRA, *s_dys = st_s + 2 * kRA, *s_bc = st_s + 3 * kRA;
 
-  float P = 1.f, S = 0.f, g = 0.f;
+  float P[4] = {1.f, 1.f, 1.f, 1.f}, S[4] = {0.f, 0.f, 0.f, 0.f}, g[4] = {0.f, 0.f, 0.f, 0.f};
   fetch(0);
   for (int j = 0; j < nsb; ++j) {
     __syncthreads();
@@ -264,20 +275,25 @@ __global__ __launch_bounds__(1024) void bw_range_transfer_kernel(BwArgs a) {
     __syncthreads();
     if (j + 1 < nsb) fetch(j + 1);
 #pragma unroll
-    for (int k = 0; k < kSB; ++k) {
-      const float dtv = s_dt[k * kCG + c];
-      const float av = exp2_hw(dtv * An2);
-      const float bu = ZOH ? expm1_sel(dtv * An) * rA * s_bc[k * 32 + n] * s_u[k * kCG + c]
-                           : s_u[k * kCG + c] * s_bc[k * 32 + n];
-      S = __builtin_fmaf(av, S, bu);
-      P *= av;
-      g = __builtin_fmaf(P, s_bc[k * 32 + 16 + n] * s_dys[k * kCG + c], g);
+    for (int k = 0; k < kRS; ++k) {
+      const float dtv = s_dt[k * kCG + c], uv = s_u[k * kCG + c], dysv = s_dys[k * kCG + c];
+      const float4 B4 = *(const float4 *)&s_bc[k * 32 + 4 * sg];
+      const float4 C4 = *(const float4 *)&s_bc[k * 32 + 16 + 4 * sg];
+      const float Bv[4] = {B4.x, B4.y, B4.z, B4.w}, Cv[4] = {C4.x, C4.y, C4.z, C4.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float av = exp2_hw(dtv * An2[q]);
+        const float bu = ZOH ? expm1_sel(dtv * An[q]) * rA[q] * Bv[q] * uv : uv * Bv[q];
+        S[q] = __builtin_fmaf(av, S[q], bu);
+        P[q] *= av;
+        g[q] = __builtin_fmaf(P[q], Cv[q] * dysv, g[q]);
+      }
     }
   }
-  const int64_t o = (((int64_t)b * a.nr + r) * a.D + i) * 16 + n;
-  a.rP[o] = P;
-  a.rS[o] = S;
-  a.rR[o] = g;
+  const int64_t o = (((int64_t)b * a.nr + r) * a.D + i) * 16 + 4 * sg;
+  *(float4 *)(a.rP + o) = make_float4(P[0], P[1], P[2], P[3]);
+  *(float4 *)(a.rS + o) = make_float4(S[0], S[1], S[2], S[3]);
+  *(float4 *)(a.rR + o) = make_float4(g[0], g[1], g[2], g[3]);
 }
 
 // sequential over the ranges of one (sequence, channel, state): rS becomes the start state
@@ -901,8 +917,8 @@ hipError_t bw_dispatch(const BwArgs &a, int stage, hipStream_t s) {
     }
     case 2: {
       const dim3 rgrid((unsigned)(a.B * a.nr * (a.D / kCG)));
-      if (a.zoh) hipLaunchKernelGGL((bw_range_transfer_kernel<T, true>), rgrid, dim3(1024), 0, s, a);
-      else hipLaunchKernelGGL((bw_range_transfer_kernel<T, false>), rgrid, dim3(1024), 0, s, a);
+      if (a.zoh) hipLaunchKernelGGL((bw_range_transfer_kernel<T, true>), rgrid, dim3(256), 0, s, a);
+      else hipLaunchKernelGGL((bw_range_transfer_kernel<T, false>), rgrid, dim3(256), 0, s, a);
       const int64_t nc = (int64_t)a.B * a.D * 16;
       hipLaunchKernelGGL(bw_range_carry_kernel, dim3((unsigned)((nc + 255) / 256)), dim3(256), 0, s, a);
       const unsigned grid = (unsigned)(a.B * a.nr * (a.D / kCG2));
