@@ -159,8 +159,9 @@ enum {
   MM_STAGE_LAYER_NORM = 6, /* mamba_layer_prefill: RMSNorm of the layer input */
   MM_STAGE_IN_PROJ = 7,    /* mamba_layer_prefill: in_proj */
   MM_STAGE_OUT_PROJ = 8,   /* mamba_layer_prefill: out_proj + residual */
-  MM_STAGE_BWD_RECOMPUTE = 9,  /* backward: u, x_proj, the norms, dt, SiLU(z) dy recomputed */
-  MM_STAGE_BWD_SCAN = 10,      /* backward: range transfers, carries, the reverse scan, dB / dC */
+  MM_STAGE_BWD_RECOMPUTE = 9,  /* backward: u, x_proj, the norms, dt_proj's product recomputed */
+  MM_STAGE_BWD_SCAN = 10,      /* backward: range transfers, carries, the reverse scan (with the
+                                  softplus and gate derivatives), dB / dC */
   MM_STAGE_BWD_PROJ = 11,      /* backward: dt_proj, RMSNorm and x_proj gradients */
   MM_STAGE_BWD_CONV = 12,      /* backward: conv1d + SiLU gradients */
   MM_STAGE_COUNT = 13
@@ -233,7 +234,9 @@ MM_API mm_status mamba_layer_prefill_timed(const mm_shape *s, int32_t d_model,
  * two carried states, i.e. the gradients of sum(dy * y):
  *   h_t = Abar_t h_{t-1} + Bbar_t u_t runs backward as dh_t = C_t dys_t + Abar_{t+1} dh_{t+1}
  *   (dys = dy * SiLU(z)); the states h are recomputed from the inputs, never stored by the
- *   forward. Arithmetic is fp32 throughout (bf16 I/O only rounds dxz on output).
+ *   forward. Arithmetic is fp32; with bf16 I/O the six products (x_proj, dt_proj and their
+ *   input and weight gradients) take each fp32 operand as two bf16 parts, hi + lo (~2^-17
+ *   relative), on bf16 MFMA with fp32 accumulation, and dxz is rounded to bf16 on output.
  *   xz, conv_state, ssm_state, states_valid: the forward's inputs (states as they were BEFORE
  *               the forward call; NULL / states_valid 0 = zeros)
  *   dy          [batch, seqlen, d_inner] io_dtype

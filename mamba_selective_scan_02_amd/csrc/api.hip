@@ -370,11 +370,12 @@ mm_status layer_impl(const mm_shape *s, int d_model, const mm_layer_params *p, c
 }
 
 // Backward workspace (fp32 arrays; T = batch * seqlen, W = dt_rank + 32, nr = ranges). With
-// bf16 I/O the products run on split bf16 planes (bwgemm.hip): u, d(dt_proj pre-activation)
-// and their transposes occupy arrays that are dead by then (du, dys, ys, dt; ys and dt hold
-// [D, Tp] planes, Tp = T rounded up to 64); the narrow planes and weight copies get their own.
+// bf16 I/O the products run on split bf16 planes (bwgemm.hip): the planes of u live in du
+// until the reverse scan writes du, those of u^T in dt once the scans have read it ([D, Tp],
+// Tp = T rounded up to 64); d(dt_proj pre-activation) and its transpose, the narrow planes and
+// the weight copies get their own regions.
 struct BwWs {
-  size_t wx32, wdt32, u, xd, dtn, bc, dt, sig, dys, du, ys, rP, rS, rR, dA_part, dD_part, bc_part,
+  size_t wx32, wdt32, u, xd, dtn, bc, dt, sig, dpp, du, dpT, rP, rS, rR, dA_part, dD_part, bc_part,
       dbc, ddtn, dxd, gc, cs_part, gsum, conv_part, conv_sum, gemm_part;
   size_t wdtp, wdtT, wxT, dtn_s, dtnT, dxd_s, dxdT;   // bf16 planes (split products only)
   size_t total;
@@ -405,9 +406,9 @@ BwWs bw_layout(const mm_shape &s) {
   take(w.bc, T * 32);
   take(w.dt, (sp ? Tp : T) * D);
   take(w.sig, T * D);
-  take(w.dys, T * D);
+  take(w.dpp, sp ? T * D : 0);    // bf16 hi / lo planes of dp [T, D]
   take(w.du, T * D);
-  take(w.ys, sp ? Tp * D : 0);   // holds the dp^T planes
+  take(w.dpT, sp ? Tp * D : 0);   // bf16 hi / lo planes of dp^T [D, Tp]
   take(w.rP, SR);
   take(w.rS, SR);
   take(w.rR, SR);
@@ -487,8 +488,7 @@ mm_status backward_impl(const mm_shape *s, const mm_params *p, const void *xz, c
   a.eps = s->rms_eps; a.zoh = (s->flags & MM_FLAG_ZOH_B) ? 1 : 0;
   a.B = B; a.L = L; a.D = D; a.K = s->d_conv; a.R = R; a.nr = bw_ranges(L); a.T = T;
   a.wx32 = F(w.wx32); a.wdt32 = F(w.wdt32); a.u = F(w.u); a.xd = F(w.xd); a.dtn = F(w.dtn);
-  a.bc = F(w.bc); a.dt = F(w.dt); a.sig = F(w.sig); a.dys = F(w.dys); a.du = F(w.du);
-  a.ys = F(w.ys);
+  a.bc = F(w.bc); a.dt = F(w.dt); a.sig = F(w.sig); a.du = F(w.du);
   a.rP = F(w.rP); a.rS = F(w.rS); a.rR = F(w.rR); a.dA_part = F(w.dA_part);
   a.dD_part = F(w.dD_part); a.bc_part = F(w.bc_part); a.dbc = F(w.dbc); a.ddtn = F(w.ddtn);
   a.dxd = F(w.dxd); a.gc = F(w.gc); a.conv_part = F(w.conv_part);
@@ -506,8 +506,8 @@ mm_status backward_impl(const mm_shape *s, const mm_params *p, const void *xz, c
   uint16_t *u_hi = H(w.du), *u_lo = u_hi + T * D;
   uint16_t *dtn_hi = H(w.dtn_s), *dtn_lo = dtn_hi + T * Rp;
   uint16_t *dtnT_hi = H(w.dtnT), *dtnT_lo = dtnT_hi + (int64_t)R * Tp;
-  uint16_t *dp_hi = H(w.dys), *dp_lo = dp_hi + T * D;
-  uint16_t *dpT_hi = H(w.ys), *dpT_lo = dpT_hi + (int64_t)D * Tp;
+  uint16_t *dp_hi = H(w.dpp), *dp_lo = dp_hi + T * D;
+  uint16_t *dpT_hi = H(w.dpT), *dpT_lo = dpT_hi + (int64_t)D * Tp;
   uint16_t *dxd_hi = H(w.dxd_s), *dxd_lo = dxd_hi + T * Wp;
   uint16_t *dxdT_hi = H(w.dxdT), *dxdT_lo = dxdT_hi + (int64_t)W * Tp;
   uint16_t *uT_hi = H(w.dt), *uT_lo = uT_hi + (int64_t)D * Tp;
@@ -552,8 +552,7 @@ mm_status backward_impl(const mm_shape *s, const mm_params *p, const void *xz, c
     MM_TRY(launch_colsum(dp, T, D, cs, g->dt_proj_b, st));
     float *gp = F(w.gemm_part);
     if (sp) {
-      // planes of dp^T and dt_low^T ([D | R, Tp]; dp^T in ys); those of dp (in dys) are the
-      // post-scan kernel's
+      // planes of dp^T and dt_low^T ([D | R, Tp]); those of dp are the reverse scan's
       MM_TRY(launch_tsplit_bf16(dp, (int)T, D, D, dpT_hi, dpT_lo, Tp, st));
       MM_TRY(launch_tsplit_bf16(a.dtn, (int)T, R, R, dtnT_hi, dtnT_lo, Tp, st));
       // d W_dt [D, R] = dp^T dt_low (over tokens); d dt_low [T, R] = dp W_dt

@@ -133,10 +133,9 @@ struct BwArgs {
   // workspace
   float *wx32, *wdt32;     // weights in fp32 (bf16 I/O)
   float *u, *xd, *dtn, *bc;                 // [T, D], [T, R+32], [T, R], [T, 32]
-  float *dt, *sig, *dys, *du, *ys;          // [T, D]: dt holds dt_proj's product (before the
+  float *dt, *sig, *du;                     // [T, D]: dt holds dt_proj's product (before the
                                             // bias); the reverse scan writes d(dt_proj
-                                            // pre-activation) into sig and du; dys and ys
-                                            // hold bf16 planes for the split products
+                                            // pre-activation) into sig, and du
   float *rP, *rS, *rR, *dA_part;            // [B, nr, D, 16]
   float *dD_part;                           // [B, nr, D]
   float *bc_part, *dbc;                     // [T, D/64, 32], [T, 32]
