@@ -225,7 +225,11 @@ __global__ __launch_bounds__(256) void decode_update_kernel(DecodeUpdateArgs a) 
     const int b = (int)(gch / a.D);
     // the wave's 16 channels of unit j lie in one sequence (d_inner % 16 == 0)
     const int bw = __builtin_amdgcn_readfirstlane((int)((w0 + 64 * j) / a.D));
-    h[j] = *(const float4 *)(a.state + gch * 16 + 4 * q);
+    {   // the state streams through once per step: non-temporal, so it does not evict the
+        // weights and staged rows the other kernels of the step reuse from L2
+      const f32x4 hv4 = __builtin_nontemporal_load((const f32x4 *)(a.state + gch * 16 + 4 * q));
+      h[j] = make_float4(hv4[0], hv4[1], hv4[2], hv4[3]);
+    }
     Av[j] = *(const float4 *)(a.A + (int64_t)i * 16 + 4 * q);
     // lane l holds value l % 32 of the sequence's B | C row; lanes fetch theirs by bpermute
     const float bcl = a.bc[(int64_t)bw * 32 + (threadIdx.x & 31)];
@@ -277,7 +281,8 @@ __global__ __launch_bounds__(256) void decode_update_kernel(DecodeUpdateArgs a) 
       }
       yp = __builtin_fmaf(Cq[j][s], hv[s], yp);
     }
-    *(float4 *)(a.state + gch * 16 + 4 * q) = make_float4(hv[0], hv[1], hv[2], hv[3]);
+    __builtin_nontemporal_store(f32x4{hv[0], hv[1], hv[2], hv[3]},
+                                (f32x4 *)(a.state + gch * 16 + 4 * q));
     // sum the channel's 4 lanes: quad_perm [1,0,3,2] then [2,3,0,1]
     yp += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, yp), 0xB1, 0xF, 0xF, false));
     yp += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, yp), 0x4E, 0xF, 0xF, false));
