@@ -390,6 +390,7 @@ __global__ __launch_bounds__(kST2, 4) void bw_scan_kernel(BwArgs a) {
   const int sk = tid >> 5, sch = tid & 31;
   const float sbias = a.dt_b[cg * kCG2 + sch];
   float pp, pu, pdy, pz, pbc;   // dt_proj's product (pre-bias), u, dy, z; B|C
+  float dDs = 0.f;              // sum over the range of dys u of this thread's staged column
   bool pl;                      // the element's token lies inside the range
   auto fetch = [&](int j) {
     const int64_t tok = tb + t0 + j * kSB2 + sk, e = tok * a.D + cg * kCG2 + sch;
@@ -413,8 +414,10 @@ __global__ __launch_bounds__(kST2, 4) void bw_scan_kernel(BwArgs a) {
     st_s[kST2 + tid] = pu;
     st_s[2 * kST2 + tid] = dt * pu;
     if (rev) {
-      st_s[3 * kST2 + tid] = pdy * silu_f(pz);
+      const float dys = pdy * silu_f(pz);
+      st_s[3 * kST2 + tid] = dys;
       st_s[4 * kST2 + tid] = sigmoid_f(p);
+      dDs = __builtin_fmaf(dys, pu, dDs);
     } else {
       st_s[5 * kST2 + tid] = pdy * dsilu_f(pz);
     }
@@ -454,10 +457,10 @@ __global__ __launch_bounds__(kST2, 4) void bw_scan_kernel(BwArgs a) {
   float h = a.rS[so];
   fetch(0);
   for (int j = 0; j < nsb; ++j) {
-    __syncthreads();
+    lds_barrier();
     stash(false);
     if (j > 0) flush_dz(j - 1);
-    __syncthreads();
+    lds_barrier();
     if (j + 1 < nsb) fetch(j + 1);
     ck_s[j][tid] = h;
     float yp[8];
@@ -479,17 +482,20 @@ __global__ __launch_bounds__(kST2, 4) void bw_scan_kernel(BwArgs a) {
 
   // pass 2: sub-blocks in reverse; carry = a_{t+1} dh_{t+1}
   float carry = a.rR[so];
-  float dA = 0.f, dD = 0.f;
+  float dA = 0.f;
   fetch(nsb - 1);
   for (int j = nsb - 1; j >= 0; --j) {
-    __syncthreads();     // the stage, red_s and o_s are free (previous sub-block consumed)
+    lds_barrier();     // the stage, red_s and o_s are free (previous sub-block consumed)
     if (j == nsb - 1) flush_dz(j);   // the forward pass's last tile
     stash(true);
-    __syncthreads();
+    lds_barrier();
     if (j > 0) fetch(j - 1);
     const int tj = t0 + j * kSB2;
     f32x4 accB = {0.f, 0.f, 0.f, 0.f}, accC = {0.f, 0.f, 0.f, 0.f};
-    float gv[8];                             // window of 4 tokens: d dt terms | du terms
+    // window of 4 tokens: with Euler Bbar the two per-state terms whose sums over the states
+    // give d dt = sum(ra A) + u sum(dh B) and du = dt sum(dh B) + D dys; with ZOH the d dt and
+    // du terms themselves
+    float gv[8];
     // A = e_k for token k: 1 in lane n == k of each row, moved down one lane per token
     float oh = n == kSB2 - 1 ? 1.f : 0.f;
     float hist[kSB2 + 1], ah[kSB2];
@@ -509,44 +515,51 @@ __global__ __launch_bounds__(kST2, 4) void bw_scan_kernel(BwArgs a) {
       const float av = ah[k];
       const float dh = __builtin_fmaf(Cn, dysv, carry);
       const float ra = dh * hist[k] * av;      // d / d a_t, times a_t
-      float pB, gdt, gdu;
+      float pB, g0, g1;
       if (ZOH) {
         const float x = dtv * An;
         const float E = expm1_sel(x), q = E * rA;
         const float dBb = dh * uv;
-        gdt = ra * An + dBb * av * Bn;
+        g0 = ra * An + dBb * av * Bn;          // d dt
         dA += ra * dtv + dBb * Bn * (x * av - E) * rA * rA;
         pB = dBb * q;
-        gdu = dh * q * Bn;
+        g1 = dh * q * Bn;                      // du
       } else {
-        const float gB = dh * Bn;
-        gdt = __builtin_fmaf(ra, An, gB * uv);
+        g0 = ra * An;
+        g1 = dh * Bn;
         dA = __builtin_fmaf(ra, dtv, dA);
         pB = dh * s_dtu[k * kCG2 + c];
-        gdu = gB * dtv;
       }
       const float pC = dysv * hist[k + 1];
       carry = av * dh;
-      dD = __builtin_fmaf(dysv, uv, dD);
       accB = __builtin_amdgcn_mfma_f32_16x16x4f32(oh, pB, accB, 0, 0, 0);   // row k += terms
       accC = __builtin_amdgcn_mfma_f32_16x16x4f32(oh, pC, accC, 0, 0, 0);
       oh = dpp_f<0x12F>(oh);                   // row_ror:15: lane n takes lane n + 1's
-      gv[k & 3] = gdt;
-      gv[4 + (k & 3)] = gdu;
+      gv[k & 3] = g0;
+      gv[4 + (k & 3)] = g1;
       if ((k & 3) == 0) {
-        // lane n: d dt (n < 8) or du (n >= 8) of token k + (n / 2) % 4 (both lanes of a pair)
+        // lane n: the sum of g0 (n < 8) or g1 (n >= 8) of token k + (n / 2) % 4 (both lanes of
+        // a pair); row_ror:8 hands lane n < 8 the g1 sum of the same token
         const float sv = tsum8(gv, n);
         const int kt = k + ((n >> 1) & 3);
+        const float s1 = dpp_f<0x128>(sv);
         if (!(n & 1)) {
-          if (n < 8) o_s[0][kt][c] = sv * s_sg[kt * kCG2 + c];   // d dt sigmoid(p)
-          else o_s[1][kt][c] = __builtin_fmaf(Dv, s_dys[kt * kCG2 + c], sv);   // with D u's term
+          const float dysk = s_dys[kt * kCG2 + c];
+          if (ZOH) {
+            if (n < 8) o_s[0][kt][c] = sv * s_sg[kt * kCG2 + c];   // d dt sigmoid(p)
+            else o_s[1][kt][c] = __builtin_fmaf(Dv, dysk, sv);    // with D u's term
+          } else if (n < 8) {
+            o_s[0][kt][c] = __builtin_fmaf(s_u[kt * kCG2 + c], s1, sv) * s_sg[kt * kCG2 + c];
+          } else {
+            o_s[1][kt][c] = __builtin_fmaf(s_dt[kt * kCG2 + c], sv, Dv * dysk);
+          }
         }
       }
     }
     // lane (n, cl): accB[q] = sum over the wave's channels of dB terms of token 4 cl + q, state n
     red_s[wv][0][lane] = accB;
     red_s[wv][1][lane] = accC;
-    __syncthreads();
+    lds_barrier();
     {   // one output per thread: token m, value v (dB states 0-15 | dC states 0-15)
       const int m = tid >> 5, v = tid & 31, qn = v >> 4, sn = v & 15;
       const int t = tj + m;
@@ -562,7 +575,16 @@ __global__ __launch_bounds__(kST2, 4) void bw_scan_kernel(BwArgs a) {
     flush_dp_du(j);
   }
   a.dA_part[so] = dA;
-  if (n == 0) a.dD_part[((int64_t)b * a.nr + r) * a.D + i] = dD;
+  // the D gradient: the 16 staging threads of each channel add their columns in a fixed order
+  __syncthreads();
+  st_s[tid] = dDs;
+  __syncthreads();
+  if (tid < kCG2) {
+    float s = 0.f;
+#pragma unroll
+    for (int q = 0; q < kSB2; ++q) s += st_s[q * kCG2 + tid];
+    a.dD_part[((int64_t)b * a.nr + r) * a.D + cg * kCG2 + tid] = s;
+  }
 }
 
 // dB | dC [T, 32] = sum over the channel groups of the scan's per-workgroup rows
