@@ -320,21 +320,23 @@ __global__ __launch_bounds__(256) void bw_range_carry_kernel(BwArgs a) {
 }
 
 // ---------------------------------------------------------------- the reverse scan
-// Lanes: 64 channels x 16 states per workgroup (1024 threads; lane n = state, the wave's four
+// Lanes: 32 channels x 16 states per workgroup (512 threads; lane n = state, the wave's four
 // 16-lane rows = four channels); one range of one sequence, in sub-blocks of kSB2 tokens whose
-// inputs are staged in LDS by coalesced loads one sub-block ahead: dt | u | dt u | dys
-// ([kSB2][64] each) and B|C ([kSB2][32]); thread tid stages elements tid + 1024 q. Tokens past
-// the range end are staged as zeros (a = 1, no input: the states and the carry pass through
-// them unchanged, and nothing of theirs is stored).
+// inputs are staged in LDS by coalesced loads one sub-block ahead (per-(token, channel) arrays
+// [kSB2][32] and B|C [kSB2][32]; thread tid stages element tid of each). Tokens past the range
+// end are staged as zeros (a = 1, no input: the states and the carry pass through them
+// unchanged, and nothing of theirs is stored).
 //
 // Sums over the 16 states of a channel (ys, and the d dt, du contributions) are transposed
 // reductions: each lane holds 8 partial values (8 tokens, or 4 tokens x 2 quantities), and
 // four DPP exchange-and-add steps inside the row leave lanes 2j and 2j + 1 with the row's sum of
-// value j, 22 VALU operations for 8 sums. Sums over channels (dB, dC: per token and state) run
-// on the matrix cores: with B[k][n] = this lane's term (k = the wave's channel) and A[m][k] = 1
-// for the token's row m only, a 16x16x4 fp32 MFMA adds the four channels' terms into row m of a
-// [token, state] accumulator; each wave's 16 x 16 result goes to LDS once per sub-block and
-// the 16 waves are added in a fixed order.
+// value j, 22 VALU operations for 8 sums. Sums over the wave's four channels (dB, dC: per token
+// and state) are transposed too, across rows, with the lane-swap instructions: a 32-lane swap
+// of (dB term, dC term) plus an add leaves rows 0-1 with dB and rows 2-3 with dC summed over
+// channel pairs; a 16-lane swap of two tokens' results plus an add finishes both tokens, row r
+// holding dB (r = 0, 1) or dC (r = 2, 3) of token 2p + (r & 1). Three swaps and three adds per
+// two tokens; each wave's sums go to LDS once per sub-block and the 8 waves are added in a fixed
+// order.
 constexpr int kSB2 = 16;                        // tokens per recomputed sub-block
 constexpr int kNSB2 = kRT / kSB2;               // sub-blocks per range
 constexpr int kCG2 = 32;                        // channels per reverse-scan workgroup
@@ -367,7 +369,7 @@ __device__ __forceinline__ float tsum8(const float (&v)[8], int n) {
 template <typename T, bool ZOH>
 __global__ __launch_bounds__(kST2, 4) void bw_scan_kernel(BwArgs a) {
   __shared__ float ck_s[kNSB2][kST2];       // state checkpoints, one column per thread
-  __shared__ f32x4 red_s[kW2][2][64];       // per wave: MFMA [token, state] sums of dB | dC
+  __shared__ float red_s[kW2][kSB2 / 2][64];  // per wave and token pair: dB | dC sums
   __shared__ float st_s[kS2NA * kST2];      // the current sub-block's inputs
   __shared__ float o_s[2][kSB2][kCG2];      // the current sub-block's per-(token, channel) outputs
 
@@ -491,13 +493,11 @@ __global__ __launch_bounds__(kST2, 4) void bw_scan_kernel(BwArgs a) {
     lds_barrier();
     if (j > 0) fetch(j - 1);
     const int tj = t0 + j * kSB2;
-    f32x4 accB = {0.f, 0.f, 0.f, 0.f}, accC = {0.f, 0.f, 0.f, 0.f};
+    float rr[kSB2 / 2], sodd = 0.f;          // per token pair: the wave's dB | dC sums
     // window of 4 tokens: with Euler Bbar the two per-state terms whose sums over the states
     // give d dt = sum(ra A) + u sum(dh B) and du = dt sum(dh B) + D dys; with ZOH the d dt and
     // du terms themselves
     float gv[8];
-    // A = e_k for token k: 1 in lane n == k of each row, moved down one lane per token
-    float oh = n == kSB2 - 1 ? 1.f : 0.f;
     float hist[kSB2 + 1], ah[kSB2];
     hist[0] = ck_s[j][tid];
 #pragma unroll
@@ -532,9 +532,20 @@ __global__ __launch_bounds__(kST2, 4) void bw_scan_kernel(BwArgs a) {
       }
       const float pC = dysv * hist[k + 1];
       carry = av * dh;
-      accB = __builtin_amdgcn_mfma_f32_16x16x4f32(oh, pB, accB, 0, 0, 0);   // row k += terms
-      accC = __builtin_amdgcn_mfma_f32_16x16x4f32(oh, pC, accC, 0, 0, 0);
-      oh = dpp_f<0x12F>(oh);                   // row_ror:15: lane n takes lane n + 1's
+      {
+        // rows 0-1: dB terms of channels (0 + 2), (1 + 3); rows 2-3: dC terms likewise
+        const auto w = __builtin_amdgcn_permlane32_swap(__float_as_uint(pB), __float_as_uint(pC),
+                                                        false, false);
+        const float sk = __uint_as_float(w[0]) + __uint_as_float(w[1]);
+        if (k & 1) {
+          sodd = sk;
+        } else {
+          // rows of (token k, token k + 1): dB k | dB k+1 | dC k | dC k+1
+          const auto v = __builtin_amdgcn_permlane16_swap(__float_as_uint(sk),
+                                                          __float_as_uint(sodd), false, false);
+          rr[k >> 1] = __uint_as_float(v[0]) + __uint_as_float(v[1]);
+        }
+      }
       gv[k & 3] = g0;
       gv[4 + (k & 3)] = g1;
       if ((k & 3) == 0) {
@@ -556,19 +567,18 @@ __global__ __launch_bounds__(kST2, 4) void bw_scan_kernel(BwArgs a) {
         }
       }
     }
-    // lane (n, cl): accB[q] = sum over the wave's channels of dB terms of token 4 cl + q, state n
-    red_s[wv][0][lane] = accB;
-    red_s[wv][1][lane] = accC;
+#pragma unroll
+    for (int p = 0; p < kSB2 / 2; ++p) red_s[wv][p][lane] = rr[p];
     lds_barrier();
     {   // one output per thread: token m, value v (dB states 0-15 | dC states 0-15)
       const int m = tid >> 5, v = tid & 31, qn = v >> 4, sn = v & 15;
       const int t = tj + m;
       if (t < t1) {
-        const float *rs = (const float *)red_s;
-        const int off = (qn * 64 + 16 * (m >> 2) + sn) * 4 + (m & 3);
+        const float *rs = &red_s[0][0][0];
+        const int off = (m >> 1) * 64 + 16 * ((m & 1) + 2 * qn) + sn;
         float sum = 0.f;
 #pragma unroll
-        for (int w = 0; w < kW2; ++w) sum += rs[w * 512 + off];
+        for (int w = 0; w < kW2; ++w) sum += rs[w * (kSB2 / 2) * 64 + off];
         a.bc_part[((tb + t) * ncg + cg) * 32 + v] = sum;
       }
     }
