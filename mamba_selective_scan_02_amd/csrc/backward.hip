@@ -229,21 +229,25 @@ __global__ __launch_bounds__(256) void bw_range_transfer_kernel(BwArgs a) {
   // [kRS][64] arrays, h < 4, and of the [kRS][32] B|C array, h < 2
   const int sch = tid & 63;
   const float sbias = a.dt_b[cg * kCG + sch];
-  float pp[4], pu[4], pdy[4], pz[4], pbc[2];
+  // dy and z stay in the I/O type until the stash: converting them where they are fetched
+  // would wait for the loads there, one sub-block too early
+  float pp[4], pu[4], pbc[2];
+  T rdy[4], rz[4];
   bool pl[4];   // the element's token lies inside the range
   auto fetch = [&](int j) {
     const int tj = t0 + j * kRS;
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
       const int k = (tid >> 6) + 4 * h;
-      pp[h] = pu[h] = pdy[h] = pz[h] = 0.f;
+      pp[h] = pu[h] = 0.f;
+      rdy[h] = rz[h] = T(0);
       pl[h] = tj + k < t1;
       if (pl[h]) {
         const int64_t tok = tb + tj + k, e = tok * a.D + cg * kCG + sch;
         pp[h] = a.dt[e];
         pu[h] = a.u[e];
-        pdy[h] = io<T>::ld((const T *)a.dy + e);
-        pz[h] = io<T>::ld((const T *)a.xz + tok * 2 * a.D + a.D + cg * kCG + sch);
+        rdy[h] = ((const T *)a.dy)[e];
+        rz[h] = ((const T *)a.xz)[tok * 2 * a.D + a.D + cg * kCG + sch];
       }
     }
 #pragma unroll
@@ -260,7 +264,7 @@ __global__ __launch_bounds__(256) void bw_range_transfer_kernel(BwArgs a) {
       const float dt = pl[h] ? softplus_f(pp[h] + sbias) : 0.f;
       st_s[tid + 256 * h] = dt;
       st_s[kRA + tid + 256 * h] = ZOH ? pu[h] : dt * pu[h];
-      st_s[2 * kRA + tid + 256 * h] = pdy[h] * silu_f(pz[h]);
+      st_s[2 * kRA + tid + 256 * h] = io<T>::cvt(rdy[h]) * silu_f(io<T>::cvt(rz[h]));
     }
     st_s[3 * kRA + tid] = pbc[0];
     st_s[3 * kRA + 256 + tid] = pbc[1];
@@ -391,18 +395,20 @@ __global__ __launch_bounds__(kST2, 4) void bw_scan_kernel(BwArgs a) {
   // this thread stages element tid of each array: token tid / 32, channel tid % 32
   const int sk = tid >> 5, sch = tid & 31;
   const float sbias = a.dt_b[cg * kCG2 + sch];
-  float pp, pu, pdy, pz, pbc;   // dt_proj's product (pre-bias), u, dy, z; B|C
+  float pp, pu, pbc;            // dt_proj's product (pre-bias), u; B|C
+  T rdy, rz;                    // dy, z in the I/O type (converted at the stash, not at the fetch)
   float dDs = 0.f;              // sum over the range of dys u of this thread's staged column
   bool pl;                      // the element's token lies inside the range
   auto fetch = [&](int j) {
     const int64_t tok = tb + t0 + j * kSB2 + sk, e = tok * a.D + cg * kCG2 + sch;
     pl = t0 + j * kSB2 + sk < t1;
-    pp = pu = pdy = pz = pbc = 0.f;
+    pp = pu = pbc = 0.f;
+    rdy = rz = T(0);
     if (pl) {
       pp = a.dt[e];
       pu = a.u[e];
-      pdy = io<T>::ld((const T *)a.dy + e);
-      pz = io<T>::ld((const T *)a.xz + tok * 2 * a.D + a.D + cg * kCG2 + sch);
+      rdy = ((const T *)a.dy)[e];
+      rz = ((const T *)a.xz)[tok * 2 * a.D + a.D + cg * kCG2 + sch];
       pbc = a.bc[tok * 32 + sch];
     }
   };
@@ -411,6 +417,7 @@ __global__ __launch_bounds__(kST2, 4) void bw_scan_kernel(BwArgs a) {
   // (the forward pass needs dy SiLU'(z), the reverse pass dys and sigmoid(p))
   auto stash = [&](bool rev) {
     const float p = pp + sbias;
+    const float pdy = io<T>::cvt(rdy), pz = io<T>::cvt(rz);
     const float dt = pl ? softplus_f(p) : 0.f;
     st_s[tid] = dt;
     st_s[kST2 + tid] = pu;
