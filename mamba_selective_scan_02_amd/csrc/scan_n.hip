@@ -28,22 +28,42 @@ namespace {
 constexpr int kGR = 512;   // tokens per range
 constexpr int kGS = 32;    // tokens per staged sub-block
 
-template <typename T> struct DeltaG;
-template <> struct DeltaG<float> {
-  static __device__ __forceinline__ float ld(const void *p, int64_t e) { return ((const float *)p)[e]; }
-};
-template <> struct DeltaG<bf16_t> {
-  static __device__ __forceinline__ float ld(const void *p, int64_t e) {
-    return (float)((const _Float16 *)p)[e];
+// Prefetched elements travel as raw bits and are decoded when they are staged: decoding a
+// 16-bit value where it is loaded would make the wave wait for the load one sub-block early.
+// dt: fp32, or fp16 for bf16 I/O; u: fp32, or bf16 high | low parts; z: the I/O type.
+template <typename T> struct Raw;
+template <> struct Raw<float> {
+  static __device__ __forceinline__ uint32_t dt(const ScanArgs &a, int64_t e) {
+    return __float_as_uint(((const float *)a.delta)[e]);
   }
+  static __device__ __forceinline__ uint32_t u(const ScanArgs &a, int64_t e) {
+    return __float_as_uint(((const float *)a.u)[e]);
+  }
+  static __device__ __forceinline__ uint32_t z(const ScanArgs &a, int64_t e) {
+    return __float_as_uint(((const float *)a.xz)[e]);
+  }
+  static __device__ __forceinline__ float dt_f(uint32_t v) { return __uint_as_float(v); }
+  static __device__ __forceinline__ float u_f(uint32_t v) { return __uint_as_float(v); }
+  static __device__ __forceinline__ float z_f(uint32_t v) { return __uint_as_float(v); }
 };
-template <typename T> __device__ __forceinline__ float ld_u(const ScanArgs &a, int64_t e);
-template <> __device__ __forceinline__ float ld_u<float>(const ScanArgs &a, int64_t e) {
-  return ((const float *)a.u)[e];
-}
-template <> __device__ __forceinline__ float ld_u<bf16_t>(const ScanArgs &a, int64_t e) {
-  return bf2f(((const bf16_t *)a.u)[e]) + bf2f(((const bf16_t *)a.u_lo)[e]);
-}
+template <> struct Raw<bf16_t> {
+  static __device__ __forceinline__ uint32_t dt(const ScanArgs &a, int64_t e) {
+    return ((const uint16_t *)a.delta)[e];
+  }
+  static __device__ __forceinline__ uint32_t u(const ScanArgs &a, int64_t e) {
+    return (uint32_t)((const bf16_t *)a.u)[e] | ((uint32_t)((const bf16_t *)a.u_lo)[e] << 16);
+  }
+  static __device__ __forceinline__ uint32_t z(const ScanArgs &a, int64_t e) {
+    return ((const bf16_t *)a.xz)[e];
+  }
+  static __device__ __forceinline__ float dt_f(uint32_t v) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)v);
+  }
+  static __device__ __forceinline__ float u_f(uint32_t v) {
+    return bf2f((bf16_t)(v & 0xFFFFu)) + bf2f((bf16_t)(v >> 16));
+  }
+  static __device__ __forceinline__ float z_f(uint32_t v) { return bf2f((bf16_t)v); }
+};
 
 // sum over the G lanes of a channel (G = 4, 8 or 16, groups aligned to G lanes); every lane
 // of the group receives it. All source lanes lie inside the row (bound_ctrl changes no value
@@ -100,20 +120,21 @@ __global__ __launch_bounds__(256) void scanN_transfer_kernel(ScanArgs a, int nr)
     P[q] = 1.f;
     Sv[q] = 0.f;
   }
-  float pf[NQ];
+  static_assert(F % 256 == 0, "each prefetch slot holds one kind of element");
+  uint32_t pf[NQ];   // slot q < F/256: dt; < 2F/256: u; then B (raw bits, see Raw)
   auto fetch = [&](int jb) {
     const int tj = t0 + jb * kGS;
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
       const int e = tid + 256 * q;
-      float v = 0.f;
+      uint32_t v = 0;
       if (e < 2 * F) {
         const int off = e % F, k = off / CPW, ch = off % CPW;
         const int64_t x = (tb + tj + k) * a.D + cg * CPW + ch;
-        if (tj + k < t1) v = e < F ? DeltaG<T>::ld(a.delta, x) : ld_u<T>(a, x);
+        if (tj + k < t1) v = q < F / 256 ? Raw<T>::dt(a, x) : Raw<T>::u(a, x);
       } else if (e < ST) {
         const int off = e - 2 * F, k = off / N, nn = off % N;
-        if (tj + k < t1) v = a.bc[(tb + tj + k) * 2 * N + nn];
+        if (tj + k < t1) v = __float_as_uint(a.bc[(tb + tj + k) * 2 * N + nn]);
       }
       pf[q] = v;
     }
@@ -121,10 +142,12 @@ __global__ __launch_bounds__(256) void scanN_transfer_kernel(ScanArgs a, int nr)
   const float *s_dt = st_s, *s_u = st_s + F, *s_b = st_s + 2 * F;
   fetch(0);
   for (int jb = 0; jb < nsb; ++jb) {
-    __syncthreads();
+    lds_barrier();
 #pragma unroll
-    for (int q = 0; q < NQ; ++q) st_s[tid + 256 * q] = pf[q];
-    __syncthreads();
+    for (int q = 0; q < NQ; ++q)
+      st_s[tid + 256 * q] = q < F / 256 ? Raw<T>::dt_f(pf[q])
+                            : q < 2 * F / 256 ? Raw<T>::u_f(pf[q]) : __uint_as_float(pf[q]);
+    lds_barrier();
     if (jb + 1 < nsb) fetch(jb + 1);
     const int tj = t0 + jb * kGS;
 #pragma unroll 4
@@ -193,25 +216,26 @@ __global__ __launch_bounds__(256) void scanN_replay_kernel(ScanArgs a, int nr) {
     h[q] = a.gS[so + q];
   }
   const float Dv = a.Dskip[i];
-  float pf[NQ];
+  static_assert(F % 256 == 0, "each prefetch slot holds one kind of element");
+  uint32_t pf[NQ];   // slot q < F/256: dt; < 2F/256: u; < 3F/256: z; then B|C (raw bits)
   auto fetch = [&](int jb) {
     const int tj = t0 + jb * kGS;
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
       const int e = tid + 256 * q;
-      float v = 0.f;
+      uint32_t v = 0;
       if (e < 3 * F) {
         const int off = e % F, k = off / CPW, ch = off % CPW;
         const int64_t tok = tb + tj + k;
         const int ic = cg * CPW + ch;
         if (tj + k < t1) {
-          if (e < F) v = DeltaG<T>::ld(a.delta, tok * a.D + ic);
-          else if (e < 2 * F) v = ld_u<T>(a, tok * a.D + ic);
-          else v = io<T>::ld((const T *)a.xz + tok * 2 * a.D + a.D + ic);
+          if (q < F / 256) v = Raw<T>::dt(a, tok * a.D + ic);
+          else if (q < 2 * F / 256) v = Raw<T>::u(a, tok * a.D + ic);
+          else v = Raw<T>::z(a, tok * 2 * a.D + a.D + ic);
         }
       } else if (e < ST) {
         const int off = e - 3 * F, k = off / (2 * N), nn = off % (2 * N);
-        if (tj + k < t1) v = a.bc[(tb + tj + k) * 2 * N + nn];
+        if (tj + k < t1) v = __float_as_uint(a.bc[(tb + tj + k) * 2 * N + nn]);
       }
       pf[q] = v;
     }
@@ -219,10 +243,14 @@ __global__ __launch_bounds__(256) void scanN_replay_kernel(ScanArgs a, int nr) {
   const float *s_dt = st_s, *s_u = st_s + F, *s_z = st_s + 2 * F, *s_bc = st_s + 3 * F;
   fetch(0);
   for (int jb = 0; jb < nsb; ++jb) {
-    __syncthreads();
+    // LDS-only barriers: the y stores of the previous sub-block stay in flight
+    lds_barrier();
 #pragma unroll
-    for (int q = 0; q < NQ; ++q) st_s[tid + 256 * q] = pf[q];
-    __syncthreads();
+    for (int q = 0; q < NQ; ++q)
+      st_s[tid + 256 * q] = q < F / 256 ? Raw<T>::dt_f(pf[q])
+                            : q < 2 * F / 256 ? Raw<T>::u_f(pf[q])
+                            : q < 3 * F / 256 ? Raw<T>::z_f(pf[q]) : __uint_as_float(pf[q]);
+    lds_barrier();
     if (jb + 1 < nsb) fetch(jb + 1);
     const int tj = t0 + jb * kGS;
 #pragma unroll 4
