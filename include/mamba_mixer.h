@@ -74,15 +74,17 @@ enum {
   MM_FLAG_ZOH_B = 1u << 0,
   /* Scan kernel selection (results agree to fp32 rounding; at most one may be set).
      Default: the time-parallel kernel when batch * d_inner / 64 < 2048 and seqlen > 128,
-     else the sequential one. */
+     else the sequential one. With d_state 32 / 64 the time-parallel kernel runs once per
+     group of 16 states and "sequential" selects the general scan. */
   MM_FLAG_SCAN_SEQUENTIAL = 1u << 1,  /* one lane per (sequence, channel), all 16 states */
   MM_FLAG_SCAN_CHUNKED = 1u << 2      /* 128-token blocks, 8 segments composed in LDS */
 };
 
 /*
  * Problem size. Limits of this build (else MM_ERR_UNSUPPORTED): d_state in {8, 16, 32, 64}
- * (16, the Jamba configuration, runs the tuned kernels; the other sizes a general
- * time-parallel scan, and the scan-selection flags apply to 16 only; the backward takes 16);
+ * (16, the Jamba configuration, runs the tuned kernels; 32 and 64 the tuned time-parallel
+ * scan once per group of 16 states where it applies, else a general time-parallel scan, as 8
+ * does; the backward takes 16);
  * 2 <= d_conv <= 4; d_inner % 64 == 0; with MM_BF16, dt_rank % 64 == 0 and
  * d_inner % 128 == 0; with MM_F32, 1 <= dt_rank <= 1024. seqlen >= 1 (prefill),
  * seqlen == 1 (decode). rms_eps > 0 is the RMSNorm epsilon.

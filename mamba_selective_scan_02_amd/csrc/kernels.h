@@ -224,8 +224,15 @@ struct ScanArgs {
   // the per-range transfers [B, ranges, D, N] (P, and S / the range start states)
   const void *u = nullptr, *u_lo = nullptr;
   float *gP = nullptr, *gS = nullptr;
+  // d_state 32 / 64 on the time-parallel kernel (scan.hip): one launch per 16-state group
+  // (first state g0), each writing its part of y as fp32 [B, L, D] to yacc + g B L D, then a
+  // combine kernel (which reads u as above)
+  float *yacc = nullptr;
+  int g0 = 0;
 };
+// N = 16, or N = 32 / 64 when scan_groups_used (then a.yacc is required)
 hipError_t launch_scan(mm_dtype dt, const ScanArgs &a, hipStream_t s);
+bool scan_groups_used(int B, int L, int D, int N, uint32_t force);
 bool scan_n_supported(int N);
 int scan_n_ranges(int L);
 hipError_t launch_scan_n(mm_dtype dt, const ScanArgs &a, hipStream_t s);

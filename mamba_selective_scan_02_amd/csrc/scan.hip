@@ -135,9 +135,15 @@ __device__ __forceinline__ void load_lds16(const void *src, void *lds) {
   dma16_opaque(src, lds_addr(lds));
 }
 
-template <typename T, bool ZOH, int K>
+// GRP: the kernel covers one group of 16 states [g0, g0 + 16) of a d_state = N > 16 problem
+// (A, B|C rows and the SSM state have stride N) and stores the group's part of C_t . h_t in
+// fp32 to a.yacc [B, L, D] (one buffer per group); scan_combine_kernel then adds the groups'
+// parts and D u and applies the gate.
+template <typename T, bool ZOH, int K, bool GRP>
 __global__ __launch_bounds__(kW * 64) void scan_chunked_kernel(ScanArgs a) {
   typedef typename Delta<T>::type DT;
+  const int NS = GRP ? a.N : kN;           // state stride
+  const int g0 = GRP ? a.g0 : 0;           // first state of this launch
   constexpr int xper = 16 / sizeof(T);                 // x/z elements per 16-byte chunk
   constexpr int xrow_chunks = kCh * sizeof(T) / 16;    // 16-byte chunks per staged x/z row
   constexpr int drow_chunks = kCh * sizeof(DT) / 16;
@@ -171,7 +177,7 @@ __global__ __launch_bounds__(kW * 64) void scan_chunked_kernel(ScanArgs a) {
   float A2[kG], Av[kG], iA[kG];
 #pragma unroll
   for (int j = 0; j < kG; ++j) {
-    Av[j] = a.A[(int64_t)ch * kN + kG * p + j];
+    Av[j] = a.A[(int64_t)ch * NS + g0 + kG * p + j];
     A2[j] = Av[j] * kLog2e;
     iA[j] = 1.0f / Av[j];
   }
@@ -179,14 +185,18 @@ __global__ __launch_bounds__(kW * 64) void scan_chunked_kernel(ScanArgs a) {
   // state j = 4 (tid >> 8) + (tid & 3) of that half: its P of segment w is float w*1024 + tid
   // of agg_s, its S float w*1024 + 512 + tid (conflict-free, lane-contiguous)
   const int ql = (tid >> 2) & 63, qj = 4 * (tid >> 8) + (tid & 3);
-  const int64_t qidx = ((int64_t)b * a.D + ch0 + (ql >> 1)) * kN + kG * (ql & 1) + qj;
+  const int64_t qidx = ((int64_t)b * a.D + ch0 + (ql >> 1)) * NS + g0 + kG * (ql & 1) + qj;
   float carry = (a.state_valid && a.state) ? a.state[qidx] : 0.f;
 
   const int64_t row = 2LL * a.D;
   const T *xzb = (const T *)a.xz + (int64_t)b * a.L * row;
   const DT *db = (const DT *)a.delta + (int64_t)b * a.L * a.D;
-  const float *bcb = a.bc + (int64_t)b * a.L * 2 * kN;
+  const float *bcb = a.bc + (int64_t)b * a.L * 2 * NS;
   T *yb = (T *)a.y + (int64_t)b * a.L * a.D;
+  float *accb = GRP ? a.yacc + (int64_t)b * a.L * a.D : nullptr;   // this group's part of y
+  // this lane's 16-byte slot of a staged B|C row: slots 0-3 B[g0 .. g0+15], 4-7 C[g0 .. g0+15]
+  const int bcq = lane & 7;
+  const int bcoff = g0 + 4 * bcq + (bcq >= 4 ? NS - kN : 0);
   const int nblocks = (a.L + kBlk - 1) / kBlk;
   const int Lm1 = a.L - 1;
 
@@ -198,11 +208,11 @@ __global__ __launch_bounds__(kW * 64) void scan_chunked_kernel(ScanArgs a) {
     const int T0w = blk * kBlk + wv * kS;
     const int rmax = Lm1 - T0w;                   // last valid segment-relative row
     // B|C: 16 rows x 128 B = 2 wave-loads, 8 lanes per row
-    const float *bcbase = bcb + (int64_t)T0w * 2 * kN;
+    const float *bcbase = bcb + (int64_t)T0w * 2 * NS;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int r = min(i * 8 + (lane >> 3), rmax);
-      load_lds16(bcbase + (r * 2 * kN + (lane & 7) * 4), &bcdst[i * 8][0]);
+      load_lds16(bcbase + (r * 2 * NS + bcoff), &bcdst[i * 8][0]);
     }
     if (!kStageXZD) return;
     // x: row r <-> token T0w - 3 + r, r < kXSeg; xrpl rows per wave-load
@@ -238,6 +248,13 @@ __global__ __launch_bounds__(kW * 64) void scan_chunked_kernel(ScanArgs a) {
     if (ypend_t0 < 0) return;
     // wave-uniform segment base, 32-bit lane offsets
     T *ybase = yb + (int64_t)(ypend_t0 + wv * kS) * a.D;
+    if (GRP) {   // this group's part of y (fp32)
+      float *abase = accb + (int64_t)(ypend_t0 + wv * kS) * a.D;
+#pragma unroll
+      for (int i = 0; i < kS / 2; ++i)
+        if (ypend_t0 + wv * kS + 2 * i + p < a.L) abase[(uint32_t)((2 * i + p) * a.D + ch)] = ypend[i];
+      return;
+    }
     if (ypend_t0 + kBlk <= a.L) {
 #pragma unroll
       for (int i = 0; i < kS / 2; ++i)
@@ -411,7 +428,7 @@ __global__ __launch_bounds__(kW * 64) void scan_chunked_kernel(ScanArgs a) {
       const float other = __builtin_bit_cast(
           float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, send), 0xB1, 0xF, 0xF, false));
       const float2 eg = eg_s[wv][t + p][c];
-      ypend[t / 2] = (keep + other + eg.x) * eg.y;
+      ypend[t / 2] = GRP ? keep + other : (keep + other + eg.x) * eg.y;
     }
     ypend_t0 = T0;
   };
@@ -425,13 +442,73 @@ __global__ __launch_bounds__(kW * 64) void scan_chunked_kernel(ScanArgs a) {
   if (a.state) a.state[qidx] = carry;
 }
 
+// y = (sum over the G state groups of their parts + D u) * SiLU(z), 4 channels per thread; u
+// from the conv kernel's output (fp32, or bf16 high + low parts), the parts fp32
+template <typename T>
+__global__ __launch_bounds__(256) void scan_combine_kernel(ScanArgs a, int G) {
+  const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;   // 4 consecutive channels
+  const int64_t TD = (int64_t)a.B * a.L * a.D;
+  if (q * 4 >= TD) return;
+  const int64_t e = q * 4, tok = e / a.D;
+  const int i = (int)(e % a.D);
+  float4 s = *(const float4 *)(a.yacc + e);
+  for (int g = 1; g < G; ++g) {
+    const float4 v = *(const float4 *)(a.yacc + g * TD + e);
+    s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+  }
+  const float sv[4] = {s.x, s.y, s.z, s.w};
+  float u[4], z[4];
+  if (sizeof(T) == 2) {
+    const uint2 uh = *(const uint2 *)((const bf16_t *)a.u + e);
+    const uint2 ul = *(const uint2 *)((const bf16_t *)a.u_lo + e);
+    const uint2 zz = *(const uint2 *)((const bf16_t *)a.xz + tok * 2 * a.D + a.D + i);
+    const uint32_t h[2] = {uh.x, uh.y}, l[2] = {ul.x, ul.y}, zw[2] = {zz.x, zz.y};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int w = c >> 1, sh = (c & 1) * 16;
+      u[c] = bf2f((bf16_t)(h[w] >> sh)) + bf2f((bf16_t)(l[w] >> sh));
+      z[c] = bf2f((bf16_t)(zw[w] >> sh));
+    }
+  } else {
+    const float4 uv = *(const float4 *)((const float *)a.u + e);
+    const float4 zv = *(const float4 *)((const float *)a.xz + tok * 2 * a.D + a.D + i);
+    u[0] = uv.x; u[1] = uv.y; u[2] = uv.z; u[3] = uv.w;
+    z[0] = zv.x; z[1] = zv.y; z[2] = zv.z; z[3] = zv.w;
+  }
+  const float4 Dv = *(const float4 *)(a.Dskip + i);
+  const float dv[4] = {Dv.x, Dv.y, Dv.z, Dv.w};
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+    io<T>::st((T *)a.y + e + c, __builtin_fmaf(dv[c], u[c], sv[c]) * silu_f(z[c]));
+}
+
 template <typename T, int K>
 hipError_t dispatch_chunked_k(const ScanArgs &a, hipStream_t s) {
   const unsigned blocks = (unsigned)((int64_t)a.B * (a.D / kCh));
-  if (a.zoh)
-    hipLaunchKernelGGL((scan_chunked_kernel<T, true, K>), dim3(blocks), dim3(kW * 64), 0, s, a);
-  else
-    hipLaunchKernelGGL((scan_chunked_kernel<T, false, K>), dim3(blocks), dim3(kW * 64), 0, s, a);
+  if (a.N == kN) {
+    if (a.zoh)
+      hipLaunchKernelGGL((scan_chunked_kernel<T, true, K, false>), dim3(blocks), dim3(kW * 64), 0, s, a);
+    else
+      hipLaunchKernelGGL((scan_chunked_kernel<T, false, K, false>), dim3(blocks), dim3(kW * 64), 0, s, a);
+    return hipGetLastError();
+  }
+  // d_state = 16 G: one launch per group of 16 states, each writing its part of y, then the
+  // combine
+  const int G = a.N / kN;
+  for (int g = 0; g < G; ++g) {
+    ScanArgs ag = a;
+    ag.g0 = g * kN;
+    ag.yacc = a.yacc + (int64_t)g * a.B * a.L * a.D;
+    if (a.zoh)
+      hipLaunchKernelGGL((scan_chunked_kernel<T, true, K, true>), dim3(blocks), dim3(kW * 64), 0, s, ag);
+    else
+      hipLaunchKernelGGL((scan_chunked_kernel<T, false, K, true>), dim3(blocks), dim3(kW * 64), 0, s, ag);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const int64_t n4 = (int64_t)a.B * a.L * a.D / 4;
+  hipLaunchKernelGGL((scan_combine_kernel<T>), dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s,
+                     a, G);
   return hipGetLastError();
 }
 
@@ -458,6 +535,7 @@ bool use_chunked(const ScanArgs &a) {
 template <typename T>
 hipError_t dispatch(const ScanArgs &a, hipStream_t s) {
   const bool ch = use_chunked(a);
+  if (a.N != kN && !(ch && a.yacc)) return hipErrorInvalidValue;
   switch (a.K) {
     case 2: return ch ? dispatch_chunked_k<T, 2>(a, s) : dispatch_k<T, 2>(a, s);
     case 3: return ch ? dispatch_chunked_k<T, 3>(a, s) : dispatch_k<T, 3>(a, s);
@@ -469,8 +547,16 @@ hipError_t dispatch(const ScanArgs &a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_scan(mm_dtype dt, const ScanArgs &a, hipStream_t s) {
-  if (a.N != kN) return hipErrorInvalidValue;
+  if (a.N != kN && !(a.N == 2 * kN || a.N == 4 * kN)) return hipErrorInvalidValue;
   return dt == MM_BF16 ? dispatch<bf16_t>(a, s) : dispatch<float>(a, s);
+}
+
+bool scan_groups_used(int B, int L, int D, int N, uint32_t force) {
+  if (N != 2 * kN && N != 4 * kN) return false;
+  ScanArgs a{};
+  a.force = force;
+  a.B = B; a.L = L; a.D = D; a.N = N;
+  return use_chunked(a);
 }
 
 }  // namespace mm

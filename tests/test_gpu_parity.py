@@ -241,6 +241,19 @@ def test_state_size_sweep_prefill(N, io):
     _case(cfg, 400 + N, states=True, conv_bias=True, gamma_random=True)
 
 
+# d_state 32 / 64 on the time-parallel kernel: one launch per group of 16 states (state offset
+# and stride N), each writing its part of y in fp32, then the combine with D u and the gate
+@pytest.mark.parametrize("N", [32, 64])
+@pytest.mark.parametrize("io,zoh", [("f32", False), ("f32", True), ("bf16", False), ("bf16", True)])
+def test_state_groups_on_the_time_parallel_kernel(N, io, zoh):
+    if io == "f32":   # two full 128-token blocks and a ragged tail of 44
+        cfg = TINY.with_(batch=2, seqlen=300, d_state=N, name=f"f32_grp_N{N}")
+    else:             # 8 blocks and a ragged tail
+        cfg = BF16_SMALL.with_(batch=1, seqlen=1100, d_state=N, name=f"bf16_grp_N{N}")
+    _case(cfg, 470 + N + 2 * zoh, states=True, conv_bias=True, gamma_random=True, zoh=zoh,
+          scan="chunked")
+
+
 @pytest.mark.parametrize("N", [8, 64])
 def test_state_size_sweep_zoh(N):
     _case(BF16_SMALL.with_(seqlen=600, d_state=N, name=f"bf16_zoh_N{N}"), 450 + N, states=True,
