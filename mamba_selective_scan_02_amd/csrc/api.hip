@@ -18,7 +18,8 @@ struct Workspace {
   bool fused_xproj;  // bf16: conv + x_proj + RMSNorm in one kernel (no u / xdbl buffers)
   bool tiled_dtproj; // bf16: token-stationary dt_proj kernel
   bool fast_decode;  // bf16 decode step: range-split x_proj, fused update (no u / xdbl buffers)
-  bool scan_groups;  // d_state 32 / 64 on the time-parallel kernel, one launch per 16 states
+  bool scan_tuned;   // d_state 8 / 32 / 64 on the time-parallel kernel of d_state 16
+  bool scan_groups;  // ... 32 / 64: one launch per 16 states
   int dec_ranges, dec_range_ch;
   size_t u, u_lo, xdbl, part, dtlow, dtlow_lo, bc, dt, yacc, gP, gS, total;
 };
@@ -33,7 +34,8 @@ uint32_t scan_force(uint32_t flags) {
 //   bf16 mode: (u_hi, u_lo [T,D] bf16 | xdbl f32, unless fused) | dt_low hi, lo [T,R] bf16 |
 //              B,C [T,2N] f32 | dt [T,D] f16
 //   bf16 decode step: partial x_proj sums [ranges, B, R+2N] f32 replace u and xdbl.
-//   d_state 32 / 64 on the time-parallel scan: each 16-state group's part of y [T,D] f32; other d_state != 16:
+//   d_state 32 / 64 on the time-parallel scan: each 16-state group's part of y [T,D] f32; other d_state != 16
+//   (not on that kernel):
 //   the general scan's per-range transfers P, S [B, ranges, D, N] f32.
 Workspace layout(const mm_shape &s, bool decode) {
   const size_t T = (size_t)s.batch * s.seqlen;
@@ -67,10 +69,11 @@ Workspace layout(const mm_shape &s, bool decode) {
   w.dt = o; o += up(T * s.d_inner * (bf ? 2 : 4));
   // d_state 32 / 64 on the time-parallel kernel: y's partial sums between the state groups;
   // other d_state != 16: per-range transfers of the general scan
-  w.scan_groups = !decode && scan_groups_used(s.batch, s.seqlen, s.d_inner, s.d_state,
-                                              scan_force(s.flags));
+  w.scan_tuned = !decode && scan_tuned_used(s.batch, s.seqlen, s.d_inner, s.d_state,
+                                            scan_force(s.flags));
+  w.scan_groups = w.scan_tuned && s.d_state > 16;
   w.yacc = o; if (w.scan_groups) o += up(T * s.d_inner * 4 * (size_t)(s.d_state / 16));
-  const size_t gsz = s.d_state != 16 && !w.scan_groups
+  const size_t gsz = s.d_state != 16 && !w.scan_tuned
                          ? (size_t)s.batch * scan_n_ranges(s.seqlen) * s.d_inner * s.d_state * 4 : 0;
   w.gP = o; o += up(gsz);
   w.gS = o; o += up(gsz);
@@ -261,7 +264,7 @@ mm_status run_mixer(const mm_shape *s, const mm_params *p, const void *xz, void 
                 y, ssm_state, states_valid && ssm_state != nullptr,
                 (s->flags & MM_FLAG_ZOH_B) ? 1 : 0,
                 (int)scan_force(s->flags), B, L, D, N};
-    if (N == 16) {
+    if (N == 16 || (w.scan_tuned && !w.scan_groups)) {
       MM_TRY(launch_scan(dt, sa, st));
     } else if (w.scan_groups) {
       sa.u = u;

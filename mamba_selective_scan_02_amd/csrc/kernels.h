@@ -230,9 +230,9 @@ struct ScanArgs {
   float *yacc = nullptr;
   int g0 = 0;
 };
-// N = 16, or N = 32 / 64 when scan_groups_used (then a.yacc is required)
+// N = 16; N = 8, 32, 64 when scan_tuned_used (32 / 64 then need a.yacc, a.u, a.u_lo)
 hipError_t launch_scan(mm_dtype dt, const ScanArgs &a, hipStream_t s);
-bool scan_groups_used(int B, int L, int D, int N, uint32_t force);
+bool scan_tuned_used(int B, int L, int D, int N, uint32_t force);
 bool scan_n_supported(int N);
 int scan_n_ranges(int L);
 hipError_t launch_scan_n(mm_dtype dt, const ScanArgs &a, hipStream_t s);

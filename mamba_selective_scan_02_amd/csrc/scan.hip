@@ -135,15 +135,20 @@ __device__ __forceinline__ void load_lds16(const void *src, void *lds) {
   dma16_opaque(src, lds_addr(lds));
 }
 
-// GRP: the kernel covers one group of 16 states [g0, g0 + 16) of a d_state = N > 16 problem
-// (A, B|C rows and the SSM state have stride N) and stores the group's part of C_t . h_t in
-// fp32 to a.yacc [B, L, D] (one buffer per group); scan_combine_kernel then adds the groups'
-// parts and D u and applies the gate.
-template <typename T, bool ZOH, int K, bool GRP>
+// MODE 0: d_state 16.
+// MODE 1 (GRP): the kernel covers one group of 16 states [g0, g0 + 16) of a d_state = N > 16
+// problem (A, B|C rows and the SSM state have stride N) and stores the group's part of
+// C_t . h_t in fp32 to a.yacc [B, L, D] (one buffer per group); scan_combine_kernel then adds
+// the groups' parts and D u and applies the gate.
+// MODE 2 (d_state 8): the lanes of state half p = 0 carry the 8 states; the p = 1 lanes run on
+// zero input (h stays 0, A = -1, B|C slots refilled with the real rows, never used) and own no
+// state, so y and the gate are those of d_state 16 with the half's terms equal to zero.
+template <typename T, bool ZOH, int K, int MODE>
 __global__ __launch_bounds__(kW * 64) void scan_chunked_kernel(ScanArgs a) {
   typedef typename Delta<T>::type DT;
-  const int NS = GRP ? a.N : kN;           // state stride
-  const int g0 = GRP ? a.g0 : 0;           // first state of this launch
+  constexpr bool GRP = MODE == 1, HALF = MODE == 2;
+  const int NS = GRP ? a.N : HALF ? kG : kN;   // state stride
+  const int g0 = GRP ? a.g0 : 0;               // first state of this launch
   constexpr int xper = 16 / sizeof(T);                 // x/z elements per 16-byte chunk
   constexpr int xrow_chunks = kCh * sizeof(T) / 16;    // 16-byte chunks per staged x/z row
   constexpr int drow_chunks = kCh * sizeof(DT) / 16;
@@ -177,7 +182,7 @@ __global__ __launch_bounds__(kW * 64) void scan_chunked_kernel(ScanArgs a) {
   float A2[kG], Av[kG], iA[kG];
 #pragma unroll
   for (int j = 0; j < kG; ++j) {
-    Av[j] = a.A[(int64_t)ch * NS + g0 + kG * p + j];
+    Av[j] = HALF && p ? -1.0f : a.A[(int64_t)ch * NS + g0 + kG * p + j];
     A2[j] = Av[j] * kLog2e;
     iA[j] = 1.0f / Av[j];
   }
@@ -186,7 +191,8 @@ __global__ __launch_bounds__(kW * 64) void scan_chunked_kernel(ScanArgs a) {
   // of agg_s, its S float w*1024 + 512 + tid (conflict-free, lane-contiguous)
   const int ql = (tid >> 2) & 63, qj = 4 * (tid >> 8) + (tid & 3);
   const int64_t qidx = ((int64_t)b * a.D + ch0 + (ql >> 1)) * NS + g0 + kG * (ql & 1) + qj;
-  float carry = (a.state_valid && a.state) ? a.state[qidx] : 0.f;
+  const bool qown = !HALF || !(ql & 1);    // the chain is one of the problem's states
+  float carry = (qown && a.state_valid && a.state) ? a.state[qidx] : 0.f;
 
   const int64_t row = 2LL * a.D;
   const T *xzb = (const T *)a.xz + (int64_t)b * a.L * row;
@@ -195,8 +201,10 @@ __global__ __launch_bounds__(kW * 64) void scan_chunked_kernel(ScanArgs a) {
   T *yb = (T *)a.y + (int64_t)b * a.L * a.D;
   float *accb = GRP ? a.yacc + (int64_t)b * a.L * a.D : nullptr;   // this group's part of y
   // this lane's 16-byte slot of a staged B|C row: slots 0-3 B[g0 .. g0+15], 4-7 C[g0 .. g0+15]
+  // (d_state 8: slots 2, 3 and 6, 7 repeat 0, 1 and 4, 5)
   const int bcq = lane & 7;
-  const int bcoff = g0 + 4 * bcq + (bcq >= 4 ? NS - kN : 0);
+  const int bcoff = HALF ? 4 * (bcq & 1) + (bcq >= 4 ? kG : 0)
+                         : g0 + 4 * bcq + (bcq >= 4 ? NS - kN : 0);
   const int nblocks = (a.L + kBlk - 1) / kBlk;
   const int Lm1 = a.L - 1;
 
@@ -345,7 +353,7 @@ __global__ __launch_bounds__(kW * 64) void scan_chunked_kernel(ScanArgs a) {
 #pragma unroll
     for (int t = 0; t < kS; ++t) {
       const float2 pd = pd_s[wv][t][c];
-      const float dt = pd.x, du = pd.y;
+      const float dt = pd.x, du = HALF && p ? 0.f : pd.y;
       sumdt += dt;
       const float4 B0 = *(const float4 *)&bc_cur[wv][t][kG * p];
       const float4 B1 = *(const float4 *)&bc_cur[wv][t][kG * p + 4];
@@ -408,7 +416,7 @@ __global__ __launch_bounds__(kW * 64) void scan_chunked_kernel(ScanArgs a) {
         const float4 C1 = *(const float4 *)&bc_cur[wv][ts][kN + kG * p + 4];
         const float Bv[kG] = {B0.x, B0.y, B0.z, B0.w, B1.x, B1.y, B1.z, B1.w};
         const float Cv[kG] = {C0.x, C0.y, C0.z, C0.w, C1.x, C1.y, C1.z, C1.w};
-        const float du = pd_s[wv][ts][c].y;
+        const float du = HALF && p ? 0.f : pd_s[wv][ts][c].y;
         float yy = 0.f;
 #pragma unroll
         for (int j = 0; j < kG; ++j) {
@@ -439,7 +447,7 @@ __global__ __launch_bounds__(kW * 64) void scan_chunked_kernel(ScanArgs a) {
     block(blk, odd ? bc_s1 : bc_s0, odd ? bc_s0 : bc_s1);
   }
   flush();
-  if (a.state) a.state[qidx] = carry;
+  if (a.state && qown) a.state[qidx] = carry;
 }
 
 // y = (sum over the G state groups of their parts + D u) * SiLU(z), 4 channels per thread; u
@@ -485,11 +493,17 @@ __global__ __launch_bounds__(256) void scan_combine_kernel(ScanArgs a, int G) {
 template <typename T, int K>
 hipError_t dispatch_chunked_k(const ScanArgs &a, hipStream_t s) {
   const unsigned blocks = (unsigned)((int64_t)a.B * (a.D / kCh));
-  if (a.N == kN) {
-    if (a.zoh)
-      hipLaunchKernelGGL((scan_chunked_kernel<T, true, K, false>), dim3(blocks), dim3(kW * 64), 0, s, a);
-    else
-      hipLaunchKernelGGL((scan_chunked_kernel<T, false, K, false>), dim3(blocks), dim3(kW * 64), 0, s, a);
+  if (a.N == kN || a.N == kG) {
+    if (a.N == kG) {
+      if (a.zoh)
+        hipLaunchKernelGGL((scan_chunked_kernel<T, true, K, 2>), dim3(blocks), dim3(kW * 64), 0, s, a);
+      else
+        hipLaunchKernelGGL((scan_chunked_kernel<T, false, K, 2>), dim3(blocks), dim3(kW * 64), 0, s, a);
+    } else if (a.zoh) {
+      hipLaunchKernelGGL((scan_chunked_kernel<T, true, K, 0>), dim3(blocks), dim3(kW * 64), 0, s, a);
+    } else {
+      hipLaunchKernelGGL((scan_chunked_kernel<T, false, K, 0>), dim3(blocks), dim3(kW * 64), 0, s, a);
+    }
     return hipGetLastError();
   }
   // d_state = 16 G: one launch per group of 16 states, each writing its part of y, then the
@@ -500,9 +514,9 @@ hipError_t dispatch_chunked_k(const ScanArgs &a, hipStream_t s) {
     ag.g0 = g * kN;
     ag.yacc = a.yacc + (int64_t)g * a.B * a.L * a.D;
     if (a.zoh)
-      hipLaunchKernelGGL((scan_chunked_kernel<T, true, K, true>), dim3(blocks), dim3(kW * 64), 0, s, ag);
+      hipLaunchKernelGGL((scan_chunked_kernel<T, true, K, 1>), dim3(blocks), dim3(kW * 64), 0, s, ag);
     else
-      hipLaunchKernelGGL((scan_chunked_kernel<T, false, K, true>), dim3(blocks), dim3(kW * 64), 0, s, ag);
+      hipLaunchKernelGGL((scan_chunked_kernel<T, false, K, 1>), dim3(blocks), dim3(kW * 64), 0, s, ag);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -535,7 +549,8 @@ bool use_chunked(const ScanArgs &a) {
 template <typename T>
 hipError_t dispatch(const ScanArgs &a, hipStream_t s) {
   const bool ch = use_chunked(a);
-  if (a.N != kN && !(ch && a.yacc)) return hipErrorInvalidValue;
+  // d_state 8 and the 16-state groups of 32 / 64 run on the time-parallel kernel only
+  if (a.N != kN && !(ch && (a.N == kG || a.yacc))) return hipErrorInvalidValue;
   switch (a.K) {
     case 2: return ch ? dispatch_chunked_k<T, 2>(a, s) : dispatch_k<T, 2>(a, s);
     case 3: return ch ? dispatch_chunked_k<T, 3>(a, s) : dispatch_k<T, 3>(a, s);
@@ -547,12 +562,12 @@ hipError_t dispatch(const ScanArgs &a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_scan(mm_dtype dt, const ScanArgs &a, hipStream_t s) {
-  if (a.N != kN && !(a.N == 2 * kN || a.N == 4 * kN)) return hipErrorInvalidValue;
+  if (a.N != kN && a.N != kG && a.N != 2 * kN && a.N != 4 * kN) return hipErrorInvalidValue;
   return dt == MM_BF16 ? dispatch<bf16_t>(a, s) : dispatch<float>(a, s);
 }
 
-bool scan_groups_used(int B, int L, int D, int N, uint32_t force) {
-  if (N != 2 * kN && N != 4 * kN) return false;
+bool scan_tuned_used(int B, int L, int D, int N, uint32_t force) {
+  if (N != kG && N != 2 * kN && N != 4 * kN) return false;
   ScanArgs a{};
   a.force = force;
   a.B = B; a.L = L; a.D = D; a.N = N;

@@ -242,8 +242,9 @@ def test_state_size_sweep_prefill(N, io):
 
 
 # d_state 32 / 64 on the time-parallel kernel: one launch per group of 16 states (state offset
-# and stride N), each writing its part of y in fp32, then the combine with D u and the gate
-@pytest.mark.parametrize("N", [32, 64])
+# and stride N), each writing its part of y in fp32, then the combine with D u and the gate;
+# d_state 8: one launch with the upper state half of every channel idle
+@pytest.mark.parametrize("N", [8, 32, 64])
 @pytest.mark.parametrize("io,zoh", [("f32", False), ("f32", True), ("bf16", False), ("bf16", True)])
 def test_state_groups_on_the_time_parallel_kernel(N, io, zoh):
     if io == "f32":   # two full 128-token blocks and a ragged tail of 44
