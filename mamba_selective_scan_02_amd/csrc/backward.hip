@@ -13,9 +13,10 @@
 //
 // Kernels, in launch order:
 //   bw_conv_u_kernel          u = SiLU(conv1d(x) + b) in fp32                  [T, D]
-//   gemm_f32_kernel           the six products (x_proj, dt_proj, their input and weight
-//                             gradients): fp32 16x16x4 MFMA, 128 x 128 (128 x 64 for
-//                             N <= 512) tiles, any strides
+//   products                  x_proj, dt_proj, their input and weight gradients: with bf16
+//                             I/O split-bf16 MFMA products (bwgemm.hip: each fp32 operand as
+//                             bf16 high + low planes); with fp32 I/O gemm_f32_kernel (fp32
+//                             16x16x4 MFMA, 128 x 128 or 128 x 64 tiles, any strides)
 //   (norm_kernel)             the forward's RMSNorm of dt_low, B, C (fp32 mode)
 //   bw_range_transfer_kernel  per range of kRT tokens and (channel, 4 states), 64 channels per
 //                             workgroup with staged inputs, one forward pass: the forward
@@ -35,8 +36,8 @@
 //                             sub-block ahead (the recurrence never waits on global memory).
 //                             Sums over the 16 states: transposed DPP reductions within a
 //                             16-lane row; dB and dC (shared by all channels) sum over the
-//                             wave's 4 channels on fp32 MFMA, over the 8 waves in LDS, into
-//                             per-workgroup rows
+//                             wave's 4 channels with lane swaps across rows, over the 8 waves
+//                             in LDS, into per-workgroup rows
 //   bw_rowsum_kernel          dB | dC from those per-workgroup rows
 //   bw_norm_bwd_kernel        the three RMSNorm backwards per token (+ gain terms)
 //   bw_colsum_kernels         fixed-order column sums (bias, gains, D, A, conv partials)
