@@ -42,9 +42,15 @@ Workspace layout(const mm_shape &s, bool decode) {
   const bool bf = s.io_dtype == MM_BF16;
   const size_t e = esz(s.io_dtype);
   Workspace w;
-  // one workgroup per 128 tokens: worth it once there are enough tokens to fill the chip
+  // d_state 8 / 32 / 64 on the time-parallel kernel of d_state 16 (which recomputes u from x)
+  w.scan_tuned = !decode && scan_tuned_used(s.batch, s.seqlen, s.d_inner, s.d_state,
+                                            scan_force(s.flags));
+  w.scan_groups = w.scan_tuned && s.d_state > 16;
+  // one workgroup per 128 tokens: worth it once there are enough tokens to fill the chip; it
+  // writes no u, so d_state != 16 takes it only where the scan recomputes u
   w.fused_xproj = !decode && bf && T >= 32768 &&
-                  xproj_fused_supported(s.dt_rank, s.d_state, s.d_inner, s.d_conv);
+                  xproj_fused_supported(s.dt_rank, s.d_state, s.d_inner, s.d_conv) &&
+                  (s.d_state == 16 || w.scan_tuned);
   w.tiled_dtproj = bf && dtproj_supported(s.dt_rank, s.d_inner);
   w.fast_decode = decode && bf && decode_fast_supported(s.dt_rank, s.d_state, s.d_inner, s.d_conv);
   w.dec_ranges = 0;
@@ -69,9 +75,6 @@ Workspace layout(const mm_shape &s, bool decode) {
   w.dt = o; o += up(T * s.d_inner * (bf ? 2 : 4));
   // d_state 32 / 64 on the time-parallel kernel: y's partial sums between the state groups;
   // other d_state != 16: per-range transfers of the general scan
-  w.scan_tuned = !decode && scan_tuned_used(s.batch, s.seqlen, s.d_inner, s.d_state,
-                                            scan_force(s.flags));
-  w.scan_groups = w.scan_tuned && s.d_state > 16;
   w.yacc = o; if (w.scan_groups) o += up(T * s.d_inner * 4 * (size_t)(s.d_state / 16));
   const size_t gsz = s.d_state != 16 && !w.scan_tuned
                          ? (size_t)s.batch * scan_n_ranges(s.seqlen) * s.d_inner * s.d_state * 4 : 0;
@@ -231,7 +234,7 @@ mm_status run_mixer(const mm_shape *s, const mm_params *p, const void *xz, void 
     XprojFusedArgs xa{(const uint16_t *)xz, (const uint16_t *)p->conv_w, (const uint16_t *)p->conv_b,
                       (const uint16_t *)conv_state, conv_valid, (const uint16_t *)p->x_proj_w,
                       (uint16_t *)dtlow, (uint16_t *)dtlow_lo, bc, p->dt_norm_w, p->B_norm_w,
-                      p->C_norm_w, s->rms_eps, B, L, D, R, K};
+                      p->C_norm_w, s->rms_eps, B, L, D, R, K, N};
     MM_TRY(launch_xproj_fused(xa, st));
   } else {
     {
@@ -267,8 +270,6 @@ mm_status run_mixer(const mm_shape *s, const mm_params *p, const void *xz, void 
     if (N == 16 || (w.scan_tuned && !w.scan_groups)) {
       MM_TRY(launch_scan(dt, sa, st));
     } else if (w.scan_groups) {
-      sa.u = u;
-      sa.u_lo = u_lo;
       sa.yacc = (float *)(ws + w.yacc);
       MM_TRY(launch_scan(dt, sa, st));
     } else {

@@ -50,6 +50,7 @@ struct XprojFusedArgs {
   const float *g_dt, *g_B, *g_C;
   float eps;
   int B, L, D, R, K;
+  int N = 16;                  // d_state: 8, 16 or 32
 };
 bool xproj_fused_supported(int R, int N, int D, int K);
 hipError_t launch_xproj_fused(const XprojFusedArgs &a, hipStream_t s);
@@ -226,11 +227,11 @@ struct ScanArgs {
   float *gP = nullptr, *gS = nullptr;
   // d_state 32 / 64 on the time-parallel kernel (scan.hip): one launch per 16-state group
   // (first state g0), each writing its part of y as fp32 [B, L, D] to yacc + g B L D, then a
-  // combine kernel (which reads u as above)
+  // combine kernel
   float *yacc = nullptr;
   int g0 = 0;
 };
-// N = 16; N = 8, 32, 64 when scan_tuned_used (32 / 64 then need a.yacc, a.u, a.u_lo)
+// N = 16; N = 8, 32, 64 when scan_tuned_used (32 / 64 then need a.yacc)
 hipError_t launch_scan(mm_dtype dt, const ScanArgs &a, hipStream_t s);
 bool scan_tuned_used(int B, int L, int D, int N, uint32_t force);
 bool scan_n_supported(int N);

@@ -136,17 +136,17 @@ __device__ __forceinline__ void load_lds16(const void *src, void *lds) {
 }
 
 // MODE 0: d_state 16.
-// MODE 1 (GRP): the kernel covers one group of 16 states [g0, g0 + 16) of a d_state = N > 16
+// MODE 1 / 3 (GRP): the kernel covers one group of 16 states [g0, g0 + 16) of a d_state = N > 16
 // problem (A, B|C rows and the SSM state have stride N) and stores the group's part of
-// C_t . h_t in fp32 to a.yacc [B, L, D] (one buffer per group); scan_combine_kernel then adds
-// the groups' parts and D u and applies the gate.
+// C_t . h_t in fp32 to a.yacc [B, L, D] (one buffer per group; MODE 3, the first group, adds
+// D u to its part); scan_combine_kernel then adds the groups' parts and applies the gate.
 // MODE 2 (d_state 8): the lanes of state half p = 0 carry the 8 states; the p = 1 lanes run on
 // zero input (h stays 0, A = -1, B|C slots refilled with the real rows, never used) and own no
 // state, so y and the gate are those of d_state 16 with the half's terms equal to zero.
 template <typename T, bool ZOH, int K, int MODE>
 __global__ __launch_bounds__(kW * 64) void scan_chunked_kernel(ScanArgs a) {
   typedef typename Delta<T>::type DT;
-  constexpr bool GRP = MODE == 1, HALF = MODE == 2;
+  constexpr bool GRP = MODE == 1 || MODE == 3, HALF = MODE == 2, GFIRST = MODE == 3;
   const int NS = GRP ? a.N : HALF ? kG : kN;   // state stride
   const int g0 = GRP ? a.g0 : 0;               // first state of this launch
   constexpr int xper = 16 / sizeof(T);                 // x/z elements per 16-byte chunk
@@ -436,7 +436,8 @@ __global__ __launch_bounds__(kW * 64) void scan_chunked_kernel(ScanArgs a) {
       const float other = __builtin_bit_cast(
           float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, send), 0xB1, 0xF, 0xF, false));
       const float2 eg = eg_s[wv][t + p][c];
-      ypend[t / 2] = GRP ? keep + other : (keep + other + eg.x) * eg.y;
+      ypend[t / 2] = GFIRST ? keep + other + eg.x
+                     : GRP ? keep + other : (keep + other + eg.x) * eg.y;
     }
     ypend_t0 = T0;
   };
@@ -450,8 +451,8 @@ __global__ __launch_bounds__(kW * 64) void scan_chunked_kernel(ScanArgs a) {
   if (a.state && qown) a.state[qidx] = carry;
 }
 
-// y = (sum over the G state groups of their parts + D u) * SiLU(z), 4 channels per thread; u
-// from the conv kernel's output (fp32, or bf16 high + low parts), the parts fp32
+// y = (sum over the G state groups of their parts; the first holds D u) * SiLU(z), 4 channels
+// per thread
 template <typename T>
 __global__ __launch_bounds__(256) void scan_combine_kernel(ScanArgs a, int G) {
   const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;   // 4 consecutive channels
@@ -465,29 +466,18 @@ __global__ __launch_bounds__(256) void scan_combine_kernel(ScanArgs a, int G) {
     s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
   }
   const float sv[4] = {s.x, s.y, s.z, s.w};
-  float u[4], z[4];
+  float z[4];
   if (sizeof(T) == 2) {
-    const uint2 uh = *(const uint2 *)((const bf16_t *)a.u + e);
-    const uint2 ul = *(const uint2 *)((const bf16_t *)a.u_lo + e);
     const uint2 zz = *(const uint2 *)((const bf16_t *)a.xz + tok * 2 * a.D + a.D + i);
-    const uint32_t h[2] = {uh.x, uh.y}, l[2] = {ul.x, ul.y}, zw[2] = {zz.x, zz.y};
+    const uint32_t zw[2] = {zz.x, zz.y};
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int w = c >> 1, sh = (c & 1) * 16;
-      u[c] = bf2f((bf16_t)(h[w] >> sh)) + bf2f((bf16_t)(l[w] >> sh));
-      z[c] = bf2f((bf16_t)(zw[w] >> sh));
-    }
+    for (int c = 0; c < 4; ++c) z[c] = bf2f((bf16_t)(zw[c >> 1] >> ((c & 1) * 16)));
   } else {
-    const float4 uv = *(const float4 *)((const float *)a.u + e);
     const float4 zv = *(const float4 *)((const float *)a.xz + tok * 2 * a.D + a.D + i);
-    u[0] = uv.x; u[1] = uv.y; u[2] = uv.z; u[3] = uv.w;
     z[0] = zv.x; z[1] = zv.y; z[2] = zv.z; z[3] = zv.w;
   }
-  const float4 Dv = *(const float4 *)(a.Dskip + i);
-  const float dv[4] = {Dv.x, Dv.y, Dv.z, Dv.w};
 #pragma unroll
-  for (int c = 0; c < 4; ++c)
-    io<T>::st((T *)a.y + e + c, __builtin_fmaf(dv[c], u[c], sv[c]) * silu_f(z[c]));
+  for (int c = 0; c < 4; ++c) io<T>::st((T *)a.y + e + c, sv[c] * silu_f(z[c]));
 }
 
 template <typename T, int K>
@@ -513,10 +503,16 @@ hipError_t dispatch_chunked_k(const ScanArgs &a, hipStream_t s) {
     ScanArgs ag = a;
     ag.g0 = g * kN;
     ag.yacc = a.yacc + (int64_t)g * a.B * a.L * a.D;
-    if (a.zoh)
+    if (g == 0) {
+      if (a.zoh)
+        hipLaunchKernelGGL((scan_chunked_kernel<T, true, K, 3>), dim3(blocks), dim3(kW * 64), 0, s, ag);
+      else
+        hipLaunchKernelGGL((scan_chunked_kernel<T, false, K, 3>), dim3(blocks), dim3(kW * 64), 0, s, ag);
+    } else if (a.zoh) {
       hipLaunchKernelGGL((scan_chunked_kernel<T, true, K, 1>), dim3(blocks), dim3(kW * 64), 0, s, ag);
-    else
+    } else {
       hipLaunchKernelGGL((scan_chunked_kernel<T, false, K, 1>), dim3(blocks), dim3(kW * 64), 0, s, ag);
+    }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -5,7 +5,7 @@
 // (RMSNorm on the mixer's internal activations). The conv1d + SiLU producing the projection's
 // input is the standard Mamba-1 block the page builds on.
 //
-// Design (bf16 I/O, dt_rank = 16 * RB, d_state = 16):
+// Design (bf16 I/O, dt_rank = 16 * RB, d_state N = 8, 16 or 32):
 //   * One workgroup = a tile of 128 consecutive tokens of one sequence and ALL R + 2N outputs
 //     of those tokens, so every (token, channel) input u is formed once and the three RMSNorms
 //     run in the epilogue (xdbl never goes to memory).
@@ -45,11 +45,12 @@ constexpr int kXR = 144;           // staged x rows: 3 before the tile + 128, pa
 // one logical slot of consecutive rows)
 __device__ __forceinline__ int swz8(int r, int c) { return c ^ ((r >> 1) & 7); }
 
-template <int RB, int K>
+template <int RB, int K, int N>
 __global__ __launch_bounds__(1024) void xproj_fused_kernel(XprojFusedArgs a) {
   static_assert(K == 4, "the staged conv taps are laid out as [channel][4]");
+  static_assert(N == 8 || N == 16 || N == 32, "B | C fill whole 16-row blocks");
   constexpr int R = RB * 16;
-  constexpr int NX = R + 32;           // outputs: dt_low | B | C
+  constexpr int NX = R + 2 * N;        // outputs: dt_low | B | C
   constexpr int NB = NX / 16;          // 16-row MFMA blocks
   constexpr int LW = NX / 16;          // 1 KB wave-loads per chunk: W_x rows
   constexpr int PW = (LW + 7) / 8;     // W_x loads per producer wave (padded)
@@ -242,6 +243,8 @@ __global__ __launch_bounds__(1024) void xproj_fused_kernel(XprojFusedArgs a) {
   }
 
   // ---- epilogue: acc[tb][nb][j] = xdbl[token (cw*TB + tb)*16 + tl][nb*16 + 4g + j]
+  // B | C column of this lane's 4 values in block nb >= RB; they are B's when below N
+  auto bcol = [&](int nb) { return (nb - RB) * 16 + 4 * g; };
 #pragma unroll
   for (int tb = 0; tb < TB; ++tb) {
     float ssd = 0.f, ssb = 0.f, ssc = 0.f;
@@ -251,7 +254,7 @@ __global__ __launch_bounds__(1024) void xproj_fused_kernel(XprojFusedArgs a) {
       for (int j = 0; j < 4; ++j) {
         const float v = acc[tb][nb][j];
         if (nb < RB) ssd = __builtin_fmaf(v, v, ssd);
-        else if (nb == RB) ssb = __builtin_fmaf(v, v, ssb);
+        else if (bcol(nb) < N) ssb = __builtin_fmaf(v, v, ssb);
         else ssc = __builtin_fmaf(v, v, ssc);
       }
     // the 4 lanes of a token are l%16 + 16 * {0, 1, 2, 3}
@@ -259,8 +262,8 @@ __global__ __launch_bounds__(1024) void xproj_fused_kernel(XprojFusedArgs a) {
     ssb += __shfl_xor(ssb, 16, 64); ssb += __shfl_xor(ssb, 32, 64);
     ssc += __shfl_xor(ssc, 16, 64); ssc += __shfl_xor(ssc, 32, 64);
     const float id = 1.0f / sqrtf(ssd / (float)R + a.eps);
-    const float ib = 1.0f / sqrtf(ssb / 16.0f + a.eps);
-    const float ic = 1.0f / sqrtf(ssc / 16.0f + a.eps);
+    const float ib = 1.0f / sqrtf(ssb / (float)N + a.eps);
+    const float ic = 1.0f / sqrtf(ssc / (float)N + a.eps);
     const int t = t0 + (cw * TB + tb) * 16 + tl;
     if (t < a.L) {
       const int64_t tok = (int64_t)b * a.L + t;
@@ -277,14 +280,16 @@ __global__ __launch_bounds__(1024) void xproj_fused_kernel(XprojFusedArgs a) {
         *(uint2 *)(a.dtlow + tok * R + n) = h;
         *(uint2 *)(a.dtlow_lo + tok * R + n) = l;
       }
-      const float4 gb = *(const float4 *)(a.g_B + 4 * g);
-      const float4 gc = *(const float4 *)(a.g_C + 4 * g);
-      *(float4 *)(a.bc + tok * 32 + 4 * g) =
-          make_float4(acc[tb][RB][0] * ib * gb.x, acc[tb][RB][1] * ib * gb.y,
-                      acc[tb][RB][2] * ib * gb.z, acc[tb][RB][3] * ib * gb.w);
-      *(float4 *)(a.bc + tok * 32 + 16 + 4 * g) =
-          make_float4(acc[tb][RB + 1][0] * ic * gc.x, acc[tb][RB + 1][1] * ic * gc.y,
-                      acc[tb][RB + 1][2] * ic * gc.z, acc[tb][RB + 1][3] * ic * gc.w);
+#pragma unroll
+      for (int nb = RB; nb < NB; ++nb) {
+        const int col = bcol(nb);
+        const bool isb = col < N;
+        const float4 gm = *(const float4 *)(isb ? a.g_B + col : a.g_C + (col - N));
+        const float sc = isb ? ib : ic;
+        *(float4 *)(a.bc + tok * (2 * N) + col) =
+            make_float4(acc[tb][nb][0] * sc * gm.x, acc[tb][nb][1] * sc * gm.y,
+                        acc[tb][nb][2] * sc * gm.z, acc[tb][nb][3] * sc * gm.w);
+      }
     }
   }
 }
@@ -293,14 +298,21 @@ template <int RB>
 hipError_t launch_rb(const XprojFusedArgs &a, hipStream_t s) {
   const unsigned grid = (unsigned)(a.B * ((a.L + kTok - 1) / kTok));
   if (a.K != 4) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((xproj_fused_kernel<RB, 4>), dim3(grid), dim3(1024), 0, s, a);
+  switch (a.N) {
+    case 8: hipLaunchKernelGGL((xproj_fused_kernel<RB, 4, 8>), dim3(grid), dim3(1024), 0, s, a); break;
+    case 16: hipLaunchKernelGGL((xproj_fused_kernel<RB, 4, 16>), dim3(grid), dim3(1024), 0, s, a); break;
+    case 32: hipLaunchKernelGGL((xproj_fused_kernel<RB, 4, 32>), dim3(grid), dim3(1024), 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
 }  // namespace
 
+// d_state 8 / 16 / 32: R + 2N output rows in whole 16-row blocks, W_x in 4 LDS stages
 bool xproj_fused_supported(int R, int N, int D, int K) {
-  return N == 16 && K == 4 && D % (2 * kKC) == 0 && (R == 64 || R == 128 || R == 256);
+  return (N == 8 || N == 16 || N == 32) && K == 4 && D % (2 * kKC) == 0 &&
+         (R == 64 || R == 128 || R == 256);
 }
 
 hipError_t launch_xproj_fused(const XprojFusedArgs &a, hipStream_t s) {

@@ -112,12 +112,14 @@ def test_both_scan_kernels_bf16(scan, L):
           scan=scan)
 
 
-@pytest.mark.parametrize("B,L,R", [(1, 32768 + 77, 64), (2, 16448, 128)])
-def test_bf16_fused_projection_path(B, L, R):
+@pytest.mark.parametrize("B,L,R,N", [(1, 32768 + 77, 64, 16), (2, 16448, 128, 16),
+                                     (1, 32768 + 77, 64, 8), (1, 32768 + 77, 128, 32)])
+def test_bf16_fused_projection_path(B, L, R, N):
     # >= 32768 tokens selects the fused conv + x_proj + RMSNorm kernel (128-token tiles, ragged
-    # last tile) and the token-stationary dt_proj kernel
-    cfg = synth.MixerConfig(f"bf16_fused_R{R}", B, L, 256, 16, 4, R, "bf16")
-    _case(cfg, 111 + R, states=True, conv_bias=True, gamma_random=True)
+    # last tile) and the token-stationary dt_proj kernel; d_state 8 / 32 take it with the
+    # time-parallel scan of d_state 16 (B|C in one, or two, 16-row blocks of the product)
+    cfg = synth.MixerConfig(f"bf16_fused_R{R}_N{N}", B, L, 256, N, 4, R, "bf16")
+    _case(cfg, 111 + R + N, states=True, conv_bias=True, gamma_random=True)
 
 
 def test_chunked_prefill_equals_whole_on_gpu_and_oracle():
