@@ -38,12 +38,17 @@ __device__ __forceinline__ int swz(int r, int c) {
 }
 
 // softplus for fp16 storage: log(1 + e) from the hardware log2 when e = exp(v) is not tiny,
-// else e - e^2/2 (the rounding of 1 + e would dominate there); v itself above 15.
+// else e - e^2/2 (the rounding of 1 + e would dominate there); v itself above 15. Both forms
+// are computed and selected bitwise, so the compiler emits selects rather than divergent
+// branches around the log.
 __device__ __forceinline__ float softplus_h(float v) {
   const float e = exp2_hw(v * kLog2e);
   const float l = __builtin_amdgcn_logf(1.0f + e) * 0.69314718055994531f;
-  const float r = e < 9.765625e-4f ? __builtin_fmaf(-0.5f * e, e, e) : l;
-  return v > 15.0f ? v : r;
+  const float sm = __builtin_fmaf(-0.5f * e, e, e);
+  const uint32_t small = 0u - (uint32_t)(e < 9.765625e-4f);
+  const uint32_t big = 0u - (uint32_t)(v > 15.0f);
+  const uint32_t r = (__float_as_uint(sm) & small) | (__float_as_uint(l) & ~small);
+  return __uint_as_float((__float_as_uint(v) & big) | (r & ~big));
 }
 
 __device__ __forceinline__ uint32_t pack_h2(float a, float b) {
@@ -58,6 +63,7 @@ __global__ __launch_bounds__(512) void dtproj_kernel(DtprojArgs a, int ch_per_wg
   constexpr int RPW = 64 / S > 0 ? 64 / S : 1;  // rows per 1 KB wave-load (S <= 64)
   __shared__ __attribute__((aligned(16))) bf16_t w_s0[kChD][R];
   __shared__ __attribute__((aligned(16))) bf16_t w_s1[kChD][R];
+  __shared__ __attribute__((aligned(16))) float b_s[2][kChD];   // the chunk's bias, with its rows
 
   const int ntok = (a.T + kTokD - 1) / kTokD;
   const int gid = xcd_remap(blockIdx.x, gridDim.x);
@@ -85,17 +91,19 @@ __global__ __launch_bounds__(512) void dtproj_kernel(DtprojArgs a, int ch_per_wg
       const int r = e / S, ps = e % S;
       load_lds16(a.w + (int64_t)(c0 + r) * R + swz<S>(r, ps) * 8, &wdst[0][0] + ld * 512);
     }
+    if (wv == 0 && lane < kChD / 4) load_lds16(a.bias + c0 + 4 * lane, &b_s[ck & 1][0]);
   };
 
   // Outputs of chunk ck are stored at the start of chunk ck+1, after that chunk's wait, so
   // the wait for the staged W_dt rows never has to cover freshly issued stores.
   uint2 pend[4];
   int pend_c = -1;
+  _Float16 *drow = a.dt + (int64_t)tokc * a.D + 4 * g;   // this lane's outputs: + channel
   auto flush = [&]() {
     if (pend_c >= 0 && tok < a.T) {
+      uint2 *p = (uint2 *)(drow + pend_c);
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb)
-        *(uint2 *)(a.dt + (int64_t)tok * a.D + pend_c + nb * 16 + 4 * g) = pend[nb];
+      for (int nb = 0; nb < 4; ++nb) p[4 * nb] = pend[nb];   // channels + 16 nb
     }
   };
   auto chunk = [&](int ck, bf16_t (*wcur)[R], bf16_t (*wnxt)[R]) {
@@ -121,9 +129,10 @@ __global__ __launch_bounds__(512) void dtproj_kernel(DtprojArgs a, int ch_per_wg
     }
     // acc[nb][j] = pre-activation of (token tok, channel c0 + 16 nb + 4 g + j)
     const int c0 = cbeg + ck * kChD;
+    const float *bcur = &b_s[ck & 1][0];
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
-      const float4 bv = *(const float4 *)(a.bias + c0 + nb * 16 + 4 * g);
+      const float4 bv = *(const float4 *)(bcur + nb * 16 + 4 * g);
       pend[nb].x = pack_h2(softplus_h(acc[nb][0] + bv.x), softplus_h(acc[nb][1] + bv.y));
       pend[nb].y = pack_h2(softplus_h(acc[nb][2] + bv.z), softplus_h(acc[nb][3] + bv.w));
     }
