@@ -152,11 +152,11 @@ struct StageScope {
     rec.stage = stage;
     rec.a = t->get();
     rec.b = t->get();
-    if (rec.a) hipEventRecord(rec.a, s);
+    if (rec.a) (void)hipEventRecord(rec.a, s);   // timing only: a failed record drops the sample
   }
   ~StageScope() {
     if (!t || !rec.a || !rec.b) return;
-    hipEventRecord(rec.b, s);
+    (void)hipEventRecord(rec.b, s);
     t->recs.push_back(rec);
   }
 };
@@ -718,7 +718,7 @@ void mm_stage_timer_reset(mm_stage_timer *t) {
 void mm_stage_timer_destroy(mm_stage_timer *t) {
   if (!t) return;
   mm_stage_timer_reset(t);
-  for (hipEvent_t e : t->pool) hipEventDestroy(e);
+  for (hipEvent_t e : t->pool) (void)hipEventDestroy(e);
   delete t;
 }
 

@@ -481,7 +481,7 @@ __global__ __launch_bounds__(kST2, 4) void bw_scan_kernel(BwArgs a) {
       yp[k & 7] = s_bc[k * 32 + 16 + n] * h;
       if ((k & 7) == 7) {
         const float ys = tsum8(yp, n);       // token k - 7 + n / 2 (both lanes of a pair)
-        const int kt = k - 7 + (n >> 1), t = t0 + j * kSB2 + kt;
+        const int kt = k - 7 + (n >> 1);
         if (!(n & 1)) {   // the gate: dz = dy ys SiLU'(z), ys = C.h + D u
           const float yv = __builtin_fmaf(Dv, s_u[kt * kCG2 + c], ys);
           o_s[0][kt][c] = s_gz[kt * kCG2 + c] * yv;

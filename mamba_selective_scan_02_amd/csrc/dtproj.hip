@@ -60,7 +60,6 @@ template <int R>
 __global__ __launch_bounds__(512) void dtproj_kernel(DtprojArgs a, int ch_per_wg) {
   constexpr int S = R / 8;             // 16-byte slots per W_dt row
   constexpr int KS = R / 32;           // k-steps
-  constexpr int RPW = 64 / S > 0 ? 64 / S : 1;  // rows per 1 KB wave-load (S <= 64)
   __shared__ __attribute__((aligned(16))) bf16_t w_s0[kChD][R];
   __shared__ __attribute__((aligned(16))) bf16_t w_s1[kChD][R];
   __shared__ __attribute__((aligned(16))) float b_s[2][kChD];   // the chunk's bias, with its rows
