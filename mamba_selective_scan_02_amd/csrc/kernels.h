@@ -139,7 +139,7 @@ struct BwArgs {
                                             // pre-activation) into sig, and du
   float *rP, *rS, *rR, *dA_part;            // [B, nr, D, 16]
   float *dD_part;                           // [B, nr, D]
-  float *bc_part, *dbc;                     // [T, D/64, 32], [T, 32]
+  float *bc_part, *dbc;                     // [T, D/32, 32], [T, 32]
   float *ddtn, *dxd, *gc;                   // [T, R], [T, R+32], [T, R+32]
   float *conv_part;                         // [B, conv strips, D, 5]
   float *conv_sum;                          // [D, 5]
