@@ -230,15 +230,17 @@ def test_outputs_are_deterministic():
     assert torch.equal(y1, y2)
 
 
-# d_state other than 16: the general path (conv, x_proj, RMSNorm, dt_proj kernels) and the
-# general time-parallel scan (512-token ranges, their transfers composed in order)
+# d_state other than 16 with the default kernel selection: fp32 at 77 tokens takes the general
+# path (conv, x_proj, RMSNorm, dt_proj kernels and the general time-parallel scan); bf16 at 1100
+# tokens the time-parallel scan of d_state 16 (half the state lanes idle for 8, one launch per
+# 16 states for 32 / 64)
 @pytest.mark.parametrize("N", [8, 32, 64])
 @pytest.mark.parametrize("io", ["f32", "bf16"])
 def test_state_size_sweep_prefill(N, io):
     if io == "f32":
         cfg = TINY.with_(batch=2, seqlen=77, d_state=N, name=f"f32_N{N}")
     else:
-        # 1100 tokens: two full ranges and a ragged third
+        # 1100 tokens: 8 full 128-token blocks and a ragged ninth
         cfg = BF16_SMALL.with_(batch=1, seqlen=1100, d_state=N, name=f"bf16_N{N}")
     _case(cfg, 400 + N, states=True, conv_bias=True, gamma_random=True)
 
@@ -255,6 +257,17 @@ def test_state_groups_on_the_time_parallel_kernel(N, io, zoh):
         cfg = BF16_SMALL.with_(batch=1, seqlen=1100, d_state=N, name=f"bf16_grp_N{N}")
     _case(cfg, 470 + N + 2 * zoh, states=True, conv_bias=True, gamma_random=True, zoh=zoh,
           scan="chunked")
+
+
+# the general time-parallel scan (csrc/scan_n.hip) where the tuned kernel would be chosen by
+# default: "sequential" selects it for d_state != 16; 1100 tokens = two full 512-token ranges and
+# a ragged third, with carried states
+@pytest.mark.parametrize("N", [8, 32, 64])
+@pytest.mark.parametrize("zoh", [False, True])
+def test_general_scan_multiple_ranges(N, zoh):
+    cfg = BF16_SMALL.with_(batch=1, seqlen=1100, d_state=N, name=f"bf16_general_N{N}")
+    _case(cfg, 480 + N + zoh, states=True, conv_bias=True, gamma_random=True, zoh=zoh,
+          scan="sequential")
 
 
 @pytest.mark.parametrize("N", [8, 64])
