@@ -73,6 +73,32 @@ def test_workspace_size_formula():
     assert mm.decode_workspace_bytes(_shape(seqlen=2)) == 0      # decode needs seqlen == 1
 
 
+def test_workspace_size_for_other_state_sizes():
+    """d_state 8 / 32 / 64: where the time-parallel scan applies (few sequences, > 128 tokens)
+    the workspace holds no general-scan transfers; 32 / 64 add one fp32 part of y per group of
+    16 states; the scan-selection flag "sequential" restores the general scan's transfers."""
+    up = lambda v: (v + 255) // 256 * 256  # noqa: E731
+    T, D, R = 1100, 256, 64
+
+    def general_projections(N):   # conv -> u hi+lo, xdbl, dt_low hi+lo, B|C, dt (fp16)
+        return (2 * up(T * D * 2) + up(T * (R + 2 * N) * 4) + 2 * up(T * R * 2)
+                + up(T * 2 * N * 4) + up(T * D * 2))
+
+    for N, groups in ((8, 0), (32, 2), (64, 4)):
+        s = _shape(seqlen=T, d_inner=D, dt_rank=R, d_state=N)
+        assert mm.prefill_workspace_bytes(s) == general_projections(N) + (
+            up(T * D * 4 * groups) if groups else 0), N
+        s.flags = mm.MM_FLAG_SCAN_SEQUENTIAL
+        nr = (T + 511) // 512
+        assert mm.prefill_workspace_bytes(s) == general_projections(N) + 2 * up(nr * D * N * 4), N
+    # >= 32768 tokens: d_state 8 / 32 also take the fused conv + x_proj + RMSNorm kernel
+    T = 32768 + 77
+    for N, groups in ((8, 0), (32, 2)):
+        s = _shape(seqlen=T, d_inner=D, dt_rank=R, d_state=N)
+        fused = 2 * up(T * R * 2) + up(T * 2 * N * 4) + up(T * D * 2)
+        assert mm.prefill_workspace_bytes(s) == fused + (up(T * D * 4 * groups) if groups else 0)
+
+
 @pytest.mark.parametrize("kw,status", [
     (dict(d_state=12), mm.MM_ERR_UNSUPPORTED),
     (dict(d_conv=5), mm.MM_ERR_UNSUPPORTED),
