@@ -145,14 +145,16 @@ __global__ __launch_bounds__(64 * kNormWaves) void decode_norm_kernel(DecodeNorm
   float v[kV];
 #pragma unroll
   for (int k = 0; k < kV; ++k) v[k] = 0.f;
+  // loads at a clamped index (always in bounds) and a masked add, so that the loads of a range
+  // are issued together rather than each behind its own branch and wait; same order of sums
 #pragma unroll 4
   for (int r = wv; r < a.nranges; r += kNormWaves) {
     const float *q = pp + r * rs;
+    float x[kV];
 #pragma unroll
-    for (int k = 0; k < kV; ++k) {
-      const int n = lane + 64 * k;
-      if (n < NX) v[k] += q[n];
-    }
+    for (int k = 0; k < kV; ++k) x[k] = q[min(lane + 64 * k, NX - 1)];
+#pragma unroll
+    for (int k = 0; k < kV; ++k) v[k] += lane + 64 * k < NX ? x[k] : 0.f;
   }
 #pragma unroll
   for (int k = 0; k < kV; ++k) red_s[wv][lane + 64 * k] = v[k];
