@@ -68,23 +68,37 @@ __global__ __launch_bounds__(256) void decode_xproj_kernel(DecodeXprojArgs a) {
     lds_barrier();
     if (ck + 1 < nck) stage(ck + 1, wnxt);
     const int c0 = cbeg + ck * kKC;
+    // every global input of the chunk's two k-steps is loaded before any is used, so that the
+    // wave waits once for all of them (one wave per SIMD: the registers are there)
+    uint4 cs_l[2][3], x_l[2], b_l[2];
+    uint2 w_l[2][8];
+    const bf16_t *cbp = a.conv_b ? a.conv_b : a.conv_w;   // without a bias: read, not used
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int ch = c0 + (ks * 4 + g) * 8;
+      const bf16_t *csp = a.conv_state + ((int64_t)bsc * a.D + ch) * 3;
+#pragma unroll
+      for (int q = 0; q < 3; ++q) cs_l[ks][q] = *(const uint4 *)(csp + 8 * q);
+      x_l[ks] = *(const uint4 *)(a.xz + (int64_t)bsc * 2 * a.D + ch);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) w_l[ks][e] = *(const uint2 *)(a.conv_w + (int64_t)(ch + e) * 4);
+      b_l[ks] = *(const uint4 *)(cbp + ch);   // the 8 channels' bias
+    }
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       const int lc = ks * 4 + g;                       // 8 channels: c0 + 8 lc .. +7
-      const int ch = c0 + lc * 8;
       // conv window: carried state (3 per channel, oldest first) then x_t
-      const bf16_t *csp = a.conv_state + ((int64_t)bsc * a.D + ch) * 3;
-      const uint4 s0 = *(const uint4 *)csp, s1 = *(const uint4 *)(csp + 8),
-                  s2 = *(const uint4 *)(csp + 16);
+      const uint4 s0 = cs_l[ks][0], s1 = cs_l[ks][1], s2 = cs_l[ks][2];
       const uint32_t sw[12] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w,
                                s2.x, s2.y, s2.z, s2.w};
-      const uint4 xv = *(const uint4 *)(a.xz + (int64_t)bsc * 2 * a.D + ch);
+      const uint4 xv = x_l[ks];
       const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
       float u[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const uint2 wr = *(const uint2 *)(a.conv_w + (int64_t)(ch + e) * 4);
-        float acc0 = a.conv_b ? bf2f(a.conv_b[ch + e]) : 0.f;
+        const uint2 wr = w_l[ks][e];
+        const uint32_t bw = e < 2 ? b_l[ks].x : e < 4 ? b_l[ks].y : e < 6 ? b_l[ks].z : b_l[ks].w;
+        float acc0 = a.conv_b ? ((e & 1) ? hi_bf(bw) : lo_bf(bw)) : 0.f;
         const int s = e * 3;  // bf16 index of channel e's first state value
         const float c0v = (s & 1) ? hi_bf(sw[s >> 1]) : lo_bf(sw[s >> 1]);
         const float c1v = ((s + 1) & 1) ? hi_bf(sw[(s + 1) >> 1]) : lo_bf(sw[(s + 1) >> 1]);
