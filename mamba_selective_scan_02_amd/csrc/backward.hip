@@ -608,13 +608,18 @@ __global__ __launch_bounds__(kST2, 4) void bw_scan_kernel(BwArgs a) {
 // dB | dC [T, 32] = sum over the channel groups of the scan's per-workgroup rows
 __global__ __launch_bounds__(256) void bw_rowsum_kernel(const float *part, float *out, int64_t T,
                                                         int ncg) {
+  // 4 consecutive values per thread (16-byte loads), each summed over the groups in order
   const int64_t e = blockIdx.x * 256ll + threadIdx.x;
-  if (e >= T * 32) return;
-  const int64_t tok = e >> 5;
-  const int c = (int)(e & 31);
-  float s = 0.f;
-  for (int g = 0; g < ncg; ++g) s += part[(tok * ncg + g) * 32 + c];
-  out[e] = s;
+  if (e >= T * 8) return;
+  const int64_t tok = e >> 3;
+  const int c = (int)(e & 7) * 4;
+  float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 8
+  for (int g = 0; g < ncg; ++g) {
+    const float4 v = *(const float4 *)(part + (tok * ncg + g) * 32 + c);
+    s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+  }
+  *(float4 *)(out + tok * 32 + c) = s;
 }
 
 // ---------------------------------------------------------------- column sums
@@ -964,7 +969,7 @@ hipError_t bw_dispatch(const BwArgs &a, int stage, hipStream_t s) {
       const unsigned grid = (unsigned)(a.B * a.nr * (a.D / kCG2));
       if (a.zoh) hipLaunchKernelGGL((bw_scan_kernel<T, true>), dim3(grid), dim3(kST2), 0, s, a);
       else hipLaunchKernelGGL((bw_scan_kernel<T, false>), dim3(grid), dim3(kST2), 0, s, a);
-      hipLaunchKernelGGL(bw_rowsum_kernel, dim3((unsigned)((a.T * 32 + 255) / 256)), dim3(256), 0, s,
+      hipLaunchKernelGGL(bw_rowsum_kernel, dim3((unsigned)((a.T * 8 + 255) / 256)), dim3(256), 0, s,
                          a.bc_part, a.dbc, a.T, a.D / kCG2);
       break;
     }
