@@ -624,15 +624,29 @@ __global__ __launch_bounds__(256) void bw_rowsum_kernel(const float *part, float
 
 // ---------------------------------------------------------------- column sums
 // part[blk][c] = sum of rows [blk * kColRows, +kColRows) of column c; then out[c] = sum_blk
+// V4: 4 consecutive columns per thread (cols % 4 == 0). Rows are added in order either way;
+// the unrolled loop lets the loads of 8 rows be in flight together.
+template <bool V4>
 __global__ __launch_bounds__(256) void bw_colsum_part_kernel(const float *in, int64_t rows,
                                                              int64_t cols, float *part) {
-  const int64_t c = blockIdx.x * 256ll + threadIdx.x;
+  const int64_t c = (blockIdx.x * 256ll + threadIdx.x) * (V4 ? 4 : 1);
   const int64_t blk = blockIdx.y;
   if (c >= cols) return;
   const int64_t r0 = blk * kColRows, r1 = min(rows, r0 + kColRows);
-  float s = 0.f;
-  for (int64_t rr = r0; rr < r1; ++rr) s += in[rr * cols + c];
-  part[blk * cols + c] = s;
+  if (V4) {
+    float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 8
+    for (int64_t rr = r0; rr < r1; ++rr) {
+      const float4 v = *(const float4 *)(in + rr * cols + c);
+      s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+    }
+    *(float4 *)(part + blk * cols + c) = s;
+  } else {
+    float s = 0.f;
+#pragma unroll 8
+    for (int64_t rr = r0; rr < r1; ++rr) s += in[rr * cols + c];
+    part[blk * cols + c] = s;
+  }
 }
 __global__ __launch_bounds__(256) void bw_colsum_final_kernel(const float *part, int64_t nblk,
                                                               int64_t cols, float *out) {
@@ -939,8 +953,14 @@ hipError_t launch_gemm_f32(const GemmF32Args &g0, hipStream_t s) {
 hipError_t launch_colsum(const float *in, int64_t rows, int64_t cols, float *part, float *out,
                          hipStream_t s) {
   const int64_t nblk = (rows + kColRows - 1) / kColRows;
-  hipLaunchKernelGGL(bw_colsum_part_kernel, dim3((unsigned)((cols + 255) / 256), (unsigned)nblk),
-                     dim3(256), 0, s, in, rows, cols, part);
+  if (cols % 4 == 0 && ((uintptr_t)in & 15) == 0 && ((uintptr_t)part & 15) == 0)
+    hipLaunchKernelGGL(bw_colsum_part_kernel<true>,
+                       dim3((unsigned)((cols / 4 + 255) / 256), (unsigned)nblk), dim3(256), 0, s,
+                       in, rows, cols, part);
+  else
+    hipLaunchKernelGGL(bw_colsum_part_kernel<false>,
+                       dim3((unsigned)((cols + 255) / 256), (unsigned)nblk), dim3(256), 0, s, in,
+                       rows, cols, part);
   hipLaunchKernelGGL(bw_colsum_final_kernel, dim3((unsigned)((cols + 255) / 256)), dim3(256), 0, s,
                      part, nblk, cols, out);
   return hipGetLastError();
