@@ -73,18 +73,25 @@ enum {
      instead of the first-order Bbar = dt * B (the default). */
   MM_FLAG_ZOH_B = 1u << 0,
   /* Scan kernel selection (results agree to fp32 rounding; at most one may be set).
-     Default: the time-parallel kernel when batch * d_inner / 64 < 2048 and seqlen > 128,
-     else the sequential one. With d_state 32 / 64 the time-parallel kernel runs once per
-     group of 16 states and "sequential" selects the general scan. */
-  MM_FLAG_SCAN_SEQUENTIAL = 1u << 1,  /* one lane per (sequence, channel), all 16 states */
-  MM_FLAG_SCAN_CHUNKED = 1u << 2      /* 128-token blocks, 8 segments composed in LDS */
+     Default: lanes over (channel, group of d_state / 8 states) when
+     batch * d_inner / 64 < 2048 and seqlen > 32, else one lane per (sequence, channel) for
+     d_state 16 and a general time-parallel scan (per-range transfers, carries, replay) for
+     the other state sizes. Both scan the sequence once, in time order. */
+  MM_FLAG_SCAN_SEQUENTIAL = 1u << 1,  /* one lane per (sequence, channel) / the general scan */
+  MM_FLAG_SCAN_CHUNKED = 1u << 2,     /* lanes over (channel, state group), 32-token blocks */
+  /* Evaluate every exp(dt A[i, n]) directly. Without it the lane kernel checks A on the
+     device and, where each lane's states are in arithmetic progression per channel
+     (A[i, n0 + k] = A[i, n0] + k delta_i, as for A = -(n + 1)), forms the decays of a lane
+     as exp(dt A[i, n0]) times powers of exp(dt delta_i): fewer exps, the same result to fp32
+     rounding. First-order Bbar only (ZOH always evaluates each exp). */
+  MM_FLAG_SCAN_GENERAL_A = 1u << 3
 };
 
 /*
  * Problem size. Limits of this build (else MM_ERR_UNSUPPORTED): d_state in {8, 16, 32, 64}
- * (16, the Jamba configuration, runs the tuned kernels; 32 and 64 the tuned time-parallel
- * scan once per group of 16 states where it applies, else a general time-parallel scan, as 8
- * does; the backward takes 16);
+ * (16, the Jamba configuration, runs the tuned projection kernels; every size runs the
+ * lane-per-state-group scan where it applies, else the scans named under the flags above;
+ * the backward takes 16);
  * 2 <= d_conv <= 4; d_inner % 64 == 0; with MM_BF16, dt_rank % 64 == 0 and
  * d_inner % 128 == 0; with MM_F32, 1 <= dt_rank <= 1024. seqlen >= 1 (prefill),
  * seqlen == 1 (decode). rms_eps > 0 is the RMSNorm epsilon.

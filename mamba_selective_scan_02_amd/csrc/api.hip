@@ -18,10 +18,9 @@ struct Workspace {
   bool fused_xproj;  // bf16: conv + x_proj + RMSNorm in one kernel (no u / xdbl buffers)
   bool tiled_dtproj; // bf16: token-stationary dt_proj kernel
   bool fast_decode;  // bf16 decode step: range-split x_proj, fused update (no u / xdbl buffers)
-  bool scan_tuned;   // d_state 8 / 32 / 64 on the time-parallel kernel of d_state 16
-  bool scan_groups;  // ... 32 / 64: one launch per 16 states
+  bool scan_tuned;   // d_state 8 / 32 / 64 on the lane-per-state-group scan kernel
   int dec_ranges, dec_range_ch;
-  size_t u, u_lo, xdbl, part, dtlow, dtlow_lo, bc, dt, yacc, gP, gS, total;
+  size_t u, u_lo, xdbl, part, dtlow, dtlow_lo, bc, dt, gP, gS, total;
 };
 
 // the scan-selection flags as ScanArgs::force (0 by size, 1 sequential / general, 2 chunked)
@@ -32,20 +31,18 @@ uint32_t scan_force(uint32_t flags) {
 // Byte offsets of the prefill intermediates for T = batch * seqlen tokens.
 //   fp32 mode: u [T,D] f32 | xdbl [T,R+2N] f32 | dt_low [T,R] f32 | B,C [T,2N] f32 | dt [T,D] f32
 //   bf16 mode: (u_hi, u_lo [T,D] bf16 | xdbl f32, unless fused) | dt_low hi, lo [T,R] bf16 |
-//              B,C [T,2N] f32 | dt [T,D] f16
+//              B,C [T,2N] f32 | dt [T,D] f32
 //   bf16 decode step: partial x_proj sums [ranges, B, R+2N] f32 replace u and xdbl.
-//   d_state 32 / 64 on the time-parallel scan: each 16-state group's part of y [T,D] f32; other d_state != 16
-//   (not on that kernel):
-//   the general scan's per-range transfers P, S [B, ranges, D, N] f32.
+//   d_state != 16 off the lane-per-state-group scan: the general scan's per-range transfers
+//   P, S [B, ranges, D, N] f32.
 Workspace layout(const mm_shape &s, bool decode) {
   const size_t T = (size_t)s.batch * s.seqlen;
   const bool bf = s.io_dtype == MM_BF16;
   const size_t e = esz(s.io_dtype);
   Workspace w;
-  // d_state 8 / 32 / 64 on the time-parallel kernel of d_state 16 (which recomputes u from x)
+  // d_state 8 / 32 / 64 on the lane-per-state-group kernel (which recomputes u from x)
   w.scan_tuned = !decode && scan_tuned_used(s.batch, s.seqlen, s.d_inner, s.d_state,
                                             scan_force(s.flags));
-  w.scan_groups = w.scan_tuned && s.d_state > 16;
   // one workgroup per 128 tokens: worth it once there are enough tokens to fill the chip; it
   // writes no u, so d_state != 16 takes it only where the scan recomputes u
   w.fused_xproj = !decode && bf && T >= 32768 &&
@@ -72,10 +69,8 @@ Workspace layout(const mm_shape &s, bool decode) {
   w.dtlow = o; o += up(T * s.dt_rank * e);
   w.dtlow_lo = o; if (bf) o += up(T * s.dt_rank * 2);
   w.bc = o; o += up(T * 2 * s.d_state * 4);
-  w.dt = o; o += up(T * s.d_inner * (bf ? 2 : 4));
-  // d_state 32 / 64 on the time-parallel kernel: y's partial sums between the state groups;
-  // other d_state != 16: per-range transfers of the general scan
-  w.yacc = o; if (w.scan_groups) o += up(T * s.d_inner * 4 * (size_t)(s.d_state / 16));
+  w.dt = o; o += up(T * s.d_inner * 4);
+  // d_state != 16 off the lane kernel: per-range transfers of the general scan
   const size_t gsz = s.d_state != 16 && !w.scan_tuned
                          ? (size_t)s.batch * scan_n_ranges(s.seqlen) * s.d_inner * s.d_state * 4 : 0;
   w.gP = o; o += up(gsz);
@@ -92,7 +87,8 @@ mm_status check_shape(const mm_shape *s, bool decode) {
       s->dt_rank <= 0 || !(s->rms_eps > 0.0f))
     return MM_ERR_INVALID_ARG;
   if (s->io_dtype != MM_F32 && s->io_dtype != MM_BF16) return MM_ERR_INVALID_ARG;
-  if (s->flags & ~(uint32_t)(MM_FLAG_ZOH_B | MM_FLAG_SCAN_SEQUENTIAL | MM_FLAG_SCAN_CHUNKED))
+  if (s->flags & ~(uint32_t)(MM_FLAG_ZOH_B | MM_FLAG_SCAN_SEQUENTIAL | MM_FLAG_SCAN_CHUNKED |
+                             MM_FLAG_SCAN_GENERAL_A))
     return MM_ERR_INVALID_ARG;
   if ((s->flags & MM_FLAG_SCAN_SEQUENTIAL) && (s->flags & MM_FLAG_SCAN_CHUNKED))
     return MM_ERR_INVALID_ARG;
@@ -175,7 +171,7 @@ mm_status run_decode_fast(const mm_shape *s, const mm_params *p, const Workspace
   float *part = (float *)(ws + w.part);
   uint16_t *dtlow = (uint16_t *)(ws + w.dtlow), *dtlow_lo = (uint16_t *)(ws + w.dtlow_lo);
   float *bc = (float *)(ws + w.bc);
-  _Float16 *delta = (_Float16 *)(ws + w.dt);
+  float *delta = (float *)(ws + w.dt);
   const uint16_t *cw = (const uint16_t *)p->conv_w, *cb = (const uint16_t *)p->conv_b;
   {
     StageScope sc(timer, st, MM_STAGE_XPROJ);
@@ -224,7 +220,7 @@ mm_status run_mixer(const mm_shape *s, const mm_params *p, const void *xz, void 
   void *dtlow = ws + w.dtlow;
   void *dtlow_lo = ws + w.dtlow_lo;
   float *bc = (float *)(ws + w.bc);
-  void *delta = ws + w.dt;
+  float *delta = (float *)(ws + w.dt);
   (void)workspace_bytes;
   const int conv_valid = states_valid && conv_state != nullptr;
 
@@ -255,7 +251,7 @@ mm_status run_mixer(const mm_shape *s, const mm_params *p, const void *xz, void 
     StageScope sc(timer, st, MM_STAGE_DTPROJ);
     if (w.tiled_dtproj) {
       DtprojArgs da{(const uint16_t *)dtlow, (const uint16_t *)dtlow_lo,
-                    (const uint16_t *)p->dt_proj_w, p->dt_proj_b, (_Float16 *)delta, T, D, R};
+                    (const uint16_t *)p->dt_proj_w, p->dt_proj_b, delta, T, D, R};
       MM_TRY(launch_dtproj_tiled(da, st));
     } else {
       MM_TRY(launch_dtproj(dt, dtlow, dtlow_lo, p->dt_proj_w, p->dt_proj_b, delta, T, D, R, st));
@@ -266,11 +262,9 @@ mm_status run_mixer(const mm_shape *s, const mm_params *p, const void *xz, void 
     ScanArgs sa{xz, p->conv_w, p->conv_b, conv_state, conv_valid, K, delta, bc, p->A, p->Dskip,
                 y, ssm_state, states_valid && ssm_state != nullptr,
                 (s->flags & MM_FLAG_ZOH_B) ? 1 : 0,
-                (int)scan_force(s->flags), B, L, D, N};
-    if (N == 16 || (w.scan_tuned && !w.scan_groups)) {
-      MM_TRY(launch_scan(dt, sa, st));
-    } else if (w.scan_groups) {
-      sa.yacc = (float *)(ws + w.yacc);
+                (int)scan_force(s->flags), (s->flags & MM_FLAG_SCAN_GENERAL_A) ? 1 : 0,
+                B, L, D, N};
+    if (N == 16 || w.scan_tuned) {
       MM_TRY(launch_scan(dt, sa, st));
     } else {
       sa.u = u;

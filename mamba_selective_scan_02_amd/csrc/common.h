@@ -56,8 +56,10 @@ __device__ __forceinline__ float expm1_f(float x) {
   return x * r;
 }
 // softplus(v) = log(1 + e^v) from the hardware exp2 / log2: above 20 it equals v to within
-// 2e-9 relative; otherwise e = e^v, w = 1 + e (rounded) and log(1 + e) = log(w) * e / (w - 1),
-// which cancels the rounding of w to first order (and is e itself when w rounds to 1).
+// 2e-9 relative; otherwise e = e^v, w = 1 + e (rounded) and log(1 + e) = log(w) * e / (w - 1)
+// (Goldberg's log1p method, "What every computer scientist should know about floating-point
+// arithmetic", 1991), which cancels the rounding of w to first order (and is e itself when w
+// rounds to 1).
 __device__ __forceinline__ float softplus_f(float v) {
   if (v > 20.0f) return v;
   const float e = exp2_hw(v * kLog2e);

@@ -232,7 +232,7 @@ __global__ __launch_bounds__(256) void decode_update_kernel(DecodeUpdateArgs a) 
   float4 h[U], Av[U];
   float Bq[U][4], Cq[U][4];
   uint32_t cs16[U], p16[U];
-  float Dv[U];
+  float Dv[U], dtv[U];
   uint2 wr[U];
 #pragma unroll
   for (int j = 0; j < U; ++j) {
@@ -254,15 +254,15 @@ __global__ __launch_bounds__(256) void decode_update_kernel(DecodeUpdateArgs a) 
       Bq[j][s] = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((4 * q + s) * 4, __builtin_bit_cast(int, bcl)));
       Cq[j][s] = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((16 + 4 * q + s) * 4, __builtin_bit_cast(int, bcl)));
     }
-    // lane q of the channel loads conv state element min(q, 2); then x | z | dt | bias by q
+    // lane q of the channel loads conv state element min(q, 2); then x | z | - | bias by q
     cs16[j] = a.conv_state[gch * 3 + (q < 3 ? q : 2)];
     const bf16_t *xrow = a.xz + (int64_t)b * 2 * a.D;
     const uint16_t *src = q == 0 ? xrow + i
-                        : q == 1 ? xrow + a.D + i
-                        : q == 2 ? (const uint16_t *)a.dt + gch
+                        : q == 1 || q == 2 ? xrow + a.D + i
                         : (a.conv_b ? a.conv_b + i : xrow + i);
     p16[j] = *src;
     if (q == 3 && !a.conv_b) p16[j] = 0;
+    dtv[j] = a.dt[gch];   // fp32 dt (the channel's 4 lanes read the same word)
     wr[j] = *(const uint2 *)(a.conv_w + (int64_t)i * 4);
     Dv[j] = a.Dskip[i];
   }
@@ -275,9 +275,8 @@ __global__ __launch_bounds__(256) void decode_update_kernel(DecodeUpdateArgs a) 
     const float c2 = bf2f((bf16_t)__builtin_amdgcn_mov_dpp(cs, 0xAA, 0xF, 0xF, false));
     const float xv = bf2f((bf16_t)__builtin_amdgcn_mov_dpp(pv, 0x00, 0xF, 0xF, false));
     const float zv = bf2f((bf16_t)__builtin_amdgcn_mov_dpp(pv, 0x55, 0xF, 0xF, false));
-    const uint16_t dth = (uint16_t)__builtin_amdgcn_mov_dpp(pv, 0xAA, 0xF, 0xF, false);
     const float bias = bf2f((bf16_t)__builtin_amdgcn_mov_dpp(pv, 0xFF, 0xF, 0xF, false));
-    const float dt = (float)__builtin_bit_cast(_Float16, dth);
+    const float dt = dtv[j];
     float acc = bias;
     acc = __builtin_fmaf(lo_bf(wr[j].x), c0, acc);
     acc = __builtin_fmaf(hi_bf(wr[j].x), c1, acc);

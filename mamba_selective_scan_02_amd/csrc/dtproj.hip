@@ -1,6 +1,6 @@
 // dt_proj + bias + softplus for bf16 I/O on split-precision bf16 MFMA.
 //
-//   dt[t, i] = softplus(W_dt[i, :] . dt_low[t, :] + b_i)        (stored as fp16)
+//   dt[t, i] = softplus(W_dt[i, :] . dt_low[t, :] + b_i)        (stored as fp32)
 //
 // Jamba analysis page, "The selective mechanism": Delta is a function of the token through a
 // small learned linear layer ("From scalar SSM to vector processing": one Delta per channel).
@@ -12,7 +12,7 @@
 // dt_rank) into VGPRs once, then streams the workgroup's channel range through LDS in chunks
 // of 64 W_dt rows (direct-to-LDS loads, double-buffered, 16-byte slots XOR-swizzled so the
 // 16-row fragment reads are bank-conflict free). Per chunk a wave issues
-// (64/16) x (dt_rank/32) x 2 MFMAs and writes 16 tokens x 64 channels of fp16 dt.
+// (64/16) x (dt_rank/32) x 2 MFMAs and writes 16 tokens x 64 channels of fp32 dt.
 #include "common.h"
 #include "kernels.h"
 
@@ -37,23 +37,17 @@ __device__ __forceinline__ int swz(int r, int c) {
   return c ^ (r & 15);
 }
 
-// softplus for fp16 storage: log(1 + e) from the hardware log2 when e = exp(v) is not tiny,
-// else e - e^2/2 (the rounding of 1 + e would dominate there); v itself above 15. Both forms
-// are computed and selected bitwise, so the compiler emits selects rather than divergent
-// branches around the log.
-__device__ __forceinline__ float softplus_h(float v) {
+// softplus(v) = log(1 + e^v) in fp32, the form of softplus_f (common.h) with every case
+// computed and selected (selects, not divergent branches around the log): e = e^v,
+// w = 1 + e, log(w) e / (w - 1) (Goldberg's log1p method), e itself where w rounds to 1, and v
+// above 20 (within 2e-9 relative there).
+__device__ __forceinline__ float softplus_sel(float v) {
   const float e = exp2_hw(v * kLog2e);
-  const float l = __builtin_amdgcn_logf(1.0f + e) * 0.69314718055994531f;
-  const float sm = __builtin_fmaf(-0.5f * e, e, e);
-  const uint32_t small = 0u - (uint32_t)(e < 9.765625e-4f);
-  const uint32_t big = 0u - (uint32_t)(v > 15.0f);
-  const uint32_t r = (__float_as_uint(sm) & small) | (__float_as_uint(l) & ~small);
-  return __uint_as_float((__float_as_uint(v) & big) | (r & ~big));
-}
-
-__device__ __forceinline__ uint32_t pack_h2(float a, float b) {
-  const _Float16 ha = (_Float16)fminf(a, 65504.0f), hb = (_Float16)fminf(b, 65504.0f);
-  return (uint32_t)__builtin_bit_cast(uint16_t, ha) | ((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16);
+  const float w = 1.0f + e;
+  const float d = w - 1.0f;
+  const float l = __builtin_amdgcn_logf(w) * 0.69314718055994531f * (e * __builtin_amdgcn_rcpf(d));
+  const float r = d == 0.0f ? e : l;
+  return v > 20.0f ? v : r;
 }
 
 template <int R>
@@ -95,12 +89,12 @@ __global__ __launch_bounds__(512) void dtproj_kernel(DtprojArgs a, int ch_per_wg
 
   // Outputs of chunk ck are stored at the start of chunk ck+1, after that chunk's wait, so
   // the wait for the staged W_dt rows never has to cover freshly issued stores.
-  uint2 pend[4];
+  float4 pend[4];
   int pend_c = -1;
-  _Float16 *drow = a.dt + (int64_t)tokc * a.D + 4 * g;   // this lane's outputs: + channel
+  float *drow = a.dt + (int64_t)tokc * a.D + 4 * g;   // this lane's outputs: + channel
   auto flush = [&]() {
     if (pend_c >= 0 && tok < a.T) {
-      uint2 *p = (uint2 *)(drow + pend_c);
+      float4 *p = (float4 *)(drow + pend_c);
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb) p[4 * nb] = pend[nb];   // channels + 16 nb
     }
@@ -132,8 +126,8 @@ __global__ __launch_bounds__(512) void dtproj_kernel(DtprojArgs a, int ch_per_wg
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
       const float4 bv = *(const float4 *)(bcur + nb * 16 + 4 * g);
-      pend[nb].x = pack_h2(softplus_h(acc[nb][0] + bv.x), softplus_h(acc[nb][1] + bv.y));
-      pend[nb].y = pack_h2(softplus_h(acc[nb][2] + bv.z), softplus_h(acc[nb][3] + bv.w));
+      pend[nb] = make_float4(softplus_sel(acc[nb][0] + bv.x), softplus_sel(acc[nb][1] + bv.y),
+                             softplus_sel(acc[nb][2] + bv.z), softplus_sel(acc[nb][3] + bv.w));
     }
     pend_c = c0;
   };

@@ -1,7 +1,7 @@
 // The mixer's two dense contractions on bf16 MFMA (fp32 accumulate), and a plain fp32 path.
 //
 //   x_proj:  xdbl[T, R+2N] = u[T, D] . W_x[R+2N, D]^T           (fp32 out)
-//   dt_proj: dt[T, D]      = softplus(dt_low[T, R] . W_dt[D, R]^T + b)   (fp32, or fp16 in bf16 mode)
+//   dt_proj: dt[T, D]      = softplus(dt_low[T, R] . W_dt[D, R]^T + b)   (fp32)
 //
 // Jamba analysis page, "The Mamba Layer", "The selective mechanism": B, C and Delta are
 // functions of the token through small learned linear layers. Both products are "NT":
@@ -14,7 +14,7 @@
 //
 // MFMA mapping (v_mfma_f32_16x16x32_bf16, lane layout checked on gfx950): the weight
 // tile is the MFMA's first operand and the token tile its second, so each lane ends with
-// 4 consecutive output columns of one token row -> 16-byte (fp32) or 8-byte (fp16) stores.
+// 4 consecutive output columns of one token row -> 16-byte stores.
 // A 256-thread workgroup computes a BM x BN tile as 2 x 2 waves; K advances in steps of 64
 // through padded LDS tiles with the next step's global loads issued before the MFMAs.
 #include "common.h"
@@ -38,23 +38,15 @@ struct EpiXproj {
   }
 };
 
-// dt is stored as fp16 (relative step 2^-11, 4x finer than bf16); values above fp16's
-// largest finite value are clamped to it.
-struct EpiDtprojF16 {
-  _Float16 *out;
+struct EpiDtprojF32 {
+  float *out;
   const float *bias;
   int ldo;
-  static __device__ __forceinline__ uint32_t pack_h2(float a, float b) {
-    const _Float16 ha = (_Float16)fminf(a, 65504.0f), hb = (_Float16)fminf(b, 65504.0f);
-    return (uint32_t)__builtin_bit_cast(uint16_t, ha) |
-           ((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16);
-  }
   __device__ __forceinline__ void operator()(int m, int n, const f32x4 &v) const {
     const float4 b = *(const float4 *)(bias + n);
-    uint2 r;
-    r.x = pack_h2(softplus_f(v[0] + b.x), softplus_f(v[1] + b.y));
-    r.y = pack_h2(softplus_f(v[2] + b.z), softplus_f(v[3] + b.w));
-    *(uint2 *)(out + (int64_t)m * ldo + n) = r;
+    *(float4 *)(out + (int64_t)m * ldo + n) =
+        make_float4(softplus_f(v[0] + b.x), softplus_f(v[1] + b.y), softplus_f(v[2] + b.z),
+                    softplus_f(v[3] + b.w));
   }
 };
 
@@ -222,8 +214,8 @@ hipError_t launch_dtproj(mm_dtype dt, const void *dtlow, const void *dtlow_lo, c
     return f32_launch((const float *)dtlow, (const float *)w, T, D, R, 1, bias, (float *)dtout, s);
   constexpr int BM = 128, BN = 128;
   const int tiles = ((T + BM - 1) / BM) * ((D + BN - 1) / BN);
-  EpiDtprojF16 e{(_Float16 *)dtout, bias, D};
-  hipLaunchKernelGGL((gemm_nt_bf16_kernel<BM, BN, EpiDtprojF16>), dim3(tiles), dim3(256), 0, s,
+  EpiDtprojF32 e{(float *)dtout, bias, D};
+  hipLaunchKernelGGL((gemm_nt_bf16_kernel<BM, BN, EpiDtprojF32>), dim3(tiles), dim3(256), 0, s,
                      (const bf16_t *)dtlow, (const bf16_t *)dtlow_lo, (const bf16_t *)w, T, D, R, e);
   return hipGetLastError();
 }

@@ -32,7 +32,7 @@ hipError_t launch_norm(mm_dtype dt, const float *xdbl, void *dtlow, void *dtlow_
                        const float *g_dt, const float *g_B, const float *g_C, int T, int R, int N,
                        float eps, hipStream_t s);
 
-// dt[T, D] = softplus(dtlow[T, R] . Wdt[D, R]^T + bias); fp32 out (fp32 mode) or fp16 out
+// dt[T, D] = softplus(dtlow[T, R] . Wdt[D, R]^T + bias); fp32 out
 // (bf16 mode, where dtlow = hi + lo takes two MFMA passes).
 hipError_t launch_dtproj(mm_dtype dt, const void *dtlow, const void *dtlow_lo, const void *w,
                          const float *bias, void *dtout, int T, int D, int R, hipStream_t s);
@@ -55,12 +55,12 @@ struct XprojFusedArgs {
 bool xproj_fused_supported(int R, int N, int D, int K);
 hipError_t launch_xproj_fused(const XprojFusedArgs &a, hipStream_t s);
 
-// bf16 I/O dt_proj: dt[T, D] (fp16) = softplus((dtlow + dtlow_lo)[T, R] . Wdt[D, R]^T + bias)
+// bf16 I/O dt_proj: dt[T, D] (fp32) = softplus((dtlow + dtlow_lo)[T, R] . Wdt[D, R]^T + bias)
 struct DtprojArgs {
   const uint16_t *dtlow, *dtlow_lo;  // [T, R] bf16
   const uint16_t *w;                 // [D, R] bf16
   const float *bias;                 // [D]
-  _Float16 *dt;                      // [T, D]
+  float *dt;                         // [T, D]
   int T, D, R;
 };
 bool dtproj_supported(int R, int D);
@@ -91,7 +91,7 @@ struct DecodeUpdateArgs {
   const uint16_t *xz;          // [B, 2D]
   const uint16_t *conv_w, *conv_b;
   uint16_t *conv_state;        // [B, D, 3] in/out
-  const _Float16 *dt;          // [B, D]
+  const float *dt;             // [B, D]
   const float *bc;             // [B, 32]
   const float *A, *Dskip;
   float *state;                // [B, D, 16] in/out
@@ -211,7 +211,7 @@ struct ScanArgs {
   const void *conv_state;  // [B, D, K-1] io dtype or null (read before it is updated)
   int conv_valid;
   int K;
-  const void *delta;    // [B, L, D]: fp32 (fp32 mode) or fp16 (bf16 mode)
+  const float *delta;   // [B, L, D] fp32
   const float *bc;      // [B*L, 2N]: B then C per token
   const float *A;       // [D, N]
   const float *Dskip;   // [D]
@@ -219,19 +219,16 @@ struct ScanArgs {
   float *state;         // [B, D, N] or null
   int state_valid;
   int zoh;
-  int force;            // 0: pick by size; 1: sequential kernel; 2: time-parallel kernel
+  int force;            // 0: pick by size; 1: one lane per channel (d_state 16) or the general
+                        // time-parallel scan; 2: lanes over (channel, state group)
+  int general_a;        // 1: evaluate every exp(dt A) directly (no paired-decay shortcut)
   int B, L, D, N;
   // d_state != 16 (scan_n.hip): u from the conv kernel (fp32, or bf16 high + low parts) and
   // the per-range transfers [B, ranges, D, N] (P, and S / the range start states)
   const void *u = nullptr, *u_lo = nullptr;
   float *gP = nullptr, *gS = nullptr;
-  // d_state 32 / 64 on the time-parallel kernel (scan.hip): one launch per 16-state group
-  // (first state g0), each writing its part of y as fp32 [B, L, D] to yacc + g B L D, then a
-  // combine kernel
-  float *yacc = nullptr;
-  int g0 = 0;
 };
-// N = 16; N = 8, 32, 64 when scan_tuned_used (32 / 64 then need a.yacc)
+// N = 16; N = 8, 32, 64 when scan_tuned_used
 hipError_t launch_scan(mm_dtype dt, const ScanArgs &a, hipStream_t s);
 bool scan_tuned_used(int B, int L, int D, int N, uint32_t force);
 bool scan_n_supported(int N);

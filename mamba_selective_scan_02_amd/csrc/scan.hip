@@ -7,12 +7,17 @@
 // SSM equation). Bbar = dt B by default, or the page's ZOH form expm1(dt A)/A B with
 // MM_FLAG_ZOH_B. Gate: y <- y * SiLU(z) (Mamba-1 block).
 //
-// The SSM input u = SiLU(conv1d(x) + b) is recomputed here in fp32 from x (4 taps per
-// token, a sliding window in registers) instead of being read back rounded, so the scan
-// sees u at full precision while reading no more bytes (x instead of u).
+// The SSM input u = SiLU(conv1d(x) + b) is recomputed here in fp32 from x (K taps per token)
+// instead of being read back rounded, so the scan sees u at full precision while reading no
+// more bytes (x instead of u). dt is read in fp32.
 //
-// Sequential kernel: one lane per (sequence, channel), all N = 16 states in VGPRs, B_t / C_t
-// wave-uniform. Exactly one exp per (token, channel, state).
+// Two kernels, both one pass over the sequence in time order with exactly one exp per
+// (token, channel, state), as in the recurrence itself:
+//  * scan_seq_kernel: one lane per (sequence, channel), all N = 16 states in VGPRs, B_t / C_t
+//    wave-uniform. For many sequences (>= 2048 waves of 64 channels).
+//  * scan_lanes_kernel: lanes over (channel, group of states), for few sequences at long L
+//    (batch 1 of 8192 channels has only 131072 (channel, state) chains: exactly two per lane
+//    of the chip at one wave per SIMD, one per lane at two). See the comment above it.
 #include "common.h"
 #include "kernels.h"
 
@@ -21,19 +26,8 @@ namespace {
 
 constexpr int kN = 16;
 
-template <typename T> struct Delta;       // storage type of dt for each I/O dtype
-template <> struct Delta<float> {
-  typedef float type;
-  static __device__ __forceinline__ float ld(const float *p) { return *p; }
-};
-template <> struct Delta<bf16_t> {
-  typedef _Float16 type;
-  static __device__ __forceinline__ float ld(const _Float16 *p) { return (float)*p; }
-};
-
 template <typename T, bool ZOH, int K>
 __global__ __launch_bounds__(64) void scan_seq_kernel(ScanArgs a) {
-  typedef typename Delta<T>::type DT;
   const int64_t gi = (int64_t)blockIdx.x * 64 + threadIdx.x;  // b * D + i
   const int i = (int)(gi % a.D);
   const int b = (int)(gi / a.D);
@@ -58,7 +52,7 @@ __global__ __launch_bounds__(64) void scan_seq_kernel(ScanArgs a) {
   const int64_t row = 2LL * a.D;
   const T *xp = (const T *)a.xz + (int64_t)b * a.L * row + i;
   const T *zp = xp + a.D;
-  const DT *dp = (const DT *)a.delta + (int64_t)b * a.L * a.D + i;
+  const float *dp = a.delta + (int64_t)b * a.L * a.D + i;
   T *yp = (T *)a.y + (int64_t)b * a.L * a.D + i;
   const float *bcp = a.bc + (int64_t)b * a.L * 2 * kN;
   for (int t = 0; t < a.L; ++t) {
@@ -71,7 +65,7 @@ __global__ __launch_bounds__(64) void scan_seq_kernel(ScanArgs a) {
     for (int j = 0; j + 1 < K - 1; ++j) win[j] = win[j + 1];
     win[K - 2] = x;
     const float u = silu_f(acc);
-    const float dt = Delta<T>::ld(dp + (int64_t)t * a.D);
+    const float dt = dp[(int64_t)t * a.D];
     const float z = io<T>::ld(zp + (int64_t)t * row);
     const float *Bt = bcp + (int64_t)t * 2 * kN;
     const float *Ct = Bt + kN;
@@ -103,423 +97,376 @@ __global__ __launch_bounds__(64) void scan_seq_kernel(ScanArgs a) {
 }
 
 // ---------------------------------------------------------------------------------------
-// Time-parallel scan for long sequences (few sequences x channels to fill 256 CUs).
+// scan_lanes_kernel: one pass in time order, lanes over (channel, state group).
 //
-// A workgroup owns kCh = 32 channels of one sequence and walks the sequence in blocks of
-// kW * kS = 128 tokens; wave w owns the 16-token segment w of every block, and everything but
-// the carry composition stays inside the wave (its own LDS rows, no workgroup barrier):
-//  0. The segment's B|C rows, its x rows (with the 3 conv-window rows before it), z and dt
-//     rows were loaded into the wave's LDS rows with direct-to-LDS 16-byte loads while the
-//     previous block was computed.
-//  1. Prep: lane l takes channel l/2 and tokens 8*(l%2) .. +7 of the segment: u = SiLU(conv1d(x)
-//     + b), dt, dt*u, D*u and SiLU(z), once per (token, channel), into the wave's LDS rows.
-//  2. Local pass: lane l works on channel l/2 and states 8*(l%2) .. +7. The segment is scanned
-//     from h = 0, keeping exp(dt*A) of every (token, state) in VGPRs (one exp per element, as
-//     in the sequential recurrence).
-//  3. Compose: the segment's transfer h -> P h + S (P = exp(A * sum dt), S = the local end
-//     state) goes to LDS. Thread i then owns one (channel, state) chain: it applies the 8
-//     transfers in order to the block's carry-in with the page's associative operator
-//     ("Parallel training via the parallel scan": (a, b) then (c, d) gives (ac, ad + b) for
-//     h -> a h + b), writing each segment's h_in over that segment's P, and keeps the result
-//     as the next block's carry-in. These are the block's only two workgroup barriers.
-//  4. Replay from the true h_in with the stored exp(dt*A); y_t = C_t . h_t; the two half-sums
-//     of a channel meet by a DPP lane swap; y = (y_ssm + D u) * SiLU(z) goes out as bf16/f32.
-constexpr int kCh = 32, kW = 8, kS = 16, kG = 8, kBlk = kW * kS;
-constexpr int kHalo = 3;                  // x rows before the segment (conv window, K - 1 <= 3)
-constexpr int kXSeg = kS + 4;             // staged x rows per segment: halo + segment, padded
+// A workgroup owns kLC = 32 channels of one sequence and all N of their states: W waves of 64
+// lanes, lane (c = lane % 32, half = lane / 32) of wave w holding the S = N / (2 W) consecutive
+// states [S (2 w + half), +S) of channel c in VGPRs (d_state 16: W = 8 waves of one state per
+// lane). At batch 1 and d_inner 8192 that is 256 workgroups, one per CU, two waves per SIMD
+// (131072 (channel, state) chains: two per lane of the chip), and no time-parallel split: no
+// second pass, no carry composition. The sequence is walked in blocks of kLT = 32 tokens, with
+// one workgroup barrier per block and three phases in flight:
+//   P(j + 1)  prep: thread (channel pair c2, token group g) forms u = SiLU(conv1d(x) + b) in
+//             fp32 (the K - 1 rows before the block come from a halo kept in LDS, never
+//             re-read), dt, dt*u (u for ZOH), D*u and SiLU(z) once per (token, channel);
+//   S(j)      scan: per token each lane reads (dt, dt*u) of its channel and B_t, C_t of its
+//             states from LDS (broadcast reads, one token ahead of use), updates its states
+//             and forms C . h over them; the two halves of a wave (the same channel, other
+//             states) are added by one v_permlane32_swap per token pair, and each wave's
+//             partial sum goes to LDS;
+//   Y(j - 1)  output: the prep thread adds the W waves' partial sums in a fixed order, applies
+//             D u and the gate, and stores two channels (4 bytes) per token.
+// x, z and dt rows of block j + 2 and the B|C rows of block j + 1 are loaded by direct-to-LDS
+// 16-byte loads while block j is scanned.
+//
+// Paired decay (S >= 2, d_state 32 / 64): when every lane's states have
+// A[i, n0 + k] = A[i, n0] + k delta_i (checked in the kernel; the configs' A = -(n + 1) has
+// delta = -1), exp(dt A[i, n0 + k]) is formed as exp(dt A[i, n0]) exp(dt delta_i)^k with
+// exp(dt delta_i) computed once per (token, channel) in the prep: one exp per lane and token
+// instead of S. ScanArgs::general_a turns the check off (every exp(dt A) evaluated directly);
+// ZOH always evaluates them directly.
+constexpr int kLC = 32, kLT = 32;
 
-// One direct-to-LDS 16-byte load per lane: lane i of the wave fills bytes [16 i, 16 i + 16)
-// of the window at `lds` (wave-uniform). Issued opaquely (see dma16_opaque): the block loop
-// waits for it explicitly.
-__device__ __forceinline__ void load_lds16(const void *src, void *lds) {
-  dma16_opaque(src, lds_addr(lds));
+// waves per workgroup: 8 (two per SIMD), or N / 2 below that; fp32 I/O at d_state 64 takes 4
+// (its staged fp32 rows would not fit 160 KB of LDS beside 8 waves' partial sums)
+template <typename T, int N>
+constexpr int lane_waves() {
+  return (N == 64 && sizeof(T) == 4) ? 4 : (N / 2 < 8 ? N / 2 : 8);
 }
 
-// MODE 0: d_state 16.
-// MODE 1 / 3 (GRP): the kernel covers one group of 16 states [g0, g0 + 16) of a d_state = N > 16
-// problem (A, B|C rows and the SSM state have stride N) and stores the group's part of
-// C_t . h_t in fp32 to a.yacc [B, L, D] (one buffer per group; MODE 3, the first group, adds
-// D u to its part); scan_combine_kernel then adds the groups' parts and applies the gate.
-// MODE 2 (d_state 8): the lanes of state half p = 0 carry the 8 states; the p = 1 lanes run on
-// zero input (h stays 0, A = -1, B|C slots refilled with the real rows, never used) and own no
-// state, so y and the gate are those of d_state 16 with the half's terms equal to zero.
-template <typename T, bool ZOH, int K, int MODE>
-__global__ __launch_bounds__(kW * 64) void scan_chunked_kernel(ScanArgs a) {
-  typedef typename Delta<T>::type DT;
-  constexpr bool GRP = MODE == 1 || MODE == 3, HALF = MODE == 2, GFIRST = MODE == 3;
-  const int NS = GRP ? a.N : HALF ? kG : kN;   // state stride
-  const int g0 = GRP ? a.g0 : 0;               // first state of this launch
-  constexpr int xper = 16 / sizeof(T);                 // x/z elements per 16-byte chunk
-  constexpr int xrow_chunks = kCh * sizeof(T) / 16;    // 16-byte chunks per staged x/z row
-  constexpr int drow_chunks = kCh * sizeof(DT) / 16;
-  // bf16 I/O stages x, z and dt through LDS too; fp32 I/O (small problems) reads them from
-  // global memory in the prep phase, which keeps its LDS within 160 KB.
-  constexpr bool kStageXZD = sizeof(T) == 2;
-  constexpr int kXR = kStageXZD ? kXSeg : 1, kZR = kStageXZD ? kS : 1;
-  // per-wave staging (written by async loads); B|C double-buffered in two arrays so that the
-  // compiler can tell the prefetch target from the tile being read
-  __shared__ __attribute__((aligned(16))) float bc_s0[kW][kS][2 * kN];
-  __shared__ __attribute__((aligned(16))) float bc_s1[kW][kS][2 * kN];
-  __shared__ __attribute__((aligned(16))) T x_s[kW][kXR][kCh];
-  __shared__ __attribute__((aligned(16))) T z_s[kW][kZR][kCh];
-  __shared__ __attribute__((aligned(16))) DT d_s[kW][kZR][kCh];
-  // prep outputs: (dt, dt*u) and (D*u, SiLU(z)) per (token, channel) of each wave's segment;
-  // rows padded by one element so that rows 8 apart fall in different LDS banks
-  __shared__ __attribute__((aligned(16))) float2 pd_s[kW][kS][kCh + 1];
-  __shared__ __attribute__((aligned(16))) float2 eg_s[kW][kS][kCh + 1];
-  // segment transfers, lane-contiguous 16-byte slots: [wave][P0..3, P4..7, S0..3, S4..7][lane]
-  __shared__ __attribute__((aligned(16))) float4 agg_s[kW][4][64];
+template <typename T, int N>
+struct LaneSmem {
+  static constexpr int W = lane_waves<T, N>(), S = N / (2 * W);
+  T xs[2][kLT][kLC];             // staged x rows (blocks j + 1, j + 2)
+  T zs[2][kLT][kLC];             // staged z rows
+  float ds[2][kLT][kLC];         // staged dt rows
+  float bcs[2][kLT][2 * N];      // staged B | C rows (blocks j, j + 1)
+  float halo[2][3][kLC];         // the 3 x rows before a block, as fp32
+  float2 pd[2][kLT][kLC];        // (dt, dt*u or u) per (token, channel)
+  float pe[S >= 2 ? 2 : 1][kLT][S >= 2 ? kLC : 1];   // exp(dt delta) (paired decay)
+  float2 eg[2][kLT][kLC];        // (D*u, SiLU(z))
+  float yp[2][W][kLT][kLC];      // each wave's partial C . h
+};
 
-  const int groups = a.D / kCh;
-  const int gid = xcd_remap(blockIdx.x, gridDim.x);
-  const int b = gid / groups;
-  const int ch0 = (gid % groups) * kCh;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wv = tid >> 6;
-  const int c = lane >> 1, p = lane & 1;
+template <typename T, bool ZOH, int K, int N, bool PAIRED>
+__device__ __forceinline__ void lanes_body(const ScanArgs &a, LaneSmem<T, N> &sm, int b,
+                                           int ch0) {
+  constexpr int W = LaneSmem<T, N>::W, S = LaneSmem<T, N>::S;
+  constexpr int TPT = kLT * 16 / (64 * W);     // tokens per prep / output thread (1 or 2)
+  static_assert(!PAIRED || S >= 2, "paired decay needs two states per lane");
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  // scan roles
+  const int c = lane & 31, half = lane >> 5, n0 = (2 * wv + half) * S;
   const int ch = ch0 + c;
-
-  float A2[kG], Av[kG], iA[kG];
-#pragma unroll
-  for (int j = 0; j < kG; ++j) {
-    Av[j] = HALF && p ? -1.0f : a.A[(int64_t)ch * NS + g0 + kG * p + j];
-    A2[j] = Av[j] * kLog2e;
-    iA[j] = 1.0f / Av[j];
-  }
-  // chain thread tid <-> publishing lane ql = (tid >> 2) & 63 (channel ql/2, state half ql&1),
-  // state j = 4 (tid >> 8) + (tid & 3) of that half: its P of segment w is float w*1024 + tid
-  // of agg_s, its S float w*1024 + 512 + tid (conflict-free, lane-contiguous)
-  const int ql = (tid >> 2) & 63, qj = 4 * (tid >> 8) + (tid & 3);
-  const int64_t qidx = ((int64_t)b * a.D + ch0 + (ql >> 1)) * NS + g0 + kG * (ql & 1) + qj;
-  const bool qown = !HALF || !(ql & 1);    // the chain is one of the problem's states
-  float carry = (qown && a.state_valid && a.state) ? a.state[qidx] : 0.f;
-
+  // prep / output roles: channels 2 c2, 2 c2 + 1 at tokens TPT g .. TPT g + TPT - 1
+  const int c2 = tid & 15, g = tid >> 4;
+  const int nb = (a.L + kLT - 1) / kLT;
+  const int Lm1 = a.L - 1;
   const int64_t row = 2LL * a.D;
   const T *xzb = (const T *)a.xz + (int64_t)b * a.L * row;
-  const DT *db = (const DT *)a.delta + (int64_t)b * a.L * a.D;
-  const float *bcb = a.bc + (int64_t)b * a.L * 2 * NS;
+  const float *db = a.delta + (int64_t)b * a.L * a.D;
+  const float *bcb = a.bc + (int64_t)b * a.L * 2 * N;
   T *yb = (T *)a.y + (int64_t)b * a.L * a.D;
-  float *accb = GRP ? a.yacc + (int64_t)b * a.L * a.D : nullptr;   // this group's part of y
-  // this lane's 16-byte slot of a staged B|C row: slots 0-3 B[g0 .. g0+15], 4-7 C[g0 .. g0+15]
-  // (d_state 8: slots 2, 3 and 6, 7 repeat 0, 1 and 4, 5)
-  const int bcq = lane & 7;
-  const int bcoff = HALF ? 4 * (bcq & 1) + (bcq >= 4 ? kG : 0)
-                         : g0 + 4 * bcq + (bcq >= 4 ? NS - kN : 0);
-  const int nblocks = (a.L + kBlk - 1) / kBlk;
-  const int Lm1 = a.L - 1;
 
-  // Issue the direct-to-LDS loads of this wave's segment of block `blk`. Rows outside
-  // [0, L) read the nearest valid row (every address is valid; prep and the scan ignore
-  // those rows). Addresses are a wave-uniform base plus signed 32-bit lane offsets (a
-  // segment past the end has rmax < 0).
-  auto stage = [&](int blk, float (*bcdst)[2 * kN]) {
-    const int T0w = blk * kBlk + wv * kS;
-    const int rmax = Lm1 - T0w;                   // last valid segment-relative row
-    // B|C: 16 rows x 128 B = 2 wave-loads, 8 lanes per row
-    const float *bcbase = bcb + (int64_t)T0w * 2 * NS;
+  float Av[S], A2[S], iA[S], h[S];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int r = min(i * 8 + (lane >> 3), rmax);
-      load_lds16(bcbase + (r * 2 * NS + bcoff), &bcdst[i * 8][0]);
-    }
-    if (!kStageXZD) return;
-    // x: row r <-> token T0w - 3 + r, r < kXSeg; xrpl rows per wave-load
-    constexpr int xrpl = 64 / xrow_chunks;
-    const T *xbase = xzb + (int64_t)T0w * row + ch0;
-    const int irow = (int)row;
+  for (int s = 0; s < S; ++s) {
+    const float An = a.A[(int64_t)ch * N + n0 + s];
+    Av[s] = An;
+    A2[s] = An * kLog2e;
+    iA[s] = 1.0f / An;
+    h[s] = (a.state_valid && a.state) ? a.state[((int64_t)b * a.D + ch) * N + n0 + s] : 0.f;
+  }
+  // prep constants of the two channels
+  float wc[2][K], cb[2], Dv[2], dl2[2];
 #pragma unroll
-    for (int ld = 0; ld * xrpl < kXSeg; ++ld) {
-      const int rr = ld * xrpl + lane / xrow_chunks;
-      if (rr < kXSeg) {
-        const int r = min(max(rr - kHalo, -T0w), rmax);
-        load_lds16(xbase + r * irow + (lane % xrow_chunks) * xper, &x_s[wv][ld * xrpl][0]);
+  for (int e = 0; e < 2; ++e) {
+    const int ce = ch0 + 2 * c2 + e;
+#pragma unroll
+    for (int k = 0; k < K; ++k) wc[e][k] = io<T>::cvt(((const T *)a.conv_w)[(int64_t)ce * K + k]);
+    cb[e] = a.conv_b ? io<T>::cvt(((const T *)a.conv_b)[ce]) : 0.f;
+    Dv[e] = a.Dskip[ce];
+    dl2[e] = PAIRED ? (a.A[(int64_t)ce * N + 1] - a.A[(int64_t)ce * N]) * kLog2e : 0.f;
+  }
+
+  // ---- direct-to-LDS staging (one 16-byte load per lane and wave-round)
+  auto stage_xzd = [&](int j) {
+    const int T0 = j * kLT;
+    const int buf = j & 1;
+    if (sizeof(T) == 2) {
+      // x, then z: 32 rows of 64 B each = 2 wave-rounds each (4 lanes per row, 16 rows)
+#pragma unroll
+      for (int q = wv; q < 4; q += W) {
+        const int r = (q & 1) * 16 + (lane >> 2);
+        const int t = min(T0 + r, Lm1);
+        const T *src = xzb + (int64_t)t * row + ch0 + (lane & 3) * 8 + (q >= 2 ? a.D : 0);
+        T *dst = q < 2 ? &sm.xs[buf][(q & 1) * 16][0] : &sm.zs[buf][(q & 1) * 16][0];
+        dma16_opaque(src, lds_addr(dst));
       }
-    }
-    {
-      const int r = min(lane / xrow_chunks, rmax);
-      load_lds16(xbase + a.D + r * irow + (lane % xrow_chunks) * xper, &z_s[wv][0][0]);
-    }
-    constexpr int dper = 16 / sizeof(DT);
-    const DT *dbase = db + (int64_t)T0w * a.D + ch0;
-    {
-      const int r = min(lane / drow_chunks, rmax);
-      load_lds16(dbase + r * a.D + (lane % drow_chunks) * dper, &d_s[wv][0][0]);
-    }
-  };
-
-  // y of block b is stored at the start of block b+1, after that block's wait, so the wait
-  // for the staged tiles never has to cover freshly issued stores. Lane (c, p) owns tokens
-  // 2i + p of its wave's segment.
-  float ypend[kS / 2];
-  int ypend_t0 = -1;
-  auto flush = [&]() {
-    if (ypend_t0 < 0) return;
-    // wave-uniform segment base, 32-bit lane offsets
-    T *ybase = yb + (int64_t)(ypend_t0 + wv * kS) * a.D;
-    if (GRP) {   // this group's part of y (fp32)
-      float *abase = accb + (int64_t)(ypend_t0 + wv * kS) * a.D;
-#pragma unroll
-      for (int i = 0; i < kS / 2; ++i)
-        if (ypend_t0 + wv * kS + 2 * i + p < a.L) abase[(uint32_t)((2 * i + p) * a.D + ch)] = ypend[i];
-      return;
-    }
-    if (ypend_t0 + kBlk <= a.L) {
-#pragma unroll
-      for (int i = 0; i < kS / 2; ++i)
-        io<T>::st(ybase + (uint32_t)((2 * i + p) * a.D + ch), ypend[i]);
     } else {
+      // fp32: rows of 128 B, 8 lanes per row, 8 rows per wave-round; 4 rounds for x, 4 for z
 #pragma unroll
-      for (int i = 0; i < kS / 2; ++i)
-        if (ypend_t0 + wv * kS + 2 * i + p < a.L)
-          io<T>::st(ybase + (uint32_t)((2 * i + p) * a.D + ch), ypend[i]);
+      for (int q = wv; q < 8; q += W) {
+        const int r = (q & 3) * 8 + (lane >> 3);
+        const int t = min(T0 + r, Lm1);
+        const T *src = xzb + (int64_t)t * row + ch0 + (lane & 7) * 4 + (q >= 4 ? a.D : 0);
+        T *dst = q < 4 ? &sm.xs[buf][(q & 3) * 8][0] : &sm.zs[buf][(q & 3) * 8][0];
+        dma16_opaque(src, lds_addr(dst));
+      }
+    }
+    // dt: rows of 128 B, 8 rows per wave-round, 4 rounds
+#pragma unroll
+    for (int q = wv; q < 4; q += W) {
+      const int r = q * 8 + (lane >> 3);
+      const int t = min(T0 + r, Lm1);
+      dma16_opaque(db + (int64_t)t * a.D + ch0 + (lane & 7) * 4, lds_addr(&sm.ds[buf][q * 8][0]));
     }
   };
-  auto block = [&](int blk, float (*bc_cur)[kS][2 * kN], float (*bc_nxt)[kS][2 * kN]) {
-    const int T0 = blk * kBlk;
-    const int T0w = T0 + wv * kS;
-    wait_vmem_all();   // this wave's staged rows (and its older stores) have landed
-    flush();
+  auto stage_bc = [&](int j) {
+    // kLT rows of 2N floats = 256 N bytes = N / 4 wave-rounds of 1 KB
+    constexpr int rounds = N / 4;
+    constexpr int rowchunks = 2 * N / 4;                 // 16-byte chunks per row
+    const int T0 = j * kLT;
+    float *dst0 = &sm.bcs[j & 1][0][0];
+#pragma unroll
+    for (int q = wv; q < rounds; q += W) {
+      const int e = q * 64 + lane;                       // chunk index within the block
+      const int r = e / rowchunks, cc = e % rowchunks;
+      const int t = min(T0 + r, Lm1);
+      dma16_opaque(bcb + (int64_t)t * 2 * N + cc * 4, lds_addr(dst0 + q * 256));
+    }
+  };
 
-    // ---- 1. prep: conv + SiLU, dt, dt*u, D*u, SiLU(z) for (c, segment tokens 8p..8p+7)
-    {
-      // per-channel constants, reloaded each block (cache hits) to keep them out of the
-      // registers that live across the scan
-      float wc[K];
+  // ---- phases
+  auto prep = [&](int j) {
+    const int T0 = j * kLT, buf = j & 1;
+    constexpr int NR = TPT + 3;
+    // x rows TPT g - 3 .. TPT g + TPT - 1 of the block for both channels (negative rows from
+    // the halo)
+    float xw[2][NR];
 #pragma unroll
-      for (int k = 0; k < K; ++k) wc[k] = io<T>::cvt(((const T *)a.conv_w)[(int64_t)ch * K + k]);
-      const float cb = a.conv_b ? io<T>::cvt(((const T *)a.conv_b)[ch]) : 0.0f;
-      const float Dp = a.Dskip[ch];
-      // segment-relative token ts (ts >= -3)
-      auto getx = [&](int ts) -> float {
-        if (kStageXZD) return io<T>::cvt(x_s[wv][kStageXZD ? ts + kHalo : 0][c]);
-        return io<T>::cvt(xzb[(int64_t)min(T0w + ts, Lm1) * row + ch]);
-      };
-      auto getz = [&](int ts) -> float {
-        if (kStageXZD) return io<T>::cvt(z_s[wv][kStageXZD ? ts : 0][c]);
-        return io<T>::cvt(xzb[(int64_t)min(T0w + ts, Lm1) * row + a.D + ch]);
-      };
-      auto getd = [&](int ts) -> float {
-        if (kStageXZD) return (float)d_s[wv][kStageXZD ? ts : 0][c];
-        return (float)db[(int64_t)min(T0w + ts, Lm1) * a.D + ch];
-      };
-      const int ts0 = 8 * p;
-      float win[K - 1];
-#pragma unroll
-      for (int j = 0; j < K - 1; ++j) {
-        const int ts = ts0 - (K - 1) + j;         // segment-relative token of this window row
-        const int t = T0w + ts;
-        float v = 0.f;
-        if (t >= 0) {
-          v = getx(ts);
-        } else if (a.conv_valid && a.conv_state) {
-          v = io<T>::cvt(((const T *)a.conv_state)[((int64_t)b * a.D + ch) * (K - 1) + (K - 1) + t]);
+    for (int r = 0; r < NR; ++r) {
+      const int br = TPT * g - 3 + r;
+      if (br >= 0) {
+        if (sizeof(T) == 2) {
+          const uint32_t v = *(const uint32_t *)&sm.xs[buf][br][2 * c2];
+          xw[0][r] = lo_bf(v);
+          xw[1][r] = hi_bf(v);
+        } else {
+          const float2 v = *(const float2 *)&sm.xs[buf][br][2 * c2];
+          xw[0][r] = v.x;
+          xw[1][r] = v.y;
         }
-        win[j] = v;
+      } else {
+        const float2 v = *(const float2 *)&sm.halo[buf][3 + br][2 * c2];
+        xw[0][r] = v.x;
+        xw[1][r] = v.y;
       }
+    }
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int ts = ts0 + e;
-        const bool valid = T0w + ts < a.L;
-        const float x = getx(ts);
-        float acc = cb;
+    for (int e = 0; e < TPT; ++e) {
+      const int tt = TPT * g + e;
+      // the last 3 rows of this block are the next block's halo
+      if (tt >= kLT - 3)
+        *(float2 *)&sm.halo[buf ^ 1][tt - (kLT - 3)][2 * c2] = make_float2(xw[0][3 + e], xw[1][3 + e]);
+      const bool valid = T0 + tt < a.L;
+      float zv[2];
+      if (sizeof(T) == 2) {
+        const uint32_t v = *(const uint32_t *)&sm.zs[buf][tt][2 * c2];
+        zv[0] = lo_bf(v);
+        zv[1] = hi_bf(v);
+      } else {
+        const float2 v = *(const float2 *)&sm.zs[buf][tt][2 * c2];
+        zv[0] = v.x;
+        zv[1] = v.y;
+      }
+      const float2 dv = *(const float2 *)&sm.ds[buf][tt][2 * c2];
+      const float dts[2] = {valid ? dv.x : 0.f, valid ? dv.y : 0.f};
+      float4 o, q;
+      float pz[2];
 #pragma unroll
-        for (int j = 0; j < K - 1; ++j) acc = __builtin_fmaf(wc[j], win[j], acc);
-        acc = __builtin_fmaf(wc[K - 1], x, acc);
+      for (int cc = 0; cc < 2; ++cc) {
+        float acc = cb[cc];
 #pragma unroll
-        for (int j = 0; j + 1 < K - 1; ++j) win[j] = win[j + 1];
-        win[K - 2] = x;
+        for (int k = 0; k < K; ++k) acc = __builtin_fmaf(wc[cc][k], xw[cc][e + 4 - K + k], acc);
         const float u = silu_f(acc);
         // Past the end only dt is zeroed: the step is then the identity (exp(0 A) = 1, no
         // input), and those tokens' outputs are never stored. Staged rows there hold copies of
-        // row L-1, so u and z stay finite.
-        const float dt = valid ? getd(ts) : 0.f;
-        const float z = getz(ts);
-        // ZOH replays Bbar u = expm1(dt A)/A * B * u, so it keeps u where Euler keeps dt*u
-        pd_s[wv][ts][c] = make_float2(dt, ZOH ? u : dt * u);
-        eg_s[wv][ts][c] = make_float2(Dp * u, silu_f(z));
-      }
-    }
-    // the staged x, z, dt rows are consumed once this wave's LDS reads have returned; then the
-    // next block's rows may land (B|C is double-buffered)
-    __builtin_amdgcn_s_waitcnt(0xC07F);           // lgkmcnt(0), vmcnt / expcnt unconstrained
-    if (blk + 1 < nblocks) stage(blk + 1, bc_nxt[wv]);
-
-    // ---- 2. local pass over this wave's segment
-    float dA[kS][kG];
-    float hl[kG];
-#pragma unroll
-    for (int j = 0; j < kG; ++j) hl[j] = 0.f;
-    float sumdt = 0.f;
-#pragma unroll
-    for (int t = 0; t < kS; ++t) {
-      const float2 pd = pd_s[wv][t][c];
-      const float dt = pd.x, du = HALF && p ? 0.f : pd.y;
-      sumdt += dt;
-      const float4 B0 = *(const float4 *)&bc_cur[wv][t][kG * p];
-      const float4 B1 = *(const float4 *)&bc_cur[wv][t][kG * p + 4];
-      const float Bv[kG] = {B0.x, B0.y, B0.z, B0.w, B1.x, B1.y, B1.z, B1.w};
-#pragma unroll
-      for (int j = 0; j < kG; ++j) {
-        if (ZOH) {
-          const float em1 = expm1_f(dt * Av[j]);
-          dA[t][j] = em1;  // ZOH keeps expm1(dt A); exp(dt A) = 1 + it
-          hl[j] = __builtin_fmaf(em1 + 1.0f, hl[j], em1 * iA[j] * Bv[j] * du);
+        // row L - 1, so u and z stay finite.
+        const float dt = dts[cc];
+        const float2 od = make_float2(dt, ZOH ? u : dt * u);
+        const float2 oq = make_float2(Dv[cc] * u, silu_f(zv[cc]));
+        if (cc == 0) {
+          o.x = od.x; o.y = od.y; q.x = oq.x; q.y = oq.y;
         } else {
-          dA[t][j] = exp2_hw(dt * A2[j]);
-          hl[j] = __builtin_fmaf(dA[t][j], hl[j], du * Bv[j]);
+          o.z = od.x; o.w = od.y; q.z = oq.x; q.w = oq.y;
         }
+        pz[cc] = PAIRED ? exp2_hw(dt * dl2[cc]) : 0.f;
       }
+      *(float4 *)&sm.pd[buf][tt][2 * c2] = o;
+      *(float4 *)&sm.eg[buf][tt][2 * c2] = q;
+      if (PAIRED) *(float2 *)&sm.pe[buf][tt][2 * c2] = make_float2(pz[0], pz[1]);
     }
-    // ---- 3. publish this segment's transfer, then compose
-    {
-      float P[kG];
-#pragma unroll
-      for (int j = 0; j < kG; ++j) P[j] = exp2_hw(A2[j] * sumdt);
-      agg_s[wv][0][lane] = make_float4(P[0], P[1], P[2], P[3]);
-      agg_s[wv][1][lane] = make_float4(P[4], P[5], P[6], P[7]);
-      agg_s[wv][2][lane] = make_float4(hl[0], hl[1], hl[2], hl[3]);
-      agg_s[wv][3][lane] = make_float4(hl[4], hl[5], hl[6], hl[7]);
-    }
-    lds_barrier();
-    // chain pass: P of segment w becomes that segment's h_in
-    {
-      float *agg = &agg_s[0][0][0].x;
-      float Pw[kW], Sw[kW];
-#pragma unroll
-      for (int w2 = 0; w2 < kW; ++w2) {
-        Pw[w2] = agg[w2 * 1024 + tid];
-        Sw[w2] = agg[w2 * 1024 + 512 + tid];
-      }
-#pragma unroll
-      for (int w2 = 0; w2 < kW; ++w2) {
-        agg[w2 * 1024 + tid] = carry;
-        carry = __builtin_fmaf(Pw[w2], carry, Sw[w2]);
-      }
-    }
-    lds_barrier();
-    float h[kG];
-    {
-      const float4 H0 = agg_s[wv][0][lane], H1 = agg_s[wv][1][lane];
-      h[0] = H0.x; h[1] = H0.y; h[2] = H0.z; h[3] = H0.w;
-      h[4] = H1.x; h[5] = H1.y; h[6] = H1.z; h[7] = H1.w;
-    }
-    // ---- 4. replay from the true h_in; y from the two half-sums of the channel
-#pragma unroll
-    for (int t = 0; t < kS; t += 2) {
-      float ys[2];
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int ts = t + e;
-        const float4 B0 = *(const float4 *)&bc_cur[wv][ts][kG * p];
-        const float4 B1 = *(const float4 *)&bc_cur[wv][ts][kG * p + 4];
-        const float4 C0 = *(const float4 *)&bc_cur[wv][ts][kN + kG * p];
-        const float4 C1 = *(const float4 *)&bc_cur[wv][ts][kN + kG * p + 4];
-        const float Bv[kG] = {B0.x, B0.y, B0.z, B0.w, B1.x, B1.y, B1.z, B1.w};
-        const float Cv[kG] = {C0.x, C0.y, C0.z, C0.w, C1.x, C1.y, C1.z, C1.w};
-        const float du = HALF && p ? 0.f : pd_s[wv][ts][c].y;
-        float yy = 0.f;
-#pragma unroll
-        for (int j = 0; j < kG; ++j) {
-          if (ZOH) {
-            const float em1 = dA[ts][j];
-            h[j] = __builtin_fmaf(em1 + 1.0f, h[j], em1 * iA[j] * Bv[j] * du);
-          } else {
-            h[j] = __builtin_fmaf(dA[ts][j], h[j], du * Bv[j]);
-          }
-          yy = __builtin_fmaf(Cv[j], h[j], yy);
-        }
-        ys[e] = yy;
-      }
-      // lane p keeps token t+p: its own half-sum plus the partner lane's half-sum of it
-      const float keep = p ? ys[1] : ys[0];
-      const float send = p ? ys[0] : ys[1];
-      const float other = __builtin_bit_cast(
-          float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, send), 0xB1, 0xF, 0xF, false));
-      const float2 eg = eg_s[wv][t + p][c];
-      ypend[t / 2] = GFIRST ? keep + other + eg.x
-                     : GRP ? keep + other : (keep + other + eg.x) * eg.y;
-    }
-    ypend_t0 = T0;
   };
 
-  stage(0, bc_s0[wv]);
-  for (int blk = 0; blk < nblocks; ++blk) {
-    const bool odd = blk & 1;
-    block(blk, odd ? bc_s1 : bc_s0, odd ? bc_s0 : bc_s1);
+  auto output = [&](int j) {
+    const int T0 = j * kLT, buf = j & 1;
+#pragma unroll
+    for (int e = 0; e < TPT; ++e) {
+      const int tt = TPT * g + e;
+      float2 s = *(const float2 *)&sm.yp[buf][0][tt][2 * c2];
+#pragma unroll
+      for (int w = 1; w < W; ++w) {
+        const float2 v = *(const float2 *)&sm.yp[buf][w][tt][2 * c2];
+        s.x += v.x;
+        s.y += v.y;
+      }
+      const float4 q = *(const float4 *)&sm.eg[buf][tt][2 * c2];
+      const float y0 = (s.x + q.x) * q.y, y1 = (s.y + q.z) * q.w;
+      if (T0 + tt < a.L) {
+        T *dst = yb + (int64_t)(T0 + tt) * a.D + ch0 + 2 * c2;
+        if (sizeof(T) == 2)
+          *(uint32_t *)dst = pack_bf2(y0, y1);
+        else
+          *(float2 *)dst = make_float2(y0, y1);
+      }
+    }
+  };
+
+  // operands of one token for this lane
+  struct Tok {
+    float2 p;
+    float e1;
+    float B[S], C[S];
+  };
+  auto load_tok = [&](int buf, int t, Tok &k) {
+    k.p = sm.pd[buf][t][c];
+    k.e1 = PAIRED ? sm.pe[buf][t][c] : 0.f;
+    const float *Bt = &sm.bcs[buf][t][n0];
+    const float *Ct = Bt + N;
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      k.B[s] = Bt[s];
+      k.C[s] = Ct[s];
+    }
+  };
+  auto step = [&](const Tok &k) -> float {
+    float dA = 0.f, yy = 0.f;
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      if (ZOH) {
+        const float em1 = expm1_f(k.p.x * Av[s]);
+        h[s] = __builtin_fmaf(em1 + 1.0f, h[s], em1 * iA[s] * k.B[s] * k.p.y);
+      } else {
+        dA = (PAIRED && s > 0) ? dA * k.e1 : exp2_hw(k.p.x * A2[s]);
+        h[s] = __builtin_fmaf(dA, h[s], k.p.y * k.B[s]);
+      }
+      yy = s == 0 ? k.C[0] * h[0] : __builtin_fmaf(k.C[s], h[s], yy);
+    }
+    return yy;
+  };
+  auto scan = [&](int j) {
+    const int buf = j & 1;
+    Tok cur[2], nxt[2];
+    load_tok(buf, 0, cur[0]);
+    load_tok(buf, 1, cur[1]);
+#pragma unroll
+    for (int t = 0; t < kLT; t += 2) {
+      if (t + 2 < kLT) {   // next pair's operands in flight while this pair is computed
+        load_tok(buf, t + 2, nxt[0]);
+        load_tok(buf, t + 3, nxt[1]);
+      }
+      const float q0 = step(cur[0]);
+      const float q1 = step(cur[1]);
+      // lanes c (half 0) and c + 32 (half 1) hold the same channel's other states: after the
+      // swap, half 0 has both halves' terms of token t, half 1 both of token t + 1
+      const auto w2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(q0), __float_as_uint(q1),
+                                                       false, false);
+      sm.yp[buf][wv][t + half][c] = __uint_as_float(w2[0]) + __uint_as_float(w2[1]);
+      if (t + 2 < kLT) {
+        cur[0] = nxt[0];
+        cur[1] = nxt[1];
+      }
+    }
+  };
+
+  // ---- prologue: stage blocks 0 (B|C), 0 and 1 (x, z, dt); halo of block 0 = the carried
+  // conv state (oldest first) or zeros; prep of block 0
+  stage_bc(0);
+  stage_xzd(0);
+  if (nb > 1) stage_xzd(1);
+  if (tid < 3 * kLC) {
+    const int r = tid / kLC, cc = tid % kLC;   // halo row r <-> token r - 3
+    const int si = r - (3 - (K - 1));          // index into the K - 1 state entries
+    float v = 0.f;
+    if (si >= 0 && a.conv_valid && a.conv_state)
+      v = io<T>::cvt(((const T *)a.conv_state)[((int64_t)b * a.D + ch0 + cc) * (K - 1) + si]);
+    sm.halo[0][r][cc] = v;
   }
-  flush();
-  if (a.state && qown) a.state[qidx] = carry;
+  wait_vmem_all();
+  lds_barrier();
+  prep(0);
+  for (int j = 0; j < nb; ++j) {
+    wait_vmem_all();   // this wave's staged rows of blocks j + 1 (x, z, dt) and j (B|C)
+    lds_barrier();     // ... everyone's; P(j), S(j - 1) are complete
+    if (j + 2 < nb) stage_xzd(j + 2);
+    if (j + 1 < nb) stage_bc(j + 1);
+    if (j > 0) output(j - 1);
+    if (j + 1 < nb) prep(j + 1);
+    scan(j);
+  }
+  wait_vmem_all();
+  lds_barrier();
+  output(nb - 1);
+  if (a.state) {
+#pragma unroll
+    for (int s = 0; s < S; ++s) a.state[((int64_t)b * a.D + ch) * N + n0 + s] = h[s];
+  }
 }
 
-// y = (sum over the G state groups of their parts; the first holds D u) * SiLU(z), 4 channels
-// per thread
-template <typename T>
-__global__ __launch_bounds__(256) void scan_combine_kernel(ScanArgs a, int G) {
-  const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;   // 4 consecutive channels
-  const int64_t TD = (int64_t)a.B * a.L * a.D;
-  if (q * 4 >= TD) return;
-  const int64_t e = q * 4, tok = e / a.D;
-  const int i = (int)(e % a.D);
-  float4 s = *(const float4 *)(a.yacc + e);
-  for (int g = 1; g < G; ++g) {
-    const float4 v = *(const float4 *)(a.yacc + g * TD + e);
-    s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
-  }
-  const float sv[4] = {s.x, s.y, s.z, s.w};
-  float z[4];
-  if (sizeof(T) == 2) {
-    const uint2 zz = *(const uint2 *)((const bf16_t *)a.xz + tok * 2 * a.D + a.D + i);
-    const uint32_t zw[2] = {zz.x, zz.y};
-#pragma unroll
-    for (int c = 0; c < 4; ++c) z[c] = bf2f((bf16_t)(zw[c >> 1] >> ((c & 1) * 16)));
+template <typename T, bool ZOH, int K, int N>
+__global__ __launch_bounds__((64 * lane_waves<T, N>())) void scan_lanes_kernel(ScanArgs a) {
+  __shared__ __attribute__((aligned(16))) LaneSmem<T, N> sm;
+  constexpr int S = LaneSmem<T, N>::S;
+  const int groups = a.D / kLC;
+  const int gid = xcd_remap(blockIdx.x, gridDim.x);
+  const int b = gid / groups, ch0 = (gid % groups) * kLC;
+  if constexpr (ZOH || S < 2) {
+    lanes_body<T, ZOH, K, N, false>(a, sm, b, ch0);
   } else {
-    const float4 zv = *(const float4 *)((const float *)a.xz + tok * 2 * a.D + a.D + i);
-    z[0] = zv.x; z[1] = zv.y; z[2] = zv.z; z[3] = zv.w;
-  }
+    // paired decay: every lane's S states in arithmetic progression with the channel's step
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int ch = ch0 + (lane & 31), n0 = (2 * wv + (lane >> 5)) * S;
+    const float *Ar = a.A + (int64_t)ch * N;
+    const float dl = Ar[1] - Ar[0];
+    int ok = !a.general_a;
 #pragma unroll
-  for (int c = 0; c < 4; ++c) io<T>::st((T *)a.y + e + c, sv[c] * silu_f(z[c]));
+    for (int s = 1; s < S; ++s) ok &= (Ar[n0 + s] - Ar[n0] == (float)s * dl);
+    if (__syncthreads_and(ok))
+      lanes_body<T, ZOH, K, N, true>(a, sm, b, ch0);
+    else
+      lanes_body<T, ZOH, K, N, false>(a, sm, b, ch0);
+  }
 }
 
 template <typename T, int K>
-hipError_t dispatch_chunked_k(const ScanArgs &a, hipStream_t s) {
-  const unsigned blocks = (unsigned)((int64_t)a.B * (a.D / kCh));
-  if (a.N == kN || a.N == kG) {
-    if (a.N == kG) {
-      if (a.zoh)
-        hipLaunchKernelGGL((scan_chunked_kernel<T, true, K, 2>), dim3(blocks), dim3(kW * 64), 0, s, a);
-      else
-        hipLaunchKernelGGL((scan_chunked_kernel<T, false, K, 2>), dim3(blocks), dim3(kW * 64), 0, s, a);
-    } else if (a.zoh) {
-      hipLaunchKernelGGL((scan_chunked_kernel<T, true, K, 0>), dim3(blocks), dim3(kW * 64), 0, s, a);
-    } else {
-      hipLaunchKernelGGL((scan_chunked_kernel<T, false, K, 0>), dim3(blocks), dim3(kW * 64), 0, s, a);
-    }
-    return hipGetLastError();
+hipError_t dispatch_lanes_k(const ScanArgs &a, hipStream_t s) {
+  const unsigned blocks = (unsigned)((int64_t)a.B * (a.D / kLC));
+#define MM_LANES(NN)                                                                         \
+  if (a.N == NN) {                                                                           \
+    constexpr int thr = 64 * lane_waves<T, NN>();                                            \
+    if (a.zoh)                                                                               \
+      hipLaunchKernelGGL((scan_lanes_kernel<T, true, K, NN>), dim3(blocks), dim3(thr), 0, s, a); \
+    else                                                                                     \
+      hipLaunchKernelGGL((scan_lanes_kernel<T, false, K, NN>), dim3(blocks), dim3(thr), 0, s, a); \
+    return hipGetLastError();                                                                \
   }
-  // d_state = 16 G: one launch per group of 16 states, each writing its part of y, then the
-  // combine
-  const int G = a.N / kN;
-  for (int g = 0; g < G; ++g) {
-    ScanArgs ag = a;
-    ag.g0 = g * kN;
-    ag.yacc = a.yacc + (int64_t)g * a.B * a.L * a.D;
-    if (g == 0) {
-      if (a.zoh)
-        hipLaunchKernelGGL((scan_chunked_kernel<T, true, K, 3>), dim3(blocks), dim3(kW * 64), 0, s, ag);
-      else
-        hipLaunchKernelGGL((scan_chunked_kernel<T, false, K, 3>), dim3(blocks), dim3(kW * 64), 0, s, ag);
-    } else if (a.zoh) {
-      hipLaunchKernelGGL((scan_chunked_kernel<T, true, K, 1>), dim3(blocks), dim3(kW * 64), 0, s, ag);
-    } else {
-      hipLaunchKernelGGL((scan_chunked_kernel<T, false, K, 1>), dim3(blocks), dim3(kW * 64), 0, s, ag);
-    }
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  const int64_t n4 = (int64_t)a.B * a.L * a.D / 4;
-  hipLaunchKernelGGL((scan_combine_kernel<T>), dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s,
-                     a, G);
-  return hipGetLastError();
+  MM_LANES(8)
+  MM_LANES(16)
+  MM_LANES(32)
+  MM_LANES(64)
+#undef MM_LANES
+  return hipErrorInvalidValue;
 }
 
 template <typename T, int K>
@@ -533,24 +480,25 @@ hipError_t dispatch_k(const ScanArgs &a, hipStream_t s) {
 }
 
 // The sequential kernel has one wave per 64 (sequence, channel) pairs; when that leaves the
-// chip underfilled (fewer than 2048 waves) and the sequence is long, the time-parallel kernel
-// runs instead.
-bool use_chunked(const ScanArgs &a) {
+// chip underfilled (fewer than 2048 waves) and the sequence is long, the lane-per-state-group
+// kernel runs instead.
+bool use_lanes(const ScanArgs &a) {
+  if (a.D % kLC != 0) return false;
   if (a.force == 1) return false;
-  if (a.force == 2) return a.D % kCh == 0;
+  if (a.force == 2) return true;
   const int64_t waves = (int64_t)a.B * a.D / 64;
-  return a.L > kBlk && waves < 2048 && a.D % kCh == 0;
+  return a.L > kLT && waves < 2048;
 }
 
 template <typename T>
 hipError_t dispatch(const ScanArgs &a, hipStream_t s) {
-  const bool ch = use_chunked(a);
-  // d_state 8 and the 16-state groups of 32 / 64 run on the time-parallel kernel only
-  if (a.N != kN && !(ch && (a.N == kG || a.yacc))) return hipErrorInvalidValue;
+  const bool ln = use_lanes(a);
+  // d_state 8, 32, 64 run on the lane kernel only (csrc/scan_n.hip otherwise)
+  if (a.N != kN && !ln) return hipErrorInvalidValue;
   switch (a.K) {
-    case 2: return ch ? dispatch_chunked_k<T, 2>(a, s) : dispatch_k<T, 2>(a, s);
-    case 3: return ch ? dispatch_chunked_k<T, 3>(a, s) : dispatch_k<T, 3>(a, s);
-    case 4: return ch ? dispatch_chunked_k<T, 4>(a, s) : dispatch_k<T, 4>(a, s);
+    case 2: return ln ? dispatch_lanes_k<T, 2>(a, s) : dispatch_k<T, 2>(a, s);
+    case 3: return ln ? dispatch_lanes_k<T, 3>(a, s) : dispatch_k<T, 3>(a, s);
+    case 4: return ln ? dispatch_lanes_k<T, 4>(a, s) : dispatch_k<T, 4>(a, s);
   }
   return hipErrorInvalidValue;
 }
@@ -558,16 +506,16 @@ hipError_t dispatch(const ScanArgs &a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_scan(mm_dtype dt, const ScanArgs &a, hipStream_t s) {
-  if (a.N != kN && a.N != kG && a.N != 2 * kN && a.N != 4 * kN) return hipErrorInvalidValue;
+  if (a.N != 8 && a.N != 16 && a.N != 32 && a.N != 64) return hipErrorInvalidValue;
   return dt == MM_BF16 ? dispatch<bf16_t>(a, s) : dispatch<float>(a, s);
 }
 
 bool scan_tuned_used(int B, int L, int D, int N, uint32_t force) {
-  if (N != kG && N != 2 * kN && N != 4 * kN) return false;
+  if (N != 8 && N != 32 && N != 64) return false;
   ScanArgs a{};
   a.force = force;
   a.B = B; a.L = L; a.D = D; a.N = N;
-  return use_chunked(a);
+  return use_lanes(a);
 }
 
 }  // namespace mm

@@ -30,7 +30,7 @@ constexpr int kGS = 32;    // tokens per staged sub-block
 
 // Prefetched elements travel as raw bits and are decoded when they are staged: decoding a
 // 16-bit value where it is loaded would make the wave wait for the load one sub-block early.
-// dt: fp32, or fp16 for bf16 I/O; u: fp32, or bf16 high | low parts; z: the I/O type.
+// dt: fp32; u: fp32, or bf16 high | low parts; z: the I/O type.
 template <typename T> struct Raw;
 template <> struct Raw<float> {
   static __device__ __forceinline__ uint32_t dt(const ScanArgs &a, int64_t e) {
@@ -48,7 +48,7 @@ template <> struct Raw<float> {
 };
 template <> struct Raw<bf16_t> {
   static __device__ __forceinline__ uint32_t dt(const ScanArgs &a, int64_t e) {
-    return ((const uint16_t *)a.delta)[e];
+    return __float_as_uint(((const float *)a.delta)[e]);
   }
   static __device__ __forceinline__ uint32_t u(const ScanArgs &a, int64_t e) {
     return (uint32_t)((const bf16_t *)a.u)[e] | ((uint32_t)((const bf16_t *)a.u_lo)[e] << 16);
@@ -56,9 +56,7 @@ template <> struct Raw<bf16_t> {
   static __device__ __forceinline__ uint32_t z(const ScanArgs &a, int64_t e) {
     return ((const bf16_t *)a.xz)[e];
   }
-  static __device__ __forceinline__ float dt_f(uint32_t v) {
-    return (float)__builtin_bit_cast(_Float16, (uint16_t)v);
-  }
+  static __device__ __forceinline__ float dt_f(uint32_t v) { return __uint_as_float(v); }
   static __device__ __forceinline__ float u_f(uint32_t v) {
     return bf2f((bf16_t)(v & 0xFFFFu)) + bf2f((bf16_t)(v >> 16));
   }

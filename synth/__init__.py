@@ -24,6 +24,12 @@ Value recipe (same for every workload, widths scaled):
   A[i, n]         = -(n + 1)                 (S4D-real; fp32, all negative)
   Dskip           = 1                        (fp32)
   norm weights    = 1 (or U(0.5, 1.5) when gamma_random)
+Edge-case options of make_params (parity tests only; the workloads use the recipe above):
+  a_random        A[i, n] = -exp(U(-2, 3)) per (channel, state): decay rates from 0.14 to 20
+  dt_range        (lo, hi): dt0 log-uniform in [lo, hi] instead of [1e-3, 1e-1] (large values
+                  push dt_proj's pre-activation past softplus's linear-branch thresholds and
+                  exp(dt A) to underflow; tiny ones give steps near 1e-7)
+  d_random        Dskip ~ U(-1, 2)
 Random numbers come from torch.Generator seeded per tensor, on the device the
 tensor is made on; a test that compares two implementations feeds both the very
 same tensors (copied, never regenerated).
@@ -77,7 +83,7 @@ CONFIGS = {
 # Tensor ids keep the streams of different tensors apart for one seed.
 _TID = {"xz": 1, "conv_w": 2, "conv_b": 3, "x_proj_w": 4, "dt_proj_w": 5, "dt0": 6,
         "gamma": 7, "conv_state": 8, "ssm_state": 9, "decode_xz": 10, "misc": 11,
-        "layer_x": 12, "in_proj_w": 13, "out_proj_w": 14, "norm_w": 15}
+        "layer_x": 12, "in_proj_w": 13, "out_proj_w": 14, "norm_w": 15, "A": 16, "Dskip": 17}
 
 
 def generator(seed: int, tensor: str, device, step: int = 0) -> torch.Generator:
@@ -99,7 +105,8 @@ def _uniform(shape, lo, hi, g, device, dtype=torch.float32):
 
 
 def make_params(cfg: MixerConfig, seed: int, device="cpu", *, conv_bias: bool = False,
-                gamma_random: bool = False) -> dict:
+                gamma_random: bool = False, a_random: bool = False,
+                dt_range: tuple = (1e-3, 1e-1), d_random: bool = False) -> dict:
     """Parameters of one mixer, laid out as the C ABI takes them."""
     D, N, K, R = cfg.d_inner, cfg.d_state, cfg.d_conv, cfg.dt_rank
     dt = cfg.torch_dtype
@@ -111,13 +118,19 @@ def make_params(cfg: MixerConfig, seed: int, device="cpu", *, conv_bias: bool = 
                             generator(seed, "x_proj_w", device), device, dt)
     p["dt_proj_w"] = _normal((D, R), 1.0 / math.sqrt(R),
                              generator(seed, "dt_proj_w", device), device, dt)
-    # dt0 log-uniform in [1e-3, 1e-1]; the bias is its inverse softplus, so that the
-    # projection's bias alone maps to dt0 (input recipe, evaluated in float64).
+    # dt0 log-uniform in dt_range ([1e-3, 1e-1] in the workloads); the bias is its inverse
+    # softplus, so that the projection's bias alone maps to dt0 (evaluated in float64).
+    lo, hi = math.log(dt_range[0]), math.log(dt_range[1])
     u = _uniform((D,), 0.0, 1.0, generator(seed, "dt0", device), device, torch.float64)
-    dt0 = torch.exp(math.log(1e-3) + u * (math.log(1e-1) - math.log(1e-3)))
+    dt0 = torch.exp(lo + u * (hi - lo))
     p["dt_proj_b"] = (dt0 + torch.log(-torch.expm1(-dt0))).to(torch.float32)
-    p["A"] = (-torch.arange(1, N + 1, dtype=torch.float32, device=device)).repeat(D, 1).contiguous()
-    p["Dskip"] = torch.ones(D, dtype=torch.float32, device=device)
+    if a_random:
+        la = _uniform((D, N), -2.0, 3.0, generator(seed, "A", device), device, torch.float64)
+        p["A"] = (-torch.exp(la)).to(torch.float32).contiguous()
+    else:
+        p["A"] = (-torch.arange(1, N + 1, dtype=torch.float32, device=device)).repeat(D, 1).contiguous()
+    p["Dskip"] = (_uniform((D,), -1.0, 2.0, generator(seed, "Dskip", device), device)
+                  if d_random else torch.ones(D, dtype=torch.float32, device=device))
     if gamma_random:
         g = generator(seed, "gamma", device)
         p["dt_norm_w"] = _uniform((R,), 0.5, 1.5, g, device)

@@ -8,3 +8,23 @@ if ROOT not in sys.path:
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+
+
+def pytest_terminal_summary(terminalreporter, exitstatus, config):
+    """Every parity check of the session with its measured errors: the asserted one (fp32:
+    max abs; bf16: relative with the floor at 0.01 rms), the bf16 ratio with the floor at rms,
+    and the normwise error."""
+    try:
+        from tests.parity import RECORDS
+    except ImportError:
+        return
+    if not RECORDS:
+        return
+    tr = terminalreporter
+    tr.write_sep("-", f"parity checks ({len(RECORDS)})")
+    worst = {}
+    for what, io, e, e_rms, nw in RECORDS:
+        rms_s = "-" if e_rms is None else f"{e_rms:.3e}"
+        tr.write_line(f"{io:5s} err {e:.3e}  rms-floor {rms_s:>9s}  normwise {nw:.3e}  {what}")
+        worst[io] = max(worst.get(io, 0.0), e)
+    tr.write_line("worst: " + ", ".join(f"{k} {v:.3e}" for k, v in sorted(worst.items())))

@@ -1,17 +1,23 @@
 """Tolerances and comparison metrics of the GPU-vs-oracle parity tests.
 
 fp32 I/O: every output within 1e-4 absolute of the fp64 oracle (the required bar).
-bf16 I/O (fp32 state): every output y_i within 2e-2 * max(|r_i|, rms(r)) of the oracle's
-r_i -- a relative error of at most 2e-2 for outputs at or above the RMS of the output,
-and an absolute error of at most 2e-2 * rms(r) below it. The floor is needed because the
-bf16 path rounds u, dt_low and dt to bf16 (relative 2^-9 each) before they meet; the
-resulting error scales with the magnitude of the terms C.h and D.u, not with their sum,
-which may cancel to near zero. The conv state is a copy of inputs and must match bit for bit.
+bf16 I/O (fp32 state): every output y_i satisfies
+    |y_i - r_i| <= 2e-2 * max(|r_i|, 0.01 * rms(r)),
+i.e. a relative error of at most 2e-2 down to one hundredth of the output's RMS, and an
+absolute error of at most 2e-4 * rms(r) below that (the floor only keeps the ratio finite
+where r_i is zero). Every check also records the same ratio with the floor at rms(r) itself
+(a looser figure, kept for comparison) and the normwise error max|y - r| / max|r|; the
+session prints all three per check at the end (tests/conftest.py).
+The conv state is a copy of inputs and must match bit for bit.
 """
 import numpy as np
 
 F32_ABS_TOL = 1e-4
 BF16_REL_TOL = 2e-2
+BF16_FLOOR = 0.01        # floor of the denominator, as a fraction of rms(r)
+
+# (what, io dtype, asserted error, rms-floor error, normwise error) of every check this session
+RECORDS = []
 
 
 def to64(t):
@@ -25,29 +31,48 @@ def abs_err(got, ref):
     return float(np.max(np.abs(got - ref))) if got.size else 0.0
 
 
-def mixed_rel_err(got, ref):
+def mixed_rel_err(got, ref, floor=BF16_FLOOR):
+    """max_i |got_i - ref_i| / max(|ref_i|, floor * rms(ref)); 0 for empty inputs, and the
+    plain absolute error when ref is identically zero."""
     got, ref = to64(got), to64(ref)
     if not got.size:
         return 0.0
     rms = float(np.sqrt(np.mean(ref * ref)))
-    scale = np.maximum(np.abs(ref), rms if rms > 0 else 1.0)
+    if rms == 0.0:
+        return float(np.max(np.abs(got - ref)))
+    scale = np.maximum(np.abs(ref), floor * rms)
     return float(np.max(np.abs(got - ref) / scale))
 
 
 def normwise_err(got, ref):
     got, ref = to64(got), to64(ref)
+    if not got.size:
+        return 0.0
     den = float(np.max(np.abs(ref)))
     return float(np.max(np.abs(got - ref))) / (den if den > 0 else 1.0)
 
 
-def check(got, ref, io_dtype: str, what: str):
-    """Assert parity to the bar of the I/O dtype; returns the measured error."""
-    assert np.all(np.isfinite(to64(got))), f"{what}: non-finite values"
+def check(got, ref, io_dtype: str, what: str, f32_large_outputs: bool = False):
+    """Assert parity to the bar of the I/O dtype; returns the measured (asserted) error.
+
+    f32_large_outputs (edge cases only): outputs far above order one (steps dt of 12 to 40 give
+    |y| in the thousands) hold the fp32 bar relative to the largest output,
+    max|got - ref| <= 1e-4 * max(1, max|ref|), since fp32 itself rounds at 6e-8 |ref|; at
+    max|ref| <= 1 this is the absolute bar."""
+    g = to64(got)
+    assert np.all(np.isfinite(g)), f"{what}: non-finite values"
+    r = to64(ref)
     if io_dtype == "f32":
-        e = abs_err(got, ref)
+        e = abs_err(g, r)
+        if f32_large_outputs and r.size:
+            e /= max(1.0, float(np.max(np.abs(r))))
+        RECORDS.append((what, io_dtype, e, None, normwise_err(g, r)))
         assert e <= F32_ABS_TOL, f"{what}: max abs err {e:.3e} > {F32_ABS_TOL}"
     else:
-        e = mixed_rel_err(got, ref)
-        assert e <= BF16_REL_TOL, (f"{what}: mixed rel err {e:.3e} > {BF16_REL_TOL} "
-                                   f"(normwise {normwise_err(got, ref):.3e})")
+        e = mixed_rel_err(g, r)
+        e_rms = mixed_rel_err(g, r, floor=1.0)
+        nw = normwise_err(g, r)
+        RECORDS.append((what, io_dtype, e, e_rms, nw))
+        assert e <= BF16_REL_TOL, (f"{what}: rel err {e:.3e} (floor 0.01 rms) > {BF16_REL_TOL} "
+                                   f"(floor rms {e_rms:.3e}, normwise {nw:.3e})")
     return e

@@ -48,55 +48,54 @@ def test_workspace_size_formula():
     up = lambda v: (v + 255) // 256 * 256  # noqa: E731
     s = _shape()
     T, D, R, N = 4096, 8192, 256, 16
-    # T < 32768: conv -> u hi+lo, xdbl, dt_low hi+lo, B|C, dt (fp16)
+    # T < 32768: conv -> u hi+lo, xdbl, dt_low hi+lo, B|C, dt (fp32)
     expect = (2 * up(T * D * 2) + up(T * (R + 2 * N) * 4) + 2 * up(T * R * 2) + up(T * 2 * N * 4)
-              + up(T * D * 2))
+              + up(T * D * 4))
     assert mm.prefill_workspace_bytes(s) == expect
     s = _shape(seqlen=131072)
     T = 131072
-    # fused conv/x_proj/RMSNorm path: dt_low hi+lo, B|C, dt (fp16)
-    expect = 2 * up(T * R * 2) + up(T * 2 * N * 4) + up(T * D * 2)
+    # fused conv/x_proj/RMSNorm path: dt_low hi+lo, B|C, dt (fp32)
+    expect = 2 * up(T * R * 2) + up(T * 2 * N * 4) + up(T * D * 4)
     assert mm.prefill_workspace_bytes(s) == expect
     s32 = _shape(dtype=torch.float32, d_inner=64, dt_rank=8, seqlen=256)
     T, D, R = 256, 64, 8
     expect = up(T * D * 4) + up(T * (R + 2 * N) * 4) + up(T * R * 4) + up(T * 2 * N * 4) + up(T * D * 4)
     assert mm.prefill_workspace_bytes(s32) == expect
     # bf16 decode step, d_conv 4: x_proj partial sums over 64 ranges of 128 channels replace
-    # u and xdbl; then dt_low hi+lo, B|C, dt (fp16)
+    # u and xdbl; then dt_low hi+lo, B|C, dt (fp32)
     T, D, R = 256, 8192, 256
-    expect = up(64 * T * (R + 2 * N) * 4) + 2 * up(T * R * 2) + up(T * 2 * N * 4) + up(T * D * 2)
+    expect = up(64 * T * (R + 2 * N) * 4) + 2 * up(T * R * 2) + up(T * 2 * N * 4) + up(T * D * 4)
     assert mm.decode_workspace_bytes(_shape(seqlen=1, batch=256)) == expect
     # d_conv 3 takes the general path: u hi+lo and xdbl as for a prefill of B tokens
     expect = (2 * up(T * D * 2) + up(T * (R + 2 * N) * 4) + 2 * up(T * R * 2) + up(T * 2 * N * 4)
-              + up(T * D * 2))
+              + up(T * D * 4))
     assert mm.decode_workspace_bytes(_shape(seqlen=1, batch=256, d_conv=3)) == expect
     assert mm.decode_workspace_bytes(_shape(seqlen=2)) == 0      # decode needs seqlen == 1
 
 
 def test_workspace_size_for_other_state_sizes():
-    """d_state 8 / 32 / 64: where the time-parallel scan applies (few sequences, > 128 tokens)
-    the workspace holds no general-scan transfers; 32 / 64 add one fp32 part of y per group of
-    16 states; the scan-selection flag "sequential" restores the general scan's transfers."""
+    """d_state 8 / 32 / 64: where the lane-per-state-group scan applies (few sequences, > 32
+    tokens) the workspace holds no general-scan transfers; the scan-selection flag
+    "sequential" restores the general scan's transfers."""
     up = lambda v: (v + 255) // 256 * 256  # noqa: E731
     T, D, R = 1100, 256, 64
 
-    def general_projections(N):   # conv -> u hi+lo, xdbl, dt_low hi+lo, B|C, dt (fp16)
+    def general_projections(N):   # conv -> u hi+lo, xdbl, dt_low hi+lo, B|C, dt (fp32)
         return (2 * up(T * D * 2) + up(T * (R + 2 * N) * 4) + 2 * up(T * R * 2)
-                + up(T * 2 * N * 4) + up(T * D * 2))
+                + up(T * 2 * N * 4) + up(T * D * 4))
 
-    for N, groups in ((8, 0), (32, 2), (64, 4)):
+    for N in (8, 32, 64):
         s = _shape(seqlen=T, d_inner=D, dt_rank=R, d_state=N)
-        assert mm.prefill_workspace_bytes(s) == general_projections(N) + (
-            up(T * D * 4 * groups) if groups else 0), N
+        assert mm.prefill_workspace_bytes(s) == general_projections(N), N
         s.flags = mm.MM_FLAG_SCAN_SEQUENTIAL
         nr = (T + 511) // 512
         assert mm.prefill_workspace_bytes(s) == general_projections(N) + 2 * up(nr * D * N * 4), N
     # >= 32768 tokens: d_state 8 / 32 also take the fused conv + x_proj + RMSNorm kernel
     T = 32768 + 77
-    for N, groups in ((8, 0), (32, 2)):
+    for N in (8, 32):
         s = _shape(seqlen=T, d_inner=D, dt_rank=R, d_state=N)
-        fused = 2 * up(T * R * 2) + up(T * 2 * N * 4) + up(T * D * 2)
-        assert mm.prefill_workspace_bytes(s) == fused + (up(T * D * 4 * groups) if groups else 0)
+        fused = 2 * up(T * R * 2) + up(T * 2 * N * 4) + up(T * D * 4)
+        assert mm.prefill_workspace_bytes(s) == fused
 
 
 @pytest.mark.parametrize("kw,status", [
