@@ -1,6 +1,7 @@
 // C ABI of the mixer library: argument validation, workspace layout, stage sequencing and
 // the per-stage timer. Declarations and contracts: include/mamba_mixer.h.
 #include <algorithm>
+#include <cstring>
 #include <vector>
 
 #include "common.h"
@@ -86,7 +87,11 @@ mm_status check_shape(const mm_shape *s, bool decode) {
   if (s->batch <= 0 || s->seqlen <= 0 || s->d_inner <= 0 || s->d_state <= 0 || s->d_conv <= 0 ||
       s->dt_rank <= 0 || !(s->rms_eps > 0.0f))
     return MM_ERR_INVALID_ARG;
-  if (s->io_dtype != MM_F32 && s->io_dtype != MM_BF16) return MM_ERR_INVALID_ARG;
+  {  // the dtype arrives from C as any int: read its bytes as an int before using the enum
+    int dt = 0;
+    std::memcpy(&dt, &s->io_dtype, sizeof(dt));
+    if (dt != MM_F32 && dt != MM_BF16) return MM_ERR_INVALID_ARG;
+  }
   if (s->flags & ~(uint32_t)(MM_FLAG_ZOH_B | MM_FLAG_SCAN_SEQUENTIAL | MM_FLAG_SCAN_CHUNKED |
                              MM_FLAG_SCAN_GENERAL_A))
     return MM_ERR_INVALID_ARG;
@@ -741,7 +746,12 @@ const char *mm_stage_name(int stage) {
 }
 
 const char *mm_status_string(mm_status st) {
-  switch (st) {
+  // Callers in C pass any int; in C++ a value outside the enumerators' range may not be read
+  // as an mm_status, so the argument's bytes are read as an int.
+  int v = 0;
+  static_assert(sizeof(v) == sizeof(st), "mm_status is int-sized");
+  std::memcpy(&v, &st, sizeof(v));
+  switch (v) {
     case MM_OK: return "ok";
     case MM_ERR_INVALID_ARG: return "invalid argument";
     case MM_ERR_UNSUPPORTED: return "unsupported size";

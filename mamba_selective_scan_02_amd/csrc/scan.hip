@@ -469,6 +469,358 @@ hipError_t dispatch_lanes_k(const ScanArgs &a, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
+// ---------------------------------------------------------------------------------------
+// scan_twopass_kernel: time-parallel scan for d_state 16 at few sequences (the 128K prefill).
+//
+// A workgroup owns kCh = 32 channels of one sequence and walks the sequence in blocks of
+// kW * kS = 128 tokens; wave w owns the 16-token segment w of every block. Lane l works on
+// channel l / 2 and the 8 states 8 (l % 2) .. +7 (8 states per lane: B_t / C_t reads from LDS
+// serve 8 updates; 256 workgroups x 8 waves = two waves per SIMD at batch 1):
+//  0. The segment's B|C rows, its x rows (with the 3 conv-window rows before it), z and dt
+//     rows were loaded into the wave's LDS rows with direct-to-LDS 16-byte loads while the
+//     previous block was computed.
+//  1. Prep: lane l takes channel l / 2 and tokens 8 (l % 2) .. +7 of the segment:
+//     u = SiLU(conv1d(x) + b), dt, dt*u, D*u and SiLU(z), once per (token, channel), into the
+//     wave's LDS rows (the wave waits on its own loads only; no workgroup barrier).
+//  2. Local pass: the segment is scanned from h = 0, keeping exp(dt A) of every (token, state)
+//     in VGPRs (one exp per element, as in the sequential recurrence).
+//  3. Compose: the segment's local end state S and sum of dt go to LDS (barrier). Thread i
+//     then owns one (channel, state) chain: for each segment in order it forms the segment's
+//     decay P = exp(A sum dt) and applies the transfer h -> P h + S to the block's carry-in
+//     with the page's associative operator ("Parallel training via the parallel scan":
+//     (a, b) then (c, d) gives (ac, ad + b) for h -> a h + b), writing each segment's h_in
+//     over its S (barrier), and keeps the result as the next block's carry-in.
+//  4. Replay from the true h_in with the stored exp(dt A); y_t = C_t . h_t; the two
+//     half-sums of a channel meet by a DPP lane swap; y = (y_ssm + D u) SiLU(z) goes out.
+// Paired decay (as in the lane kernel; off with ScanArgs::general_a, never with ZOH): when
+// A[i, 8 p + k] = A[i, 8 p] + k delta_i for every lane, the local pass forms a lane's 8
+// decays as exp(dt A[i, 8 p]) times powers of exp(dt delta_i): 2 exps per lane and token
+// instead of 8.
+constexpr int kCh = 32, kW = 8, kS = 16, kG = 8, kBlk = kW * kS;
+constexpr int kHalo = 3;                  // x rows before the segment (conv window, K - 1 <= 3)
+constexpr int kXSeg = kS + 4;             // staged x rows per segment: halo + segment, padded
+
+template <typename T>
+struct TwoPassSmem {
+  // bf16 I/O stages x, z and dt through LDS; fp32 I/O (small problems) reads them from
+  // global memory in the prep, which keeps its LDS within 160 KB
+  static constexpr bool kStage = sizeof(T) == 2;
+  static constexpr int kXR = kStage ? kXSeg : 1, kZR = kStage ? kS : 1;
+  // per-wave staging (written by async loads); B|C double-buffered
+  float bc[2][kW][kS][2 * kN];
+  T x[kW][kXR][kCh];
+  T z[kW][kZR][kCh];
+  float d[kW][kZR][kCh];
+  // prep outputs: (dt, dt*u or u) and (D*u, SiLU(z)) per (token, channel) of each wave's
+  // segment; rows padded by one element so that rows 8 apart fall in different LDS banks
+  float2 pd[kW][kS][kCh + 1];
+  float2 eg[kW][kS][kCh + 1];
+  // segment local end states, lane-contiguous 16-byte slots [wave][S0..3, S4..7][lane]
+  // (overwritten by the segments' true start states), and each segment's sum of dt
+  float4 agg[kW][2][64];
+  float sdt[kW][kCh];
+};
+
+template <typename T, bool ZOH, int K, bool PAIRED>
+__device__ __forceinline__ void twopass_body(const ScanArgs &a, TwoPassSmem<T> &sm, int b,
+                                             int ch0) {
+  constexpr bool kStage = TwoPassSmem<T>::kStage;
+  constexpr int xper = 16 / sizeof(T);                 // x/z elements per 16-byte chunk
+  constexpr int xrow_chunks = kCh * sizeof(T) / 16;    // 16-byte chunks per staged x/z row
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wv = tid >> 6;
+  const int c = lane >> 1, p = lane & 1;
+  const int ch = ch0 + c;
+
+  float A2[kG], Av[kG], iA[kG];
+#pragma unroll
+  for (int j = 0; j < kG; ++j) {
+    Av[j] = a.A[(int64_t)ch * kN + kG * p + j];
+    A2[j] = Av[j] * kLog2e;
+    iA[j] = 1.0f / Av[j];
+  }
+  const float dl2 = PAIRED ? (Av[1] - Av[0]) * kLog2e : 0.f;
+  // chain thread tid <-> publishing lane ql = (tid >> 2) & 63 (channel ql / 2, state half
+  // ql & 1), state j = 4 (tid >> 8) + (tid & 3) of that half: its S of segment w is float
+  // w * 512 + tid of agg (conflict-free, lane-contiguous)
+  const int ql = (tid >> 2) & 63, qj = 4 * (tid >> 8) + (tid & 3);
+  const int64_t qidx = ((int64_t)b * a.D + ch0 + (ql >> 1)) * kN + kG * (ql & 1) + qj;
+  const float qA2 = a.A[(int64_t)(ch0 + (ql >> 1)) * kN + kG * (ql & 1) + qj] * kLog2e;
+  float carry = (a.state_valid && a.state) ? a.state[qidx] : 0.f;
+
+  const int64_t row = 2LL * a.D;
+  const T *xzb = (const T *)a.xz + (int64_t)b * a.L * row;
+  const float *db = a.delta + (int64_t)b * a.L * a.D;
+  const float *bcb = a.bc + (int64_t)b * a.L * 2 * kN;
+  T *yb = (T *)a.y + (int64_t)b * a.L * a.D;
+  // this lane's 16-byte slot of a staged B|C row: slots 0-3 B, 4-7 C
+  const int bcoff = 4 * (lane & 7);
+  const int nblocks = (a.L + kBlk - 1) / kBlk;
+  const int Lm1 = a.L - 1;
+
+  // Issue the direct-to-LDS loads of this wave's segment of block `blk`. Rows outside
+  // [0, L) read the nearest valid row (every address is valid; prep and the scan ignore
+  // those rows).
+  auto stage = [&](int blk, float (*bcdst)[2 * kN]) {
+    const int T0w = blk * kBlk + wv * kS;
+    const int rmax = Lm1 - T0w;                   // last valid segment-relative row
+    // B|C: 16 rows x 128 B = 2 wave-loads, 8 lanes per row
+    const float *bcbase = bcb + (int64_t)T0w * 2 * kN;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int r = min(i * 8 + (lane >> 3), rmax);
+      dma16_opaque(bcbase + (r * 2 * kN + bcoff), lds_addr(&bcdst[i * 8][0]));
+    }
+    if (!kStage) return;
+    // x: row r <-> token T0w - 3 + r, r < kXSeg; xrpl rows per wave-load
+    constexpr int xrpl = 64 / xrow_chunks;
+    const T *xbase = xzb + (int64_t)T0w * row + ch0;
+    const int irow = (int)row;
+#pragma unroll
+    for (int ld = 0; ld * xrpl < kXSeg; ++ld) {
+      const int rr = ld * xrpl + lane / xrow_chunks;
+      if (rr < kXSeg) {
+        const int r = min(max(rr - kHalo, -T0w), rmax);
+        dma16_opaque(xbase + r * irow + (lane % xrow_chunks) * xper, lds_addr(&sm.x[wv][ld * xrpl][0]));
+      }
+    }
+    {
+      const int r = min(lane / xrow_chunks, rmax);
+      dma16_opaque(xbase + a.D + r * irow + (lane % xrow_chunks) * xper, lds_addr(&sm.z[wv][0][0]));
+    }
+    // dt (fp32): 16 rows x 128 B = 2 wave-loads, 8 lanes per row
+    const float *dbase = db + (int64_t)T0w * a.D + ch0;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int r = min(i * 8 + (lane >> 3), rmax);
+      dma16_opaque(dbase + r * a.D + (lane & 7) * 4, lds_addr(&sm.d[wv][i * 8][0]));
+    }
+  };
+
+  // y of block b is stored at the start of block b+1, after that block's wait, so the wait
+  // for the staged tiles never has to cover freshly issued stores. Lane (c, p) owns tokens
+  // 2i + p of its wave's segment.
+  float ypend[kS / 2];
+  int ypend_t0 = -1;
+  auto flush = [&]() {
+    if (ypend_t0 < 0) return;
+    T *ybase = yb + (int64_t)(ypend_t0 + wv * kS) * a.D;   // wave-uniform, 32-bit lane offsets
+    // the lane offsets are formed here, per block: held across the block (the compiler's
+    // choice otherwise) they would take 16 more VGPRs than the kernel has
+    uint32_t off = (uint32_t)(p * a.D + ch);
+    asm volatile("" : "+v"(off));
+    const uint32_t step = 2u * (uint32_t)a.D;
+    if (ypend_t0 + kBlk <= a.L) {
+#pragma unroll
+      for (int i = 0; i < kS / 2; ++i) io<T>::st(ybase + off + i * step, ypend[i]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < kS / 2; ++i)
+        if (ypend_t0 + wv * kS + 2 * i + p < a.L) io<T>::st(ybase + off + i * step, ypend[i]);
+    }
+  };
+  auto block = [&](int blk, float (*bc_cur)[kS][2 * kN], float (*bc_nxt)[kS][2 * kN]) {
+    const int T0 = blk * kBlk;
+    const int T0w = T0 + wv * kS;
+    wait_vmem_all();   // this wave's staged rows (and its older stores) have landed
+    flush();
+
+    // ---- 1. prep: conv + SiLU, dt, dt*u, D*u, SiLU(z) for (c, segment tokens 8p..8p+7)
+    {
+      // per-channel constants, reloaded each block (cache hits) to keep them out of the
+      // registers that live across the scan
+      float wc[K];
+#pragma unroll
+      for (int k = 0; k < K; ++k) wc[k] = io<T>::cvt(((const T *)a.conv_w)[(int64_t)ch * K + k]);
+      const float cb = a.conv_b ? io<T>::cvt(((const T *)a.conv_b)[ch]) : 0.0f;
+      const float Dp = a.Dskip[ch];
+      // segment-relative token ts (ts >= -3)
+      auto getx = [&](int ts) -> float {
+        if (kStage) return io<T>::cvt(sm.x[wv][kStage ? ts + kHalo : 0][c]);
+        return io<T>::cvt(xzb[(int64_t)min(T0w + ts, Lm1) * row + ch]);
+      };
+      auto getz = [&](int ts) -> float {
+        if (kStage) return io<T>::cvt(sm.z[wv][kStage ? ts : 0][c]);
+        return io<T>::cvt(xzb[(int64_t)min(T0w + ts, Lm1) * row + a.D + ch]);
+      };
+      auto getd = [&](int ts) -> float {
+        if (kStage) return sm.d[wv][kStage ? ts : 0][c];
+        return db[(int64_t)min(T0w + ts, Lm1) * a.D + ch];
+      };
+      const int ts0 = 8 * p;
+      float win[K - 1];
+#pragma unroll
+      for (int j = 0; j < K - 1; ++j) {
+        const int ts = ts0 - (K - 1) + j;         // segment-relative token of this window row
+        const int t = T0w + ts;
+        float v = 0.f;
+        if (t >= 0) {
+          v = getx(ts);
+        } else if (a.conv_valid && a.conv_state) {
+          v = io<T>::cvt(((const T *)a.conv_state)[((int64_t)b * a.D + ch) * (K - 1) + (K - 1) + t]);
+        }
+        win[j] = v;
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int ts = ts0 + e;
+        const bool valid = T0w + ts < a.L;
+        const float x = getx(ts);
+        float acc = cb;
+#pragma unroll
+        for (int j = 0; j < K - 1; ++j) acc = __builtin_fmaf(wc[j], win[j], acc);
+        acc = __builtin_fmaf(wc[K - 1], x, acc);
+#pragma unroll
+        for (int j = 0; j + 1 < K - 1; ++j) win[j] = win[j + 1];
+        win[K - 2] = x;
+        const float u = silu_f(acc);
+        // Past the end only dt is zeroed: the step is then the identity (exp(0 A) = 1, no
+        // input), and those tokens' outputs are never stored. Staged rows there hold copies of
+        // row L-1, so u and z stay finite.
+        const float dt = valid ? getd(ts) : 0.f;
+        const float z = getz(ts);
+        // ZOH replays Bbar u = expm1(dt A)/A * B * u, so it keeps u where Euler keeps dt*u
+        sm.pd[wv][ts][c] = make_float2(dt, ZOH ? u : dt * u);
+        sm.eg[wv][ts][c] = make_float2(Dp * u, silu_f(z));
+      }
+    }
+    // the staged x, z, dt rows are consumed once this wave's LDS reads have returned; then the
+    // next block's rows may land (B|C is double-buffered)
+    __builtin_amdgcn_s_waitcnt(0xC07F);           // lgkmcnt(0), vmcnt / expcnt unconstrained
+    if (blk + 1 < nblocks) stage(blk + 1, bc_nxt[wv]);
+
+    // ---- 2. local pass over this wave's segment
+    float dA[kS][kG];
+    float hl[kG];
+#pragma unroll
+    for (int j = 0; j < kG; ++j) hl[j] = 0.f;
+    float sumdt = 0.f;
+#pragma unroll
+    for (int t = 0; t < kS; ++t) {
+      const float2 pd = sm.pd[wv][t][c];
+      const float dt = pd.x, du = pd.y;
+      sumdt += dt;
+      const float4 B0 = *(const float4 *)&bc_cur[wv][t][kG * p];
+      const float4 B1 = *(const float4 *)&bc_cur[wv][t][kG * p + 4];
+      const float Bv[kG] = {B0.x, B0.y, B0.z, B0.w, B1.x, B1.y, B1.z, B1.w};
+      float e1 = 0.f;
+      if (PAIRED) e1 = exp2_hw(dt * dl2);
+#pragma unroll
+      for (int j = 0; j < kG; ++j) {
+        if (ZOH) {
+          const float em1 = expm1_f(dt * Av[j]);
+          dA[t][j] = em1;  // ZOH keeps expm1(dt A); exp(dt A) = 1 + it
+          hl[j] = __builtin_fmaf(em1 + 1.0f, hl[j], em1 * iA[j] * Bv[j] * du);
+        } else {
+          dA[t][j] = (PAIRED && j > 0) ? dA[t][j - 1] * e1 : exp2_hw(dt * A2[j]);
+          hl[j] = __builtin_fmaf(dA[t][j], hl[j], du * Bv[j]);
+        }
+      }
+    }
+    // ---- 3. publish this segment's local end state and sum of dt, then compose
+    sm.agg[wv][0][lane] = make_float4(hl[0], hl[1], hl[2], hl[3]);
+    sm.agg[wv][1][lane] = make_float4(hl[4], hl[5], hl[6], hl[7]);
+    if (!p) sm.sdt[wv][c] = sumdt;
+    lds_barrier();
+    // chain pass: each segment's S becomes its h_in
+    {
+      float *agg = &sm.agg[0][0][0].x;
+      float Sw[kW], Pw[kW];
+#pragma unroll
+      for (int w2 = 0; w2 < kW; ++w2) {
+        Sw[w2] = agg[w2 * 512 + tid];
+        Pw[w2] = exp2_hw(qA2 * sm.sdt[w2][ql >> 1]);
+      }
+#pragma unroll
+      for (int w2 = 0; w2 < kW; ++w2) {
+        agg[w2 * 512 + tid] = carry;
+        carry = __builtin_fmaf(Pw[w2], carry, Sw[w2]);
+      }
+    }
+    lds_barrier();
+    float h[kG];
+    {
+      const float4 H0 = sm.agg[wv][0][lane], H1 = sm.agg[wv][1][lane];
+      h[0] = H0.x; h[1] = H0.y; h[2] = H0.z; h[3] = H0.w;
+      h[4] = H1.x; h[5] = H1.y; h[6] = H1.z; h[7] = H1.w;
+    }
+    // ---- 4. replay from the true h_in; y from the two half-sums of the channel
+#pragma unroll
+    for (int t = 0; t < kS; t += 2) {
+      float ys[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int ts = t + e;
+        const float4 B0 = *(const float4 *)&bc_cur[wv][ts][kG * p];
+        const float4 B1 = *(const float4 *)&bc_cur[wv][ts][kG * p + 4];
+        const float4 C0 = *(const float4 *)&bc_cur[wv][ts][kN + kG * p];
+        const float4 C1 = *(const float4 *)&bc_cur[wv][ts][kN + kG * p + 4];
+        const float Bv[kG] = {B0.x, B0.y, B0.z, B0.w, B1.x, B1.y, B1.z, B1.w};
+        const float Cv[kG] = {C0.x, C0.y, C0.z, C0.w, C1.x, C1.y, C1.z, C1.w};
+        const float du = sm.pd[wv][ts][c].y;
+        float yy = 0.f;
+#pragma unroll
+        for (int j = 0; j < kG; ++j) {
+          if (ZOH) {
+            const float em1 = dA[ts][j];
+            h[j] = __builtin_fmaf(em1 + 1.0f, h[j], em1 * iA[j] * Bv[j] * du);
+          } else {
+            h[j] = __builtin_fmaf(dA[ts][j], h[j], du * Bv[j]);
+          }
+          yy = __builtin_fmaf(Cv[j], h[j], yy);
+        }
+        ys[e] = yy;
+      }
+      // lane p keeps token t+p: its own half-sum plus the partner lane's half-sum of it
+      const float keep = p ? ys[1] : ys[0];
+      const float send = p ? ys[0] : ys[1];
+      const float other = __builtin_bit_cast(
+          float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, send), 0xB1, 0xF, 0xF, false));
+      const float2 eg = sm.eg[wv][t + p][c];
+      ypend[t / 2] = (keep + other + eg.x) * eg.y;
+    }
+    ypend_t0 = T0;
+  };
+
+  stage(0, sm.bc[0][wv]);
+  for (int blk = 0; blk < nblocks; ++blk) {
+    const bool odd = blk & 1;
+    block(blk, odd ? sm.bc[1] : sm.bc[0], odd ? sm.bc[0] : sm.bc[1]);
+  }
+  flush();
+  if (a.state) a.state[qidx] = carry;
+}
+
+template <typename T, bool ZOH, int K>
+__global__ __launch_bounds__(kW * 64) void scan_twopass_kernel(ScanArgs a) {
+  static_assert(!ZOH, "the two-pass kernel takes first-order Bbar only");
+  __shared__ __attribute__((aligned(16))) TwoPassSmem<T> sm;
+  const int groups = a.D / kCh;
+  const int gid = xcd_remap(blockIdx.x, gridDim.x);
+  const int b = gid / groups, ch0 = (gid % groups) * kCh;
+  {
+    // paired decay: every lane's 8 states in arithmetic progression with the channel's step
+    const int lane = threadIdx.x & 63;
+    const int ch = ch0 + (lane >> 1), n0 = kG * (lane & 1);
+    const float *Ar = a.A + (int64_t)ch * kN;
+    const float dl = Ar[1] - Ar[0];
+    int ok = !a.general_a;
+#pragma unroll
+    for (int s = 1; s < kG; ++s) ok &= (Ar[n0 + s] - Ar[n0] == (float)s * dl);
+    if (__syncthreads_and(ok))
+      twopass_body<T, ZOH, K, true>(a, sm, b, ch0);
+    else
+      twopass_body<T, ZOH, K, false>(a, sm, b, ch0);
+  }
+}
+
+template <typename T, int K>
+hipError_t dispatch_twopass_k(const ScanArgs &a, hipStream_t s) {
+  const unsigned blocks = (unsigned)((int64_t)a.B * (a.D / kCh));
+  hipLaunchKernelGGL((scan_twopass_kernel<T, false, K>), dim3(blocks), dim3(kW * 64), 0, s, a);
+  return hipGetLastError();
+}
+
 template <typename T, int K>
 hipError_t dispatch_k(const ScanArgs &a, hipStream_t s) {
   const unsigned blocks = (unsigned)(((int64_t)a.B * a.D) / 64);
@@ -490,15 +842,22 @@ bool use_lanes(const ScanArgs &a) {
   return a.L > kLT && waves < 2048;
 }
 
+// d_state 16 with first-order Bbar: the two-pass kernel (its ZOH form would not fit the VGPRs:
+// it keeps expm1(dt A) for the replay and needs 1 / A besides); everything else the lane kernel
+template <typename T, int K>
+hipError_t dispatch_few_k(const ScanArgs &a, hipStream_t s) {
+  return a.N == kN && !a.zoh ? dispatch_twopass_k<T, K>(a, s) : dispatch_lanes_k<T, K>(a, s);
+}
+
 template <typename T>
 hipError_t dispatch(const ScanArgs &a, hipStream_t s) {
-  const bool ln = use_lanes(a);
+  const bool few = use_lanes(a);
   // d_state 8, 32, 64 run on the lane kernel only (csrc/scan_n.hip otherwise)
-  if (a.N != kN && !ln) return hipErrorInvalidValue;
+  if (a.N != kN && !few) return hipErrorInvalidValue;
   switch (a.K) {
-    case 2: return ln ? dispatch_lanes_k<T, 2>(a, s) : dispatch_k<T, 2>(a, s);
-    case 3: return ln ? dispatch_lanes_k<T, 3>(a, s) : dispatch_k<T, 3>(a, s);
-    case 4: return ln ? dispatch_lanes_k<T, 4>(a, s) : dispatch_k<T, 4>(a, s);
+    case 2: return few ? dispatch_few_k<T, 2>(a, s) : dispatch_k<T, 2>(a, s);
+    case 3: return few ? dispatch_few_k<T, 3>(a, s) : dispatch_k<T, 3>(a, s);
+    case 4: return few ? dispatch_few_k<T, 4>(a, s) : dispatch_k<T, 4>(a, s);
   }
   return hipErrorInvalidValue;
 }

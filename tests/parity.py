@@ -52,8 +52,12 @@ def normwise_err(got, ref):
     return float(np.max(np.abs(got - ref))) / (den if den > 0 else 1.0)
 
 
-def check(got, ref, io_dtype: str, what: str, f32_large_outputs: bool = False):
+def check(got, ref, io_dtype: str, what: str, f32_large_outputs: bool = False,
+          bf16_floor: float = BF16_FLOOR):
     """Assert parity to the bar of the I/O dtype; returns the measured (asserted) error.
+
+    bf16_floor: the floor of the relative bar as a fraction of rms(ref); 0.01 everywhere except
+    the Mamba layer's bf16 output (tests/test_gpu_layer.py states why it takes rms(ref)).
 
     f32_large_outputs (edge cases only): outputs far above order one (steps dt of 12 to 40 give
     |y| in the thousands) hold the fp32 bar relative to the largest output,
@@ -69,10 +73,13 @@ def check(got, ref, io_dtype: str, what: str, f32_large_outputs: bool = False):
         RECORDS.append((what, io_dtype, e, None, normwise_err(g, r)))
         assert e <= F32_ABS_TOL, f"{what}: max abs err {e:.3e} > {F32_ABS_TOL}"
     else:
-        e = mixed_rel_err(g, r)
+        e01 = mixed_rel_err(g, r)
         e_rms = mixed_rel_err(g, r, floor=1.0)
+        e = mixed_rel_err(g, r, floor=bf16_floor)
         nw = normwise_err(g, r)
-        RECORDS.append((what, io_dtype, e, e_rms, nw))
-        assert e <= BF16_REL_TOL, (f"{what}: rel err {e:.3e} (floor 0.01 rms) > {BF16_REL_TOL} "
-                                   f"(floor rms {e_rms:.3e}, normwise {nw:.3e})")
+        RECORDS.append((what if bf16_floor == BF16_FLOOR else f"{what} [asserted at floor "
+                        f"{bf16_floor:g} rms: {e:.3e}]", io_dtype, e01, e_rms, nw))
+        assert e <= BF16_REL_TOL, (f"{what}: rel err {e:.3e} (floor {bf16_floor:g} rms) > "
+                                   f"{BF16_REL_TOL} (floor 0.01 rms {e01:.3e}, floor rms "
+                                   f"{e_rms:.3e}, normwise {nw:.3e})")
     return e
