@@ -152,6 +152,22 @@ MM_API mm_status mamba_mixer_decode_step(const mm_shape *s, const mm_params *p, 
                                   size_t workspace_bytes, void *stream);
 
 /*
+ * mamba_mixer_decode_step without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the step's intermediates live in a device array inside the library, one per GPU,
+ * of mm_noalloc_scratch_bytes() = 64 MiB, held until the process ends. It allocates nothing and
+ * calls no allocating routine; results equal mamba_mixer_decode_step's bit for bit (the same
+ * kernels). Returns MM_ERR_WORKSPACE when the shape's decode workspace
+ * (mm_decode_workspace_bytes) exceeds the array, and the other errors of
+ * mamba_mixer_decode_step. Every call on one GPU shares that GPU's array: calls that overlap on
+ * one GPU (other streams, other threads) race and must be serialised by the caller.
+ */
+MM_API size_t mm_noalloc_scratch_bytes(void);
+MM_API mm_status mamba_mixer_decode_step_noalloc(const mm_shape *s, const mm_params *p,
+                                                 const void *xz, void *y, void *conv_state,
+                                                 float *ssm_state, void *stream);
+
+/*
  * Per-stage timing (a measurement aid). A timer records a pair of HIP events around
  * each kernel stage of every *_timed call on that call's stream; mm_stage_timer_read
  * synchronises on the recorded events and returns the summed milliseconds and the

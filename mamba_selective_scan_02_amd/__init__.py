@@ -80,6 +80,8 @@ def lib() -> ctypes.CDLL:
             ("mamba_mixer_prefill_timed", [P(S), P(Params), V, V, V, V, I, V, Z, V, V], I),
             ("mamba_mixer_decode_step", [P(S), P(Params), V, V, V, V, V, Z, V], I),
             ("mamba_mixer_decode_step_timed", [P(S), P(Params), V, V, V, V, V, Z, V, V], I),
+            ("mm_noalloc_scratch_bytes", [], Z),
+            ("mamba_mixer_decode_step_noalloc", [P(S), P(Params), V, V, V, V, V], I),
             ("mm_stage_timer_create", [], V),
             ("mm_stage_timer_destroy", [V], None),
             ("mm_stage_timer_reset", [V], None),
@@ -240,6 +242,20 @@ def decode_step(xz, params, conv_state, ssm_state, *, y=None, workspace=None, ep
         st = lib().mamba_mixer_decode_step_timed(*args, timer.h)
     if st != MM_OK:
         raise MixerError(st, "mamba_mixer_decode_step")
+    return y
+
+
+def decode_step_noalloc(xz, params, conv_state, ssm_state, *, y, eps=1e-6, zoh=False,
+                        stream=None):
+    """Run mamba_mixer_decode_step_noalloc (no workspace: the library's per-GPU scratch) on
+    xz [B, 2D] into the caller's y [B, D]; states are updated in place. Returns y."""
+    shape = shape_of(xz, params, decode=True, eps=eps, zoh=zoh)
+    p = params_struct(params)
+    st = lib().mamba_mixer_decode_step_noalloc(ctypes.byref(shape), ctypes.byref(p), _ptr(xz),
+                                               _ptr(y), _ptr(conv_state), _ptr(ssm_state),
+                                               _stream(stream))
+    if st != MM_OK:
+        raise MixerError(st, "mamba_mixer_decode_step_noalloc")
     return y
 
 

@@ -2,6 +2,7 @@
 // the per-stage timer. Declarations and contracts: include/mamba_mixer.h.
 #include <algorithm>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "common.h"
@@ -614,9 +615,51 @@ mm_status backward_impl(const mm_shape *s, const mm_params *p, const void *xz, c
   return MM_OK;
 }
 
+// ---- allocation-free decode step
+// Device scratch that stands in for the caller's workspace in
+// mamba_mixer_decode_step_noalloc: each GPU the library runs on holds one copy, at its own
+// address, until the process ends. The host-side name of the array is not a device address;
+// the per-device address comes from hipGetSymbolAddress and is the only one kernels receive.
+constexpr size_t kNoallocScratchBytes = size_t(64) << 20;
+__device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// The scratch array's device address on the current device, looked up once per device.
+mm_status noalloc_scratch(void **out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MM_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return MM_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return MM_ERR_HIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return MM_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t mm_noalloc_scratch_bytes(void) { return kNoallocScratchBytes; }
+
+mm_status mamba_mixer_decode_step_noalloc(const mm_shape *s, const mm_params *p, const void *xz,
+                                          void *y, void *conv_state, float *ssm_state,
+                                          void *stream) {
+  mm_status r = check_shape(s, true);
+  if (r != MM_OK) return r;
+  if (layout(*s, true).total > kNoallocScratchBytes) return MM_ERR_WORKSPACE;
+  void *ws = nullptr;
+  if ((r = noalloc_scratch(&ws)) != MM_OK) return r;
+  // every workspace region of the decode step is written before it is read: nothing to clear
+  return decode_impl(s, p, xz, y, conv_state, ssm_state, ws, kNoallocScratchBytes, stream,
+                     nullptr);
+}
 
 size_t mm_layer_workspace_bytes(const mm_shape *s, int32_t d_model) {
   if (!s || check_shape(s, false) != MM_OK || d_model <= 0) return 0;

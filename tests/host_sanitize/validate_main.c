@@ -106,6 +106,13 @@ int main() {
          MM_ERR_INVALID_ARG);
   EXPECT(mamba_mixer_decode_step(&dec, &p, f, f2, f, (float *)f, f, needd - 1, NULL) ==
          MM_ERR_WORKSPACE);
+  // the allocation-free decode step: a shape beyond its scratch is refused before any HIP call
+  const mm_shape huge = shape(4096, 1, 16384, 16, 4, 512, MM_BF16, 0);
+  EXPECT(mm_decode_workspace_bytes(&huge) > mm_noalloc_scratch_bytes());
+  EXPECT(mamba_mixer_decode_step_noalloc(&huge, &p, f, f2, f, (float *)f, NULL) ==
+         MM_ERR_WORKSPACE);
+  EXPECT(mamba_mixer_decode_step_noalloc(&ok, &p, f, f2, f, (float *)f, NULL) ==
+         MM_ERR_INVALID_ARG);
   mm_layer_params lp;
   lp.mixer = p;
   lp.norm_w = (const float *)f;
