@@ -519,6 +519,7 @@ struct TwoPassSmem {
   // (overwritten by the segments' true start states), and each segment's sum of dt
   float4 agg[kW][2][64];
   float sdt[kW][kCh];
+  float cst[kCh][8];             // per channel: conv taps (K), conv bias, D
 };
 
 template <typename T, bool ZOH, int K, bool PAIRED>
@@ -543,10 +544,12 @@ __device__ __forceinline__ void twopass_body(const ScanArgs &a, TwoPassSmem<T> &
   // chain thread tid <-> publishing lane ql = (tid >> 2) & 63 (channel ql / 2, state half
   // ql & 1), state j = 4 (tid >> 8) + (tid & 3) of that half: its S of segment w is float
   // w * 512 + tid of agg (conflict-free, lane-contiguous)
-  const int ql = (tid >> 2) & 63, qj = 4 * (tid >> 8) + (tid & 3);
+  // (threads 512 and up, when kW > 8, own no chain)
+  const bool chain = tid < 512;
+  const int ql = (tid >> 2) & 63, qj = 4 * ((tid >> 8) & 1) + (tid & 3);
   const int64_t qidx = ((int64_t)b * a.D + ch0 + (ql >> 1)) * kN + kG * (ql & 1) + qj;
   const float qA2 = a.A[(int64_t)(ch0 + (ql >> 1)) * kN + kG * (ql & 1) + qj] * kLog2e;
-  float carry = (a.state_valid && a.state) ? a.state[qidx] : 0.f;
+  float carry = (chain && a.state_valid && a.state) ? a.state[qidx] : 0.f;
 
   const int64_t row = 2LL * a.D;
   const T *xzb = (const T *)a.xz + (int64_t)b * a.L * row;
@@ -562,38 +565,44 @@ __device__ __forceinline__ void twopass_body(const ScanArgs &a, TwoPassSmem<T> &
   // [0, L) read the nearest valid row (every address is valid; prep and the scan ignore
   // those rows).
   auto stage = [&](int blk, float (*bcdst)[2 * kN]) {
+    // wave-uniform bases (SGPRs) and 32-bit lane offsets, so that no 64-bit address lives in
+    // VGPRs across the block; rows outside [0, L) are clamped into it
     const int T0w = blk * kBlk + wv * kS;
-    const int rmax = Lm1 - T0w;                   // last valid segment-relative row
-    // B|C: 16 rows x 128 B = 2 wave-loads, 8 lanes per row
-    const float *bcbase = bcb + (int64_t)T0w * 2 * kN;
+    const int tb = min(T0w, Lm1);                 // first staged row of B|C, z, dt
+    // B|C: kS rows x 128 B = kS / 8 wave-loads, 8 lanes per row
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int r = min(i * 8 + (lane >> 3), rmax);
-      dma16_opaque(bcbase + (r * 2 * kN + bcoff), lds_addr(&bcdst[i * 8][0]));
+    for (int i = 0; i < kS / 8; ++i) {
+      const int r = min(T0w + i * 8 + (lane >> 3), Lm1) - tb;
+      dma16_opaque_so(bcb + (int64_t)tb * 2 * kN, (uint32_t)(r * 2 * kN + bcoff) * 4u,
+                      lds_addr(&bcdst[i * 8][0]));
     }
     if (!kStage) return;
-    // x: row r <-> token T0w - 3 + r, r < kXSeg; xrpl rows per wave-load
+    // x: row rr <-> token T0w - 3 + rr, rr < kXSeg; xrpl rows per wave-load
     constexpr int xrpl = 64 / xrow_chunks;
-    const T *xbase = xzb + (int64_t)T0w * row + ch0;
-    const int irow = (int)row;
+    const int xb = min(max(T0w - kHalo, 0), Lm1);
+    const T *xbase = xzb + (int64_t)xb * row + ch0;
+    const uint32_t rowb = (uint32_t)row * (uint32_t)sizeof(T);
 #pragma unroll
     for (int ld = 0; ld * xrpl < kXSeg; ++ld) {
       const int rr = ld * xrpl + lane / xrow_chunks;
       if (rr < kXSeg) {
-        const int r = min(max(rr - kHalo, -T0w), rmax);
-        dma16_opaque(xbase + r * irow + (lane % xrow_chunks) * xper, lds_addr(&sm.x[wv][ld * xrpl][0]));
+        const int r = min(max(T0w - kHalo + rr, 0), Lm1) - xb;
+        dma16_opaque_so(xbase, (uint32_t)r * rowb + (uint32_t)((lane % xrow_chunks) * 16),
+                        lds_addr(&sm.x[wv][ld * xrpl][0]));
       }
     }
-    {
-      const int r = min(lane / xrow_chunks, rmax);
-      dma16_opaque(xbase + a.D + r * irow + (lane % xrow_chunks) * xper, lds_addr(&sm.z[wv][0][0]));
+    if (lane < kS * xrow_chunks) {   // lanes past the segment's rows stay inactive
+      const int r = min(T0w + lane / xrow_chunks, Lm1) - tb;
+      dma16_opaque_so(xzb + (int64_t)tb * row + a.D + ch0,
+                      (uint32_t)r * rowb + (uint32_t)((lane % xrow_chunks) * 16),
+                      lds_addr(&sm.z[wv][0][0]));
     }
-    // dt (fp32): 16 rows x 128 B = 2 wave-loads, 8 lanes per row
-    const float *dbase = db + (int64_t)T0w * a.D + ch0;
+    // dt (fp32): kS rows x 128 B = kS / 8 wave-loads, 8 lanes per row
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int r = min(i * 8 + (lane >> 3), rmax);
-      dma16_opaque(dbase + r * a.D + (lane & 7) * 4, lds_addr(&sm.d[wv][i * 8][0]));
+    for (int i = 0; i < kS / 8; ++i) {
+      const int r = min(T0w + i * 8 + (lane >> 3), Lm1) - tb;
+      dma16_opaque_so(db + (int64_t)tb * a.D + ch0, (uint32_t)r * (uint32_t)a.D * 4u + (uint32_t)((lane & 7) * 16),
+                      lds_addr(&sm.d[wv][i * 8][0]));
     }
   };
 
@@ -625,15 +634,16 @@ __device__ __forceinline__ void twopass_body(const ScanArgs &a, TwoPassSmem<T> &
     wait_vmem_all();   // this wave's staged rows (and its older stores) have landed
     flush();
 
-    // ---- 1. prep: conv + SiLU, dt, dt*u, D*u, SiLU(z) for (c, segment tokens 8p..8p+7)
+    // ---- 1. prep: conv + SiLU, dt, dt*u, D*u, SiLU(z) for (c, segment tokens kS/2 p ..)
     {
-      // per-channel constants, reloaded each block (cache hits) to keep them out of the
-      // registers that live across the scan
+      // per-channel constants from the workgroup's LDS table (read per block, so that they
+      // are not held in registers across the scan)
+      const float4 c0 = *(const float4 *)&sm.cst[c][0], c1 = *(const float4 *)&sm.cst[c][4];
+      const float cv[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
       float wc[K];
 #pragma unroll
-      for (int k = 0; k < K; ++k) wc[k] = io<T>::cvt(((const T *)a.conv_w)[(int64_t)ch * K + k]);
-      const float cb = a.conv_b ? io<T>::cvt(((const T *)a.conv_b)[ch]) : 0.0f;
-      const float Dp = a.Dskip[ch];
+      for (int k = 0; k < K; ++k) wc[k] = cv[k];
+      const float cb = cv[4], Dp = cv[5];
       // segment-relative token ts (ts >= -3)
       auto getx = [&](int ts) -> float {
         if (kStage) return io<T>::cvt(sm.x[wv][kStage ? ts + kHalo : 0][c]);
@@ -647,7 +657,7 @@ __device__ __forceinline__ void twopass_body(const ScanArgs &a, TwoPassSmem<T> &
         if (kStage) return sm.d[wv][kStage ? ts : 0][c];
         return db[(int64_t)min(T0w + ts, Lm1) * a.D + ch];
       };
-      const int ts0 = 8 * p;
+      const int ts0 = (kS / 2) * p;
       float win[K - 1];
 #pragma unroll
       for (int j = 0; j < K - 1; ++j) {
@@ -662,7 +672,7 @@ __device__ __forceinline__ void twopass_body(const ScanArgs &a, TwoPassSmem<T> &
         win[j] = v;
       }
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
+      for (int e = 0; e < kS / 2; ++e) {
         const int ts = ts0 + e;
         const bool valid = T0w + ts < a.L;
         const float x = getx(ts);
@@ -723,7 +733,7 @@ __device__ __forceinline__ void twopass_body(const ScanArgs &a, TwoPassSmem<T> &
     if (!p) sm.sdt[wv][c] = sumdt;
     lds_barrier();
     // chain pass: each segment's S becomes its h_in
-    {
+    if (chain) {
       float *agg = &sm.agg[0][0][0].x;
       float Sw[kW], Pw[kW];
 #pragma unroll
@@ -782,13 +792,24 @@ __device__ __forceinline__ void twopass_body(const ScanArgs &a, TwoPassSmem<T> &
     ypend_t0 = T0;
   };
 
+  if (tid < kCh) {   // the per-channel constants table (read after the first block's barrier)
+    const int cc = ch0 + tid;
+    float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < K; ++k) v[k] = io<T>::cvt(((const T *)a.conv_w)[(int64_t)cc * K + k]);
+    v[4] = a.conv_b ? io<T>::cvt(((const T *)a.conv_b)[cc]) : 0.0f;
+    v[5] = a.Dskip[cc];
+    *(float4 *)&sm.cst[tid][0] = make_float4(v[0], v[1], v[2], v[3]);
+    *(float4 *)&sm.cst[tid][4] = make_float4(v[4], v[5], v[6], v[7]);
+  }
+  __syncthreads();
   stage(0, sm.bc[0][wv]);
   for (int blk = 0; blk < nblocks; ++blk) {
     const bool odd = blk & 1;
     block(blk, odd ? sm.bc[1] : sm.bc[0], odd ? sm.bc[0] : sm.bc[1]);
   }
   flush();
-  if (a.state) a.state[qidx] = carry;
+  if (chain && a.state) a.state[qidx] = carry;
 }
 
 template <typename T, bool ZOH, int K>
