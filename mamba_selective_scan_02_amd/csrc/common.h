@@ -122,6 +122,19 @@ __device__ __forceinline__ void dma16_opaque_so(const void *sbase, uint32_t voff
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
 }
+// A pointer to LDS from a 32-bit LDS address (the inverse of lds_addr); the compiler infers
+// the LDS address space from the cast, so accesses through it are LDS instructions.
+template <typename U>
+__device__ __forceinline__ U *lds_ptr(uint32_t addr) {
+  return (U *)(__attribute__((address_space(3))) void *)(uintptr_t)addr;
+}
+// The same LDS address, opaque to the compiler: constant offsets from it then fold into the
+// offset fields of the LDS instructions that use it. (From a loop-invariant address the
+// compiler would form every base + offset ahead of the loop and hold each in a VGPR.)
+__device__ __forceinline__ uint32_t lds_opaque(uint32_t addr) {
+  asm volatile("" : "+v"(addr));
+  return addr;
+}
 
 // ---------------------------------------------------------------- launch geometry
 // Workgroup i runs on XCD (i mod 8). Map hardware ids so that logical ids

@@ -473,130 +473,123 @@ hipError_t dispatch_lanes_k(const ScanArgs &a, hipStream_t s) {
 // scan_twopass_kernel: time-parallel scan for d_state 16 at few sequences (the 128K prefill).
 //
 // A workgroup owns kCh = 32 channels of one sequence and walks the sequence in blocks of
-// kW * kS = 128 tokens; wave w owns the 16-token segment w of every block. Lane l works on
-// channel l / 2 and the 8 states 8 (l % 2) .. +7 (8 states per lane: B_t / C_t reads from LDS
-// serve 8 updates; 256 workgroups x 8 waves = two waves per SIMD at batch 1):
+// kW * kS = 96 tokens; wave w owns the kS-token segment w of every block. 12 waves of 8
+// tokens give three waves per SIMD at batch 1 (256 workgroups): the VALU and v_exp_f32 issue
+// rates are lower at two, and at four the 128 VGPRs a wave may then hold do not keep the
+// segment's exp(dt A) without spilling. Lane l works on channel l / 2 and the 8 states
+// 8 (l % 2) .. +7 (B_t / C_t reads from LDS serve 8 updates):
 //  0. The segment's B|C rows, its x rows (with the 3 conv-window rows before it), z and dt
 //     rows were loaded into the wave's LDS rows with direct-to-LDS 16-byte loads while the
 //     previous block was computed.
-//  1. Prep: lane l takes channel l / 2 and tokens 8 (l % 2) .. +7 of the segment:
-//     u = SiLU(conv1d(x) + b), dt, dt*u, D*u and SiLU(z), once per (token, channel), into the
-//     wave's LDS rows (the wave waits on its own loads only; no workgroup barrier).
+//  1. Prep: lane l takes channel l / 2 and the segment's tokens kS/2 (l % 2) .. +kS/2-1:
+//     u = SiLU(conv1d(x) + b), dt and dt*u go to the wave's LDS rows; D*u and SiLU(z) of
+//     those tokens stay in the lane's registers for step 4 (the wave waits on its own loads
+//     only; no workgroup barrier).
 //  2. Local pass: the segment is scanned from h = 0, keeping exp(dt A) of every (token, state)
 //     in VGPRs (one exp per element, as in the sequential recurrence).
-//  3. Compose: the segment's local end state S and sum of dt go to LDS (barrier). Thread i
-//     then owns one (channel, state) chain: for each segment in order it forms the segment's
-//     decay P = exp(A sum dt) and applies the transfer h -> P h + S to the block's carry-in
-//     with the page's associative operator ("Parallel training via the parallel scan":
-//     (a, b) then (c, d) gives (ac, ad + b) for h -> a h + b), writing each segment's h_in
-//     over its S (barrier), and keeps the result as the next block's carry-in.
-//  4. Replay from the true h_in with the stored exp(dt A); y_t = C_t . h_t; the two
-//     half-sums of a channel meet by a DPP lane swap; y = (y_ssm + D u) SiLU(z) goes out.
-// Paired decay (as in the lane kernel; off with ScanArgs::general_a, never with ZOH): when
+//  3. Compose: the segment's transfer h -> P h + S (local end state S, decay
+//     P = exp(A sum dt), formed by the segment's own lanes) goes to LDS (barrier). Thread i
+//     then owns one (channel, state) chain: it applies the segments' transfers in order to
+//     the block's carry-in with the page's associative operator ("Parallel training via the
+//     parallel scan": (a, b) then (c, d) gives (ac, ad + b) for h -> a h + b), writing each
+//     segment's h_in over its S (barrier), and keeps the result as the next block's carry-in.
+//  4. Replay from the true h_in with the stored exp(dt A); y_t = C_t . h_t as two half-sums
+//     per channel, one per lane; the halves meet by a DPP lane swap, each lane keeping the
+//     tokens of its prep, and y = (y_ssm + D u) SiLU(z) goes out.
+// First-order Bbar only (the ZOH form would need expm1(dt A) and 1 / A in VGPRs besides).
+// Paired decay (as in the lane kernel; off with ScanArgs::general_a): when
 // A[i, 8 p + k] = A[i, 8 p] + k delta_i for every lane, the local pass forms a lane's 8
 // decays as exp(dt A[i, 8 p]) times powers of exp(dt delta_i): 2 exps per lane and token
 // instead of 8.
-constexpr int kCh = 32, kW = 8, kS = 16, kG = 8, kBlk = kW * kS;
+constexpr int kCh = 32, kW = 12, kS = 8, kG = 8, kBlk = kW * kS;
+constexpr int kHalf = kS / 2;             // tokens per lane in the prep and the output
 constexpr int kHalo = 3;                  // x rows before the segment (conv window, K - 1 <= 3)
-constexpr int kXSeg = kS + 4;             // staged x rows per segment: halo + segment, padded
+constexpr int kXSeg = kS + kHalo;         // x rows a segment needs: halo + segment
+constexpr int kXZR = 16;                  // staged x / z rows per wave: one 16-byte slot per lane
+static_assert(kXSeg <= kXZR && kS <= kXZR, "a wave's x and z rows fit one wave-load");
+constexpr int kChains = kCh * kN;         // (channel, state) chains of a workgroup
+static_assert(kChains == 512 && kW * 64 >= kChains, "chain threads map onto 512 agg floats");
+static_assert(kW * kS * 64 <= 65536 && kW * 4 * 64 * 16 <= 65536, "LDS offsets fit 16 bits");
 
 template <typename T>
 struct TwoPassSmem {
   // bf16 I/O stages x, z and dt through LDS; fp32 I/O (small problems) reads them from
   // global memory in the prep, which keeps its LDS within 160 KB
   static constexpr bool kStage = sizeof(T) == 2;
-  static constexpr int kXR = kStage ? kXSeg : 1, kZR = kStage ? kS : 1;
-  // per-wave staging (written by async loads); B|C double-buffered
+  static constexpr int kXR = kStage ? kXZR : 1, kZR = kStage ? kS : 1;
+  // per-wave staging (written by async loads); B|C double-buffered. Every lane of a wave
+  // issues each load (no divergent branch around them): the x and z loads fill 16 rows, the
+  // rows past those the segment needs repeating its last row
   float bc[2][kW][kS][2 * kN];
   T x[kW][kXR][kCh];
-  T z[kW][kZR][kCh];
+  T z[kW][kXR][kCh];
   float d[kW][kZR][kCh];
-  // prep outputs: (dt, dt*u or u) and (D*u, SiLU(z)) per (token, channel) of each wave's
-  // segment; rows padded by one element so that rows 8 apart fall in different LDS banks
+  // prep output: (dt, dt*u) per (token, channel) of each wave's segment; rows padded by one
+  // element so that the rows of the two lanes of a channel fall in different LDS banks
   float2 pd[kW][kS][kCh + 1];
-  float2 eg[kW][kS][kCh + 1];
-  // segment local end states, lane-contiguous 16-byte slots [wave][S0..3, S4..7][lane]
-  // (overwritten by the segments' true start states), and each segment's sum of dt
-  float4 agg[kW][2][64];
-  float sdt[kW][kCh];
+  // per segment and lane, 16-byte slots [wave][S0..3, S4..7, P0..3, P4..7][lane]: the local
+  // end states S (overwritten by the segments' true start states) and decays P = exp(A sum dt)
+  float4 agg[kW][4][64];
   float cst[kCh][8];             // per channel: conv taps (K), conv bias, D
+  float a2[kCh][kN];             // A log2(e) per (channel, state)
 };
 
-template <typename T, bool ZOH, int K, bool PAIRED>
+template <typename T, int K, bool PAIRED>
 __device__ __forceinline__ void twopass_body(const ScanArgs &a, TwoPassSmem<T> &sm, int b,
                                              int ch0) {
   constexpr bool kStage = TwoPassSmem<T>::kStage;
-  constexpr int xper = 16 / sizeof(T);                 // x/z elements per 16-byte chunk
   constexpr int xrow_chunks = kCh * sizeof(T) / 16;    // 16-byte chunks per staged x/z row
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wv = tid >> 6;
-  const int c = lane >> 1, p = lane & 1;
-  const int ch = ch0 + c;
-
-  float A2[kG], Av[kG], iA[kG];
-#pragma unroll
-  for (int j = 0; j < kG; ++j) {
-    Av[j] = a.A[(int64_t)ch * kN + kG * p + j];
-    A2[j] = Av[j] * kLog2e;
-    iA[j] = 1.0f / Av[j];
+  constexpr uint32_t kPdRow = (kCh + 1) * sizeof(float2), kBcRow = 2 * kN * sizeof(float);
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
+  // chain thread tid (waves 0-7) <-> publishing lane ql = (tid >> 2) & 63 (channel ql / 2,
+  // state half ql & 1), state j = 4 (tid >> 8) + (tid & 3) of that half: its S and P of
+  // segment w are floats w * 1024 + tid and w * 1024 + 512 + tid of agg (conflict-free)
+  const bool chain = wv < kChains / 64;
+  float carry = 0.f;
+  if (chain && a.state_valid && a.state) {
+    const int tid = threadIdx.x, ql = (tid >> 2) & 63, qj = 4 * ((tid >> 8) & 1) + (tid & 3);
+    carry = a.state[((int64_t)b * a.D + ch0 + (ql >> 1)) * kN + kG * (ql & 1) + qj];
   }
-  const float dl2 = PAIRED ? (Av[1] - Av[0]) * kLog2e : 0.f;
-  // chain thread tid <-> publishing lane ql = (tid >> 2) & 63 (channel ql / 2, state half
-  // ql & 1), state j = 4 (tid >> 8) + (tid & 3) of that half: its S of segment w is float
-  // w * 512 + tid of agg (conflict-free, lane-contiguous)
-  // (threads 512 and up, when kW > 8, own no chain)
-  const bool chain = tid < 512;
-  const int ql = (tid >> 2) & 63, qj = 4 * ((tid >> 8) & 1) + (tid & 3);
-  const int64_t qidx = ((int64_t)b * a.D + ch0 + (ql >> 1)) * kN + kG * (ql & 1) + qj;
-  const float qA2 = a.A[(int64_t)(ch0 + (ql >> 1)) * kN + kG * (ql & 1) + qj] * kLog2e;
-  float carry = (chain && a.state_valid && a.state) ? a.state[qidx] : 0.f;
+  const float dl2 = PAIRED ? (a.A[(ch0 + (threadIdx.x & 63) / 2) * kN + kG * (threadIdx.x & 1) + 1] -
+                              a.A[(ch0 + (threadIdx.x & 63) / 2) * kN + kG * (threadIdx.x & 1)]) * kLog2e
+                           : 0.f;
 
   const int64_t row = 2LL * a.D;
   const T *xzb = (const T *)a.xz + (int64_t)b * a.L * row;
   const float *db = a.delta + (int64_t)b * a.L * a.D;
   const float *bcb = a.bc + (int64_t)b * a.L * 2 * kN;
   T *yb = (T *)a.y + (int64_t)b * a.L * a.D;
-  // this lane's 16-byte slot of a staged B|C row: slots 0-3 B, 4-7 C
-  const int bcoff = 4 * (lane & 7);
   const int nblocks = (a.L + kBlk - 1) / kBlk;
   const int Lm1 = a.L - 1;
 
-  // Issue the direct-to-LDS loads of this wave's segment of block `blk`. Rows outside
-  // [0, L) read the nearest valid row (every address is valid; prep and the scan ignore
-  // those rows).
-  auto stage = [&](int blk, float (*bcdst)[2 * kN]) {
+  // Issue the direct-to-LDS loads of this wave's segment of block `blk` (lane = this lane).
+  // Rows outside [0, L) read the nearest valid row (every address is valid; prep and the scan
+  // ignore those rows).
+  auto stage = [&](int blk, float (*bcdst)[2 * kN], int lane) {
     // wave-uniform bases (SGPRs) and 32-bit lane offsets, so that no 64-bit address lives in
     // VGPRs across the block; rows outside [0, L) are clamped into it
     const int T0w = blk * kBlk + wv * kS;
     const int tb = min(T0w, Lm1);                 // first staged row of B|C, z, dt
-    // B|C: kS rows x 128 B = kS / 8 wave-loads, 8 lanes per row
+    // B|C: kS rows x 128 B = kS / 8 wave-loads, 8 lanes per row; slots 0-3 B, 4-7 C
 #pragma unroll
     for (int i = 0; i < kS / 8; ++i) {
       const int r = min(T0w + i * 8 + (lane >> 3), Lm1) - tb;
-      dma16_opaque_so(bcb + (int64_t)tb * 2 * kN, (uint32_t)(r * 2 * kN + bcoff) * 4u,
+      dma16_opaque_so(bcb + (int64_t)tb * 2 * kN, (uint32_t)(r * 2 * kN + 4 * (lane & 7)) * 4u,
                       lds_addr(&bcdst[i * 8][0]));
     }
     if (!kStage) return;
-    // x: row rr <-> token T0w - 3 + rr, rr < kXSeg; xrpl rows per wave-load
-    constexpr int xrpl = 64 / xrow_chunks;
-    const int xb = min(max(T0w - kHalo, 0), Lm1);
-    const T *xbase = xzb + (int64_t)xb * row + ch0;
+    // x: row rr <-> token T0w - 3 + rr (rr < kXSeg); z: row rr <-> token T0w + rr (rr < kS)
+    static_assert(!kStage || 64 / xrow_chunks == kXZR, "one wave-load covers kXZR rows");
+    const int rr = lane / xrow_chunks;
     const uint32_t rowb = (uint32_t)row * (uint32_t)sizeof(T);
-#pragma unroll
-    for (int ld = 0; ld * xrpl < kXSeg; ++ld) {
-      const int rr = ld * xrpl + lane / xrow_chunks;
-      if (rr < kXSeg) {
-        const int r = min(max(T0w - kHalo + rr, 0), Lm1) - xb;
-        dma16_opaque_so(xbase, (uint32_t)r * rowb + (uint32_t)((lane % xrow_chunks) * 16),
-                        lds_addr(&sm.x[wv][ld * xrpl][0]));
-      }
-    }
-    if (lane < kS * xrow_chunks) {   // lanes past the segment's rows stay inactive
-      const int r = min(T0w + lane / xrow_chunks, Lm1) - tb;
-      dma16_opaque_so(xzb + (int64_t)tb * row + a.D + ch0,
-                      (uint32_t)r * rowb + (uint32_t)((lane % xrow_chunks) * 16),
-                      lds_addr(&sm.z[wv][0][0]));
-    }
+    const uint32_t cb16 = (uint32_t)((lane % xrow_chunks) * 16);
+    const int xb = min(max(T0w - kHalo, 0), Lm1);
+    const int rx = min(max(T0w - kHalo + min(rr, kXSeg - 1), 0), Lm1) - xb;
+    dma16_opaque_so(xzb + (int64_t)xb * row + ch0, (uint32_t)rx * rowb + cb16,
+                    lds_addr(&sm.x[wv][0][0]));
+    const int rz = min(T0w + min(rr, kS - 1), Lm1) - tb;
+    dma16_opaque_so(xzb + (int64_t)tb * row + a.D + ch0, (uint32_t)rz * rowb + cb16,
+                    lds_addr(&sm.z[wv][0][0]));
     // dt (fp32): kS rows x 128 B = kS / 8 wave-loads, 8 lanes per row
 #pragma unroll
     for (int i = 0; i < kS / 8; ++i) {
@@ -608,36 +601,47 @@ __device__ __forceinline__ void twopass_body(const ScanArgs &a, TwoPassSmem<T> &
 
   // y of block b is stored at the start of block b+1, after that block's wait, so the wait
   // for the staged tiles never has to cover freshly issued stores. Lane (c, p) owns tokens
-  // 2i + p of its wave's segment.
-  float ypend[kS / 2];
+  // kHalf p .. kHalf p + kHalf - 1 of its wave's segment.
+  float ypend[kHalf];
   int ypend_t0 = -1;
-  auto flush = [&]() {
+  auto flush = [&](int c, int p) {
     if (ypend_t0 < 0) return;
     T *ybase = yb + (int64_t)(ypend_t0 + wv * kS) * a.D;   // wave-uniform, 32-bit lane offsets
-    // the lane offsets are formed here, per block: held across the block (the compiler's
-    // choice otherwise) they would take 16 more VGPRs than the kernel has
-    uint32_t off = (uint32_t)(p * a.D + ch);
-    asm volatile("" : "+v"(off));
-    const uint32_t step = 2u * (uint32_t)a.D;
+    const uint32_t off = (uint32_t)(p * kHalf * a.D + ch0 + c);
+    const uint32_t step = (uint32_t)a.D;
     if (ypend_t0 + kBlk <= a.L) {
 #pragma unroll
-      for (int i = 0; i < kS / 2; ++i) io<T>::st(ybase + off + i * step, ypend[i]);
+      for (int i = 0; i < kHalf; ++i) io<T>::st(ybase + off + i * step, ypend[i]);
     } else {
 #pragma unroll
-      for (int i = 0; i < kS / 2; ++i)
-        if (ypend_t0 + wv * kS + 2 * i + p < a.L) io<T>::st(ybase + off + i * step, ypend[i]);
+      for (int i = 0; i < kHalf; ++i)
+        if (ypend_t0 + wv * kS + kHalf * p + i < a.L) io<T>::st(ybase + off + i * step, ypend[i]);
     }
   };
   auto block = [&](int blk, float (*bc_cur)[kS][2 * kN], float (*bc_nxt)[kS][2 * kN]) {
     const int T0 = blk * kBlk;
     const int T0w = T0 + wv * kS;
+    // Lane-dependent values are re-formed per block from an opaque copy of the thread id:
+    // held across the block loop (the compiler's choice for loop-invariant values) they
+    // would take VGPRs the scan needs.
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int lane = tid & 63, c = lane >> 1, p = lane & 1, ch = ch0 + c;
     wait_vmem_all();   // this wave's staged rows (and its older stores) have landed
-    flush();
+    flush(c, p);
+    // this lane's LDS rows: (dt, dt*u) column, B|C slot
+    const uint32_t pdl = lds_addr(&sm.pd[wv][0][c]);
+    const uint32_t bcl = lds_addr(&bc_cur[wv][0][kG * p]);
+    auto pd_at = [&](int t) -> float2 { return *lds_ptr<const float2>(pdl + t * kPdRow); };
+    auto du_at = [&](int t) -> float { return *lds_ptr<const float>(pdl + t * kPdRow + 4); };
+    auto b4_at = [&](int t, int q) -> float4 {   // q = 0, 1: B; 2, 3: C
+      return *lds_ptr<const float4>(bcl + t * kBcRow + (q & 1) * 16 + (q >> 1) * kN * 4);
+    };
 
-    // ---- 1. prep: conv + SiLU, dt, dt*u, D*u, SiLU(z) for (c, segment tokens kS/2 p ..)
+    // ---- 1. prep: conv + SiLU, dt, dt*u into LDS; D*u, SiLU(z) kept for the output
+    float eDu[kHalf], eg[kHalf];
     {
-      // per-channel constants from the workgroup's LDS table (read per block, so that they
-      // are not held in registers across the scan)
+      // per-channel constants from the workgroup's LDS table
       const float4 c0 = *(const float4 *)&sm.cst[c][0], c1 = *(const float4 *)&sm.cst[c][4];
       const float cv[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
       float wc[K];
@@ -645,34 +649,42 @@ __device__ __forceinline__ void twopass_body(const ScanArgs &a, TwoPassSmem<T> &
       for (int k = 0; k < K; ++k) wc[k] = cv[k];
       const float cb = cv[4], Dp = cv[5];
       // segment-relative token ts (ts >= -3)
+      const uint32_t xl = lds_addr(&sm.x[wv][0][c]);
+      const uint32_t zl = lds_addr(&sm.z[wv][0][c]);
+      const uint32_t dl = lds_addr(&sm.d[wv][0][c]);
       auto getx = [&](int ts) -> float {
-        if (kStage) return io<T>::cvt(sm.x[wv][kStage ? ts + kHalo : 0][c]);
+        if (kStage) return io<T>::cvt(*lds_ptr<const T>(xl + (ts + kHalo) * kCh * sizeof(T)));
         return io<T>::cvt(xzb[(int64_t)min(T0w + ts, Lm1) * row + ch]);
       };
       auto getz = [&](int ts) -> float {
-        if (kStage) return io<T>::cvt(sm.z[wv][kStage ? ts : 0][c]);
+        if (kStage) return io<T>::cvt(*lds_ptr<const T>(zl + ts * kCh * sizeof(T)));
         return io<T>::cvt(xzb[(int64_t)min(T0w + ts, Lm1) * row + a.D + ch]);
       };
       auto getd = [&](int ts) -> float {
-        if (kStage) return sm.d[wv][kStage ? ts : 0][c];
+        if (kStage) return *lds_ptr<const float>(dl + ts * kCh * 4);
         return db[(int64_t)min(T0w + ts, Lm1) * a.D + ch];
       };
-      const int ts0 = (kS / 2) * p;
+      const int ts0 = kHalf * p;
       float win[K - 1];
+      if (T0w >= kHalo) {   // wave-uniform: every window row is a row of this sequence
 #pragma unroll
-      for (int j = 0; j < K - 1; ++j) {
-        const int ts = ts0 - (K - 1) + j;         // segment-relative token of this window row
-        const int t = T0w + ts;
-        float v = 0.f;
-        if (t >= 0) {
-          v = getx(ts);
-        } else if (a.conv_valid && a.conv_state) {
-          v = io<T>::cvt(((const T *)a.conv_state)[((int64_t)b * a.D + ch) * (K - 1) + (K - 1) + t]);
+        for (int j = 0; j < K - 1; ++j) win[j] = getx(ts0 - (K - 1) + j);
+      } else {              // the first segment: rows before token 0 come from the conv state
+#pragma unroll
+        for (int j = 0; j < K - 1; ++j) {
+          const int ts = ts0 - (K - 1) + j;       // segment-relative token of this window row
+          const int t = T0w + ts;
+          float v = 0.f;
+          if (t >= 0) {
+            v = getx(ts);
+          } else if (a.conv_valid && a.conv_state) {
+            v = io<T>::cvt(((const T *)a.conv_state)[((int64_t)b * a.D + ch) * (K - 1) + (K - 1) + t]);
+          }
+          win[j] = v;
         }
-        win[j] = v;
       }
 #pragma unroll
-      for (int e = 0; e < kS / 2; ++e) {
+      for (int e = 0; e < kHalf; ++e) {
         const int ts = ts0 + e;
         const bool valid = T0w + ts < a.L;
         const float x = getx(ts);
@@ -688,62 +700,67 @@ __device__ __forceinline__ void twopass_body(const ScanArgs &a, TwoPassSmem<T> &
         // input), and those tokens' outputs are never stored. Staged rows there hold copies of
         // row L-1, so u and z stay finite.
         const float dt = valid ? getd(ts) : 0.f;
-        const float z = getz(ts);
-        // ZOH replays Bbar u = expm1(dt A)/A * B * u, so it keeps u where Euler keeps dt*u
-        sm.pd[wv][ts][c] = make_float2(dt, ZOH ? u : dt * u);
-        sm.eg[wv][ts][c] = make_float2(Dp * u, silu_f(z));
+        *lds_ptr<float2>(pdl + ts * kPdRow) = make_float2(dt, dt * u);
+        eDu[e] = Dp * u;
+        eg[e] = silu_f(getz(ts));
       }
     }
     // the staged x, z, dt rows are consumed once this wave's LDS reads have returned; then the
     // next block's rows may land (B|C is double-buffered)
     __builtin_amdgcn_s_waitcnt(0xC07F);           // lgkmcnt(0), vmcnt / expcnt unconstrained
-    if (blk + 1 < nblocks) stage(blk + 1, bc_nxt[wv]);
+    if (blk + 1 < nblocks) stage(blk + 1, bc_nxt[wv], lane);
 
     // ---- 2. local pass over this wave's segment
+    float A2[kG];
+    {
+      const float4 q0 = *(const float4 *)&sm.a2[c][kG * p], q1 = *(const float4 *)&sm.a2[c][kG * p + 4];
+      A2[0] = q0.x; A2[1] = q0.y; A2[2] = q0.z; A2[3] = q0.w;
+      A2[4] = q1.x; A2[5] = q1.y; A2[6] = q1.z; A2[7] = q1.w;
+    }
     float dA[kS][kG];
     float hl[kG];
-#pragma unroll
-    for (int j = 0; j < kG; ++j) hl[j] = 0.f;
     float sumdt = 0.f;
 #pragma unroll
     for (int t = 0; t < kS; ++t) {
-      const float2 pd = sm.pd[wv][t][c];
+      const float2 pd = pd_at(t);
       const float dt = pd.x, du = pd.y;
       sumdt += dt;
-      const float4 B0 = *(const float4 *)&bc_cur[wv][t][kG * p];
-      const float4 B1 = *(const float4 *)&bc_cur[wv][t][kG * p + 4];
+      const float4 B0 = b4_at(t, 0), B1 = b4_at(t, 1);
       const float Bv[kG] = {B0.x, B0.y, B0.z, B0.w, B1.x, B1.y, B1.z, B1.w};
       float e1 = 0.f;
       if (PAIRED) e1 = exp2_hw(dt * dl2);
 #pragma unroll
       for (int j = 0; j < kG; ++j) {
-        if (ZOH) {
-          const float em1 = expm1_f(dt * Av[j]);
-          dA[t][j] = em1;  // ZOH keeps expm1(dt A); exp(dt A) = 1 + it
-          hl[j] = __builtin_fmaf(em1 + 1.0f, hl[j], em1 * iA[j] * Bv[j] * du);
-        } else {
-          dA[t][j] = (PAIRED && j > 0) ? dA[t][j - 1] * e1 : exp2_hw(dt * A2[j]);
-          hl[j] = __builtin_fmaf(dA[t][j], hl[j], du * Bv[j]);
-        }
+        dA[t][j] = (PAIRED && j > 0) ? dA[t][j - 1] * e1 : exp2_hw(dt * A2[j]);
+        // the segment starts from h = 0
+        hl[j] = t == 0 ? du * Bv[j] : __builtin_fmaf(dA[t][j], hl[j], du * Bv[j]);
       }
     }
-    // ---- 3. publish this segment's local end state and sum of dt, then compose
+    // ---- 3. publish this segment's transfer h -> P h + S, then compose
     sm.agg[wv][0][lane] = make_float4(hl[0], hl[1], hl[2], hl[3]);
     sm.agg[wv][1][lane] = make_float4(hl[4], hl[5], hl[6], hl[7]);
-    if (!p) sm.sdt[wv][c] = sumdt;
+    {
+      float P[kG];
+#pragma unroll
+      for (int j = 0; j < kG; ++j) P[j] = exp2_hw(A2[j] * sumdt);
+      sm.agg[wv][2][lane] = make_float4(P[0], P[1], P[2], P[3]);
+      sm.agg[wv][3][lane] = make_float4(P[4], P[5], P[6], P[7]);
+    }
     lds_barrier();
-    // chain pass: each segment's S becomes its h_in
+    // chain pass: each segment's S becomes its h_in (all reads in flight together, then the
+    // dependent fmas)
     if (chain) {
-      float *agg = &sm.agg[0][0][0].x;
+      const uint32_t al = lds_addr(&sm.agg[0][0][0].x) + 4u * tid;
+      constexpr uint32_t kSeg = 4 * 64 * 16;      // bytes per segment in agg
       float Sw[kW], Pw[kW];
 #pragma unroll
       for (int w2 = 0; w2 < kW; ++w2) {
-        Sw[w2] = agg[w2 * 512 + tid];
-        Pw[w2] = exp2_hw(qA2 * sm.sdt[w2][ql >> 1]);
+        Sw[w2] = *lds_ptr<const float>(al + w2 * kSeg);
+        Pw[w2] = *lds_ptr<const float>(al + w2 * kSeg + kChains * 4);
       }
 #pragma unroll
       for (int w2 = 0; w2 < kW; ++w2) {
-        agg[w2 * 512 + tid] = carry;
+        *lds_ptr<float>(al + w2 * kSeg) = carry;
         carry = __builtin_fmaf(Pw[w2], carry, Sw[w2]);
       }
     }
@@ -755,90 +772,99 @@ __device__ __forceinline__ void twopass_body(const ScanArgs &a, TwoPassSmem<T> &
       h[4] = H1.x; h[5] = H1.y; h[6] = H1.z; h[7] = H1.w;
     }
     // ---- 4. replay from the true h_in; y from the two half-sums of the channel
+    float ys[kHalf];
 #pragma unroll
-    for (int t = 0; t < kS; t += 2) {
-      float ys[2];
+    for (int t = 0; t < kS; ++t) {
+      const float4 B0 = b4_at(t, 0), B1 = b4_at(t, 1), C0 = b4_at(t, 2), C1 = b4_at(t, 3);
+      const float Bv[kG] = {B0.x, B0.y, B0.z, B0.w, B1.x, B1.y, B1.z, B1.w};
+      const float Cv[kG] = {C0.x, C0.y, C0.z, C0.w, C1.x, C1.y, C1.z, C1.w};
+      const float du = du_at(t);
+      float yy = 0.f;
 #pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int ts = t + e;
-        const float4 B0 = *(const float4 *)&bc_cur[wv][ts][kG * p];
-        const float4 B1 = *(const float4 *)&bc_cur[wv][ts][kG * p + 4];
-        const float4 C0 = *(const float4 *)&bc_cur[wv][ts][kN + kG * p];
-        const float4 C1 = *(const float4 *)&bc_cur[wv][ts][kN + kG * p + 4];
-        const float Bv[kG] = {B0.x, B0.y, B0.z, B0.w, B1.x, B1.y, B1.z, B1.w};
-        const float Cv[kG] = {C0.x, C0.y, C0.z, C0.w, C1.x, C1.y, C1.z, C1.w};
-        const float du = sm.pd[wv][ts][c].y;
-        float yy = 0.f;
-#pragma unroll
-        for (int j = 0; j < kG; ++j) {
-          if (ZOH) {
-            const float em1 = dA[ts][j];
-            h[j] = __builtin_fmaf(em1 + 1.0f, h[j], em1 * iA[j] * Bv[j] * du);
-          } else {
-            h[j] = __builtin_fmaf(dA[ts][j], h[j], du * Bv[j]);
-          }
-          yy = __builtin_fmaf(Cv[j], h[j], yy);
-        }
-        ys[e] = yy;
+      for (int j = 0; j < kG; ++j) {
+        h[j] = __builtin_fmaf(dA[t][j], h[j], du * Bv[j]);
+        yy = __builtin_fmaf(Cv[j], h[j], yy);
       }
-      // lane p keeps token t+p: its own half-sum plus the partner lane's half-sum of it
-      const float keep = p ? ys[1] : ys[0];
-      const float send = p ? ys[0] : ys[1];
-      const float other = __builtin_bit_cast(
-          float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, send), 0xB1, 0xF, 0xF, false));
-      const float2 eg = sm.eg[wv][t + p][c];
-      ypend[t / 2] = (keep + other + eg.x) * eg.y;
+      if (t < kHalf) {
+        ys[t] = yy;
+      } else {
+        // lane p keeps token kHalf p + e: its own half-sum plus the partner lane's half-sum
+        const int e = t - kHalf;
+        const float keep = p ? yy : ys[e];
+        const float send = p ? ys[e] : yy;
+        const float other = __builtin_bit_cast(
+            float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, send), 0xB1, 0xF, 0xF, false));
+        ypend[e] = (keep + other + eDu[e]) * eg[e];
+      }
     }
     ypend_t0 = T0;
   };
 
-  if (tid < kCh) {   // the per-channel constants table (read after the first block's barrier)
-    const int cc = ch0 + tid;
-    float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  {
+    const int tid = threadIdx.x;
+    if (tid < kCh) {   // the per-channel constants table (read after the first barrier)
+      const int cc = ch0 + tid;
+      float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int k = 0; k < K; ++k) v[k] = io<T>::cvt(((const T *)a.conv_w)[(int64_t)cc * K + k]);
-    v[4] = a.conv_b ? io<T>::cvt(((const T *)a.conv_b)[cc]) : 0.0f;
-    v[5] = a.Dskip[cc];
-    *(float4 *)&sm.cst[tid][0] = make_float4(v[0], v[1], v[2], v[3]);
-    *(float4 *)&sm.cst[tid][4] = make_float4(v[4], v[5], v[6], v[7]);
+      for (int k = 0; k < K; ++k) v[k] = io<T>::cvt(((const T *)a.conv_w)[(int64_t)cc * K + k]);
+      v[4] = a.conv_b ? io<T>::cvt(((const T *)a.conv_b)[cc]) : 0.0f;
+      v[5] = a.Dskip[cc];
+      *(float4 *)&sm.cst[tid][0] = make_float4(v[0], v[1], v[2], v[3]);
+      *(float4 *)&sm.cst[tid][4] = make_float4(v[4], v[5], v[6], v[7]);
+    }
+    if (tid < kCh * kN) sm.a2[tid / kN][tid % kN] = a.A[(int64_t)ch0 * kN + tid] * kLog2e;
+    __syncthreads();
+    stage(0, sm.bc[0][wv], tid & 63);
   }
-  __syncthreads();
-  stage(0, sm.bc[0][wv]);
   for (int blk = 0; blk < nblocks; ++blk) {
     const bool odd = blk & 1;
     block(blk, odd ? sm.bc[1] : sm.bc[0], odd ? sm.bc[0] : sm.bc[1]);
   }
-  flush();
-  if (chain && a.state) a.state[qidx] = carry;
+  {
+    const int tid = threadIdx.x;
+    flush((tid & 63) >> 1, tid & 1);
+    if (chain && a.state) {
+      const int ql = (tid >> 2) & 63, qj = 4 * ((tid >> 8) & 1) + (tid & 3);
+      a.state[((int64_t)b * a.D + ch0 + (ql >> 1)) * kN + kG * (ql & 1) + qj] = carry;
+    }
+  }
 }
 
-template <typename T, bool ZOH, int K>
+// DETECT: look for paired decay (A given as -(n + 1) per state, or any equal step per lane);
+// off when the caller declares A general, which also leaves the paired path out of the kernel
+// (its registers would otherwise count against the general path's)
+template <typename T, int K, bool DETECT>
 __global__ __launch_bounds__(kW * 64) void scan_twopass_kernel(ScanArgs a) {
-  static_assert(!ZOH, "the two-pass kernel takes first-order Bbar only");
   __shared__ __attribute__((aligned(16))) TwoPassSmem<T> sm;
   const int groups = a.D / kCh;
   const int gid = xcd_remap(blockIdx.x, gridDim.x);
-  const int b = gid / groups, ch0 = (gid % groups) * kCh;
-  {
+  // workgroup-uniform (readfirstlane keeps the bases derived from them in SGPRs)
+  const int b = __builtin_amdgcn_readfirstlane(gid / groups);
+  const int ch0 = __builtin_amdgcn_readfirstlane((gid % groups) * kCh);
+  if (DETECT) {
     // paired decay: every lane's 8 states in arithmetic progression with the channel's step
     const int lane = threadIdx.x & 63;
     const int ch = ch0 + (lane >> 1), n0 = kG * (lane & 1);
     const float *Ar = a.A + (int64_t)ch * kN;
     const float dl = Ar[1] - Ar[0];
-    int ok = !a.general_a;
+    int ok = 1;
 #pragma unroll
     for (int s = 1; s < kG; ++s) ok &= (Ar[n0 + s] - Ar[n0] == (float)s * dl);
-    if (__syncthreads_and(ok))
-      twopass_body<T, ZOH, K, true>(a, sm, b, ch0);
-    else
-      twopass_body<T, ZOH, K, false>(a, sm, b, ch0);
+    if (__syncthreads_and(ok)) {
+      twopass_body<T, K, true>(a, sm, b, ch0);
+      return;
+    }
   }
+  twopass_body<T, K, false>(a, sm, b, ch0);
 }
 
 template <typename T, int K>
 hipError_t dispatch_twopass_k(const ScanArgs &a, hipStream_t s) {
   const unsigned blocks = (unsigned)((int64_t)a.B * (a.D / kCh));
-  hipLaunchKernelGGL((scan_twopass_kernel<T, false, K>), dim3(blocks), dim3(kW * 64), 0, s, a);
+  if (a.general_a)
+    hipLaunchKernelGGL((scan_twopass_kernel<T, K, false>), dim3(blocks), dim3(kW * 64), 0, s, a);
+  else
+    hipLaunchKernelGGL((scan_twopass_kernel<T, K, true>), dim3(blocks), dim3(kW * 64), 0, s, a);
   return hipGetLastError();
 }
 
