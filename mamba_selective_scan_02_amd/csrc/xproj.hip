@@ -15,9 +15,10 @@
 //         chunk i in fp32 (the 4-tap conv as two packed bf16 dot products per channel), split
 //         it as u = hi + lo (both bf16) and write both into LDS; they also issue the
 //         direct-to-LDS loads of the x rows, conv taps and W_x rows of chunk i + 2;
-//       - consumer waves 8..15 multiply chunk i - 1: wave 8 + c owns tokens 16c .. 16c+15 and
-//         every output row, two MFMAs (u_lo, u_hi) per W fragment, so the product carries u
-//         to ~2^-17 relative.
+//       - consumer waves 8..15 multiply chunk i - 1: wave 8 + c owns tokens 32 (c % 4) .. +31
+//         and one half of the output rows, two MFMAs (u_lo, u_hi) per W fragment and token
+//         block (each W fragment read from LDS feeds four), so the product carries u to
+//         ~2^-17 relative.
 //     Each SIMD runs two producer and two consumer waves (<= 128 VGPRs each), so the VALU
 //     work of one role overlaps the MFMAs of the other.
 //     W_x chunks are 4-deep buffered, x rows (128 B = two chunks per stage) 2-deep, u
@@ -25,8 +26,9 @@
 //     with lane i's 16 bytes at 16 i), so every fragment read is one contiguous,
 //     bank-conflict-free 1 KB access; x rows have their 16-byte slots XOR-swizzled by row.
 //   * Epilogue (consumers): lane (token, 4 consecutive outputs per 16-wide block) squares and
-//     sums its dt_low / B / C values, the 4 lanes of a token reduce by lane shuffles, and the
-//     normalised dt_low (as bf16 hi + lo for dt_proj) and B|C (fp32) are written.
+//     sums its dt_low / B / C values, the 4 lanes of a token reduce by lane shuffles, the two
+//     halves' sums meet through LDS, and the normalised dt_low (as bf16 hi + lo for dt_proj)
+//     and B|C (fp32) are written.
 #include "common.h"
 #include "kernels.h"
 
@@ -67,6 +69,7 @@ __global__ __launch_bounds__(1024) void xproj_fused_kernel(XprojFusedArgs a) {
   __shared__ __attribute__((aligned(16))) bf16_t u_s[2][2][kTok / 16][64 * 8];  // [buf][hi, lo]
   __shared__ __attribute__((aligned(16))) bf16_t cw_s[3][kKC * 4];       // conv taps [ch][4]
   __shared__ __attribute__((aligned(16))) bf16_t cb_s[3][kKC];           // conv bias
+  __shared__ __attribute__((aligned(16))) float ss_s[8][32][4];           // consumers' sums
 
   const int tiles_per_seq = (a.L + kTok - 1) / kTok;
   const int gid = xcd_remap(blockIdx.x, gridDim.x);
@@ -189,37 +192,48 @@ __global__ __launch_bounds__(1024) void xproj_fused_kernel(XprojFusedArgs a) {
     }
   };
 
-  // ---- consumer: wave 8 + cw, tokens 16 cw .. +15 (one MFMA column block)
-  constexpr int TB = 1;
+  // ---- consumer: wave 8 + cw owns tokens 32 (cw & 3) .. +31 (two MFMA column blocks) and the
+  // output blocks of half og = cw >> 2 (blocks og NB0 .. og NB0 + nbn - 1), so every W_x
+  // fragment read from LDS feeds four MFMAs
+  constexpr int TB = 2;
+  constexpr int NB0 = (NB + 1) / 2;              // blocks in the first half (the second: NB - NB0)
   const int cw = wv - 8;
+  const int tg = cw & 3, og = cw >> 2;
+  const int nb0 = og * NB0, nbn = og ? NB - NB0 : NB0;
   const int tl = lane & 15, g = lane >> 4;
-  f32x4 acc[TB][NB];
+  f32x4 acc[TB][NB0];
 #pragma unroll
   for (int tb = 0; tb < TB; ++tb)
 #pragma unroll
-    for (int i = 0; i < NB; ++i) acc[tb][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < NB0; ++i) acc[tb][i] = f32x4{0.f, 0.f, 0.f, 0.f};
   auto consume = [&](int ck) {
     const int ub = ck & 1, b4 = ck & 3;
     bf16x8 fh[TB], fl[TB];
 #pragma unroll
     for (int tb = 0; tb < TB; ++tb) {
-      const int cb = cw * TB + tb;
+      const int cb = tg * TB + tb;
       fh[tb] = __builtin_bit_cast(bf16x8, *(const uint4 *)&u_s[ub][0][cb][lane * 8]);
       fl[tb] = __builtin_bit_cast(bf16x8, *(const uint4 *)&u_s[ub][1][cb][lane * 8]);
     }
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const bf16x8 fw = __builtin_bit_cast(bf16x8, *(const uint4 *)&w_s[b4][nb][lane * 8]);
+    for (int i = 0; i < NB0; ++i) {
+      if (i < nbn) {   // wave-uniform
+        const bf16x8 fw = __builtin_bit_cast(bf16x8, *(const uint4 *)&w_s[b4][nb0 + i][lane * 8]);
 #pragma unroll
-      for (int tb = 0; tb < TB; ++tb) {
-        acc[tb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fw, fl[tb], acc[tb][nb], 0, 0, 0);
-        acc[tb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fw, fh[tb], acc[tb][nb], 0, 0, 0);
+        for (int tb = 0; tb < TB; ++tb) {
+          acc[tb][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fw, fl[tb], acc[tb][i], 0, 0, 0);
+          acc[tb][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fw, fh[tb], acc[tb][i], 0, 0, 0);
+        }
       }
     }
   };
 
   // The two roles run separate loops with the same barrier count (nck + 1), so the consumers'
-  // accumulators are not live in the producers' code.
+  // accumulators are not live in the producers' code; one more barrier (every wave) passes the
+  // consumers' partial sums of squares between the two output halves of each token.
+  // acc[tb][i][j] = xdbl[token (tg TB + tb) 16 + tl][(nb0 + i) 16 + 4 g + j]; the B | C column
+  // of block nb >= RB is (nb - RB) 16 + 4 g (B below N)
+  auto bcol = [&](int nb) { return (nb - RB) * 16 + 4 * g; };
   if (producer) {
     issue(0);
     if (nck > 1) issue(1);
@@ -235,60 +249,75 @@ __global__ __launch_bounds__(1024) void xproj_fused_kernel(XprojFusedArgs a) {
       if (it + 2 < nck) issue(it + 2);
       if (it < nck) produce(it);
     }
-    return;
+  } else {
+    for (int it = 0; it <= nck; ++it) {
+      lds_barrier();
+      if (it > 0) consume(it - 1);
+    }
+    // this half's sums of squares of dt_low, B and C per token (the 4 lanes of a token are
+    // l % 16 + 16 {0, 1, 2, 3})
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) {
+      float ssd = 0.f, ssb = 0.f, ssc = 0.f;
+#pragma unroll
+      for (int i = 0; i < NB0; ++i) {
+        if (i < nbn) {
+          const int nb = nb0 + i;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float v = acc[tb][i][j];
+            if (nb < RB) ssd = __builtin_fmaf(v, v, ssd);
+            else if (bcol(nb) < N) ssb = __builtin_fmaf(v, v, ssb);
+            else ssc = __builtin_fmaf(v, v, ssc);
+          }
+        }
+      }
+      ssd += __shfl_xor(ssd, 16, 64); ssd += __shfl_xor(ssd, 32, 64);
+      ssb += __shfl_xor(ssb, 16, 64); ssb += __shfl_xor(ssb, 32, 64);
+      ssc += __shfl_xor(ssc, 16, 64); ssc += __shfl_xor(ssc, 32, 64);
+      if (g == 0) *(float4 *)&ss_s[cw][tb * 16 + tl][0] = make_float4(ssd, ssb, ssc, 0.f);
+    }
   }
-  for (int it = 0; it <= nck; ++it) {
-    lds_barrier();
-    if (it > 0) consume(it - 1);
-  }
+  lds_barrier();
+  if (producer) return;
 
-  // ---- epilogue: acc[tb][nb][j] = xdbl[token (cw*TB + tb)*16 + tl][nb*16 + 4g + j]
-  // B | C column of this lane's 4 values in block nb >= RB; they are B's when below N
-  auto bcol = [&](int nb) { return (nb - RB) * 16 + 4 * g; };
+  // ---- epilogue: both halves' sums (first half + second half, the same order in both
+  // waves), the three RMSNorms, and this half's outputs
 #pragma unroll
   for (int tb = 0; tb < TB; ++tb) {
-    float ssd = 0.f, ssb = 0.f, ssc = 0.f;
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float v = acc[tb][nb][j];
-        if (nb < RB) ssd = __builtin_fmaf(v, v, ssd);
-        else if (bcol(nb) < N) ssb = __builtin_fmaf(v, v, ssb);
-        else ssc = __builtin_fmaf(v, v, ssc);
-      }
-    // the 4 lanes of a token are l%16 + 16 * {0, 1, 2, 3}
-    ssd += __shfl_xor(ssd, 16, 64); ssd += __shfl_xor(ssd, 32, 64);
-    ssb += __shfl_xor(ssb, 16, 64); ssb += __shfl_xor(ssb, 32, 64);
-    ssc += __shfl_xor(ssc, 16, 64); ssc += __shfl_xor(ssc, 32, 64);
+    const float4 s0 = *(const float4 *)&ss_s[tg][tb * 16 + tl][0];
+    const float4 s1 = *(const float4 *)&ss_s[tg + 4][tb * 16 + tl][0];
+    const float ssd = s0.x + s1.x, ssb = s0.y + s1.y, ssc = s0.z + s1.z;
     const float id = 1.0f / sqrtf(ssd / (float)R + a.eps);
     const float ib = 1.0f / sqrtf(ssb / (float)N + a.eps);
     const float ic = 1.0f / sqrtf(ssc / (float)N + a.eps);
-    const int t = t0 + (cw * TB + tb) * 16 + tl;
+    const int t = t0 + (tg * TB + tb) * 16 + tl;
     if (t < a.L) {
       const int64_t tok = (int64_t)b * a.L + t;
 #pragma unroll
-      for (int nb = 0; nb < RB; ++nb) {
-        const int n = nb * 16 + 4 * g;
-        const float4 gm = *(const float4 *)(a.g_dt + n);
-        const float v0 = acc[tb][nb][0] * id * gm.x, v1 = acc[tb][nb][1] * id * gm.y;
-        const float v2 = acc[tb][nb][2] * id * gm.z, v3 = acc[tb][nb][3] * id * gm.w;
-        uint2 h, l;
-        h.x = pack_bf2(v0, v1); h.y = pack_bf2(v2, v3);
-        l.x = pack_bf2(v0 - bf2f(f2bf(v0)), v1 - bf2f(f2bf(v1)));
-        l.y = pack_bf2(v2 - bf2f(f2bf(v2)), v3 - bf2f(f2bf(v3)));
-        *(uint2 *)(a.dtlow + tok * R + n) = h;
-        *(uint2 *)(a.dtlow_lo + tok * R + n) = l;
-      }
-#pragma unroll
-      for (int nb = RB; nb < NB; ++nb) {
-        const int col = bcol(nb);
-        const bool isb = col < N;
-        const float4 gm = *(const float4 *)(isb ? a.g_B + col : a.g_C + (col - N));
-        const float sc = isb ? ib : ic;
-        *(float4 *)(a.bc + tok * (2 * N) + col) =
-            make_float4(acc[tb][nb][0] * sc * gm.x, acc[tb][nb][1] * sc * gm.y,
-                        acc[tb][nb][2] * sc * gm.z, acc[tb][nb][3] * sc * gm.w);
+      for (int i = 0; i < NB0; ++i) {
+        if (i >= nbn) continue;
+        const int nb = nb0 + i;
+        if (nb < RB) {
+          const int n = nb * 16 + 4 * g;
+          const float4 gm = *(const float4 *)(a.g_dt + n);
+          const float v0 = acc[tb][i][0] * id * gm.x, v1 = acc[tb][i][1] * id * gm.y;
+          const float v2 = acc[tb][i][2] * id * gm.z, v3 = acc[tb][i][3] * id * gm.w;
+          uint2 h, l;
+          h.x = pack_bf2(v0, v1); h.y = pack_bf2(v2, v3);
+          l.x = pack_bf2(v0 - bf2f(f2bf(v0)), v1 - bf2f(f2bf(v1)));
+          l.y = pack_bf2(v2 - bf2f(f2bf(v2)), v3 - bf2f(f2bf(v3)));
+          *(uint2 *)(a.dtlow + tok * R + n) = h;
+          *(uint2 *)(a.dtlow_lo + tok * R + n) = l;
+        } else {
+          const int col = bcol(nb);
+          const bool isb = col < N;
+          const float4 gm = *(const float4 *)(isb ? a.g_B + col : a.g_C + (col - N));
+          const float sc = isb ? ib : ic;
+          *(float4 *)(a.bc + tok * (2 * N) + col) =
+              make_float4(acc[tb][i][0] * sc * gm.x, acc[tb][i][1] * sc * gm.y,
+                          acc[tb][i][2] * sc * gm.z, acc[tb][i][3] * sc * gm.w);
+        }
       }
     }
   }
