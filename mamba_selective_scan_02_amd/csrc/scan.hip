@@ -507,6 +507,17 @@ constexpr int kHalo = 3;                  // x rows before the segment (conv win
 constexpr int kXSeg = kS + kHalo;         // x rows a segment needs: halo + segment
 constexpr int kXZR = 16;                  // staged x / z rows per wave: one 16-byte slot per lane
 static_assert(kXSeg <= kXZR && kS <= kXZR, "a wave's x and z rows fit one wave-load");
+// The two lanes of a channel read staged rows kHalf = 4 apart in the same instruction; the rows
+// are placed so that the two lane halves hit different LDS banks:
+//  * x (64-byte rows k <-> token T0w - 3 + k): lane half p reads rows 4 p .. 4 p + 6, kept at
+//    slots 9 p + (k - 4 p) (rows 0..6 at slots 0..6, rows 4..10 again at slots 9..15);
+//  * z (64-byte rows k <-> token T0w + k): row k at slot k + (k >= 4), i.e. row 4 p + e at
+//    slot 5 p + e;
+//  * dt (128-byte rows): row k at slot k ^ ((k >> 2) & 1), so rows e and 4 + e differ in parity.
+static_assert(kS == 8 && kHalf == 4 && kHalo == 3, "the staged-row placement assumes these");
+__device__ __forceinline__ int x_slot_row(int s) { return s < 7 ? s : (s < 9 ? 6 : s - 5); }
+__device__ __forceinline__ int z_slot_row(int s) { return s < 4 ? s : min(s - 1, 7); }
+__device__ __forceinline__ int d_slot_row(int s) { return s ^ ((s >> 2) & 1); }
 constexpr int kChains = kCh * kN;         // (channel, state) chains of a workgroup
 static_assert(kChains == 512 && kW * 64 >= kChains, "chain threads map onto 512 agg floats");
 static_assert(kW * kS * 64 <= 65536 && kW * 4 * 64 * 16 <= 65536, "LDS offsets fit 16 bits");
@@ -530,8 +541,11 @@ struct TwoPassSmem {
   // per segment and lane, 16-byte slots [wave][S0..3, S4..7, P0..3, P4..7][lane]: the local
   // end states S (overwritten by the segments' true start states) and decays P = exp(A sum dt)
   float4 agg[kW][4][64];
-  float cst[kCh][8];             // per channel: conv taps (K), conv bias, D
-  float a2[kCh][kN];             // A log2(e) per (channel, state)
+  // per channel: conv taps (K) | conv bias, D, -, -; and A log2(e) as [half][lane] 16-byte
+  // slots (lane 2 c + p holds states 8 p + 4 half .. +3 of channel c): the per-block reads are
+  // lane-contiguous
+  float4 cst[2][kCh];
+  float4 a2[2][2 * kCh];
 };
 
 template <typename T, int K, bool PAIRED>
@@ -578,25 +592,23 @@ __device__ __forceinline__ void twopass_body(const ScanArgs &a, TwoPassSmem<T> &
                       lds_addr(&bcdst[i * 8][0]));
     }
     if (!kStage) return;
-    // x: row rr <-> token T0w - 3 + rr (rr < kXSeg); z: row rr <-> token T0w + rr (rr < kS)
+    // x: slot s holds row x_slot_row(s) <-> token T0w - 3 + row; z: slot s holds row
+    // z_slot_row(s) <-> token T0w + row; dt: slot s holds row d_slot_row(s)
     static_assert(!kStage || 64 / xrow_chunks == kXZR, "one wave-load covers kXZR rows");
-    const int rr = lane / xrow_chunks;
+    const int sl = lane / xrow_chunks;
     const uint32_t rowb = (uint32_t)row * (uint32_t)sizeof(T);
     const uint32_t cb16 = (uint32_t)((lane % xrow_chunks) * 16);
     const int xb = min(max(T0w - kHalo, 0), Lm1);
-    const int rx = min(max(T0w - kHalo + min(rr, kXSeg - 1), 0), Lm1) - xb;
+    const int rx = min(max(T0w - kHalo + x_slot_row(sl), 0), Lm1) - xb;
     dma16_opaque_so(xzb + (int64_t)xb * row + ch0, (uint32_t)rx * rowb + cb16,
                     lds_addr(&sm.x[wv][0][0]));
-    const int rz = min(T0w + min(rr, kS - 1), Lm1) - tb;
+    const int rz = min(T0w + z_slot_row(sl), Lm1) - tb;
     dma16_opaque_so(xzb + (int64_t)tb * row + a.D + ch0, (uint32_t)rz * rowb + cb16,
                     lds_addr(&sm.z[wv][0][0]));
-    // dt (fp32): kS rows x 128 B = kS / 8 wave-loads, 8 lanes per row
-#pragma unroll
-    for (int i = 0; i < kS / 8; ++i) {
-      const int r = min(T0w + i * 8 + (lane >> 3), Lm1) - tb;
-      dma16_opaque_so(db + (int64_t)tb * a.D + ch0, (uint32_t)r * (uint32_t)a.D * 4u + (uint32_t)((lane & 7) * 16),
-                      lds_addr(&sm.d[wv][i * 8][0]));
-    }
+    // dt (fp32): kS = 8 rows x 128 B = one wave-load, 8 lanes per row
+    const int rd = min(T0w + d_slot_row(lane >> 3), Lm1) - tb;
+    dma16_opaque_so(db + (int64_t)tb * a.D + ch0, (uint32_t)rd * (uint32_t)a.D * 4u + (uint32_t)((lane & 7) * 16),
+                    lds_addr(&sm.d[wv][0][0]));
   };
 
   // y of block b is stored at the start of block b+1, after that block's wait, so the wait
@@ -642,33 +654,36 @@ __device__ __forceinline__ void twopass_body(const ScanArgs &a, TwoPassSmem<T> &
     float eDu[kHalf], eg[kHalf];
     {
       // per-channel constants from the workgroup's LDS table
-      const float4 c0 = *(const float4 *)&sm.cst[c][0], c1 = *(const float4 *)&sm.cst[c][4];
+      const float4 c0 = sm.cst[0][c], c1 = sm.cst[1][c];
       const float cv[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
       float wc[K];
 #pragma unroll
       for (int k = 0; k < K; ++k) wc[k] = cv[k];
       const float cb = cv[4], Dp = cv[5];
-      // segment-relative token ts (ts >= -3)
-      const uint32_t xl = lds_addr(&sm.x[wv][0][c]);
-      const uint32_t zl = lds_addr(&sm.z[wv][0][c]);
-      const uint32_t dl = lds_addr(&sm.d[wv][0][c]);
-      auto getx = [&](int ts) -> float {
-        if (kStage) return io<T>::cvt(*lds_ptr<const T>(xl + (ts + kHalo) * kCh * sizeof(T)));
-        return io<T>::cvt(xzb[(int64_t)min(T0w + ts, Lm1) * row + ch]);
-      };
-      auto getz = [&](int ts) -> float {
-        if (kStage) return io<T>::cvt(*lds_ptr<const T>(zl + ts * kCh * sizeof(T)));
-        return io<T>::cvt(xzb[(int64_t)min(T0w + ts, Lm1) * row + a.D + ch]);
-      };
-      auto getd = [&](int ts) -> float {
-        if (kStage) return *lds_ptr<const float>(dl + ts * kCh * 4);
-        return db[(int64_t)min(T0w + ts, Lm1) * a.D + ch];
-      };
+      // m: this lane's x row relative to its first window row (token T0w + ts0 + m - 3); e:
+      // its e-th token (T0w + ts0 + e); staged slots as placed above
       const int ts0 = kHalf * p;
+      constexpr uint32_t kXRow = kCh * sizeof(T);
+      const uint32_t xl = lds_addr(&sm.x[wv][0][c]) + 9u * kXRow * p;
+      const uint32_t zl = lds_addr(&sm.z[wv][0][c]) + 5u * kXRow * p;
+      const uint32_t dle = lds_addr(&sm.d[wv][0][c]) + 5u * kCh * 4 * p;   // even e
+      const uint32_t dlo = lds_addr(&sm.d[wv][0][c]) + 3u * kCh * 4 * p;   // odd e
+      auto getx = [&](int m) -> float {
+        if (kStage) return io<T>::cvt(*lds_ptr<const T>(xl + m * kXRow));
+        return io<T>::cvt(xzb[(int64_t)min(T0w + ts0 + m - kHalo, Lm1) * row + ch]);
+      };
+      auto getz = [&](int e) -> float {
+        if (kStage) return io<T>::cvt(*lds_ptr<const T>(zl + e * kXRow));
+        return io<T>::cvt(xzb[(int64_t)min(T0w + ts0 + e, Lm1) * row + a.D + ch]);
+      };
+      auto getd = [&](int e) -> float {
+        if (kStage) return *lds_ptr<const float>(((e & 1) ? dlo : dle) + e * kCh * 4);
+        return db[(int64_t)min(T0w + ts0 + e, Lm1) * a.D + ch];
+      };
       float win[K - 1];
       if (T0w >= kHalo) {   // wave-uniform: every window row is a row of this sequence
 #pragma unroll
-        for (int j = 0; j < K - 1; ++j) win[j] = getx(ts0 - (K - 1) + j);
+        for (int j = 0; j < K - 1; ++j) win[j] = getx(kHalo - (K - 1) + j);
       } else {              // the first segment: rows before token 0 come from the conv state
 #pragma unroll
         for (int j = 0; j < K - 1; ++j) {
@@ -676,7 +691,7 @@ __device__ __forceinline__ void twopass_body(const ScanArgs &a, TwoPassSmem<T> &
           const int t = T0w + ts;
           float v = 0.f;
           if (t >= 0) {
-            v = getx(ts);
+            v = getx(kHalo - (K - 1) + j);
           } else if (a.conv_valid && a.conv_state) {
             v = io<T>::cvt(((const T *)a.conv_state)[((int64_t)b * a.D + ch) * (K - 1) + (K - 1) + t]);
           }
@@ -687,7 +702,7 @@ __device__ __forceinline__ void twopass_body(const ScanArgs &a, TwoPassSmem<T> &
       for (int e = 0; e < kHalf; ++e) {
         const int ts = ts0 + e;
         const bool valid = T0w + ts < a.L;
-        const float x = getx(ts);
+        const float x = getx(kHalo + e);
         float acc = cb;
 #pragma unroll
         for (int j = 0; j < K - 1; ++j) acc = __builtin_fmaf(wc[j], win[j], acc);
@@ -699,10 +714,10 @@ __device__ __forceinline__ void twopass_body(const ScanArgs &a, TwoPassSmem<T> &
         // Past the end only dt is zeroed: the step is then the identity (exp(0 A) = 1, no
         // input), and those tokens' outputs are never stored. Staged rows there hold copies of
         // row L-1, so u and z stay finite.
-        const float dt = valid ? getd(ts) : 0.f;
+        const float dt = valid ? getd(e) : 0.f;
         *lds_ptr<float2>(pdl + ts * kPdRow) = make_float2(dt, dt * u);
         eDu[e] = Dp * u;
-        eg[e] = silu_f(getz(ts));
+        eg[e] = silu_f(getz(e));
       }
     }
     // the staged x, z, dt rows are consumed once this wave's LDS reads have returned; then the
@@ -713,7 +728,7 @@ __device__ __forceinline__ void twopass_body(const ScanArgs &a, TwoPassSmem<T> &
     // ---- 2. local pass over this wave's segment
     float A2[kG];
     {
-      const float4 q0 = *(const float4 *)&sm.a2[c][kG * p], q1 = *(const float4 *)&sm.a2[c][kG * p + 4];
+      const float4 q0 = sm.a2[0][lane], q1 = sm.a2[1][lane];
       A2[0] = q0.x; A2[1] = q0.y; A2[2] = q0.z; A2[3] = q0.w;
       A2[4] = q1.x; A2[5] = q1.y; A2[6] = q1.z; A2[7] = q1.w;
     }
@@ -809,10 +824,13 @@ __device__ __forceinline__ void twopass_body(const ScanArgs &a, TwoPassSmem<T> &
       for (int k = 0; k < K; ++k) v[k] = io<T>::cvt(((const T *)a.conv_w)[(int64_t)cc * K + k]);
       v[4] = a.conv_b ? io<T>::cvt(((const T *)a.conv_b)[cc]) : 0.0f;
       v[5] = a.Dskip[cc];
-      *(float4 *)&sm.cst[tid][0] = make_float4(v[0], v[1], v[2], v[3]);
-      *(float4 *)&sm.cst[tid][4] = make_float4(v[4], v[5], v[6], v[7]);
+      sm.cst[0][tid] = make_float4(v[0], v[1], v[2], v[3]);
+      sm.cst[1][tid] = make_float4(v[4], v[5], v[6], v[7]);
     }
-    if (tid < kCh * kN) sm.a2[tid / kN][tid % kN] = a.A[(int64_t)ch0 * kN + tid] * kLog2e;
+    if (tid < kCh * kN) {   // state n of channel cc: lane 2 cc + n / 8, half (n / 4) % 2
+      const int cc = tid / kN, n = tid % kN;
+      (&sm.a2[(n >> 2) & 1][2 * cc + (n >> 3)].x)[n & 3] = a.A[(int64_t)ch0 * kN + tid] * kLog2e;
+    }
     __syncthreads();
     stage(0, sm.bc[0][wv], tid & 63);
   }
