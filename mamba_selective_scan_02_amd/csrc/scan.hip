@@ -618,16 +618,18 @@ __device__ __forceinline__ void twopass_body(const ScanArgs &a, TwoPassSmem<T> &
   int ypend_t0 = -1;
   auto flush = [&](int c, int p) {
     if (ypend_t0 < 0) return;
-    T *ybase = yb + (int64_t)(ypend_t0 + wv * kS) * a.D;   // wave-uniform, 32-bit lane offsets
-    const uint32_t off = (uint32_t)(p * kHalf * a.D + ch0 + c);
-    const uint32_t step = (uint32_t)a.D;
+    // wave-uniform base and unsigned 32-bit byte offsets (an SGPR base + VGPR offset store)
+    char *ybase = (char *)(yb + (int64_t)(ypend_t0 + wv * kS) * a.D);
+    const uint32_t off = (uint32_t)(p * kHalf * a.D + ch0 + c) * (uint32_t)sizeof(T);
+    const uint32_t step = (uint32_t)a.D * (uint32_t)sizeof(T);
     if (ypend_t0 + kBlk <= a.L) {
 #pragma unroll
-      for (int i = 0; i < kHalf; ++i) io<T>::st(ybase + off + i * step, ypend[i]);
+      for (int i = 0; i < kHalf; ++i) io<T>::st((T *)(ybase + (off + i * step)), ypend[i]);
     } else {
 #pragma unroll
       for (int i = 0; i < kHalf; ++i)
-        if (ypend_t0 + wv * kS + kHalf * p + i < a.L) io<T>::st(ybase + off + i * step, ypend[i]);
+        if (ypend_t0 + wv * kS + kHalf * p + i < a.L)
+          io<T>::st((T *)(ybase + (off + i * step)), ypend[i]);
     }
   };
   auto block = [&](int blk, float (*bc_cur)[kS][2 * kN], float (*bc_nxt)[kS][2 * kN]) {
