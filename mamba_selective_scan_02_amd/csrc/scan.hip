@@ -850,10 +850,24 @@ __device__ __forceinline__ void twopass_body(const ScanArgs &a, TwoPassSmem<T> &
   }
 }
 
-// DETECT: look for paired decay (A given as -(n + 1) per state, or any equal step per lane);
-// off when the caller declares A general, which also leaves the paired path out of the kernel
-// (its registers would otherwise count against the general path's)
-template <typename T, int K, bool DETECT>
+// MODE 0: every workgroup takes the general path (the caller declares A general). Otherwise
+// each workgroup checks its channels for paired decay (A given as -(n + 1) per state, or any
+// equal step per lane): MODE 1 runs the workgroups that have it (paired path) and MODE 2 those
+// that do not (general path), each kernel exiting on the others, so that no kernel holds both
+// paths (their registers would add up and spill).
+__device__ __forceinline__ bool twopass_paired(const ScanArgs &a, int ch0) {
+  // every lane's 8 states in arithmetic progression with the channel's step
+  const int lane = threadIdx.x & 63;
+  const int ch = ch0 + (lane >> 1), n0 = kG * (lane & 1);
+  const float *Ar = a.A + (int64_t)ch * kN;
+  const float dl = Ar[1] - Ar[0];
+  int ok = 1;
+#pragma unroll
+  for (int s = 1; s < kG; ++s) ok &= (Ar[n0 + s] - Ar[n0] == (float)s * dl);
+  return __syncthreads_and(ok) != 0;
+}
+
+template <typename T, int K, int MODE>
 __global__ __launch_bounds__(kW * 64) void scan_twopass_kernel(ScanArgs a) {
   __shared__ __attribute__((aligned(16))) TwoPassSmem<T> sm;
   const int groups = a.D / kCh;
@@ -861,30 +875,19 @@ __global__ __launch_bounds__(kW * 64) void scan_twopass_kernel(ScanArgs a) {
   // workgroup-uniform (readfirstlane keeps the bases derived from them in SGPRs)
   const int b = __builtin_amdgcn_readfirstlane(gid / groups);
   const int ch0 = __builtin_amdgcn_readfirstlane((gid % groups) * kCh);
-  if (DETECT) {
-    // paired decay: every lane's 8 states in arithmetic progression with the channel's step
-    const int lane = threadIdx.x & 63;
-    const int ch = ch0 + (lane >> 1), n0 = kG * (lane & 1);
-    const float *Ar = a.A + (int64_t)ch * kN;
-    const float dl = Ar[1] - Ar[0];
-    int ok = 1;
-#pragma unroll
-    for (int s = 1; s < kG; ++s) ok &= (Ar[n0 + s] - Ar[n0] == (float)s * dl);
-    if (__syncthreads_and(ok)) {
-      twopass_body<T, K, true>(a, sm, b, ch0);
-      return;
-    }
-  }
-  twopass_body<T, K, false>(a, sm, b, ch0);
+  if (MODE != 0 && twopass_paired(a, ch0) != (MODE == 1)) return;   // the other kernel's
+  twopass_body<T, K, MODE == 1>(a, sm, b, ch0);
 }
 
 template <typename T, int K>
 hipError_t dispatch_twopass_k(const ScanArgs &a, hipStream_t s) {
   const unsigned blocks = (unsigned)((int64_t)a.B * (a.D / kCh));
-  if (a.general_a)
-    hipLaunchKernelGGL((scan_twopass_kernel<T, K, false>), dim3(blocks), dim3(kW * 64), 0, s, a);
-  else
-    hipLaunchKernelGGL((scan_twopass_kernel<T, K, true>), dim3(blocks), dim3(kW * 64), 0, s, a);
+  if (a.general_a) {
+    hipLaunchKernelGGL((scan_twopass_kernel<T, K, 0>), dim3(blocks), dim3(kW * 64), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((scan_twopass_kernel<T, K, 1>), dim3(blocks), dim3(kW * 64), 0, s, a);
+    hipLaunchKernelGGL((scan_twopass_kernel<T, K, 2>), dim3(blocks), dim3(kW * 64), 0, s, a);
+  }
   return hipGetLastError();
 }
 

@@ -6,8 +6,8 @@ The workloads draw A = -(n + 1), D = 1 and dt in [1e-3, 1e-1]. Here instead:
     "The Mamba Layer", continuous SSM equation: A, D are parameters; ZOH equation: the decay
     exp(dt A) depends on both);
   * large steps: dt0 in [12, 40], so dt_proj's pre-activation crosses softplus's linear-branch
-    thresholds (15 and 20 in the kernels) and dt A reaches -800: exp(dt A) underflows to 0 and
-    the recurrence becomes memoryless (h = Bbar u);
+    threshold (20 in the kernels) and dt A reaches -800: exp(dt A) underflows to 0 and the
+    recurrence becomes memoryless (h = Bbar u);
   * tiny steps: dt0 in [1e-7, 1e-5] (pre-activation near -16 .. -11.5);
   * zero input x = 0 with a carried SSM state: u = 0 and B = C = RMSNorm(0) = 0, so y = 0
     exactly and the state decays in closed form, h_L = exp(L dt A) h_0 with dt = softplus(bias)
@@ -180,3 +180,29 @@ def test_paired_decay_and_general_paths(io, N):
     assert float((s1 - s2).abs().max()) <= 1e-5 * max(1.0, float(s2.abs().max()))
     _prefill_case(cfg.with_(name=f"edge_unpaired_{io}_N{N}"), 680 + N, INPUTS["general_A"],
                   scan="chunked")
+
+
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+def test_mixed_paired_and_general_channels(io):
+    """A = -(n + 1) on the first half of the channels and random A on the rest, default flags:
+    the time-parallel d_state-16 scan runs the workgroups with paired decay and the others in
+    two launches (each exits on the other's); every channel matches the oracle."""
+    _need_gpu()
+    cfg = BASE.with_(io_dtype=io, name=f"edge_mixed_A_{io}")
+    seed = 690
+    print(f"[edge] {cfg.name} seed={seed} mixed A, scan=chunked", flush=True)
+    dev = "cuda"
+    p = synth.make_params(cfg, seed, dev, conv_bias=True, gamma_random=True,
+                          **INPUTS["general_A"])
+    half = cfg.d_inner // 2
+    p["A"][:half] = -torch.arange(1, cfg.d_state + 1, dtype=torch.float32, device=dev)
+    xz = synth.make_xz(cfg, seed, dev)
+    cs, ss = synth.make_states(cfg, seed, dev)
+    cs_in, ss_in = cs.clone(), ss.clone()
+    y = mm.prefill(xz, p, conv_state=cs, ssm_state=ss, states_valid=True, scan="chunked")
+    torch.cuda.synchronize()
+    yr, csr, ssr = oracle.mixer_prefill(to64(xz), oracle.as_f64_params(p), to64(cs_in),
+                                        to64(ss_in))
+    check(y, yr, cfg.io_dtype, f"{cfg.name} y", f32_large_outputs=True)
+    check(ss, ssr, cfg.io_dtype, f"{cfg.name} ssm_state", f32_large_outputs=True)
+    np.testing.assert_array_equal(to64(cs), csr)
