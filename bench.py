@@ -9,7 +9,8 @@ final conv/SSM states. The headline evaluates every exp(dt A) of the scan direct
 (MM_FLAG_SCAN_GENERAL_A), as for an arbitrary A. Inputs are synthetic, seeded, resident in HBM
 before timing. Further legs, reported beside the headline: the same prefill with the library's
 default, which detects that A = -(n + 1) has equally spaced decay rates and forms the decays
-from fewer exps ("paired_decay"); the ZOH input matrix; the 4K and 2 x 256K prefills; 512
+from fewer exps ("paired_decay"); dt_proj fused into the scan (MM_FLAG_FUSED_DTPROJ, no dt
+buffer); the ZOH input matrix; the 4K and 2 x 256K prefills; 512
 batched decode steps (B=256) at d_inner 8192 and 16384 after a 1024-token prefill seeds the
 states; mamba_layer_prefill (pre-RMSNorm, in_proj 4096 -> 16384, the mixer, out_proj 8192 ->
 4096 with the residual) and mamba_mixer_prefill_backward on the 128K tokens; the prefill at
@@ -125,7 +126,7 @@ def stage_view(ms, nbytes=None, flops=None, copy_gbs=None):
 
 
 def prefill_leg(args, mm, workload=PREFILL_WORKLOAD, general_a=True, zoh=False, steps=None,
-                warmup=None):
+                warmup=None, fused_dt=False):
     """Time mamba_mixer_prefill on a prefill workload; per-stage times from HIP events on the
     launch stream (the *_timed entry point)."""
     cfg = synth.CONFIGS[workload]
@@ -138,19 +139,20 @@ def prefill_leg(args, mm, workload=PREFILL_WORKLOAD, general_a=True, zoh=False, 
     y = torch.empty(cfg.batch, cfg.seqlen, cfg.d_inner, dtype=cfg.torch_dtype, device=dev)
     cs = torch.zeros(cfg.batch, cfg.d_inner, cfg.d_conv - 1, dtype=cfg.torch_dtype, device=dev)
     ss = torch.zeros(cfg.batch, cfg.d_inner, cfg.d_state, dtype=torch.float32, device=dev)
-    shape = mm.shape_of(xz, p, eps=cfg.rms_eps, zoh=zoh, general_a=general_a)
+    shape = mm.shape_of(xz, p, eps=cfg.rms_eps, zoh=zoh, general_a=general_a, fused_dt=fused_dt)
     ws = mm.alloc_workspace(mm.prefill_workspace_bytes(shape), dev)
     timer = mm.StageTimer()
 
     def step(t=None):
         mm.prefill(xz, p, conv_state=cs, ssm_state=ss, states_valid=False, y=y, workspace=ws,
-                   eps=cfg.rms_eps, timer=t, zoh=zoh, general_a=general_a)
+                   eps=cfg.rms_eps, timer=t, zoh=zoh, general_a=general_a, fused_dt=fused_dt)
 
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
     timer.reset()
-    print(f"[bench] prefill {workload} general_a={general_a} zoh={zoh}: {warmup} warmup done, "
+    print(f"[bench] prefill {workload} general_a={general_a} zoh={zoh} fused_dt={fused_dt}: "
+          f"{warmup} warmup done, "
           f"timing {steps}", file=sys.stderr, flush=True)
     t0 = time.perf_counter()
     for _ in range(steps):
@@ -173,7 +175,9 @@ def prefill_leg(args, mm, workload=PREFILL_WORKLOAD, general_a=True, zoh=False, 
                    "dt_rank": cfg.dt_rank, "io_dtype": cfg.io_dtype, "state_dtype": "f32",
                    "scan_exps": "every exp(dt A)" if (general_a or zoh) else
                                 "paired decay (A = -(n + 1) detected)",
-                   "bbar": "zoh" if zoh else "first-order"},
+                   "bbar": "zoh" if zoh else "first-order",
+                   "dt_proj": "fused into the scan" if fused_dt else "own kernel, dt via HBM",
+                   "workspace_bytes": mm.prefill_workspace_bytes(shape)},
         "scan": {"ms": scan_avg_s * 1e3, "state_updates_per_s": updates / scan_avg_s,
                  "algorithmic_bytes": sbytes, "GBs": sbytes / scan_avg_s / 1e9,
                  "hbm_frac": sbytes / scan_avg_s / 1e9 / HBM_PEAK_GBS},
@@ -465,6 +469,9 @@ def profile_run(args, mm):
     prefill_leg(args, mm, general_a=False)
     torch.cuda.synchronize()
     print("[profile] paired-decay prefill done", file=sys.stderr, flush=True)
+    prefill_leg(args, mm, fused_dt=True)
+    torch.cuda.synchronize()
+    print("[profile] fused dt_proj prefill done", file=sys.stderr, flush=True)
     decode_leg(args, mm, steps=32)
     torch.cuda.synchronize()
     print("[profile] decode done", file=sys.stderr, flush=True)
@@ -490,7 +497,7 @@ def main():
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-prefill-legs", action="store_true",
-                    help="skip the paired-decay, ZOH, 4K and 2 x 256K prefill legs")
+                    help="skip the paired-decay, fused dt_proj, ZOH, 4K and 2 x 256K prefill legs")
     ap.add_argument("--profile", action="store_true",
                     help="short run for rocprofv3: a few prefill and decode steps plus one plain "
                          "1 GiB device copy (the reference kernel for counter calibration)")
@@ -522,6 +529,7 @@ def main():
         legs = {}
         few = max(2, min(args.steps, 5))
         for name, kw in (("paired_decay", dict(general_a=False)),
+                         ("fused_dt_proj", dict(fused_dt=True)),
                          ("zoh", dict(zoh=True)),
                          ("mini_prefill_4k", dict(workload="mini_prefill_4k", steps=args.steps)),
                          ("prefill_256k_b2", dict(workload="prefill_256k_b2", steps=few,

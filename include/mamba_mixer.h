@@ -84,7 +84,16 @@ enum {
      (A[i, n0 + k] = A[i, n0] + k delta_i, as for A = -(n + 1)), forms the decays of a lane
      as exp(dt A[i, n0]) times powers of exp(dt delta_i): fewer exps, the same result to fp32
      rounding. First-order Bbar only (ZOH always evaluates each exp). */
-  MM_FLAG_SCAN_GENERAL_A = 1u << 3
+  MM_FLAG_SCAN_GENERAL_A = 1u << 3,
+  /* Fuse dt_proj + bias + softplus into the scan ("The selective mechanism": Delta from a
+     small linear layer of the token): the scan forms dt from the normalised dt_low with the
+     same MFMA sequence as the separate dt_proj kernel (the same dt, bit for bit), so the
+     [tokens, d_inner] fp32 dt buffer is neither written nor read and the workspace shrinks by
+     4 * batch * seqlen * d_inner bytes. It applies to MM_BF16 with d_state 16, dt_rank 256 and
+     first-order Bbar where the prefill runs the time-parallel two-pass scan (the default for
+     few sequences of more than 32 tokens, or MM_FLAG_SCAN_CHUNKED); elsewhere the flag changes
+     nothing. */
+  MM_FLAG_FUSED_DTPROJ = 1u << 4
 };
 
 /*

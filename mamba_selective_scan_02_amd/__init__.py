@@ -24,6 +24,7 @@ MM_FLAG_ZOH_B = 1
 MM_FLAG_SCAN_SEQUENTIAL = 2
 MM_FLAG_SCAN_CHUNKED = 4
 MM_FLAG_SCAN_GENERAL_A = 8
+MM_FLAG_FUSED_DTPROJ = 16
 STAGES = ("conv_silu", "x_proj", "rmsnorm", "dt_proj_softplus", "selective_scan", "conv_state",
           "layer_rmsnorm", "in_proj", "out_proj", "bwd_recompute", "bwd_scan", "bwd_proj",
           "bwd_conv")
@@ -128,7 +129,7 @@ def make_shape(batch, seqlen, d_inner, d_state, d_conv, dt_rank, dtype, eps=1e-6
 
 
 def shape_of(xz: torch.Tensor, params: dict, *, decode=False, eps=1e-6, zoh=False,
-             scan: str | None = None, general_a: bool = False) -> Shape:
+             scan: str | None = None, general_a: bool = False, fused_dt: bool = False) -> Shape:
     if decode:
         B, D2 = xz.shape
         L = 1
@@ -143,6 +144,8 @@ def shape_of(xz: torch.Tensor, params: dict, *, decode=False, eps=1e-6, zoh=Fals
         flags |= {"sequential": MM_FLAG_SCAN_SEQUENTIAL, "chunked": MM_FLAG_SCAN_CHUNKED}[scan]
     if general_a:
         flags |= MM_FLAG_SCAN_GENERAL_A
+    if fused_dt:
+        flags |= MM_FLAG_FUSED_DTPROJ
     return make_shape(B, L, D, N, K, R, xz.dtype, eps, flags)
 
 
@@ -199,12 +202,14 @@ class StageTimer:
 
 def prefill(xz, params, *, conv_state=None, ssm_state=None, states_valid=False, y=None,
             workspace=None, eps=1e-6, zoh=False, stream=None, timer: StageTimer | None = None,
-            scan: str | None = None, general_a: bool = False):
+            scan: str | None = None, general_a: bool = False, fused_dt: bool = False):
     """Run mamba_mixer_prefill. xz [B, L, 2D] (bf16 or fp32, on the GPU); conv_state
     [B, D, K-1] and ssm_state [B, D, N] are updated in place when given. scan = None picks
     the scan kernel by size; "sequential" / "chunked" force one. general_a sets
-    MM_FLAG_SCAN_GENERAL_A (every exp(dt A) evaluated directly). Returns y."""
-    shape = shape_of(xz, params, eps=eps, zoh=zoh, scan=scan, general_a=general_a)
+    MM_FLAG_SCAN_GENERAL_A (every exp(dt A) evaluated directly); fused_dt sets
+    MM_FLAG_FUSED_DTPROJ (dt_proj inside the scan where it applies). Returns y."""
+    shape = shape_of(xz, params, eps=eps, zoh=zoh, scan=scan, general_a=general_a,
+                     fused_dt=fused_dt)
     if y is None:
         y = torch.empty(xz.shape[:-1] + (shape.d_inner,), dtype=xz.dtype, device=xz.device)
     need = prefill_workspace_bytes(shape)

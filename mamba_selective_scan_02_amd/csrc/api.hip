@@ -21,6 +21,7 @@ struct Workspace {
   bool tiled_dtproj; // bf16: token-stationary dt_proj kernel
   bool fast_decode;  // bf16 decode step: range-split x_proj, fused update (no u / xdbl buffers)
   bool scan_tuned;   // d_state 8 / 32 / 64 on the lane-per-state-group scan kernel
+  bool fused_dt;     // bf16: dt_proj + softplus inside the two-pass scan (no dt buffer)
   int dec_ranges, dec_range_ch;
   size_t u, u_lo, xdbl, part, dtlow, dtlow_lo, bc, dt, gP, gS, total;
 };
@@ -33,7 +34,7 @@ uint32_t scan_force(uint32_t flags) {
 // Byte offsets of the prefill intermediates for T = batch * seqlen tokens.
 //   fp32 mode: u [T,D] f32 | xdbl [T,R+2N] f32 | dt_low [T,R] f32 | B,C [T,2N] f32 | dt [T,D] f32
 //   bf16 mode: (u_hi, u_lo [T,D] bf16 | xdbl f32, unless fused) | dt_low hi, lo [T,R] bf16 |
-//              B,C [T,2N] f32 | dt [T,D] f32
+//              B,C [T,2N] f32 | dt [T,D] f32 (none with the fused dt_proj)
 //   bf16 decode step: partial x_proj sums [ranges, B, R+2N] f32 replace u and xdbl.
 //   d_state != 16 off the lane-per-state-group scan: the general scan's per-range transfers
 //   P, S [B, ranges, D, N] f32.
@@ -51,6 +52,9 @@ Workspace layout(const mm_shape &s, bool decode) {
                   xproj_fused_supported(s.dt_rank, s.d_state, s.d_inner, s.d_conv) &&
                   (s.d_state == 16 || w.scan_tuned);
   w.tiled_dtproj = bf && dtproj_supported(s.dt_rank, s.d_inner);
+  w.fused_dt = !decode && bf && (s.flags & MM_FLAG_FUSED_DTPROJ) &&
+               scan_fused_dt_used(s.batch, s.seqlen, s.d_inner, s.d_state, s.dt_rank,
+                                  scan_force(s.flags), (s.flags & MM_FLAG_ZOH_B) ? 1 : 0);
   w.fast_decode = decode && bf && decode_fast_supported(s.dt_rank, s.d_state, s.d_inner, s.d_conv);
   w.dec_ranges = 0;
   w.dec_range_ch = 0;
@@ -71,7 +75,7 @@ Workspace layout(const mm_shape &s, bool decode) {
   w.dtlow = o; o += up(T * s.dt_rank * e);
   w.dtlow_lo = o; if (bf) o += up(T * s.dt_rank * 2);
   w.bc = o; o += up(T * 2 * s.d_state * 4);
-  w.dt = o; o += up(T * s.d_inner * 4);
+  w.dt = o; if (!w.fused_dt) o += up(T * s.d_inner * 4);
   // d_state != 16 off the lane kernel: per-range transfers of the general scan
   const size_t gsz = s.d_state != 16 && !w.scan_tuned
                          ? (size_t)s.batch * scan_n_ranges(s.seqlen) * s.d_inner * s.d_state * 4 : 0;
@@ -94,7 +98,7 @@ mm_status check_shape(const mm_shape *s, bool decode) {
     if (dt != MM_F32 && dt != MM_BF16) return MM_ERR_INVALID_ARG;
   }
   if (s->flags & ~(uint32_t)(MM_FLAG_ZOH_B | MM_FLAG_SCAN_SEQUENTIAL | MM_FLAG_SCAN_CHUNKED |
-                             MM_FLAG_SCAN_GENERAL_A))
+                             MM_FLAG_SCAN_GENERAL_A | MM_FLAG_FUSED_DTPROJ))
     return MM_ERR_INVALID_ARG;
   if ((s->flags & MM_FLAG_SCAN_SEQUENTIAL) && (s->flags & MM_FLAG_SCAN_CHUNKED))
     return MM_ERR_INVALID_ARG;
@@ -253,7 +257,7 @@ mm_status run_mixer(const mm_shape *s, const mm_params *p, const void *xz, void 
                          R, N, s->rms_eps, st));
     }
   }
-  {
+  if (!w.fused_dt) {
     StageScope sc(timer, st, MM_STAGE_DTPROJ);
     if (w.tiled_dtproj) {
       DtprojArgs da{(const uint16_t *)dtlow, (const uint16_t *)dtlow_lo,
@@ -270,6 +274,13 @@ mm_status run_mixer(const mm_shape *s, const mm_params *p, const void *xz, void 
                 (s->flags & MM_FLAG_ZOH_B) ? 1 : 0,
                 (int)scan_force(s->flags), (s->flags & MM_FLAG_SCAN_GENERAL_A) ? 1 : 0,
                 B, L, D, N};
+    if (w.fused_dt) {
+      sa.delta = nullptr;
+      sa.dtlow = (const uint16_t *)dtlow;
+      sa.dtlow_lo = (const uint16_t *)dtlow_lo;
+      sa.dt_w = (const uint16_t *)p->dt_proj_w;
+      sa.dt_b = p->dt_proj_b;
+    }
     if (N == 16 || w.scan_tuned) {
       MM_TRY(launch_scan(dt, sa, st));
     } else {

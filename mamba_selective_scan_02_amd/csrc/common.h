@@ -67,6 +67,17 @@ __device__ __forceinline__ float softplus_f(float v) {
   if (w == 1.0f) return e;
   return __builtin_amdgcn_logf(w) * 0.69314718055994531f * (e * __builtin_amdgcn_rcpf(w - 1.0f));
 }
+// softplus_f with every case computed and selected (selects, not divergent branches around the
+// log): e = e^v, w = 1 + e, log(w) e / (w - 1) (Goldberg's log1p method), e itself where w
+// rounds to 1, and v above 20. dt_proj's epilogue (on its own or fused into the scan) uses it.
+__device__ __forceinline__ float softplus_sel(float v) {
+  const float e = exp2_hw(v * kLog2e);
+  const float w = 1.0f + e;
+  const float d = w - 1.0f;
+  const float l = __builtin_amdgcn_logf(w) * 0.69314718055994531f * (e * __builtin_amdgcn_rcpf(d));
+  const float r = d == 0.0f ? e : l;
+  return v > 20.0f ? v : r;
+}
 
 // Wait until every vector-memory operation of this wave has completed, without waiting on the
 // LDS/scalar or export counters. (Stores and direct-to-LDS loads need not retire in issue order,
@@ -115,6 +126,19 @@ __device__ __forceinline__ void dma16_opaque_so(const void *sbase, uint32_t voff
   const uint64_t sb = ((uint64_t)bhi << 32) | (uint64_t)blo;
   const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_base);
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(sb), "s"(m0v)
+               : "memory", "m0");
+}
+// As dma16_opaque_so with 4 bytes per lane (lane i writes [lds_base + 4 i, +4)).
+__device__ __forceinline__ void dma4_opaque_so(const void *sbase, uint32_t voff,
+                                               uint32_t lds_base) {
+  const uint64_t bp = (uint64_t)(uintptr_t)sbase;
+  const uint32_t bhi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(bp >> 32));
+  const uint32_t blo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)bp);
+  const uint64_t sb = ((uint64_t)bhi << 32) | (uint64_t)blo;
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_base);
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
                :
                : "v"(voff), "s"(sb), "s"(m0v)
                : "memory", "m0");

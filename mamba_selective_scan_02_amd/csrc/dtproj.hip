@@ -37,19 +37,6 @@ __device__ __forceinline__ int swz(int r, int c) {
   return c ^ (r & 15);
 }
 
-// softplus(v) = log(1 + e^v) in fp32, the form of softplus_f (common.h) with every case
-// computed and selected (selects, not divergent branches around the log): e = e^v,
-// w = 1 + e, log(w) e / (w - 1) (Goldberg's log1p method), e itself where w rounds to 1, and v
-// above 20 (within 2e-9 relative there).
-__device__ __forceinline__ float softplus_sel(float v) {
-  const float e = exp2_hw(v * kLog2e);
-  const float w = 1.0f + e;
-  const float d = w - 1.0f;
-  const float l = __builtin_amdgcn_logf(w) * 0.69314718055994531f * (e * __builtin_amdgcn_rcpf(d));
-  const float r = d == 0.0f ? e : l;
-  return v > 20.0f ? v : r;
-}
-
 template <int R>
 __global__ __launch_bounds__(512) void dtproj_kernel(DtprojArgs a, int ch_per_wg) {
   constexpr int S = R / 8;             // 16-byte slots per W_dt row

@@ -227,10 +227,17 @@ struct ScanArgs {
   // the per-range transfers [B, ranges, D, N] (P, and S / the range start states)
   const void *u = nullptr, *u_lo = nullptr;
   float *gP = nullptr, *gS = nullptr;
+  // fused dt_proj (bf16 on the two-pass scan, dt_rank 256; scan_fused_dt_used): dt is formed in
+  // the scan from the normalised dt_low planes [B*L, 256] bf16 (high, low), W_dt [D, 256] bf16
+  // and the bias [D]; delta is then not read. Null dtlow: dt comes from delta.
+  const uint16_t *dtlow = nullptr, *dtlow_lo = nullptr, *dt_w = nullptr;
+  const float *dt_b = nullptr;
 };
 // N = 16; N = 8, 32, 64 when scan_tuned_used
 hipError_t launch_scan(mm_dtype dt, const ScanArgs &a, hipStream_t s);
 bool scan_tuned_used(int B, int L, int D, int N, uint32_t force);
+// the shapes on which launch_scan accepts ScanArgs::dtlow (bf16 I/O is the caller's check)
+bool scan_fused_dt_used(int B, int L, int D, int N, int R, uint32_t force, int zoh);
 bool scan_n_supported(int N);
 int scan_n_ranges(int L);
 hipError_t launch_scan_n(mm_dtype dt, const ScanArgs &a, hipStream_t s);

@@ -522,7 +522,12 @@ constexpr int kChains = kCh * kN;         // (channel, state) chains of a workgr
 static_assert(kChains == 512 && kW * 64 >= kChains, "chain threads map onto 512 agg floats");
 static_assert(kW * kS * 64 <= 65536 && kW * 4 * 64 * 16 <= 65536, "LDS offsets fit 16 bits");
 
-template <typename T>
+constexpr int kFR = 256;                  // dt_rank of the fused dt_proj
+constexpr int kFK = kFR / 32;             // its k-steps (16x16x32 MFMAs per plane)
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+
+template <typename T, bool FDT>
 struct TwoPassSmem {
   // bf16 I/O stages x, z and dt through LDS; fp32 I/O (small problems) reads them from
   // global memory in the prep, which keeps its LDS within 160 KB
@@ -534,7 +539,7 @@ struct TwoPassSmem {
   float bc[2][kW][kS][2 * kN];
   T x[kW][kXR][kCh];
   T z[kW][kXR][kCh];
-  float d[kW][kZR][kCh];
+  float d[kW][kZR][kCh];      // staged dt rows, or dt formed in the workgroup (fused dt_proj)
   // prep output: (dt, dt*u) per (token, channel) of each wave's segment; rows padded by one
   // element so that the rows of the two lanes of a channel fall in different LDS banks
   float2 pd[kW][kS][kCh + 1];
@@ -546,12 +551,19 @@ struct TwoPassSmem {
   // lane-contiguous
   float4 cst[2][kCh];
   float4 a2[2][2 * kCh];
+  // fused dt_proj: the workgroup's W_dt rows (16-byte slot c of row r at slot c ^ (r % 16), so
+  // that a fragment read of 16 rows is bank-conflict free), their biases, and the sink of the
+  // dt_low prefetch (written, never read)
+  bf16_t wdt[FDT ? kCh : 1][FDT ? kFR : 8];
+  float dtb[FDT ? kCh : 4];
+  float pf[FDT ? kW : 1][64];
 };
 
-template <typename T, int K, bool PAIRED>
-__device__ __forceinline__ void twopass_body(const ScanArgs &a, TwoPassSmem<T> &sm, int b,
+template <typename T, int K, bool PAIRED, bool FDT>
+__device__ __forceinline__ void twopass_body(const ScanArgs &a, TwoPassSmem<T, FDT> &sm, int b,
                                              int ch0) {
-  constexpr bool kStage = TwoPassSmem<T>::kStage;
+  constexpr bool kStage = TwoPassSmem<T, FDT>::kStage;
+  static_assert(!FDT || kStage, "the fused dt_proj is built for bf16 I/O");
   constexpr int xrow_chunks = kCh * sizeof(T) / 16;    // 16-byte chunks per staged x/z row
   constexpr uint32_t kPdRow = (kCh + 1) * sizeof(float2), kBcRow = 2 * kN * sizeof(float);
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
@@ -605,10 +617,64 @@ __device__ __forceinline__ void twopass_body(const ScanArgs &a, TwoPassSmem<T> &
     const int rz = min(T0w + z_slot_row(sl), Lm1) - tb;
     dma16_opaque_so(xzb + (int64_t)tb * row + a.D + ch0, (uint32_t)rz * rowb + cb16,
                     lds_addr(&sm.z[wv][0][0]));
-    // dt (fp32): kS = 8 rows x 128 B = one wave-load, 8 lanes per row
-    const int rd = min(T0w + d_slot_row(lane >> 3), Lm1) - tb;
-    dma16_opaque_so(db + (int64_t)tb * a.D + ch0, (uint32_t)rd * (uint32_t)a.D * 4u + (uint32_t)((lane & 7) * 16),
-                    lds_addr(&sm.d[wv][0][0]));
+    if (!FDT) {
+      // dt (fp32): kS = 8 rows x 128 B = one wave-load, 8 lanes per row
+      const int rd = min(T0w + d_slot_row(lane >> 3), Lm1) - tb;
+      dma16_opaque_so(db + (int64_t)tb * a.D + ch0, (uint32_t)rd * (uint32_t)a.D * 4u + (uint32_t)((lane & 7) * 16),
+                      lds_addr(&sm.d[wv][0][0]));
+    } else {
+      // fused dt_proj: touch this segment's dt_low rows (both planes, 512 B per row each) so
+      // that the dt phase at the end of the block finds them in L2; lane l reads 4 bytes at
+      // row l / 8, byte 64 (l % 8) into the wave's sink
+      const uint32_t po = (uint32_t)(min(T0w + (lane >> 3), Lm1) - tb) * (kFR * 2u) + 64u * (lane & 7);
+      const int64_t pr = ((int64_t)b * a.L + tb) * kFR;
+      dma4_opaque_so(a.dtlow + pr, po, lds_addr(&sm.pf[wv][0]));
+      dma4_opaque_so(a.dtlow_lo + pr, po, lds_addr(&sm.pf[wv][0]));
+    }
+  };
+
+  // Fused dt_proj: dt of block blk into sm.d, in the staged rows' slots, for the prep after the
+  // next barrier. Waves 0-5 each form 16 tokens of the block (wave w: tokens 16 w .. +15) for
+  // all 32 channels, as two 16 x 16 tiles (lane (tl, g) = (lane % 16, lane / 16) holding token
+  // tl and channels 16 nb + 4 g .. +3) that share the dt_low fragments, so that every dt_low
+  // row crosses from L2 once per workgroup. The MFMA sequence is dtproj_kernel's (per k-step
+  // the low plane, then the high plane, into one fp32 accumulator per tile), which makes dt the
+  // same bit for bit.
+  auto dt_phase = [&](int blk) {
+    constexpr int kTiles = kBlk / 16;              // 16-token tiles per block: waves 0 .. 5
+    if (wv >= kTiles) return;
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int lane = tid & 63, tl = lane & 15, g = lane >> 4;
+    const int t0 = blk * kBlk + 16 * wv;           // wave-uniform
+    const int tb = min(t0, Lm1);
+    const uint32_t off = (uint32_t)(min(t0 + tl, Lm1) - tb) * (kFR * 2u) + 16u * g;
+    const char *hb = (const char *)(a.dtlow + ((int64_t)b * a.L + tb) * kFR);
+    const char *lb = (const char *)(a.dtlow_lo + ((int64_t)b * a.L + tb) * kFR);
+    uint4 fh[kFK], fl[kFK];
+#pragma unroll
+    for (int ks = 0; ks < kFK; ++ks) {
+      fh[ks] = *(const uint4 *)(hb + (off + 64u * ks));
+      fl[ks] = *(const uint4 *)(lb + (off + 64u * ks));
+    }
+    f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int ks = 0; ks < kFK; ++ks) {
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        const uint32_t wl = lds_addr(&sm.wdt[16 * nb + tl][0]);
+        const bf16x8 fw = __builtin_bit_cast(bf16x8, *lds_ptr<const uint4>(wl + 16u * ((4 * ks + g) ^ tl)));
+        acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fw, __builtin_bit_cast(bf16x8, fl[ks]), acc[nb], 0, 0, 0);
+        acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fw, __builtin_bit_cast(bf16x8, fh[ks]), acc[nb], 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const float4 bv = *lds_ptr<const float4>(lds_addr(&sm.dtb[16 * nb + 4 * g]));
+      const float4 v = make_float4(softplus_sel(acc[nb][0] + bv.x), softplus_sel(acc[nb][1] + bv.y),
+                                   softplus_sel(acc[nb][2] + bv.z), softplus_sel(acc[nb][3] + bv.w));
+      *lds_ptr<float4>(lds_addr(&sm.d[2 * wv + (tl >> 3)][d_slot_row(tl & 7)][16 * nb + 4 * g])) = v;
+    }
   };
 
   // y of block b is stored at the start of block b+1, after that block's wait, so the wait
@@ -815,6 +881,11 @@ __device__ __forceinline__ void twopass_body(const ScanArgs &a, TwoPassSmem<T> &
       }
     }
     ypend_t0 = T0;
+    if (FDT && blk + 1 < nblocks) {
+      // every wave's prep of this block has read sm.d (first barrier above)
+      dt_phase(blk + 1);
+      lds_barrier();
+    }
   };
 
   {
@@ -833,8 +904,20 @@ __device__ __forceinline__ void twopass_body(const ScanArgs &a, TwoPassSmem<T> &
       const int cc = tid / kN, n = tid % kN;
       (&sm.a2[(n >> 2) & 1][2 * cc + (n >> 3)].x)[n & 3] = a.A[(int64_t)ch0 * kN + tid] * kLog2e;
     }
+    if (FDT) {
+      // W_dt rows of the workgroup's channels (swizzled as above) and their biases
+      for (int e = tid; e < kCh * (kFR / 8); e += kW * 64) {
+        const int r = e / (kFR / 8), c = e % (kFR / 8);
+        *(uint4 *)&sm.wdt[r][8 * (c ^ (r & 15))] = *(const uint4 *)(a.dt_w + (int64_t)(ch0 + r) * kFR + 8 * c);
+      }
+      if (tid < kCh) sm.dtb[tid] = a.dt_b[ch0 + tid];
+    }
     __syncthreads();
     stage(0, sm.bc[0][wv], tid & 63);
+    if (FDT) {
+      dt_phase(0);
+      lds_barrier();
+    }
   }
   for (int blk = 0; blk < nblocks; ++blk) {
     const bool odd = blk & 1;
@@ -867,28 +950,37 @@ __device__ __forceinline__ bool twopass_paired(const ScanArgs &a, int ch0) {
   return __syncthreads_and(ok) != 0;
 }
 
-template <typename T, int K, int MODE>
+template <typename T, int K, int MODE, bool FDT>
 __global__ __launch_bounds__(kW * 64) void scan_twopass_kernel(ScanArgs a) {
-  __shared__ __attribute__((aligned(16))) TwoPassSmem<T> sm;
+  __shared__ __attribute__((aligned(16))) TwoPassSmem<T, FDT> sm;
   const int groups = a.D / kCh;
   const int gid = xcd_remap(blockIdx.x, gridDim.x);
   // workgroup-uniform (readfirstlane keeps the bases derived from them in SGPRs)
   const int b = __builtin_amdgcn_readfirstlane(gid / groups);
   const int ch0 = __builtin_amdgcn_readfirstlane((gid % groups) * kCh);
   if (MODE != 0 && twopass_paired(a, ch0) != (MODE == 1)) return;   // the other kernel's
-  twopass_body<T, K, MODE == 1>(a, sm, b, ch0);
+  twopass_body<T, K, MODE == 1, FDT>(a, sm, b, ch0);
+}
+
+template <typename T, int K, bool FDT>
+hipError_t dispatch_twopass_kf(const ScanArgs &a, hipStream_t s) {
+  const unsigned blocks = (unsigned)((int64_t)a.B * (a.D / kCh));
+  if (a.general_a) {
+    hipLaunchKernelGGL((scan_twopass_kernel<T, K, 0, FDT>), dim3(blocks), dim3(kW * 64), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((scan_twopass_kernel<T, K, 1, FDT>), dim3(blocks), dim3(kW * 64), 0, s, a);
+    hipLaunchKernelGGL((scan_twopass_kernel<T, K, 2, FDT>), dim3(blocks), dim3(kW * 64), 0, s, a);
+  }
+  return hipGetLastError();
 }
 
 template <typename T, int K>
 hipError_t dispatch_twopass_k(const ScanArgs &a, hipStream_t s) {
-  const unsigned blocks = (unsigned)((int64_t)a.B * (a.D / kCh));
-  if (a.general_a) {
-    hipLaunchKernelGGL((scan_twopass_kernel<T, K, 0>), dim3(blocks), dim3(kW * 64), 0, s, a);
-  } else {
-    hipLaunchKernelGGL((scan_twopass_kernel<T, K, 1>), dim3(blocks), dim3(kW * 64), 0, s, a);
-    hipLaunchKernelGGL((scan_twopass_kernel<T, K, 2>), dim3(blocks), dim3(kW * 64), 0, s, a);
+  if (a.dtlow) {
+    if constexpr (sizeof(T) == 2) return dispatch_twopass_kf<T, K, true>(a, s);
+    return hipErrorInvalidValue;
   }
-  return hipGetLastError();
+  return dispatch_twopass_kf<T, K, false>(a, s);
 }
 
 template <typename T, int K>
@@ -936,6 +1028,9 @@ hipError_t dispatch(const ScanArgs &a, hipStream_t s) {
 
 hipError_t launch_scan(mm_dtype dt, const ScanArgs &a, hipStream_t s) {
   if (a.N != 8 && a.N != 16 && a.N != 32 && a.N != 64) return hipErrorInvalidValue;
+  if (a.dtlow && (dt != MM_BF16 || !scan_fused_dt_used(a.B, a.L, a.D, a.N, kFR, a.force, a.zoh) ||
+                  !a.dtlow_lo || !a.dt_w || !a.dt_b))
+    return hipErrorInvalidValue;
   return dt == MM_BF16 ? dispatch<bf16_t>(a, s) : dispatch<float>(a, s);
 }
 
@@ -945,6 +1040,14 @@ bool scan_tuned_used(int B, int L, int D, int N, uint32_t force) {
   a.force = force;
   a.B = B; a.L = L; a.D = D; a.N = N;
   return use_lanes(a);
+}
+
+bool scan_fused_dt_used(int B, int L, int D, int N, int R, uint32_t force, int zoh) {
+  ScanArgs a{};
+  a.force = force;
+  a.B = B; a.L = L; a.D = D; a.N = N;
+  // the two-pass kernel (dispatch_few_k) at dt_rank 256
+  return N == kN && !zoh && R == kFR && use_lanes(a);
 }
 
 }  // namespace mm

@@ -73,6 +73,35 @@ def test_workspace_size_formula():
     assert mm.decode_workspace_bytes(_shape(seqlen=2)) == 0      # decode needs seqlen == 1
 
 
+def test_workspace_size_with_fused_dt_proj():
+    """MM_FLAG_FUSED_DTPROJ drops the fp32 dt buffer where the fused path applies (bf16,
+    d_state 16, dt_rank 256, first-order Bbar, the two-pass scan) and changes nothing
+    elsewhere."""
+    import torch
+    up = lambda v: (v + 255) // 256 * 256  # noqa: E731
+
+    def ws(flags, **kw):
+        s = _shape(**kw)
+        s.flags = flags
+        return mm.prefill_workspace_bytes(s)
+
+    F = mm.MM_FLAG_FUSED_DTPROJ
+    for kw in (dict(seqlen=131072), dict(seqlen=4096), dict(seqlen=1000, batch=2, d_inner=256),
+               dict(seqlen=33)):
+        T = kw.get("batch", 1) * kw["seqlen"]
+        D = kw.get("d_inner", 8192)
+        assert ws(0, **kw) - ws(F, **kw) == up(T * D * 4), kw
+        assert ws(F | mm.MM_FLAG_SCAN_CHUNKED, **kw) == ws(F, **kw), kw
+    for flags, kw in ((mm.MM_FLAG_ZOH_B, dict(seqlen=4096)),
+                      (mm.MM_FLAG_SCAN_SEQUENTIAL, dict(seqlen=4096)),
+                      (0, dict(seqlen=4096, dt_rank=128)),
+                      (0, dict(seqlen=4096, d_state=32)),
+                      (0, dict(seqlen=32)),                       # the sequential kernel's length
+                      (0, dict(seqlen=4096, batch=1024, d_inner=256)),   # many sequences
+                      (0, dict(seqlen=256, d_inner=64, dt_rank=256, dtype=torch.float32))):
+        assert ws(flags | F, **kw) == ws(flags, **kw), (flags, kw)
+
+
 def test_workspace_size_for_other_state_sizes():
     """d_state 8 / 32 / 64: where the lane-per-state-group scan applies (few sequences, > 32
     tokens) the workspace holds no general-scan transfers; the scan-selection flag
