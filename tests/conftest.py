@@ -23,8 +23,9 @@ def pytest_terminal_summary(terminalreporter, exitstatus, config):
     tr = terminalreporter
     tr.write_sep("-", f"parity checks ({len(RECORDS)})")
     worst = {}
-    for what, io, e, e_rms, nw in RECORDS:
+    for what, io, e, e_rms, nw, asserted in RECORDS:
         rms_s = "-" if e_rms is None else f"{e_rms:.3e}"
         tr.write_line(f"{io:5s} err {e:.3e}  rms-floor {rms_s:>9s}  normwise {nw:.3e}  {what}")
-        worst[io] = max(worst.get(io, 0.0), e)
-    tr.write_line("worst: " + ", ".join(f"{k} {v:.3e}" for k, v in sorted(worst.items())))
+        worst[io] = max(worst.get(io, 0.0), asserted)
+    tr.write_line("worst asserted error (bars: bf16 2e-2 relative, f32 1e-4): " +
+                  ", ".join(f"{k} {v:.3e}" for k, v in sorted(worst.items())))

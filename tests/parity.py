@@ -16,7 +16,8 @@ F32_ABS_TOL = 1e-4
 BF16_REL_TOL = 2e-2
 BF16_FLOOR = 0.01        # floor of the denominator, as a fraction of rms(r)
 
-# (what, io dtype, asserted error, rms-floor error, normwise error) of every check this session
+# (what, io dtype, error at the 0.01 rms floor (fp32: max abs), rms-floor error, normwise error,
+# the asserted error) of every check this session
 RECORDS = []
 
 
@@ -70,7 +71,7 @@ def check(got, ref, io_dtype: str, what: str, f32_large_outputs: bool = False,
         e = abs_err(g, r)
         if f32_large_outputs and r.size:
             e /= max(1.0, float(np.max(np.abs(r))))
-        RECORDS.append((what, io_dtype, e, None, normwise_err(g, r)))
+        RECORDS.append((what, io_dtype, e, None, normwise_err(g, r), e))
         assert e <= F32_ABS_TOL, f"{what}: max abs err {e:.3e} > {F32_ABS_TOL}"
     else:
         e01 = mixed_rel_err(g, r)
@@ -78,7 +79,7 @@ def check(got, ref, io_dtype: str, what: str, f32_large_outputs: bool = False,
         e = mixed_rel_err(g, r, floor=bf16_floor)
         nw = normwise_err(g, r)
         RECORDS.append((what if bf16_floor == BF16_FLOOR else f"{what} [asserted at floor "
-                        f"{bf16_floor:g} rms: {e:.3e}]", io_dtype, e01, e_rms, nw))
+                        f"{bf16_floor:g} rms: {e:.3e}]", io_dtype, e01, e_rms, nw, e))
         assert e <= BF16_REL_TOL, (f"{what}: rel err {e:.3e} (floor {bf16_floor:g} rms) > "
                                    f"{BF16_REL_TOL} (floor 0.01 rms {e01:.3e}, floor rms "
                                    f"{e_rms:.3e}, normwise {nw:.3e})")
