@@ -77,9 +77,10 @@ def test_fused_dt_declared_general_a(general_a):
     _case(cfg, 740, INPUTS["workload"], general_a=general_a)
 
 
-@pytest.mark.parametrize("L", [33, 95, 96, 97, 192, 289])
+@pytest.mark.parametrize("L", [1, 7, 33, 95, 96, 97, 192, 289])
 def test_fused_dt_lengths(L):
-    # one block and less, exactly one and two blocks, one token past a block
+    # a single token, less than one segment, one block and less, exactly one and two blocks,
+    # one token past a block (the chunked scan is forced, so the fused path runs at every L)
     cfg = BASE.with_(batch=1, seqlen=L, name=f"fused_dt_L{L}")
     _case(cfg, 750 + L, INPUTS["general_A"])
 
