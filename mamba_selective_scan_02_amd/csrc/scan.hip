@@ -557,6 +557,10 @@ struct TwoPassSmem {
   bf16_t wdt[FDT ? kCh : 1][FDT ? kFR : 8];
   float dtb[FDT ? kCh : 4];
   float pf[FDT ? kW : 1][64];
+  // bf16, unfused: each lane's byte offsets of its B|C, x, z and dt staging loads for blocks
+  // whose rows all lie inside the sequence (formed once; the edge blocks clamp rows instead)
+  static constexpr bool kOffTab = kStage && !FDT;
+  uint4 doff[kOffTab ? kW : 1][64];
 };
 
 template <typename T, int K, bool PAIRED, bool FDT>
@@ -591,10 +595,29 @@ __device__ __forceinline__ void twopass_body(const ScanArgs &a, TwoPassSmem<T, F
   // Issue the direct-to-LDS loads of this wave's segment of block `blk` (lane = this lane).
   // Rows outside [0, L) read the nearest valid row (every address is valid; prep and the scan
   // ignore those rows).
-  auto stage = [&](int blk, float (*bcdst)[2 * kN], int lane) {
+  constexpr bool kOffTab = TwoPassSmem<T, FDT>::kOffTab;
+  // this lane's staging offsets for a block inside the sequence: B|C row lane / 8 (16 bytes at
+  // 16 (lane % 8)), x row x_slot_row(sl) from the third row before the segment, z row
+  // z_slot_row(sl), dt row d_slot_row(lane / 8) (sl = lane / xrow_chunks)
+  auto interior_offsets = [&](int lane) -> uint4 {
+    const int sl = lane / xrow_chunks;
+    const uint32_t rowb = (uint32_t)row * (uint32_t)sizeof(T);
+    const uint32_t cb16 = (uint32_t)((lane % xrow_chunks) * 16);
+    return make_uint4((uint32_t)((lane >> 3) * 2 * kN + 4 * (lane & 7)) * 4u,
+                      (uint32_t)x_slot_row(sl) * rowb + cb16, (uint32_t)z_slot_row(sl) * rowb + cb16,
+                      (uint32_t)d_slot_row(lane >> 3) * (uint32_t)a.D * 4u + (uint32_t)((lane & 7) * 16));
+  };
+  auto stage = [&](int blk, float (*bcdst)[2 * kN], int lane, uint4 off) {
     // wave-uniform bases (SGPRs) and 32-bit lane offsets, so that no 64-bit address lives in
     // VGPRs across the block; rows outside [0, L) are clamped into it
     const int T0w = blk * kBlk + wv * kS;
+    if (kOffTab && T0w >= kHalo && T0w + kS - 1 <= Lm1) {   // wave-uniform: no row is clamped
+      dma16_opaque_so(bcb + (int64_t)T0w * 2 * kN, off.x, lds_addr(&bcdst[0][0]));
+      dma16_opaque_so(xzb + (int64_t)(T0w - kHalo) * row + ch0, off.y, lds_addr(&sm.x[wv][0][0]));
+      dma16_opaque_so(xzb + (int64_t)T0w * row + a.D + ch0, off.z, lds_addr(&sm.z[wv][0][0]));
+      dma16_opaque_so(db + (int64_t)T0w * a.D + ch0, off.w, lds_addr(&sm.d[wv][0][0]));
+      return;
+    }
     const int tb = min(T0w, Lm1);                 // first staged row of B|C, z, dt
     // B|C: kS rows x 128 B = kS / 8 wave-loads, 8 lanes per row; slots 0-3 B, 4-7 C
 #pragma unroll
@@ -709,6 +732,8 @@ __device__ __forceinline__ void twopass_body(const ScanArgs &a, TwoPassSmem<T, F
     const int lane = tid & 63, c = lane >> 1, p = lane & 1, ch = ch0 + c;
     wait_vmem_all();   // this wave's staged rows (and its older stores) have landed
     flush(c, p);
+    uint4 doffs = make_uint4(0u, 0u, 0u, 0u);
+    if (kOffTab) doffs = sm.doff[wv][lane];
     // this lane's LDS rows: (dt, dt*u) column, B|C slot
     const uint32_t pdl = lds_addr(&sm.pd[wv][0][c]);
     const uint32_t bcl = lds_addr(&bc_cur[wv][0][kG * p]);
@@ -791,7 +816,7 @@ __device__ __forceinline__ void twopass_body(const ScanArgs &a, TwoPassSmem<T, F
     // the staged x, z, dt rows are consumed once this wave's LDS reads have returned; then the
     // next block's rows may land (B|C is double-buffered)
     __builtin_amdgcn_s_waitcnt(0xC07F);           // lgkmcnt(0), vmcnt / expcnt unconstrained
-    if (blk + 1 < nblocks) stage(blk + 1, bc_nxt[wv], lane);
+    if (blk + 1 < nblocks) stage(blk + 1, bc_nxt[wv], lane, doffs);
 
     // ---- 2. local pass over this wave's segment
     float A2[kG];
@@ -912,8 +937,9 @@ __device__ __forceinline__ void twopass_body(const ScanArgs &a, TwoPassSmem<T, F
       }
       if (tid < kCh) sm.dtb[tid] = a.dt_b[ch0 + tid];
     }
+    if (kOffTab) sm.doff[wv][tid & 63] = interior_offsets(tid & 63);
     __syncthreads();
-    stage(0, sm.bc[0][wv], tid & 63);
+    stage(0, sm.bc[0][wv], tid & 63, kOffTab ? sm.doff[wv][tid & 63] : make_uint4(0u, 0u, 0u, 0u));
     if (FDT) {
       dt_phase(0);
       lds_barrier();
