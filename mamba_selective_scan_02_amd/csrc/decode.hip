@@ -217,18 +217,26 @@ __global__ __launch_bounds__(64 * kNormWaves) void decode_norm_kernel(DecodeNorm
   }
 }
 
-// State update. A workgroup covers U x 64 consecutive (b, i) channels; in unit j, lane l of a
-// wave takes channel 64 j + l / 4 of its 16-channel slice, states 4 (l % 4) .. +3, so each
-// state load / store of a wave is 1 KB contiguous. The loads of all U units are issued before
-// any arithmetic; per-channel scalars are fetched once per channel (one lane each) and shared
-// within the channel's 4 lanes by DPP, the sequence's B | C row once per wave and shared by
-// bpermute. U = 2 keeps the kernel under 64 VGPRs (the most waves per SIMD) with two units of
-// state in flight per lane.
-template <bool ZOH, int U>
+// State update. With SEQ = false a workgroup covers U x 64 consecutive (b, i) channels; in
+// unit j, lane l of a wave takes channel 64 j + l / 4 of its 16-channel slice, states
+// 4 (l % 4) .. +3, so each state load / store of a wave is 1 KB contiguous. With SEQ = true a
+// workgroup covers 64 channels of U consecutive sequences (unit j = sequence j of the group):
+// the channel's A row, taps, bias and D are then loaded once for the U units. The loads of all
+// U units are issued before any arithmetic; per-channel scalars are fetched once per channel
+// (one lane each) and shared within the channel's 4 lanes by DPP, the sequence's B | C row
+// once per wave and shared by bpermute. U = 2 keeps the kernel under 64 VGPRs (the most waves
+// per SIMD) with two units of state in flight per lane.
+template <bool ZOH, int U, bool SEQ>
 __global__ __launch_bounds__(256) void decode_update_kernel(DecodeUpdateArgs a) {
   const int q = threadIdx.x & 3;
-  const int64_t g0 = (int64_t)blockIdx.x * (64 * U) + (threadIdx.x >> 2);   // b * D + i
-  const int64_t w0 = (int64_t)blockIdx.x * (64 * U) + (threadIdx.x >> 6) * 16;
+  // unit j: (b, i) = gch(j) / D, gch(j) % D
+  const int ngc = a.D / 64;
+  const int64_t seq0 = SEQ ? (int64_t)(blockIdx.x / ngc) * U : 0;
+  const int ich = SEQ ? (int)(blockIdx.x % ngc) * 64 + (threadIdx.x >> 2) : 0;
+  const int64_t g0 = SEQ ? seq0 * a.D + ich
+                         : (int64_t)blockIdx.x * (64 * U) + (threadIdx.x >> 2);   // b * D + i
+  const int64_t w0 = SEQ ? seq0 * a.D : (int64_t)blockIdx.x * (64 * U) + (threadIdx.x >> 6) * 16;
+  const int64_t ustep = SEQ ? (int64_t)a.D : 64;   // gch(j + 1) - gch(j)
   float4 h[U], Av[U];
   float Bq[U][4], Cq[U][4];
   uint32_t cs16[U], p16[U];
@@ -236,17 +244,18 @@ __global__ __launch_bounds__(256) void decode_update_kernel(DecodeUpdateArgs a) 
   uint2 wr[U];
 #pragma unroll
   for (int j = 0; j < U; ++j) {
-    const int64_t gch = g0 + 64 * j;
-    const int i = (int)(gch % a.D);
-    const int b = (int)(gch / a.D);
+    const int64_t gch = g0 + ustep * j;
+    const int i = SEQ ? ich : (int)(gch % a.D);
+    const int b = SEQ ? (int)seq0 + j : (int)(gch / a.D);
     // the wave's 16 channels of unit j lie in one sequence (d_inner % 16 == 0)
-    const int bw = __builtin_amdgcn_readfirstlane((int)((w0 + 64 * j) / a.D));
+    const int bw = SEQ ? (int)seq0 + j : __builtin_amdgcn_readfirstlane((int)((w0 + 64 * j) / a.D));
     {   // the state streams through once per step: non-temporal, so it does not evict the
         // weights and staged rows the other kernels of the step reuse from L2
       const f32x4 hv4 = __builtin_nontemporal_load((const f32x4 *)(a.state + gch * 16 + 4 * q));
       h[j] = make_float4(hv4[0], hv4[1], hv4[2], hv4[3]);
     }
-    Av[j] = *(const float4 *)(a.A + (int64_t)i * 16 + 4 * q);
+    if (!SEQ || j == 0) Av[j] = *(const float4 *)(a.A + (int64_t)i * 16 + 4 * q);
+    else Av[j] = Av[0];
     // lane l holds value l % 32 of the sequence's B | C row; lanes fetch theirs by bpermute
     const float bcl = a.bc[(int64_t)bw * 32 + (threadIdx.x & 31)];
 #pragma unroll
@@ -263,12 +272,17 @@ __global__ __launch_bounds__(256) void decode_update_kernel(DecodeUpdateArgs a) 
     p16[j] = *src;
     if (q == 3 && !a.conv_b) p16[j] = 0;
     dtv[j] = a.dt[gch];   // fp32 dt (the channel's 4 lanes read the same word)
-    wr[j] = *(const uint2 *)(a.conv_w + (int64_t)i * 4);
-    Dv[j] = a.Dskip[i];
+    if (!SEQ || j == 0) {
+      wr[j] = *(const uint2 *)(a.conv_w + (int64_t)i * 4);
+      Dv[j] = a.Dskip[i];
+    } else {
+      wr[j] = wr[0];
+      Dv[j] = Dv[0];
+    }
   }
 #pragma unroll
   for (int j = 0; j < U; ++j) {
-    const int64_t gch = g0 + 64 * j;
+    const int64_t gch = g0 + ustep * j;
     const int cs = (int)cs16[j], pv = (int)p16[j];
     const float c0 = bf2f((bf16_t)__builtin_amdgcn_mov_dpp(cs, 0x00, 0xF, 0xF, false));
     const float c1 = bf2f((bf16_t)__builtin_amdgcn_mov_dpp(cs, 0x55, 0xF, 0xF, false));
@@ -338,10 +352,12 @@ hipError_t launch_decode_norm(const DecodeNormArgs &a, hipStream_t s) {
 template <bool ZOH>
 hipError_t launch_upd(const DecodeUpdateArgs &a, hipStream_t s) {
   const int64_t n = (int64_t)a.B * a.D;   // a multiple of 64
-  if (n % 128 == 0)
-    hipLaunchKernelGGL((decode_update_kernel<ZOH, 2>), dim3((unsigned)(n / 128)), dim3(256), 0, s, a);
+  if (a.B % 2 == 0)        // pairs of sequences share each channel's parameters
+    hipLaunchKernelGGL((decode_update_kernel<ZOH, 2, true>), dim3((unsigned)(n / 128)), dim3(256), 0, s, a);
+  else if (n % 128 == 0)
+    hipLaunchKernelGGL((decode_update_kernel<ZOH, 2, false>), dim3((unsigned)(n / 128)), dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL((decode_update_kernel<ZOH, 1>), dim3((unsigned)(n / 64)), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((decode_update_kernel<ZOH, 1, false>), dim3((unsigned)(n / 64)), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
