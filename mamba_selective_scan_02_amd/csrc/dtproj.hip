@@ -94,18 +94,25 @@ __global__ __launch_bounds__(512) void dtproj_kernel(DtprojArgs a, int ch_per_wg
     f32x4 acc[4];
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // per k-step: the four W_dt fragments are read together, then the low-plane MFMAs of the
+    // four accumulators and their high-plane MFMAs (each accumulator still takes low, then
+    // high, k-step by k-step), so no MFMA waits on the LDS read or on its own predecessor
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const bf16x8 bh = __builtin_bit_cast(bf16x8, fh[ks]);
       const bf16x8 bl = __builtin_bit_cast(bf16x8, fl[ks]);
+      bf16x8 fw[4];
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb) {
         const int r = nb * 16 + tl;
-        const bf16x8 fw = __builtin_bit_cast(
-            bf16x8, *(const uint4 *)&wcur[r][swz<S>(r, ks * 4 + g) * 8]);
-        acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fw, bl, acc[nb], 0, 0, 0);
-        acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fw, bh, acc[nb], 0, 0, 0);
+        fw[nb] = __builtin_bit_cast(bf16x8, *(const uint4 *)&wcur[r][swz<S>(r, ks * 4 + g) * 8]);
       }
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+        acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fw[nb], bl, acc[nb], 0, 0, 0);
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+        acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fw[nb], bh, acc[nb], 0, 0, 0);
     }
     // acc[nb][j] = pre-activation of (token tok, channel c0 + 16 nb + 4 g + j)
     const int c0 = cbeg + ck * kChD;
