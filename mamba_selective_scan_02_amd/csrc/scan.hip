@@ -480,7 +480,8 @@ hipError_t dispatch_lanes_k(const ScanArgs &a, hipStream_t s) {
 // 8 (l % 2) .. +7 (B_t / C_t reads from LDS serve 8 updates):
 //  0. The segment's B|C rows, its x rows (with the 3 conv-window rows before it), z and dt
 //     rows were loaded into the wave's LDS rows with direct-to-LDS 16-byte loads while the
-//     previous block was computed.
+//     previous block was computed (blocks inside the sequence take each lane's byte offsets
+//     from a table formed once; edge blocks clamp rows into the sequence).
 //  1. Prep: lane l takes channel l / 2 and the segment's tokens kS/2 (l % 2) .. +kS/2-1:
 //     u = SiLU(conv1d(x) + b), dt and dt*u go to the wave's LDS rows; D*u and SiLU(z) of
 //     those tokens stay in the lane's registers for step 4 (the wave waits on its own loads
@@ -501,6 +502,9 @@ hipError_t dispatch_lanes_k(const ScanArgs &a, hipStream_t s) {
 // A[i, 8 p + k] = A[i, 8 p] + k delta_i for every lane, the local pass forms a lane's 8
 // decays as exp(dt A[i, 8 p]) times powers of exp(dt delta_i): 2 exps per lane and token
 // instead of 8.
+// Fused dt_proj (ScanArgs::dtlow set): instead of staging dt rows, the workgroup forms the
+// next block's dt after each replay from the normalised dt_low with split-precision MFMAs
+// (dt_phase below) and a third barrier hands it to the prep.
 constexpr int kCh = 32, kW = 12, kS = 8, kG = 8, kBlk = kW * kS;
 constexpr int kHalf = kS / 2;             // tokens per lane in the prep and the output
 constexpr int kHalo = 3;                  // x rows before the segment (conv window, K - 1 <= 3)
@@ -683,13 +687,18 @@ __device__ __forceinline__ void twopass_body(const ScanArgs &a, TwoPassSmem<T, F
     f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
     for (int ks = 0; ks < kFK; ++ks) {
+      // both fragments read first, then the low-plane MFMAs, then the high-plane ones
+      bf16x8 fw[2];
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        const uint32_t wl = lds_addr(&sm.wdt[16 * nb + tl][0]);
-        const bf16x8 fw = __builtin_bit_cast(bf16x8, *lds_ptr<const uint4>(wl + 16u * ((4 * ks + g) ^ tl)));
-        acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fw, __builtin_bit_cast(bf16x8, fl[ks]), acc[nb], 0, 0, 0);
-        acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fw, __builtin_bit_cast(bf16x8, fh[ks]), acc[nb], 0, 0, 0);
-      }
+      for (int nb = 0; nb < 2; ++nb)
+        fw[nb] = __builtin_bit_cast(bf16x8, *lds_ptr<const uint4>(lds_addr(&sm.wdt[16 * nb + tl][0]) +
+                                                                 16u * ((4 * ks + g) ^ tl)));
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+        acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fw[nb], __builtin_bit_cast(bf16x8, fl[ks]), acc[nb], 0, 0, 0);
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+        acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fw[nb], __builtin_bit_cast(bf16x8, fh[ks]), acc[nb], 0, 0, 0);
     }
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
