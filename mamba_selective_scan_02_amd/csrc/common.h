@@ -67,15 +67,19 @@ __device__ __forceinline__ float softplus_f(float v) {
   if (w == 1.0f) return e;
   return __builtin_amdgcn_logf(w) * 0.69314718055994531f * (e * __builtin_amdgcn_rcpf(w - 1.0f));
 }
-// softplus_f with every case computed and selected (selects, not divergent branches around the
-// log): e = e^v, w = 1 + e, log(w) e / (w - 1) (Goldberg's log1p method), e itself where w
-// rounds to 1, and v above 20. dt_proj's epilogue (on its own or fused into the scan) uses it.
+// softplus_f without branches (dt_proj's epilogue, on its own or fused into the scan). With
+// e = e^v and w = 1 + e rounded, delta = (w - 1) - e is that rounding exactly (w - 1 is exact),
+// so log(1 + e) = log(w - delta) = log(w) - delta / w to within delta^2 / w^2 < 2^-48. 1 / w is
+// taken as 2 - w (exact to second order in w - 1, where the correction matters) and as 0 once
+// w >= 2 (there |delta| / w <= 2^-24 of log(w) >= log 2). Where 1 + e rounds to 1 this gives
+// e itself (delta = -e). Above 20, v (within 2e-9 relative). One transcendental fewer than
+// Goldberg's form log(w) e / (w - 1) of softplus_f.
 __device__ __forceinline__ float softplus_sel(float v) {
   const float e = exp2_hw(v * kLog2e);
   const float w = 1.0f + e;
-  const float d = w - 1.0f;
-  const float l = __builtin_amdgcn_logf(w) * 0.69314718055994531f * (e * __builtin_amdgcn_rcpf(d));
-  const float r = d == 0.0f ? e : l;
+  const float delta = (w - 1.0f) - e;
+  const float r = __builtin_fmaf(-delta, fmaxf(2.0f - w, 0.0f),
+                                 __builtin_amdgcn_logf(w) * 0.69314718055994531f);
   return v > 20.0f ? v : r;
 }
 
