@@ -16,8 +16,18 @@ __device__ __forceinline__ bf16_t f2bf(float f) {
   __bf16 h = (__bf16)f;
   return __builtin_bit_cast(bf16_t, h);
 }
+// two floats to a bf16 pair (lo in the low half), both rounded to nearest even by one
+// v_cvt_pk_bf16_f32 (the same rounding as f2bf)
+typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
 __device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
-  return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
+}
+// split-precision pair: hi = (bf16(u0), bf16(u1)), lo = (bf16(u0 - hi0), bf16(u1 - hi1)), the
+// high parts widened back by shifting / masking their packed halves
+__device__ __forceinline__ void split_bf2(float u0, float u1, uint32_t &hi, uint32_t &lo) {
+  hi = pack_bf2(u0, u1);
+  lo = pack_bf2(u0 - __uint_as_float(hi << 16), u1 - __uint_as_float(hi & 0xffff0000u));
 }
 __device__ __forceinline__ float lo_bf(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float hi_bf(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }

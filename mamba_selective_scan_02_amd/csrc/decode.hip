@@ -111,15 +111,10 @@ __global__ __launch_bounds__(256) void decode_xproj_kernel(DecodeXprojArgs a) {
         u[e] = silu_f(acc0);
       }
       uint4 hi, lo;
-      {
-        float l8[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) l8[e] = u[e] - bf2f(f2bf(u[e]));
-        hi.x = pack_bf2(u[0], u[1]); hi.y = pack_bf2(u[2], u[3]);
-        hi.z = pack_bf2(u[4], u[5]); hi.w = pack_bf2(u[6], u[7]);
-        lo.x = pack_bf2(l8[0], l8[1]); lo.y = pack_bf2(l8[2], l8[3]);
-        lo.z = pack_bf2(l8[4], l8[5]); lo.w = pack_bf2(l8[6], l8[7]);
-      }
+      split_bf2(u[0], u[1], hi.x, lo.x);
+      split_bf2(u[2], u[3], hi.y, lo.y);
+      split_bf2(u[4], u[5], hi.z, lo.z);
+      split_bf2(u[6], u[7], hi.w, lo.w);
       const bf16x8 fh = __builtin_bit_cast(bf16x8, hi), fl = __builtin_bit_cast(bf16x8, lo);
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {

@@ -176,15 +176,10 @@ __global__ __launch_bounds__(1024) void xproj_fused_kernel(XprojFusedArgs a) {
         u[e] = silu_f(accv);
       }
       uint4 hi, lo;
-      {
-        float l8[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) l8[e] = u[e] - bf2f(f2bf(u[e]));
-        hi.x = pack_bf2(u[0], u[1]); hi.y = pack_bf2(u[2], u[3]);
-        hi.z = pack_bf2(u[4], u[5]); hi.w = pack_bf2(u[6], u[7]);
-        lo.x = pack_bf2(l8[0], l8[1]); lo.y = pack_bf2(l8[2], l8[3]);
-        lo.z = pack_bf2(l8[4], l8[5]); lo.w = pack_bf2(l8[6], l8[7]);
-      }
+      split_bf2(u[0], u[1], hi.x, lo.x);
+      split_bf2(u[2], u[3], hi.y, lo.y);
+      split_bf2(u[4], u[5], hi.z, lo.z);
+      split_bf2(u[6], u[7], hi.w, lo.w);
       // fragment lane (token % 16) + 16 * grp of column block token / 16
       const int fo = (grp * 16 + (ptok & 15)) * 8;
       *(uint4 *)&u_s[ck & 1][0][ptok >> 4][fo] = hi;
@@ -304,9 +299,8 @@ __global__ __launch_bounds__(1024) void xproj_fused_kernel(XprojFusedArgs a) {
           const float v0 = acc[tb][i][0] * id * gm.x, v1 = acc[tb][i][1] * id * gm.y;
           const float v2 = acc[tb][i][2] * id * gm.z, v3 = acc[tb][i][3] * id * gm.w;
           uint2 h, l;
-          h.x = pack_bf2(v0, v1); h.y = pack_bf2(v2, v3);
-          l.x = pack_bf2(v0 - bf2f(f2bf(v0)), v1 - bf2f(f2bf(v1)));
-          l.y = pack_bf2(v2 - bf2f(f2bf(v2)), v3 - bf2f(f2bf(v3)));
+          split_bf2(v0, v1, h.x, l.x);
+          split_bf2(v2, v3, h.y, l.y);
           *(uint2 *)(a.dtlow + tok * R + n) = h;
           *(uint2 *)(a.dtlow_lo + tok * R + n) = l;
         } else {
