@@ -48,7 +48,8 @@ __global__ __launch_bounds__(512) void dtproj_kernel(DtprojArgs a, int ch_per_wg
   const int ntok = (a.T + kTokD - 1) / kTokD;
   const int gid = xcd_remap(blockIdx.x, gridDim.x);
   const int tt = gid % ntok, cg = gid / ntok;      // token tile, channel group
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: scalar load loops
   const int tl = lane & 15, g = lane >> 4;
   const int tok = tt * kTokD + wv * 16 + tl;
   const int tokc = min(tok, a.T - 1);
