@@ -75,7 +75,8 @@ __global__ __launch_bounds__(1024) void xproj_fused_kernel(XprojFusedArgs a) {
   const int gid = xcd_remap(blockIdx.x, gridDim.x);
   const int b = gid / tiles_per_seq;
   const int t0 = (gid % tiles_per_seq) * kTok;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: scalar role / load branches
   const bool producer = wv < 8;
   const int64_t row = 2LL * a.D;
   const bf16_t *xzb = a.xz + (int64_t)b * a.L * row;
