@@ -42,7 +42,8 @@ __global__ __launch_bounds__(256) void decode_xproj_kernel(DecodeXprojArgs a) {
   const int nseqt = (a.B + kSeqW - 1) / kSeqW;
   const int gid = blockIdx.x;
   const int st = gid % nseqt, kr = gid / nseqt;   // sequence tile, channel range
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: scalar load loop
   const int tl = lane & 15, g = lane >> 4;
   const int bs = st * kSeqW + wv * 16 + tl;       // this lane's sequence
   const int bsc = min(bs, a.B - 1);
