@@ -489,8 +489,9 @@ hipError_t dispatch_lanes_k(const ScanArgs &a, hipStream_t s) {
 //  2. Local pass: the segment is scanned from h = 0, keeping exp(dt A) of every (token, state)
 //     in VGPRs (one exp per element, as in the sequential recurrence).
 //  3. Compose: the segment's transfer h -> P h + S (local end state S, decay
-//     P = exp(A sum dt), formed by the segment's own lanes) goes to LDS (barrier). Thread i
-//     then owns one (channel, state) chain: it applies the segments' transfers in order to
+//     P = exp(A sum dt)) goes to LDS as S and the segment's sum dt per channel (barrier).
+//     Thread i then owns one (channel, state) chain: it forms each segment's P from its sum dt
+//     and applies the segments' transfers in order to
 //     the block's carry-in with the page's associative operator ("Parallel training via the
 //     parallel scan": (a, b) then (c, d) gives (ac, ad + b) for h -> a h + b), writing each
 //     segment's h_in over its S (barrier), and keeps the result as the next block's carry-in.
@@ -524,7 +525,7 @@ __device__ __forceinline__ int z_slot_row(int s) { return s < 4 ? s : min(s - 1,
 __device__ __forceinline__ int d_slot_row(int s) { return s ^ ((s >> 2) & 1); }
 constexpr int kChains = kCh * kN;         // (channel, state) chains of a workgroup
 static_assert(kChains == 512 && kW * 64 >= kChains, "chain threads map onto 512 agg floats");
-static_assert(kW * kS * 64 <= 65536 && kW * 4 * 64 * 16 <= 65536, "LDS offsets fit 16 bits");
+static_assert(kW * kS * 64 <= 65536 && kW * 2 * 64 * 16 <= 65536, "LDS offsets fit 16 bits");
 
 constexpr int kFR = 256;                  // dt_rank of the fused dt_proj
 constexpr int kFK = kFR / 32;             // its k-steps (16x16x32 MFMAs per plane)
@@ -547,9 +548,11 @@ struct TwoPassSmem {
   // prep output: (dt, dt*u) per (token, channel) of each wave's segment; rows padded by one
   // element so that the rows of the two lanes of a channel fall in different LDS banks
   float2 pd[kW][kS][kCh + 1];
-  // per segment and lane, 16-byte slots [wave][S0..3, S4..7, P0..3, P4..7][lane]: the local
-  // end states S (overwritten by the segments' true start states) and decays P = exp(A sum dt)
-  float4 agg[kW][4][64];
+  // per segment and lane, 16-byte slots [wave][S0..3, S4..7][lane]: the local end states S
+  // (overwritten by the segments' true start states); and per segment and channel, the sum
+  // of dt over the segment, from which the chain threads form the decays P = exp(A sum dt)
+  float4 agg[kW][2][64];
+  float sdt[kW][kCh];
   // per channel: conv taps (K) | conv bias, D, -, -; and A log2(e) as [half][lane] 16-byte
   // slots (lane 2 c + p holds states 8 p + 4 half .. +3 of channel c): the per-block reads are
   // lane-contiguous
@@ -576,8 +579,8 @@ __device__ __forceinline__ void twopass_body(const ScanArgs &a, TwoPassSmem<T, F
   constexpr uint32_t kPdRow = (kCh + 1) * sizeof(float2), kBcRow = 2 * kN * sizeof(float);
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
   // chain thread tid (waves 0-7) <-> publishing lane ql = (tid >> 2) & 63 (channel ql / 2,
-  // state half ql & 1), state j = 4 (tid >> 8) + (tid & 3) of that half: its S and P of
-  // segment w are floats w * 1024 + tid and w * 1024 + 512 + tid of agg (conflict-free)
+  // state half ql & 1), state j = 4 (tid >> 8) + (tid & 3) of that half: its S of segment w
+  // is float w * 512 + tid of agg (conflict-free)
   const bool chain = wv < kChains / 64;
   float carry = 0.f;
   if (chain && a.state_valid && a.state) {
@@ -856,25 +859,25 @@ __device__ __forceinline__ void twopass_body(const ScanArgs &a, TwoPassSmem<T, F
     // ---- 3. publish this segment's transfer h -> P h + S, then compose
     sm.agg[wv][0][lane] = make_float4(hl[0], hl[1], hl[2], hl[3]);
     sm.agg[wv][1][lane] = make_float4(hl[4], hl[5], hl[6], hl[7]);
-    {
-      float P[kG];
-#pragma unroll
-      for (int j = 0; j < kG; ++j) P[j] = exp2_hw(A2[j] * sumdt);
-      sm.agg[wv][2][lane] = make_float4(P[0], P[1], P[2], P[3]);
-      sm.agg[wv][3][lane] = make_float4(P[4], P[5], P[6], P[7]);
-    }
+    if (p == 0) sm.sdt[wv][c] = sumdt;   // the channel's two lanes hold the same sum
     lds_barrier();
-    // chain pass: each segment's S becomes its h_in (all reads in flight together, then the
-    // dependent fmas)
+    // chain pass: each segment's S becomes its h_in (all reads in flight together, the decays
+    // formed from them, then the dependent fmas); the decay exp(A sum dt) is the one the
+    // segment's lanes would form (A log2(e) from the same table, the same sum)
     if (chain) {
       const uint32_t al = lds_addr(&sm.agg[0][0][0].x) + 4u * tid;
-      constexpr uint32_t kSeg = 4 * 64 * 16;      // bytes per segment in agg
+      constexpr uint32_t kSeg = 2 * 64 * 16;      // bytes per segment in agg
+      const int ql = (tid >> 2) & 63;
+      const float a2v = (&sm.a2[(tid >> 8) & 1][ql].x)[tid & 3];
+      const uint32_t sl = lds_addr(&sm.sdt[0][ql >> 1]);
       float Sw[kW], Pw[kW];
 #pragma unroll
       for (int w2 = 0; w2 < kW; ++w2) {
         Sw[w2] = *lds_ptr<const float>(al + w2 * kSeg);
-        Pw[w2] = *lds_ptr<const float>(al + w2 * kSeg + kChains * 4);
+        Pw[w2] = *lds_ptr<const float>(sl + w2 * kCh * 4);
       }
+#pragma unroll
+      for (int w2 = 0; w2 < kW; ++w2) Pw[w2] = exp2_hw(a2v * Pw[w2]);
 #pragma unroll
       for (int w2 = 0; w2 < kW; ++w2) {
         *lds_ptr<float>(al + w2 * kSeg) = carry;
