@@ -77,7 +77,6 @@ def measured_scan_traffic():
     """HBM bytes per launch of the scan kernel from the committed rocprofv3 FETCH_SIZE /
     WRITE_SIZE passes (profiles/selective_scan_traffic.json), or None when the scan kernel's
     sources have changed since those counters were taken."""
-    import hashlib
     path = os.path.join(ROOT, "profiles", "selective_scan_traffic.json")
     if not os.path.exists(path):
         return None
