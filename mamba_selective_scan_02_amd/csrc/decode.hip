@@ -7,10 +7,12 @@
 // ("The Mamba Layer": ZOH and recurrence equations; RMSNorm equation).
 //
 // Kernels:
-//   decode_xproj_kernel  64 sequences x a 1024-channel range of d_inner per workgroup: u in fp32
-//                        from the carried conv state and x_t (each lane forms exactly its MFMA
-//                        fragment), split hi + lo, two bf16 MFMA passes against W_x chunks that
-//                        stream through XOR-swizzled LDS (direct-to-LDS loads, double-buffered).
+//   decode_xproj_kernel  64 sequences x one channel range of d_inner per workgroup (the sequence
+//                        tiles of a range on one XCD): u in fp32 from the carried conv state
+//                        and x_t (each lane forms exactly its MFMA fragment), split hi + lo,
+//                        two bf16 MFMA passes against W_x chunks that stream through
+//                        XOR-swizzled LDS (direct-to-LDS loads, double-buffered; a chunk's
+//                        global inputs are loaded during the previous chunk's arithmetic).
 //                        Writes the range's fp32 partial sums of xdbl.
 //   decode_norm_kernel   sums the ranges' partials in a fixed order (deterministic) and applies
 //                        the three RMSNorms: dt_low (bf16 hi + lo, for dt_proj) and B | C (fp32);
@@ -40,7 +42,9 @@ __global__ __launch_bounds__(256) void decode_xproj_kernel(DecodeXprojArgs a) {
   __shared__ __attribute__((aligned(16))) bf16_t w_s1[NX][kKC];
 
   const int nseqt = (a.B + kSeqW - 1) / kSeqW;
-  const int gid = blockIdx.x;
+  // the sequence tiles of one channel range run on one XCD, so that range's W_x rows cross
+  // from memory into that XCD's L2 once and serve every tile from there
+  const int gid = xcd_remap(blockIdx.x, gridDim.x);
   const int st = gid % nseqt, kr = gid / nseqt;   // sequence tile, channel range
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: scalar load loop
@@ -64,41 +68,51 @@ __global__ __launch_bounds__(256) void decode_xproj_kernel(DecodeXprojArgs a) {
 #pragma unroll
   for (int i = 0; i < NB; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto chunk = [&](int ck, bf16_t (*wcur)[kKC], bf16_t (*wnxt)[kKC]) {
-    wait_vmem_all();
-    lds_barrier();
-    if (ck + 1 < nck) stage(ck + 1, wnxt);
+  // the global inputs of one chunk's two k-steps: carried conv state, x_t, taps and bias
+  struct ChunkIn {
+    uint4 cs[2][3], x[2], b[2];
+    uint2 w[2][8];
+  };
+  const bf16_t *cbp = a.conv_b ? a.conv_b : a.conv_w;   // without a bias: read, not used
+  auto load_in = [&](int ck, ChunkIn &in) {
     const int c0 = cbeg + ck * kKC;
-    // every global input of the chunk's two k-steps is loaded before any is used, so that the
-    // wave waits once for all of them (one wave per SIMD: the registers are there)
-    uint4 cs_l[2][3], x_l[2], b_l[2];
-    uint2 w_l[2][8];
-    const bf16_t *cbp = a.conv_b ? a.conv_b : a.conv_w;   // without a bias: read, not used
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       const int ch = c0 + (ks * 4 + g) * 8;
       const bf16_t *csp = a.conv_state + ((int64_t)bsc * a.D + ch) * 3;
 #pragma unroll
-      for (int q = 0; q < 3; ++q) cs_l[ks][q] = *(const uint4 *)(csp + 8 * q);
-      x_l[ks] = *(const uint4 *)(a.xz + (int64_t)bsc * 2 * a.D + ch);
+      for (int q = 0; q < 3; ++q) in.cs[ks][q] = *(const uint4 *)(csp + 8 * q);
+      in.x[ks] = *(const uint4 *)(a.xz + (int64_t)bsc * 2 * a.D + ch);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) w_l[ks][e] = *(const uint2 *)(a.conv_w + (int64_t)(ch + e) * 4);
-      b_l[ks] = *(const uint4 *)(cbp + ch);   // the 8 channels' bias
+      for (int e = 0; e < 8; ++e) in.w[ks][e] = *(const uint2 *)(a.conv_w + (int64_t)(ch + e) * 4);
+      in.b[ks] = *(const uint4 *)(cbp + ch);   // the 8 channels' bias
+    }
+  };
+  // Chunk ck: its W_x rows and global inputs were issued one chunk earlier, so their latency
+  // is hidden behind the previous chunk's arithmetic; the next chunk's are issued before this
+  // one's arithmetic. Nothing newer than them is in flight at the wait.
+  auto chunk = [&](int ck, const ChunkIn &in, ChunkIn &nxt, bf16_t (*wcur)[kKC],
+                   bf16_t (*wnxt)[kKC]) {
+    wait_vmem_all();
+    lds_barrier();
+    if (ck + 1 < nck) {
+      stage(ck + 1, wnxt);
+      load_in(ck + 1, nxt);
     }
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       const int lc = ks * 4 + g;                       // 8 channels: c0 + 8 lc .. +7
       // conv window: carried state (3 per channel, oldest first) then x_t
-      const uint4 s0 = cs_l[ks][0], s1 = cs_l[ks][1], s2 = cs_l[ks][2];
+      const uint4 s0 = in.cs[ks][0], s1 = in.cs[ks][1], s2 = in.cs[ks][2];
       const uint32_t sw[12] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w,
                                s2.x, s2.y, s2.z, s2.w};
-      const uint4 xv = x_l[ks];
+      const uint4 xv = in.x[ks];
       const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
       float u[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const uint2 wr = w_l[ks][e];
-        const uint32_t bw = e < 2 ? b_l[ks].x : e < 4 ? b_l[ks].y : e < 6 ? b_l[ks].z : b_l[ks].w;
+        const uint2 wr = in.w[ks][e];
+        const uint32_t bw = e < 2 ? in.b[ks].x : e < 4 ? in.b[ks].y : e < 6 ? in.b[ks].z : in.b[ks].w;
         float acc0 = a.conv_b ? ((e & 1) ? hi_bf(bw) : lo_bf(bw)) : 0.f;
         const int s = e * 3;  // bf16 index of channel e's first state value
         const float c0v = (s & 1) ? hi_bf(sw[s >> 1]) : lo_bf(sw[s >> 1]);
@@ -127,10 +141,13 @@ __global__ __launch_bounds__(256) void decode_xproj_kernel(DecodeXprojArgs a) {
     }
   };
 
+  // two register sets of inputs, alternating with the two W_x buffers
+  ChunkIn in0, in1;
   stage(0, w_s0);
-  for (int ck = 0; ck < nck; ++ck) {
-    const bool odd = ck & 1;
-    chunk(ck, odd ? w_s1 : w_s0, odd ? w_s0 : w_s1);
+  load_in(0, in0);
+  for (int ck = 0; ck < nck; ck += 2) {
+    chunk(ck, in0, in1, w_s0, w_s1);
+    if (ck + 1 < nck) chunk(ck + 1, in1, in0, w_s1, w_s0);
   }
   // partial sums of this channel range: part[kr][b][n]
   if (bs < a.B) {
