@@ -170,6 +170,9 @@ DECODE_CASES = [
     ("dec_b65_r256_zoh", 65, 2048, 256, 4, True, True, True),
     ("dec_b200_r512", 200, 512, 512, 4, True, False, False),
     ("dec_b70_k3", 70, 512, 64, 3, True, False, False),
+    # 5 sequence tiles x 38 ranges of 3 chunks (the last of 1): a grid of 190 workgroups, not a
+    # multiple of the 8 XCDs, so the XCD mapping of the x_proj workgroups has a tail
+    ("dec_b300_d7168_r64", 300, 7168, 64, 4, True, False, True),
 ]
 
 
